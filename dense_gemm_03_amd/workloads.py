@@ -1,0 +1,147 @@
+"""Seeded synthetic GEMM workloads: shapes, value distributions and generators.
+
+This module holds no GEMM arithmetic.  It only draws operands, so that the GPU
+library and the CPU oracle are fed identical bits.  Both sides may import it.
+
+Shapes and distributions (all row-major, tight leading dimensions):
+
+==========  =====================  ==========================  ======
+name        M x N x K              entries                     seed
+==========  =====================  ==========================  ======
+fp32-256    256 x 256 x 256        fp32 uniform[-1, 1]         101
+fp32-4096   4096 x 4096 x 4096     fp32 uniform[-1, 1]         102
+fp32-1000   1000 x 1000 x 1000     fp32 uniform[-1, 1]         103
+fp32-rag    4097 x 4095 x 4099     fp32 uniform[-1, 1]         104
+bf16-8192   8192 x 8192 x 8192     normal(0,1) rounded to bf16 105
+im2col      64 x 16384 x 61504     fp32 uniform[-1, 1]         106
+tall        65536 x 64 x 1024      fp32 uniform[-1, 1]         107
+==========  =====================  ==========================  ======
+
+A is drawn with ``seed`` and B with ``seed + 1000`` from
+``numpy.random.default_rng``.  Large operands are drawn in row chunks; the
+PCG64 stream yields the same values whether drawn at once or in chunks.
+
+The im2col shape is the weight-gradient GEMM of a 2-D convolution with a large
+kernel ("Three X's: large convolutions in PyTorch for model training",
+sections on where large kernels come from and on the im2col route through
+cuBLAS): 64 output channels, 64 input channels times a 31 x 31 kernel area
+(K = 61504) and 128 x 128 output positions (N = 16384).  Its operands here are
+i.i.d. uniform, without the repeated entries a real column matrix carries.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+_CHUNK_ELEMS = 1 << 24  # draw at most 16M values at a time
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str  # "f32" or "bf16" (bf16 inputs, fp32 output)
+    M: int
+    N: int
+    K: int
+    dist: str  # "uniform" or "normal_bf16"
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Compulsory HBM bytes: read A and B once, write C once (C is not read)."""
+        return (self.M * self.K + self.K * self.N) * self.in_bytes + self.M * self.N * 4
+
+    def operands(self):
+        """(A, B) as numpy arrays: float32, or uint16 bf16 bit patterns."""
+        if self.dist == "uniform":
+            return (uniform_f32((self.M, self.K), self.seed),
+                    uniform_f32((self.K, self.N), self.seed + 1000))
+        if self.dist == "normal_bf16":
+            return (normal_bf16_bits((self.M, self.K), self.seed),
+                    normal_bf16_bits((self.K, self.N), self.seed + 1000))
+        raise ValueError(self.dist)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("fp32-256", "f32", 256, 256, 256, "uniform", 101),
+        Workload("fp32-4096", "f32", 4096, 4096, 4096, "uniform", 102),
+        Workload("fp32-1000", "f32", 1000, 1000, 1000, "uniform", 103),
+        Workload("fp32-rag", "f32", 4097, 4095, 4099, "uniform", 104),
+        Workload("bf16-8192", "bf16", 8192, 8192, 8192, "normal_bf16", 105),
+        Workload("im2col", "f32", 64, 16384, 61504, "uniform", 106),
+        Workload("tall", "f32", 65536, 64, 1024, "uniform", 107),
+    ]
+}
+
+
+def _rows_per_chunk(cols: int) -> int:
+    return max(1, _CHUNK_ELEMS // max(cols, 1))
+
+
+def uniform_f32(shape, seed: int) -> np.ndarray:
+    """i.i.d. uniform[-1, 1) float32 values (drawn in float64, then rounded)."""
+    rows, cols = shape
+    rng = np.random.default_rng(seed)
+    out = np.empty((rows, cols), dtype=np.float32)
+    step = _rows_per_chunk(cols)
+    for r in range(0, rows, step):
+        r1 = min(rows, r + step)
+        out[r:r1] = rng.uniform(-1.0, 1.0, size=(r1 - r, cols))
+    return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return the
+    16-bit patterns.  Inputs must be finite (the generators only make finite
+    values)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def normal_bf16_bits(shape, seed: int) -> np.ndarray:
+    """i.i.d. standard normal values, drawn as float32 and rounded to bf16."""
+    rows, cols = shape
+    rng = np.random.default_rng(seed)
+    out = np.empty((rows, cols), dtype=np.uint16)
+    step = _rows_per_chunk(cols)
+    for r in range(0, rows, step):
+        r1 = min(rows, r + step)
+        out[r:r1] = f32_to_bf16_bits(rng.standard_normal(size=(r1 - r, cols), dtype=np.float32))
+    return out
+
+
+def small_int_f32(shape, seed: int, lo: int = -3, hi: int = 3) -> np.ndarray:
+    """Integers in [lo, hi] stored as float32.  Every partial sum of products of
+    such values is an exact integer well below 2^24, so any summation order
+    gives the same bits."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def small_int_bf16_bits(shape, seed: int, lo: int = -3, hi: int = 3) -> np.ndarray:
+    """Integers in [lo, hi] as bf16 bit patterns (exactly representable)."""
+    return f32_to_bf16_bits(small_int_f32(shape, seed, lo, hi))
+
+
+def sample_positions(M: int, N: int, count: int, seed: int):
+    """``count`` (i, j) positions spread over an M x N output: its four corners,
+    the last row and column, and the rest uniform at random."""
+    rng = np.random.default_rng(seed)
+    fixed_i = [0, 0, M - 1, M - 1]
+    fixed_j = [0, N - 1, 0, N - 1]
+    extra = max(0, count - len(fixed_i))
+    I = np.concatenate([np.array(fixed_i), rng.integers(0, M, size=extra)])
+    J = np.concatenate([np.array(fixed_j), rng.integers(0, N, size=extra)])
+    return I.astype(np.int64), J.astype(np.int64)

@@ -1,0 +1,31 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size case that takes more than a few seconds")
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.fixture(scope="session")
+def cuda():
+    """The torch device for GPU tests; fails (not skips) when a gpu-marked test
+    runs without a GPU, so that a silent skip cannot pass for a green run."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("gpu-marked test run without a visible GPU")
+    return torch.device("cuda:0")
