@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the dense GEMM on one MI355X.
+
+One step is one call of the library's GEMM (grid decomposition, global->LDS
+staging, MFMA main loop, edge handling and epilogue, and for the split-K class
+the reduce) on a seeded synthetic workload whose operands are already resident
+in HBM.  Prints ONE JSON line:
+
+  metric / value / unit   GEMM TFLOP/s (2*M*N*K per step over the timed steps)
+  roofline                the GEMM kernel against the MI355X dense matrix peak of
+                          its input type, from HIP events on the stream the
+                          kernel runs on; traffic from the committed rocprofv3
+                          counter summary when it matches the current sources
+  cpu_baseline            the oracle (CPU, fp64) timed on a bounded sample of the
+                          same workload on this host
+  also                    the same measurement for the other headline workload
+                          (bf16 8192^3), and with --all for the im2col and
+                          tall-skinny shapes
+
+Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix peaks
+HBM_PEAK_GBS = 8000.0
+PRIMARY = "fp32-4096"
+SECONDARY = ["bf16-8192"]
+EXTRA = ["im2col", "tall"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """Hash of the HIP sources, so stored counter readings are only used for
+    the kernels they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_03_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from profiles/traffic.json, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("sources") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def measure(name: str, steps: int, warmup: int):
+    """Time `steps` GEMM calls on workload `name`; returns a result dict."""
+    import torch
+
+    import dense_gemm_03_amd as dg
+    from dense_gemm_03_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[name]
+    log("[bench] %s: drawing operands %dx%dx%d (%s)" % (name, w.M, w.N, w.K, w.dtype))
+    A_np, B_np = w.operands()
+    if w.dtype == "f32":
+        A = torch.from_numpy(A_np).to("cuda:0")
+        B = torch.from_numpy(B_np).to("cuda:0")
+    else:
+        A = torch.from_numpy(A_np.view("int16")).view(torch.bfloat16).to("cuda:0")
+        B = torch.from_numpy(B_np.view("int16")).view(torch.bfloat16).to("cuda:0")
+    del A_np, B_np
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    dtype_id = dg.GEMM_DTYPE_F32 if w.dtype == "f32" else dg.GEMM_DTYPE_BF16
+    cfg = dg.gemm_select_config(dtype_id, w.M, w.N, w.K)
+    splits = dg.gemm_split_k(dtype_id, cfg, w.M, w.N, w.K)
+
+    for _ in range(warmup):
+        dg.gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    log("[bench] %s: warmup done (%d), timing %d steps with %s" % (
+        name, warmup, steps, dg.gemm_config_name(dtype_id, cfg)))
+
+    # HIP events on the stream the library launches on (torch's current
+    # stream, passed to the C ABI), bracketing the timed region.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        dg.gemm(A, B, out=C)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    event_ms = ev0.elapsed_time(ev1) / steps
+    ms_per_step = wall * 1e3 / steps
+    tflops = w.flops * steps / wall / 1e12
+    achieved = w.flops / (event_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = stored_traffic(name)
+    res = {
+        "workload": name,
+        "M": w.M, "N": w.N, "K": w.K,
+        "dtype": w.dtype,
+        "value": tflops,
+        "ms_per_step": ms_per_step,
+        "kernel_config": dg.gemm_config_name(dtype_id, cfg),
+        "split_k": splits,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": traffic,
+        },
+        "hbm_gbs": w.algorithmic_bytes / (event_ms * 1e-3) / 1e9,
+    }
+    del A, B, C
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name: str, budget_s: float = 10.0):
+    """The oracle on a bounded row sample of the workload, scaled to TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    from dense_gemm_03_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[name]
+    threads = oracle.default_threads()
+    A, B = w.operands()
+    fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+    rows = min(w.M, max(threads, 16))
+    t = time.perf_counter()
+    fn(np.ascontiguousarray(A[:rows]), B, threads=threads, with_s=False)
+    dt = time.perf_counter() - t
+    # grow the sample to about budget_s seconds of wall time
+    target = int(rows * budget_s / max(dt, 1e-3))
+    rows2 = max(rows, min(w.M, target - target % threads if target > threads else target))
+    if rows2 > rows:
+        t = time.perf_counter()
+        fn(np.ascontiguousarray(A[:rows2]), B, threads=threads, with_s=False)
+        dt = time.perf_counter() - t
+        rows = rows2
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "first %d of %d rows of A times all of B (%dx%dx%d, fp64 accumulation), %.1f s"
+                  % (rows, w.M, rows, w.N, w.K, dt),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--all", action="store_true", help="also time the im2col and tall shapes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this GEMM is built and timed on a single MI355X, "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (none visible)", file=sys.stderr)
+        return 1
+    import dense_gemm_03_amd as dg
+    dg.load_library()
+
+    main_res = measure(args.workload, args.steps, args.warmup)
+    also = {}
+    others = [n for n in SECONDARY + (EXTRA if args.all else []) if n != args.workload]
+    for n in others:
+        also[n] = measure(n, max(5, args.steps // 2), max(2, args.warmup // 2))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] oracle baseline on the host")
+        cpu = cpu_baseline(args.workload)
+
+    w = main_res
+    line = {
+        "metric": "GEMM TFLOP/s and % of MI355X matrix peak (fp32 4096^3, bf16 8192^3)",
+        "value": w["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": w["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded uniform[-1,1] fp32 / normal(0,1) rounded to bf16)",
+        "config": {
+            "workload": "%s GEMM %dx%dx%d" % (w["dtype"], w["M"], w["N"], w["K"]),
+            "name": w["workload"],
+            "kernel_config": w["kernel_config"],
+            "split_k": w["split_k"],
+            "parallelism": "single GPU",
+        },
+        "roofline": w["roofline"],
+        "cpu_baseline": cpu,
+        "also": {n: {k: r[k] for k in ("value", "ms_per_step", "dtype", "kernel_config", "split_k",
+                                        "roofline", "hbm_gbs")} for n, r in also.items()},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,1 +1,151 @@
-"""MI355X-native dense GEMM (placeholder until the binding lands)."""
+"""MI355X-native dense GEMM: C = A . B on gfx950 matrix cores.
+
+A thin ctypes binding over the C ABI of ``include/gemm.h`` (library
+``libdense_gemm.so`` next to this file).  The functions of the same names take
+the same arguments as the C entry points -- sizes, device pointers as
+integers, leading dimensions and a stream handle -- and only marshal them;
+every step of the product runs in the HIP kernels.  ``gemm`` is a convenience
+over torch tensors (torch provides device memory and streams, nothing else).
+
+The library is loaded on first use.  When it is missing this raises; there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdense_gemm.so")
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_ARG = -1
+GEMM_ERR_HIP = -2
+GEMM_ERR_NO_DEVICE = -3
+GEMM_ERR_OUT_OF_MEMORY = -4
+GEMM_DTYPE_F32 = 0
+GEMM_DTYPE_BF16 = 1
+
+# Every symbol include/gemm.h declares, with its ctypes signature.
+_i64, _p, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_GEMM_ARGS = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+SIGNATURES = {
+    "gemm_f32": (_int, _GEMM_ARGS),
+    "gemm_bf16": (_int, _GEMM_ARGS),
+    "gemm_status_string": (ctypes.c_char_p, [_int]),
+    "gemm_num_configs": (_int, [_int]),
+    "gemm_select_config": (_int, [_int, _i64, _i64, _i64]),
+    "gemm_config_name": (ctypes.c_char_p, [_int, _int]),
+    "gemm_split_k": (_int, [_int, _int, _i64, _i64, _i64]),
+    "gemm_f32_with_config": (_int, [_int, _int] + _GEMM_ARGS),
+    "gemm_bf16_with_config": (_int, [_int, _int] + _GEMM_ARGS),
+}
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__("gemm failed: %s (status %d)" % (gemm_status_string(status), status))
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "HIP library %s is missing: build it with `python -m dense_gemm_03_amd.build` "
+            "(there is no CPU fallback)" % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- C names --
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load_library().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load_library().gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_with_config(cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load_library().gemm_f32_with_config(cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_bf16_with_config(cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load_library().gemm_bf16_with_config(cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_status_string(status: int) -> str:
+    return load_library().gemm_status_string(status).decode()
+
+
+def gemm_num_configs(dtype: int) -> int:
+    return load_library().gemm_num_configs(dtype)
+
+
+def gemm_select_config(dtype: int, M: int, N: int, K: int) -> int:
+    return load_library().gemm_select_config(dtype, M, N, K)
+
+
+def gemm_config_name(dtype: int, cfg: int):
+    name = load_library().gemm_config_name(dtype, cfg)
+    return name.decode() if name is not None else None
+
+
+def gemm_split_k(dtype: int, cfg: int, M: int, N: int, K: int) -> int:
+    return load_library().gemm_split_k(dtype, cfg, M, N, K)
+
+
+# ----------------------------------------------------------- torch helper --
+
+def _ld(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor, got shape %s" % (tuple(t.shape),))
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (unit column stride)")
+    rows, cols = t.shape
+    return int(t.stride(0)) if rows > 1 else max(int(cols), 1)
+
+
+def gemm(A, B, out=None, cfg: int | None = None, split_k: int = 0, stream=None):
+    """C = A . B for CUDA (HIP) tensors A (M x K) and B (K x N), both float32
+    or both bfloat16; C is float32.  Row-major operands with unit column
+    stride; row strides become the leading dimensions.  Runs on ``stream``
+    (default: torch's current stream) and returns without synchronising."""
+    import torch
+
+    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("A and B must both be float32 or both bfloat16")
+    if A.device.type != "cuda" or B.device.type != "cuda":
+        raise ValueError("A and B must be GPU tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %s vs %s" % (tuple(A.shape), tuple(B.shape)))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or out.device != A.device:
+        raise ValueError("out must be a float32 (M, N) tensor on A's device")
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(out)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    bf16 = A.dtype == torch.bfloat16
+    args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, stream)
+    if cfg is None:
+        rc = (gemm_bf16 if bf16 else gemm_f32)(*args)
+    else:
+        rc = (gemm_bf16_with_config if bf16 else gemm_f32_with_config)(cfg, split_k, *args)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return out

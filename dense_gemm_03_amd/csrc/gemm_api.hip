@@ -1,0 +1,263 @@
+// C ABI of the dense GEMM library: argument checks, shape-class dispatch over
+// the tile table, split-K workspace, launches.  Declared in include/gemm.h.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "gemm.h"
+#include "gemm_configs.hpp"
+
+namespace dg {
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps all in-kernel int math exact
+constexpr int kComputeUnits = 256;             // MI355X: 8 XCDs x 32 CUs
+constexpr int kTargetBlocks = 4 * kComputeUnits;
+
+const TileConfig *table(int dtype, int *count)
+{
+    if (dtype == GEMM_DTYPE_F32) return f32_configs(count);
+    if (dtype == GEMM_DTYPE_BF16) return bf16_configs(count);
+    *count = 0;
+    return nullptr;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape classes -> table entry (indices into the tables of gemm_f32.hip and
+// gemm_bf16.hip).
+int select_config(int dtype, int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    if (dtype == GEMM_DTYPE_F32) {
+        if (N <= 64 && M >= 4096) return 4;            // tall-skinny: 256x64
+        if (M <= 64 && N >= 1024) return 3;            // few rows, wide N, split-K: 64x256
+        if (M >= 2048 && N >= 2048) return 0;          // large square: 128x128
+        if (N <= 64) return 5;                          // narrow N: 128x64
+        return 2;                                       // small: 64x64
+    }
+    if (M * N >= int64_t(4096) * 4096) return 0;        // large: 256x256
+    if (M * N >= int64_t(1024) * 1024) return 1;        // medium: 128x128
+    return 3;                                           // small: 64x64
+}
+
+// Number of K slices: 1 when the output alone yields enough blocks to fill the
+// chip; otherwise enough slices for about four blocks per compute unit, each
+// slice keeping at least four k-tiles.  forced > 0 overrides the target.
+void plan_split(const TileConfig &c, int64_t M, int64_t N, int64_t K, int forced, int *splits,
+                int *k_per_split)
+{
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const int64_t ktiles = ceil_div(K, c.bk);
+    int64_t s;
+    if (forced > 0) {
+        s = forced;
+    } else if (tiles >= kComputeUnits) {
+        s = 1;
+    } else {
+        s = ceil_div(kTargetBlocks, tiles);
+        const int64_t max_s = ktiles / 4;
+        if (s > max_s) s = max_s;
+    }
+    if (s < 1) s = 1;
+    if (s > ktiles) s = ktiles;
+    const int64_t kps = ceil_div(ktiles, s) * c.bk;  // whole k-tiles per slice
+    *k_per_split = (int)kps;
+    *splits = (int)ceil_div(K, kps);                 // every slice non-empty
+}
+
+// Split-K partial sums live in a library-owned buffer per (device, stream), so
+// that calls on different streams never share one.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+struct WorkspaceReleaser {
+    ~WorkspaceReleaser()
+    {
+        // At unload the runtime may already be gone; freeing is best effort.
+        for (auto &kv : g_ws)
+            if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    }
+} g_ws_releaser;
+
+int get_workspace(int device, hipStream_t stream, size_t bytes, float **out)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(device, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // hipFree waits for the device, so earlier work using it is done.
+            if (hipFree(w.ptr) != hipSuccess) return GEMM_ERR_HIP;
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return GEMM_ERR_OUT_OF_MEMORY;
+        }
+        w.ptr = p;
+        w.bytes = bytes;
+    }
+    *out = static_cast<float *>(w.ptr);
+    return GEMM_OK;
+}
+
+int check_args(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+               const void *B, int64_t ldb, const float *C, int64_t ldc)
+{
+    const size_t esz = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_INVALID_ARG;
+    if (lda < (K > 0 ? K : 1) || ldb < (N > 0 ? N : 1) || ldc < (N > 0 ? N : 1))
+        return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && C == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_ARG;
+    if ((uintptr_t)A % esz || (uintptr_t)B % esz || (uintptr_t)C % 4) return GEMM_ERR_INVALID_ARG;
+    return GEMM_OK;
+}
+
+int run(int dtype, int forced_cfg, int forced_split, int64_t M, int64_t N, int64_t K,
+        const void *A, int64_t lda, const void *B, int64_t ldb, float *C, int64_t ldc,
+        hipStream_t stream)
+{
+    int rc = check_args(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+    if (rc != GEMM_OK) return rc;
+    int count = 0;
+    const TileConfig *tab = table(dtype, &count);
+    if (tab == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (forced_cfg >= count) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return GEMM_OK;
+
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_NO_DEVICE;
+    }
+    if (K == 0) return launch_zero_fill((int)M, (int)N, C, ldc, stream) == hipSuccess ? GEMM_OK
+                                                                                      : GEMM_ERR_HIP;
+
+    const int ci = forced_cfg >= 0 ? forced_cfg : select_config(dtype, M, N, K);
+    const TileConfig &cfg = tab[ci];
+    int splits = 1, kps = 0;
+    plan_split(cfg, M, N, K, forced_split, &splits, &kps);
+
+    KernelArgs a{};
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.ws = nullptr;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.tiles_m = (int)ceil_div(M, cfg.bm);
+    a.tiles_n = (int)ceil_div(N, cfg.bn);
+    a.splits = splits;
+    a.k_per_split = kps;
+    a.group_m = cfg.group_m;
+    if (splits > 1) {
+        rc = get_workspace(device, stream, (size_t)splits * (size_t)M * (size_t)N * sizeof(float),
+                           &a.ws);
+        if (rc != GEMM_OK) return rc;
+    }
+
+    const int vec = dtype == GEMM_DTYPE_F32 ? 4 : 8;
+    const bool aligned = lda % vec == 0 && ldb % vec == 0 && (uintptr_t)A % 16 == 0 &&
+                         (uintptr_t)B % 16 == 0;
+    const int64_t blocks = (int64_t)splits * a.tiles_m * a.tiles_n;
+    if (blocks > INT32_MAX) return GEMM_ERR_INVALID_ARG;
+    launch_fn fn = aligned ? cfg.aligned : cfg.unaligned;
+    if (fn(a, (int)blocks, stream) != hipSuccess) return GEMM_ERR_HIP;
+    if (splits > 1 &&
+        launch_splitk_reduce(a.ws, splits, (int)M, (int)N, C, ldc, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    return GEMM_OK;
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+             int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
+{
+    return dg::run(GEMM_DTYPE_F32, -1, 0, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
+              int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
+{
+    return dg::run(GEMM_DTYPE_BF16, -1, 0, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K, const float *A,
+                         int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+                         hipStream_t stream)
+{
+    if (cfg < 0) return GEMM_ERR_INVALID_ARG;
+    return dg::run(GEMM_DTYPE_F32, cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_bf16_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                          float *C, int64_t ldc, hipStream_t stream)
+{
+    if (cfg < 0) return GEMM_ERR_INVALID_ARG;
+    return dg::run(GEMM_DTYPE_BF16, cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+const char *gemm_status_string(int status)
+{
+    switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_NO_DEVICE: return "no HIP device";
+    case GEMM_ERR_OUT_OF_MEMORY: return "out of device memory";
+    default: return "unknown status";
+    }
+}
+
+int gemm_num_configs(int dtype)
+{
+    int count = 0;
+    return dg::table(dtype, &count) ? count : GEMM_ERR_INVALID_ARG;
+}
+
+int gemm_select_config(int dtype, int64_t M, int64_t N, int64_t K)
+{
+    int count = 0;
+    if (!dg::table(dtype, &count) || M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    return dg::select_config(dtype, M, N, K);
+}
+
+const char *gemm_config_name(int dtype, int cfg)
+{
+    int count = 0;
+    const dg::TileConfig *tab = dg::table(dtype, &count);
+    if (!tab || cfg < 0 || cfg >= count) return nullptr;
+    return tab[cfg].name;
+}
+
+int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K)
+{
+    int count = 0;
+    const dg::TileConfig *tab = dg::table(dtype, &count);
+    if (!tab || cfg < 0 || cfg >= count || M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || K == 0) return 1;
+    int splits = 1, kps = 0;
+    dg::plan_split(tab[cfg], M, N, K, 0, &splits, &kps);
+    return splits;
+}
+
+}  // extern "C"

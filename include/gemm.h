@@ -1,0 +1,136 @@
+/*
+ * Dense GEMM for AMD Instinct MI355X (gfx950): C = A . B on one GPU.
+ *
+ * The operation ("Learning to develop for GPUs through the GEMM operation",
+ * section "Matrix product"): A is M x K, B is K x N, C is M x N, and each
+ * element of C is the dot product of a row of A with a column of B,
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j].
+ *
+ * The generalised form of that page's next section scales the product and
+ * adds a scaled accumulator; this library computes the plain product: C is
+ * overwritten (alpha = 1, beta = 0) and never read.
+ *
+ * Layout: every matrix is row-major with a leading dimension, counted in
+ * elements, between the starts of consecutive rows:
+ *     A[i][k] = A[i*lda + k],  lda >= K
+ *     B[k][j] = B[k*ldb + j],  ldb >= N
+ *     C[i][j] = C[i*ldc + j],  ldc >= N
+ * A column-major caller computes C^T = B^T . A^T with the same call by
+ * swapping the operands.  Elements of C outside the M x N window (the ldc
+ * padding) are never written.
+ *
+ * Precision: gemm_f32 multiplies and accumulates in fp32 (true fp32 matrix-core
+ * products, no reduced-precision emulation).  gemm_bf16 takes bf16 inputs as
+ * raw 16-bit patterns (the upper half of an IEEE binary32), multiplies them
+ * exactly and accumulates in fp32; C is fp32.  The order of the k sum is not
+ * specified, but a given call on a given device is bitwise reproducible (no
+ * atomics are used).
+ *
+ * Memory and ownership: A, B and C are device pointers owned by the caller
+ * (for example tensors allocated by PyTorch).  C must not overlap A or B.  The
+ * library never frees caller memory.  It owns one split-K workspace per
+ * device, allocated on first need, grown when a larger one is needed and
+ * released when the library is unloaded; growing it synchronises the device.
+ *
+ * Streams: all work is enqueued on `stream` (NULL is the default stream) and
+ * the calls return without waiting for it.  A fault inside a kernel surfaces
+ * at the caller's next synchronisation on that stream.
+ *
+ * Errors: every entry point returns a gemm_status and never throws.
+ *   - M, N or K negative; a leading dimension smaller than its row
+ *     (lda < max(K,1), ldb < max(N,1), ldc < max(N,1)); a null pointer for a
+ *     non-empty operand; a pointer not aligned to its element size:
+ *     GEMM_ERR_INVALID_ARG, and nothing is launched.
+ *   - M == 0 or N == 0: GEMM_OK, nothing is launched.
+ *   - K == 0: C is filled with zeros (the empty sum), GEMM_OK.
+ *   - a HIP error while launching or allocating: GEMM_ERR_HIP or
+ *     GEMM_ERR_OUT_OF_MEMORY.
+ * Argument checks happen before any HIP call, so an invalid call does not
+ * touch the GPU.
+ *
+ * Threads: the entry points may be called from several host threads; the
+ * tile table is read-only and the workspace is guarded by a mutex.
+ */
+#ifndef DENSE_GEMM_03_AMD_GEMM_H
+#define DENSE_GEMM_03_AMD_GEMM_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = -1,
+    GEMM_ERR_HIP = -2,
+    GEMM_ERR_NO_DEVICE = -3,
+    GEMM_ERR_OUT_OF_MEMORY = -4
+} gemm_status;
+
+typedef enum { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1 } gemm_dtype;
+
+/* C := A . B for fp32 A (M x K), B (K x N) and C (M x N), row-major. */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             hipStream_t stream);
+
+/* C := A . B for bf16 A and B (uint16 bit patterns) and fp32 C, row-major,
+ * fp32 accumulation. */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const uint16_t *A, int64_t lda,
+              const uint16_t *B, int64_t ldb,
+              float *C, int64_t ldc,
+              hipStream_t stream);
+
+/* A static, human-readable description of a gemm_status value. */
+const char *gemm_status_string(int status);
+
+/*
+ * Tile-table hooks, for tests and tuning.  The dispatcher of gemm_f32 and
+ * gemm_bf16 picks one entry of a per-dtype table of tile configurations by the
+ * shape class of (M, N, K) -- how tile sizes must be chosen per task and
+ * device is the point of "How to do even better" on the GEMM page.
+ *
+ * gemm_num_configs: number of table entries for a dtype (negative on a bad
+ *   dtype).
+ * gemm_select_config: the entry the dispatcher would use for this shape
+ *   (pure host logic, no GPU access); negative on bad arguments.
+ * gemm_config_name: a static string naming an entry ("f32_128x128x32_w2x2"...),
+ *   NULL when out of range.
+ * gemm_split_k: the number of K slices the dispatcher would use with entry cfg
+ *   for this shape (1 = no split); negative on bad arguments.
+ * gemm_f32_with_config / gemm_bf16_with_config: as gemm_f32 / gemm_bf16 but
+ *   with the table entry forced; split_k <= 0 lets the dispatcher choose the
+ *   number of K slices, a positive value forces it (clamped so that every
+ *   slice holds at least one k-tile).
+ */
+int gemm_num_configs(int dtype);
+int gemm_select_config(int dtype, int64_t M, int64_t N, int64_t K);
+const char *gemm_config_name(int dtype, int cfg);
+int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K);
+
+int gemm_f32_with_config(int cfg, int split_k,
+                         int64_t M, int64_t N, int64_t K,
+                         const float *A, int64_t lda,
+                         const float *B, int64_t ldb,
+                         float *C, int64_t ldc,
+                         hipStream_t stream);
+
+int gemm_bf16_with_config(int cfg, int split_k,
+                          int64_t M, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda,
+                          const uint16_t *B, int64_t ldb,
+                          float *C, int64_t ldc,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_03_AMD_GEMM_H */
