@@ -59,6 +59,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             "HIP library %s is missing: build it with `python -m dense_gemm_03_amd.build` "
             "(there is no CPU fallback)" % path)
+    # One HIP runtime per process: torch ships its own libamdhip64 (same
+    # soname), and device pointers and streams from torch are only valid in
+    # that runtime.  Importing torch first makes the library bind to it instead
+    # of loading a second runtime next to it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - C callers without torch
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
