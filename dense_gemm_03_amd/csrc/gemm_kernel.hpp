@@ -73,6 +73,10 @@ struct Op<true> {                // bf16 inputs (raw 16-bit patterns)
 };
 
 // Tile geometry and LDS layout for one configuration.
+//
+// LDS banks (measured on gfx950 with the bank-conflict counter): 64 banks of
+// 4 bytes, and a 16-byte read serves 16 lanes per pass, so the 16 addresses of
+// a pass must cover 256 bytes that fall on distinct banks.
 template <bool BF16, int BM_, int BN_, int WM_, int WN_>
 struct Geo {
     using O = Op<BF16>;
@@ -87,31 +91,59 @@ struct Geo {
     static constexpr int KS = KH / STEPS;             // k values per lane and step (4 or 8)
     static_assert(KS * (int)sizeof(In) == 16, "one step is one 16-byte read per lane");
 
-    // A tile: BM rows of BK elements = 8 chunks of 16 bytes, padded to 144 bytes
-    // so that 16 consecutive rows read at the same column land on distinct banks.
-    static constexpr int A_ROW_BYTES = BK * (int)sizeof(In) + 16;
+    // A tile: BM rows of BK elements (8 chunks of 16 bytes).
+    //   fp32: rows padded to 144 bytes -- 16 rows read at one column start 36
+    //         banks apart, covering all 64 banks once.
+    //   bf16: rows of 128 bytes, chunk c of row r stored in slot c ^ ((r>>1)&7);
+    //         the two rows sharing a 256-byte bank line use the two halves and
+    //         the 8 row pairs of a pass see 8 different slots.
+    static constexpr int A_ROW_BYTES = BF16 ? 128 : 144;
     static constexpr int A_BYTES = BM * A_ROW_BYTES;
     static constexpr int A_CHUNKS = BM * 8;
     static_assert(A_CHUNKS % NT == 0, "A chunks must divide evenly over the threads");
     static constexpr int A_PER_THREAD = A_CHUNKS / NT;
 
-    // B tile, fp32: BK rows of BN floats, row-major; the 32-float halves of a
-    // row swap places in rows 16..31 so the two lane halves of a fragment read
-    // (rows k and k+16, same columns) hit different banks.
-    // B tile, bf16: stored transposed, BN rows of BK k-values (same padded
-    // layout as A), filled from 8x8 blocks transposed in registers.
-    static constexpr int B_ROW_BYTES = BF16 ? A_ROW_BYTES : BN * 4;
-    static constexpr int B_BYTES = BF16 ? BN * A_ROW_BYTES : BK * BN * 4;
-    static constexpr int B_UNITS = BF16 ? (BK / 8) * (BN / 8) : BK * BN / 4;  // 8x8 blocks or chunks
-    static constexpr int B_PER_THREAD = (B_UNITS + NT - 1) / NT;
-    static_assert(B_UNITS % 64 == 0, "B units must fill whole waves");
+    // B tile: BK rows of BN elements, row-major as in memory.
+    //   fp32: the two 32-float halves of each 64-float group swap places in
+    //         rows 16..31, so the two lane halves of a fragment read (rows k
+    //         and k+16, same columns) use different banks.
+    //   bf16: read with the LDS transpose load, 4 rows x 16 columns per
+    //         16 lanes; the 64-byte segments of row k are XOR-permuted by
+    //         (k & 3) so those 4 rows land on 4 different bank quarters.
+    static constexpr int B_ROW_BYTES = BN * (int)sizeof(In);
+    static constexpr int B_BYTES = BK * B_ROW_BYTES;
+    static constexpr int B_CHUNKS = BK * BN / VEC;
+    static_assert(B_CHUNKS % NT == 0, "B chunks must divide evenly over the threads");
+    static constexpr int B_PER_THREAD = B_CHUNKS / NT;
+    static constexpr int B_SEGMASK = (BN / 32 >= 4) ? 3 : (BN / 32 - 1);
     static_assert(BF16 || BN % 64 == 0, "fp32 B swizzle needs BN a multiple of 64");
-    static_assert(BF16 || B_UNITS % NT == 0, "fp32 B chunks must divide evenly over the threads");
+    static_assert(!BF16 || BN % 32 == 0, "bf16 B segments are 32 columns wide");
 
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int SMEM_BYTES = 2 * STAGE_BYTES;
     static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave sub-block must be whole fragments");
+
+    // Byte offset of 16-byte chunk `chunk` (0..7) of A row `row` in a stage.
+    static __device__ __forceinline__ int a_off(int row, int chunk)
+    {
+        if constexpr (BF16)
+            return row * A_ROW_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
+        else
+            return row * A_ROW_BYTES + (chunk << 4);
+    }
+
+    // Byte offset of element (k, n) of the B tile in a stage (n a multiple of
+    // 4, so an 8- or 16-byte access stays inside one swizzle unit).
+    static __device__ __forceinline__ int b_off(int k, int n)
+    {
+        if constexpr (BF16) {
+            const int seg = (n >> 5) ^ (k & B_SEGMASK);
+            return k * B_ROW_BYTES + (seg << 6) + ((n & 31) << 1);
+        } else {
+            return k * B_ROW_BYTES + ((n ^ (((k >> 4) & 1) << 5)) << 2);
+        }
+    }
 };
 
 // ------------------------------------------------------------ small helpers --
@@ -152,23 +184,6 @@ __device__ __forceinline__ u32x4 load_chunk_masked(const In *row, bool row_ok, i
     return u.v;
 }
 
-// Transpose an 8x8 block of 16-bit values held as 8 rows of 16 bytes:
-// out[c] holds column c, i.e. (in[0][c], in[1][c], ..., in[7][c]).
-__device__ __forceinline__ void transpose8x8_b16(const u32x4 in[8], u32x4 out[8])
-{
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int d = c >> 1;         // dword holding column c in each row
-        const int hi = (c & 1) * 16;  // which half of that dword
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const unsigned lo_row = (in[2 * q][d] >> hi) & 0xFFFFu;
-            const unsigned hi_row = (in[2 * q + 1][d] >> hi) & 0xFFFFu;
-            out[c][q] = lo_row | (hi_row << 16);
-        }
-    }
-}
-
 // Map a linear block id to (slice, tile row, tile column).
 //
 // The hardware hands consecutive workgroups to the 8 XCDs in turn, and each
@@ -194,215 +209,260 @@ __device__ __forceinline__ void block_coords(const KernelArgs &p, int &slice, in
 
 // ------------------------------------------------------------------ kernel --
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// LDS transpose load (gfx950): within each group of 16 lanes, lane s names
+// row s/4, columns 4*(s%4)..+3 of a 4 x 16 block of 16-bit values, and lane i
+// receives column i of that block (its 4 rows).
+__device__ __forceinline__ v4i16 lds_read_tr16(const unsigned char *smem, int off)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)((__attribute__((address_space(3))) unsigned char *)smem + off));
+}
+
+// Per-block state shared by the main-loop helpers.
+template <bool BF16, int BM, int BN, int WM, int WN>
+struct BlockCtx {
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    using In = typename G::In;
+    const In *A;
+    const In *B;
+    int64_t lda, ldb;
+    int M, N;
+    int bm, bn;   // block origin in C
+    int kend;     // end of this block's K range
+    int tid, lane, wrow, wcol;
+};
+
+// The operand tiles of one k-tile, between their global load and LDS store.
+template <bool BF16, int BM, int BN, int WM, int WN>
+struct StageRegs {
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    u32x4 a[G::A_PER_THREAD];
+    u32x4 b[G::B_PER_THREAD];
+};
+
+// Fragments of one step: per 32-row A fragment 16 bytes (4 fp32 or 8 bf16 k
+// values); per 32-column B fragment the same k values of the lane's column.
+template <bool BF16, int BM, int BN, int WM, int WN>
+struct Frags {
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    u32x4 a[G::FM];
+    u32x4 b[G::FN];
+};
+
+// Global -> registers for the k-tile starting at k0.  MASKED: zero outside
+// the matrix (rows >= M, columns >= N, k >= kend); otherwise the whole tile is
+// known to be inside and 16-byte aligned.
+//   A chunk u: row tid/8 + u*NT/8, elements (tid%8)*VEC .. +VEC
+//   B chunk u: c = tid + u*NT; row c/(BN/VEC), elements (c%(BN/VEC))*VEC .. +VEC
+// Consecutive lanes read consecutive 16-byte chunks of a row (coalesced).
+template <bool MASKED, bool ALIGNED, bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void global_load(const BlockCtx<BF16, BM, BN, WM, WN> &c, int k0,
+                                            StageRegs<BF16, BM, BN, WM, WN> &r)
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    using In = typename G::In;
+    constexpr int VEC = G::VEC, NT = G::NT, CPR = BN / VEC;
+    const int ka = k0 + (c.tid & 7) * VEC;
+#pragma unroll
+    for (int u = 0; u < G::A_PER_THREAD; ++u) {
+        const int gi = c.bm + (c.tid >> 3) + u * (NT / 8);
+        const In *row = c.A + (int64_t)gi * c.lda;
+        if constexpr (MASKED)
+            r.a[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gi < c.M, ka, c.kend);
+        else
+            r.a[u] = load16(row + ka);
+    }
+#pragma unroll
+    for (int u = 0; u < G::B_PER_THREAD; ++u) {
+        const int ch = c.tid + u * NT;
+        const int gk = k0 + ch / CPR;
+        const int gn = c.bn + (ch % CPR) * VEC;
+        const In *row = c.B + (int64_t)gk * c.ldb;
+        if constexpr (MASKED)
+            r.b[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gk < c.kend, gn, c.N);
+        else
+            r.b[u] = load16(row + gn);
+    }
+}
+
+template <bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void lds_store(unsigned char *stage, int tid,
+                                          const StageRegs<BF16, BM, BN, WM, WN> &r)
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    constexpr int NT = G::NT, CPR = BN / G::VEC;
+    unsigned char *sb = stage + G::A_BYTES;
+#pragma unroll
+    for (int u = 0; u < G::A_PER_THREAD; ++u)
+        lds_store16(stage, G::a_off((tid >> 3) + u * (NT / 8), tid & 7), r.a[u]);
+#pragma unroll
+    for (int u = 0; u < G::B_PER_THREAD; ++u) {
+        const int ch = tid + u * NT;
+        lds_store16(sb, G::b_off(ch / CPR, (ch % CPR) * G::VEC), r.b[u]);
+    }
+}
+
+// Fragments of step `step` (0..3) of the tile in `stage`.  Lane half h
+// (lanes 32h..32h+31) supplies k = h*BK/2 + step*KS .. +KS of the tile.
+template <bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void load_frags(const unsigned char *stage,
+                                           const BlockCtx<BF16, BM, BN, WM, WN> &c, int step,
+                                           Frags<BF16, BM, BN, WM, WN> &f)
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    const unsigned char *sb = stage + G::A_BYTES;
+    const int half = c.lane >> 5, l32 = c.lane & 31;
+    const int kk = half * G::KH + step * G::KS;
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm) {
+        const int row = c.wrow * G::WTM + fm * 32 + l32;
+        f.a[fm] = lds_load16(stage, G::a_off(row, 4 * half + step));
+    }
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn) {
+        if constexpr (BF16) {
+            // two transpose loads: k = kk..kk+3 and kk+4..kk+7 of column
+            // (fragment column) + lane%32
+            const int p = c.lane & 15, g = (c.lane >> 4) & 1;
+            const int col = c.wcol * G::WTN + fn * 32 + 16 * g + 4 * (p & 3);
+            const int k = kk + (p >> 2);
+            const v4i16 lo = lds_read_tr16(sb, G::b_off(k, col));
+            const v4i16 hi = lds_read_tr16(sb, G::b_off(k + 4, col));
+            f.b[fn] = u32x4{(unsigned)(unsigned short)lo[0] | ((unsigned)(unsigned short)lo[1] << 16),
+                            (unsigned)(unsigned short)lo[2] | ((unsigned)(unsigned short)lo[3] << 16),
+                            (unsigned)(unsigned short)hi[0] | ((unsigned)(unsigned short)hi[1] << 16),
+                            (unsigned)(unsigned short)hi[2] | ((unsigned)(unsigned short)hi[3] << 16)};
+        } else {
+            const int col = c.wcol * G::WTN + fn * 32 + l32;
+#pragma unroll
+            for (int e = 0; e < G::KS; ++e)
+                f.b[fn][e] = __float_as_uint(lds_loadf(sb, G::b_off(kk + e, col)));
+        }
+    }
+}
+
+template <bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void mma(const Frags<BF16, BM, BN, WM, WN> &f,
+                                    floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
+                                                   [Geo<BF16, BM, BN, WM, WN>::FN])
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    if constexpr (BF16) {
+#pragma unroll
+        for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < G::FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, f.a[fm]), __builtin_bit_cast(bf16x8, f.b[fn]),
+                    acc[fm][fn], 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int e = 0; e < G::KS; ++e)
+#pragma unroll
+            for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < G::FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        __uint_as_float(f.a[fm][e]), __uint_as_float(f.b[fn][e]), acc[fm][fn], 0,
+                        0, 0);
+    }
+}
+
+// `ntiles` k-tiles starting at k_first, accumulated into acc.  One barrier
+// per tile: stage t&1 is read while stage (t+1)&1 receives tile t+1; the
+// fragments of step j+1 are read before the products of step j are issued,
+// and the first fragments of tile t+1 right after the barrier, under the last
+// products of tile t.  On entry no wave may still read stage 0.
+template <bool MASKED, bool ALIGNED, bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void main_loop(unsigned char *smem,
+                                          const BlockCtx<BF16, BM, BN, WM, WN> &c, int k_first,
+                                          int ntiles,
+                                          floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
+                                                         [Geo<BF16, BM, BN, WM, WN>::FN])
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    StageRegs<BF16, BM, BN, WM, WN> regs;
+    Frags<BF16, BM, BN, WM, WN> cur, nxt;
+
+    global_load<MASKED, ALIGNED>(c, k_first, regs);
+    lds_store(smem, c.tid, regs);
+    __syncthreads();
+    load_frags(smem, c, 0, cur);
+
+    for (int t = 0; t < ntiles; ++t) {
+        unsigned char *stage = smem + (t & 1) * G::STAGE_BYTES;
+        unsigned char *other = smem + ((t & 1) ^ 1) * G::STAGE_BYTES;
+        const bool more = t + 1 < ntiles;
+        if (more) global_load<MASKED, ALIGNED>(c, k_first + (t + 1) * G::BK, regs);
+#pragma unroll
+        for (int step = 0; step < G::STEPS - 1; ++step) {
+            load_frags(stage, c, step + 1, nxt);
+            mma(cur, acc);
+            cur = nxt;
+        }
+        if (more) lds_store(other, c.tid, regs);
+        __syncthreads();
+        if (more) load_frags(other, c, 0, nxt);
+        mma(cur, acc);
+        cur = nxt;
+    }
+}
+
 template <bool BF16, int BM, int BN, int WM, int WN, bool ALIGNED>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(KernelArgs p)
 {
     using G = Geo<BF16, BM, BN, WM, WN>;
     using In = typename G::In;
-    constexpr int BK = G::BK, VEC = G::VEC, NT = G::NT;
-    constexpr int FM = G::FM, FN = G::FN, KS = G::KS;
+    constexpr int BK = G::BK;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM_BYTES];
 
-    const int tid = (int)threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wrow = wave / WN, wcol = wave % WN;
-    const int half = lane >> 5;   // which k half this lane feeds
-    const int l32 = lane & 31;    // row (A) or column (B) within a fragment
+    BlockCtx<BF16, BM, BN, WM, WN> c;
+    c.tid = (int)threadIdx.x;
+    c.lane = c.tid & 63;
+    const int wave = c.tid >> 6;
+    c.wrow = wave / WN;
+    c.wcol = wave % WN;
 
     int slice, tm, tn;
     block_coords(p, slice, tm, tn);
-    const int bm = tm * BM, bn = tn * BN;
+    c.bm = tm * BM;
+    c.bn = tn * BN;
+    c.A = static_cast<const In *>(p.A);
+    c.B = static_cast<const In *>(p.B);
+    c.lda = p.lda;
+    c.ldb = p.ldb;
+    c.M = p.M;
+    c.N = p.N;
     const int kbeg = slice * p.k_per_split;
-    const int kend = min(p.K, kbeg + p.k_per_split);
-    const int ntiles = (kend - kbeg + BK - 1) / BK;
+    c.kend = min(p.K, kbeg + p.k_per_split);
+    const int ntiles = (c.kend - kbeg + BK - 1) / BK;
 
-    const In *__restrict__ A = static_cast<const In *>(p.A);
-    const In *__restrict__ B = static_cast<const In *>(p.B);
-    const bool edge = !ALIGNED || bm + BM > p.M || bn + BN > p.N;
-
-    // ---- per-thread global offsets (fixed across tiles; k0 is added per tile)
-    // A: chunk u covers row (tid/8 + u*NT/8), columns (tid%8)*VEC .. +VEC
-    int a_row[G::A_PER_THREAD];
-    const int a_col = (tid & 7) * VEC;
+    floatx16 acc[G::FM][G::FN];
 #pragma unroll
-    for (int u = 0; u < G::A_PER_THREAD; ++u) a_row[u] = (tid >> 3) + u * (NT / 8);
-
-    // ---- registers holding the next tile between its global load and LDS store
-    u32x4 ga[G::A_PER_THREAD];
-    u32x4 gb[BF16 ? 8 * G::B_PER_THREAD : G::B_PER_THREAD];
-
-    auto global_load = [&](int k0) {
-        const bool full = !edge && k0 + BK <= kend;
+    for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
-        for (int u = 0; u < G::A_PER_THREAD; ++u) {
-            const int gi = bm + a_row[u];
-            const In *row = A + (int64_t)gi * p.lda;
-            if (full)
-                ga[u] = load16(row + k0 + a_col);
-            else
-                ga[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gi < p.M, k0 + a_col, kend);
-        }
-        if constexpr (BF16) {
-            // 8x8 blocks: block b covers k rows (b%8)*8..+8, n columns (b/8)*8..+8
-#pragma unroll
-            for (int u = 0; u < G::B_PER_THREAD; ++u) {
-                const int b = tid + u * NT;
-                if (G::B_UNITS % NT == 0 || b < G::B_UNITS) {
-                    const int kr = (b & 7) * 8;
-                    const int gn = bn + (b >> 3) * 8;
-#pragma unroll
-                    for (int rr = 0; rr < 8; ++rr) {
-                        const int gk = k0 + kr + rr;
-                        const In *row = B + (int64_t)gk * p.ldb;
-                        if (full)
-                            gb[u * 8 + rr] = load16(row + gn);
-                        else
-                            gb[u * 8 + rr] = load_chunk_masked<In, VEC, ALIGNED>(
-                                row, gk < kend, gn, p.N);
-                    }
-                }
-            }
-        } else {
-            // chunks: chunk c covers k row c/(BN/4), columns (c%(BN/4))*4 .. +4
-#pragma unroll
-            for (int u = 0; u < G::B_PER_THREAD; ++u) {
-                const int c = tid + u * NT;
-                const int kr = c / (BN / 4);
-                const int gn = bn + (c % (BN / 4)) * 4;
-                const int gk = k0 + kr;
-                const In *row = B + (int64_t)gk * p.ldb;
-                if (full)
-                    gb[u] = load16(row + gn);
-                else
-                    gb[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gk < kend, gn, p.N);
-            }
-        }
-    };
-
-    auto lds_store = [&](int stage) {
-        unsigned char *sa = smem + stage * G::STAGE_BYTES;
-        unsigned char *sb = sa + G::A_BYTES;
-#pragma unroll
-        for (int u = 0; u < G::A_PER_THREAD; ++u)
-            lds_store16(sa, a_row[u] * G::A_ROW_BYTES + a_col * (int)sizeof(In), ga[u]);
-        if constexpr (BF16) {
-#pragma unroll
-            for (int u = 0; u < G::B_PER_THREAD; ++u) {
-                const int b = tid + u * NT;
-                if (G::B_UNITS % NT == 0 || b < G::B_UNITS) {
-                    u32x4 t[8];
-                    transpose8x8_b16(&gb[u * 8], t);
-                    const int kr = (b & 7) * 8;
-                    const int n0 = (b >> 3) * 8;
-#pragma unroll
-                    for (int c = 0; c < 8; ++c)
-                        lds_store16(sb, (n0 + c) * G::B_ROW_BYTES + kr * 2, t[c]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < G::B_PER_THREAD; ++u) {
-                const int c = tid + u * NT;
-                const int kr = c / (BN / 4);
-                const int n = ((c % (BN / 4)) * 4) ^ (((kr >> 4) & 1) * 32);
-                lds_store16(sb, kr * G::B_ROW_BYTES + n * 4, gb[u]);
-            }
-        }
-    };
-
-    // ---- fragments of one step: A as 16 bytes per fragment row, B likewise
-    // (bf16) or as KS single floats (fp32).
-    struct Frags {
-        u32x4 a[FM];
-        u32x4 b[FN];   // fp32: the KS floats of one column; bf16: 8 k values
-    };
-
-    auto load_frags = [&](int stage, int step, Frags &f) {
-        const unsigned char *sa = smem + stage * G::STAGE_BYTES;
-        const unsigned char *sb = sa + G::A_BYTES;
-        const int kk = half * G::KH + step * KS;  // first k of this lane's slot range
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int row = wrow * G::WTM + fm * 32 + l32;
-            f.a[fm] = lds_load16(sa, row * G::A_ROW_BYTES + kk * (int)sizeof(In));
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int col = wcol * G::WTN + fn * 32 + l32;
-            if constexpr (BF16) {
-                f.b[fn] = lds_load16(sb, col * G::B_ROW_BYTES + kk * 2);
-            } else {
-                const int n = col ^ (half * 32);  // rows kk.. have bit 4 == half
-#pragma unroll
-                for (int e = 0; e < KS; ++e)
-                    f.b[fn][e] = __float_as_uint(lds_loadf(sb, (kk + e) * G::B_ROW_BYTES + n * 4));
-            }
-        }
-    };
-
-    floatx16 acc[FM][FN];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+        for (int fn = 0; fn < G::FN; ++fn)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-    auto mma = [&](const Frags &f) {
-        if constexpr (BF16) {
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, f.a[fm]), __builtin_bit_cast(bf16x8, f.b[fn]),
-                        acc[fm][fn], 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int e = 0; e < KS; ++e)
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            __uint_as_float(f.a[fm][e]), __uint_as_float(f.b[fn][e]),
-                            acc[fm][fn], 0, 0, 0);
-        }
-    };
-
-    // ---- prologue: tile 0 into stage 0
-    global_load(kbeg);
-    lds_store(0);
-    __syncthreads();
-    Frags cur, nxt;
-    load_frags(0, 0, cur);
-
-    // ---- main loop: one barrier per tile.  Stage s = t&1 is read while the
-    // other stage receives tile t+1; fragments of step j+1 are read before the
-    // products of step j are issued, and the first fragments of tile t+1 are
-    // read right after the barrier, under the last products of tile t.
-    for (int t = 0; t < ntiles; ++t) {
-        const int stage = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) global_load(kbeg + (t + 1) * BK);
-#pragma unroll
-        for (int step = 0; step < G::STEPS - 1; ++step) {
-            load_frags(stage, step + 1, nxt);
-            mma(cur);
-            cur = nxt;
-        }
-        if (more) lds_store(stage ^ 1);
-        __syncthreads();
-        if (more) load_frags(stage ^ 1, 0, nxt);
-        mma(cur);
-        cur = nxt;
+    // Interior blocks run their whole k-tiles without bounds checks; the
+    // partial last k-tile, blocks crossing the M or N edge and unaligned
+    // operands take the masked loads.  The choice is uniform per workgroup.
+    const bool edge = !ALIGNED || c.bm + BM > p.M || c.bn + BN > p.N;
+    const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
+    if (nfast > 0) main_loop<false, ALIGNED>(smem, c, kbeg, nfast, acc);
+    if (ntiles > nfast) {
+        if (nfast > 0) __syncthreads();
+        main_loop<true, ALIGNED>(smem, c, kbeg + nfast * BK, ntiles - nfast, acc);
     }
 
-    // ---- epilogue: accumulator element r of a 32x32 fragment sits at row
-    // 8*(r/4) + 4*half + r%4 and column l32 of that fragment.
+    // Epilogue: accumulator element r of a 32x32 fragment sits at row
+    // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that fragment.
     float *out;
     int64_t ldo;
     if (p.splits > 1) {
@@ -412,15 +472,16 @@ gemm_kernel(KernelArgs p)
         out = p.C;
         ldo = p.ldc;
     }
-    const bool store_edge = bm + BM > p.M || bn + BN > p.N;
+    const int half = c.lane >> 5, l32 = c.lane & 31;
+    const bool store_edge = c.bm + BM > p.M || c.bn + BN > p.N;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
+    for (int fm = 0; fm < G::FM; ++fm) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int gj = bn + wcol * G::WTN + fn * 32 + l32;
+        for (int fn = 0; fn < G::FN; ++fn) {
+            const int gj = c.bn + c.wcol * G::WTN + fn * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int gi = bm + wrow * G::WTM + fm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int gi = c.bm + c.wrow * G::WTM + fm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (!store_edge || (gi < p.M && gj < p.N)) out[(int64_t)gi * ldo + gj] = acc[fm][fn][r];
             }
         }
