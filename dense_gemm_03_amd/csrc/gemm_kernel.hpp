@@ -91,13 +91,11 @@ struct Geo {
     static constexpr int KS = KH / STEPS;             // k values per lane and step (4 or 8)
     static_assert(KS * (int)sizeof(In) == 16, "one step is one 16-byte read per lane");
 
-    // A tile: BM rows of BK elements (8 chunks of 16 bytes).
-    //   fp32: rows padded to 144 bytes -- 16 rows read at one column start 36
-    //         banks apart, covering all 64 banks once.
-    //   bf16: rows of 128 bytes, chunk c of row r stored in slot c ^ ((r>>1)&7);
-    //         the two rows sharing a 256-byte bank line use the two halves and
-    //         the 8 row pairs of a pass see 8 different slots.
-    static constexpr int A_ROW_BYTES = BF16 ? 128 : 144;
+    // A tile: BM rows of BK elements = 128 bytes (8 chunks of 16 bytes), chunk
+    // c of row r stored in slot c ^ ((r>>1)&7): the two rows sharing a 256-byte
+    // bank line use its two halves, and the 8 row pairs of a 16-lane pass see
+    // 8 different slots, so fragment reads and tile writes are conflict-free.
+    static constexpr int A_ROW_BYTES = 128;
     static constexpr int A_BYTES = BM * A_ROW_BYTES;
     static constexpr int A_CHUNKS = BM * 8;
     static_assert(A_CHUNKS % NT == 0, "A chunks must divide evenly over the threads");
@@ -119,6 +117,15 @@ struct Geo {
     static_assert(BF16 || BN % 64 == 0, "fp32 B swizzle needs BN a multiple of 64");
     static_assert(!BF16 || BN % 32 == 0, "bf16 B segments are 32 columns wide");
 
+    // Direct global->LDS loads write 64 lanes x 16 bytes = 1 KiB contiguous
+    // LDS bytes per instruction; the tiles are cut into such pieces.
+    static constexpr int NW = WM * WN;                        // waves
+    static constexpr int A_PIECES = A_BYTES / 1024;           // 8 rows each
+    static constexpr int B_PIECES = B_BYTES / 1024;
+    static constexpr int B_LANES_PER_ROW = B_ROW_BYTES / 16;
+    static_assert(A_PIECES % NW == 0 && B_PIECES % NW == 0, "direct loads must divide over waves");
+    static_assert(1024 % B_ROW_BYTES == 0, "a B row must fit a 1 KiB piece evenly");
+
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int SMEM_BYTES = 2 * STAGE_BYTES;
     static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
@@ -127,10 +134,7 @@ struct Geo {
     // Byte offset of 16-byte chunk `chunk` (0..7) of A row `row` in a stage.
     static __device__ __forceinline__ int a_off(int row, int chunk)
     {
-        if constexpr (BF16)
-            return row * A_ROW_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
-        else
-            return row * A_ROW_BYTES + (chunk << 4);
+        return row * A_ROW_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
     }
 
     // Byte offset of element (k, n) of the B tile in a stage (n a multiple of
@@ -371,13 +375,171 @@ __device__ __forceinline__ void mma(const Frags<BF16, BM, BN, WM, WN> &f,
     }
 }
 
+// One direct global->LDS load: each lane copies 16 bytes from `src`, and the
+// 64 lanes' bytes land contiguously at `lds` + 16 * lane (measured on gfx950).
+__device__ __forceinline__ void direct_load16(const void *src, unsigned char *lds)
+{
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)src,
+        (__attribute__((address_space(3))) void *)((__attribute__((address_space(3)))
+                                                     unsigned char *)lds),
+        16, 0, 0);
+}
+
+// Per-thread byte offsets of the direct loads, relative to the tile origin
+// in A (row bm, column k0) and in B (row k0, column bn).  They do not change
+// from one k-tile to the next, so they are computed once per block and the
+// per-tile address is a uniform base plus a 32-bit offset.
+template <bool BF16, int BM, int BN, int WM, int WN>
+struct DirectOffsets {
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    uint32_t a[G::A_PIECES / G::NW];
+    uint32_t b[G::B_PIECES / G::NW];
+};
+
+// Direct copy of a k-tile into a stage (interior tiles only: every address
+// is inside the matrix and 16-byte aligned).  The LDS side is fixed -- 1 KiB
+// per instruction, lane l at byte 16*l -- so each lane fetches the global
+// chunk that the tile's XOR swizzle places at its LDS position (the
+// swizzles are their own inverses).
+template <bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void direct_offsets(const BlockCtx<BF16, BM, BN, WM, WN> &c,
+                                               DirectOffsets<BF16, BM, BN, WM, WN> &o)
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    using In = typename G::In;
+    constexpr int NW = G::NW, LPR = G::B_LANES_PER_ROW;
+    const int wave = c.tid >> 6;
+#pragma unroll
+    for (int i = 0; i < G::A_PIECES / NW; ++i) {
+        const int j = wave + NW * i;                 // piece: rows 8j .. 8j+7
+        const int r = 8 * j + (c.lane >> 3);
+        const int chunk = (c.lane & 7) ^ ((r >> 1) & 7);
+        o.a[i] = (uint32_t)(((int64_t)r * c.lda + chunk * G::VEC) * (int64_t)sizeof(In));
+    }
+#pragma unroll
+    for (int i = 0; i < G::B_PIECES / NW; ++i) {
+        const int j = wave + NW * i;                 // piece: rows j*(64/LPR) ..
+        const int k = j * (64 / LPR) + c.lane / LPR;
+        const int phys = (c.lane % LPR) * G::VEC;    // element position in the LDS row
+        int n;
+        if constexpr (BF16)
+            n = ((((phys >> 5) ^ (k & G::B_SEGMASK))) << 5) | (phys & 31);
+        else
+            n = phys ^ (((k >> 4) & 1) << 5);
+        o.b[i] = (uint32_t)(((int64_t)k * c.ldb + n) * (int64_t)sizeof(In));
+    }
+}
+
+template <bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void direct_tile_load(unsigned char *stage,
+                                                 const BlockCtx<BF16, BM, BN, WM, WN> &c,
+                                                 const DirectOffsets<BF16, BM, BN, WM, WN> &o,
+                                                 int k0)
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    constexpr int NW = G::NW;
+    const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+    const unsigned char *a_base =
+        reinterpret_cast<const unsigned char *>(c.A + ((int64_t)c.bm * c.lda + k0));
+    const unsigned char *b_base =
+        reinterpret_cast<const unsigned char *>(c.B + ((int64_t)k0 * c.ldb + c.bn));
+#pragma unroll
+    for (int i = 0; i < G::A_PIECES / NW; ++i)
+        direct_load16(a_base + o.a[i], stage + 1024 * (wave + NW * i));
+#pragma unroll
+    for (int i = 0; i < G::B_PIECES / NW; ++i)
+        direct_load16(b_base + o.b[i], stage + G::A_BYTES + 1024 * (wave + NW * i));
+}
+
+// Instruction interleave for one step: each MFMA is followed by up to one
+// direct global->LDS load and one LDS fragment read, so the loads and reads
+// issue while the matrix core is busy instead of in a burst after it.
+template <int N_MMA, int N_DS, int N_VMEM>
+__device__ __forceinline__ void interleave_step()
+{
+#pragma unroll
+    for (int i = 0; i < N_MMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+        if (i < N_VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        if (i < N_DS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+    }
+    if (N_DS > N_MMA) __builtin_amdgcn_sched_group_barrier(0x100, N_DS - N_MMA, 0);
+    if (N_VMEM > N_MMA) __builtin_amdgcn_sched_group_barrier(0x020, N_VMEM - N_MMA, 0);
+}
+
+// One interior k-tile in the direct-load pipeline: multiply the tile held in
+// `stage` while the tile at k_next streams into `other`; the barrier that
+// ends the tile also waits for those loads.  (After the last tile the caller
+// passes an in-bounds k_next again, so the code has no branch; `other` is
+// not read after that.)  The two stages are distinct __shared__ arrays,
+// passed as restrict pointers: the alias scopes this gives the LDS reads and
+// the direct loads let the compiler see that reading one stage need not wait
+// for the loads into the other.
+template <bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void direct_tile(unsigned char *__restrict__ stage,
+                                            unsigned char *__restrict__ other,
+                                            const BlockCtx<BF16, BM, BN, WM, WN> &c,
+                                            const DirectOffsets<BF16, BM, BN, WM, WN> &o,
+                                            int k_next, Frags<BF16, BM, BN, WM, WN> &cur,
+                                            floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
+                                                           [Geo<BF16, BM, BN, WM, WN>::FN])
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    constexpr int N_MMA = BF16 ? G::FM * G::FN : G::KS * G::FM * G::FN;
+    constexpr int N_DS = G::FM + (BF16 ? 2 * G::FN : G::KS * G::FN);
+    constexpr int N_VMEM = (G::A_PIECES + G::B_PIECES) / G::NW;
+    Frags<BF16, BM, BN, WM, WN> nxt;
+    direct_tile_load(other, c, o, k_next);
+    load_frags(stage, c, 1, nxt);
+    mma(cur, acc);
+    interleave_step<N_MMA, N_DS, N_VMEM>();
+    cur = nxt;
+#pragma unroll
+    for (int step = 1; step < G::STEPS - 1; ++step) {
+        load_frags(stage, c, step + 1, nxt);
+        mma(cur, acc);
+        interleave_step<N_MMA, N_DS, 0>();
+        cur = nxt;
+    }
+    __syncthreads();
+    load_frags(other, c, 0, nxt);
+    mma(cur, acc);
+    interleave_step<N_MMA, N_DS, 0>();
+    cur = nxt;
+}
+
+// Interior k-tiles with direct loads, two tiles per iteration so that each
+// stage is always the same array.  On entry no wave may still read stage 0.
+template <bool BF16, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void main_loop_direct(unsigned char *smem0, unsigned char *smem1,
+                                                 const BlockCtx<BF16, BM, BN, WM, WN> &c,
+                                                 int k_first, int ntiles,
+                                                 floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
+                                                                [Geo<BF16, BM, BN, WM, WN>::FN])
+{
+    using G = Geo<BF16, BM, BN, WM, WN>;
+    Frags<BF16, BM, BN, WM, WN> cur;
+    DirectOffsets<BF16, BM, BN, WM, WN> o;
+    direct_offsets(c, o);
+    direct_tile_load(smem0, c, o, k_first);
+    __syncthreads();
+    load_frags(smem0, c, 0, cur);
+    const int k_last = k_first + (ntiles - 1) * G::BK;
+    for (int t = 0; t < ntiles; t += 2) {
+        const int k1 = min(k_first + (t + 1) * G::BK, k_last);
+        direct_tile(smem0, smem1, c, o, k1, cur, acc);
+        if (t + 1 < ntiles) direct_tile(smem1, smem0, c, o, min(k1 + G::BK, k_last), cur, acc);
+    }
+}
+
 // `ntiles` k-tiles starting at k_first, accumulated into acc.  One barrier
 // per tile: stage t&1 is read while stage (t+1)&1 receives tile t+1; the
 // fragments of step j+1 are read before the products of step j are issued,
 // and the first fragments of tile t+1 right after the barrier, under the last
 // products of tile t.  On entry no wave may still read stage 0.
 template <bool MASKED, bool ALIGNED, bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void main_loop(unsigned char *smem,
+__device__ __forceinline__ void main_loop(unsigned char *smem0, unsigned char *smem1,
                                           const BlockCtx<BF16, BM, BN, WM, WN> &c, int k_first,
                                           int ntiles,
                                           floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
@@ -388,13 +550,13 @@ __device__ __forceinline__ void main_loop(unsigned char *smem,
     Frags<BF16, BM, BN, WM, WN> cur, nxt;
 
     global_load<MASKED, ALIGNED>(c, k_first, regs);
-    lds_store(smem, c.tid, regs);
+    lds_store(smem0, c.tid, regs);
     __syncthreads();
-    load_frags(smem, c, 0, cur);
+    load_frags(smem0, c, 0, cur);
 
     for (int t = 0; t < ntiles; ++t) {
-        unsigned char *stage = smem + (t & 1) * G::STAGE_BYTES;
-        unsigned char *other = smem + ((t & 1) ^ 1) * G::STAGE_BYTES;
+        unsigned char *stage = (t & 1) ? smem1 : smem0;
+        unsigned char *other = (t & 1) ? smem0 : smem1;
         const bool more = t + 1 < ntiles;
         if (more) global_load<MASKED, ALIGNED>(c, k_first + (t + 1) * G::BK, regs);
 #pragma unroll
@@ -419,7 +581,8 @@ gemm_kernel(KernelArgs p)
     using In = typename G::In;
     constexpr int BK = G::BK;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem0[G::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem1[G::STAGE_BYTES];
 
     BlockCtx<BF16, BM, BN, WM, WN> c;
     c.tid = (int)threadIdx.x;
@@ -455,10 +618,10 @@ gemm_kernel(KernelArgs p)
     // operands take the masked loads.  The choice is uniform per workgroup.
     const bool edge = !ALIGNED || c.bm + BM > p.M || c.bn + BN > p.N;
     const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
-    if (nfast > 0) main_loop<false, ALIGNED>(smem, c, kbeg, nfast, acc);
+    if (nfast > 0) main_loop_direct(smem0, smem1, c, kbeg, nfast, acc);
     if (ntiles > nfast) {
         if (nfast > 0) __syncthreads();
-        main_loop<true, ALIGNED>(smem, c, kbeg + nfast * BK, ntiles - nfast, acc);
+        main_loop<true, ALIGNED>(smem0, smem1, c, kbeg + nfast * BK, ntiles - nfast, acc);
     }
 
     // Epilogue: accumulator element r of a 32x32 fragment sits at row
