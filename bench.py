@@ -179,6 +179,9 @@ def main() -> int:
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--all", action="store_true", help="also time the im2col and tall shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (reference kernel "
+                         "for the HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -190,6 +193,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (none visible)", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        return 0
+
     import dense_gemm_03_amd as dg
     dg.load_library()
 

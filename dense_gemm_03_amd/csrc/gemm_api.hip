@@ -2,6 +2,7 @@
 // the tile table, split-K workspace, launches.  Declared in include/gemm.h.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -14,7 +15,7 @@ namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps all in-kernel int math exact
 constexpr int kComputeUnits = 256;             // MI355X: 8 XCDs x 32 CUs
-constexpr int kTargetBlocks = 4 * kComputeUnits;
+constexpr int kTargetBlocks = 2 * kComputeUnits;
 
 const TileConfig *table(int dtype, int *count)
 {
@@ -26,25 +27,88 @@ const TileConfig *table(int dtype, int *count)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shape classes -> table entry (indices into the tables of gemm_f32.hip and
-// gemm_bf16.hip).
+// Index of the table entry called `name` (the tables are fixed, so each
+// lookup result is cached by the caller).
+int config_index(int dtype, const char *name)
+{
+    int count = 0;
+    const TileConfig *tab = table(dtype, &count);
+    for (int i = 0; i < count; ++i)
+        if (std::strcmp(tab[i].name, name) == 0) return i;
+    return 0;
+}
+
+// Fraction of the GPU's block slots a grid of `tiles` blocks keeps busy over
+// its rounds: tiles / (rounds * slots), slots = compute units x resident
+// blocks per unit.
+double fill(int64_t tiles, int64_t slots)
+{
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    return (double)tiles / (double)(rounds * slots);
+}
+
+struct Candidate {
+    const char *name;
+    int per_cu;        // resident blocks per compute unit (LDS-limited)
+    double measured;   // fraction of the dtype's matrix peak on a full-chip run
+};
+
+// Among `cands`, the entry with the best measured efficiency times the fill
+// of its grid for this M x N.
+int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N)
+{
+    int count = 0;
+    const TileConfig *tab = table(dtype, &count);
+    int best = -1;
+    double best_score = -1.0;
+    for (int i = 0; i < n; ++i) {
+        const int idx = config_index(dtype, cands[i].name);
+        const int64_t tiles = ceil_div(M, tab[idx].bm) * ceil_div(N, tab[idx].bn);
+        const double score = cands[i].measured * fill(tiles, (int64_t)kComputeUnits * cands[i].per_cu);
+        if (score > best_score) {
+            best_score = score;
+            best = idx;
+        }
+    }
+    return best;
+}
+
+// Shape classes -> table entry.  The "measured" factors are the fractions of
+// peak each tile shape reached on 4096^3 fp32 / 8192^3 bf16 (full grids), so
+// the choice trades per-block efficiency against quantisation of the grid
+// over 256 compute units.
 int select_config(int dtype, int64_t M, int64_t N, int64_t K)
 {
     (void)K;
     if (dtype == GEMM_DTYPE_F32) {
-        if (N <= 64 && M >= 4096) return 4;            // tall-skinny: 256x64
-        if (M <= 64 && N >= 1024) return 3;            // few rows, wide N, split-K: 64x256
-        if (M >= 2048 && N >= 2048) return 0;          // large square: 128x128
-        if (N <= 64) return 5;                          // narrow N: 128x64
-        return 2;                                       // small: 64x64
+        static const int tall = config_index(dtype, "f32_64x64_w2x2_s2");
+        static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
+        static const int narrow = config_index(dtype, "f32_128x64_w2x1_s2");
+        static const int small = config_index(dtype, "f32_64x64_w2x2_s2");
+        static const Candidate large[] = {
+            {"f32_256x256_w4x2_s2", 1, 0.93},
+            {"f32_256x128_w4x2_s2", 1, 0.85},
+            {"f32_64x64_w2x2_s3", 3, 0.89},
+        };
+        if (N <= 64 && M >= 4096) return tall;   // tall-skinny: many 64-row blocks
+        if (M <= 64 && N >= 1024) return wide;   // few rows, wide N, split-K
+        if (M >= 2048 && N >= 2048) return best_of(dtype, large, 3, M, N);
+        if (N <= 64) return narrow;
+        return small;
     }
-    if (M * N >= int64_t(4096) * 4096) return 0;        // large: 256x256
-    if (M * N >= int64_t(1024) * 1024) return 1;        // medium: 128x128
-    return 3;                                           // small: 64x64
+    static const Candidate large[] = {
+        {"bf16_256x256x32_w4x2_s4", 1, 0.52},
+        {"bf16_128x128x64_w2x2_s2", 2, 0.42},
+    };
+    static const int medium = config_index(dtype, "bf16_128x128x64_w2x2_s2");
+    static const int small = config_index(dtype, "bf16_64x64x64_w2x2_s2");
+    if (M >= 2048 && N >= 2048) return best_of(dtype, large, 2, M, N);
+    if (M * N >= int64_t(1024) * 1024) return medium;
+    return small;
 }
 
 // Number of K slices: 1 when the output alone yields enough blocks to fill the
-// chip; otherwise enough slices for about four blocks per compute unit, each
+// chip; otherwise enough slices for about two blocks per compute unit, each
 // slice keeping at least four k-tiles.  forced > 0 overrides the target.
 void plan_split(const TileConfig &c, int64_t M, int64_t N, int64_t K, int forced, int *splits,
                 int *k_per_split)
@@ -173,6 +237,11 @@ int run(int dtype, int forced_cfg, int forced_split, int64_t M, int64_t N, int64
     const int vec = dtype == GEMM_DTYPE_F32 ? 4 : 8;
     const bool aligned = lda % vec == 0 && ldb % vec == 0 && (uintptr_t)A % 16 == 0 &&
                          (uintptr_t)B % 16 == 0;
+    // The direct-load path addresses a tile with per-thread 32-bit byte
+    // offsets from the tile origin: rows 0..BM-1 of A and 0..BK-1 of B.
+    const int64_t esz = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    a.direct_ok = ((int64_t)cfg.bm * lda * esz < (int64_t(1) << 32)) &&
+                  ((int64_t)cfg.bk * ldb * esz < (int64_t(1) << 32));
     const int64_t blocks = (int64_t)splits * a.tiles_m * a.tiles_n;
     if (blocks > INT32_MAX) return GEMM_ERR_INVALID_ARG;
     launch_fn fn = aligned ? cfg.aligned : cfg.unaligned;

@@ -7,10 +7,17 @@ namespace dg {
 const TileConfig *bf16_configs(int *count)
 {
     static const TileConfig table[] = {
-        DG_TILE_CONFIG("bf16_256x256_w2x2", true, 256, 256, 2, 2, 8),
-        DG_TILE_CONFIG("bf16_128x128_w2x2", true, 128, 128, 2, 2, 8),
-        DG_TILE_CONFIG("bf16_256x128_w2x2", true, 256, 128, 2, 2, 8),
-        DG_TILE_CONFIG("bf16_64x64_w2x2", true, 64, 64, 2, 2, 8),
+        //              name                             bf16  BM   BN  BK WM WN  S   G
+        DG_TILE_CONFIG("bf16_256x256x64_w2x2_s2", true, 256, 256, 64, 2, 2, 2, 8),
+        DG_TILE_CONFIG("bf16_256x256x32_w2x2_s4", true, 256, 256, 32, 2, 2, 4, 8),
+        DG_TILE_CONFIG("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8),
+        DG_TILE_CONFIG("bf16_256x256x64_w2x4_s2", true, 256, 256, 64, 2, 4, 2, 8),
+        DG_TILE_CONFIG("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 8),
+        DG_TILE_CONFIG("bf16_256x256x64_w2x2_s2_g4", true, 256, 256, 64, 2, 2, 2, 4),
+        DG_TILE_CONFIG("bf16_256x256x64_w2x2_s2_g16", true, 256, 256, 64, 2, 2, 2, 16),
+        DG_TILE_CONFIG("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8),
+        DG_TILE_CONFIG("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8),
+        DG_TILE_CONFIG("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -13,12 +13,17 @@ namespace dg {
 const TileConfig *f32_configs(int *count)
 {
     static const TileConfig table[] = {
-        DG_TILE_CONFIG("f32_128x128_w2x2", false, 128, 128, 2, 2, 8),
-        DG_TILE_CONFIG("f32_256x128_w4x2", false, 256, 128, 4, 2, 8),
-        DG_TILE_CONFIG("f32_64x64_w2x2", false, 64, 64, 2, 2, 8),
-        DG_TILE_CONFIG("f32_64x256_w1x4", false, 64, 256, 1, 4, 1),
-        DG_TILE_CONFIG("f32_256x64_w4x1", false, 256, 64, 4, 1, 8),
-        DG_TILE_CONFIG("f32_128x64_w2x1", false, 128, 64, 2, 1, 8),
+        //              name                    bf16   BM   BN  BK WM WN  S  G
+        DG_TILE_CONFIG("f32_256x128_w4x2_s2", false, 256, 128, 32, 4, 2, 2, 8),
+        DG_TILE_CONFIG("f32_128x128_w2x2_s2", false, 128, 128, 32, 2, 2, 2, 8),
+        DG_TILE_CONFIG("f32_256x256_w4x2_s2", false, 256, 256, 32, 4, 2, 2, 8),
+        DG_TILE_CONFIG("f32_64x64_w2x2_s2", false, 64, 64, 32, 2, 2, 2, 8),
+        DG_TILE_CONFIG("f32_64x64_w2x2_s3", false, 64, 64, 32, 2, 2, 3, 8),
+        DG_TILE_CONFIG("f32_64x256_w1x4_s3", false, 64, 256, 32, 1, 4, 3, 1),
+        DG_TILE_CONFIG("f32_64x256_w1x4_s4", false, 64, 256, 32, 1, 4, 4, 1),
+        DG_TILE_CONFIG("f32_64x128_w1x2_s4", false, 64, 128, 32, 1, 2, 4, 1),
+        DG_TILE_CONFIG("f32_256x64_w4x1_s3", false, 256, 64, 32, 4, 1, 3, 8),
+        DG_TILE_CONFIG("f32_128x64_w2x1_s2", false, 128, 64, 32, 2, 1, 2, 8),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

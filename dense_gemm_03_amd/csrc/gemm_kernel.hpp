@@ -8,19 +8,20 @@
 // operation", sections "Making the GPU implementation better" through "How to
 // do even better", rebuilt for CDNA4 wave64 matrix cores):
 //   * each workgroup owns a BM x BN block of C and walks K in tiles of BK;
-//   * each tile of A (BM x BK) and B (BK x BN) is copied from HBM with 16-byte
-//     loads into LDS, double buffered, so the copy of tile t+1 overlaps the
-//     products of tile t and one barrier per tile suffices;
-//   * LDS rows are padded (or XOR-swizzled) so the 16-byte fragment reads of a
-//     wave spread over all banks ("How to do even better": padding moves rows
-//     onto different banks);
+//   * tiles of A (BM x BK) and B (BK x BN) stream from HBM into a ring of LDS
+//     stages with direct global->LDS 16-byte loads, several tiles ahead of
+//     the products, one barrier per tile;
+//   * LDS rows are XOR-swizzled so the 16-byte fragment reads of a wave spread
+//     over all 64 banks ("How to do even better": shifting rows across banks
+//     removes the conflicts);
 //   * each wave owns a (BM/WM) x (BN/WN) sub-block held as 32x32 accumulator
 //     fragments in registers and reuses every A and B fragment it reads across
 //     that sub-block (the register blocking of "Improving the solution and
 //     balancing memory work");
-//   * blocks that cross the M, N or K edge take a masked path that loads zeros
-//     outside the matrix and stores only inside it; the branch is uniform over
-//     the workgroup.
+//   * blocks that cross the M or N edge, the partial last k-tile and
+//     unaligned operands take a masked path that loads zeros outside the
+//     matrix (through registers) and stores only inside it; the choice is
+//     uniform over the workgroup.
 //
 // k-slot assignment.  A 32x32 MFMA pairs, in each of its k slots, the A value a
 // lane supplies with the B value the same-numbered lane half supplies.  Lanes
@@ -34,11 +35,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dg {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // Arguments of one launch.  The grid is 1-D: splits * tiles_m * tiles_n blocks.
 struct KernelArgs {
@@ -52,89 +57,84 @@ struct KernelArgs {
     int splits;       // number of K slices
     int k_per_split;  // K extent of a slice, a multiple of the k-tile
     int group_m;      // tile rows per raster group (L2 reuse of B columns)
+    int direct_ok;    // per-thread byte offsets of a tile fit in 32 bits
 };
 
-// Element-type policy.
-template <bool BF16>
-struct Op;
-
-template <>
-struct Op<false> {               // fp32 inputs
-    using In = float;
-    static constexpr int BK = 32;   // k extent of one tile
-    static constexpr int VEC = 4;   // elements per 16-byte chunk
-};
-
-template <>
-struct Op<true> {                // bf16 inputs (raw 16-bit patterns)
-    using In = uint16_t;
-    static constexpr int BK = 64;
-    static constexpr int VEC = 8;
-};
-
-// Tile geometry and LDS layout for one configuration.
+// Tile geometry and LDS layout of one configuration.
 //
 // LDS banks (measured on gfx950 with the bank-conflict counter): 64 banks of
 // 4 bytes, and a 16-byte read serves 16 lanes per pass, so the 16 addresses of
 // a pass must cover 256 bytes that fall on distinct banks.
-template <bool BF16, int BM_, int BN_, int WM_, int WN_>
+template <bool BF16_, int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
 struct Geo {
-    using O = Op<BF16>;
-    using In = typename O::In;
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int BK = O::BK, VEC = O::VEC;
-    static constexpr int NT = 64 * WM * WN;          // threads per workgroup
+    static constexpr bool BF16 = BF16_;
+    using In = typename std::conditional<BF16, uint16_t, float>::type;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int STAGES = STAGES_;
+    static constexpr int ES = (int)sizeof(In);        // element bytes
+    static constexpr int VEC = 16 / ES;               // elements per 16-byte chunk
+    static constexpr int NW = WM * WN;                // waves
+    static constexpr int NT = 64 * NW;                // threads per workgroup
     static constexpr int WTM = BM / WM, WTN = BN / WN; // wave sub-block
     static constexpr int FM = WTM / 32, FN = WTN / 32; // 32x32 fragments per wave
     static constexpr int KH = BK / 2;                 // k values per lane half and tile
-    static constexpr int STEPS = 4;                   // fragment steps per tile
-    static constexpr int KS = KH / STEPS;             // k values per lane and step (4 or 8)
-    static_assert(KS * (int)sizeof(In) == 16, "one step is one 16-byte read per lane");
+    static constexpr int KS = VEC;                    // k values per lane and step (one 16-byte read)
+    static constexpr int STEPS = KH / KS;             // fragment steps per tile
+    static_assert(KH % KS == 0 && STEPS >= 2, "a tile needs at least two fragment steps");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave sub-block must be whole fragments");
 
-    // A tile: BM rows of BK elements = 128 bytes (8 chunks of 16 bytes), chunk
-    // c of row r stored in slot c ^ ((r>>1)&7): the two rows sharing a 256-byte
-    // bank line use its two halves, and the 8 row pairs of a 16-lane pass see
-    // 8 different slots, so fragment reads and tile writes are conflict-free.
-    static constexpr int A_ROW_BYTES = 128;
+    // MFMAs and LDS fragment reads per step and wave.
+    static constexpr int N_MMA = BF16 ? FM * FN : KS * FM * FN;
+    static constexpr int N_DS = FM + (BF16 ? 2 * FN : KS * FN);
+
+    // A tile: BM rows of BK elements (ACH chunks of 16 bytes).  Chunk c of row
+    // r sits in slot c ^ ((r / RPL) % ACH), RPL rows sharing one 256-byte bank
+    // line: the 16 rows read at one chunk by a 16-lane pass then cover all 64
+    // banks once, and so do the writes.
+    static constexpr int A_ROW_BYTES = BK * ES;
+    static constexpr int ACH = A_ROW_BYTES / 16;
+    static constexpr int RPL = 256 / A_ROW_BYTES;
+    static_assert(ACH * RPL == 16, "A rows of 64 or 128 bytes");
     static constexpr int A_BYTES = BM * A_ROW_BYTES;
-    static constexpr int A_CHUNKS = BM * 8;
+    static constexpr int A_CHUNKS = BM * ACH;
     static_assert(A_CHUNKS % NT == 0, "A chunks must divide evenly over the threads");
     static constexpr int A_PER_THREAD = A_CHUNKS / NT;
 
     // B tile: BK rows of BN elements, row-major as in memory.
     //   fp32: the two 32-float halves of each 64-float group swap places in
-    //         rows 16..31, so the two lane halves of a fragment read (rows k
-    //         and k+16, same columns) use different banks.
+    //         rows with bit 4 set, so the two lane halves of a fragment read
+    //         (rows k and k+16, same columns) use different banks.
     //   bf16: read with the LDS transpose load, 4 rows x 16 columns per
     //         16 lanes; the 64-byte segments of row k are XOR-permuted by
     //         (k & 3) so those 4 rows land on 4 different bank quarters.
-    static constexpr int B_ROW_BYTES = BN * (int)sizeof(In);
+    static constexpr int B_ROW_BYTES = BN * ES;
     static constexpr int B_BYTES = BK * B_ROW_BYTES;
     static constexpr int B_CHUNKS = BK * BN / VEC;
     static_assert(B_CHUNKS % NT == 0, "B chunks must divide evenly over the threads");
     static constexpr int B_PER_THREAD = B_CHUNKS / NT;
     static constexpr int B_SEGMASK = (BN / 32 >= 4) ? 3 : (BN / 32 - 1);
-    static_assert(BF16 || BN % 64 == 0, "fp32 B swizzle needs BN a multiple of 64");
+    static_assert(BF16 || (BN % 64 == 0 && BK == 32), "fp32 B swizzle: BN % 64 == 0, BK == 32");
     static_assert(!BF16 || BN % 32 == 0, "bf16 B segments are 32 columns wide");
 
     // Direct global->LDS loads write 64 lanes x 16 bytes = 1 KiB contiguous
     // LDS bytes per instruction; the tiles are cut into such pieces.
-    static constexpr int NW = WM * WN;                        // waves
-    static constexpr int A_PIECES = A_BYTES / 1024;           // 8 rows each
+    static constexpr int A_PIECES = A_BYTES / 1024;
     static constexpr int B_PIECES = B_BYTES / 1024;
+    static constexpr int A_ROWS_PER_PIECE = 1024 / A_ROW_BYTES;
     static constexpr int B_LANES_PER_ROW = B_ROW_BYTES / 16;
     static_assert(A_PIECES % NW == 0 && B_PIECES % NW == 0, "direct loads must divide over waves");
     static_assert(1024 % B_ROW_BYTES == 0, "a B row must fit a 1 KiB piece evenly");
+    static constexpr int LOADS_PER_TILE = (A_PIECES + B_PIECES) / NW;  // per wave
 
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int SMEM_BYTES = 2 * STAGE_BYTES;
-    static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave sub-block must be whole fragments");
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
+    static_assert(LOADS_PER_TILE * (STAGES - 2) <= 63, "vmcnt counts at most 63 loads");
 
-    // Byte offset of 16-byte chunk `chunk` (0..7) of A row `row` in a stage.
+    // Byte offset of 16-byte chunk `chunk` of A row `row` in a stage.
     static __device__ __forceinline__ int a_off(int row, int chunk)
     {
-        return row * A_ROW_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
+        return row * A_ROW_BYTES + ((chunk ^ ((row / RPL) % ACH)) << 4);
     }
 
     // Byte offset of element (k, n) of the B tile in a stage (n a multiple of
@@ -171,6 +171,46 @@ __device__ __forceinline__ float lds_loadf(const unsigned char *smem, int off)
 {
     return *reinterpret_cast<const float *>(smem + off);
 }
+
+// LDS transpose load (gfx950): within each group of 16 lanes, lane s names
+// row s/4, columns 4*(s%4)..+3 of a 4 x 16 block of 16-bit values, and lane i
+// receives column i of that block (its 4 rows).
+__device__ __forceinline__ v4i16 lds_read_tr16(const unsigned char *smem, int off)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)((__attribute__((address_space(3))) unsigned char *)smem + off));
+}
+
+// One direct global->LDS load: each lane copies 16 bytes from base + voff
+// (base uniform, voff a per-lane 32-bit byte offset), and the 64 lanes' bytes
+// land contiguously at LDS byte address lds_addr + 16 * lane (measured on
+// gfx950).  It is written as an instruction rather than the compiler builtin:
+// the builtin makes every later LDS transpose read wait for all such loads
+// in flight, which would undo the multi-stage pipeline.  The code that uses
+// it waits for the loads itself (s_waitcnt vmcnt before each barrier).  M0
+// carries the LDS address; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void direct_load16(const void *base, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(base)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a __shared__ location (the offset inside the
+// workgroup's LDS allocation).
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory loads are
+// outstanding and every LDS access has completed (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
 
 // Masked 16-byte chunk: elements [k, k+VEC) of one row, zero where the row is
 // outside the matrix (row_ok false) or k+e >= kend.  Never dereferences an
@@ -211,24 +251,11 @@ __device__ __forceinline__ void block_coords(const KernelArgs &p, int &slice, in
     tn = in_group / gsize;
 }
 
-// ------------------------------------------------------------------ kernel --
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// LDS transpose load (gfx950): within each group of 16 lanes, lane s names
-// row s/4, columns 4*(s%4)..+3 of a 4 x 16 block of 16-bit values, and lane i
-// receives column i of that block (its 4 rows).
-__device__ __forceinline__ v4i16 lds_read_tr16(const unsigned char *smem, int off)
-{
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)((__attribute__((address_space(3))) unsigned char *)smem + off));
-}
+// ---------------------------------------------------------- block context --
 
 // Per-block state shared by the main-loop helpers.
-template <bool BF16, int BM, int BN, int WM, int WN>
+template <class G>
 struct BlockCtx {
-    using G = Geo<BF16, BM, BN, WM, WN>;
     using In = typename G::In;
     const In *A;
     const In *B;
@@ -239,95 +266,31 @@ struct BlockCtx {
     int tid, lane, wrow, wcol;
 };
 
-// The operand tiles of one k-tile, between their global load and LDS store.
-template <bool BF16, int BM, int BN, int WM, int WN>
-struct StageRegs {
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    u32x4 a[G::A_PER_THREAD];
-    u32x4 b[G::B_PER_THREAD];
-};
-
 // Fragments of one step: per 32-row A fragment 16 bytes (4 fp32 or 8 bf16 k
 // values); per 32-column B fragment the same k values of the lane's column.
-template <bool BF16, int BM, int BN, int WM, int WN>
+template <class G>
 struct Frags {
-    using G = Geo<BF16, BM, BN, WM, WN>;
     u32x4 a[G::FM];
     u32x4 b[G::FN];
 };
 
-// Global -> registers for the k-tile starting at k0.  MASKED: zero outside
-// the matrix (rows >= M, columns >= N, k >= kend); otherwise the whole tile is
-// known to be inside and 16-byte aligned.
-//   A chunk u: row tid/8 + u*NT/8, elements (tid%8)*VEC .. +VEC
-//   B chunk u: c = tid + u*NT; row c/(BN/VEC), elements (c%(BN/VEC))*VEC .. +VEC
-// Consecutive lanes read consecutive 16-byte chunks of a row (coalesced).
-template <bool MASKED, bool ALIGNED, bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void global_load(const BlockCtx<BF16, BM, BN, WM, WN> &c, int k0,
-                                            StageRegs<BF16, BM, BN, WM, WN> &r)
+// Fragments of step `step` of the tile in `stage`.  Lane half h (lanes
+// 32h..32h+31) supplies k = h*BK/2 + step*KS .. +KS of the tile.
+template <class G>
+__device__ __forceinline__ void load_frags(const unsigned char *stage, const BlockCtx<G> &c,
+                                           int step, Frags<G> &f)
 {
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    using In = typename G::In;
-    constexpr int VEC = G::VEC, NT = G::NT, CPR = BN / VEC;
-    const int ka = k0 + (c.tid & 7) * VEC;
-#pragma unroll
-    for (int u = 0; u < G::A_PER_THREAD; ++u) {
-        const int gi = c.bm + (c.tid >> 3) + u * (NT / 8);
-        const In *row = c.A + (int64_t)gi * c.lda;
-        if constexpr (MASKED)
-            r.a[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gi < c.M, ka, c.kend);
-        else
-            r.a[u] = load16(row + ka);
-    }
-#pragma unroll
-    for (int u = 0; u < G::B_PER_THREAD; ++u) {
-        const int ch = c.tid + u * NT;
-        const int gk = k0 + ch / CPR;
-        const int gn = c.bn + (ch % CPR) * VEC;
-        const In *row = c.B + (int64_t)gk * c.ldb;
-        if constexpr (MASKED)
-            r.b[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gk < c.kend, gn, c.N);
-        else
-            r.b[u] = load16(row + gn);
-    }
-}
-
-template <bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void lds_store(unsigned char *stage, int tid,
-                                          const StageRegs<BF16, BM, BN, WM, WN> &r)
-{
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    constexpr int NT = G::NT, CPR = BN / G::VEC;
-    unsigned char *sb = stage + G::A_BYTES;
-#pragma unroll
-    for (int u = 0; u < G::A_PER_THREAD; ++u)
-        lds_store16(stage, G::a_off((tid >> 3) + u * (NT / 8), tid & 7), r.a[u]);
-#pragma unroll
-    for (int u = 0; u < G::B_PER_THREAD; ++u) {
-        const int ch = tid + u * NT;
-        lds_store16(sb, G::b_off(ch / CPR, (ch % CPR) * G::VEC), r.b[u]);
-    }
-}
-
-// Fragments of step `step` (0..3) of the tile in `stage`.  Lane half h
-// (lanes 32h..32h+31) supplies k = h*BK/2 + step*KS .. +KS of the tile.
-template <bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void load_frags(const unsigned char *stage,
-                                           const BlockCtx<BF16, BM, BN, WM, WN> &c, int step,
-                                           Frags<BF16, BM, BN, WM, WN> &f)
-{
-    using G = Geo<BF16, BM, BN, WM, WN>;
     const unsigned char *sb = stage + G::A_BYTES;
     const int half = c.lane >> 5, l32 = c.lane & 31;
     const int kk = half * G::KH + step * G::KS;
 #pragma unroll
     for (int fm = 0; fm < G::FM; ++fm) {
         const int row = c.wrow * G::WTM + fm * 32 + l32;
-        f.a[fm] = lds_load16(stage, G::a_off(row, 4 * half + step));
+        f.a[fm] = lds_load16(stage, G::a_off(row, kk / G::VEC));
     }
 #pragma unroll
     for (int fn = 0; fn < G::FN; ++fn) {
-        if constexpr (BF16) {
+        if constexpr (G::BF16) {
             // two transpose loads: k = kk..kk+3 and kk+4..kk+7 of column
             // (fragment column) + lane%32
             const int p = c.lane & 15, g = (c.lane >> 4) & 1;
@@ -348,13 +311,10 @@ __device__ __forceinline__ void load_frags(const unsigned char *stage,
     }
 }
 
-template <bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void mma(const Frags<BF16, BM, BN, WM, WN> &f,
-                                    floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
-                                                   [Geo<BF16, BM, BN, WM, WN>::FN])
+template <class G>
+__device__ __forceinline__ void mma(const Frags<G> &f, floatx16 (&acc)[G::FM][G::FN])
 {
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    if constexpr (BF16) {
+    if constexpr (G::BF16) {
 #pragma unroll
         for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
@@ -375,83 +335,6 @@ __device__ __forceinline__ void mma(const Frags<BF16, BM, BN, WM, WN> &f,
     }
 }
 
-// One direct global->LDS load: each lane copies 16 bytes from `src`, and the
-// 64 lanes' bytes land contiguously at `lds` + 16 * lane (measured on gfx950).
-__device__ __forceinline__ void direct_load16(const void *src, unsigned char *lds)
-{
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void *)src,
-        (__attribute__((address_space(3))) void *)((__attribute__((address_space(3)))
-                                                     unsigned char *)lds),
-        16, 0, 0);
-}
-
-// Per-thread byte offsets of the direct loads, relative to the tile origin
-// in A (row bm, column k0) and in B (row k0, column bn).  They do not change
-// from one k-tile to the next, so they are computed once per block and the
-// per-tile address is a uniform base plus a 32-bit offset.
-template <bool BF16, int BM, int BN, int WM, int WN>
-struct DirectOffsets {
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    uint32_t a[G::A_PIECES / G::NW];
-    uint32_t b[G::B_PIECES / G::NW];
-};
-
-// Direct copy of a k-tile into a stage (interior tiles only: every address
-// is inside the matrix and 16-byte aligned).  The LDS side is fixed -- 1 KiB
-// per instruction, lane l at byte 16*l -- so each lane fetches the global
-// chunk that the tile's XOR swizzle places at its LDS position (the
-// swizzles are their own inverses).
-template <bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void direct_offsets(const BlockCtx<BF16, BM, BN, WM, WN> &c,
-                                               DirectOffsets<BF16, BM, BN, WM, WN> &o)
-{
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    using In = typename G::In;
-    constexpr int NW = G::NW, LPR = G::B_LANES_PER_ROW;
-    const int wave = c.tid >> 6;
-#pragma unroll
-    for (int i = 0; i < G::A_PIECES / NW; ++i) {
-        const int j = wave + NW * i;                 // piece: rows 8j .. 8j+7
-        const int r = 8 * j + (c.lane >> 3);
-        const int chunk = (c.lane & 7) ^ ((r >> 1) & 7);
-        o.a[i] = (uint32_t)(((int64_t)r * c.lda + chunk * G::VEC) * (int64_t)sizeof(In));
-    }
-#pragma unroll
-    for (int i = 0; i < G::B_PIECES / NW; ++i) {
-        const int j = wave + NW * i;                 // piece: rows j*(64/LPR) ..
-        const int k = j * (64 / LPR) + c.lane / LPR;
-        const int phys = (c.lane % LPR) * G::VEC;    // element position in the LDS row
-        int n;
-        if constexpr (BF16)
-            n = ((((phys >> 5) ^ (k & G::B_SEGMASK))) << 5) | (phys & 31);
-        else
-            n = phys ^ (((k >> 4) & 1) << 5);
-        o.b[i] = (uint32_t)(((int64_t)k * c.ldb + n) * (int64_t)sizeof(In));
-    }
-}
-
-template <bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void direct_tile_load(unsigned char *stage,
-                                                 const BlockCtx<BF16, BM, BN, WM, WN> &c,
-                                                 const DirectOffsets<BF16, BM, BN, WM, WN> &o,
-                                                 int k0)
-{
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    constexpr int NW = G::NW;
-    const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
-    const unsigned char *a_base =
-        reinterpret_cast<const unsigned char *>(c.A + ((int64_t)c.bm * c.lda + k0));
-    const unsigned char *b_base =
-        reinterpret_cast<const unsigned char *>(c.B + ((int64_t)k0 * c.ldb + c.bn));
-#pragma unroll
-    for (int i = 0; i < G::A_PIECES / NW; ++i)
-        direct_load16(a_base + o.a[i], stage + 1024 * (wave + NW * i));
-#pragma unroll
-    for (int i = 0; i < G::B_PIECES / NW; ++i)
-        direct_load16(b_base + o.b[i], stage + G::A_BYTES + 1024 * (wave + NW * i));
-}
-
 // Instruction interleave for one step: each MFMA is followed by up to one
 // direct global->LDS load and one LDS fragment read, so the loads and reads
 // issue while the matrix core is busy instead of in a burst after it.
@@ -468,97 +351,216 @@ __device__ __forceinline__ void interleave_step()
     if (N_VMEM > N_MMA) __builtin_amdgcn_sched_group_barrier(0x020, N_VMEM - N_MMA, 0);
 }
 
-// One interior k-tile in the direct-load pipeline: multiply the tile held in
-// `stage` while the tile at k_next streams into `other`; the barrier that
-// ends the tile also waits for those loads.  (After the last tile the caller
-// passes an in-bounds k_next again, so the code has no branch; `other` is
-// not read after that.)  The two stages are distinct __shared__ arrays,
-// passed as restrict pointers: the alias scopes this gives the LDS reads and
-// the direct loads let the compiler see that reading one stage need not wait
-// for the loads into the other.
-template <bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void direct_tile(unsigned char *__restrict__ stage,
-                                            unsigned char *__restrict__ other,
-                                            const BlockCtx<BF16, BM, BN, WM, WN> &c,
-                                            const DirectOffsets<BF16, BM, BN, WM, WN> &o,
-                                            int k_next, Frags<BF16, BM, BN, WM, WN> &cur,
-                                            floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
-                                                           [Geo<BF16, BM, BN, WM, WN>::FN])
+// -------------------------------------------------- interior (direct) path --
+
+// Per-thread byte offsets of the direct loads, relative to the tile origin
+// in A (row bm, column k0) and in B (row k0, column bn).  They do not change
+// from one k-tile to the next, so they are computed once per block and the
+// per-tile address is a uniform base plus a 32-bit offset.
+template <class G>
+struct DirectOffsets {
+    uint32_t a[G::A_PIECES / G::NW];
+    uint32_t b[G::B_PIECES / G::NW];
+};
+
+// The LDS side of a direct load is fixed -- 1 KiB per instruction, lane l at
+// byte 16*l -- so each lane fetches the global chunk that the tile's XOR
+// swizzle places at its LDS position (the swizzles are their own inverses).
+template <class G>
+__device__ __forceinline__ void direct_offsets(const BlockCtx<G> &c, DirectOffsets<G> &o)
 {
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    constexpr int N_MMA = BF16 ? G::FM * G::FN : G::KS * G::FM * G::FN;
-    constexpr int N_DS = G::FM + (BF16 ? 2 * G::FN : G::KS * G::FN);
-    constexpr int N_VMEM = (G::A_PIECES + G::B_PIECES) / G::NW;
-    Frags<BF16, BM, BN, WM, WN> nxt;
-    direct_tile_load(other, c, o, k_next);
+    constexpr int NW = G::NW, LPR = G::B_LANES_PER_ROW;
+    const int wave = c.tid >> 6;
+#pragma unroll
+    for (int i = 0; i < G::A_PIECES / NW; ++i) {
+        const int j = wave + NW * i;  // piece: A rows j*A_ROWS_PER_PIECE ..
+        const int r = j * G::A_ROWS_PER_PIECE + c.lane / G::ACH;
+        const int chunk = (c.lane % G::ACH) ^ ((r / G::RPL) % G::ACH);
+        o.a[i] = (uint32_t)(((int64_t)r * c.lda + chunk * G::VEC) * G::ES);
+    }
+#pragma unroll
+    for (int i = 0; i < G::B_PIECES / NW; ++i) {
+        const int j = wave + NW * i;  // piece: B rows j*(64/LPR) ..
+        const int k = j * (64 / LPR) + c.lane / LPR;
+        const int phys = (c.lane % LPR) * G::VEC;  // element position in the LDS row
+        int n;
+        if constexpr (G::BF16)
+            n = (((phys >> 5) ^ (k & G::B_SEGMASK)) << 5) | (phys & 31);
+        else
+            n = phys ^ (((k >> 4) & 1) << 5);
+        o.b[i] = (uint32_t)(((int64_t)k * c.ldb + n) * G::ES);
+    }
+}
+
+// Direct copy of the k-tile at k0 into `stage` (interior tiles only: every
+// address is inside the matrix and 16-byte aligned).
+template <class G>
+__device__ __forceinline__ void direct_tile_load(unsigned char *stage, const BlockCtx<G> &c,
+                                                 const DirectOffsets<G> &o, int k0)
+{
+    constexpr int NW = G::NW;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + 1024 * wave;
+    const void *a_base = c.A + ((int64_t)c.bm * c.lda + k0);
+    const void *b_base = c.B + ((int64_t)k0 * c.ldb + c.bn);
+#pragma unroll
+    for (int i = 0; i < G::A_PIECES / NW; ++i) direct_load16(a_base, o.a[i], lds + 1024 * NW * i);
+#pragma unroll
+    for (int i = 0; i < G::B_PIECES / NW; ++i)
+        direct_load16(b_base, o.b[i], lds + G::A_BYTES + 1024 * NW * i);
+}
+
+// One interior k-tile: multiply the tile in `stage` while the tile at k_load
+// streams into `load` (STAGES-1 tiles ahead).  The tile ends with a wait for
+// the next tile's loads -- only those: the later tiles stay in flight -- and
+// a barrier, after which the next tile's first fragments are read under the
+// last products of this one.  (Past the last tile the caller passes an
+// in-bounds k_load again, so the code has no branch.)
+template <class G>
+__device__ __forceinline__ void direct_tile(const unsigned char *stage, const unsigned char *next,
+                                            unsigned char *load,
+                                            const BlockCtx<G> &c, const DirectOffsets<G> &o,
+                                            int k_load, Frags<G> &cur,
+                                            floatx16 (&acc)[G::FM][G::FN])
+{
+    Frags<G> nxt;
+    direct_tile_load(load, c, o, k_load);
     load_frags(stage, c, 1, nxt);
     mma(cur, acc);
-    interleave_step<N_MMA, N_DS, N_VMEM>();
+    interleave_step<G::N_MMA, G::N_DS, G::LOADS_PER_TILE>();
     cur = nxt;
 #pragma unroll
     for (int step = 1; step < G::STEPS - 1; ++step) {
         load_frags(stage, c, step + 1, nxt);
         mma(cur, acc);
-        interleave_step<N_MMA, N_DS, 0>();
+        interleave_step<G::N_MMA, G::N_DS, 0>();
         cur = nxt;
     }
-    __syncthreads();
-    load_frags(other, c, 0, nxt);
+    // The next tile's loads were issued STAGES-2 tiles before the ones just
+    // issued; every wave waits for its own share before the barrier, so after
+    // it the whole tile is in LDS.  lgkmcnt(0): this tile's reads are done
+    // before anyone may overwrite the stage.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(G::LOADS_PER_TILE * (G::STAGES - 2)));
+    __builtin_amdgcn_s_barrier();
+    load_frags(next, c, 0, nxt);
     mma(cur, acc);
-    interleave_step<N_MMA, N_DS, 0>();
+    interleave_step<G::N_MMA, G::N_DS, 0>();
     cur = nxt;
 }
 
-// Interior k-tiles with direct loads, two tiles per iteration so that each
-// stage is always the same array.  On entry no wave may still read stage 0.
-template <bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void main_loop_direct(unsigned char *smem0, unsigned char *smem1,
-                                                 const BlockCtx<BF16, BM, BN, WM, WN> &c,
-                                                 int k_first, int ntiles,
-                                                 floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
-                                                                [Geo<BF16, BM, BN, WM, WN>::FN])
+// Interior k-tiles [0, ntiles) from k_first, STAGES tiles per loop iteration
+// so that each stage is always the same array.  The stages are distinct
+// __shared__ arrays passed as restrict pointers of this one function: the
+// alias scopes this gives every LDS read and direct load let the compiler see
+// that reading one stage need not wait for loads into the others.  On entry
+// no wave may read or load any stage; on exit no load is in flight.
+template <class G>
+__device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
+                                                 unsigned char *__restrict__ s1,
+                                                 unsigned char *__restrict__ s2,
+                                                 unsigned char *__restrict__ s3,
+                                                 const BlockCtx<G> &c, int k_first, int ntiles,
+                                                 floatx16 (&acc)[G::FM][G::FN])
 {
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    Frags<BF16, BM, BN, WM, WN> cur;
-    DirectOffsets<BF16, BM, BN, WM, WN> o;
+    constexpr int S = G::STAGES, BK = G::BK;
+    unsigned char *const st[4] = {s0, s1, s2, s3};
+    Frags<G> cur;
+    DirectOffsets<G> o;
     direct_offsets(c, o);
-    direct_tile_load(smem0, c, o, k_first);
-    __syncthreads();
-    load_frags(smem0, c, 0, cur);
-    const int k_last = k_first + (ntiles - 1) * G::BK;
-    for (int t = 0; t < ntiles; t += 2) {
-        const int k1 = min(k_first + (t + 1) * G::BK, k_last);
-        direct_tile(smem0, smem1, c, o, k1, cur, acc);
-        if (t + 1 < ntiles) direct_tile(smem1, smem0, c, o, min(k1 + G::BK, k_last), cur, acc);
+    const int k_last = k_first + (ntiles - 1) * BK;
+    // prologue: tiles 0 .. S-2 in flight, tile 0 complete
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) direct_tile_load(st[s], c, o, min(k_first + s * BK, k_last));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(G::LOADS_PER_TILE * (S - 2)));
+    __builtin_amdgcn_s_barrier();
+    load_frags(st[0], c, 0, cur);
+
+    for (int t = 0; t < ntiles; t += S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            if (s == 0 || t + s < ntiles) {
+                const int kl = min(k_first + (t + s + S - 1) * BK, k_last);
+                direct_tile(st[s], st[(s + 1) % S], st[(s + S - 1) % S], c, o, kl, cur, acc);
+            }
+        }
+    }
+    // drain the loads issued past the last tile before the stages are reused
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+}
+
+// ------------------------------------------------------------ masked path --
+
+// The operand tiles of one k-tile, between their global load and LDS store.
+template <class G>
+struct StageRegs {
+    u32x4 a[G::A_PER_THREAD];
+    u32x4 b[G::B_PER_THREAD];
+};
+
+// Global -> registers for the k-tile starting at k0, zero outside the matrix
+// (rows >= M, columns >= N, k >= kend).
+//   A chunk u: row (tid + u*NT) / ACH, chunk (tid + u*NT) % ACH
+//   B chunk u: c = tid + u*NT; row c/(BN/VEC), elements (c%(BN/VEC))*VEC .. +VEC
+// Consecutive lanes read consecutive 16-byte chunks of a row (coalesced).
+template <bool ALIGNED, class G>
+__device__ __forceinline__ void global_load_masked(const BlockCtx<G> &c, int k0, StageRegs<G> &r)
+{
+    using In = typename G::In;
+    constexpr int VEC = G::VEC, NT = G::NT, CPR = G::BN / VEC;
+#pragma unroll
+    for (int u = 0; u < G::A_PER_THREAD; ++u) {
+        const int ch = c.tid + u * NT;
+        const int gi = c.bm + ch / G::ACH;
+        const In *row = c.A + (int64_t)gi * c.lda;
+        r.a[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gi < c.M, k0 + (ch % G::ACH) * VEC, c.kend);
+    }
+#pragma unroll
+    for (int u = 0; u < G::B_PER_THREAD; ++u) {
+        const int ch = c.tid + u * NT;
+        const int gk = k0 + ch / CPR;
+        const int gn = c.bn + (ch % CPR) * VEC;
+        const In *row = c.B + (int64_t)gk * c.ldb;
+        r.b[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gk < c.kend, gn, c.N);
     }
 }
 
-// `ntiles` k-tiles starting at k_first, accumulated into acc.  One barrier
-// per tile: stage t&1 is read while stage (t+1)&1 receives tile t+1; the
-// fragments of step j+1 are read before the products of step j are issued,
-// and the first fragments of tile t+1 right after the barrier, under the last
-// products of tile t.  On entry no wave may still read stage 0.
-template <bool MASKED, bool ALIGNED, bool BF16, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void main_loop(unsigned char *smem0, unsigned char *smem1,
-                                          const BlockCtx<BF16, BM, BN, WM, WN> &c, int k_first,
-                                          int ntiles,
-                                          floatx16 (&acc)[Geo<BF16, BM, BN, WM, WN>::FM]
-                                                         [Geo<BF16, BM, BN, WM, WN>::FN])
+template <class G>
+__device__ __forceinline__ void lds_store(unsigned char *stage, int tid, const StageRegs<G> &r)
 {
-    using G = Geo<BF16, BM, BN, WM, WN>;
-    StageRegs<BF16, BM, BN, WM, WN> regs;
-    Frags<BF16, BM, BN, WM, WN> cur, nxt;
+    constexpr int NT = G::NT, CPR = G::BN / G::VEC;
+    unsigned char *sb = stage + G::A_BYTES;
+#pragma unroll
+    for (int u = 0; u < G::A_PER_THREAD; ++u) {
+        const int ch = tid + u * NT;
+        lds_store16(stage, G::a_off(ch / G::ACH, ch % G::ACH), r.a[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < G::B_PER_THREAD; ++u) {
+        const int ch = tid + u * NT;
+        lds_store16(sb, G::b_off(ch / CPR, (ch % CPR) * G::VEC), r.b[u]);
+    }
+}
 
-    global_load<MASKED, ALIGNED>(c, k_first, regs);
+// `ntiles` masked k-tiles from k_first, double buffered through registers
+// (stage t&1 is read while stage (t+1)&1 receives tile t+1).  On entry no
+// wave may still use stages 0 and 1.
+template <bool ALIGNED, class G>
+__device__ __forceinline__ void main_loop_masked(unsigned char *smem0, unsigned char *smem1,
+                                                 const BlockCtx<G> &c, int k_first, int ntiles,
+                                                 floatx16 (&acc)[G::FM][G::FN])
+{
+    StageRegs<G> regs;
+    Frags<G> cur, nxt;
+    global_load_masked<ALIGNED>(c, k_first, regs);
     lds_store(smem0, c.tid, regs);
     __syncthreads();
     load_frags(smem0, c, 0, cur);
-
     for (int t = 0; t < ntiles; ++t) {
         unsigned char *stage = (t & 1) ? smem1 : smem0;
         unsigned char *other = (t & 1) ? smem0 : smem1;
         const bool more = t + 1 < ntiles;
-        if (more) global_load<MASKED, ALIGNED>(c, k_first + (t + 1) * G::BK, regs);
+        if (more) global_load_masked<ALIGNED>(c, k_first + (t + 1) * G::BK, regs);
 #pragma unroll
         for (int step = 0; step < G::STEPS - 1; ++step) {
             load_frags(stage, c, step + 1, nxt);
@@ -573,18 +575,22 @@ __device__ __forceinline__ void main_loop(unsigned char *smem0, unsigned char *s
     }
 }
 
-template <bool BF16, int BM, int BN, int WM, int WN, bool ALIGNED>
+// ------------------------------------------------------------------ kernel --
+
+template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, bool ALIGNED>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(KernelArgs p)
 {
-    using G = Geo<BF16, BM, BN, WM, WN>;
+    using G = Geo<BF16, BM, BN, BK, WM, WN, STAGES>;
     using In = typename G::In;
-    constexpr int BK = G::BK;
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem0[G::STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char smem1[G::STAGE_BYTES];
+    // One __shared__ array per stage (unused ones are one byte).
+    __shared__ __attribute__((aligned(1024))) unsigned char lds0[G::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds2[STAGES > 2 ? G::STAGE_BYTES : 1];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds3[STAGES > 3 ? G::STAGE_BYTES : 1];
 
-    BlockCtx<BF16, BM, BN, WM, WN> c;
+    BlockCtx<G> c;
     c.tid = (int)threadIdx.x;
     c.lane = c.tid & 63;
     const int wave = c.tid >> 6;
@@ -614,15 +620,13 @@ gemm_kernel(KernelArgs p)
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
     // Interior blocks run their whole k-tiles without bounds checks; the
-    // partial last k-tile, blocks crossing the M or N edge and unaligned
-    // operands take the masked loads.  The choice is uniform per workgroup.
-    const bool edge = !ALIGNED || c.bm + BM > p.M || c.bn + BN > p.N;
+    // partial last k-tile, blocks crossing the M or N edge, unaligned operands
+    // and leading dimensions too large for 32-bit tile offsets take the
+    // masked loads.  The choice is uniform per workgroup.
+    const bool edge = !ALIGNED || !p.direct_ok || c.bm + BM > p.M || c.bn + BN > p.N;
     const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
-    if (nfast > 0) main_loop_direct(smem0, smem1, c, kbeg, nfast, acc);
-    if (ntiles > nfast) {
-        if (nfast > 0) __syncthreads();
-        main_loop<true, ALIGNED>(smem0, smem1, c, kbeg + nfast * BK, ntiles - nfast, acc);
-    }
+    if (nfast > 0) main_loop_direct(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
+    if (ntiles > nfast) main_loop_masked<ALIGNED>(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc);
 
     // Epilogue: accumulator element r of a 32x32 fragment sits at row
     // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that fragment.

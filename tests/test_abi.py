@@ -61,14 +61,24 @@ def _cfg_for(name):
 
 
 def test_shape_classes_of_the_workloads():
-    assert _cfg_for("fp32-4096")[2] == "f32_128x128_w2x2"
-    assert _cfg_for("fp32-rag")[2] == "f32_128x128_w2x2"
-    assert _cfg_for("bf16-8192")[2] == "bf16_256x256_w2x2"
-    assert _cfg_for("tall")[2] == "f32_256x64_w4x1"
+    assert _cfg_for("fp32-4096")[2] == "f32_256x256_w4x2_s2"
+    assert _cfg_for("fp32-rag")[2] == "f32_64x64_w2x2_s3"
+    assert _cfg_for("bf16-8192")[2] == "bf16_256x256x32_w4x2_s4"
+    assert _cfg_for("tall")[2] == "f32_64x64_w2x2_s2"
     dtype, c, name, splits = _cfg_for("im2col")
-    assert name == "f32_64x256_w1x4" and splits > 1
+    assert name == "f32_64x256_w1x4_s3" and splits == 8
     for big in ("fp32-4096", "bf16-8192", "tall"):
         assert _cfg_for(big)[3] == 1
+
+
+def test_grid_fill_steers_the_large_class():
+    """A 4096^2 output is 256 blocks of 256x256, one per compute unit; a
+    6144^2 output would leave 3/4 of the second round idle with those blocks,
+    so the 64x64 blocks (9216 of them, 3 per unit) win."""
+    name = lambda M, N: dg.gemm_config_name(dg.GEMM_DTYPE_F32, dg.gemm_select_config(dg.GEMM_DTYPE_F32, M, N, 1024))
+    assert name(4096, 4096) == "f32_256x256_w4x2_s2"
+    assert name(8192, 8192) == "f32_256x256_w4x2_s2"
+    assert name(6144, 6144) == "f32_64x64_w2x2_s3"
 
 
 def test_split_plan_covers_k_with_nonempty_slices():
