@@ -81,7 +81,7 @@ int select_config(int dtype, int64_t M, int64_t N, int64_t K)
 {
     (void)K;
     if (dtype == GEMM_DTYPE_F32) {
-        static const int tall = config_index(dtype, "f32_64x64_w2x2_s2");
+        static const int tall = config_index(dtype, "f32_128x64_w2x2_s2");
         static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
         static const int narrow = config_index(dtype, "f32_128x64_w2x1_s2");
         static const int small = config_index(dtype, "f32_64x64_w2x2_s2");

@@ -12,9 +12,7 @@ const TileConfig *bf16_configs(int *count)
         DG_TILE_CONFIG("bf16_256x256x32_w2x2_s4", true, 256, 256, 32, 2, 2, 4, 8),
         DG_TILE_CONFIG("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8),
         DG_TILE_CONFIG("bf16_256x256x64_w2x4_s2", true, 256, 256, 64, 2, 4, 2, 8),
-        DG_TILE_CONFIG("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 8),
-        DG_TILE_CONFIG("bf16_256x256x64_w2x2_s2_g4", true, 256, 256, 64, 2, 2, 2, 4),
-        DG_TILE_CONFIG("bf16_256x256x64_w2x2_s2_g16", true, 256, 256, 64, 2, 2, 2, 16),
+        DG_TILE_CONFIG("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 4),
         DG_TILE_CONFIG("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8),
         DG_TILE_CONFIG("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8),
         DG_TILE_CONFIG("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8),

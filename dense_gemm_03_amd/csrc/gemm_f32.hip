@@ -24,6 +24,11 @@ const TileConfig *f32_configs(int *count)
         DG_TILE_CONFIG("f32_64x128_w1x2_s4", false, 64, 128, 32, 1, 2, 4, 1),
         DG_TILE_CONFIG("f32_256x64_w4x1_s3", false, 256, 64, 32, 4, 1, 3, 8),
         DG_TILE_CONFIG("f32_128x64_w2x1_s2", false, 128, 64, 32, 2, 1, 2, 8),
+        DG_TILE_CONFIG("f32_128x64_w2x2_s2", false, 128, 64, 32, 2, 2, 2, 8),
+        DG_TILE_CONFIG("f32_128x64_w4x1_s2", false, 128, 64, 32, 4, 1, 2, 8),
+        DG_TILE_CONFIG("f32_64x64_w1x1_s2", false, 64, 64, 32, 1, 1, 2, 8),
+        DG_TILE_CONFIG("f32_64x64_w1x1_s4", false, 64, 64, 32, 1, 1, 4, 8),
+        DG_TILE_CONFIG("f32_64x256_w1x4_s2", false, 64, 256, 32, 1, 4, 2, 1),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

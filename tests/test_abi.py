@@ -64,7 +64,7 @@ def test_shape_classes_of_the_workloads():
     assert _cfg_for("fp32-4096")[2] == "f32_256x256_w4x2_s2"
     assert _cfg_for("fp32-rag")[2] == "f32_64x64_w2x2_s3"
     assert _cfg_for("bf16-8192")[2] == "bf16_256x256x32_w4x2_s4"
-    assert _cfg_for("tall")[2] == "f32_64x64_w2x2_s2"
+    assert _cfg_for("tall")[2] == "f32_128x64_w2x2_s2"
     dtype, c, name, splits = _cfg_for("im2col")
     assert name == "f32_64x256_w1x4_s3" and splits == 8
     for big in ("fp32-4096", "bf16-8192", "tall"):
