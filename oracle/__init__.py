@@ -162,3 +162,76 @@ def max_error_ratio(C, C_ref: np.ndarray, S: np.ndarray) -> tuple[float, bool]:
         ratio = float("inf")
     zeros_ok = bool(np.all(C[~pos] == 0.0))
     return ratio, zeros_ok
+
+
+def _stored_to_op(X: np.ndarray, trans: bool) -> np.ndarray:
+    """op(X): X itself, or a row-major copy of its transpose."""
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def gemm_general(A: np.ndarray, B: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+                 C0: np.ndarray | None = None, transa: bool = False, transb: bool = False,
+                 kind: str = "f32", threads: int | None = None):
+    """The generalised product of "Learning to develop for GPUs through the GEMM
+    operation", section "Generalized matrix multiplication GEMM": the matrix
+    product weighted by alpha, plus the accumulator C0 weighted by beta,
+
+        C = alpha * op(A) . op(B) + beta * C0,    op(X) = X or X^T,
+
+    in float64.  A and B are the stored matrices (``kind`` "f32": float32,
+    "bf16": uint16 bit patterns): A is M x K, or K x M when ``transa``; B is
+    K x N, or N x K when ``transb``.  op() is a transposed copy; the product is
+    the C code above.  alpha and beta are applied exactly in float64 to that
+    exact product.  C0 is the initial C as float64 (decoded when C is bf16).
+
+    The conventions of the BLAS routine this generalises (a reading, the page's
+    formula being an image): C0 is not read when beta == 0 (it may hold NaN),
+    and A and B are not read when alpha == 0 or K == 0.
+
+    Returns (C_ref, S) with S = |alpha| * sum_k |op(A)[i][k]| |op(B)[k][j]|
+    + |beta| * |C0[i][j]|, the scale of the tolerance test."""
+    opA = _stored_to_op(A, transa)
+    opB = _stored_to_op(B, transb)
+    M, K = opA.shape
+    K2, N = opB.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: op(A) is %s, op(B) is %s" % (opA.shape, opB.shape))
+    alpha = float(alpha)
+    beta = float(beta)
+    if alpha != 0.0 and K > 0:
+        P, SP = _gemm(kind, opA, opB, threads, True)
+        C = alpha * P
+        S = abs(alpha) * SP
+    else:
+        C = np.zeros((M, N), dtype=np.float64)
+        S = np.zeros((M, N), dtype=np.float64)
+    if beta != 0.0:
+        if C0 is None or C0.shape != (M, N):
+            raise ValueError("beta != 0 needs C0 of shape (%d, %d)" % (M, N))
+        C0 = np.asarray(C0, dtype=np.float64)
+        C = C + beta * C0
+        S = S + abs(beta) * np.abs(C0)
+    return C, S
+
+
+def round_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (8 significant bits), ties to
+    the even significand, and return the bit patterns; overflow gives +-inf and
+    NaN a quiet NaN.  Subnormals keep the binary32 spacing 2^-133."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat, res = x.reshape(-1), out.reshape(-1)
+    for t, v in enumerate(flat):
+        if np.isnan(v):
+            res[t] = 0x7FC0
+            continue
+        if np.isinf(v) or v == 0.0:
+            res[t] = np.array([v], dtype=np.float32).view(np.uint32)[0] >> 16
+            continue
+        _, e = np.frexp(v)                     # |v| = m * 2^e, 0.5 <= m < 1
+        step = np.ldexp(1.0, max(int(e) - 8, -133))   # spacing of 8-bit significands
+        q = np.rint(v / step) * step           # np.rint rounds halves to even
+        if abs(q) >= 2.0 ** 128:
+            q = np.copysign(np.inf, v)
+        res[t] = np.array([q], dtype=np.float32).view(np.uint32)[0] >> 16
+    return out
