@@ -15,7 +15,8 @@ in HBM.  Prints ONE JSON line:
                           same workload on this host
   also                    the same measurement for the other headline workload
                           (bf16 8192^3), and with --all for the im2col and
-                          tall-skinny shapes
+                          tall-skinny shapes and the generalised-GEMM variants
+                          (transposed operands, alpha/beta, bf16 C)
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -28,6 +29,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -35,7 +38,7 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix peaks
 HBM_PEAK_GBS = 8000.0
 PRIMARY = "fp32-4096"
 SECONDARY = ["bf16-8192"]
-EXTRA = ["im2col", "tall"]
+EXTRA = ["im2col", "tall", "bf16-8192-nt-bf16c", "bf16-8192-tn-acc", "fp32-4096-tt-ab"]
 
 
 def log(msg: str) -> None:
@@ -67,31 +70,45 @@ def stored_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
+def _workload(name: str):
+    from dense_gemm_03_amd.workloads import VARIANTS, WORKLOADS
+    return WORKLOADS[name] if name in WORKLOADS else VARIANTS[name]
+
+
 def measure(name: str, steps: int, warmup: int):
     """Time `steps` GEMM calls on workload `name`; returns a result dict."""
     import torch
 
     import dense_gemm_03_amd as dg
-    from dense_gemm_03_amd.workloads import WORKLOADS
 
-    w = WORKLOADS[name]
+    w = _workload(name)
     log("[bench] %s: drawing operands %dx%dx%d (%s)" % (name, w.M, w.N, w.K, w.dtype))
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        return torch.from_numpy(x).to("cuda:0")
+
     A_np, B_np = w.operands()
-    if w.dtype == "f32":
-        A = torch.from_numpy(A_np).to("cuda:0")
-        B = torch.from_numpy(B_np).to("cuda:0")
-    else:
-        A = torch.from_numpy(A_np.view("int16")).view(torch.bfloat16).to("cuda:0")
-        B = torch.from_numpy(B_np.view("int16")).view(torch.bfloat16).to("cuda:0")
+    A, B = dev(A_np), dev(B_np)
     del A_np, B_np
-    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+    if w.beta != 0.0:
+        C = dev(w.initial_c())
+    else:
+        C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out == "f32" else torch.bfloat16,
+                        device="cuda:0")
     stream = torch.cuda.current_stream()
     dtype_id = dg.GEMM_DTYPE_F32 if w.dtype == "f32" else dg.GEMM_DTYPE_BF16
     cfg = dg.gemm_select_config(dtype_id, w.M, w.N, w.K)
     splits = dg.gemm_split_k(dtype_id, cfg, w.M, w.N, w.K)
 
+    def step():
+        # with beta != 0 every step accumulates into C again: same work, the
+        # values only grow (they stay finite over these step counts)
+        dg.gemm(A, B, out=C, alpha=w.alpha, beta=w.beta, transa=w.transa, transb=w.transb)
+
     for _ in range(warmup):
-        dg.gemm(A, B, out=C)
+        step()
     torch.cuda.synchronize()
     log("[bench] %s: warmup done (%d), timing %d steps with %s" % (
         name, warmup, steps, dg.gemm_config_name(dtype_id, cfg)))
@@ -104,7 +121,7 @@ def measure(name: str, steps: int, warmup: int):
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
-        dg.gemm(A, B, out=C)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -118,6 +135,8 @@ def measure(name: str, steps: int, warmup: int):
         "workload": name,
         "M": w.M, "N": w.N, "K": w.K,
         "dtype": w.dtype,
+        "op": ("A^T" if w.transa else "A") + "." + ("B^T" if w.transb else "B"),
+        "alpha": w.alpha, "beta": w.beta, "c_dtype": w.out,
         "value": tflops,
         "ms_per_step": ms_per_step,
         "kernel_config": dg.gemm_config_name(dtype_id, cfg),
@@ -139,26 +158,37 @@ def measure(name: str, steps: int, warmup: int):
 
 def cpu_baseline(name: str, budget_s: float = 10.0):
     """The oracle on a bounded row sample of the workload, scaled to TFLOP/s."""
-    import numpy as np
-
     import oracle
-    from dense_gemm_03_amd.workloads import WORKLOADS
 
-    w = WORKLOADS[name]
+    w = _workload(name)
     threads = oracle.default_threads()
     A, B = w.operands()
-    fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+    C0 = w.initial_c() if w.beta != 0.0 else None
+    kind = "f32" if w.dtype == "f32" else "bf16"
+
+    def run(rows):
+        # rows of op(A): leading rows of A, or leading columns of A^T's storage
+        a = np.ascontiguousarray(A[:, :rows] if w.transa else A[:rows])
+        c0 = None
+        if C0 is not None:
+            c0 = C0[:rows].astype(np.float64) if w.out == "f32" else oracle.bf16_bits_to_f64(C0[:rows])
+        t = time.perf_counter()
+        if w.plain:
+            # the plain product alone (no tolerance scale S)
+            (oracle.gemm_f32 if kind == "f32" else oracle.gemm_bf16)(a, B, threads=threads,
+                                                                     with_s=False)
+        else:
+            oracle.gemm_general(a, B, w.alpha, w.beta, c0, w.transa, w.transb, kind=kind,
+                                threads=threads)
+        return time.perf_counter() - t
+
     rows = min(w.M, max(threads, 16))
-    t = time.perf_counter()
-    fn(np.ascontiguousarray(A[:rows]), B, threads=threads, with_s=False)
-    dt = time.perf_counter() - t
+    dt = run(rows)
     # grow the sample to about budget_s seconds of wall time
     target = int(rows * budget_s / max(dt, 1e-3))
     rows2 = max(rows, min(w.M, target - target % threads if target > threads else target))
     if rows2 > rows:
-        t = time.perf_counter()
-        fn(np.ascontiguousarray(A[:rows2]), B, threads=threads, with_s=False)
-        dt = time.perf_counter() - t
+        dt = run(rows2)
         rows = rows2
     flops = 2.0 * rows * w.N * w.K
     return {
@@ -166,7 +196,7 @@ def cpu_baseline(name: str, budget_s: float = 10.0):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "first %d of %d rows of A times all of B (%dx%dx%d, fp64 accumulation), %.1f s"
+        "sample": "first %d of %d rows of op(A) times all of op(B) (%dx%dx%d, fp64 accumulation), %.1f s"
                   % (rows, w.M, rows, w.N, w.K, dt),
     }
 
@@ -174,11 +204,14 @@ def cpu_baseline(name: str, budget_s: float = 10.0):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=PRIMARY)
-    ap.add_argument("--all", action="store_true", help="also time the im2col and tall shapes")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the im2col and tall shapes and the generalised-GEMM variants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true",
+                    help="time only --workload (for per-kernel profiler passes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference kernel "
                          "for the HBM byte counters) and exit")
@@ -208,9 +241,10 @@ def main() -> int:
 
     main_res = measure(args.workload, args.steps, args.warmup)
     also = {}
-    others = [n for n in SECONDARY + (EXTRA if args.all else []) if n != args.workload]
+    others = [] if args.no_also else [
+        n for n in SECONDARY + (EXTRA if args.all else []) if n != args.workload]
     for n in others:
-        also[n] = measure(n, max(5, args.steps // 2), max(2, args.warmup // 2))
+        also[n] = measure(n, max(10, args.steps // 2), max(20, args.warmup))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -240,8 +274,9 @@ def main() -> int:
         },
         "roofline": w["roofline"],
         "cpu_baseline": cpu,
-        "also": {n: {k: r[k] for k in ("value", "ms_per_step", "dtype", "kernel_config", "split_k",
-                                        "roofline", "hbm_gbs")} for n, r in also.items()},
+        "also": {n: {k: r[k] for k in ("value", "ms_per_step", "dtype", "op", "alpha", "beta",
+                                        "c_dtype", "kernel_config", "split_k", "roofline",
+                                        "hbm_gbs")} for n, r in also.items()},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -1,4 +1,5 @@
-"""MI355X-native dense GEMM: C = A . B on gfx950 matrix cores.
+"""MI355X-native dense GEMM on gfx950 matrix cores: C = A . B, and the
+generalised C = alpha * op(A) * op(B) + beta * C with fp32 or bf16 C.
 
 A thin ctypes binding over the C ABI of ``include/gemm.h`` (library
 ``libdense_gemm.so`` next to this file).  The functions of the same names take
@@ -25,10 +26,13 @@ GEMM_ERR_NO_DEVICE = -3
 GEMM_ERR_OUT_OF_MEMORY = -4
 GEMM_DTYPE_F32 = 0
 GEMM_DTYPE_BF16 = 1
+GEMM_OP_N = 0
+GEMM_OP_T = 1
 
 # Every symbol include/gemm.h declares, with its ctypes signature.
-_i64, _p, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_i64, _p, _int, _f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 _GEMM_ARGS = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_GEMM_EX_ARGS = [_int, _int, _int, _int, _i64, _i64, _i64, _f, _p, _i64, _p, _i64, _f, _p, _i64, _p]
 SIGNATURES = {
     "gemm_f32": (_int, _GEMM_ARGS),
     "gemm_bf16": (_int, _GEMM_ARGS),
@@ -39,6 +43,9 @@ SIGNATURES = {
     "gemm_split_k": (_int, [_int, _int, _i64, _i64, _i64]),
     "gemm_f32_with_config": (_int, [_int, _int] + _GEMM_ARGS),
     "gemm_bf16_with_config": (_int, [_int, _int] + _GEMM_ARGS),
+    "gemm_ex": (_int, _GEMM_EX_ARGS),
+    "gemm_ex_with_config": (_int, [_int, _int] + _GEMM_EX_ARGS),
+    "gemm_config_layouts": (_int, [_int, _int]),
 }
 
 _lib = None
@@ -94,6 +101,22 @@ def gemm_bf16_with_config(cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream=
     return load_library().gemm_bf16_with_config(cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
+def gemm_ex(dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+            stream=None) -> int:
+    return load_library().gemm_ex(dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda, B, ldb,
+                                  beta, C, ldc, stream)
+
+
+def gemm_ex_with_config(cfg, split_k, dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda, B,
+                        ldb, beta, C, ldc, stream=None) -> int:
+    return load_library().gemm_ex_with_config(cfg, split_k, dtype_ab, dtype_c, transa, transb, M, N,
+                                              K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_config_layouts(dtype: int, cfg: int) -> int:
+    return load_library().gemm_config_layouts(dtype, cfg)
+
+
 def gemm_status_string(status: int) -> str:
     return load_library().gemm_status_string(status).decode()
 
@@ -120,40 +143,68 @@ def gemm_split_k(dtype: int, cfg: int, M: int, N: int, K: int) -> int:
 def _ld(t) -> int:
     if t.dim() != 2:
         raise ValueError("expected a 2-D tensor, got shape %s" % (tuple(t.shape),))
-    if t.shape[1] > 1 and t.stride(1) != 1:
-        raise ValueError("rows must be contiguous (unit column stride)")
     rows, cols = t.shape
+    if t.numel() == 0:
+        return max(int(cols), 1)   # nothing is read or written: any stride will do
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (unit column stride)")
     return int(t.stride(0)) if rows > 1 else max(int(cols), 1)
 
 
-def gemm(A, B, out=None, cfg: int | None = None, split_k: int = 0, stream=None):
-    """C = A . B for CUDA (HIP) tensors A (M x K) and B (K x N), both float32
-    or both bfloat16; C is float32.  Row-major operands with unit column
-    stride; row strides become the leading dimensions.  Runs on ``stream``
-    (default: torch's current stream) and returns without synchronising."""
+def gemm(A, B, out=None, cfg: int | None = None, split_k: int = 0, stream=None, *,
+         alpha: float = 1.0, beta: float = 0.0, transa: bool = False, transb: bool = False,
+         out_dtype=None):
+    """C = alpha * op(A) . op(B) + beta * C for CUDA (HIP) tensors.
+
+    A and B are both float32 or both bfloat16, stored row-major with unit
+    column stride (row strides become the leading dimensions): A is M x K, or
+    K x M with ``transa``; B is K x N, or N x K with ``transb``.  C (``out``)
+    is float32 or bfloat16 (``out_dtype``, default float32), M x N; it is
+    created when not given (then ``beta`` must be 0).  With the defaults this
+    is the plain product C = A . B (the gemm_f32 / gemm_bf16 entry points);
+    otherwise gemm_ex runs.  Runs on ``stream`` (default: torch's current
+    stream) and returns without synchronising."""
     import torch
 
     if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("A and B must both be float32 or both bfloat16")
     if A.device.type != "cuda" or B.device.type != "cuda":
         raise ValueError("A and B must be GPU tensors")
-    M, K = A.shape
-    K2, N = B.shape
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = (A.shape[1], A.shape[0]) if transa else (A.shape[0], A.shape[1])
+    K2, N = (B.shape[1], B.shape[0]) if transb else (B.shape[0], B.shape[1])
     if K != K2:
-        raise ValueError("inner dimensions differ: %s vs %s" % (tuple(A.shape), tuple(B.shape)))
+        raise ValueError("inner dimensions differ: op(A) is %dx%d, op(B) is %dx%d" % (M, K, K2, N))
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("C must be float32 or bfloat16")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or out.device != A.device:
-        raise ValueError("out must be a float32 (M, N) tensor on A's device")
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing C (out=...)")
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
+        raise ValueError("out must be a %s (%d, %d) tensor on A's device" % (out_dtype, M, N))
     lda, ldb, ldc = _ld(A), _ld(B), _ld(out)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     bf16 = A.dtype == torch.bfloat16
-    args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, stream)
-    if cfg is None:
-        rc = (gemm_bf16 if bf16 else gemm_f32)(*args)
+    plain = (alpha == 1.0 and beta == 0.0 and not transa and not transb
+             and out_dtype == torch.float32)
+    if plain:
+        args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, stream)
+        if cfg is None:
+            rc = (gemm_bf16 if bf16 else gemm_f32)(*args)
+        else:
+            rc = (gemm_bf16_with_config if bf16 else gemm_f32_with_config)(cfg, split_k, *args)
     else:
-        rc = (gemm_bf16_with_config if bf16 else gemm_f32_with_config)(cfg, split_k, *args)
+        args = (GEMM_DTYPE_BF16 if bf16 else GEMM_DTYPE_F32,
+                GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32,
+                GEMM_OP_T if transa else GEMM_OP_N, GEMM_OP_T if transb else GEMM_OP_N,
+                M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta),
+                out.data_ptr(), ldc, stream)
+        rc = gemm_ex(*args) if cfg is None else gemm_ex_with_config(cfg, split_k, *args)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return out

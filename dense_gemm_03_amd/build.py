@@ -21,7 +21,16 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdense_gemm.so")
 
-SOURCES = ["gemm_api.hip", "gemm_f32.hip", "gemm_bf16.hip", "gemm_aux.hip"]
+# (source, object name, extra defines).  gemm_instances.hip is compiled once
+# per input type and operand layout, so the kernel instantiations build in
+# parallel.
+SOURCES = [("gemm_api.hip", "gemm_api", []),
+           ("gemm_tables.hip", "gemm_tables", []),
+           ("gemm_aux.hip", "gemm_aux", [])]
+for _dtype in ("F32", "BF16"):
+    for _layout in ("NN", "NT", "TN", "TT"):
+        SOURCES.append(("gemm_instances.hip", "gemm_%s_%s" % (_dtype.lower(), _layout.lower()),
+                        ["DG_DTYPE_TABLE=DG_%s_TABLE" % _dtype, "DG_LAYOUT=" + _layout]))
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [
@@ -42,16 +51,18 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(item) -> str:
+    src, name, defines = item
+    obj = os.path.join(OBJDIR, name + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-I", INCLUDE, "-I", CSRC,
+           "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; that
     # note is expected.  Anything else is printed.
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if ln.strip() and noise not in ln]
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed on %s:\n%s" % (src, "\n".join(msgs)))
+        raise RuntimeError("hipcc failed on %s (%s):\n%s" % (src, name, "\n".join(msgs)))
     if msgs:
         print("\n".join(msgs), file=sys.stderr)
     return obj

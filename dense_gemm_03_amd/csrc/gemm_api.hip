@@ -173,30 +173,61 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, float **out)
     return GEMM_OK;
 }
 
-int check_args(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-               const void *B, int64_t ldb, const float *C, int64_t ldc)
+int elem_size(int dtype) { return dtype == GEMM_DTYPE_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == GEMM_DTYPE_F32 || dtype == GEMM_DTYPE_BF16; }
+
+// One call, after the public entry points have named its variant.
+struct Call {
+    int dtype;      // of A and B
+    int dtype_c;    // of C
+    int transa, transb;
+    int64_t M, N, K;
+    float alpha, beta;
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    void *C;
+    int64_t ldc;
+};
+
+int check_args(const Call &c)
 {
-    const size_t esz = dtype == GEMM_DTYPE_F32 ? 4 : 2;
-    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_INVALID_ARG;
-    if (lda < (K > 0 ? K : 1) || ldb < (N > 0 ? N : 1) || ldc < (N > 0 ? N : 1))
+    if (!valid_dtype(c.dtype) || !valid_dtype(c.dtype_c)) return GEMM_ERR_INVALID_ARG;
+    if ((c.transa != GEMM_OP_N && c.transa != GEMM_OP_T) ||
+        (c.transb != GEMM_OP_N && c.transb != GEMM_OP_T))
         return GEMM_ERR_INVALID_ARG;
-    if (M > 0 && N > 0 && C == nullptr) return GEMM_ERR_INVALID_ARG;
-    if (M > 0 && N > 0 && K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_ARG;
-    if ((uintptr_t)A % esz || (uintptr_t)B % esz || (uintptr_t)C % 4) return GEMM_ERR_INVALID_ARG;
+    if (c.M < 0 || c.N < 0 || c.K < 0) return GEMM_ERR_INVALID_ARG;
+    if (c.M > kMaxDim || c.N > kMaxDim || c.K > kMaxDim) return GEMM_ERR_INVALID_ARG;
+    // Row lengths of the stored matrices: A is M x K (or K x M when
+    // transposed), B is K x N (or N x K), C is M x N.
+    const int64_t a_row = c.transa == GEMM_OP_T ? c.M : c.K;
+    const int64_t b_row = c.transb == GEMM_OP_T ? c.K : c.N;
+    if (c.lda < (a_row > 0 ? a_row : 1) || c.ldb < (b_row > 0 ? b_row : 1) ||
+        c.ldc < (c.N > 0 ? c.N : 1))
+        return GEMM_ERR_INVALID_ARG;
+    if (c.M > 0 && c.N > 0 && c.C == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (c.M > 0 && c.N > 0 && c.K > 0 && (c.A == nullptr || c.B == nullptr))
+        return GEMM_ERR_INVALID_ARG;
+    const uintptr_t esz = (uintptr_t)elem_size(c.dtype);
+    if ((uintptr_t)c.A % esz || (uintptr_t)c.B % esz ||
+        (uintptr_t)c.C % (uintptr_t)elem_size(c.dtype_c))
+        return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
 }
 
-int run(int dtype, int forced_cfg, int forced_split, int64_t M, int64_t N, int64_t K,
-        const void *A, int64_t lda, const void *B, int64_t ldb, float *C, int64_t ldc,
-        hipStream_t stream)
+int run(const Call &call, int forced_cfg, int forced_split, hipStream_t stream)
 {
-    int rc = check_args(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+    int rc = check_args(call);
     if (rc != GEMM_OK) return rc;
     int count = 0;
-    const TileConfig *tab = table(dtype, &count);
+    const TileConfig *tab = table(call.dtype, &count);
     if (tab == nullptr) return GEMM_ERR_INVALID_ARG;
     if (forced_cfg >= count) return GEMM_ERR_INVALID_ARG;
+    const int layout = call.transa * 2 + call.transb;
+    if (forced_cfg >= 0 && tab[forced_cfg].fn[layout][0] == nullptr) return GEMM_ERR_INVALID_ARG;
+    const int64_t M = call.M, N = call.N, K = call.K;
     if (M == 0 || N == 0) return GEMM_OK;
 
     int device = -1;
@@ -204,22 +235,29 @@ int run(int dtype, int forced_cfg, int forced_split, int64_t M, int64_t N, int64
         (void)hipGetLastError();
         return GEMM_ERR_NO_DEVICE;
     }
-    if (K == 0) return launch_zero_fill((int)M, (int)N, C, ldc, stream) == hipSuccess ? GEMM_OK
-                                                                                      : GEMM_ERR_HIP;
+    const int out_bf16 = call.dtype_c == GEMM_DTYPE_BF16;
+    // The product term vanishes (empty sum, or alpha == 0): A and B are not
+    // read and C := beta * C.
+    if (K == 0 || call.alpha == 0.0f)
+        return launch_scale((int)M, (int)N, call.C, call.ldc, call.beta, out_bf16, stream) ==
+                       hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
 
-    const int ci = forced_cfg >= 0 ? forced_cfg : select_config(dtype, M, N, K);
+    const int ci = forced_cfg >= 0 ? forced_cfg : select_config(call.dtype, M, N, K);
     const TileConfig &cfg = tab[ci];
+    if (cfg.fn[layout][0] == nullptr) return GEMM_ERR_INVALID_ARG;
     int splits = 1, kps = 0;
     plan_split(cfg, M, N, K, forced_split, &splits, &kps);
 
     KernelArgs a{};
-    a.A = A;
-    a.B = B;
-    a.C = C;
+    a.A = call.A;
+    a.B = call.B;
+    a.C = call.C;
     a.ws = nullptr;
-    a.lda = lda;
-    a.ldb = ldb;
-    a.ldc = ldc;
+    a.lda = call.lda;
+    a.ldb = call.ldb;
+    a.ldc = call.ldc;
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
@@ -228,28 +266,43 @@ int run(int dtype, int forced_cfg, int forced_split, int64_t M, int64_t N, int64
     a.splits = splits;
     a.k_per_split = kps;
     a.group_m = cfg.group_m;
+    a.alpha = call.alpha;
+    a.beta = call.beta;
+    a.out_bf16 = out_bf16;
     if (splits > 1) {
         rc = get_workspace(device, stream, (size_t)splits * (size_t)M * (size_t)N * sizeof(float),
                            &a.ws);
         if (rc != GEMM_OK) return rc;
     }
 
-    const int vec = dtype == GEMM_DTYPE_F32 ? 4 : 8;
-    const bool aligned = lda % vec == 0 && ldb % vec == 0 && (uintptr_t)A % 16 == 0 &&
-                         (uintptr_t)B % 16 == 0;
+    const int64_t esz = elem_size(call.dtype);
+    const int vec = (int)(16 / esz);
+    const bool aligned = call.lda % vec == 0 && call.ldb % vec == 0 &&
+                         (uintptr_t)call.A % 16 == 0 && (uintptr_t)call.B % 16 == 0;
     // The direct-load path addresses a tile with per-thread 32-bit byte
-    // offsets from the tile origin: rows 0..BM-1 of A and 0..BK-1 of B.
-    const int64_t esz = dtype == GEMM_DTYPE_F32 ? 4 : 2;
-    a.direct_ok = ((int64_t)cfg.bm * lda * esz < (int64_t(1) << 32)) &&
-                  ((int64_t)cfg.bk * ldb * esz < (int64_t(1) << 32));
+    // offsets from the tile origin, over the tile's memory rows: BM (A as
+    // given) or BK (A transposed) rows of A, BK (B as given) or BN (B
+    // transposed) rows of B.
+    const int64_t a_rows = call.transa == GEMM_OP_T ? cfg.bk : cfg.bm;
+    const int64_t b_rows = call.transb == GEMM_OP_T ? cfg.bn : cfg.bk;
+    a.direct_ok = (a_rows * call.lda * esz < (int64_t(1) << 32)) &&
+                  (b_rows * call.ldb * esz < (int64_t(1) << 32));
     const int64_t blocks = (int64_t)splits * a.tiles_m * a.tiles_n;
     if (blocks > INT32_MAX) return GEMM_ERR_INVALID_ARG;
-    launch_fn fn = aligned ? cfg.aligned : cfg.unaligned;
+    launch_fn fn = cfg.fn[layout][aligned ? 0 : 1];
     if (fn(a, (int)blocks, stream) != hipSuccess) return GEMM_ERR_HIP;
-    if (splits > 1 &&
-        launch_splitk_reduce(a.ws, splits, (int)M, (int)N, C, ldc, stream) != hipSuccess)
+    if (splits > 1 && launch_splitk_reduce(a.ws, splits, (int)M, (int)N, call.C, call.ldc,
+                                           call.alpha, call.beta, out_bf16, stream) != hipSuccess)
         return GEMM_ERR_HIP;
     return GEMM_OK;
+}
+
+// The plain product C := A . B with fp32 C.
+Call plain_call(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                const void *B, int64_t ldb, float *C, int64_t ldc)
+{
+    return Call{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_N, M, N, K, 1.0f, 0.0f,
+                A, lda, B, ldb, C, ldc};
 }
 
 }  // namespace
@@ -260,13 +313,13 @@ extern "C" {
 int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
              int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
 {
-    return dg::run(GEMM_DTYPE_F32, -1, 0, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return dg::run(dg::plain_call(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc), -1, 0, stream);
 }
 
 int gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
               int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
 {
-    return dg::run(GEMM_DTYPE_BF16, -1, 0, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return dg::run(dg::plain_call(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc), -1, 0, stream);
 }
 
 int gemm_f32_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K, const float *A,
@@ -274,7 +327,8 @@ int gemm_f32_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K, 
                          hipStream_t stream)
 {
     if (cfg < 0) return GEMM_ERR_INVALID_ARG;
-    return dg::run(GEMM_DTYPE_F32, cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return dg::run(dg::plain_call(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc), cfg, split_k,
+                   stream);
 }
 
 int gemm_bf16_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K,
@@ -282,7 +336,39 @@ int gemm_bf16_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K,
                           float *C, int64_t ldc, hipStream_t stream)
 {
     if (cfg < 0) return GEMM_ERR_INVALID_ARG;
-    return dg::run(GEMM_DTYPE_BF16, cfg, split_k, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return dg::run(dg::plain_call(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc), cfg, split_k,
+                   stream);
+}
+
+int gemm_ex(int dtype_ab, int dtype_c, int transa, int transb, int64_t M, int64_t N, int64_t K,
+            float alpha, const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
+            void *C, int64_t ldc, hipStream_t stream)
+{
+    return dg::run(dg::Call{dtype_ab, dtype_c, transa, transb, M, N, K, alpha, beta, A, lda, B,
+                            ldb, C, ldc},
+                   -1, 0, stream);
+}
+
+int gemm_ex_with_config(int cfg, int split_k, int dtype_ab, int dtype_c, int transa, int transb,
+                        int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                        const void *B, int64_t ldb, float beta, void *C, int64_t ldc,
+                        hipStream_t stream)
+{
+    if (cfg < 0) return GEMM_ERR_INVALID_ARG;
+    return dg::run(dg::Call{dtype_ab, dtype_c, transa, transb, M, N, K, alpha, beta, A, lda, B,
+                            ldb, C, ldc},
+                   cfg, split_k, stream);
+}
+
+int gemm_config_layouts(int dtype, int cfg)
+{
+    int count = 0;
+    const dg::TileConfig *tab = dg::table(dtype, &count);
+    if (!tab || cfg < 0 || cfg >= count) return GEMM_ERR_INVALID_ARG;
+    int mask = 0;
+    for (int l = 0; l < 4; ++l)
+        if (tab[cfg].fn[l][0] != nullptr) mask |= 1 << l;
+    return mask;
 }
 
 const char *gemm_status_string(int status)

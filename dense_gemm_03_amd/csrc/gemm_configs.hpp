@@ -1,6 +1,16 @@
-// Host-side description of the tile table: one entry per compiled kernel
-// configuration, with launchers for the aligned (16-byte vector loads) and
-// the unaligned (element-wise loads) variant.
+// Host-side description of the tile table: one entry per kernel
+// configuration, with launchers for each operand layout it is built for and,
+// per layout, an aligned (16-byte vector loads) and an unaligned (element-wise
+// loads) variant.
+//
+// The entries are listed once, in the X-macro lists below.  Each list item is
+//   X(NAME, BF16, BM, BN, BK, WM, WN, STAGES, GROUP_M, LAYOUTS)
+// with the tile shape (BM x BN block, BK k-tile), the wave grid (WM x WN
+// waves), the number of LDS stages, the raster group height, and LAYOUTS =
+// ALL (kernels for all four combinations of transposed operands) or NN (only
+// A and B as given).  The kernels of one input type and operand layout are
+// instantiated by one compilation of gemm_instances.hip, so the slices compile
+// in parallel; the tables (gemm_tables.hip) only take their addresses.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,40 +22,103 @@ namespace dg {
 
 typedef hipError_t (*launch_fn)(const KernelArgs &args, int blocks, hipStream_t stream);
 
+// Operand layout combinations, indexed by transa * 2 + transb.
+enum { LAYOUT_NN = 0, LAYOUT_NT = 1, LAYOUT_TN = 2, LAYOUT_TT = 3 };
+
 struct TileConfig {
     const char *name;
     int bm, bn, bk;
     int threads;
     int stages;
     int group_m;
-    launch_fn aligned;    // needs 16-byte aligned rows of A and B
-    launch_fn unaligned;  // element-wise loads, any alignment of the element type
+    // fn[layout][0]: needs 16-byte aligned rows of A and B; fn[layout][1]:
+    // element-wise loads, any alignment of the element type.  nullptr where
+    // the entry has no kernel for that layout.
+    launch_fn fn[4][2];
 };
 
-template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, bool ALIGNED>
-hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
-{
-    hipLaunchKernelGGL((gemm_kernel<BF16, BM, BN, BK, WM, WN, STAGES, ALIGNED>), dim3(blocks),
-                       dim3(64 * WM * WN), 0, stream, args);
-    return hipGetLastError();
-}
+// Declared here; defined in gemm_launch.hpp and explicitly instantiated by the
+// compilations of gemm_instances.hip.
+template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
+          bool ALIGNED>
+hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 
-// One table entry: a name, the tile shape (BM x BN block, BK k-tile), the wave
-// grid (WM x WN waves), the number of LDS stages and the raster group height.
-#define DG_TILE_CONFIG(NAME, BF16, BM, BN, BK, WM, WN, STAGES, GROUP_M)                     \
-    TileConfig                                                                             \
-    {                                                                                      \
-        NAME, BM, BN, BK, 64 * (WM) * (WN), STAGES, GROUP_M,                               \
-            &launch_gemm<BF16, BM, BN, BK, WM, WN, STAGES, true>,                          \
-            &launch_gemm<BF16, BM, BN, BK, WM, WN, STAGES, false>                          \
-    }
+// Memory orientation of op(A) / op(B) per layout combination: A as given is
+// k-contiguous, A^T (stored K x M) outer-contiguous; B as given is
+// outer-contiguous, B^T (stored N x K) k-contiguous.
+#define DG_LA_NN ::dg::KMAJOR
+#define DG_LB_NN ::dg::MNMAJOR
+#define DG_LA_NT ::dg::KMAJOR
+#define DG_LB_NT ::dg::KMAJOR
+#define DG_LA_TN ::dg::MNMAJOR
+#define DG_LB_TN ::dg::MNMAJOR
+#define DG_LA_TT ::dg::MNMAJOR
+#define DG_LB_TT ::dg::KMAJOR
 
-// Tables, defined in gemm_f32.hip and gemm_bf16.hip.
+// The tile tables.  The shape classes they serve (tile sizes per task, "How to
+// do even better" on the GEMM page): square/large blocks for big M and N, a
+// wide-N block with split-K for M of a few dozen rows and long K (the im2col
+// weight-gradient shape), a tall block for N of a few dozen columns, and a
+// small block when the output holds too few large blocks to fill 256 compute
+// units.  Every entry the dispatcher can choose is built for all layouts.
+#define DG_F32_TABLE(X)                                                     \
+    X("f32_256x128_w4x2_s2", false, 256, 128, 32, 4, 2, 2, 8, ALL)          \
+    X("f32_128x128_w2x2_s2", false, 128, 128, 32, 2, 2, 2, 8, NN)           \
+    X("f32_256x256_w4x2_s2", false, 256, 256, 32, 4, 2, 2, 8, ALL)          \
+    X("f32_64x64_w2x2_s2", false, 64, 64, 32, 2, 2, 2, 8, ALL)              \
+    X("f32_64x64_w2x2_s3", false, 64, 64, 32, 2, 2, 3, 8, ALL)              \
+    X("f32_64x256_w1x4_s3", false, 64, 256, 32, 1, 4, 3, 1, ALL)            \
+    X("f32_64x256_w1x4_s4", false, 64, 256, 32, 1, 4, 4, 1, NN)             \
+    X("f32_64x128_w1x2_s4", false, 64, 128, 32, 1, 2, 4, 1, NN)             \
+    X("f32_256x64_w4x1_s3", false, 256, 64, 32, 4, 1, 3, 8, NN)             \
+    X("f32_128x64_w2x1_s2", false, 128, 64, 32, 2, 1, 2, 8, ALL)            \
+    X("f32_128x64_w2x2_s2", false, 128, 64, 32, 2, 2, 2, 8, ALL)            \
+    X("f32_128x64_w4x1_s2", false, 128, 64, 32, 4, 1, 2, 8, NN)             \
+    X("f32_64x64_w1x1_s2", false, 64, 64, 32, 1, 1, 2, 8, NN)               \
+    X("f32_64x64_w1x1_s4", false, 64, 64, 32, 1, 1, 4, 8, NN)               \
+    X("f32_64x256_w1x4_s2", false, 64, 256, 32, 1, 4, 2, 1, NN)
+
+#define DG_BF16_TABLE(X)                                                    \
+    X("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8, NN)        \
+    X("bf16_256x256x64_w2x4_s2", true, 256, 256, 64, 2, 4, 2, 8, NN)        \
+    X("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 4, ALL)       \
+    X("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8, ALL)       \
+    X("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8, NN)        \
+    X("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8, ALL)
+
+// Launcher pointers of one entry and layout: both alignments, or nullptr.
+#define DG_FNS(BF16, BM, BN, BK, WM, WN, S, L)                                               \
+    {&launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L, true>,                  \
+     &launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L, false>}
+#define DG_NOFNS {nullptr, nullptr}
+#define DG_FNS_ALL_NN(...) DG_FNS(__VA_ARGS__, NN)
+#define DG_FNS_ALL_NT(...) DG_FNS(__VA_ARGS__, NT)
+#define DG_FNS_ALL_TN(...) DG_FNS(__VA_ARGS__, TN)
+#define DG_FNS_ALL_TT(...) DG_FNS(__VA_ARGS__, TT)
+#define DG_FNS_NN_NN(...) DG_FNS(__VA_ARGS__, NN)
+#define DG_FNS_NN_NT(...) DG_NOFNS
+#define DG_FNS_NN_TN(...) DG_NOFNS
+#define DG_FNS_NN_TT(...) DG_NOFNS
+
+// One table entry from one list item.
+#define DG_TABLE_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                        \
+    TileConfig{NAME, BM, BN, BK, 64 * (WM) * (WN), S, G,                                    \
+               {DG_FNS_##LAYOUTS##_NN(BF16, BM, BN, BK, WM, WN, S),                         \
+                DG_FNS_##LAYOUTS##_NT(BF16, BM, BN, BK, WM, WN, S),                         \
+                DG_FNS_##LAYOUTS##_TN(BF16, BM, BN, BK, WM, WN, S),                         \
+                DG_FNS_##LAYOUTS##_TT(BF16, BM, BN, BK, WM, WN, S)}},
+
+// Tables, defined in gemm_tables.hip.
 const TileConfig *f32_configs(int *count);
 const TileConfig *bf16_configs(int *count);
 
-hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, float *C, int64_t ldc,
-                                hipStream_t stream);
-hipError_t launch_zero_fill(int M, int N, float *C, int64_t ldc, hipStream_t stream);
+// Split-K reduce: C := alpha * (sum of the slices, in slice order) + beta * C
+// (C read only when beta != 0), stored as fp32 or bf16.
+hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, void *C, int64_t ldc,
+                                float alpha, float beta, int out_bf16, hipStream_t stream);
+// C := beta * C over the M x N window, or C := 0 when beta == 0 (C not read):
+// the whole result when K == 0 or alpha == 0.
+hipError_t launch_scale(int M, int N, void *C, int64_t ldc, float beta, int out_bf16,
+                        hipStream_t stream);
 
 }  // namespace dg

@@ -1,18 +1,24 @@
-// Device code of the dense GEMM: C = A . B on gfx950 matrix cores.
+// Device code of the dense GEMM on gfx950 matrix cores:
 //
-// One kernel template serves both input types:
+//     C := alpha * op(A) * op(B) + beta * C,   op(X) = X or X^T
+//
+// the generalised product of "Learning to develop for GPUs through the GEMM
+// operation", section "Generalized matrix multiplication GEMM"; the plain
+// product C = A.B of its section "Matrix product" is alpha = 1, beta = 0 and
+// no transposes.  One kernel template serves both input types:
 //   fp32 inputs  -> v_mfma_f32_32x32x2_f32    (fp32 products, fp32 accumulate)
 //   bf16 inputs  -> v_mfma_f32_32x32x16_bf16  (exact products, fp32 accumulate)
+// and writes C as fp32 or as bf16 (rounded to nearest, ties to even).
 //
-// Structure (the tiling of "Learning to develop for GPUs through the GEMM
-// operation", sections "Making the GPU implementation better" through "How to
-// do even better", rebuilt for CDNA4 wave64 matrix cores):
+// Structure (the tiling of the GEMM page, sections "Making the GPU
+// implementation better" through "How to do even better", rebuilt for CDNA4
+// wave64 matrix cores):
 //   * each workgroup owns a BM x BN block of C and walks K in tiles of BK;
-//   * tiles of A (BM x BK) and B (BK x BN) stream from HBM into a ring of LDS
-//     stages with direct global->LDS 16-byte loads, several tiles ahead of
-//     the products, one barrier per tile;
-//   * LDS rows are XOR-swizzled so the 16-byte fragment reads of a wave spread
-//     over all 64 banks ("How to do even better": shifting rows across banks
+//   * tiles of op(A) (BM x BK) and op(B) (BK x BN) stream from HBM into a ring
+//     of LDS stages with direct global->LDS 16-byte loads, several tiles ahead
+//     of the products, one barrier per tile;
+//   * LDS rows are XOR-swizzled so the fragment reads of a wave spread over
+//     all 64 banks ("How to do even better": shifting rows across banks
 //     removes the conflicts);
 //   * each wave owns a (BM/WM) x (BN/WN) sub-block held as 32x32 accumulator
 //     fragments in registers and reuses every A and B fragment it reads across
@@ -23,13 +29,21 @@
 //     matrix (through registers) and stores only inside it; the choice is
 //     uniform over the workgroup.
 //
+// Operand tiles.  Both operands are described by one template (OpTile): a
+// tile of OUTER (m for A, n for B) by BK elements, stored in memory either
+// k-contiguous (KMAJOR: A as given, or B given transposed as N x K) or
+// outer-contiguous (MNMAJOR: B as given, or A given transposed as K x M).
+// LDS keeps the memory orientation, so the global->LDS copy is a plain
+// 16-byte copy either way; the fragment read adapts: a KMAJOR fragment is one
+// 16-byte LDS read per lane, an MNMAJOR one is 4 single-float reads (fp32) or
+// two LDS transpose reads (bf16).
+//
 // k-slot assignment.  A 32x32 MFMA pairs, in each of its k slots, the A value a
 // lane supplies with the B value the same-numbered lane half supplies.  Lanes
 // 0-31 feed one slot group and lanes 32-63 the other.  Within one tile, lane
-// half h takes the contiguous k range [h*BK/2, (h+1)*BK/2), so a lane's A
-// values for a whole tile are contiguous in an LDS row and come in 16-byte
-// reads.  B is laid out so that the same k reaches the same slot, so every
-// product A[i][k]*B[k][j] of the definition is formed exactly once.
+// half h takes the contiguous k range [h*BK/2, (h+1)*BK/2) of both operands,
+// so every product op(A)[i][k]*op(B)[k][j] of the definition is formed
+// exactly once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,12 +59,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// Memory orientation of an operand tile.
+enum Layout { KMAJOR = 0, MNMAJOR = 1 };
+
 // Arguments of one launch.  The grid is 1-D: splits * tiles_m * tiles_n blocks.
 struct KernelArgs {
-    const void *A;
-    const void *B;
-    float *C;       // final output (splits == 1)
-    float *ws;      // split-K partial sums, slice-major, ld = N (splits > 1)
+    const void *A;    // op(A) = A (M x K, k-contiguous) or A^T (A stored K x M)
+    const void *B;    // op(B) = B (K x N, n-contiguous) or B^T (B stored N x K)
+    void *C;          // final output (splits == 1): fp32, or bf16 when out_bf16
+    float *ws;        // split-K partial sums, slice-major, ld = N (splits > 1)
     int64_t lda, ldb, ldc;
     int M, N, K;
     int tiles_m, tiles_n;
@@ -58,96 +75,119 @@ struct KernelArgs {
     int k_per_split;  // K extent of a slice, a multiple of the k-tile
     int group_m;      // tile rows per raster group (L2 reuse of B columns)
     int direct_ok;    // per-thread byte offsets of a tile fit in 32 bits
+    float alpha, beta;
+    int out_bf16;     // C holds bf16 bit patterns (1) or fp32 (0)
 };
 
-// Tile geometry and LDS layout of one configuration.
+// ----------------------------------------------------------- operand tile --
+
+// One operand tile in LDS: OUTER x BK elements of op(A) (OUTER = BM) or of
+// op(B) (OUTER = BN).
 //
 // LDS banks (measured on gfx950 with the bank-conflict counter): 64 banks of
 // 4 bytes, and a 16-byte read serves 16 lanes per pass, so the 16 addresses of
 // a pass must cover 256 bytes that fall on distinct banks.
-template <bool BF16_, int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+//
+//   KMAJOR:  OUTER rows of BK elements (64 or 128 bytes).  Chunk c of row r
+//            sits in slot c ^ ((r / RPL) % CPR), RPL rows sharing a 256-byte
+//            bank line: the 16 rows a 16-lane pass reads at one chunk cover
+//            all 64 banks once, and so do the writes.
+//   MNMAJOR: BK rows of OUTER elements, row-major as in memory.
+//     fp32:  the two 32-float halves of each 64-float group swap places in
+//            rows with bit 4 set, so the two lane halves of a fragment read
+//            (rows k and k+16, same columns) use different banks.
+//     bf16:  read with the LDS transpose load, 4 rows x 16 columns per 16
+//            lanes; the 64-byte segments of row k are XOR-permuted by (k & 3)
+//            so those 4 rows land on 4 different bank quarters.
+template <bool BF16_, int OUTER_, int BK_, int LAYOUT_, int NT_, int NW_>
+struct OpTile {
+    static constexpr bool BF16 = BF16_;
+    using In = typename std::conditional<BF16, uint16_t, float>::type;
+    static constexpr int OUTER = OUTER_, BK = BK_, LAYOUT = LAYOUT_, NT = NT_, NW = NW_;
+    static constexpr int ES = (int)sizeof(In);
+    static constexpr int VEC = 16 / ES;                   // elements per 16-byte chunk
+    static constexpr int ROWS = LAYOUT == KMAJOR ? OUTER : BK;
+    static constexpr int ROW_BYTES = (LAYOUT == KMAJOR ? BK : OUTER) * ES;
+    static constexpr int BYTES = ROWS * ROW_BYTES;
+    static constexpr int CPR = ROW_BYTES / 16;            // 16-byte chunks per row
+    static constexpr int CHUNKS = ROWS * CPR;
+    static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly over the threads");
+    static constexpr int PER_THREAD = CHUNKS / NT;
+    // Direct global->LDS loads write 64 lanes x 16 bytes = 1 KiB contiguous
+    // LDS bytes per instruction; the tile is cut into such pieces.
+    static constexpr int PIECES = BYTES / 1024;
+    static_assert(PIECES % NW == 0, "direct loads must divide over the waves");
+    static_assert(ROW_BYTES <= 1024 && 1024 % ROW_BYTES == 0, "rows must tile a 1 KiB piece");
+    static constexpr int ROWS_PER_PIECE = 1024 / ROW_BYTES;
+    static constexpr int RPL = 256 / ROW_BYTES;           // KMAJOR rows per bank line
+    static_assert(LAYOUT != KMAJOR || CPR * RPL == 16, "k-contiguous rows of 64 or 128 bytes");
+    static constexpr int SEGMASK = (OUTER / 32 >= 4) ? 3 : (OUTER / 32 - 1);
+    static_assert(LAYOUT != MNMAJOR || BF16 || (OUTER % 64 == 0 && BK == 32),
+                  "fp32 outer-contiguous tiles: OUTER % 64 == 0, BK == 32");
+    static_assert(LAYOUT != MNMAJOR || !BF16 || (OUTER % 32 == 0 && (OUTER & (OUTER - 1)) == 0),
+                  "bf16 outer-contiguous tiles: a power-of-two count of 32-column segments");
+
+    // Byte offset of element `e` of LDS row `row` (e a multiple of 4 for the
+    // bf16 MNMAJOR transpose reads, of VEC for KMAJOR).
+    static __device__ __forceinline__ int off(int row, int e)
+    {
+        if constexpr (LAYOUT == KMAJOR)
+            return row * ROW_BYTES + (((e / VEC) ^ ((row / RPL) % CPR)) << 4);
+        else if constexpr (BF16)
+            return row * ROW_BYTES + (((e >> 5) ^ (row & SEGMASK)) << 6) + ((e & 31) << 1);
+        else
+            return row * ROW_BYTES + ((e ^ (((row >> 4) & 1) << 5)) << 2);
+    }
+
+    // Logical element held at the 16-byte-aligned physical element position
+    // `phys` of LDS row `row`: the inverse of off(), which is the same XOR.
+    static __device__ __forceinline__ int logical(int row, int phys)
+    {
+        if constexpr (LAYOUT == KMAJOR)
+            return ((phys / VEC) ^ ((row / RPL) % CPR)) * VEC;
+        else if constexpr (BF16)
+            return (((phys >> 5) ^ (row & SEGMASK)) << 5) | (phys & 31);
+        else
+            return phys ^ (((row >> 4) & 1) << 5);
+    }
+
+    // LDS reads per fragment and step.
+    static constexpr int READS = LAYOUT == KMAJOR ? 1 : (BF16 ? 2 : VEC);
+};
+
+// Tile geometry of one configuration.
+template <bool BF16_, int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int LA_, int LB_>
 struct Geo {
     static constexpr bool BF16 = BF16_;
     using In = typename std::conditional<BF16, uint16_t, float>::type;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int STAGES = STAGES_;
-    static constexpr int ES = (int)sizeof(In);        // element bytes
-    static constexpr int VEC = 16 / ES;               // elements per 16-byte chunk
-    static constexpr int NW = WM * WN;                // waves
-    static constexpr int NT = 64 * NW;                // threads per workgroup
+    static constexpr int STAGES = STAGES_, LA = LA_, LB = LB_;
+    static constexpr int ES = (int)sizeof(In);         // element bytes
+    static constexpr int VEC = 16 / ES;                // elements per 16-byte chunk
+    static constexpr int NW = WM * WN;                 // waves
+    static constexpr int NT = 64 * NW;                 // threads per workgroup
     static constexpr int WTM = BM / WM, WTN = BN / WN; // wave sub-block
     static constexpr int FM = WTM / 32, FN = WTN / 32; // 32x32 fragments per wave
-    static constexpr int KH = BK / 2;                 // k values per lane half and tile
-    static constexpr int KS = VEC;                    // k values per lane and step (one 16-byte read)
-    static constexpr int STEPS = KH / KS;             // fragment steps per tile
+    static constexpr int KH = BK / 2;                  // k values per lane half and tile
+    static constexpr int KS = VEC;                     // k values per lane and step
+    static constexpr int STEPS = KH / KS;              // fragment steps per tile
     static_assert(KH % KS == 0 && STEPS >= 2, "a tile needs at least two fragment steps");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave sub-block must be whole fragments");
 
-    // MFMAs and LDS fragment reads per step and wave.
+    using TA = OpTile<BF16, BM, BK, LA, NT, NW>;
+    using TB = OpTile<BF16, BN, BK, LB, NT, NW>;
+    static constexpr int A_BYTES = TA::BYTES;
+    static constexpr int STAGE_BYTES = TA::BYTES + TB::BYTES;
+
+    // MFMAs and LDS fragment reads per step and wave; direct loads per tile
+    // and wave.
     static constexpr int N_MMA = BF16 ? FM * FN : KS * FM * FN;
-    static constexpr int N_DS = FM + (BF16 ? 2 * FN : KS * FN);
+    static constexpr int N_DS = FM * TA::READS + FN * TB::READS;
+    static constexpr int LOADS_PER_TILE = (TA::PIECES + TB::PIECES) / NW;
 
-    // A tile: BM rows of BK elements (ACH chunks of 16 bytes).  Chunk c of row
-    // r sits in slot c ^ ((r / RPL) % ACH), RPL rows sharing one 256-byte bank
-    // line: the 16 rows read at one chunk by a 16-lane pass then cover all 64
-    // banks once, and so do the writes.
-    static constexpr int A_ROW_BYTES = BK * ES;
-    static constexpr int ACH = A_ROW_BYTES / 16;
-    static constexpr int RPL = 256 / A_ROW_BYTES;
-    static_assert(ACH * RPL == 16, "A rows of 64 or 128 bytes");
-    static constexpr int A_BYTES = BM * A_ROW_BYTES;
-    static constexpr int A_CHUNKS = BM * ACH;
-    static_assert(A_CHUNKS % NT == 0, "A chunks must divide evenly over the threads");
-    static constexpr int A_PER_THREAD = A_CHUNKS / NT;
-
-    // B tile: BK rows of BN elements, row-major as in memory.
-    //   fp32: the two 32-float halves of each 64-float group swap places in
-    //         rows with bit 4 set, so the two lane halves of a fragment read
-    //         (rows k and k+16, same columns) use different banks.
-    //   bf16: read with the LDS transpose load, 4 rows x 16 columns per
-    //         16 lanes; the 64-byte segments of row k are XOR-permuted by
-    //         (k & 3) so those 4 rows land on 4 different bank quarters.
-    static constexpr int B_ROW_BYTES = BN * ES;
-    static constexpr int B_BYTES = BK * B_ROW_BYTES;
-    static constexpr int B_CHUNKS = BK * BN / VEC;
-    static_assert(B_CHUNKS % NT == 0, "B chunks must divide evenly over the threads");
-    static constexpr int B_PER_THREAD = B_CHUNKS / NT;
-    static constexpr int B_SEGMASK = (BN / 32 >= 4) ? 3 : (BN / 32 - 1);
-    static_assert(BF16 || (BN % 64 == 0 && BK == 32), "fp32 B swizzle: BN % 64 == 0, BK == 32");
-    static_assert(!BF16 || BN % 32 == 0, "bf16 B segments are 32 columns wide");
-
-    // Direct global->LDS loads write 64 lanes x 16 bytes = 1 KiB contiguous
-    // LDS bytes per instruction; the tiles are cut into such pieces.
-    static constexpr int A_PIECES = A_BYTES / 1024;
-    static constexpr int B_PIECES = B_BYTES / 1024;
-    static constexpr int A_ROWS_PER_PIECE = 1024 / A_ROW_BYTES;
-    static constexpr int B_LANES_PER_ROW = B_ROW_BYTES / 16;
-    static_assert(A_PIECES % NW == 0 && B_PIECES % NW == 0, "direct loads must divide over waves");
-    static_assert(1024 % B_ROW_BYTES == 0, "a B row must fit a 1 KiB piece evenly");
-    static constexpr int LOADS_PER_TILE = (A_PIECES + B_PIECES) / NW;  // per wave
-
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
     static_assert(LOADS_PER_TILE * (STAGES - 2) <= 63, "vmcnt counts at most 63 loads");
-
-    // Byte offset of 16-byte chunk `chunk` of A row `row` in a stage.
-    static __device__ __forceinline__ int a_off(int row, int chunk)
-    {
-        return row * A_ROW_BYTES + ((chunk ^ ((row / RPL) % ACH)) << 4);
-    }
-
-    // Byte offset of element (k, n) of the B tile in a stage (n a multiple of
-    // 4, so an 8- or 16-byte access stays inside one swizzle unit).
-    static __device__ __forceinline__ int b_off(int k, int n)
-    {
-        if constexpr (BF16) {
-            const int seg = (n >> 5) ^ (k & B_SEGMASK);
-            return k * B_ROW_BYTES + (seg << 6) + ((n & 31) << 1);
-        } else {
-            return k * B_ROW_BYTES + ((n ^ (((k >> 4) & 1) << 5)) << 2);
-        }
-    }
 };
 
 // ------------------------------------------------------------ small helpers --
@@ -212,20 +252,29 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p)
 // bits 3:0 and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
 
-// Masked 16-byte chunk: elements [k, k+VEC) of one row, zero where the row is
-// outside the matrix (row_ok false) or k+e >= kend.  Never dereferences an
-// address outside the matrix.
+// Masked 16-byte chunk: elements [e0, e0+VEC) of one row, zero where the row
+// is outside the matrix (row_ok false) or e0+e >= eend.  Never dereferences
+// an address outside the matrix.
 template <typename In, int VEC, bool ALIGNED>
-__device__ __forceinline__ u32x4 load_chunk_masked(const In *row, bool row_ok, int k, int kend)
+__device__ __forceinline__ u32x4 load_chunk_masked(const In *row, bool row_ok, int e0, int eend)
 {
-    if (ALIGNED && row_ok && k + VEC <= kend) return load16(row + k);
+    if (ALIGNED && row_ok && e0 + VEC <= eend) return load16(row + e0);
     union {
         u32x4 v;
         In e[VEC];
     } u;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) u.e[e] = (row_ok && k + e < kend) ? row[k + e] : In(0);
+    for (int e = 0; e < VEC; ++e) u.e[e] = (row_ok && e0 + e < eend) ? row[e0 + e] : In(0);
     return u.v;
+}
+
+// fp32 -> bf16 bit pattern, rounded to nearest with ties to even; a NaN stays
+// a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 // Map a linear block id to (slice, tile row, tile column).
@@ -267,12 +316,40 @@ struct BlockCtx {
 };
 
 // Fragments of one step: per 32-row A fragment 16 bytes (4 fp32 or 8 bf16 k
-// values); per 32-column B fragment the same k values of the lane's column.
+// values of the lane's row); per 32-column B fragment the same k values of
+// the lane's column.
 template <class G>
 struct Frags {
     u32x4 a[G::FM];
     u32x4 b[G::FN];
 };
+
+// One operand fragment: the KS k values from kk of outer index ob + lane%32.
+template <class T>
+__device__ __forceinline__ u32x4 read_frag(const unsigned char *tile, int lane, int ob, int kk)
+{
+    if constexpr (T::LAYOUT == KMAJOR) {
+        return lds_load16(tile, T::off(ob + (lane & 31), kk));
+    } else if constexpr (T::BF16) {
+        // two transpose loads: k = kk..kk+3 and kk+4..kk+7 of outer index
+        // ob + lane%32
+        const int s = lane & 15, g = (lane >> 4) & 1;
+        const int col = ob + 16 * g + 4 * (s & 3);
+        const int k = kk + (s >> 2);
+        const v4i16 lo = lds_read_tr16(tile, T::off(k, col));
+        const v4i16 hi = lds_read_tr16(tile, T::off(k + 4, col));
+        return u32x4{(unsigned)(unsigned short)lo[0] | ((unsigned)(unsigned short)lo[1] << 16),
+                     (unsigned)(unsigned short)lo[2] | ((unsigned)(unsigned short)lo[3] << 16),
+                     (unsigned)(unsigned short)hi[0] | ((unsigned)(unsigned short)hi[1] << 16),
+                     (unsigned)(unsigned short)hi[2] | ((unsigned)(unsigned short)hi[3] << 16)};
+    } else {
+        u32x4 v;
+        const int col = ob + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < T::VEC; ++e) v[e] = __float_as_uint(lds_loadf(tile, T::off(kk + e, col)));
+        return v;
+    }
+}
 
 // Fragments of step `step` of the tile in `stage`.  Lane half h (lanes
 // 32h..32h+31) supplies k = h*BK/2 + step*KS .. +KS of the tile.
@@ -281,34 +358,13 @@ __device__ __forceinline__ void load_frags(const unsigned char *stage, const Blo
                                            int step, Frags<G> &f)
 {
     const unsigned char *sb = stage + G::A_BYTES;
-    const int half = c.lane >> 5, l32 = c.lane & 31;
-    const int kk = half * G::KH + step * G::KS;
+    const int kk = (c.lane >> 5) * G::KH + step * G::KS;
 #pragma unroll
-    for (int fm = 0; fm < G::FM; ++fm) {
-        const int row = c.wrow * G::WTM + fm * 32 + l32;
-        f.a[fm] = lds_load16(stage, G::a_off(row, kk / G::VEC));
-    }
+    for (int fm = 0; fm < G::FM; ++fm)
+        f.a[fm] = read_frag<typename G::TA>(stage, c.lane, c.wrow * G::WTM + fm * 32, kk);
 #pragma unroll
-    for (int fn = 0; fn < G::FN; ++fn) {
-        if constexpr (G::BF16) {
-            // two transpose loads: k = kk..kk+3 and kk+4..kk+7 of column
-            // (fragment column) + lane%32
-            const int p = c.lane & 15, g = (c.lane >> 4) & 1;
-            const int col = c.wcol * G::WTN + fn * 32 + 16 * g + 4 * (p & 3);
-            const int k = kk + (p >> 2);
-            const v4i16 lo = lds_read_tr16(sb, G::b_off(k, col));
-            const v4i16 hi = lds_read_tr16(sb, G::b_off(k + 4, col));
-            f.b[fn] = u32x4{(unsigned)(unsigned short)lo[0] | ((unsigned)(unsigned short)lo[1] << 16),
-                            (unsigned)(unsigned short)lo[2] | ((unsigned)(unsigned short)lo[3] << 16),
-                            (unsigned)(unsigned short)hi[0] | ((unsigned)(unsigned short)hi[1] << 16),
-                            (unsigned)(unsigned short)hi[2] | ((unsigned)(unsigned short)hi[3] << 16)};
-        } else {
-            const int col = c.wcol * G::WTN + fn * 32 + l32;
-#pragma unroll
-            for (int e = 0; e < G::KS; ++e)
-                f.b[fn][e] = __float_as_uint(lds_loadf(sb, G::b_off(kk + e, col)));
-        }
-    }
+    for (int fn = 0; fn < G::FN; ++fn)
+        f.b[fn] = read_frag<typename G::TB>(sb, c.lane, c.wcol * G::WTN + fn * 32, kk);
 }
 
 template <class G>
@@ -353,43 +409,48 @@ __device__ __forceinline__ void interleave_step()
 
 // -------------------------------------------------- interior (direct) path --
 
-// Per-thread byte offsets of the direct loads, relative to the tile origin
-// in A (row bm, column k0) and in B (row k0, column bn).  They do not change
-// from one k-tile to the next, so they are computed once per block and the
-// per-tile address is a uniform base plus a 32-bit offset.
-template <class G>
-struct DirectOffsets {
-    uint32_t a[G::A_PIECES / G::NW];
-    uint32_t b[G::B_PIECES / G::NW];
+// Per-thread byte offsets of one operand's direct loads, relative to the tile
+// origin.  They do not change from one k-tile to the next, so they are
+// computed once per block and the per-tile address is a uniform base plus a
+// 32-bit offset.
+template <class T>
+struct TileOffsets {
+    uint32_t v[T::PIECES / T::NW];
 };
 
 // The LDS side of a direct load is fixed -- 1 KiB per instruction, lane l at
-// byte 16*l -- so each lane fetches the global chunk that the tile's XOR
-// swizzle places at its LDS position (the swizzles are their own inverses).
-template <class G>
-__device__ __forceinline__ void direct_offsets(const BlockCtx<G> &c, DirectOffsets<G> &o)
+// byte 16*l -- so each lane fetches the global chunk that the tile's swizzle
+// places at its LDS position.  LDS row r is memory row r of the tile (an
+// outer index for KMAJOR, a k for MNMAJOR).
+template <class T>
+__device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t ld, TileOffsets<T> &o)
 {
-    constexpr int NW = G::NW, LPR = G::B_LANES_PER_ROW;
-    const int wave = c.tid >> 6;
 #pragma unroll
-    for (int i = 0; i < G::A_PIECES / NW; ++i) {
-        const int j = wave + NW * i;  // piece: A rows j*A_ROWS_PER_PIECE ..
-        const int r = j * G::A_ROWS_PER_PIECE + c.lane / G::ACH;
-        const int chunk = (c.lane % G::ACH) ^ ((r / G::RPL) % G::ACH);
-        o.a[i] = (uint32_t)(((int64_t)r * c.lda + chunk * G::VEC) * G::ES);
+    for (int i = 0; i < T::PIECES / T::NW; ++i) {
+        const int piece = wave + T::NW * i;
+        const int row = piece * T::ROWS_PER_PIECE + lane / T::CPR;
+        const int e = T::logical(row, (lane % T::CPR) * T::VEC);
+        o.v[i] = (uint32_t)(((int64_t)row * ld + e) * T::ES);
     }
-#pragma unroll
-    for (int i = 0; i < G::B_PIECES / NW; ++i) {
-        const int j = wave + NW * i;  // piece: B rows j*(64/LPR) ..
-        const int k = j * (64 / LPR) + c.lane / LPR;
-        const int phys = (c.lane % LPR) * G::VEC;  // element position in the LDS row
-        int n;
-        if constexpr (G::BF16)
-            n = (((phys >> 5) ^ (k & G::B_SEGMASK)) << 5) | (phys & 31);
-        else
-            n = phys ^ (((k >> 4) & 1) << 5);
-        o.b[i] = (uint32_t)(((int64_t)k * c.ldb + n) * G::ES);
-    }
+}
+
+template <class G>
+struct DirectOffsets {
+    TileOffsets<typename G::TA> a;
+    TileOffsets<typename G::TB> b;
+};
+
+// Global address of the origin of one operand's k-tile: KMAJOR rows are
+// outer indices (origin row outer0, column k0), MNMAJOR rows are k (origin
+// row k0, column outer0).
+template <class T>
+__device__ __forceinline__ const void *tile_origin(const typename T::In *X, int64_t ld, int outer0,
+                                                   int k0)
+{
+    if constexpr (T::LAYOUT == KMAJOR)
+        return X + ((int64_t)outer0 * ld + k0);
+    else
+        return X + ((int64_t)k0 * ld + outer0);
 }
 
 // Direct copy of the k-tile at k0 into `stage` (interior tiles only: every
@@ -398,16 +459,18 @@ template <class G>
 __device__ __forceinline__ void direct_tile_load(unsigned char *stage, const BlockCtx<G> &c,
                                                  const DirectOffsets<G> &o, int k0)
 {
+    using TA = typename G::TA;
+    using TB = typename G::TB;
     constexpr int NW = G::NW;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
     const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + 1024 * wave;
-    const void *a_base = c.A + ((int64_t)c.bm * c.lda + k0);
-    const void *b_base = c.B + ((int64_t)k0 * c.ldb + c.bn);
+    const void *a_base = tile_origin<TA>(c.A, c.lda, c.bm, k0);
+    const void *b_base = tile_origin<TB>(c.B, c.ldb, c.bn, k0);
 #pragma unroll
-    for (int i = 0; i < G::A_PIECES / NW; ++i) direct_load16(a_base, o.a[i], lds + 1024 * NW * i);
+    for (int i = 0; i < TA::PIECES / NW; ++i) direct_load16(a_base, o.a.v[i], lds + 1024 * NW * i);
 #pragma unroll
-    for (int i = 0; i < G::B_PIECES / NW; ++i)
-        direct_load16(b_base, o.b[i], lds + G::A_BYTES + 1024 * NW * i);
+    for (int i = 0; i < TB::PIECES / NW; ++i)
+        direct_load16(b_base, o.b.v[i], lds + G::A_BYTES + 1024 * NW * i);
 }
 
 // One interior k-tile: multiply the tile in `stage` while the tile at k_load
@@ -470,7 +533,8 @@ __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
     unsigned char *const st[4] = {s0, s1, s2, s3};
     Frags<G> cur;
     DirectOffsets<G> o;
-    direct_offsets(c, o);
+    tile_offsets(c.tid >> 6, c.lane, c.lda, o.a);
+    tile_offsets(c.tid >> 6, c.lane, c.ldb, o.b);
     const int k_last = k_first + (ntiles - 1) * BK;
     // prologue: tiles 0 .. S-2 in flight, tile 0 complete
 #pragma unroll
@@ -498,52 +562,61 @@ __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
 // The operand tiles of one k-tile, between their global load and LDS store.
 template <class G>
 struct StageRegs {
-    u32x4 a[G::A_PER_THREAD];
-    u32x4 b[G::B_PER_THREAD];
+    u32x4 a[G::TA::PER_THREAD];
+    u32x4 b[G::TB::PER_THREAD];
 };
 
-// Global -> registers for the k-tile starting at k0, zero outside the matrix
-// (rows >= M, columns >= N, k >= kend).
-//   A chunk u: row (tid + u*NT) / ACH, chunk (tid + u*NT) % ACH
-//   B chunk u: c = tid + u*NT; row c/(BN/VEC), elements (c%(BN/VEC))*VEC .. +VEC
-// Consecutive lanes read consecutive 16-byte chunks of a row (coalesced).
+// Global -> registers for one operand's k-tile at k0, zero outside the
+// matrix.  Chunk u of a thread is ch = tid + u*NT: memory row ch/CPR of the
+// tile, elements (ch%CPR)*VEC .. +VEC, so consecutive lanes read consecutive
+// 16-byte chunks of a row (coalesced).  KMAJOR rows are outer indices (valid
+// below n_outer) and k runs along the row (valid below kend); MNMAJOR rows
+// are k and the outer index runs along the row.
+template <bool ALIGNED, class T>
+__device__ __forceinline__ void load_tile_masked(const typename T::In *X, int64_t ld, int outer0,
+                                                 int n_outer, int k0, int kend, int tid,
+                                                 u32x4 (&r)[T::PER_THREAD])
+{
+    using In = typename T::In;
+#pragma unroll
+    for (int u = 0; u < T::PER_THREAD; ++u) {
+        const int ch = tid + u * T::NT;
+        const int row = ch / T::CPR, e = (ch % T::CPR) * T::VEC;
+        if constexpr (T::LAYOUT == KMAJOR) {
+            const int go = outer0 + row;
+            r[u] = load_chunk_masked<In, T::VEC, ALIGNED>(X + (int64_t)go * ld, go < n_outer,
+                                                          k0 + e, kend);
+        } else {
+            const int gk = k0 + row;
+            r[u] = load_chunk_masked<In, T::VEC, ALIGNED>(X + (int64_t)gk * ld, gk < kend,
+                                                          outer0 + e, n_outer);
+        }
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void store_tile(unsigned char *tile, int tid,
+                                           const u32x4 (&r)[T::PER_THREAD])
+{
+#pragma unroll
+    for (int u = 0; u < T::PER_THREAD; ++u) {
+        const int ch = tid + u * T::NT;
+        lds_store16(tile, T::off(ch / T::CPR, (ch % T::CPR) * T::VEC), r[u]);
+    }
+}
+
 template <bool ALIGNED, class G>
 __device__ __forceinline__ void global_load_masked(const BlockCtx<G> &c, int k0, StageRegs<G> &r)
 {
-    using In = typename G::In;
-    constexpr int VEC = G::VEC, NT = G::NT, CPR = G::BN / VEC;
-#pragma unroll
-    for (int u = 0; u < G::A_PER_THREAD; ++u) {
-        const int ch = c.tid + u * NT;
-        const int gi = c.bm + ch / G::ACH;
-        const In *row = c.A + (int64_t)gi * c.lda;
-        r.a[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gi < c.M, k0 + (ch % G::ACH) * VEC, c.kend);
-    }
-#pragma unroll
-    for (int u = 0; u < G::B_PER_THREAD; ++u) {
-        const int ch = c.tid + u * NT;
-        const int gk = k0 + ch / CPR;
-        const int gn = c.bn + (ch % CPR) * VEC;
-        const In *row = c.B + (int64_t)gk * c.ldb;
-        r.b[u] = load_chunk_masked<In, VEC, ALIGNED>(row, gk < c.kend, gn, c.N);
-    }
+    load_tile_masked<ALIGNED, typename G::TA>(c.A, c.lda, c.bm, c.M, k0, c.kend, c.tid, r.a);
+    load_tile_masked<ALIGNED, typename G::TB>(c.B, c.ldb, c.bn, c.N, k0, c.kend, c.tid, r.b);
 }
 
 template <class G>
 __device__ __forceinline__ void lds_store(unsigned char *stage, int tid, const StageRegs<G> &r)
 {
-    constexpr int NT = G::NT, CPR = G::BN / G::VEC;
-    unsigned char *sb = stage + G::A_BYTES;
-#pragma unroll
-    for (int u = 0; u < G::A_PER_THREAD; ++u) {
-        const int ch = tid + u * NT;
-        lds_store16(stage, G::a_off(ch / G::ACH, ch % G::ACH), r.a[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < G::B_PER_THREAD; ++u) {
-        const int ch = tid + u * NT;
-        lds_store16(sb, G::b_off(ch / CPR, (ch % CPR) * G::VEC), r.b[u]);
-    }
+    store_tile<typename G::TA>(stage, tid, r.a);
+    store_tile<typename G::TB>(stage + G::A_BYTES, tid, r.b);
 }
 
 // `ntiles` masked k-tiles from k_first, double buffered through registers
@@ -579,13 +652,34 @@ __device__ __forceinline__ void main_loop_masked(unsigned char *smem0, unsigned 
     }
 }
 
+// --------------------------------------------------------------- epilogue --
+
+// Final value of one element of C: alpha * sum, plus beta * (old C) when
+// beta != 0 (C is not read when beta == 0, so it may hold anything then),
+// stored as fp32 or as bf16.
+__device__ __forceinline__ void store_out(void *C, int64_t idx, float sum, float alpha, float beta,
+                                          bool out_bf16)
+{
+    float v = alpha * sum;
+    if (out_bf16) {
+        uint16_t *c = static_cast<uint16_t *>(C);
+        if (beta != 0.0f) v += beta * __uint_as_float((uint32_t)c[idx] << 16);
+        c[idx] = f32_to_bf16_rne(v);
+    } else {
+        float *c = static_cast<float *>(C);
+        if (beta != 0.0f) v += beta * c[idx];
+        c[idx] = v;
+    }
+}
+
 // ------------------------------------------------------------------ kernel --
 
-template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, bool ALIGNED>
+template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
+          bool ALIGNED>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(KernelArgs p)
 {
-    using G = Geo<BF16, BM, BN, BK, WM, WN, STAGES>;
+    using G = Geo<BF16, BM, BN, BK, WM, WN, STAGES, LA, LB>;
     using In = typename G::In;
 
     // One __shared__ array per stage (unused ones are one byte).
@@ -630,33 +724,48 @@ gemm_kernel(KernelArgs p)
     const bool edge = !ALIGNED || !p.direct_ok || c.bm + BM > p.M || c.bn + BN > p.N;
     const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
     if (nfast > 0) main_loop_direct(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
-    if (ntiles > nfast) main_loop_masked<ALIGNED>(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc);
+    if (ntiles > nfast)
+        main_loop_masked<ALIGNED>(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc);
 
-    // Epilogue: accumulator element r of a 32x32 fragment sits at row
-    // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that fragment.
-    float *out;
-    int64_t ldo;
-    if (p.splits > 1) {
-        out = p.ws + (int64_t)slice * p.M * p.N;
-        ldo = p.N;
-    } else {
-        out = p.C;
-        ldo = p.ldc;
-    }
+    // Epilogue: element r of a 32x32 accumulator fragment sits at row
+    // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that fragment.  With
+    // split-K the raw partial sums go to the workspace (the reduce applies
+    // alpha, beta and the output type); otherwise they are finished here.
     const int half = c.lane >> 5, l32 = c.lane & 31;
     const bool store_edge = c.bm + BM > p.M || c.bn + BN > p.N;
+    const bool partial = p.splits > 1;
+    if (partial || (p.alpha == 1.0f && p.beta == 0.0f && !p.out_bf16)) {
+        // raw sums: the split-K partials, or the plain product into fp32 C
+        float *out = partial ? p.ws + (int64_t)slice * p.M * p.N : static_cast<float *>(p.C);
+        const int64_t ldo = partial ? (int64_t)p.N : p.ldc;
 #pragma unroll
-    for (int fm = 0; fm < G::FM; ++fm) {
+        for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < G::FN; ++fn) {
+                const int gj = c.bn + c.wcol * G::WTN + fn * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gi =
+                        c.bm + c.wrow * G::WTM + fm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (!store_edge || (gi < p.M && gj < p.N))
+                        out[(int64_t)gi * ldo + gj] = acc[fm][fn][r];
+                }
+            }
+        return;
+    }
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < G::FN; ++fn) {
             const int gj = c.bn + c.wcol * G::WTN + fn * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gi = c.bm + c.wrow * G::WTM + fm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (!store_edge || (gi < p.M && gj < p.N)) out[(int64_t)gi * ldo + gj] = acc[fm][fn][r];
+                if (!store_edge || (gi < p.M && gj < p.N))
+                    store_out(p.C, (int64_t)gi * p.ldc + gj, acc[fm][fn][r], p.alpha, p.beta,
+                              p.out_bf16 != 0);
             }
         }
-    }
 }
 
 }  // namespace dg

@@ -1,0 +1,41 @@
+// Definition of the kernel launcher and the explicit instantiation of one
+// operand layout's kernels from the tile lists.  Included by the per-layout
+// source files, each of which defines DG_DTYPE_TABLE (the list), DG_LAYOUT
+// (NN, NT, TN or TT) and then includes this header.
+#pragma once
+
+#include "gemm_configs.hpp"
+
+namespace dg {
+
+template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
+          bool ALIGNED>
+hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_kernel<BF16, BM, BN, BK, WM, WN, STAGES, LA, LB, ALIGNED>),
+                       dim3(blocks), dim3(64 * WM * WN), 0, stream, args);
+    return hipGetLastError();
+}
+
+}  // namespace dg
+
+// Explicit instantiation of both alignments of one entry for layout L.
+#define DG_INST(BF16, BM, BN, BK, WM, WN, S, L)                                                 \
+    template hipError_t dg::launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L,      \
+                                        true>(const dg::KernelArgs &, int, hipStream_t);        \
+    template hipError_t dg::launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L,      \
+                                        false>(const dg::KernelArgs &, int, hipStream_t);
+#define DG_INST_ALL_NN(...) DG_INST(__VA_ARGS__, NN)
+#define DG_INST_ALL_NT(...) DG_INST(__VA_ARGS__, NT)
+#define DG_INST_ALL_TN(...) DG_INST(__VA_ARGS__, TN)
+#define DG_INST_ALL_TT(...) DG_INST(__VA_ARGS__, TT)
+#define DG_INST_NN_NN(...) DG_INST(__VA_ARGS__, NN)
+#define DG_INST_NN_NT(...)
+#define DG_INST_NN_TN(...)
+#define DG_INST_NN_TT(...)
+#define DG_INST_SEL2(LAYOUTS, L) DG_INST_##LAYOUTS##_##L
+#define DG_INST_SEL(LAYOUTS, L) DG_INST_SEL2(LAYOUTS, L)
+#define DG_INST_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                            \
+    DG_INST_SEL(LAYOUTS, DG_LAYOUT)(BF16, BM, BN, BK, WM, WN, S)
+
+DG_DTYPE_TABLE(DG_INST_ENTRY)

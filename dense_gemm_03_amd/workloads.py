@@ -18,7 +18,21 @@ tall        65536 x 64 x 1024      fp32 uniform[-1, 1]         107
 ==========  =====================  ==========================  ======
 
 A is drawn with ``seed`` and B with ``seed + 1000`` from
-``numpy.random.default_rng``.  Large operands are drawn in row chunks; the
+``numpy.random.default_rng``.
+
+Variants of the generalised product C := alpha op(A) op(B) + beta C (the
+GEMM page's section "Generalized matrix multiplication GEMM") reuse those
+shapes and distributions; the operands are drawn in their stored shapes (A as
+K x M when transposed, B as N x K), and an initial C, needed when beta != 0,
+is drawn with ``seed + 2000`` in the output type:
+
+==================  ==========  =====  =====  =====  ==========
+name                base        op     alpha  beta   C
+==================  ==========  =====  =====  =====  ==========
+bf16-8192-nt-bf16c  bf16-8192   A B^T  1      0      bf16
+bf16-8192-tn-acc    bf16-8192   A^T B  0.5    1      fp32
+fp32-4096-tt-ab     fp32-4096   A^T B^T 1.5   -0.5   fp32
+==================  ==========  =====  =====  =====  ==========  Large operands are drawn in row chunks; the
 PCG64 stream yields the same values whether drawn at once or in chunks.
 
 The im2col shape is the weight-gradient GEMM of a 2-D convolution with a large
@@ -46,6 +60,11 @@ class Workload:
     K: int
     dist: str  # "uniform" or "normal_bf16"
     seed: int
+    transa: bool = False
+    transb: bool = False
+    alpha: float = 1.0
+    beta: float = 0.0
+    out: str = "f32"  # type of C: "f32" or "bf16"
 
     @property
     def flops(self) -> int:
@@ -56,19 +75,48 @@ class Workload:
         return 4 if self.dtype == "f32" else 2
 
     @property
+    def out_bytes(self) -> int:
+        return 4 if self.out == "f32" else 2
+
+    @property
+    def plain(self) -> bool:
+        """The plain product C = A . B with fp32 C."""
+        return (not self.transa and not self.transb and self.alpha == 1.0 and self.beta == 0.0
+                and self.out == "f32")
+
+    @property
+    def a_shape(self):
+        return (self.K, self.M) if self.transa else (self.M, self.K)
+
+    @property
+    def b_shape(self):
+        return (self.N, self.K) if self.transb else (self.K, self.N)
+
+    @property
     def algorithmic_bytes(self) -> int:
-        """Compulsory HBM bytes: read A and B once, write C once (C is not read)."""
-        return (self.M * self.K + self.K * self.N) * self.in_bytes + self.M * self.N * 4
+        """Compulsory HBM bytes: read A and B once, write C once, and read C
+        once when beta != 0."""
+        c_passes = 2 if self.beta != 0.0 else 1
+        return (self.M * self.K + self.K * self.N) * self.in_bytes \
+            + c_passes * self.M * self.N * self.out_bytes
 
     def operands(self):
-        """(A, B) as numpy arrays: float32, or uint16 bf16 bit patterns."""
+        """(A, B) in their stored shapes as numpy arrays: float32, or uint16
+        bf16 bit patterns."""
         if self.dist == "uniform":
-            return (uniform_f32((self.M, self.K), self.seed),
-                    uniform_f32((self.K, self.N), self.seed + 1000))
+            return (uniform_f32(self.a_shape, self.seed),
+                    uniform_f32(self.b_shape, self.seed + 1000))
         if self.dist == "normal_bf16":
-            return (normal_bf16_bits((self.M, self.K), self.seed),
-                    normal_bf16_bits((self.K, self.N), self.seed + 1000))
+            return (normal_bf16_bits(self.a_shape, self.seed),
+                    normal_bf16_bits(self.b_shape, self.seed + 1000))
         raise ValueError(self.dist)
+
+    def initial_c(self):
+        """The initial C (M x N) for beta != 0: float32 uniform[-1, 1], or
+        normal(0, 1) rounded to bf16 bit patterns for bf16 C."""
+        if self.out == "f32":
+            return uniform_f32((self.M, self.N), self.seed + 2000)
+        return normal_bf16_bits((self.M, self.N), self.seed + 2000)
 
 
 WORKLOADS = {
@@ -81,6 +129,18 @@ WORKLOADS = {
         Workload("bf16-8192", "bf16", 8192, 8192, 8192, "normal_bf16", 105),
         Workload("im2col", "f32", 64, 16384, 61504, "uniform", 106),
         Workload("tall", "f32", 65536, 64, 1024, "uniform", 107),
+    ]
+}
+
+VARIANTS = {
+    w.name: w
+    for w in [
+        Workload("bf16-8192-nt-bf16c", "bf16", 8192, 8192, 8192, "normal_bf16", 105,
+                 transb=True, out="bf16"),
+        Workload("bf16-8192-tn-acc", "bf16", 8192, 8192, 8192, "normal_bf16", 105,
+                 transa=True, alpha=0.5, beta=1.0),
+        Workload("fp32-4096-tt-ab", "f32", 4096, 4096, 4096, "uniform", 102,
+                 transa=True, transb=True, alpha=1.5, beta=-0.5),
     ]
 }
 

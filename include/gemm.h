@@ -7,12 +7,16 @@
  *
  *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j].
  *
- * The generalised form of that page's next section scales the product and
- * adds a scaled accumulator; this library computes the plain product: C is
- * overwritten (alpha = 1, beta = 0) and never read.
+ * gemm_f32 and gemm_bf16 compute exactly that product: C is overwritten and
+ * never read.  gemm_ex computes the generalised product of the page's next
+ * section, "Generalized matrix multiplication GEMM":
+ *
+ *     C := alpha * op(A) * op(B) + beta * C,    op(X) = X or X^T,
+ *
+ * with C stored as fp32 or bf16 (see gemm_ex below).
  *
  * Layout: every matrix is row-major with a leading dimension, counted in
- * elements, between the starts of consecutive rows:
+ * elements, between the starts of consecutive rows (for the plain product):
  *     A[i][k] = A[i*lda + k],  lda >= K
  *     B[k][j] = B[k*ldb + j],  ldb >= N
  *     C[i][j] = C[i*ldc + j],  ldc >= N
@@ -73,6 +77,9 @@ typedef enum {
 
 typedef enum { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1 } gemm_dtype;
 
+/* Operand form for gemm_ex: as stored, or transposed. */
+typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op;
+
 /* C := A . B for fp32 A (M x K), B (K x N) and C (M x N), row-major. */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
@@ -87,6 +94,41 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const uint16_t *B, int64_t ldb,
               float *C, int64_t ldc,
               hipStream_t stream);
+
+/*
+ * C := alpha * op(A) * op(B) + beta * C   ("Generalized matrix multiplication
+ * GEMM" on the GEMM page; BLAS's xGEMM with row-major storage).
+ *
+ * dtype_ab: GEMM_DTYPE_F32 or GEMM_DTYPE_BF16, the type of both A and B
+ *   (bf16 as raw 16-bit patterns).  Products are fp32 (fp32 inputs) or exact
+ *   (bf16 inputs) and are accumulated in fp32.
+ * dtype_c: GEMM_DTYPE_F32 or GEMM_DTYPE_BF16, the type of C on input and
+ *   output.  alpha * sum + beta * C is formed in fp32 and, for bf16 C, rounded
+ *   once to nearest (ties to even); a NaN stays a NaN.
+ * transa, transb: GEMM_OP_N or GEMM_OP_T.  The stored matrices, row-major:
+ *   transa == N: A is M x K, op(A)[i][k] = A[i*lda + k], lda >= max(K,1)
+ *   transa == T: A is K x M, op(A)[i][k] = A[k*lda + i], lda >= max(M,1)
+ *   transb == N: B is K x N, op(B)[k][j] = B[k*ldb + j], ldb >= max(N,1)
+ *   transb == T: B is N x K, op(B)[k][j] = B[j*ldb + k], ldb >= max(K,1)
+ *   C is M x N, C[i][j] = C[i*ldc + j], ldc >= max(N,1).
+ *   (A column-major caller passes its matrices with the transpose flags
+ *   flipped and computes C^T.)
+ * alpha, beta: fp32 scalars.  When beta == 0, C is not read (it may hold
+ *   anything, NaN included).  When alpha == 0 or K == 0, A and B are not read
+ *   and C := beta * C (or 0 when beta == 0).
+ *
+ * Errors as for gemm_f32, and GEMM_ERR_INVALID_ARG for an unknown dtype or
+ * transpose flag or for C not aligned to its element size.  Ownership,
+ * streams, workspace and threads as above; C must not overlap A or B.
+ */
+int gemm_ex(int dtype_ab, int dtype_c, int transa, int transb,
+            int64_t M, int64_t N, int64_t K,
+            float alpha,
+            const void *A, int64_t lda,
+            const void *B, int64_t ldb,
+            float beta,
+            void *C, int64_t ldc,
+            hipStream_t stream);
 
 /* A static, human-readable description of a gemm_status value. */
 const char *gemm_status_string(int status);
@@ -105,15 +147,20 @@ const char *gemm_status_string(int status);
  *   NULL when out of range.
  * gemm_split_k: the number of K slices the dispatcher would use with entry cfg
  *   for this shape (1 = no split); negative on bad arguments.
- * gemm_f32_with_config / gemm_bf16_with_config: as gemm_f32 / gemm_bf16 but
- *   with the table entry forced; split_k <= 0 lets the dispatcher choose the
- *   number of K slices, a positive value forces it (clamped so that every
- *   slice holds at least one k-tile).
+ * gemm_config_layouts: bit (transa * 2 + transb) is set when entry cfg has
+ *   kernels for that operand form (every entry the dispatcher chooses has all
+ *   four); negative on bad arguments.
+ * gemm_f32_with_config / gemm_bf16_with_config / gemm_ex_with_config: as
+ *   gemm_f32 / gemm_bf16 / gemm_ex but with the table entry forced (an entry
+ *   without kernels for the requested operand form is GEMM_ERR_INVALID_ARG);
+ *   split_k <= 0 lets the dispatcher choose the number of K slices, a positive
+ *   value forces it (clamped so that every slice holds at least one k-tile).
  */
 int gemm_num_configs(int dtype);
 int gemm_select_config(int dtype, int64_t M, int64_t N, int64_t K);
 const char *gemm_config_name(int dtype, int cfg);
 int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K);
+int gemm_config_layouts(int dtype, int cfg);
 
 int gemm_f32_with_config(int cfg, int split_k,
                          int64_t M, int64_t N, int64_t K,
@@ -128,6 +175,16 @@ int gemm_bf16_with_config(int cfg, int split_k,
                           const uint16_t *B, int64_t ldb,
                           float *C, int64_t ldc,
                           hipStream_t stream);
+
+int gemm_ex_with_config(int cfg, int split_k,
+                        int dtype_ab, int dtype_c, int transa, int transb,
+                        int64_t M, int64_t N, int64_t K,
+                        float alpha,
+                        const void *A, int64_t lda,
+                        const void *B, int64_t ldb,
+                        float beta,
+                        void *C, int64_t ldc,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -235,3 +235,26 @@ def round_to_bf16_bits(x) -> np.ndarray:
             q = np.copysign(np.inf, v)
         res[t] = np.array([q], dtype=np.float32).view(np.uint32)[0] >> 16
     return out
+
+
+def entries_general(A: np.ndarray, B: np.ndarray, I, J, alpha: float = 1.0, beta: float = 0.0,
+                    C0_at: np.ndarray | None = None, transa: bool = False,
+                    transb: bool = False, kind: str = "f32"):
+    """gemm_general at the positions (I[t], J[t]) only, one dot product each:
+    (C_ref, S) at those positions.  C0_at holds the initial C at the same
+    positions (float64; read only when beta != 0).  Same conventions as
+    gemm_general."""
+    opA = _stored_to_op(A, transa)
+    opB = _stored_to_op(B, transb)
+    I = np.ascontiguousarray(I, dtype=np.int64)
+    alpha = float(alpha)
+    beta = float(beta)
+    if alpha != 0.0 and opA.shape[1] > 0:
+        P, SP = _entries(kind, opA, opB, I, J)
+        C, S = alpha * P, abs(alpha) * SP
+    else:
+        C, S = np.zeros(I.shape), np.zeros(I.shape)
+    if beta != 0.0:
+        C0_at = np.asarray(C0_at, dtype=np.float64)
+        C, S = C + beta * C0_at, S + abs(beta) * np.abs(C0_at)
+    return C, S

@@ -27,7 +27,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -111,6 +111,60 @@ def test_invalid_arguments_rejected_before_any_device_call():
     assert dg.gemm_bf16(4, 4, 4, p + 1, 4, p, 4, p, 4, None) == dg.GEMM_ERR_INVALID_ARG
     assert dg.gemm_f32_with_config(99, 0, 4, 4, 4, p, 4, p, 4, p, 4, None) == dg.GEMM_ERR_INVALID_ARG
     assert dg.gemm_f32_with_config(-1, 0, 4, 4, 4, p, 4, p, 4, p, 4, None) == dg.GEMM_ERR_INVALID_ARG
+
+
+def test_gemm_ex_invalid_arguments_rejected_before_any_device_call():
+    p = 4096
+    F32, BF16, N_, T_ = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16, dg.GEMM_OP_N, dg.GEMM_OP_T
+    ok = (F32, F32, N_, N_, 4, 6, 8, 1.0, p, 8, p, 6, 0.0, p, 6)
+
+    def call(**kw):
+        names = ["dt", "dtc", "ta", "tb", "M", "N", "K", "alpha", "A", "lda", "B", "ldb", "beta",
+                 "C", "ldc"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return dg.gemm_ex(*[args[n] for n in names], None)
+
+    bad = [
+        dict(dt=2), dict(dtc=-1), dict(ta=2), dict(tb=-1),
+        dict(M=-1), dict(K=1 << 31),
+        dict(lda=7),                      # A as given: lda >= K = 8
+        dict(ta=T_, lda=3),               # A transposed (K x M): lda >= M = 4
+        dict(ldb=5),                      # B as given: ldb >= N = 6
+        dict(tb=T_, ldb=7),               # B transposed (N x K): ldb >= K = 8
+        dict(ldc=5),                      # ldc >= N
+        dict(A=None), dict(B=None), dict(C=None),
+        dict(C=p + 2),                    # fp32 C not 4-byte aligned
+        dict(dtc=BF16, C=p + 1),          # bf16 C not 2-byte aligned
+        dict(dt=BF16, A=p + 1),           # bf16 A not 2-byte aligned
+    ]
+    for kw in bad:
+        assert call(**kw) == dg.GEMM_ERR_INVALID_ARG, kw
+    # transposed leading dimensions that are valid for the stored shapes pass
+    # validation; M == 0 then returns before any device call
+    assert call(M=0, ta=T_, lda=1, C=None) == dg.GEMM_OK
+    assert call(N=0, tb=T_, ldb=8, ldc=1, C=None) == dg.GEMM_OK
+    # forced entries: out of range, or without kernels for the operand form
+    assert dg.gemm_ex_with_config(99, 0, *ok, None) == dg.GEMM_ERR_INVALID_ARG
+    for dtype in (F32, BF16):
+        for c in range(dg.gemm_num_configs(dtype)):
+            if not dg.gemm_config_layouts(dtype, c) & (1 << 3):
+                args = (dtype, F32, T_, T_, 4, 6, 8, 1.0, p, 4, p, 8, 0.0, p, 6)
+                assert dg.gemm_ex_with_config(c, 0, *args, None) == dg.GEMM_ERR_INVALID_ARG
+                break
+
+
+def test_layout_masks_cover_every_dispatched_entry():
+    """Every entry the dispatcher picks has kernels for all four operand
+    forms, and every entry has the plain form."""
+    for dtype in (dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16):
+        for c in range(dg.gemm_num_configs(dtype)):
+            assert dg.gemm_config_layouts(dtype, c) & 1
+        assert dg.gemm_config_layouts(dtype, -1) == dg.GEMM_ERR_INVALID_ARG
+        for M in (1, 33, 64, 65, 100, 1000, 2048, 4096, 8192, 65536):
+            for N in (1, 33, 64, 65, 100, 1000, 2048, 4096, 16384):
+                c = dg.gemm_select_config(dtype, M, N, 1024)
+                assert dg.gemm_config_layouts(dtype, c) == 0xF, (dtype, M, N)
 
 
 def test_empty_output_is_a_no_op():

@@ -250,3 +250,24 @@ def test_round_to_bf16_matches_torch_on_float32():
     want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     got = oracle.round_to_bf16_bits(x.astype(np.float64))
     assert np.array_equal(got, want)
+
+
+def test_entries_general_match_full_product_bitwise():
+    """The one-entry-at-a-time form equals the full generalised product at
+    the same positions, bit for bit (same k order), for every transpose
+    combination and both encodings."""
+    rng = np.random.default_rng(21)
+    M, N, K = 37, 29, 53
+    I = rng.integers(0, M, 60)
+    J = rng.integers(0, N, 60)
+    for ta, tb in TRANS:
+        A = rng.uniform(-1, 1, size=(K, M) if ta else (M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, size=(N, K) if tb else (K, N)).astype(np.float32)
+        C0 = rng.uniform(-1, 1, size=(M, N))
+        for kind in ("f32", "bf16"):
+            a, b = (A, B) if kind == "f32" else (
+                (A.view(np.uint32) >> 16).astype(np.uint16), (B.view(np.uint32) >> 16).astype(np.uint16))
+            for alpha, beta in [(0.75, -1.5), (1.0, 0.0), (0.0, 2.0)]:
+                C, S = oracle.gemm_general(a, b, alpha, beta, C0, ta, tb, kind=kind)
+                Ce, Se = oracle.entries_general(a, b, I, J, alpha, beta, C0[I, J], ta, tb, kind=kind)
+                assert np.array_equal(C[I, J], Ce) and np.array_equal(S[I, J], Se)

@@ -1,0 +1,258 @@
+"""GPU parity of the generalised GEMM C := alpha * op(A) . op(B) + beta * C
+("Generalized matrix multiplication GEMM" on the GEMM page): transposed
+operands, alpha/beta and bf16 output, against ``oracle.gemm_general``,
+through the C ABI (gemm_ex / gemm_ex_with_config).
+
+Integer-valued operands, alpha, beta and C make every intermediate exact, so
+fp32 results must equal the oracle bit for bit, and bf16 results must equal
+the oracle's exact value rounded once to bf16 (ties to even).  Random operands
+check |C - C_ref| <= tol * S with S = |alpha| sum |op(A)||op(B)| + |beta| |C0|
+(tol 1e-5 for fp32 inputs, 4e-3 for bf16 inputs), plus half a bf16 unit of
+C_ref for bf16 output.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+
+import dense_gemm_03_amd as dg
+import oracle
+from dense_gemm_03_amd import workloads as wl
+from tests.gpu_util import DIAGNOSTIC, TOL, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
+TRANS = list(itertools.product([False, True], [False, True]))
+TNAME = {(False, False): "NN", (False, True): "NT", (True, False): "TN", (True, True): "TT"}
+BF16_NAN = 0x7FC1       # sentinel in bf16 padding: a NaN pattern the library never writes
+
+
+def _ints(shape, seed, bf16):
+    return wl.small_int_bf16_bits(shape, seed) if bf16 else wl.small_int_f32(shape, seed)
+
+
+def _randn(shape, seed, bf16):
+    return wl.normal_bf16_bits(shape, seed) if bf16 else wl.uniform_f32(shape, seed)
+
+
+def _padded(x, extra, fill):
+    if extra == 0:
+        return x
+    buf = np.full((x.shape[0], x.shape[1] + extra), fill, dtype=x.dtype)
+    buf[:, :x.shape[1]] = x
+    return buf
+
+
+def _fill(dtype):
+    return np.uint16(BF16_NAN) if dtype == np.uint16 else np.float32(np.nan)
+
+
+def run_ex(A, B, ta, tb, alpha=1.0, beta=0.0, C0=None, out_bf16=False, cfg=None, split_k=0,
+           pad=0, pad_c=3):
+    """C := alpha op(A) op(B) + beta C on the GPU.  A, B are the stored
+    matrices (numpy; uint16 = bf16 bits).  C0 is the initial C as float64
+    (values representable in the output type) or None (C starts as NaN).
+    pad > 0 gives A and B leading dimensions of cols + pad (NaN padding); C
+    always sits in a NaN-padded buffer with pad_c extra columns.  Returns C
+    as float64 (decoded) and the raw padding columns."""
+    import torch
+    M = A.shape[1] if ta else A.shape[0]
+    N = B.shape[0] if tb else B.shape[1]
+    Ad = to_device(_padded(A, pad, _fill(A.dtype)))[:, :A.shape[1]]
+    Bd = to_device(_padded(B, pad, _fill(B.dtype)))[:, :B.shape[1]]
+    if out_bf16:
+        init = np.full((M, N + pad_c), BF16_NAN, dtype=np.uint16)
+        if C0 is not None:
+            init[:, :N] = oracle.round_to_bf16_bits(C0)
+        buf = torch.from_numpy(init.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    else:
+        init = np.full((M, N + pad_c), np.nan, dtype=np.float32)
+        if C0 is not None:
+            init[:, :N] = C0
+        buf = torch.from_numpy(init).to("cuda:0")
+    out = buf[:, :N]
+    dg.gemm(Ad, Bd, out=out, cfg=cfg, split_k=split_k, alpha=alpha, beta=beta, transa=ta,
+            transb=tb, out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    host = buf.cpu()
+    if out_bf16:
+        raw = host.view(torch.int16).numpy().view(np.uint16)
+        C = oracle.bf16_bits_to_f64(raw[:, :N])
+        guard = raw[:, N:]
+        assert np.all(guard == BF16_NAN), "bf16 padding of C was written"
+    else:
+        raw = host.numpy()
+        C = raw[:, :N].astype(np.float64)
+        assert np.all(np.isnan(raw[:, N:])), "padding of C was written"
+    return C, raw[:, :N]
+
+
+def expected(A, B, ta, tb, alpha, beta, C0):
+    kind = "bf16" if A.dtype == np.uint16 else "f32"
+    return oracle.gemm_general(A, B, alpha, beta, C0 if beta != 0.0 else None, ta, tb, kind=kind)
+
+
+def check_exact_ex(C_raw, A, B, ta, tb, alpha, beta, C0, out_bf16, what):
+    C_ref, _ = expected(A, B, ta, tb, alpha, beta, C0)
+    if out_bf16:
+        want = oracle.round_to_bf16_bits(C_ref)
+        bad = np.argwhere(C_raw != want)
+        assert bad.size == 0, "%s: %d entries differ, first %s: gpu %#06x want %#06x" % (
+            what, len(bad), tuple(bad[0]), int(C_raw[tuple(bad[0])]), int(want[tuple(bad[0])]))
+    else:
+        bad = np.argwhere(C_raw.astype(np.float64) != C_ref)
+        assert bad.size == 0, "%s: %d entries differ, first %s: gpu %r oracle %r" % (
+            what, len(bad), tuple(bad[0]), C_raw[tuple(bad[0])], C_ref[tuple(bad[0])])
+
+
+def check_close_ex(C, A, B, ta, tb, alpha, beta, C0, out_bf16, what):
+    """|C - C_ref| <= tol S (+ the bf16 output rounding: half a unit, at most
+    2^-8 |value|), and C exactly 0 where S == 0."""
+    dt = "bf16" if A.dtype == np.uint16 else "f32"
+    C_ref, S = expected(A, B, ta, tb, alpha, beta, C0)
+    err = np.abs(C - C_ref)
+    bound = TOL[dt] * S
+    if out_bf16:
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(C_ref)
+    pos = bound > 0
+    ratio = float(np.max(err[pos] / bound[pos])) if np.any(pos) else 0.0
+    plain = float(np.max(err[S > 0] / S[S > 0])) if np.any(S > 0) else 0.0
+    log("  %s: max err/bound = %.3e, max err/S = %.3e%s" % (
+        what, ratio, plain,
+        "  [diagnostic: above %.0e]" % DIAGNOSTIC if (plain > DIAGNOSTIC and not out_bf16) else ""))
+    assert np.all(np.isfinite(C)), "%s: non-finite output" % what
+    assert np.all(C[~pos] == 0.0), "%s: nonzero output where the scale is zero" % what
+    assert ratio <= 1.0, "%s: error %.3e of the bound" % (what, ratio)
+
+
+def _operands(M, N, K, ta, tb, gen, seed, bf16):
+    A = gen((K, M) if ta else (M, K), seed, bf16)
+    B = gen((N, K) if tb else (K, N), seed + 1, bf16)
+    return A, B
+
+
+SHAPES = [(1, 1, 1), (64, 64, 64), (300, 200, 100), (129, 257, 71), (33, 300, 1000), (520, 72, 260)]
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_exact_every_layout_every_config(bf16):
+    """Every table entry, every operand layout it is built for, aligned and
+    unaligned leading dimensions: bitwise against the oracle."""
+    dtype = BF16 if bf16 else F32
+    for cfg in range(dg.gemm_num_configs(dtype)):
+        name = dg.gemm_config_name(dtype, cfg)
+        mask = dg.gemm_config_layouts(dtype, cfg)
+        for ta, tb in TRANS:
+            if not mask & (1 << (2 * ta + tb)):
+                continue
+            for t, (M, N, K) in enumerate(SHAPES):
+                A, B = _operands(M, N, K, ta, tb, _ints, 30 + t, bf16)
+                for pad in (0, 1):
+                    what = "%s %s %dx%dx%d pad %d" % (name, TNAME[ta, tb], M, N, K, pad)
+                    log(what)
+                    _, raw = run_ex(A, B, ta, tb, cfg=cfg, pad=pad)
+                    check_exact_ex(raw, A, B, ta, tb, 1.0, 0.0, None, False, what)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("out_bf16", [False, True], ids=["c_f32", "c_bf16"])
+def test_exact_alpha_beta(bf16, out_bf16):
+    """alpha/beta epilogue on integers, with the dispatcher's choice and with
+    forced split-K (the reduce applies alpha, beta and the output type)."""
+    rng_c = np.random.default_rng(4)
+    for (M, N, K) in [(300, 200, 100), (70, 520, 3001), (257, 129, 64)]:
+        C0 = rng_c.integers(-9, 10, size=(M, N)).astype(np.float64)
+        for ta, tb in TRANS:
+            A, B = _operands(M, N, K, ta, tb, _ints, 7, bf16)
+            for alpha, beta in [(2.0, -3.0), (1.0, 1.0), (-1.0, 0.0), (0.5, 0.0), (1.0, 0.0)]:
+                for split in (0, 3):
+                    what = "%s %dx%dx%d a=%g b=%g split %d %s" % (
+                        TNAME[ta, tb], M, N, K, alpha, beta, split, "c_bf16" if out_bf16 else "c_f32")
+                    log(what)
+                    # integers * 0.5 stay exact in fp32; bf16 C holds them once rounded
+                    _, raw = run_ex(A, B, ta, tb, alpha, beta, C0, out_bf16, split_k=split)
+                    check_exact_ex(raw, A, B, ta, tb, alpha, beta, C0, out_bf16, what)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_random_within_tolerance(bf16):
+    rng_c = np.random.default_rng(8)
+    M, N, K = 333, 301, 517
+    for ta, tb in TRANS:
+        A, B = _operands(M, N, K, ta, tb, _randn, 11, bf16)
+        for out_bf16 in (False, True):
+            C0 = rng_c.standard_normal((M, N))
+            C0 = oracle.bf16_bits_to_f64(oracle.round_to_bf16_bits(C0)) if out_bf16 \
+                else C0.astype(np.float32).astype(np.float64)
+            for alpha, beta, split in [(0.75, -1.25, 0), (1.0, 0.0, 0), (-2.0, 0.5, 4)]:
+                what = "%s a=%g b=%g split %d %s" % (TNAME[ta, tb], alpha, beta, split,
+                                                     "c_bf16" if out_bf16 else "c_f32")
+                C, _ = run_ex(A, B, ta, tb, alpha, beta, C0, out_bf16, split_k=split)
+                check_close_ex(C, A, B, ta, tb, alpha, beta, C0, out_bf16, what)
+
+
+def test_beta_zero_does_not_read_c_and_alpha_zero_does_not_read_ab():
+    """beta == 0: a NaN-filled C is overwritten, never read.  alpha == 0: A and
+    B (NaN-filled) are not read and C := beta * C.  Both output types, and on
+    the split-K path."""
+    M, N, K = 150, 130, 400
+    for bf16 in (False, True):
+        for ta, tb in TRANS:
+            A, B = _operands(M, N, K, ta, tb, _ints, 3, bf16)
+            for out_bf16 in (False, True):
+                for split in (0, 4):
+                    C, raw = run_ex(A, B, ta, tb, 3.0, 0.0, None, out_bf16, split_k=split)
+                    check_exact_ex(raw, A, B, ta, tb, 3.0, 0.0, None, out_bf16, "beta 0 NaN C")
+            nanA = np.full(A.shape, _fill(A.dtype))
+            nanB = np.full(B.shape, _fill(B.dtype))
+            C0 = np.arange(M * N, dtype=np.float64).reshape(M, N) % 97 - 48
+            for out_bf16 in (False, True):
+                C, raw = run_ex(nanA, nanB, ta, tb, 0.0, -2.0, C0, out_bf16)
+                want = -2.0 * C0
+                assert np.array_equal(C, want), "alpha == 0 must give beta * C"
+
+
+def test_k_zero_scales_c():
+    """K == 0 (empty sum): C := beta * C, or 0 when beta == 0."""
+    M, N = 37, 45
+    C0 = np.arange(M * N, dtype=np.float64).reshape(M, N) % 13 - 6
+    for bf16 in (False, True):
+        dt = np.uint16 if bf16 else np.float32
+        for ta, tb in TRANS:
+            A = np.zeros((0, M) if ta else (M, 0), dtype=dt)
+            B = np.zeros((N, 0) if tb else (0, N), dtype=dt)
+            for out_bf16 in (False, True):
+                C, _ = run_ex(A, B, ta, tb, 5.0, 0.25, C0, out_bf16)
+                assert np.array_equal(C, 0.25 * C0)
+                C, _ = run_ex(A, B, ta, tb, 5.0, 0.0, None, out_bf16)
+                assert np.all(C == 0.0)
+
+
+def test_bf16_output_rounds_to_nearest_even():
+    """Results at exact bf16 midpoints: sums 257, 259, -385 (halfway cases)
+    and 1 + 2^-8 (with alpha) must round to the even neighbour."""
+    # A is 1 x K of ones, B holds the value in its first row: C = alpha * value
+    for value, alpha in [(257.0, 1.0), (259.0, 1.0), (-385.0, 1.0), (257.0, 2.0 ** -8)]:
+        A = np.ones((4, 1), dtype=np.float32)
+        B = np.full((1, 8), value, dtype=np.float32)
+        _, raw = run_ex(A, B, False, False, alpha, 0.0, None, True)
+        want = oracle.round_to_bf16_bits(np.full((4, 8), value * alpha))
+        assert np.array_equal(raw, want), (value, alpha, raw[0, 0], want[0, 0])
+
+
+def test_variants_deterministic():
+    import torch
+    M, N, K = 512, 384, 2048
+    A = to_device(wl.normal_bf16_bits((K, M), 1))
+    B = to_device(wl.normal_bf16_bits((N, K), 2))
+    C0 = torch.randn((M, N), device="cuda:0").to(torch.bfloat16)
+    outs = []
+    for _ in range(3):
+        C = C0.clone()
+        dg.gemm(A, B, out=C, alpha=0.5, beta=2.0, transa=True, transb=True)
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
