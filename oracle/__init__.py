@@ -23,6 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_SOURCES = [_SRC, os.path.join(_HERE, "conv.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # Plain C, no fast-math, no FMA contraction: every product of two fp32 or bf16
@@ -32,9 +33,10 @@ CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-ffp-contract=off"
 
 
 def build() -> str:
-    """Compile ``oracle.c`` into ``liboracle.so`` with gcc.  Returns the path."""
+    """Compile ``oracle.c`` and ``conv.c`` into ``liboracle.so`` with gcc.
+    Returns the path."""
     tmp = _LIB + ".tmp%d" % os.getpid()
-    subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, *_SOURCES, "-lm"], check=True)
     os.replace(tmp, _LIB)
     return _LIB
 
@@ -46,7 +48,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(src)
+                                       for src in _SOURCES):
         build()
     lib = ctypes.CDLL(_LIB)
     i64, p = ctypes.c_int64, ctypes.c_void_p
