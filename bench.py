@@ -17,6 +17,9 @@ in HBM.  Prints ONE JSON line:
                           (bf16 8192^3), and with --all for the im2col and
                           tall-skinny shapes and the generalised-GEMM variants
                           (transposed operands, alpha/beta, bf16 C)
+  convolution             with --all: the im2col + GEMM convolution of the
+                          64-channel 31x31-filter workload (forward, filter
+                          gradient, and the im2col kernel against HBM)
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -39,6 +42,7 @@ HBM_PEAK_GBS = 8000.0
 PRIMARY = "fp32-4096"
 SECONDARY = ["bf16-8192"]
 EXTRA = ["im2col", "tall", "bf16-8192-nt-bf16c", "bf16-8192-tn-acc", "fp32-4096-tt-ab"]
+CONV = ["conv-64c-31k", "conv-64c-31k-bf16"]
 
 
 def log(msg: str) -> None:
@@ -156,6 +160,86 @@ def measure(name: str, steps: int, warmup: int):
     return res
 
 
+def measure_conv(name: str, steps: int, warmup: int):
+    """Time the im2col + GEMM convolution `name`: the forward pass, the filter
+    gradient, and the im2col kernel alone (its HBM roofline)."""
+    import ctypes
+
+    import torch
+
+    import dense_gemm_03_amd as dg
+    from dense_gemm_03_amd.workloads import CONV_WORKLOADS
+
+    c = CONV_WORKLOADS[name]
+    log("[bench] %s: drawing x %s, filters and output gradient" % (name, (c.batch, c.cin, c.h, c.w)))
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        return torch.from_numpy(a).to("cuda:0")
+
+    x, w, dy = dev(c.x()), dev(c.weights()), dev(c.dy())
+    dtype = dg.GEMM_DTYPE_F32 if c.dtype == "f32" else dg.GEMM_DTYPE_BF16
+    params = dg.conv2d_params(c.batch, c.cin, c.h, c.w, c.cout, c.r, c.s, (c.pad, c.pad),
+                              (c.stride, c.stride), (c.dilation, c.dilation))
+    need = dg.conv2d_workspace_size(dtype, params)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty((c.batch, c.cout, c.p, c.q), dtype=torch.float32, device="cuda:0")
+    dw = torch.empty((c.cout, c.cin, c.r, c.s), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    ld = need // (c.crs * c.in_bytes)
+
+    def fwd():
+        assert dg.conv2d_fwd(dtype, dg.GEMM_DTYPE_F32, params, x.data_ptr(), w.data_ptr(),
+                             y.data_ptr(), ws.data_ptr(), need, sp) == dg.GEMM_OK
+
+    def wgrad():
+        assert dg.conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                                    ws.data_ptr(), need, sp) == dg.GEMM_OK
+
+    def im2col():
+        assert dg.conv2d_im2col(dtype, params, 0, x.data_ptr(), ws.data_ptr(), ld, sp) == dg.GEMM_OK
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n, e0.elapsed_time(e1) / n
+
+    res = {}
+    peak = PEAK_TFLOPS[c.dtype]
+    for label, fn in (("fwd", fwd), ("wgrad", wgrad)):
+        wall_ms, ev_ms = timed(fn, steps)
+        log("[bench] %s %s: %.3f ms per call" % (name, label, ev_ms))
+        ach = c.flops / (ev_ms * 1e-3) / 1e12
+        res[label] = {"value": c.flops / (wall_ms * 1e-3) / 1e12, "ms_per_step": wall_ms,
+                      "roofline": {"bound": "mfma", "achieved": ach, "peak": peak,
+                                   "unit": "TFLOP/s", "frac": ach / peak, "traffic": None}}
+    _, ev_ms = timed(im2col, steps)
+    gbs = c.im2col_bytes / (ev_ms * 1e-3) / 1e9
+    traffic = stored_traffic(name + "-im2col")
+    res["im2col"] = {"ms_per_call": ev_ms,
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}}
+    log("[bench] %s im2col: %.3f ms, %.0f GB/s" % (name, ev_ms, gbs))
+    out = {"workload": name, "dtype": c.dtype,
+           "shape": {"batch": c.batch, "cin": c.cin, "hw": [c.h, c.w], "cout": c.cout,
+                     "rs": [c.r, c.s], "pad": c.pad, "stride": c.stride, "dilation": c.dilation},
+           "gemm_fwd": [c.cout, c.p * c.q, c.crs], "gemm_wgrad": [c.cout, c.crs, c.p * c.q]}
+    out.update(res)
+    del x, w, dy, ws, y, dw
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(name: str, budget_s: float = 10.0):
     """The oracle on a bounded row sample of the workload, scaled to TFLOP/s."""
     import oracle
@@ -212,6 +296,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true",
                     help="time only --workload (for per-kernel profiler passes)")
+    ap.add_argument("--conv", default=None, metavar="NAME",
+                    help="only time the convolution workload NAME (for per-kernel profiler "
+                         "passes) and print its result")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference kernel "
                          "for the HBM byte counters) and exit")
@@ -238,6 +325,10 @@ def main() -> int:
 
     import dense_gemm_03_amd as dg
     dg.load_library()
+    if args.conv:
+        print(json.dumps({"convolution": {args.conv: measure_conv(args.conv, args.steps,
+                                                                   args.warmup)}}), flush=True)
+        return 0
 
     main_res = measure(args.workload, args.steps, args.warmup)
     also = {}
@@ -245,6 +336,11 @@ def main() -> int:
         n for n in SECONDARY + (EXTRA if args.all else []) if n != args.workload]
     for n in others:
         also[n] = measure(n, max(10, args.steps // 2), max(20, args.warmup))
+
+    conv = {}
+    if args.all and not args.no_also:
+        for n in CONV:
+            conv[n] = measure_conv(n, max(10, args.steps // 5), max(5, args.warmup // 5))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -278,6 +374,8 @@ def main() -> int:
                                         "c_dtype", "kernel_config", "split_k", "roofline",
                                         "hbm_gbs")} for n, r in also.items()},
     }
+    if conv:
+        line["convolution"] = conv
     print(json.dumps(line), flush=True)
     return 0
 

@@ -1,7 +1,9 @@
 """MI355X-native dense GEMM on gfx950 matrix cores: C = A . B, and the
-generalised C = alpha * op(A) * op(B) + beta * C with fp32 or bf16 C.
+generalised C = alpha * op(A) * op(B) + beta * C with fp32 or bf16 C; and 2-D
+convolution (forward and filter gradient) as im2col + that GEMM.
 
-A thin ctypes binding over the C ABI of ``include/gemm.h`` (library
+A thin ctypes binding over the C ABI of ``include/gemm.h`` and
+``include/conv.h`` (library
 ``libdense_gemm.so`` next to this file).  The functions of the same names take
 the same arguments as the C entry points -- sizes, device pointers as
 integers, leading dimensions and a stream handle -- and only marshal them;
@@ -47,6 +49,25 @@ SIGNATURES = {
     "gemm_ex_with_config": (_int, [_int, _int] + _GEMM_EX_ARGS),
     "gemm_config_layouts": (_int, [_int, _int]),
 }
+
+
+
+class Conv2dParams(ctypes.Structure):
+    """conv2d_params of include/conv.h."""
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "batch", "in_channels", "height", "width", "out_channels", "kernel_h", "kernel_w",
+        "pad_h", "pad_w", "stride_h", "stride_w", "dilation_h", "dilation_w")]
+
+
+_pp = ctypes.POINTER(Conv2dParams)
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+SIGNATURES.update({
+    "conv2d_output_size": (_int, [_pp, _pi64, _pi64]),
+    "conv2d_workspace_size": (_i64, [_int, _pp]),
+    "conv2d_im2col": (_int, [_int, _pp, _i64, _p, _p, _i64, _p]),
+    "conv2d_fwd": (_int, [_int, _int, _pp, _p, _p, _p, _p, _i64, _p]),
+    "conv2d_bwd_weight": (_int, [_int, _pp, _p, _p, _p, _p, _i64, _p]),
+})
 
 _lib = None
 
@@ -208,3 +229,110 @@ def gemm(A, B, out=None, cfg: int | None = None, split_k: int = 0, stream=None, 
     if rc != GEMM_OK:
         raise GemmError(rc)
     return out
+
+
+# ------------------------------------------------------------ convolution --
+
+def conv2d_params(batch, in_channels, height, width, out_channels, kernel_h, kernel_w,
+                  pad=(0, 0), stride=(1, 1), dilation=(1, 1)) -> Conv2dParams:
+    return Conv2dParams(batch, in_channels, height, width, out_channels, kernel_h, kernel_w,
+                        pad[0], pad[1], stride[0], stride[1], dilation[0], dilation[1])
+
+
+def conv2d_output_size(params: Conv2dParams):
+    """(status, P, Q)."""
+    ph, pw = ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = load_library().conv2d_output_size(ctypes.byref(params), ctypes.byref(ph), ctypes.byref(pw))
+    return rc, ph.value, pw.value
+
+
+def conv2d_workspace_size(dtype: int, params: Conv2dParams) -> int:
+    return load_library().conv2d_workspace_size(dtype, ctypes.byref(params))
+
+
+def conv2d_im2col(dtype, params, image, x, cols, ld_cols, stream=None) -> int:
+    return load_library().conv2d_im2col(dtype, ctypes.byref(params), image, x, cols, ld_cols, stream)
+
+
+def conv2d_fwd(dtype, dtype_y, params, x, w, y, workspace, workspace_bytes, stream=None) -> int:
+    return load_library().conv2d_fwd(dtype, dtype_y, ctypes.byref(params), x, w, y, workspace,
+                                     workspace_bytes, stream)
+
+
+def conv2d_bwd_weight(dtype, params, x, dy, dw, workspace, workspace_bytes, stream=None) -> int:
+    return load_library().conv2d_bwd_weight(dtype, ctypes.byref(params), x, dy, dw, workspace,
+                                            workspace_bytes, stream)
+
+
+def _pair(v):
+    return (v, v) if isinstance(v, int) else tuple(v)
+
+
+def _conv_setup(x, weight_shape, stride, padding, dilation):
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16) or x.device.type != "cuda" or x.dim() != 4:
+        raise TypeError("x must be a 4-D float32 or bfloat16 GPU tensor (N, C, H, W)")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (channel-first)")
+    co, ci, r, s = weight_shape
+    if ci != x.shape[1]:
+        raise ValueError("channel mismatch: x has %d, the filters %d" % (x.shape[1], ci))
+    params = conv2d_params(x.shape[0], ci, x.shape[2], x.shape[3], co, r, s, _pair(padding),
+                           _pair(stride), _pair(dilation))
+    dtype = GEMM_DTYPE_BF16 if x.dtype == torch.bfloat16 else GEMM_DTYPE_F32
+    rc, P, Q = conv2d_output_size(params)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    need = conv2d_workspace_size(dtype, params)
+    return params, dtype, P, Q, need
+
+
+def _workspace(workspace, need, device):
+    import torch
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace of %d bytes needed" % need)
+    return workspace
+
+
+def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None):
+    """y = conv2d(x, w) through the im2col + GEMM path (cross-correlation form,
+    as torch.nn.functional.conv2d).  x (N, C_in, H, W) and w (C_out, C_in, R, S)
+    are both float32 or both bfloat16; y is float32 (default) or bfloat16.
+    The workspace (one image's convolution matrix) is allocated when not given."""
+    import torch
+    if w.dtype != x.dtype or not w.is_contiguous() or w.dim() != 4:
+        raise TypeError("w must be a contiguous 4-D tensor of x's dtype")
+    params, dtype, P, Q, need = _conv_setup(x, tuple(w.shape), stride, padding, dilation)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    y = torch.empty((x.shape[0], w.shape[0], P, Q), dtype=out_dtype, device=x.device)
+    ws = _workspace(workspace, need, x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = conv2d_fwd(dtype, GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32,
+                    params, x.data_ptr(), w.data_ptr(), y.data_ptr(), ws.data_ptr(),
+                    ws.numel() * ws.element_size(), stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return y
+
+
+def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, workspace=None,
+                       stream=None):
+    """dw (float32, weight_shape) = the filter gradient of conv2d for input x
+    and output gradient dy, through the im2col + GEMM path."""
+    import torch
+    params, dtype, P, Q, need = _conv_setup(x, tuple(weight_shape), stride, padding, dilation)
+    if dy.dtype != x.dtype or not dy.is_contiguous() or \
+            tuple(dy.shape) != (x.shape[0], weight_shape[0], P, Q):
+        raise ValueError("dy must be a contiguous (N, C_out, P, Q) tensor of x's dtype")
+    dw = torch.empty(tuple(weight_shape), dtype=torch.float32, device=x.device)
+    ws = _workspace(workspace, need, x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                           ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return dw

@@ -26,7 +26,8 @@ LIB = os.path.join(HERE, "libdense_gemm.so")
 # parallel.
 SOURCES = [("gemm_api.hip", "gemm_api", []),
            ("gemm_tables.hip", "gemm_tables", []),
-           ("gemm_aux.hip", "gemm_aux", [])]
+           ("gemm_aux.hip", "gemm_aux", []),
+           ("conv.hip", "conv", [])]
 for _dtype in ("F32", "BF16"):
     for _layout in ("NN", "NT", "TN", "TT"):
         SOURCES.append(("gemm_instances.hip", "gemm_%s_%s" % (_dtype.lower(), _layout.lower()),

@@ -9,6 +9,7 @@
 
 #include "gemm.h"
 #include "gemm_configs.hpp"
+#include "gemm_internal.hpp"
 
 namespace dg {
 namespace {
@@ -177,20 +178,7 @@ int elem_size(int dtype) { return dtype == GEMM_DTYPE_F32 ? 4 : 2; }
 
 bool valid_dtype(int dtype) { return dtype == GEMM_DTYPE_F32 || dtype == GEMM_DTYPE_BF16; }
 
-// One call, after the public entry points have named its variant.
-struct Call {
-    int dtype;      // of A and B
-    int dtype_c;    // of C
-    int transa, transb;
-    int64_t M, N, K;
-    float alpha, beta;
-    const void *A;
-    int64_t lda;
-    const void *B;
-    int64_t ldb;
-    void *C;
-    int64_t ldc;
-};
+using Call = GemmCall;
 
 int check_args(const Call &c)
 {
@@ -217,7 +205,7 @@ int check_args(const Call &c)
     return GEMM_OK;
 }
 
-int run(const Call &call, int forced_cfg, int forced_split, hipStream_t stream)
+int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t stream)
 {
     int rc = check_args(call);
     if (rc != GEMM_OK) return rc;
@@ -306,6 +294,12 @@ Call plain_call(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64
 }
 
 }  // namespace
+
+int gemm_run(const GemmCall &call, int forced_cfg, int forced_split, hipStream_t stream)
+{
+    return run_call(call, forced_cfg, forced_split, stream);
+}
+
 }  // namespace dg
 
 extern "C" {
@@ -313,13 +307,13 @@ extern "C" {
 int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
              int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
 {
-    return dg::run(dg::plain_call(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc), -1, 0, stream);
+    return dg::gemm_run(dg::plain_call(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc), -1, 0, stream);
 }
 
 int gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
               int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
 {
-    return dg::run(dg::plain_call(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc), -1, 0, stream);
+    return dg::gemm_run(dg::plain_call(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc), -1, 0, stream);
 }
 
 int gemm_f32_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K, const float *A,
@@ -327,7 +321,7 @@ int gemm_f32_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K, 
                          hipStream_t stream)
 {
     if (cfg < 0) return GEMM_ERR_INVALID_ARG;
-    return dg::run(dg::plain_call(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc), cfg, split_k,
+    return dg::gemm_run(dg::plain_call(GEMM_DTYPE_F32, M, N, K, A, lda, B, ldb, C, ldc), cfg, split_k,
                    stream);
 }
 
@@ -336,7 +330,7 @@ int gemm_bf16_with_config(int cfg, int split_k, int64_t M, int64_t N, int64_t K,
                           float *C, int64_t ldc, hipStream_t stream)
 {
     if (cfg < 0) return GEMM_ERR_INVALID_ARG;
-    return dg::run(dg::plain_call(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc), cfg, split_k,
+    return dg::gemm_run(dg::plain_call(GEMM_DTYPE_BF16, M, N, K, A, lda, B, ldb, C, ldc), cfg, split_k,
                    stream);
 }
 
@@ -344,7 +338,7 @@ int gemm_ex(int dtype_ab, int dtype_c, int transa, int transb, int64_t M, int64_
             float alpha, const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
             void *C, int64_t ldc, hipStream_t stream)
 {
-    return dg::run(dg::Call{dtype_ab, dtype_c, transa, transb, M, N, K, alpha, beta, A, lda, B,
+    return dg::gemm_run(dg::Call{dtype_ab, dtype_c, transa, transb, M, N, K, alpha, beta, A, lda, B,
                             ldb, C, ldc},
                    -1, 0, stream);
 }
@@ -355,7 +349,7 @@ int gemm_ex_with_config(int cfg, int split_k, int dtype_ab, int dtype_c, int tra
                         hipStream_t stream)
 {
     if (cfg < 0) return GEMM_ERR_INVALID_ARG;
-    return dg::run(dg::Call{dtype_ab, dtype_c, transa, transb, M, N, K, alpha, beta, A, lda, B,
+    return dg::gemm_run(dg::Call{dtype_ab, dtype_c, transa, transb, M, N, K, alpha, beta, A, lda, B,
                             ldb, C, ldc},
                    cfg, split_k, stream);
 }

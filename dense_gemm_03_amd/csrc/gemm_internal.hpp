@@ -1,0 +1,31 @@
+// Library-internal entry into the GEMM dispatcher, for the other operations
+// built on the GEMM (the im2col convolution).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// One generalised product C := alpha * op(A) * op(B) + beta * C, with the
+// argument meaning of gemm_ex in include/gemm.h.
+struct GemmCall {
+    int dtype;      // of A and B (GEMM_DTYPE_*)
+    int dtype_c;    // of C
+    int transa, transb;
+    int64_t M, N, K;
+    float alpha, beta;
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    void *C;
+    int64_t ldc;
+};
+
+// Checks the arguments, picks a tile entry (or uses forced_cfg >= 0) and a
+// split-K plan (forced_split > 0 forces it), and launches on `stream`.
+// Returns a gemm_status.
+int gemm_run(const GemmCall &call, int forced_cfg, int forced_split, hipStream_t stream);
+
+}  // namespace dg

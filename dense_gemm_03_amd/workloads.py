@@ -32,7 +32,20 @@ name                base        op     alpha  beta   C
 bf16-8192-nt-bf16c  bf16-8192   A B^T  1      0      bf16
 bf16-8192-tn-acc    bf16-8192   A^T B  0.5    1      fp32
 fp32-4096-tt-ab     fp32-4096   A^T B^T 1.5   -0.5   fp32
-==================  ==========  =====  =====  =====  ==========  Large operands are drawn in row chunks; the
+==================  ==========  =====  =====  =====  ==========
+
+Convolutions (``CONV_WORKLOADS``, channel-first; "Three X's: large
+convolutions in PyTorch for model training"): x, filters and output gradient
+drawn with ``seed``, ``seed + 1000`` and ``seed + 2000``, uniform[-1, 1] (fp32)
+or normal(0, 1) rounded to bf16:
+
+==================  =====  ======  ========  =====  ======  ===  ====
+name                batch  C_in    H x W     C_out  R x S   pad  seed
+==================  =====  ======  ========  =====  ======  ===  ====
+conv-64c-31k        1      64      128x128   64     31x31   15   108
+conv-64c-31k-bf16   1      64      128x128   64     31x31   15   109
+conv-small-batch    4      16      40x36     24     5x3     2    110
+==================  =====  ======  ========  =====  ======  ===  ====  Large operands are drawn in row chunks; the
 PCG64 stream yields the same values whether drawn at once or in chunks.
 
 The im2col shape is the weight-gradient GEMM of a 2-D convolution with a large
@@ -149,16 +162,26 @@ def _rows_per_chunk(cols: int) -> int:
     return max(1, _CHUNK_ELEMS // max(cols, 1))
 
 
+def _rows_cols(shape):
+    """An N-D shape seen as (product of the leading dimensions, last dimension):
+    values are drawn row by row of that 2-D view, so a 2-D shape draws exactly
+    what it always did."""
+    shape = tuple(int(d) for d in shape)
+    if len(shape) == 1:
+        return 1, shape[0], shape
+    return int(np.prod(shape[:-1], dtype=np.int64)), shape[-1], shape
+
+
 def uniform_f32(shape, seed: int) -> np.ndarray:
     """i.i.d. uniform[-1, 1) float32 values (drawn in float64, then rounded)."""
-    rows, cols = shape
+    rows, cols, shape = _rows_cols(shape)
     rng = np.random.default_rng(seed)
     out = np.empty((rows, cols), dtype=np.float32)
     step = _rows_per_chunk(cols)
     for r in range(0, rows, step):
         r1 = min(rows, r + step)
         out[r:r1] = rng.uniform(-1.0, 1.0, size=(r1 - r, cols))
-    return out
+    return out.reshape(shape)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -172,14 +195,14 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def normal_bf16_bits(shape, seed: int) -> np.ndarray:
     """i.i.d. standard normal values, drawn as float32 and rounded to bf16."""
-    rows, cols = shape
+    rows, cols, shape = _rows_cols(shape)
     rng = np.random.default_rng(seed)
     out = np.empty((rows, cols), dtype=np.uint16)
     step = _rows_per_chunk(cols)
     for r in range(0, rows, step):
         r1 = min(rows, r + step)
         out[r:r1] = f32_to_bf16_bits(rng.standard_normal(size=(r1 - r, cols), dtype=np.float32))
-    return out
+    return out.reshape(shape)
 
 
 def small_int_f32(shape, seed: int, lo: int = -3, hi: int = 3) -> np.ndarray:
@@ -205,3 +228,79 @@ def sample_positions(M: int, N: int, count: int, seed: int):
     I = np.concatenate([np.array(fixed_i), rng.integers(0, M, size=extra)])
     J = np.concatenate([np.array(fixed_j), rng.integers(0, N, size=extra)])
     return I.astype(np.int64), J.astype(np.int64)
+
+
+# ------------------------------------------------------------ convolutions --
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    """A 2-D convolution, channel-first: x (batch, cin, h, w), filters
+    (cout, cin, r, s), output (batch, cout, p, q)."""
+    name: str
+    dtype: str  # "f32" or "bf16" (x, w and dy)
+    batch: int
+    cin: int
+    h: int
+    w: int
+    cout: int
+    r: int
+    s: int
+    pad: int
+    stride: int
+    dilation: int
+    seed: int
+
+    @property
+    def p(self) -> int:
+        return (self.h + 2 * self.pad - self.dilation * (self.r - 1) - 1) // self.stride + 1
+
+    @property
+    def q(self) -> int:
+        return (self.w + 2 * self.pad - self.dilation * (self.s - 1) - 1) // self.stride + 1
+
+    @property
+    def crs(self) -> int:
+        return self.cin * self.r * self.s
+
+    @property
+    def flops(self) -> int:
+        """Multiply-adds of the forward pass (or of the filter gradient) x 2."""
+        return 2 * self.batch * self.cout * self.p * self.q * self.crs
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def im2col_bytes(self) -> int:
+        """Compulsory HBM bytes of one image's convolution matrix: read the
+        image once, write the matrix once."""
+        return (self.cin * self.h * self.w + self.crs * self.p * self.q) * self.in_bytes
+
+    def _draw(self, shape, seed):
+        if self.dtype == "f32":
+            return uniform_f32(shape, seed)
+        return normal_bf16_bits(shape, seed)
+
+    def x(self):
+        return self._draw((self.batch, self.cin, self.h, self.w), self.seed)
+
+    def weights(self):
+        return self._draw((self.cout, self.cin, self.r, self.s), self.seed + 1000)
+
+    def dy(self):
+        return self._draw((self.batch, self.cout, self.p, self.q), self.seed + 2000)
+
+
+# The large-kernel convolution whose forward GEMM is the im2col workload above
+# (64 x 16384 x 61504): 64 channels in and out, 31 x 31 filters, 128 x 128
+# images with "same" zero padding.  Its filter gradient is the GEMM
+# 64 x 61504 x 16384 with the convolution matrix transposed.
+CONV_WORKLOADS = {
+    c.name: c
+    for c in [
+        ConvWorkload("conv-64c-31k", "f32", 1, 64, 128, 128, 64, 31, 31, 15, 1, 1, 108),
+        ConvWorkload("conv-64c-31k-bf16", "bf16", 1, 64, 128, 128, 64, 31, 31, 15, 1, 1, 109),
+        ConvWorkload("conv-small-batch", "f32", 4, 16, 40, 36, 24, 5, 3, 2, 1, 1, 110),
+    ]
+}

@@ -1,0 +1,256 @@
+"""GPU parity of the im2col + GEMM convolution ("Three X's: a new level of
+working with large convolutions in PyTorch for model training") against the
+direct-convolution oracle, through the C ABI (include/conv.h).
+
+* The im2col kernel is a copy with zero fill: its convolution matrix must
+  equal the oracle's bit for bit (both element types), and columns beyond P Q
+  of a padded leading dimension must stay untouched.
+* Forward and filter gradient on integer-valued tensors: every sum is exact,
+  so results equal the oracle bit for bit (bf16 y: the exact value rounded
+  once to bf16).
+* Random tensors: |y - y_ref| <= tol * S with S the sum of |products|
+  (1e-5 for fp32, 4e-3 for bf16 inputs), plus half a bf16 unit for bf16 y.
+* The full-size large-kernel convolution at sampled outputs and taps.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dense_gemm_03_amd as dg
+import oracle
+from dense_gemm_03_amd import workloads as wl
+from oracle import conv as oc
+from oracle.conv import ConvShape
+from tests.gpu_util import DIAGNOSTIC, TOL, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
+
+SHAPES = [
+    # batch, cin, h, w, cout, r, s, ph, pw, sh, sw, dh, dw
+    ConvShape(1, 1, 3, 3, 1, 3, 3, 1, 1),                     # the page's worked example
+    ConvShape(2, 3, 17, 13, 5, 3, 3, 1, 1),
+    ConvShape(1, 4, 20, 23, 6, 5, 2, 2, 0, 2, 3),             # strides
+    ConvShape(2, 2, 19, 21, 3, 3, 4, 3, 1, 1, 2, 2, 3),       # dilation, uneven padding
+    ConvShape(1, 8, 9, 64, 4, 1, 7, 0, 3, 1, 1),              # 1 x S filters, wide rows
+    ConvShape(3, 5, 33, 31, 7, 7, 7, 3, 3),                   # P Q = 1023, ragged tiles
+    ConvShape(1, 2, 40, 1100, 3, 3, 3, 1, 1, 1, 1),           # Q = 1100: P Q > one block row
+    ConvShape(1, 3, 6, 6, 2, 6, 6, 0, 0),                     # filter covers the image: P = Q = 1
+]
+
+
+def _dev(a):
+    return to_device(np.ascontiguousarray(a))
+
+
+def _ints(shape, seed, bf16):
+    return wl.small_int_bf16_bits(shape, seed) if bf16 else wl.small_int_f32(shape, seed)
+
+
+def _randn(shape, seed, bf16):
+    return wl.normal_bf16_bits(shape, seed) if bf16 else wl.uniform_f32(shape, seed)
+
+
+def _params(c: ConvShape):
+    return dg.conv2d_params(c.batch, c.cin, c.h, c.w, c.cout, c.r, c.s, (c.ph, c.pw), (c.sh, c.sw),
+                            (c.dh, c.dw))
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def run_im2col(x: np.ndarray, c: ConvShape, n: int, ld: int, rows=None):
+    """The library's convolution matrix of image n (all rows, or the listed
+    ones), written into a device buffer of ld + 5 columns prefilled with a
+    sentinel; columns beyond P Q must keep it."""
+    import torch
+    bf16 = x.dtype == np.uint16
+    sentinel = 0x7FC1 if bf16 else 0x7FC00001
+    buf = torch.full((c.crs, ld + 5), sentinel, dtype=torch.int16 if bf16 else torch.int32,
+                     device="cuda:0")
+    xd = _dev(x)
+    rc = dg.conv2d_im2col(BF16 if bf16 else F32, _params(c), n, xd.data_ptr(), buf.data_ptr(),
+                          ld + 5, _stream())
+    assert rc == dg.GEMM_OK
+    torch.cuda.synchronize()
+    if rows is not None:
+        buf = buf[torch.as_tensor(np.asarray(rows), device="cuda:0")]
+    got = buf.cpu().numpy().view(np.uint16 if bf16 else np.uint32)
+    assert np.all(got[:, c.p * c.q:] == sentinel), "columns beyond P Q were written"
+    return got[:, :c.p * c.q]
+
+
+def run_fwd(x, w, c: ConvShape, out_bf16=False):
+    import torch
+    y = dg.conv2d(_dev(x) if x.dtype == np.float32 else _dev(x), _dev(w), stride=(c.sh, c.sw),
+                  padding=(c.ph, c.pw), dilation=(c.dh, c.dw),
+                  out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    if out_bf16:
+        raw = y.cpu().view(torch.int16).numpy().view(np.uint16)
+        return oracle.bf16_bits_to_f64(raw), raw
+    raw = y.cpu().numpy()
+    return raw.astype(np.float64), raw
+
+
+def run_bwd(x, dy, c: ConvShape):
+    import torch
+    dw = dg.conv2d_weight_grad(_dev(x), _dev(dy), (c.cout, c.cin, c.r, c.s), stride=(c.sh, c.sw),
+                               padding=(c.ph, c.pw), dilation=(c.dh, c.dw))
+    torch.cuda.synchronize()
+    return dw.cpu().numpy().astype(np.float64)
+
+
+def check_close(got, ref, S, tol, what, out_bf16=False):
+    bound = tol * S
+    if out_bf16:
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
+    pos = bound > 0
+    ratio = float(np.max(np.abs(got - ref)[pos] / bound[pos])) if np.any(pos) else 0.0
+    plain = float(np.max(np.abs(got - ref)[S > 0] / S[S > 0])) if np.any(S > 0) else 0.0
+    log("  %s: max err/bound %.3e, max err/S %.3e%s" % (
+        what, ratio, plain, "  [diagnostic: above %.0e]" % DIAGNOSTIC
+        if plain > DIAGNOSTIC and not out_bf16 else ""))
+    assert np.all(np.isfinite(got)), what
+    assert np.all(got[~pos] == 0.0), "%s: nonzero where the scale is zero" % what
+    assert ratio <= 1.0, "%s: error %.3e of the bound" % (what, ratio)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_im2col_bit_exact(bf16):
+    for t, c in enumerate(SHAPES):
+        x = _randn(c.x_shape, 200 + t, bf16)
+        for n in sorted({0, c.batch - 1}):
+            log("im2col %s image %d" % (c, n))
+            got = run_im2col(x, c, n, c.p * c.q + 3 * t)
+            want = oc.im2col(x, c, n)
+            if not bf16:
+                want = want.view(np.uint32)
+            assert np.array_equal(got, want), "%s image %d" % (c, n)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_fwd_exact_integers(bf16):
+    for t, c in enumerate(SHAPES):
+        x, w = _ints(c.x_shape, 300 + t, bf16), _ints(c.w_shape, 310 + t, bf16)
+        ref, _ = oc.conv2d_fwd(x, w, c)
+        for out_bf16 in (False, True):
+            log("fwd %s y %s" % (c, "bf16" if out_bf16 else "f32"))
+            got, raw = run_fwd(x, w, c, out_bf16)
+            if out_bf16:
+                assert np.array_equal(raw, oracle.round_to_bf16_bits(ref)), str(c)
+            else:
+                assert np.array_equal(got, ref), str(c)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_bwd_weight_exact_integers(bf16):
+    for t, c in enumerate(SHAPES):
+        x, dy = _ints(c.x_shape, 400 + t, bf16), _ints(c.y_shape, 410 + t, bf16)
+        log("filter gradient %s" % (c,))
+        ref, _ = oc.conv2d_bwd_weight(x, dy, c)
+        assert np.array_equal(run_bwd(x, dy, c), ref), str(c)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_random_within_tolerance(bf16):
+    tol = TOL["bf16" if bf16 else "f32"]
+    for t, c in enumerate(SHAPES[1:], 1):
+        x, w = _randn(c.x_shape, 500 + t, bf16), _randn(c.w_shape, 510 + t, bf16)
+        dy = _randn(c.y_shape, 520 + t, bf16)
+        ref, S = oc.conv2d_fwd(x, w, c)
+        check_close(run_fwd(x, w, c)[0], ref, S, tol, "fwd %s" % (c,))
+        check_close(run_fwd(x, w, c, True)[0], ref, S, tol, "fwd bf16 y %s" % (c,), True)
+        ref, S = oc.conv2d_bwd_weight(x, dy, c)
+        check_close(run_bwd(x, dy, c), ref, S, tol, "filter gradient %s" % (c,))
+
+
+def test_empty_batch_and_workload_small_batch():
+    """batch 0: forward does nothing, the filter gradient is the empty sum
+    (zeros); and the small batched workload against the oracle."""
+    import torch
+    c = ConvShape(0, 3, 8, 8, 2, 3, 3, 1, 1)
+    p = _params(c)
+    dw = torch.full((2, 3, 3, 3), float("nan"), device="cuda:0")
+    assert dg.conv2d_bwd_weight(F32, p, None, None, dw.data_ptr(), None, 0, _stream()) == dg.GEMM_OK
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+    wk = wl.CONV_WORKLOADS["conv-small-batch"]
+    c = ConvShape(wk.batch, wk.cin, wk.h, wk.w, wk.cout, wk.r, wk.s, wk.pad, wk.pad, wk.stride,
+                  wk.stride, wk.dilation, wk.dilation)
+    x, w, dy = wk.x(), wk.weights(), wk.dy()
+    ref, S = oc.conv2d_fwd(x, w, c)
+    check_close(run_fwd(x, w, c)[0], ref, S, TOL["f32"], wk.name + " fwd")
+    ref, S = oc.conv2d_bwd_weight(x, dy, c)
+    check_close(run_bwd(x, dy, c), ref, S, TOL["f32"], wk.name + " filter gradient")
+
+
+def test_deterministic_repeats():
+    import torch
+    c = ConvShape(2, 8, 30, 30, 16, 5, 5, 2, 2)
+    x, w, dy = _dev(_randn(c.x_shape, 1, False)), _dev(_randn(c.w_shape, 2, False)), \
+        _dev(_randn(c.y_shape, 3, False))
+    ys = [dg.conv2d(x, w, padding=2) for _ in range(3)]
+    gs = [dg.conv2d_weight_grad(x, dy, (16, 8, 5, 5), padding=2) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(ys[0], y) for y in ys[1:])
+    assert all(torch.equal(gs[0], g) for g in gs[1:])
+
+
+def _shape_of(wk):
+    return ConvShape(wk.batch, wk.cin, wk.h, wk.w, wk.cout, wk.r, wk.s, wk.pad, wk.pad, wk.stride,
+                     wk.stride, wk.dilation, wk.dilation)
+
+
+@pytest.mark.parametrize("name", ["conv-64c-31k", "conv-64c-31k-bf16"])
+def test_full_size_sampled(name):
+    """The large-kernel convolution at full size: forward outputs and filter-
+    gradient taps at sampled positions against the oracle, one sum each, and
+    the convolution matrix bit for bit at sampled rows."""
+    wk = wl.CONV_WORKLOADS[name]
+    c = _shape_of(wk)
+    bf16 = wk.dtype == "bf16"
+    tol = TOL[wk.dtype]
+    x, w, dy = wk.x(), wk.weights(), wk.dy()
+    log("[%s] forward" % name)
+    y, _ = run_fwd(x, w, c)
+    rng = np.random.default_rng(wk.seed + 5)
+    idx = [np.zeros(256, np.int64), rng.integers(0, c.cout, 256), rng.integers(0, c.p, 256),
+           rng.integers(0, c.q, 256)]
+    idx[2][:4], idx[3][:4] = [0, 0, c.p - 1, c.p - 1], [0, c.q - 1, 0, c.q - 1]  # corners
+    ref, S = oc.conv2d_fwd_entries(x, w, c, *idx)
+    check_close(y[tuple(idx)], ref, S, tol, name + " fwd (256 sampled)")
+    log("[%s] filter gradient" % name)
+    dw = run_bwd(x, dy, c)
+    tidx = [rng.integers(0, d, 256) for d in c.w_shape]
+    tidx[2][:2], tidx[3][:2] = [0, c.r - 1], [0, c.s - 1]
+    ref, S = oc.conv2d_bwd_weight_entries(x, dy, c, *tidx)
+    check_close(dw[tuple(tidx)], ref, S, tol, name + " filter gradient (256 sampled)")
+    log("[%s] convolution matrix rows" % name)
+    rows = np.sort(rng.integers(0, c.crs, 16))
+    got = run_im2col(x, c, 0, c.p * c.q, rows=rows)
+    small = ConvShape(1, 1, c.h, c.w, 1, c.r, c.s, c.ph, c.pw, c.sh, c.sw, c.dh, c.dw)
+    for t, row in enumerate(rows):
+        ci, rs = divmod(int(row), c.r * c.s)
+        sub = oc.im2col(np.ascontiguousarray(x[:, ci:ci + 1]), small, 0)[rs]
+        assert np.array_equal(got[t], sub.view(np.uint16) if bf16 else sub.view(np.uint32)), row
+
+
+def test_full_size_exact_integers_sampled():
+    """Integer tensors of the full-size shape: sampled outputs and taps exact."""
+    wk = wl.CONV_WORKLOADS["conv-64c-31k"]
+    c = _shape_of(wk)
+    x, w, dy = _ints(c.x_shape, 7, False), _ints(c.w_shape, 8, False), _ints(c.y_shape, 9, False)
+    y, _ = run_fwd(x, w, c)
+    rng = np.random.default_rng(3)
+    idx = [np.zeros(256, np.int64)] + [rng.integers(0, d, 256) for d in c.y_shape[1:]]
+    ref, _ = oc.conv2d_fwd_entries(x, w, c, *idx)
+    assert np.array_equal(y[tuple(idx)], ref)
+    dw = run_bwd(x, dy, c)
+    tidx = [rng.integers(0, d, 256) for d in c.w_shape]
+    ref, _ = oc.conv2d_bwd_weight_entries(x, dy, c, *tidx)
+    assert np.array_equal(dw[tuple(tidx)], ref)

@@ -272,3 +272,20 @@ def test_generators_are_seeded_and_chunk_stable():
     assert np.array_equal(n, workloads.normal_bf16_bits((4, 5), 9))
     v = oracle.bf16_bits_to_f64(workloads.normal_bf16_bits((512, 512), 1))
     assert abs(v.mean()) < 0.01 and abs(v.std() - 1) < 0.01
+
+
+def test_generators_nd_shapes_and_conv_workloads():
+    """N-D shapes draw the same values as their 2-D view (leading dimensions
+    flattened), and every convolution workload draws tensors of its shapes."""
+    a = workloads.uniform_f32((2, 3, 4, 5), 11)
+    assert a.shape == (2, 3, 4, 5)
+    assert np.array_equal(a.reshape(24, 5), workloads.uniform_f32((24, 5), 11))
+    b = workloads.normal_bf16_bits((3, 2, 7), 12)
+    assert b.shape == (3, 2, 7) and np.array_equal(b.reshape(6, 7), workloads.normal_bf16_bits((6, 7), 12))
+    assert workloads.uniform_f32((9,), 1).shape == (9,)
+    for c in workloads.CONV_WORKLOADS.values():
+        if c.crs * c.p * c.q > 1 << 24:
+            continue  # the full-size ones are drawn on the GPU box only
+        assert c.x().shape == (c.batch, c.cin, c.h, c.w)
+        assert c.weights().shape == (c.cout, c.cin, c.r, c.s)
+        assert c.dy().shape == (c.batch, c.cout, c.p, c.q)
