@@ -15,6 +15,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "conv.h"
 #include "gemm.h"
 #include "gemm_internal.hpp"
@@ -41,17 +43,92 @@ struct Im2colArgs {
 };
 
 // Word types: the copy moves element bits, never converts.
-template <int ESIZE>
+template <int BYTES>
 struct Word;
-template <>
-struct Word<4> {
-    typedef uint32_t T;
-};
 template <>
 struct Word<2> {
     typedef uint16_t T;
 };
+template <>
+struct Word<4> {
+    typedef uint32_t T;
+};
 
+// Block b covers filter row (ci, r) = b / jblocks and matrix columns
+// [jb * kEpt * kThreads, (jb + 1) * kEpt * kThreads), jb = b % jblocks; lane t
+// owns columns jb * kEpt * kThreads + e * kThreads + t (e < kEpt), so a wave
+// reads and writes 64 consecutive elements per instruction.  The thread keeps
+// its columns for all S taps s of the filter row.
+
+// Buffer-load form, used when an image channel spans less than 2 GiB.  For
+// each column the taps s whose image column lies inside the image form one
+// range [s_lo, s_lo + s_n) (empty when the image row is in the padding); a tap
+// outside it reads from an offset past the end of the channel's buffer
+// resource, which the hardware answers with zero.  Per element and tap this
+// leaves an add, a compare, a select, one load and one store.
+template <int ESIZE>
+__global__ void __launch_bounds__(kThreads) im2col_buffer_kernel(Im2colArgs a)
+{
+    typedef typename Word<ESIZE>::T T;
+    const int jb = (int)(blockIdx.x % (unsigned)a.jblocks);
+    const int cr = (int)(blockIdx.x / (unsigned)a.jblocks);  // ci * R + r
+    const int ci = cr / a.r, r = cr - ci * a.r;
+    const char *img = static_cast<const char *>(a.x) + (int64_t)ci * a.h * a.w * ESIZE;
+    // dword 3: the gfx9 raw-buffer format word (32-bit data format)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(img), 0, a.h * a.w * ESIZE, 0x00020000);
+    char *out = static_cast<char *>(a.cols) + (int64_t)cr * a.s * a.ld * ESIZE;
+
+    int off[kEpt], s_lo[kEpt];
+    unsigned s_n[kEpt], jo[kEpt];
+    bool ok[kEpt];
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) {
+        const int j = (jb * kEpt + e) * kThreads + (int)threadIdx.x;
+        ok[e] = j < a.pq;
+        const int jj = min(j, a.pq - 1);
+        const int p = (int)(((uint64_t)(uint32_t)jj * a.q_magic) >> a.q_shift);
+        const int q = jj - p * a.q_out;
+        const int y = p * a.sh - a.ph + r * a.dh;
+        const int xb = q * a.sw - a.pw;
+        // taps with 0 <= xb + s * dw < w
+        int lo = xb >= 0 ? 0 : (-xb + a.dw - 1) / a.dw;
+        int hi = xb < a.w ? min(a.s, (a.w - 1 - xb) / a.dw + 1) : 0;
+        const bool row_ok = y >= 0 && y < a.h;
+        if (!row_ok || hi < lo) hi = lo;
+        s_lo[e] = lo;
+        s_n[e] = (unsigned)(hi - lo);
+        off[e] = row_ok ? (y * a.w + xb) * ESIZE : 0;
+        jo[e] = (unsigned)jj * ESIZE;
+    }
+    const int step = a.dw * ESIZE;
+    auto taps = [&](auto check) {
+        for (int s = 0; s < a.s; ++s) {
+            char *dst = out + (int64_t)s * a.ld * ESIZE;
+            T v[kEpt];
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) {
+                const bool inside = (unsigned)(s - s_lo[e]) < s_n[e];
+                const int vo = inside ? off[e] + s * step : (int)0x80000000u;
+                if constexpr (ESIZE == 4)
+                    v[e] = (T)__builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, 0, 0);
+                else
+                    v[e] = (T)__builtin_amdgcn_raw_buffer_load_b16(rsrc, vo, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e)
+                if (!decltype(check)::value || ok[e]) *reinterpret_cast<T *>(dst + jo[e]) = v[e];
+        }
+    };
+    // every block but the last of a filter row stores all its columns
+    if ((jb + 1) * kEpt * kThreads <= a.pq)
+        taps(std::false_type());
+    else
+        taps(std::true_type());
+}
+
+// Plain-load form for any image size: clamped in-image addresses, zero
+// selected in the padding.
 template <int ESIZE>
 __global__ void __launch_bounds__(kThreads) im2col_kernel(Im2colArgs a)
 {
@@ -69,8 +146,11 @@ __global__ void __launch_bounds__(kThreads) im2col_kernel(Im2colArgs a)
     for (int e = 0; e < kEpt; ++e) {
         j[e] = (jb * kEpt + e) * kThreads + (int)threadIdx.x;
         ok[e] = j[e] < a.pq;
-        const int p = (int)(((uint64_t)(uint32_t)j[e] * a.q_magic) >> a.q_shift);
-        const int q = j[e] - p * a.q_out;
+        // columns past P Q (never stored) take the last column's position,
+        // which keeps the index math in range
+        const int jj = min(j[e], a.pq - 1);
+        const int p = (int)(((uint64_t)(uint32_t)jj * a.q_magic) >> a.q_shift);
+        const int q = jj - p * a.q_out;
         const int y = p * a.sh - a.ph + r * a.dh;
         row[e] = (y >= 0 && y < a.h) ? (int64_t)y * a.w : -1;
         xb[e] = q * a.sw - a.pw;
@@ -78,19 +158,17 @@ __global__ void __launch_bounds__(kThreads) im2col_kernel(Im2colArgs a)
     for (int s = 0; s < a.s; ++s) {
         const int xoff = s * a.dw;
         T *dst = out + (int64_t)s * a.ld;
-        // All loads first, from a clamped in-image address (element 0 in the
-        // padding), so they issue back to back; the padding is zeroed after.
         T v[kEpt];
-        bool inside[kEpt];
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) {
             const int x = xb[e] + xoff;
-            inside[e] = row[e] >= 0 && x >= 0 && x < a.w;
-            v[e] = img[inside[e] ? row[e] + x : 0];
+            const bool inside = row[e] >= 0 && x >= 0 && x < a.w;
+            const T t = img[inside ? row[e] + x : 0];
+            v[e] = inside ? t : T(0);
         }
 #pragma unroll
         for (int e = 0; e < kEpt; ++e)
-            if (ok[e]) dst[j[e]] = inside[e] ? v[e] : T(0);
+            if (ok[e]) dst[j[e]] = v[e];
     }
 }
 
@@ -181,10 +259,20 @@ hipError_t launch_im2col(int esize, const Dims &d, const void *image, void *cols
     a.jblocks = (int)((d.pq() + per_block - 1) / per_block);
     const int64_t blocks = d.c * d.r * a.jblocks;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    if (esize == 4)
-        hipLaunchKernelGGL(im2col_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(im2col_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    // buffer offsets are signed 32-bit: the channel must span less than 2 GiB
+    const bool buffer = d.h * d.w * esize < (int64_t(1) << 31);
+    if (esize == 4) {
+        if (buffer)
+            hipLaunchKernelGGL(im2col_buffer_kernel<4>, grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL(im2col_kernel<4>, grid, block, 0, stream, a);
+    } else {
+        if (buffer)
+            hipLaunchKernelGGL(im2col_buffer_kernel<2>, grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL(im2col_kernel<2>, grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

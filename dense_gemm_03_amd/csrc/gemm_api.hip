@@ -103,6 +103,8 @@ int select_config(int dtype, int64_t M, int64_t N, int64_t K)
     };
     static const int medium = config_index(dtype, "bf16_128x128x64_w2x2_s2");
     static const int small = config_index(dtype, "bf16_64x64x64_w2x2_s2");
+    static const int wide = config_index(dtype, "bf16_64x256x64_w1x4_s3");
+    if (M <= 64 && N >= 1024) return wide;   // few rows, wide N, split-K
     if (M >= 2048 && N >= 2048) return best_of(dtype, large, 2, M, N);
     if (M * N >= int64_t(1024) * 1024) return medium;
     return small;

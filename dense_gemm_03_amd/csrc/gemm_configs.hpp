@@ -84,7 +84,9 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 4, ALL)       \
     X("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8, ALL)       \
     X("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8, NN)        \
-    X("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8, ALL)
+    X("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8, ALL)           \
+    X("bf16_64x256x64_w1x4_s3", true, 64, 256, 64, 1, 4, 3, 1, ALL)         \
+    X("bf16_64x256x64_w1x4_s2", true, 64, 256, 64, 1, 4, 2, 1, NN)
 
 // Launcher pointers of one entry and layout: both alignments, or nullptr.
 #define DG_FNS(BF16, BM, BN, BK, WM, WN, S, L)                                               \
