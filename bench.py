@@ -17,9 +17,9 @@ in HBM.  Prints ONE JSON line:
                           (bf16 8192^3), and with --all for the im2col and
                           tall-skinny shapes and the generalised-GEMM variants
                           (transposed operands, alpha/beta, bf16 C)
-  convolution             with --all: the im2col + GEMM convolution of the
-                          64-channel 31x31-filter workload (forward, filter
-                          gradient, and the im2col kernel against HBM)
+  convolution             the im2col + GEMM convolution of the 64-channel
+                          31x31-filter workload, fp32 and bf16 (forward,
+                          filter gradient, and the im2col kernel against HBM)
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -49,19 +49,27 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    """Hash of the HIP sources, so stored counter readings are only used for
-    the kernels they were taken on."""
+# Sources that define each kernel family's device code: stored counter
+# readings are used only while these are unchanged.
+KERNEL_SOURCES = {
+    "gemm": ["gemm_kernel.hpp", "gemm_launch.hpp", "gemm_instances.hip"],
+    "im2col": ["conv.hip"],
+}
+
+
+def source_digest(family: str = "gemm") -> str:
+    """Hash of the HIP sources of one kernel family."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_03_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[family]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per launch from profiles/traffic.json, if taken on these sources."""
+def stored_traffic(workload: str, family: str = "gemm", config: str | None = None):
+    """HBM bytes per launch from profiles/traffic.json, if taken on these
+    sources (and, for a GEMM, on the tile configuration dispatched now)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -69,7 +77,9 @@ def stored_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if not entry or entry.get("sources") != source_digest():
+    if not entry or entry.get("sources") != source_digest(family):
+        return None
+    if config is not None and entry.get("config") != config:
         return None
     return entry.get("bytes_per_launch")
 
@@ -134,7 +144,7 @@ def measure(name: str, steps: int, warmup: int):
     tflops = w.flops * steps / wall / 1e12
     achieved = w.flops / (event_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = stored_traffic(name)
+    traffic = stored_traffic(name, "gemm", dg.gemm_config_name(dtype_id, cfg))
     res = {
         "workload": name,
         "M": w.M, "N": w.N, "K": w.K,
@@ -225,7 +235,7 @@ def measure_conv(name: str, steps: int, warmup: int):
                                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": None}}
     _, ev_ms = timed(im2col, steps)
     gbs = c.im2col_bytes / (ev_ms * 1e-3) / 1e9
-    traffic = stored_traffic(name + "-im2col")
+    traffic = stored_traffic(name + "-im2col", "im2col")
     res["im2col"] = {"ms_per_call": ev_ms,
                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}}
@@ -338,7 +348,7 @@ def main() -> int:
         also[n] = measure(n, max(10, args.steps // 2), max(20, args.warmup))
 
     conv = {}
-    if args.all and not args.no_also:
+    if not args.no_also:
         for n in CONV:
             conv[n] = measure_conv(n, max(10, args.steps // 5), max(5, args.warmup // 5))
 
