@@ -171,8 +171,9 @@ def measure(name: str, steps: int, warmup: int):
 
 
 def measure_conv(name: str, steps: int, warmup: int):
-    """Time the im2col + GEMM convolution `name`: the forward pass, the filter
-    gradient, and the im2col kernel alone (its HBM roofline)."""
+    """Time the convolution `name`: forward pass and filter gradient through
+    im2col + GEMM and through the implicit GEMM, and the im2col kernel alone
+    (its HBM roofline)."""
     import ctypes
 
     import torch
@@ -224,9 +225,18 @@ def measure_conv(name: str, steps: int, warmup: int):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / n, e0.elapsed_time(e1) / n
 
+    def fwd_implicit():
+        assert dg.conv2d_fwd_implicit(dtype, dg.GEMM_DTYPE_F32, params, x.data_ptr(),
+                                      w.data_ptr(), y.data_ptr(), sp) == dg.GEMM_OK
+
+    def wgrad_implicit():
+        assert dg.conv2d_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(),
+                                             dw.data_ptr(), sp) == dg.GEMM_OK
+
     res = {}
     peak = PEAK_TFLOPS[c.dtype]
-    for label, fn in (("fwd", fwd), ("wgrad", wgrad)):
+    for label, fn in (("fwd", fwd), ("wgrad", wgrad), ("fwd_implicit", fwd_implicit),
+                      ("wgrad_implicit", wgrad_implicit)):
         wall_ms, ev_ms = timed(fn, steps)
         log("[bench] %s %s: %.3f ms per call" % (name, label, ev_ms))
         ach = c.flops / (ev_ms * 1e-3) / 1e12

@@ -67,6 +67,8 @@ SIGNATURES.update({
     "conv2d_im2col": (_int, [_int, _pp, _i64, _p, _p, _i64, _p]),
     "conv2d_fwd": (_int, [_int, _int, _pp, _p, _p, _p, _p, _i64, _p]),
     "conv2d_bwd_weight": (_int, [_int, _pp, _p, _p, _p, _p, _i64, _p]),
+    "conv2d_fwd_implicit": (_int, [_int, _int, _pp, _p, _p, _p, _p]),
+    "conv2d_bwd_weight_implicit": (_int, [_int, _pp, _p, _p, _p, _p]),
 })
 
 _lib = None
@@ -264,6 +266,14 @@ def conv2d_bwd_weight(dtype, params, x, dy, dw, workspace, workspace_bytes, stre
                                             workspace_bytes, stream)
 
 
+def conv2d_fwd_implicit(dtype, dtype_y, params, x, w, y, stream=None) -> int:
+    return load_library().conv2d_fwd_implicit(dtype, dtype_y, ctypes.byref(params), x, w, y, stream)
+
+
+def conv2d_bwd_weight_implicit(dtype, params, x, dy, dw, stream=None) -> int:
+    return load_library().conv2d_bwd_weight_implicit(dtype, ctypes.byref(params), x, dy, dw, stream)
+
+
 def _pair(v):
     return (v, v) if isinstance(v, int) else tuple(v)
 
@@ -296,43 +306,55 @@ def _workspace(workspace, need, device):
     return workspace
 
 
-def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None):
-    """y = conv2d(x, w) through the im2col + GEMM path (cross-correlation form,
-    as torch.nn.functional.conv2d).  x (N, C_in, H, W) and w (C_out, C_in, R, S)
-    are both float32 or both bfloat16; y is float32 (default) or bfloat16.
-    The workspace (one image's convolution matrix) is allocated when not given."""
+def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None,
+           implicit=False):
+    """y = conv2d(x, w) (cross-correlation form, as torch.nn.functional.conv2d)
+    through the im2col + GEMM path, or with ``implicit`` through the
+    implicit-GEMM path (no convolution matrix).  x (N, C_in, H, W) and w
+    (C_out, C_in, R, S) are both float32 or both bfloat16; y is float32
+    (default) or bfloat16.  The im2col workspace (one image's convolution
+    matrix) is allocated when not given."""
     import torch
     if w.dtype != x.dtype or not w.is_contiguous() or w.dim() != 4:
         raise TypeError("w must be a contiguous 4-D tensor of x's dtype")
     params, dtype, P, Q, need = _conv_setup(x, tuple(w.shape), stride, padding, dilation)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     y = torch.empty((x.shape[0], w.shape[0], P, Q), dtype=out_dtype, device=x.device)
-    ws = _workspace(workspace, need, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    rc = conv2d_fwd(dtype, GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32,
-                    params, x.data_ptr(), w.data_ptr(), y.data_ptr(), ws.data_ptr(),
-                    ws.numel() * ws.element_size(), stream)
+    dtype_y = GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32
+    if implicit:
+        rc = conv2d_fwd_implicit(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                                 stream)
+    else:
+        ws = _workspace(workspace, need, x.device)
+        rc = conv2d_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                        ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return y
 
 
 def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, workspace=None,
-                       stream=None):
+                       stream=None, implicit=False):
     """dw (float32, weight_shape) = the filter gradient of conv2d for input x
-    and output gradient dy, through the im2col + GEMM path."""
+    and output gradient dy, through the im2col + GEMM path (or, with
+    ``implicit``, the implicit-GEMM path)."""
     import torch
     params, dtype, P, Q, need = _conv_setup(x, tuple(weight_shape), stride, padding, dilation)
     if dy.dtype != x.dtype or not dy.is_contiguous() or \
             tuple(dy.shape) != (x.shape[0], weight_shape[0], P, Q):
         raise ValueError("dy must be a contiguous (N, C_out, P, Q) tensor of x's dtype")
     dw = torch.empty(tuple(weight_shape), dtype=torch.float32, device=x.device)
-    ws = _workspace(workspace, need, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    rc = conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                           ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if implicit:
+        rc = conv2d_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                                        stream)
+    else:
+        ws = _workspace(workspace, need, x.device)
+        rc = conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                               ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return dw

@@ -276,6 +276,31 @@ hipError_t launch_im2col(int esize, const Dims &d, const void *image, void *cols
     return hipGetLastError();
 }
 
+// Geometry of the implicit-GEMM loaders; the image of one batch element must
+// span less than 2 GiB (buffer offsets are signed 32-bit).
+int make_geom(const Dims &d, int esize, ConvGeom *g)
+{
+    if (d.c * d.h * d.w * esize >= (int64_t(1) << 31)) return GEMM_ERR_INVALID_ARG;
+    g->h = (int)d.h;
+    g->w = (int)d.w;
+    g->r = (int)d.r;
+    g->s = (int)d.s;
+    g->ph = (int)d.ph;
+    g->pw = (int)d.pw;
+    g->sh = (int)d.sh;
+    g->sw = (int)d.sw;
+    g->dh = (int)d.dh;
+    g->dw = (int)d.dw;
+    g->q = (int)d.Q;
+    g->pq = (int)d.pq();
+    g->crs = (int)d.crs();
+    div_magic((uint32_t)d.Q, &g->q_magic, &g->q_shift);
+    div_magic((uint32_t)(d.r * d.s), &g->rs_magic, &g->rs_shift);
+    div_magic((uint32_t)d.s, &g->s_magic, &g->s_shift);
+    g->img_bytes = (int)(d.c * d.h * d.w * esize);
+    return GEMM_OK;
+}
+
 int check_workspace(const Dims &d, int dtype, const void *ws, int64_t ws_bytes)
 {
     if (ws == nullptr || (uintptr_t)ws % 16 != 0) return GEMM_ERR_INVALID_ARG;
@@ -392,6 +417,63 @@ int conv2d_bwd_weight(int dtype, const conv2d_params *p, const void *x, const vo
                        n == 0 ? 0.0f : 1.0f,
                        static_cast<const char *>(dy) + n * d.k * d.pq() * es, d.pq(),
                        workspace, ld, dw, d.crs()};
+        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    return GEMM_OK;
+}
+
+int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const void *x,
+                        const void *w, void *y, hipStream_t stream)
+{
+    dg::Dims d;
+    if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
+    int rc = dg::check_dims(p, &d);
+    if (rc != GEMM_OK) return rc;
+    if (d.n == 0) return GEMM_OK;
+    const int es = dg::elem_size(dtype), esy = dg::elem_size(dtype_y);
+    if (x == nullptr || w == nullptr || y == nullptr || !dg::aligned_to(x, es) ||
+        !dg::aligned_to(w, es) || !dg::aligned_to(y, esy))
+        return GEMM_ERR_INVALID_ARG;
+    dg::ConvGeom geom;
+    if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
+    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    for (int64_t n = 0; n < d.n; ++n) {
+        // y[n] (C_out x PQ) = w (C_out x C_in R S) . cols(x[n]), cols formed in the loader
+        dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, d.pq(), d.crs(), 1.0f, 0.0f,
+                       w, d.crs(), static_cast<const char *>(x) + n * d.c * d.h * d.w * es, 1,
+                       static_cast<char *>(y) + n * d.k * d.pq() * esy, d.pq(),
+                       dg::B_CONV_FWD, &geom};
+        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    return GEMM_OK;
+}
+
+int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x, const void *dy,
+                               float *dw, hipStream_t stream)
+{
+    dg::Dims d;
+    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
+    int rc = dg::check_dims(p, &d);
+    if (rc != GEMM_OK) return rc;
+    const int es = dg::elem_size(dtype);
+    if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
+    if (d.n == 0) {
+        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), 0, 1.0f, 0.0f,
+                       nullptr, 1, nullptr, 1, dw, d.crs()};
+        return dg::gemm_run(g, -1, 0, stream);
+    }
+    if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
+        return GEMM_ERR_INVALID_ARG;
+    dg::ConvGeom geom;
+    if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
+    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    for (int64_t n = 0; n < d.n; ++n) {
+        // dw (C_out x C_in R S) (+)= dy[n] (C_out x PQ) . cols(x[n])^T
+        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), d.pq(), 1.0f,
+                       n == 0 ? 0.0f : 1.0f,
+                       static_cast<const char *>(dy) + n * d.k * d.pq() * es, d.pq(),
+                       static_cast<const char *>(x) + n * d.c * d.h * d.w * es, 1, dw, d.crs(),
+                       dg::B_CONV_WGRAD, &geom};
         if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
     }
     return GEMM_OK;

@@ -110,6 +110,22 @@ int select_config(int dtype, int64_t M, int64_t N, int64_t K)
     return small;
 }
 
+// Entry for an implicit-GEMM convolution product (the entries built with
+// implicit kernels), by the number of output channels M.
+int select_implicit(int dtype, int64_t M)
+{
+    if (dtype == GEMM_DTYPE_F32) {
+        static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
+        static const int mid = config_index(dtype, "f32_128x128_w2x2_s2");
+        static const int large = config_index(dtype, "f32_256x128_w4x2_s2");
+        return M <= 64 ? wide : M <= 128 ? mid : large;
+    }
+    static const int wide = config_index(dtype, "bf16_64x256x64_w1x4_s3");
+    static const int mid = config_index(dtype, "bf16_128x128x64_w2x2_s2");
+    static const int large = config_index(dtype, "bf16_256x128x64_w2x2_s2");
+    return M <= 64 ? wide : M <= 128 ? mid : large;
+}
+
 // Number of K slices: 1 when the output alone yields enough blocks to fill the
 // chip; otherwise enough slices for about two blocks per compute unit, each
 // slice keeping at least four k-tiles.  forced > 0 overrides the target.
@@ -194,7 +210,11 @@ int check_args(const Call &c)
     // transposed), B is K x N (or N x K), C is M x N.
     const int64_t a_row = c.transa == GEMM_OP_T ? c.M : c.K;
     const int64_t b_row = c.transb == GEMM_OP_T ? c.K : c.N;
-    if (c.lda < (a_row > 0 ? a_row : 1) || c.ldb < (b_row > 0 ? b_row : 1) ||
+    const bool implicit = c.bsrc != B_MATRIX;
+    if (implicit && (c.conv == nullptr || c.transa != GEMM_OP_N ||
+                     c.transb != (c.bsrc == B_CONV_FWD ? GEMM_OP_N : GEMM_OP_T)))
+        return GEMM_ERR_INVALID_ARG;
+    if (c.lda < (a_row > 0 ? a_row : 1) || (!implicit && c.ldb < (b_row > 0 ? b_row : 1)) ||
         c.ldc < (c.N > 0 ? c.N : 1))
         return GEMM_ERR_INVALID_ARG;
     if (c.M > 0 && c.N > 0 && c.C == nullptr) return GEMM_ERR_INVALID_ARG;
@@ -216,7 +236,12 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     if (tab == nullptr) return GEMM_ERR_INVALID_ARG;
     if (forced_cfg >= count) return GEMM_ERR_INVALID_ARG;
     const int layout = call.transa * 2 + call.transb;
-    if (forced_cfg >= 0 && tab[forced_cfg].fn[layout][0] == nullptr) return GEMM_ERR_INVALID_ARG;
+    const int impl = call.bsrc == B_CONV_FWD ? 0 : 1;  // implicit slot, for bsrc != B_MATRIX
+    auto kernel_of = [&](const TileConfig &t, bool aligned) -> launch_fn {
+        return call.bsrc == B_MATRIX ? t.fn[layout][aligned ? 0 : 1]
+                                     : t.implicit[impl][aligned ? 0 : 1];
+    };
+    if (forced_cfg >= 0 && kernel_of(tab[forced_cfg], true) == nullptr) return GEMM_ERR_INVALID_ARG;
     const int64_t M = call.M, N = call.N, K = call.K;
     if (M == 0 || N == 0) return GEMM_OK;
 
@@ -234,9 +259,11 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
                    ? GEMM_OK
                    : GEMM_ERR_HIP;
 
-    const int ci = forced_cfg >= 0 ? forced_cfg : select_config(call.dtype, M, N, K);
+    const int ci = forced_cfg >= 0             ? forced_cfg
+                   : call.bsrc != B_MATRIX ? select_implicit(call.dtype, M)
+                                           : select_config(call.dtype, M, N, K);
     const TileConfig &cfg = tab[ci];
-    if (cfg.fn[layout][0] == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (kernel_of(cfg, true) == nullptr) return GEMM_ERR_INVALID_ARG;
     int splits = 1, kps = 0;
     plan_split(cfg, M, N, K, forced_split, &splits, &kps);
 
@@ -267,8 +294,10 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
 
     const int64_t esz = elem_size(call.dtype);
     const int vec = (int)(16 / esz);
-    const bool aligned = call.lda % vec == 0 && call.ldb % vec == 0 &&
-                         (uintptr_t)call.A % 16 == 0 && (uintptr_t)call.B % 16 == 0;
+    // (an implicit B is gathered element by element: only A's alignment counts)
+    const bool aligned = call.lda % vec == 0 && (uintptr_t)call.A % 16 == 0 &&
+                         (call.bsrc != B_MATRIX ||
+                          (call.ldb % vec == 0 && (uintptr_t)call.B % 16 == 0));
     // The direct-load path addresses a tile with per-thread 32-bit byte
     // offsets from the tile origin, over the tile's memory rows: BM (A as
     // given) or BK (A transposed) rows of A, BK (B as given) or BN (B
@@ -277,9 +306,13 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     const int64_t b_rows = call.transb == GEMM_OP_T ? cfg.bn : cfg.bk;
     a.direct_ok = (a_rows * call.lda * esz < (int64_t(1) << 32)) &&
                   (b_rows * call.ldb * esz < (int64_t(1) << 32));
+    if (call.bsrc != B_MATRIX) {
+        a.conv = *call.conv;
+        a.direct_ok = 0;
+    }
     const int64_t blocks = (int64_t)splits * a.tiles_m * a.tiles_n;
     if (blocks > INT32_MAX) return GEMM_ERR_INVALID_ARG;
-    launch_fn fn = cfg.fn[layout][aligned ? 0 : 1];
+    launch_fn fn = kernel_of(cfg, aligned);
     if (fn(a, (int)blocks, stream) != hipSuccess) return GEMM_ERR_HIP;
     if (splits > 1 && launch_splitk_reduce(a.ws, splits, (int)M, (int)N, call.C, call.ldc,
                                            call.alpha, call.beta, out_bf16, stream) != hipSuccess)

@@ -7,8 +7,8 @@
 //   X(NAME, BF16, BM, BN, BK, WM, WN, STAGES, GROUP_M, LAYOUTS)
 // with the tile shape (BM x BN block, BK k-tile), the wave grid (WM x WN
 // waves), the number of LDS stages, the raster group height, and LAYOUTS =
-// ALL (kernels for all four combinations of transposed operands) or NN (only
-// A and B as given).  The kernels of one input type and operand layout are
+// ALL (kernels for all four combinations of transposed operands), CONV (ALL,
+// plus implicit-GEMM convolution kernels) or NN (only A and B as given).  The kernels of one input type and operand layout are
 // instantiated by one compilation of gemm_instances.hip, so the slices compile
 // in parallel; the tables (gemm_tables.hip) only take their addresses.
 #pragma once
@@ -35,13 +35,28 @@ struct TileConfig {
     // element-wise loads, any alignment of the element type.  nullptr where
     // the entry has no kernel for that layout.
     launch_fn fn[4][2];
+    // implicit-GEMM convolution kernels (B tiles formed from an image):
+    // implicit[0] forward (B = cols), implicit[1] filter gradient (B = cols^T);
+    // [aligned], as fn.  nullptr where the entry has none.
+    launch_fn implicit[2][2];
 };
 
 // Declared here; defined in gemm_launch.hpp and explicitly instantiated by the
 // compilations of gemm_instances.hip.
 template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
-          bool ALIGNED>
+          bool ALIGNED, int BSRC>
 hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
+
+// Implicit-GEMM slices: forward (A = filters k-contiguous, B = convolution
+// matrix tiles n-contiguous) and filter gradient (A = output gradient
+// k-contiguous, B = transposed matrix tiles k-contiguous).  They run the
+// register-staged loop, which uses two LDS stages.
+#define DG_LA_CF ::dg::KMAJOR
+#define DG_LB_CF ::dg::MNMAJOR
+#define DG_LA_CW ::dg::KMAJOR
+#define DG_LB_CW ::dg::KMAJOR
+#define DG_BSRC_CF ::dg::B_CONV_FWD
+#define DG_BSRC_CW ::dg::B_CONV_WGRAD
 
 // Memory orientation of op(A) / op(B) per layout combination: A as given is
 // k-contiguous, A^T (stored K x M) outer-contiguous; B as given is
@@ -62,12 +77,12 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 // small block when the output holds too few large blocks to fill 256 compute
 // units.  Every entry the dispatcher can choose is built for all layouts.
 #define DG_F32_TABLE(X)                                                     \
-    X("f32_256x128_w4x2_s2", false, 256, 128, 32, 4, 2, 2, 8, ALL)          \
-    X("f32_128x128_w2x2_s2", false, 128, 128, 32, 2, 2, 2, 8, NN)           \
+    X("f32_256x128_w4x2_s2", false, 256, 128, 32, 4, 2, 2, 8, CONV)         \
+    X("f32_128x128_w2x2_s2", false, 128, 128, 32, 2, 2, 2, 8, CONV)         \
     X("f32_256x256_w4x2_s2", false, 256, 256, 32, 4, 2, 2, 8, ALL)          \
     X("f32_64x64_w2x2_s2", false, 64, 64, 32, 2, 2, 2, 8, ALL)              \
     X("f32_64x64_w2x2_s3", false, 64, 64, 32, 2, 2, 3, 8, ALL)              \
-    X("f32_64x256_w1x4_s3", false, 64, 256, 32, 1, 4, 3, 1, ALL)            \
+    X("f32_64x256_w1x4_s3", false, 64, 256, 32, 1, 4, 3, 1, CONV)           \
     X("f32_64x256_w1x4_s4", false, 64, 256, 32, 1, 4, 4, 1, NN)             \
     X("f32_64x128_w1x2_s4", false, 64, 128, 32, 1, 2, 4, 1, NN)             \
     X("f32_256x64_w4x1_s3", false, 256, 64, 32, 4, 1, 3, 8, NN)             \
@@ -82,25 +97,37 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8, NN)        \
     X("bf16_256x256x64_w2x4_s2", true, 256, 256, 64, 2, 4, 2, 8, NN)        \
     X("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 4, ALL)       \
-    X("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8, ALL)       \
-    X("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8, NN)        \
+    X("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8, CONV)      \
+    X("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8, CONV)      \
     X("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8, ALL)           \
-    X("bf16_64x256x64_w1x4_s3", true, 64, 256, 64, 1, 4, 3, 1, ALL)         \
+    X("bf16_64x256x64_w1x4_s3", true, 64, 256, 64, 1, 4, 3, 1, CONV)        \
     X("bf16_64x256x64_w1x4_s2", true, 64, 256, 64, 1, 4, 2, 1, NN)
 
 // Launcher pointers of one entry and layout: both alignments, or nullptr.
 #define DG_FNS(BF16, BM, BN, BK, WM, WN, S, L)                                               \
-    {&launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L, true>,                  \
-     &launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L, false>}
+    {&launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L, true, ::dg::B_MATRIX>,  \
+     &launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L, false, ::dg::B_MATRIX>}
+#define DG_IFNS(BF16, BM, BN, BK, WM, WN, L)                                                 \
+    {&launch_gemm<BF16, BM, BN, BK, WM, WN, 2, DG_LA_##L, DG_LB_##L, true, DG_BSRC_##L>,     \
+     &launch_gemm<BF16, BM, BN, BK, WM, WN, 2, DG_LA_##L, DG_LB_##L, false, DG_BSRC_##L>}
 #define DG_NOFNS {nullptr, nullptr}
 #define DG_FNS_ALL_NN(...) DG_FNS(__VA_ARGS__, NN)
 #define DG_FNS_ALL_NT(...) DG_FNS(__VA_ARGS__, NT)
 #define DG_FNS_ALL_TN(...) DG_FNS(__VA_ARGS__, TN)
 #define DG_FNS_ALL_TT(...) DG_FNS(__VA_ARGS__, TT)
+#define DG_FNS_CONV_NN(...) DG_FNS(__VA_ARGS__, NN)
+#define DG_FNS_CONV_NT(...) DG_FNS(__VA_ARGS__, NT)
+#define DG_FNS_CONV_TN(...) DG_FNS(__VA_ARGS__, TN)
+#define DG_FNS_CONV_TT(...) DG_FNS(__VA_ARGS__, TT)
 #define DG_FNS_NN_NN(...) DG_FNS(__VA_ARGS__, NN)
 #define DG_FNS_NN_NT(...) DG_NOFNS
 #define DG_FNS_NN_TN(...) DG_NOFNS
 #define DG_FNS_NN_TT(...) DG_NOFNS
+
+#define DG_IMPL_CONV(BF16, BM, BN, BK, WM, WN)                                                \
+    {DG_IFNS(BF16, BM, BN, BK, WM, WN, CF), DG_IFNS(BF16, BM, BN, BK, WM, WN, CW)}
+#define DG_IMPL_ALL(...) {DG_NOFNS, DG_NOFNS}
+#define DG_IMPL_NN(...) {DG_NOFNS, DG_NOFNS}
 
 // One table entry from one list item.
 #define DG_TABLE_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                        \
@@ -108,7 +135,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
                {DG_FNS_##LAYOUTS##_NN(BF16, BM, BN, BK, WM, WN, S),                         \
                 DG_FNS_##LAYOUTS##_NT(BF16, BM, BN, BK, WM, WN, S),                         \
                 DG_FNS_##LAYOUTS##_TN(BF16, BM, BN, BK, WM, WN, S),                         \
-                DG_FNS_##LAYOUTS##_TT(BF16, BM, BN, BK, WM, WN, S)}},
+                DG_FNS_##LAYOUTS##_TT(BF16, BM, BN, BK, WM, WN, S)},                        \
+               DG_IMPL_##LAYOUTS(BF16, BM, BN, BK, WM, WN)},
 
 // Tables, defined in gemm_tables.hip.
 const TileConfig *f32_configs(int *count);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_kernel.hpp"
+
 namespace dg {
 
 // One generalised product C := alpha * op(A) * op(B) + beta * C, with the
@@ -21,6 +23,10 @@ struct GemmCall {
     int64_t ldb;
     void *C;
     int64_t ldc;
+    // B_MATRIX, or an implicit convolution source: then B is the image of
+    // one batch element, ldb is not used, and conv describes the geometry
+    int bsrc = B_MATRIX;
+    const ConvGeom *conv = nullptr;
 };
 
 // Checks the arguments, picks a tile entry (or uses forced_cfg >= 0) and a

@@ -62,6 +62,25 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // Memory orientation of an operand tile.
 enum Layout { KMAJOR = 0, MNMAJOR = 1 };
 
+// Where op(B) comes from: a matrix in memory, or tiles of a convolution
+// matrix formed from an image inside the loader (implicit GEMM).
+enum BSource {
+    B_MATRIX = 0,
+    B_CONV_FWD = 1,    // op(B) = cols (C_in R S x P Q): B points at the image
+    B_CONV_WGRAD = 2,  // op(B) = cols^T (P Q x C_in R S), read as the k-contiguous
+                       // B^T tile (rows C_in R S, columns P Q)
+};
+
+// Geometry of the convolution behind an implicit op(B), for one image
+// [C_in][H][W]: matrix row (ci R + r) S + s, column p Q + q holds
+// image[ci][p sh - ph + r dh][q sw - pw + s dw], zero outside the image.
+struct ConvGeom {
+    int h, w, r, s, ph, pw, sh, sw, dh, dw, q, pq, crs;
+    uint64_t q_magic, rs_magic, s_magic;  // j / Q, k / (R S), k / S (exact below 2^31)
+    int q_shift, rs_shift, s_shift;
+    int img_bytes;                        // C_in H W element bytes (< 2^31)
+};
+
 // Arguments of one launch.  The grid is 1-D: splits * tiles_m * tiles_n blocks.
 struct KernelArgs {
     const void *A;    // op(A) = A (M x K, k-contiguous) or A^T (A stored K x M)
@@ -77,6 +96,7 @@ struct KernelArgs {
     int direct_ok;    // per-thread byte offsets of a tile fit in 32 bits
     float alpha, beta;
     int out_bf16;     // C holds bf16 bit patterns (1) or fp32 (0)
+    ConvGeom conv;    // used by the implicit (convolution) B sources only
 };
 
 // ----------------------------------------------------------- operand tile --
@@ -620,16 +640,17 @@ __device__ __forceinline__ void lds_store(unsigned char *stage, int tid, const S
 }
 
 // `ntiles` masked k-tiles from k_first, double buffered through registers
-// (stage t&1 is read while stage (t+1)&1 receives tile t+1).  On entry no
-// wave may still use stages 0 and 1.
-template <bool ALIGNED, class G>
+// (stage t&1 is read while stage (t+1)&1 receives tile t+1); `load(k0, regs)`
+// fetches the tiles of the k-tile at k0.  On entry no wave may still use
+// stages 0 and 1.
+template <class G, class Loader>
 __device__ __forceinline__ void main_loop_masked(unsigned char *smem0, unsigned char *smem1,
                                                  const BlockCtx<G> &c, int k_first, int ntiles,
-                                                 floatx16 (&acc)[G::FM][G::FN])
+                                                 floatx16 (&acc)[G::FM][G::FN], Loader &&load)
 {
     StageRegs<G> regs;
     Frags<G> cur, nxt;
-    global_load_masked<ALIGNED>(c, k_first, regs);
+    load(k_first, regs);
     lds_store(smem0, c.tid, regs);
     __syncthreads();
     load_frags(smem0, c, 0, cur);
@@ -637,7 +658,7 @@ __device__ __forceinline__ void main_loop_masked(unsigned char *smem0, unsigned 
         unsigned char *stage = (t & 1) ? smem1 : smem0;
         unsigned char *other = (t & 1) ? smem0 : smem1;
         const bool more = t + 1 < ntiles;
-        if (more) global_load_masked<ALIGNED>(c, k_first + (t + 1) * G::BK, regs);
+        if (more) load(k_first + (t + 1) * G::BK, regs);
 #pragma unroll
         for (int step = 0; step < G::STEPS - 1; ++step) {
             load_frags(stage, c, step + 1, nxt);
@@ -651,6 +672,146 @@ __device__ __forceinline__ void main_loop_masked(unsigned char *smem0, unsigned 
         cur = nxt;
     }
 }
+
+// ------------------------------------------------- implicit (convolution) B --
+
+// Exact floor(j / d) for 0 <= j < 2^31 from host-made constants.
+__device__ __forceinline__ int div_magic(int j, uint64_t m, int shift)
+{
+    return (int)(((uint64_t)(uint32_t)j * m) >> shift);
+}
+
+// Loader of B tiles of the convolution matrix, formed from the image ("Three
+// X's: large convolutions in PyTorch for model training", section "CUTLASS":
+// the implicit GEMM builds the matrix tiles inside the blocks, from output
+// coordinates (p, q) and filter taps (ci, r, s), instead of materialising the
+// matrix).  Addresses are computed on the fly (the page's analytic iterator).
+//
+// Every matrix element is image[ci][y][x] with y = (p sh - ph) + r dh and
+// x = (q sw - pw) + s dw: a column term (from p, q) plus a row term (from
+// ci, r, s).  A thread's chunks share their column positions across its chunk
+// rows (NT is a multiple of the chunks per tile row), so in the forward tile
+// (rows k = taps, columns n = outputs) the column terms are fixed for the
+// whole K loop and the row terms change per k-tile; in the filter-gradient
+// tile (rows n = taps, columns k = outputs) it is the other way round.
+// Elements in the padding, or past K or N, read at an offset beyond the
+// image's buffer resource, which the hardware answers with zero.
+template <class G, int MODE>
+struct ConvGather {
+    using T = typename G::TB;
+    using In = typename G::In;
+    static constexpr int U = T::PER_THREAD, V = T::VEC, RSTEP = T::NT / T::CPR;
+    static_assert(T::NT % T::CPR == 0, "a thread's chunks must share their columns");
+    static_assert((MODE == B_CONV_FWD && T::LAYOUT == MNMAJOR) ||
+                      (MODE == B_CONV_WGRAD && T::LAYOUT == KMAJOR),
+                  "tile orientation of the convolution source");
+
+    __amdgpu_buffer_rsrc_t rsrc;
+    const ConvGeom *g;
+    int row0, e0;      // first chunk row of this thread, first element in the row
+    // fixed terms: column terms (forward) or row terms (filter gradient), and
+    // whether that column / row lies inside the matrix
+    static constexpr int NF = MODE == B_CONV_FWD ? V : U;
+    int fy[NF], fx[NF], fb[NF];
+    bool fok[NF];
+
+    // (y, x, channel offset) terms of tap k = (ci R + r) S + s, or (y, x)
+    // terms of output position j = p Q + q
+    __device__ __forceinline__ void tap_terms(int k, int &ty, int &tx, int &tb) const
+    {
+        const int ci = div_magic(k, g->rs_magic, g->rs_shift);
+        const int rem = k - ci * g->r * g->s;
+        const int r = div_magic(rem, g->s_magic, g->s_shift);
+        const int s = rem - r * g->s;
+        ty = r * g->dh;
+        tx = s * g->dw;
+        tb = ci * g->h * g->w;
+    }
+    __device__ __forceinline__ void out_terms(int j, int &ty, int &tx) const
+    {
+        const int p = div_magic(j, g->q_magic, g->q_shift);
+        const int q = j - p * g->q;
+        ty = p * g->sh - g->ph;
+        tx = q * g->sw - g->pw;
+    }
+
+    __device__ __forceinline__ ConvGather(const KernelArgs &a, int bn, int tid) : g(&a.conv)
+    {
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.B), 0, a.conv.img_bytes,
+                                                 0x00020000);  // gfx9 raw-buffer format word
+        row0 = tid / T::CPR;
+        e0 = (tid % T::CPR) * V;
+        if constexpr (MODE == B_CONV_FWD) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const int n = bn + e0 + e;
+                fok[e] = n < a.N;
+                out_terms(min(n, a.N - 1), fy[e], fx[e]);
+                fb[e] = 0;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int n = bn + row0 + u * RSTEP;
+                fok[u] = n < a.N;
+                tap_terms(min(n, a.N - 1), fy[u], fx[u], fb[u]);
+            }
+        }
+    }
+
+    // The image element at (y, x) of the channel at element offset base, or
+    // zero when ok is false or (y, x) lies in the padding.
+    __device__ __forceinline__ In fetch(bool ok, int y, int x, int base) const
+    {
+        const bool inside = ok && y >= 0 && y < g->h && x >= 0 && x < g->w;
+        // unsigned arithmetic: the unused value of the select may wrap
+        const unsigned el = (unsigned)base + (unsigned)y * (unsigned)g->w + (unsigned)x;
+        const int off = inside ? (int)(el * (unsigned)sizeof(In)) : (int)0x80000000u;
+        if constexpr (sizeof(In) == 4)
+            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0));
+        else
+            return (In)__builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, 0);
+    }
+
+    // The B tile of the k-tile at k0 (k below kend), chunk u of this thread in r[u].
+    __device__ __forceinline__ void load(int k0, int kend, u32x4 (&r)[U]) const
+    {
+        union Chunk {
+            u32x4 v;
+            In e[V];
+        };
+        if constexpr (MODE == B_CONV_FWD) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + row0 + u * RSTEP;
+                int ty, tx, tb;
+                tap_terms(min(k, kend - 1), ty, tx, tb);
+                const bool kok = k < kend;
+                Chunk c;
+#pragma unroll
+                for (int e = 0; e < V; ++e) c.e[e] = fetch(kok && fok[e], fy[e] + ty, fx[e] + tx, tb);
+                r[u] = c.v;
+            }
+        } else {
+            int cy[V], cx[V];
+            bool cok[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const int k = k0 + e0 + e;
+                cok[e] = k < kend;
+                out_terms(min(k, kend - 1), cy[e], cx[e]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                Chunk c;
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    c.e[e] = fetch(fok[u] && cok[e], fy[u] + cy[e], fx[u] + cx[e], fb[u]);
+                r[u] = c.v;
+            }
+        }
+    }
+};
 
 // --------------------------------------------------------------- epilogue --
 
@@ -675,7 +836,7 @@ __device__ __forceinline__ void store_out(void *C, int64_t idx, float sum, float
 // ------------------------------------------------------------------ kernel --
 
 template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
-          bool ALIGNED>
+          bool ALIGNED, int BSRC = B_MATRIX>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(KernelArgs p)
 {
@@ -721,11 +882,21 @@ gemm_kernel(KernelArgs p)
     // partial last k-tile, blocks crossing the M or N edge, unaligned operands
     // and leading dimensions too large for 32-bit tile offsets take the
     // masked loads.  The choice is uniform per workgroup.
-    const bool edge = !ALIGNED || !p.direct_ok || c.bm + BM > p.M || c.bn + BN > p.N;
-    const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
-    if (nfast > 0) main_loop_direct(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
-    if (ntiles > nfast)
-        main_loop_masked<ALIGNED>(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc);
+    if constexpr (BSRC == B_MATRIX) {
+        const bool edge = !ALIGNED || !p.direct_ok || c.bm + BM > p.M || c.bn + BN > p.N;
+        const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
+        if (nfast > 0) main_loop_direct(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
+        if (ntiles > nfast)
+            main_loop_masked(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc,
+                             [&](int k0, StageRegs<G> &r) { global_load_masked<ALIGNED>(c, k0, r); });
+    } else {
+        // implicit GEMM: A from memory, B tiles formed from the image
+        const ConvGather<G, BSRC> gather(p, c.bn, c.tid);
+        main_loop_masked(lds0, lds1, c, kbeg, ntiles, acc, [&](int k0, StageRegs<G> &r) {
+            load_tile_masked<ALIGNED, typename G::TA>(c.A, c.lda, c.bm, c.M, k0, c.kend, c.tid, r.a);
+            gather.load(k0, c.kend, r.b);
+        });
+    }
 
     // Epilogue: element r of a 32x32 accumulator fragment sits at row
     // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of that fragment.  With

@@ -1,7 +1,8 @@
 // Definition of the kernel launcher and the explicit instantiation of one
 // operand layout's kernels from the tile lists.  Included by the per-layout
 // source files, each of which defines DG_DTYPE_TABLE (the list), DG_LAYOUT
-// (NN, NT, TN or TT) and then includes this header.
+// (NN, NT, TN, TT, or CF / CW for the implicit-GEMM convolution kernels) and
+// then includes this header.
 #pragma once
 
 #include "gemm_configs.hpp"
@@ -9,10 +10,10 @@
 namespace dg {
 
 template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
-          bool ALIGNED>
+          bool ALIGNED, int BSRC>
 hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_kernel<BF16, BM, BN, BK, WM, WN, STAGES, LA, LB, ALIGNED>),
+    hipLaunchKernelGGL((gemm_kernel<BF16, BM, BN, BK, WM, WN, STAGES, LA, LB, ALIGNED, BSRC>),
                        dim3(blocks), dim3(64 * WM * WN), 0, stream, args);
     return hipGetLastError();
 }
@@ -22,17 +23,37 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 // Explicit instantiation of both alignments of one entry for layout L.
 #define DG_INST(BF16, BM, BN, BK, WM, WN, S, L)                                                 \
     template hipError_t dg::launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L,      \
-                                        true>(const dg::KernelArgs &, int, hipStream_t);        \
+                                        true, ::dg::B_MATRIX>(const dg::KernelArgs &, int,      \
+                                                              hipStream_t);                      \
     template hipError_t dg::launch_gemm<BF16, BM, BN, BK, WM, WN, S, DG_LA_##L, DG_LB_##L,      \
-                                        false>(const dg::KernelArgs &, int, hipStream_t);
+                                        false, ::dg::B_MATRIX>(const dg::KernelArgs &, int,     \
+                                                               hipStream_t);
+// implicit-GEMM slice (CF or CW): two LDS stages
+#define DG_IINST(BF16, BM, BN, BK, WM, WN, S, L)                                                \
+    template hipError_t dg::launch_gemm<BF16, BM, BN, BK, WM, WN, 2, DG_LA_##L, DG_LB_##L,      \
+                                        true, DG_BSRC_##L>(const dg::KernelArgs &, int,         \
+                                                           hipStream_t);                         \
+    template hipError_t dg::launch_gemm<BF16, BM, BN, BK, WM, WN, 2, DG_LA_##L, DG_LB_##L,      \
+                                        false, DG_BSRC_##L>(const dg::KernelArgs &, int,        \
+                                                            hipStream_t);
 #define DG_INST_ALL_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_ALL_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_ALL_TN(...) DG_INST(__VA_ARGS__, TN)
 #define DG_INST_ALL_TT(...) DG_INST(__VA_ARGS__, TT)
+#define DG_INST_ALL_CF(...)
+#define DG_INST_ALL_CW(...)
+#define DG_INST_CONV_NN(...) DG_INST(__VA_ARGS__, NN)
+#define DG_INST_CONV_NT(...) DG_INST(__VA_ARGS__, NT)
+#define DG_INST_CONV_TN(...) DG_INST(__VA_ARGS__, TN)
+#define DG_INST_CONV_TT(...) DG_INST(__VA_ARGS__, TT)
+#define DG_INST_CONV_CF(...) DG_IINST(__VA_ARGS__, CF)
+#define DG_INST_CONV_CW(...) DG_IINST(__VA_ARGS__, CW)
 #define DG_INST_NN_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_NN_NT(...)
 #define DG_INST_NN_TN(...)
 #define DG_INST_NN_TT(...)
+#define DG_INST_NN_CF(...)
+#define DG_INST_NN_CW(...)
 #define DG_INST_SEL2(LAYOUTS, L) DG_INST_##LAYOUTS##_##L
 #define DG_INST_SEL(LAYOUTS, L) DG_INST_SEL2(LAYOUTS, L)
 #define DG_INST_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                            \

@@ -95,6 +95,20 @@ int conv2d_fwd(int dtype, int dtype_y, const conv2d_params *p, const void *x, co
 int conv2d_bwd_weight(int dtype, const conv2d_params *p, const void *x, const void *dy, float *dw,
                       void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Implicit-GEMM forms of the same two products ("Three X's", section
+ * "CUTLASS": the matrix is not built; the GEMM's loader forms each tile of
+ * it from the image, from the output coordinates and filter taps, with
+ * addresses computed on the fly).  No workspace from the caller (a split of
+ * K uses the library's own GEMM workspace).  Same arguments, layouts, types
+ * and results as conv2d_fwd / conv2d_bwd_weight; additionally
+ * GEMM_ERR_INVALID_ARG when one batch element of x spans 2 GiB or more.
+ */
+int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const void *x,
+                        const void *w, void *y, hipStream_t stream);
+int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x, const void *dy,
+                               float *dw, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

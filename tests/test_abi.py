@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -234,5 +234,14 @@ def test_conv_host_logic_and_invalid_arguments():
     ]
     for t, call in enumerate(calls):
         assert call() == dg.GEMM_ERR_INVALID_ARG, t
+    # implicit-GEMM forms: same checks, no workspace; one image must span < 2 GiB
+    assert dg.conv2d_fwd_implicit(F32, F32, bad[0], p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_fwd_implicit(F32, F32, ok, None, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_fwd_implicit(F32, 9, ok, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_bwd_weight_implicit(F32, ok, p, p, p + 2) == dg.GEMM_ERR_INVALID_ARG
+    huge = P(1, 2, 1 << 15, 1 << 14, 1, 3, 3)       # 2 x 2^29 fp32 elements = 4 GiB per image
+    assert dg.conv2d_output_size(huge)[0] == dg.GEMM_OK
+    assert dg.conv2d_fwd_implicit(F32, F32, huge, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_bwd_weight_implicit(BF16, huge, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     # an empty batch: nothing to compute for the forward
     assert dg.conv2d_fwd(F32, F32, P(0, 3, 10, 9, 4, 3, 2), None, None, None, None, 0) == dg.GEMM_OK

@@ -38,6 +38,8 @@ SHAPES = [
     ConvShape(3, 5, 33, 31, 7, 7, 7, 3, 3),                   # P Q = 1023, ragged tiles
     ConvShape(1, 2, 40, 1100, 3, 3, 3, 1, 1, 1, 1),           # Q = 1100: P Q > one block row
     ConvShape(1, 3, 6, 6, 2, 6, 6, 0, 0),                     # filter covers the image: P = Q = 1
+    ConvShape(2, 6, 15, 17, 100, 3, 3, 1, 1),                 # C_out in (64, 128]
+    ConvShape(1, 4, 12, 14, 300, 3, 5, 1, 2, 1, 1),           # C_out > 128, ragged
 ]
 
 
@@ -84,11 +86,11 @@ def run_im2col(x: np.ndarray, c: ConvShape, n: int, ld: int, rows=None):
     return got[:, :c.p * c.q]
 
 
-def run_fwd(x, w, c: ConvShape, out_bf16=False):
+def run_fwd(x, w, c: ConvShape, out_bf16=False, implicit=False):
     import torch
-    y = dg.conv2d(_dev(x) if x.dtype == np.float32 else _dev(x), _dev(w), stride=(c.sh, c.sw),
-                  padding=(c.ph, c.pw), dilation=(c.dh, c.dw),
-                  out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    y = dg.conv2d(_dev(x), _dev(w), stride=(c.sh, c.sw), padding=(c.ph, c.pw),
+                  dilation=(c.dh, c.dw), out_dtype=torch.bfloat16 if out_bf16 else torch.float32,
+                  implicit=implicit)
     torch.cuda.synchronize()
     if out_bf16:
         raw = y.cpu().view(torch.int16).numpy().view(np.uint16)
@@ -97,10 +99,10 @@ def run_fwd(x, w, c: ConvShape, out_bf16=False):
     return raw.astype(np.float64), raw
 
 
-def run_bwd(x, dy, c: ConvShape):
+def run_bwd(x, dy, c: ConvShape, implicit=False):
     import torch
     dw = dg.conv2d_weight_grad(_dev(x), _dev(dy), (c.cout, c.cin, c.r, c.s), stride=(c.sh, c.sw),
-                               padding=(c.ph, c.pw), dilation=(c.dh, c.dw))
+                               padding=(c.ph, c.pw), dilation=(c.dh, c.dw), implicit=implicit)
     torch.cuda.synchronize()
     return dw.cpu().numpy().astype(np.float64)
 
@@ -133,50 +135,57 @@ def test_im2col_bit_exact(bf16):
             assert np.array_equal(got, want), "%s image %d" % (c, n)
 
 
+@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-def test_fwd_exact_integers(bf16):
+def test_fwd_exact_integers(bf16, implicit):
     for t, c in enumerate(SHAPES):
         x, w = _ints(c.x_shape, 300 + t, bf16), _ints(c.w_shape, 310 + t, bf16)
         ref, _ = oc.conv2d_fwd(x, w, c)
         for out_bf16 in (False, True):
             log("fwd %s y %s" % (c, "bf16" if out_bf16 else "f32"))
-            got, raw = run_fwd(x, w, c, out_bf16)
+            got, raw = run_fwd(x, w, c, out_bf16, implicit)
             if out_bf16:
                 assert np.array_equal(raw, oracle.round_to_bf16_bits(ref)), str(c)
             else:
                 assert np.array_equal(got, ref), str(c)
 
 
+@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-def test_bwd_weight_exact_integers(bf16):
+def test_bwd_weight_exact_integers(bf16, implicit):
     for t, c in enumerate(SHAPES):
         x, dy = _ints(c.x_shape, 400 + t, bf16), _ints(c.y_shape, 410 + t, bf16)
         log("filter gradient %s" % (c,))
         ref, _ = oc.conv2d_bwd_weight(x, dy, c)
-        assert np.array_equal(run_bwd(x, dy, c), ref), str(c)
+        assert np.array_equal(run_bwd(x, dy, c, implicit), ref), str(c)
 
 
+@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-def test_random_within_tolerance(bf16):
+def test_random_within_tolerance(bf16, implicit):
     tol = TOL["bf16" if bf16 else "f32"]
     for t, c in enumerate(SHAPES[1:], 1):
         x, w = _randn(c.x_shape, 500 + t, bf16), _randn(c.w_shape, 510 + t, bf16)
         dy = _randn(c.y_shape, 520 + t, bf16)
         ref, S = oc.conv2d_fwd(x, w, c)
-        check_close(run_fwd(x, w, c)[0], ref, S, tol, "fwd %s" % (c,))
-        check_close(run_fwd(x, w, c, True)[0], ref, S, tol, "fwd bf16 y %s" % (c,), True)
+        check_close(run_fwd(x, w, c, False, implicit)[0], ref, S, tol, "fwd %s" % (c,))
+        check_close(run_fwd(x, w, c, True, implicit)[0], ref, S, tol, "fwd bf16 y %s" % (c,), True)
         ref, S = oc.conv2d_bwd_weight(x, dy, c)
-        check_close(run_bwd(x, dy, c), ref, S, tol, "filter gradient %s" % (c,))
+        check_close(run_bwd(x, dy, c, implicit), ref, S, tol, "filter gradient %s" % (c,))
 
 
-def test_empty_batch_and_workload_small_batch():
+@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+def test_empty_batch_and_workload_small_batch(implicit):
     """batch 0: forward does nothing, the filter gradient is the empty sum
     (zeros); and the small batched workload against the oracle."""
     import torch
     c = ConvShape(0, 3, 8, 8, 2, 3, 3, 1, 1)
     p = _params(c)
     dw = torch.full((2, 3, 3, 3), float("nan"), device="cuda:0")
-    assert dg.conv2d_bwd_weight(F32, p, None, None, dw.data_ptr(), None, 0, _stream()) == dg.GEMM_OK
+    if implicit:
+        assert dg.conv2d_bwd_weight_implicit(F32, p, None, None, dw.data_ptr(), _stream()) == dg.GEMM_OK
+    else:
+        assert dg.conv2d_bwd_weight(F32, p, None, None, dw.data_ptr(), None, 0, _stream()) == dg.GEMM_OK
     torch.cuda.synchronize()
     assert torch.all(dw == 0)
     wk = wl.CONV_WORKLOADS["conv-small-batch"]
@@ -184,18 +193,20 @@ def test_empty_batch_and_workload_small_batch():
                   wk.stride, wk.dilation, wk.dilation)
     x, w, dy = wk.x(), wk.weights(), wk.dy()
     ref, S = oc.conv2d_fwd(x, w, c)
-    check_close(run_fwd(x, w, c)[0], ref, S, TOL["f32"], wk.name + " fwd")
+    check_close(run_fwd(x, w, c, False, implicit)[0], ref, S, TOL["f32"], wk.name + " fwd")
     ref, S = oc.conv2d_bwd_weight(x, dy, c)
-    check_close(run_bwd(x, dy, c), ref, S, TOL["f32"], wk.name + " filter gradient")
+    check_close(run_bwd(x, dy, c, implicit), ref, S, TOL["f32"], wk.name + " filter gradient")
 
 
-def test_deterministic_repeats():
+@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+def test_deterministic_repeats(implicit):
     import torch
     c = ConvShape(2, 8, 30, 30, 16, 5, 5, 2, 2)
     x, w, dy = _dev(_randn(c.x_shape, 1, False)), _dev(_randn(c.w_shape, 2, False)), \
         _dev(_randn(c.y_shape, 3, False))
-    ys = [dg.conv2d(x, w, padding=2) for _ in range(3)]
-    gs = [dg.conv2d_weight_grad(x, dy, (16, 8, 5, 5), padding=2) for _ in range(3)]
+    ys = [dg.conv2d(x, w, padding=2, implicit=implicit) for _ in range(3)]
+    gs = [dg.conv2d_weight_grad(x, dy, (16, 8, 5, 5), padding=2, implicit=implicit)
+          for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(ys[0], y) for y in ys[1:])
     assert all(torch.equal(gs[0], g) for g in gs[1:])
@@ -206,8 +217,9 @@ def _shape_of(wk):
                      wk.stride, wk.dilation, wk.dilation)
 
 
+@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
 @pytest.mark.parametrize("name", ["conv-64c-31k", "conv-64c-31k-bf16"])
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, implicit):
     """The large-kernel convolution at full size: forward outputs and filter-
     gradient taps at sampled positions against the oracle, one sum each, and
     the convolution matrix bit for bit at sampled rows."""
@@ -217,7 +229,7 @@ def test_full_size_sampled(name):
     tol = TOL[wk.dtype]
     x, w, dy = wk.x(), wk.weights(), wk.dy()
     log("[%s] forward" % name)
-    y, _ = run_fwd(x, w, c)
+    y, _ = run_fwd(x, w, c, False, implicit)
     rng = np.random.default_rng(wk.seed + 5)
     idx = [np.zeros(256, np.int64), rng.integers(0, c.cout, 256), rng.integers(0, c.p, 256),
            rng.integers(0, c.q, 256)]
@@ -225,7 +237,7 @@ def test_full_size_sampled(name):
     ref, S = oc.conv2d_fwd_entries(x, w, c, *idx)
     check_close(y[tuple(idx)], ref, S, tol, name + " fwd (256 sampled)")
     log("[%s] filter gradient" % name)
-    dw = run_bwd(x, dy, c)
+    dw = run_bwd(x, dy, c, implicit)
     tidx = [rng.integers(0, d, 256) for d in c.w_shape]
     tidx[2][:2], tidx[3][:2] = [0, c.r - 1], [0, c.s - 1]
     ref, S = oc.conv2d_bwd_weight_entries(x, dy, c, *tidx)
@@ -240,17 +252,18 @@ def test_full_size_sampled(name):
         assert np.array_equal(got[t], sub.view(np.uint16) if bf16 else sub.view(np.uint32)), row
 
 
-def test_full_size_exact_integers_sampled():
+@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+def test_full_size_exact_integers_sampled(implicit):
     """Integer tensors of the full-size shape: sampled outputs and taps exact."""
     wk = wl.CONV_WORKLOADS["conv-64c-31k"]
     c = _shape_of(wk)
     x, w, dy = _ints(c.x_shape, 7, False), _ints(c.w_shape, 8, False), _ints(c.y_shape, 9, False)
-    y, _ = run_fwd(x, w, c)
+    y, _ = run_fwd(x, w, c, False, implicit)
     rng = np.random.default_rng(3)
     idx = [np.zeros(256, np.int64)] + [rng.integers(0, d, 256) for d in c.y_shape[1:]]
     ref, _ = oc.conv2d_fwd_entries(x, w, c, *idx)
     assert np.array_equal(y[tuple(idx)], ref)
-    dw = run_bwd(x, dy, c)
+    dw = run_bwd(x, dy, c, implicit)
     tidx = [rng.integers(0, d, 256) for d in c.w_shape]
     ref, _ = oc.conv2d_bwd_weight_entries(x, dy, c, *tidx)
     assert np.array_equal(dw[tuple(tidx)], ref)
