@@ -709,15 +709,17 @@ struct ConvGather {
     __amdgpu_buffer_rsrc_t rsrc;
     const ConvGeom *g;
     int row0, e0;      // first chunk row of this thread, first element in the row
-    // fixed terms: column terms (forward) or row terms (filter gradient), and
-    // whether that column / row lies inside the matrix
+    // Fixed terms -- column terms (forward) or row terms (filter gradient) --
+    // as (y, x, byte offset) plus whether that column / row lies inside the
+    // matrix.  The byte offset of an element is the sum of its column and row
+    // offsets; (y, x) only decide whether it lies in the image.
     static constexpr int NF = MODE == B_CONV_FWD ? V : U;
-    int fy[NF], fx[NF], fb[NF];
+    int fy[NF], fx[NF], fo[NF];
     bool fok[NF];
 
-    // (y, x, channel offset) terms of tap k = (ci R + r) S + s, or (y, x)
-    // terms of output position j = p Q + q
-    __device__ __forceinline__ void tap_terms(int k, int &ty, int &tx, int &tb) const
+    // Terms of tap k = (ci R + r) S + s: y = r dh, x = s dw, offset of
+    // (ci, r dh, s dw) in the image.
+    __device__ __forceinline__ void tap_terms(int k, int &ty, int &tx, int &to) const
     {
         const int ci = div_magic(k, g->rs_magic, g->rs_shift);
         const int rem = k - ci * g->r * g->s;
@@ -725,14 +727,17 @@ struct ConvGather {
         const int s = rem - r * g->s;
         ty = r * g->dh;
         tx = s * g->dw;
-        tb = ci * g->h * g->w;
+        to = ((ci * g->h + ty) * g->w + tx) * (int)sizeof(In);
     }
-    __device__ __forceinline__ void out_terms(int j, int &ty, int &tx) const
+    // Terms of output position j = p Q + q: y = p sh - ph, x = q sw - pw and
+    // the (possibly negative) offset of (y, x).
+    __device__ __forceinline__ void out_terms(int j, int &ty, int &tx, int &to) const
     {
         const int p = div_magic(j, g->q_magic, g->q_shift);
         const int q = j - p * g->q;
         ty = p * g->sh - g->ph;
         tx = q * g->sw - g->pw;
+        to = (ty * g->w + tx) * (int)sizeof(In);
     }
 
     __device__ __forceinline__ ConvGather(const KernelArgs &a, int bn, int tid) : g(&a.conv)
@@ -746,31 +751,29 @@ struct ConvGather {
             for (int e = 0; e < V; ++e) {
                 const int n = bn + e0 + e;
                 fok[e] = n < a.N;
-                out_terms(min(n, a.N - 1), fy[e], fx[e]);
-                fb[e] = 0;
+                out_terms(min(n, a.N - 1), fy[e], fx[e], fo[e]);
             }
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int n = bn + row0 + u * RSTEP;
                 fok[u] = n < a.N;
-                tap_terms(min(n, a.N - 1), fy[u], fx[u], fb[u]);
+                tap_terms(min(n, a.N - 1), fy[u], fx[u], fo[u]);
             }
         }
     }
 
-    // The image element at (y, x) of the channel at element offset base, or
-    // zero when ok is false or (y, x) lies in the padding.
-    __device__ __forceinline__ In fetch(bool ok, int y, int x, int base) const
+    // The element at image position (y, x) and byte offset off, or zero when
+    // ok is false or (y, x) lies in the padding.  Straight-line code: the
+    // range checks are unsigned compares joined without short-circuits.
+    __device__ __forceinline__ In fetch(bool ok, int y, int x, int off) const
     {
-        const bool inside = ok && y >= 0 && y < g->h && x >= 0 && x < g->w;
-        // unsigned arithmetic: the unused value of the select may wrap
-        const unsigned el = (unsigned)base + (unsigned)y * (unsigned)g->w + (unsigned)x;
-        const int off = inside ? (int)(el * (unsigned)sizeof(In)) : (int)0x80000000u;
+        const bool inside = ok & ((unsigned)y < (unsigned)g->h) & ((unsigned)x < (unsigned)g->w);
+        const int vo = inside ? off : (int)0x80000000u;
         if constexpr (sizeof(In) == 4)
-            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0));
+            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, 0, 0));
         else
-            return (In)__builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, 0);
+            return (In)__builtin_amdgcn_raw_buffer_load_b16(rsrc, vo, 0, 0);
     }
 
     // The B tile of the k-tile at k0 (k below kend), chunk u of this thread in r[u].
@@ -784,29 +787,30 @@ struct ConvGather {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + row0 + u * RSTEP;
-                int ty, tx, tb;
-                tap_terms(min(k, kend - 1), ty, tx, tb);
+                int ty, tx, to;
+                tap_terms(min(k, kend - 1), ty, tx, to);
                 const bool kok = k < kend;
                 Chunk c;
 #pragma unroll
-                for (int e = 0; e < V; ++e) c.e[e] = fetch(kok && fok[e], fy[e] + ty, fx[e] + tx, tb);
+                for (int e = 0; e < V; ++e)
+                    c.e[e] = fetch(kok & fok[e], fy[e] + ty, fx[e] + tx, fo[e] + to);
                 r[u] = c.v;
             }
         } else {
-            int cy[V], cx[V];
+            int cy[V], cx[V], co[V];
             bool cok[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const int k = k0 + e0 + e;
                 cok[e] = k < kend;
-                out_terms(min(k, kend - 1), cy[e], cx[e]);
+                out_terms(min(k, kend - 1), cy[e], cx[e], co[e]);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 Chunk c;
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    c.e[e] = fetch(fok[u] && cok[e], fy[u] + cy[e], fx[u] + cx[e], fb[u]);
+                    c.e[e] = fetch(fok[u] & cok[e], fy[u] + cy[e], fx[u] + cx[e], fo[u] + co[e]);
                 r[u] = c.v;
             }
         }
