@@ -23,7 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_SOURCES = [_SRC, os.path.join(_HERE, "conv.c")]
+_SOURCES = [_SRC, os.path.join(_HERE, "conv.c"), os.path.join(_HERE, "convnd.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # Plain C, no fast-math, no FMA contraction: every product of two fp32 or bf16
@@ -33,7 +33,7 @@ CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-ffp-contract=off"
 
 
 def build() -> str:
-    """Compile ``oracle.c`` and ``conv.c`` into ``liboracle.so`` with gcc.
+    """Compile ``oracle.c``, ``conv.c`` and ``convnd.c`` into ``liboracle.so`` with gcc.
     Returns the path."""
     tmp = _LIB + ".tmp%d" % os.getpid()
     subprocess.run(["gcc", *CFLAGS, "-o", tmp, *_SOURCES, "-lm"], check=True)
