@@ -71,6 +71,23 @@ SIGNATURES.update({
     "conv2d_bwd_weight_implicit": (_int, [_int, _pp, _p, _p, _p, _p]),
 })
 
+
+class ConvNdParams(ctypes.Structure):
+    """convnd_params of include/conv.h."""
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "batch", "in_channels", "out_channels", "ndim")] + \
+        [(name, ctypes.c_int64 * 4) for name in ("size", "kernel", "pad", "stride", "dilation")]
+
+
+_pnd = ctypes.POINTER(ConvNdParams)
+SIGNATURES.update({
+    "convnd_output_size": (_int, [_pnd, _pi64]),
+    "convnd_workspace_size": (_i64, [_int, _pnd]),
+    "convnd_im2col": (_int, [_int, _pnd, _i64, _p, _p, _i64, _p]),
+    "convnd_fwd": (_int, [_int, _int, _pnd, _p, _p, _p, _p, _i64, _p]),
+    "convnd_bwd_weight": (_int, [_int, _pnd, _p, _p, _p, _p, _i64, _p]),
+})
+
 _lib = None
 
 
@@ -274,8 +291,51 @@ def conv2d_bwd_weight_implicit(dtype, params, x, dy, dw, stream=None) -> int:
     return load_library().conv2d_bwd_weight_implicit(dtype, ctypes.byref(params), x, dy, dw, stream)
 
 
+def convnd_params(batch, in_channels, out_channels, size, kernel, pad=None, stride=None,
+                  dilation=None) -> ConvNdParams:
+    """ConvNdParams for len(size) spatial dimensions (unused entries 0)."""
+    nd = len(size)
+    pad = (0,) * nd if pad is None else tuple(pad)
+    stride = (1,) * nd if stride is None else tuple(stride)
+    dilation = (1,) * nd if dilation is None else tuple(dilation)
+    if not 1 <= nd <= 4 or not all(len(v) == nd for v in (kernel, pad, stride, dilation)):
+        raise ValueError("size, kernel, pad, stride and dilation need 1 to 4 entries each, alike")
+    arr = lambda v: (ctypes.c_int64 * 4)(*(tuple(v) + (0,) * (4 - nd)))  # noqa: E731
+    return ConvNdParams(batch, in_channels, out_channels, nd, arr(size), arr(kernel), arr(pad),
+                        arr(stride), arr(dilation))
+
+
+def convnd_output_size(params: ConvNdParams):
+    """(status, (O_0, .., O_{ndim-1}))."""
+    out = (ctypes.c_int64 * 4)()
+    rc = load_library().convnd_output_size(ctypes.byref(params), out)
+    return rc, tuple(out[i] for i in range(max(0, min(params.ndim, 4))))
+
+
+def convnd_workspace_size(dtype: int, params: ConvNdParams) -> int:
+    return load_library().convnd_workspace_size(dtype, ctypes.byref(params))
+
+
+def convnd_im2col(dtype, params, image, x, cols, ld_cols, stream=None) -> int:
+    return load_library().convnd_im2col(dtype, ctypes.byref(params), image, x, cols, ld_cols, stream)
+
+
+def convnd_fwd(dtype, dtype_y, params, x, w, y, workspace, workspace_bytes, stream=None) -> int:
+    return load_library().convnd_fwd(dtype, dtype_y, ctypes.byref(params), x, w, y, workspace,
+                                     workspace_bytes, stream)
+
+
+def convnd_bwd_weight(dtype, params, x, dy, dw, workspace, workspace_bytes, stream=None) -> int:
+    return load_library().convnd_bwd_weight(dtype, ctypes.byref(params), x, dy, dw, workspace,
+                                            workspace_bytes, stream)
+
+
 def _pair(v):
     return (v, v) if isinstance(v, int) else tuple(v)
+
+
+def _tuple_nd(v, nd):
+    return (v,) * nd if isinstance(v, int) else tuple(v)
 
 
 def _conv_setup(x, weight_shape, stride, padding, dilation):
@@ -355,6 +415,69 @@ def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wor
         ws = _workspace(workspace, need, x.device)
         rc = conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
                                ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return dw
+
+
+def _convnd_setup(x, weight_shape, stride, padding, dilation):
+    import torch
+    nd = x.dim() - 2
+    if x.dtype not in (torch.float32, torch.bfloat16) or x.device.type != "cuda" or \
+            not 1 <= nd <= 4:
+        raise TypeError("x must be a float32 or bfloat16 GPU tensor (N, C, S_0 .. S_{D-1}), "
+                        "D = 1 to 4")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (channel-first)")
+    if len(weight_shape) != nd + 2 or weight_shape[1] != x.shape[1]:
+        raise ValueError("filters must be (C_out, C_in, K_0 .. K_{D-1}) with x's C_in")
+    params = convnd_params(x.shape[0], x.shape[1], weight_shape[0], tuple(x.shape[2:]),
+                           tuple(weight_shape[2:]), _tuple_nd(padding, nd), _tuple_nd(stride, nd),
+                           _tuple_nd(dilation, nd))
+    dtype = GEMM_DTYPE_BF16 if x.dtype == torch.bfloat16 else GEMM_DTYPE_F32
+    rc, out = convnd_output_size(params)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return params, dtype, out, convnd_workspace_size(dtype, params)
+
+
+def conv_nd(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None):
+    """y = convolution of x (N, C_in, S_0 .. S_{D-1}) with w (C_out, C_in,
+    K_0 .. K_{D-1}), D = 1 to 4 (cross-correlation form, as torch's conv1d /
+    conv2d / conv3d), through the im2col + GEMM path.  x and w are both
+    float32 or both bfloat16; y is float32 (default) or bfloat16."""
+    import torch
+    if w.dtype != x.dtype or not w.is_contiguous():
+        raise TypeError("w must be a contiguous tensor of x's dtype")
+    params, dtype, out, need = _convnd_setup(x, tuple(w.shape), stride, padding, dilation)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    y = torch.empty((x.shape[0], w.shape[0]) + out, dtype=out_dtype, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    dtype_y = GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32
+    ws = _workspace(workspace, need, x.device)
+    rc = convnd_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                    ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+    return y
+
+
+def conv_nd_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, workspace=None,
+                        stream=None):
+    """dw (float32, weight_shape) = the filter gradient of conv_nd for input x
+    and output gradient dy, through the im2col + GEMM path."""
+    import torch
+    params, dtype, out, need = _convnd_setup(x, tuple(weight_shape), stride, padding, dilation)
+    if dy.dtype != x.dtype or not dy.is_contiguous() or \
+            tuple(dy.shape) != (x.shape[0], weight_shape[0]) + out:
+        raise ValueError("dy must be a contiguous (N, C_out, O_0 ..) tensor of x's dtype")
+    dw = torch.empty(tuple(weight_shape), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    ws = _workspace(workspace, need, x.device)
+    rc = convnd_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                           ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return dw

@@ -1,16 +1,19 @@
-// 2-D convolution as im2col + GEMM ("Three X's: a new level of working with
-// large convolutions in PyTorch for model training", section "CuBLAS"): the
-// im2col kernel writes one image's convolution matrix into the caller's
-// workspace, then one GEMM of this library finishes the image.  Declared in
-// include/conv.h.
+// Convolution in 1 to 4 spatial dimensions as im2col + GEMM ("Three X's: a
+// new level of working with large convolutions in PyTorch for model
+// training", section "CuBLAS": the convolution matrix of each image is built
+// and one GEMM finishes the image; more spatial dimensions add one index to
+// the matrix's row and column numbering and one loop over the filter), and
+// 2-D convolution as an implicit GEMM (section "CUTLASS": the GEMM's loader
+// forms the matrix tiles from the image).  Declared in include/conv.h.
 //
 // The im2col kernel is a copy with zero fill, bound by HBM writes (the matrix
-// is C_in R S times larger than a row of outputs per tap).  Consecutive lanes
-// write consecutive elements of one matrix row (256 bytes per fp32 store
-// instruction, coalesced); each thread keeps the (p, q) decomposition of its
-// elements across all S taps of a filter row, so the division by Q happens
-// once per element and block, and the image rows it reads stay in the CU's L1
-// for the S taps.
+// holds C_in times the filter volume elements per output position).
+// Consecutive lanes write consecutive elements of one matrix row (a wave
+// store instruction covers 64 consecutive elements); each thread keeps the
+// decomposition of its columns into output coordinates across all taps of
+// the innermost filter dimension, so the divisions happen once per element
+// and block, and the image rows it reads stay in the CU's L1 for those taps.
+// 2-D calls run the same kernel with two spatial dimensions.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -24,22 +27,27 @@
 namespace dg {
 namespace {
 
+constexpr int kMaxD = 4;
 constexpr int64_t kMaxExtent = int64_t(1) << 30;   // keeps in-kernel int32 math exact
 constexpr int64_t kMaxElems = int64_t(1) << 62;
 constexpr int kThreads = 256;
 constexpr int kEpt = 4;                            // elements per thread and tap
 constexpr int64_t kLdAlign = 8;                    // matrix rows padded to 16 bytes (bf16)
 
+// Geometry of one image's convolution matrix with D spatial dimensions, the
+// last one innermost (contiguous in memory).  Matrix row (ci, k_0 .. k_{D-1})
+// and column (o_0 .. o_{D-1}), both numbered row-major.
 struct Im2colArgs {
-    const void *x;      // image n: [C_in][H][W]
-    void *cols;         // [C_in R S][ld]
+    const void *x;                 // image n: [C_in][size_0]..[size_{D-1}]
+    void *cols;                    // [C_in * filter volume][ld]
     int64_t ld;
-    int h, w, r, s;
-    int ph, pw, sh, sw, dh, dw;
-    int q_out, pq;      // Q and P Q
-    uint64_t q_magic;   // floor(j / Q) = (j * q_magic) >> q_shift for j < 2^31
-    int q_shift;
-    int jblocks;        // blocks per filter row (ci, r)
+    int size[kMaxD], kern[kMaxD], pad[kMaxD], stride[kMaxD], dil[kMaxD], out[kMaxD];
+    uint64_t out_magic[kMaxD];     // floor(j / out[d]) = (j * out_magic[d]) >> out_shift[d]
+    int out_shift[kMaxD];
+    int vol_out;                   // product of out: the matrix's columns
+    int img_elems;                 // elements of one channel
+    int groups_per_ci;             // product of kern[0 .. D-2]
+    int jblocks;                   // blocks per row group (ci, k_0 .. k_{D-2})
 };
 
 // Word types: the copy moves element bits, never converts.
@@ -54,30 +62,85 @@ struct Word<4> {
     typedef uint32_t T;
 };
 
-// Block b covers filter row (ci, r) = b / jblocks and matrix columns
-// [jb * kEpt * kThreads, (jb + 1) * kEpt * kThreads), jb = b % jblocks; lane t
-// owns columns jb * kEpt * kThreads + e * kThreads + t (e < kEpt), so a wave
-// reads and writes 64 consecutive elements per instruction.  The thread keeps
-// its columns for all S taps s of the filter row.
+__device__ __forceinline__ int magic_div(int j, uint64_t m, int shift)
+{
+    return (int)(((uint64_t)(uint32_t)j * m) >> shift);
+}
 
+// Row group g = (ci, k_0 .. k_{D-2}) of the block: the channel and the outer
+// filter taps (kk[D-1] is unused).
+template <int D>
+__device__ __forceinline__ int row_group(const Im2colArgs &a, int g, int (&kk)[kMaxD])
+{
+    const int ci = g / a.groups_per_ci;
+    int rest = g - ci * a.groups_per_ci;
+#pragma unroll
+    for (int d = D - 2; d >= 0; --d) {
+        kk[d] = rest % a.kern[d];
+        rest /= a.kern[d];
+    }
+    return ci;
+}
+
+// Column j -> output coordinates; for the block's outer taps kk: whether the
+// outer image coordinates z_d = o_d t_d - p_d + k_d l_d (d < D-1) lie inside
+// the image, the innermost start xb = o_{D-1} t - p (possibly negative), and
+// the channel offset of (z_0 .. z_{D-2}, xb) (meaningful when inside; formed
+// in wrapping unsigned arithmetic, since xb may be negative).
+template <int D>
+__device__ __forceinline__ void column_terms(const Im2colArgs &a, const int (&kk)[kMaxD], int j,
+                                             bool &row_ok, int &off, int &xb)
+{
+    int o[kMaxD];
+    int rest = j;
+#pragma unroll
+    for (int d = D - 1; d > 0; --d) {
+        const int qd = magic_div(rest, a.out_magic[d], a.out_shift[d]);
+        o[d] = rest - qd * a.out[d];
+        rest = qd;
+    }
+    o[0] = rest;
+    bool ok = true;
+    unsigned u = 0;
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        const int z = o[d] * a.stride[d] - a.pad[d] + kk[d] * a.dil[d];
+        ok = ok & ((unsigned)z < (unsigned)a.size[d]);
+        u = u * (unsigned)a.size[d] + (unsigned)z;
+    }
+    xb = o[D - 1] * a.stride[D - 1] - a.pad[D - 1];
+    u = u * (unsigned)a.size[D - 1] + (unsigned)xb;
+    row_ok = ok;
+    off = (int)u;
+}
+
+// Block b covers row group g = b / jblocks and matrix columns
+// [jb * kEpt * kThreads, (jb + 1) * kEpt * kThreads), jb = b % jblocks; lane t
+// owns columns jb * kEpt * kThreads + e * kThreads + t (e < kEpt).  The thread
+// writes its columns for every tap s of the innermost filter dimension
+// (matrix row g * kern[D-1] + s).
+//
 // Buffer-load form, used when an image channel spans less than 2 GiB.  For
-// each column the taps s whose image column lies inside the image form one
-// range [s_lo, s_lo + s_n) (empty when the image row is in the padding); a tap
-// outside it reads from an offset past the end of the channel's buffer
-// resource, which the hardware answers with zero.  Per element and tap this
-// leaves an add, a compare, a select, one load and one store.
-template <int ESIZE>
+// each column the taps s whose innermost image coordinate lies inside the
+// image form one range [s_lo, s_lo + s_n) (empty when an outer coordinate is
+// in the padding); a tap outside it reads from an offset past the end of the
+// channel's buffer resource, which the hardware answers with zero.  Per
+// element and tap this leaves an add, a compare, a select, one load and one
+// store.
+template <int ESIZE, int D>
 __global__ void __launch_bounds__(kThreads) im2col_buffer_kernel(Im2colArgs a)
 {
     typedef typename Word<ESIZE>::T T;
     const int jb = (int)(blockIdx.x % (unsigned)a.jblocks);
-    const int cr = (int)(blockIdx.x / (unsigned)a.jblocks);  // ci * R + r
-    const int ci = cr / a.r, r = cr - ci * a.r;
-    const char *img = static_cast<const char *>(a.x) + (int64_t)ci * a.h * a.w * ESIZE;
+    const int g = (int)(blockIdx.x / (unsigned)a.jblocks);
+    int kk[kMaxD] = {0, 0, 0, 0};
+    const int ci = row_group<D>(a, g, kk);
+    const char *img = static_cast<const char *>(a.x) + (int64_t)ci * a.img_elems * ESIZE;
     // dword 3: the gfx9 raw-buffer format word (32-bit data format)
     const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(img), 0, a.h * a.w * ESIZE, 0x00020000);
-    char *out = static_cast<char *>(a.cols) + (int64_t)cr * a.s * a.ld * ESIZE;
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(img), 0, a.img_elems * ESIZE, 0x00020000);
+    const int S = a.kern[D - 1], W = a.size[D - 1], dw = a.dil[D - 1];
+    char *out = static_cast<char *>(a.cols) + (int64_t)g * S * a.ld * ESIZE;
 
     int off[kEpt], s_lo[kEpt];
     unsigned s_n[kEpt], jo[kEpt];
@@ -85,25 +148,23 @@ __global__ void __launch_bounds__(kThreads) im2col_buffer_kernel(Im2colArgs a)
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         const int j = (jb * kEpt + e) * kThreads + (int)threadIdx.x;
-        ok[e] = j < a.pq;
-        const int jj = min(j, a.pq - 1);
-        const int p = (int)(((uint64_t)(uint32_t)jj * a.q_magic) >> a.q_shift);
-        const int q = jj - p * a.q_out;
-        const int y = p * a.sh - a.ph + r * a.dh;
-        const int xb = q * a.sw - a.pw;
-        // taps with 0 <= xb + s * dw < w
-        int lo = xb >= 0 ? 0 : (-xb + a.dw - 1) / a.dw;
-        int hi = xb < a.w ? min(a.s, (a.w - 1 - xb) / a.dw + 1) : 0;
-        const bool row_ok = y >= 0 && y < a.h;
+        ok[e] = j < a.vol_out;
+        const int jj = min(j, a.vol_out - 1);
+        bool row_ok;
+        int o, xb;
+        column_terms<D>(a, kk, jj, row_ok, o, xb);
+        // taps with 0 <= xb + s * dw < W
+        const int lo = xb >= 0 ? 0 : (-xb + dw - 1) / dw;
+        int hi = xb < W ? min(S, (W - 1 - xb) / dw + 1) : 0;
         if (!row_ok || hi < lo) hi = lo;
         s_lo[e] = lo;
         s_n[e] = (unsigned)(hi - lo);
-        off[e] = row_ok ? (y * a.w + xb) * ESIZE : 0;
+        off[e] = row_ok ? o * ESIZE : 0;
         jo[e] = (unsigned)jj * ESIZE;
     }
-    const int step = a.dw * ESIZE;
+    const int step = dw * ESIZE;
     auto taps = [&](auto check) {
-        for (int s = 0; s < a.s; ++s) {
+        for (int s = 0; s < S; ++s) {
             char *dst = out + (int64_t)s * a.ld * ESIZE;
             T v[kEpt];
 #pragma unroll
@@ -120,50 +181,49 @@ __global__ void __launch_bounds__(kThreads) im2col_buffer_kernel(Im2colArgs a)
                 if (!decltype(check)::value || ok[e]) *reinterpret_cast<T *>(dst + jo[e]) = v[e];
         }
     };
-    // every block but the last of a filter row stores all its columns
-    if ((jb + 1) * kEpt * kThreads <= a.pq)
+    // every block but the last of a row group stores all its columns
+    if ((jb + 1) * kEpt * kThreads <= a.vol_out)
         taps(std::false_type());
     else
         taps(std::true_type());
 }
 
-// Plain-load form for any image size: clamped in-image addresses, zero
+// Plain-load form for any channel size: clamped in-image addresses, zero
 // selected in the padding.
-template <int ESIZE>
+template <int ESIZE, int D>
 __global__ void __launch_bounds__(kThreads) im2col_kernel(Im2colArgs a)
 {
     typedef typename Word<ESIZE>::T T;
     const int jb = (int)(blockIdx.x % (unsigned)a.jblocks);
-    const int cr = (int)(blockIdx.x / (unsigned)a.jblocks);  // ci * R + r
-    const int ci = cr / a.r, r = cr - ci * a.r;
-    const T *img = static_cast<const T *>(a.x) + (int64_t)ci * a.h * a.w;
-    T *out = static_cast<T *>(a.cols) + (int64_t)cr * a.s * a.ld;
+    const int g = (int)(blockIdx.x / (unsigned)a.jblocks);
+    int kk[kMaxD] = {0, 0, 0, 0};
+    const int ci = row_group<D>(a, g, kk);
+    const T *img = static_cast<const T *>(a.x) + (int64_t)ci * a.img_elems;
+    const int S = a.kern[D - 1], W = a.size[D - 1], dw = a.dil[D - 1];
+    T *out = static_cast<T *>(a.cols) + (int64_t)g * S * a.ld;
 
     int j[kEpt], xb[kEpt];
-    int64_t row[kEpt];  // offset of image row y in img, or -1 when y is in the padding
+    int64_t base[kEpt];  // offset of (z_0 .. z_{D-2}, 0), or -1 when an outer z is in the padding
     bool ok[kEpt];
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         j[e] = (jb * kEpt + e) * kThreads + (int)threadIdx.x;
-        ok[e] = j[e] < a.pq;
-        // columns past P Q (never stored) take the last column's position,
-        // which keeps the index math in range
-        const int jj = min(j[e], a.pq - 1);
-        const int p = (int)(((uint64_t)(uint32_t)jj * a.q_magic) >> a.q_shift);
-        const int q = jj - p * a.q_out;
-        const int y = p * a.sh - a.ph + r * a.dh;
-        row[e] = (y >= 0 && y < a.h) ? (int64_t)y * a.w : -1;
-        xb[e] = q * a.sw - a.pw;
+        ok[e] = j[e] < a.vol_out;
+        bool row_ok;
+        int o;
+        // columns past the matrix (never stored) take the last column's
+        // position, which keeps the index math in range
+        column_terms<D>(a, kk, min(j[e], a.vol_out - 1), row_ok, o, xb[e]);
+        base[e] = row_ok ? (int64_t)o - xb[e] : -1;
     }
-    for (int s = 0; s < a.s; ++s) {
-        const int xoff = s * a.dw;
+    for (int s = 0; s < S; ++s) {
         T *dst = out + (int64_t)s * a.ld;
         T v[kEpt];
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) {
-            const int x = xb[e] + xoff;
-            const bool inside = row[e] >= 0 && x >= 0 && x < a.w;
-            const T t = img[inside ? row[e] + x : 0];
+            const int x = xb[e] + s * dw;
+            const bool inside = base[e] >= 0 && x >= 0 && x < W;
+            const T t = img[inside ? base[e] + x : 0];
             v[e] = inside ? t : T(0);
         }
 #pragma unroll
@@ -172,11 +232,21 @@ __global__ void __launch_bounds__(kThreads) im2col_kernel(Im2colArgs a)
     }
 }
 
+// Shape of a convolution with nd spatial dimensions (2-D calls have nd = 2).
 struct Dims {
-    int64_t n, c, h, w, k, r, s, ph, pw, sh, sw, dh, dw, P, Q;
-    int64_t pq() const { return P * Q; }
-    int64_t crs() const { return c * r * s; }
-    int64_t ld() const { return (pq() + kLdAlign - 1) / kLdAlign * kLdAlign; }
+    int64_t n, c, k, nd;
+    int64_t size[kMaxD], kern[kMaxD], pad[kMaxD], stride[kMaxD], dil[kMaxD], out[kMaxD];
+    int64_t vol(const int64_t *v) const
+    {
+        int64_t p = 1;
+        for (int d = 0; d < nd; ++d) p *= v[d];
+        return p;
+    }
+    int64_t vol_out() const { return vol(out); }
+    int64_t vol_kern() const { return vol(kern); }
+    int64_t img_elems() const { return vol(size); }
+    int64_t crs() const { return c * vol_kern(); }
+    int64_t ld() const { return (vol_out() + kLdAlign - 1) / kLdAlign * kLdAlign; }
 };
 
 int64_t out_extent(int64_t in, int64_t pad, int64_t k, int64_t stride, int64_t dil)
@@ -188,36 +258,66 @@ int64_t out_extent(int64_t in, int64_t pad, int64_t k, int64_t stride, int64_t d
 // a * b <= limit, for non-negative a and b, without overflow.
 bool fits(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 
-int check_dims(const conv2d_params *p, Dims *d)
+int check_dims(Dims *d)
 {
-    if (p == nullptr) return GEMM_ERR_INVALID_ARG;
-    *d = Dims{p->batch, p->in_channels, p->height, p->width, p->out_channels, p->kernel_h,
-              p->kernel_w, p->pad_h, p->pad_w, p->stride_h, p->stride_w, p->dilation_h,
-              p->dilation_w, 0, 0};
-    if (d->n < 0 || d->c < 1 || d->h < 1 || d->w < 1 || d->k < 1 || d->r < 1 || d->s < 1 ||
-        d->ph < 0 || d->pw < 0 || d->sh < 1 || d->sw < 1 || d->dh < 1 || d->dw < 1)
-        return GEMM_ERR_INVALID_ARG;
     const int64_t lim = kMaxExtent;
-    for (int64_t v : {d->n, d->c, d->h, d->w, d->k, d->r, d->s, d->ph, d->pw, d->sh, d->sw, d->dh,
-                      d->dw})
-        if (v > lim) return GEMM_ERR_INVALID_ARG;
-    // padded extents and dilated filter spans stay within int32 kernel math
-    if (d->h + 2 * d->ph > lim || d->w + 2 * d->pw > lim || !fits(d->dh, d->r - 1, lim) ||
-        !fits(d->dw, d->s - 1, lim))
+    if (d->nd < 1 || d->nd > kMaxD || d->n < 0 || d->c < 1 || d->k < 1 || d->n > lim ||
+        d->c > lim || d->k > lim)
         return GEMM_ERR_INVALID_ARG;
-    d->P = out_extent(d->h, d->ph, d->r, d->sh, d->dh);
-    d->Q = out_extent(d->w, d->pw, d->s, d->sw, d->dw);
-    if (d->P < 1 || d->Q < 1) return GEMM_ERR_INVALID_ARG;
-    // GEMM extents: C_out, P Q and C_in R S
-    if (!fits(d->P, d->Q, lim) || !fits(d->c, d->r, lim) || !fits(d->c * d->r, d->s, lim))
-        return GEMM_ERR_INVALID_ARG;
+    for (int i = 0; i < d->nd; ++i) {
+        if (d->size[i] < 1 || d->kern[i] < 1 || d->pad[i] < 0 || d->stride[i] < 1 ||
+            d->dil[i] < 1)
+            return GEMM_ERR_INVALID_ARG;
+        for (int64_t v : {d->size[i], d->kern[i], d->pad[i], d->stride[i], d->dil[i]})
+            if (v > lim) return GEMM_ERR_INVALID_ARG;
+        // padded extents and dilated filter spans stay within int32 kernel math
+        if (d->size[i] + 2 * d->pad[i] > lim || !fits(d->dil[i], d->kern[i] - 1, lim))
+            return GEMM_ERR_INVALID_ARG;
+        d->out[i] = out_extent(d->size[i], d->pad[i], d->kern[i], d->stride[i], d->dil[i]);
+        if (d->out[i] < 1) return GEMM_ERR_INVALID_ARG;
+    }
+    // GEMM extents (output volume, C_in times the filter volume) and the
+    // elements of one channel stay within the kernels' int32 range
+    int64_t vo = 1, vk = d->c, vi = 1;
+    for (int i = 0; i < d->nd; ++i) {
+        if (!fits(vo, d->out[i], lim) || !fits(vk, d->kern[i], lim) || !fits(vi, d->size[i], lim))
+            return GEMM_ERR_INVALID_ARG;
+        vo *= d->out[i];
+        vk *= d->kern[i];
+        vi *= d->size[i];
+    }
     // tensor sizes
-    if (!fits(d->crs(), d->ld(), kMaxElems) || !fits(d->n, d->c, kMaxElems) ||
-        !fits(d->n * d->c, d->h, kMaxElems) || !fits(d->n * d->c * d->h, d->w, kMaxElems) ||
-        !fits(d->n, d->k, kMaxElems) || !fits(d->n * d->k, d->pq(), kMaxElems) ||
-        !fits(d->k, d->crs(), kMaxElems))
+    if (!fits(d->crs(), d->ld(), kMaxElems) || !fits(d->n * d->c, vi, kMaxElems) ||
+        !fits(d->n * d->k, vo, kMaxElems) || !fits(d->k, d->crs(), kMaxElems))
         return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
+}
+
+int dims_2d(const conv2d_params *p, Dims *d)
+{
+    if (p == nullptr) return GEMM_ERR_INVALID_ARG;
+    *d = Dims{p->batch, p->in_channels, p->out_channels, 2,
+              {p->height, p->width}, {p->kernel_h, p->kernel_w}, {p->pad_h, p->pad_w},
+              {p->stride_h, p->stride_w}, {p->dilation_h, p->dilation_w}, {0, 0}};
+    return check_dims(d);
+}
+
+int dims_nd(const convnd_params *p, Dims *d)
+{
+    if (p == nullptr || p->ndim < 1 || p->ndim > kMaxD) return GEMM_ERR_INVALID_ARG;
+    *d = Dims{};
+    d->n = p->batch;
+    d->c = p->in_channels;
+    d->k = p->out_channels;
+    d->nd = p->ndim;
+    for (int i = 0; i < p->ndim; ++i) {
+        d->size[i] = p->size[i];
+        d->kern[i] = p->kernel[i];
+        d->pad[i] = p->pad[i];
+        d->stride[i] = p->stride[i];
+        d->dil[i] = p->dilation[i];
+    }
+    return check_dims(d);
 }
 
 int elem_size(int dtype) { return dtype == GEMM_DTYPE_F32 ? 4 : 2; }
@@ -235,69 +335,81 @@ void div_magic(uint32_t d, uint64_t *m, int *shift)
     *shift = 32 + l;
 }
 
+template <int D>
+void launch_d(int esize, bool buffer, dim3 grid, hipStream_t stream, const Im2colArgs &a)
+{
+    const dim3 block(kThreads);
+    if (esize == 4) {
+        if (buffer)
+            hipLaunchKernelGGL((im2col_buffer_kernel<4, D>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((im2col_kernel<4, D>), grid, block, 0, stream, a);
+    } else {
+        if (buffer)
+            hipLaunchKernelGGL((im2col_buffer_kernel<2, D>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((im2col_kernel<2, D>), grid, block, 0, stream, a);
+    }
+}
+
 hipError_t launch_im2col(int esize, const Dims &d, const void *image, void *cols, int64_t ld,
                          hipStream_t stream)
 {
-    Im2colArgs a;
+    Im2colArgs a{};
     a.x = image;
     a.cols = cols;
     a.ld = ld;
-    a.h = (int)d.h;
-    a.w = (int)d.w;
-    a.r = (int)d.r;
-    a.s = (int)d.s;
-    a.ph = (int)d.ph;
-    a.pw = (int)d.pw;
-    a.sh = (int)d.sh;
-    a.sw = (int)d.sw;
-    a.dh = (int)d.dh;
-    a.dw = (int)d.dw;
-    a.q_out = (int)d.Q;
-    a.pq = (int)d.pq();
-    div_magic((uint32_t)d.Q, &a.q_magic, &a.q_shift);
+    for (int i = 0; i < d.nd; ++i) {
+        a.size[i] = (int)d.size[i];
+        a.kern[i] = (int)d.kern[i];
+        a.pad[i] = (int)d.pad[i];
+        a.stride[i] = (int)d.stride[i];
+        a.dil[i] = (int)d.dil[i];
+        a.out[i] = (int)d.out[i];
+        div_magic((uint32_t)d.out[i], &a.out_magic[i], &a.out_shift[i]);
+    }
+    a.vol_out = (int)d.vol_out();
+    a.img_elems = (int)d.img_elems();
+    a.groups_per_ci = (int)(d.vol_kern() / d.kern[d.nd - 1]);
     const int64_t per_block = (int64_t)kThreads * kEpt;
-    a.jblocks = (int)((d.pq() + per_block - 1) / per_block);
-    const int64_t blocks = d.c * d.r * a.jblocks;
+    a.jblocks = (int)((d.vol_out() + per_block - 1) / per_block);
+    const int64_t blocks = d.c * a.groups_per_ci * a.jblocks;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)blocks), block(kThreads);
     // buffer offsets are signed 32-bit: the channel must span less than 2 GiB
-    const bool buffer = d.h * d.w * esize < (int64_t(1) << 31);
-    if (esize == 4) {
-        if (buffer)
-            hipLaunchKernelGGL(im2col_buffer_kernel<4>, grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL(im2col_kernel<4>, grid, block, 0, stream, a);
-    } else {
-        if (buffer)
-            hipLaunchKernelGGL(im2col_buffer_kernel<2>, grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL(im2col_kernel<2>, grid, block, 0, stream, a);
+    const bool buffer = d.img_elems() * esize < (int64_t(1) << 31);
+    const dim3 grid((unsigned)blocks);
+    switch (d.nd) {
+    case 1: launch_d<1>(esize, buffer, grid, stream, a); break;
+    case 2: launch_d<2>(esize, buffer, grid, stream, a); break;
+    case 3: launch_d<3>(esize, buffer, grid, stream, a); break;
+    default: launch_d<4>(esize, buffer, grid, stream, a); break;
     }
     return hipGetLastError();
 }
 
-// Geometry of the implicit-GEMM loaders; the image of one batch element must
-// span less than 2 GiB (buffer offsets are signed 32-bit).
+// Geometry of the implicit-GEMM loaders (2-D only); the image of one batch
+// element must span less than 2 GiB (buffer offsets are signed 32-bit).
 int make_geom(const Dims &d, int esize, ConvGeom *g)
 {
-    if (d.c * d.h * d.w * esize >= (int64_t(1) << 31)) return GEMM_ERR_INVALID_ARG;
-    g->h = (int)d.h;
-    g->w = (int)d.w;
-    g->r = (int)d.r;
-    g->s = (int)d.s;
-    g->ph = (int)d.ph;
-    g->pw = (int)d.pw;
-    g->sh = (int)d.sh;
-    g->sw = (int)d.sw;
-    g->dh = (int)d.dh;
-    g->dw = (int)d.dw;
-    g->q = (int)d.Q;
-    g->pq = (int)d.pq();
+    if (d.nd != 2 || d.c * d.img_elems() * esize >= (int64_t(1) << 31))
+        return GEMM_ERR_INVALID_ARG;
+    g->h = (int)d.size[0];
+    g->w = (int)d.size[1];
+    g->r = (int)d.kern[0];
+    g->s = (int)d.kern[1];
+    g->ph = (int)d.pad[0];
+    g->pw = (int)d.pad[1];
+    g->sh = (int)d.stride[0];
+    g->sw = (int)d.stride[1];
+    g->dh = (int)d.dil[0];
+    g->dw = (int)d.dil[1];
+    g->q = (int)d.out[1];
+    g->pq = (int)d.vol_out();
     g->crs = (int)d.crs();
-    div_magic((uint32_t)d.Q, &g->q_magic, &g->q_shift);
-    div_magic((uint32_t)(d.r * d.s), &g->rs_magic, &g->rs_shift);
-    div_magic((uint32_t)d.s, &g->s_magic, &g->s_shift);
-    g->img_bytes = (int)(d.c * d.h * d.w * esize);
+    div_magic((uint32_t)d.out[1], &g->q_magic, &g->q_shift);
+    div_magic((uint32_t)(d.kern[0] * d.kern[1]), &g->rs_magic, &g->rs_shift);
+    div_magic((uint32_t)d.kern[1], &g->s_magic, &g->s_shift);
+    g->img_bytes = (int)(d.c * d.img_elems() * esize);
     return GEMM_OK;
 }
 
@@ -320,106 +432,134 @@ int device_ok()
     return GEMM_OK;
 }
 
+// ------------------------------------ routines shared by 2-D and N-D calls --
+
+int64_t workspace_bytes(int dtype, int rc, const Dims &d)
+{
+    if (!valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
+    if (rc != GEMM_OK) return rc;
+    return d.crs() * d.ld() * elem_size(dtype);
+}
+
+int im2col(int dtype, const Dims &d, int64_t image, const void *x, void *cols, int64_t ld_cols,
+           hipStream_t stream)
+{
+    if (!valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    if (image < 0 || image >= d.n || x == nullptr || cols == nullptr || ld_cols < d.vol_out() ||
+        !fits(d.crs(), ld_cols, kMaxElems) || !aligned_to(x, es) || !aligned_to(cols, es))
+        return GEMM_ERR_INVALID_ARG;
+    const int rc = device_ok();
+    if (rc != GEMM_OK) return rc;
+    const char *img = static_cast<const char *>(x) + image * d.c * d.img_elems() * es;
+    return launch_im2col(es, d, img, cols, ld_cols, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int fwd(int dtype, int dtype_y, const Dims &d, const void *x, const void *w, void *y,
+        void *workspace, int64_t ws_bytes, hipStream_t stream)
+{
+    if (!valid_dtype(dtype) || !valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
+    if (d.n == 0) return GEMM_OK;
+    const int es = elem_size(dtype), esy = elem_size(dtype_y);
+    if (x == nullptr || w == nullptr || y == nullptr || !aligned_to(x, es) || !aligned_to(w, es) ||
+        !aligned_to(y, esy))
+        return GEMM_ERR_INVALID_ARG;
+    int rc = check_workspace(d, dtype, workspace, ws_bytes);
+    if (rc != GEMM_OK) return rc;
+    if ((rc = device_ok()) != GEMM_OK) return rc;
+    const int64_t ld = d.ld(), vo = d.vol_out();
+    for (int64_t n = 0; n < d.n; ++n) {
+        const char *img = static_cast<const char *>(x) + n * d.c * d.img_elems() * es;
+        if (launch_im2col(es, d, img, workspace, ld, stream) != hipSuccess) return GEMM_ERR_HIP;
+        // y[n] (C_out x output volume) = w (C_out x C_in filter volume) . cols
+        GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f, w, d.crs(),
+                   workspace, ld, static_cast<char *>(y) + n * d.k * vo * esy, vo};
+        if ((rc = gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    return GEMM_OK;
+}
+
+// dw := 0 through a GEMM with K == 0 (the empty sum over a batch of 0).
+int zero_dw(int dtype, const Dims &d, float *dw, hipStream_t stream)
+{
+    GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), 0, 1.0f, 0.0f,
+               nullptr, 1, nullptr, 1, dw, d.crs()};
+    return gemm_run(g, -1, 0, stream);
+}
+
+int bwd_weight(int dtype, const Dims &d, const void *x, const void *dy, float *dw, void *workspace,
+               int64_t ws_bytes, hipStream_t stream)
+{
+    if (!valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    if (dw == nullptr || !aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
+    if (d.n == 0) return zero_dw(dtype, d, dw, stream);
+    if (x == nullptr || dy == nullptr || !aligned_to(x, es) || !aligned_to(dy, es))
+        return GEMM_ERR_INVALID_ARG;
+    int rc = check_workspace(d, dtype, workspace, ws_bytes);
+    if (rc != GEMM_OK) return rc;
+    if ((rc = device_ok()) != GEMM_OK) return rc;
+    const int64_t ld = d.ld(), vo = d.vol_out();
+    for (int64_t n = 0; n < d.n; ++n) {
+        const char *img = static_cast<const char *>(x) + n * d.c * d.img_elems() * es;
+        if (launch_im2col(es, d, img, workspace, ld, stream) != hipSuccess) return GEMM_ERR_HIP;
+        // dw (C_out x C_in filter volume) (+)= dy[n] (C_out x output volume) . cols^T
+        GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
+                   n == 0 ? 0.0f : 1.0f, static_cast<const char *>(dy) + n * d.k * vo * es, vo,
+                   workspace, ld, dw, d.crs()};
+        if ((rc = gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    return GEMM_OK;
+}
+
 }  // namespace
 }  // namespace dg
 
 extern "C" {
 
+// ------------------------------------------------------------------- 2-D --
+
 int conv2d_output_size(const conv2d_params *p, int64_t *out_h, int64_t *out_w)
 {
     dg::Dims d;
-    const int rc = dg::check_dims(p, &d);
+    const int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (out_h) *out_h = d.P;
-    if (out_w) *out_w = d.Q;
+    if (out_h) *out_h = d.out[0];
+    if (out_w) *out_w = d.out[1];
     return GEMM_OK;
 }
 
 int64_t conv2d_workspace_size(int dtype, const conv2d_params *p)
 {
     dg::Dims d;
-    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
-    const int rc = dg::check_dims(p, &d);
-    if (rc != GEMM_OK) return rc;
-    return d.crs() * d.ld() * dg::elem_size(dtype);
+    const int rc = dg::dims_2d(p, &d);
+    return dg::workspace_bytes(dtype, rc, d);
 }
 
 int conv2d_im2col(int dtype, const conv2d_params *p, int64_t image, const void *x, void *cols,
                   int64_t ld_cols, hipStream_t stream)
 {
     dg::Dims d;
-    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::check_dims(p, &d);
-    if (rc != GEMM_OK) return rc;
-    const int es = dg::elem_size(dtype);
-    if (image < 0 || image >= d.n || x == nullptr || cols == nullptr || ld_cols < d.pq() ||
-        !dg::fits(d.crs(), ld_cols, dg::kMaxElems) || !dg::aligned_to(x, es) ||
-        !dg::aligned_to(cols, es))
-        return GEMM_ERR_INVALID_ARG;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    const char *img = static_cast<const char *>(x) + image * d.c * d.h * d.w * es;
-    return dg::launch_im2col(es, d, img, cols, ld_cols, stream) == hipSuccess ? GEMM_OK
-                                                                              : GEMM_ERR_HIP;
+    const int rc = dg::dims_2d(p, &d);
+    return rc != GEMM_OK ? rc : dg::im2col(dtype, d, image, x, cols, ld_cols, stream);
 }
 
 int conv2d_fwd(int dtype, int dtype_y, const conv2d_params *p, const void *x, const void *w,
                void *y, void *workspace, int64_t workspace_bytes, hipStream_t stream)
 {
     dg::Dims d;
-    if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::check_dims(p, &d);
-    if (rc != GEMM_OK) return rc;
-    if (d.n == 0) return GEMM_OK;
-    const int es = dg::elem_size(dtype), esy = dg::elem_size(dtype_y);
-    if (x == nullptr || w == nullptr || y == nullptr || !dg::aligned_to(x, es) ||
-        !dg::aligned_to(w, es) || !dg::aligned_to(y, esy))
-        return GEMM_ERR_INVALID_ARG;
-    if ((rc = dg::check_workspace(d, dtype, workspace, workspace_bytes)) != GEMM_OK) return rc;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    const int64_t ld = d.ld();
-    for (int64_t n = 0; n < d.n; ++n) {
-        const char *img = static_cast<const char *>(x) + n * d.c * d.h * d.w * es;
-        if (dg::launch_im2col(es, d, img, workspace, ld, stream) != hipSuccess) return GEMM_ERR_HIP;
-        // y[n] (C_out x PQ) = w (C_out x C_in R S) . cols (C_in R S x PQ)
-        dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, d.pq(), d.crs(), 1.0f, 0.0f,
-                       w, d.crs(), workspace, ld,
-                       static_cast<char *>(y) + n * d.k * d.pq() * esy, d.pq()};
-        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
-    }
-    return GEMM_OK;
+    const int rc = dg::dims_2d(p, &d);
+    return rc != GEMM_OK ? rc
+                         : dg::fwd(dtype, dtype_y, d, x, w, y, workspace, workspace_bytes, stream);
 }
 
 int conv2d_bwd_weight(int dtype, const conv2d_params *p, const void *x, const void *dy, float *dw,
                       void *workspace, int64_t workspace_bytes, hipStream_t stream)
 {
     dg::Dims d;
-    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::check_dims(p, &d);
-    if (rc != GEMM_OK) return rc;
-    const int es = dg::elem_size(dtype);
-    if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
-    if (d.n == 0) {
-        // the empty sum: dw := 0 (a GEMM with K == 0)
-        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), 0, 1.0f, 0.0f,
-                       nullptr, 1, nullptr, 1, dw, d.crs()};
-        return dg::gemm_run(g, -1, 0, stream);
-    }
-    if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
-        return GEMM_ERR_INVALID_ARG;
-    if ((rc = dg::check_workspace(d, dtype, workspace, workspace_bytes)) != GEMM_OK) return rc;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    const int64_t ld = d.ld();
-    for (int64_t n = 0; n < d.n; ++n) {
-        const char *img = static_cast<const char *>(x) + n * d.c * d.h * d.w * es;
-        if (dg::launch_im2col(es, d, img, workspace, ld, stream) != hipSuccess) return GEMM_ERR_HIP;
-        // dw (C_out x C_in R S) (+)= dy[n] (C_out x PQ) . cols^T, cols stored C_in R S x PQ
-        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), d.pq(), 1.0f,
-                       n == 0 ? 0.0f : 1.0f,
-                       static_cast<const char *>(dy) + n * d.k * d.pq() * es, d.pq(),
-                       workspace, ld, dw, d.crs()};
-        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
-    }
-    return GEMM_OK;
+    const int rc = dg::dims_2d(p, &d);
+    return rc != GEMM_OK ? rc
+                         : dg::bwd_weight(dtype, d, x, dy, dw, workspace, workspace_bytes, stream);
 }
 
 int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const void *x,
@@ -427,7 +567,7 @@ int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const vo
 {
     dg::Dims d;
     if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::check_dims(p, &d);
+    int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
     if (d.n == 0) return GEMM_OK;
     const int es = dg::elem_size(dtype), esy = dg::elem_size(dtype_y);
@@ -437,12 +577,12 @@ int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const vo
     dg::ConvGeom geom;
     if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
     if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    const int64_t vo = d.vol_out();
     for (int64_t n = 0; n < d.n; ++n) {
         // y[n] (C_out x PQ) = w (C_out x C_in R S) . cols(x[n]), cols formed in the loader
-        dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, d.pq(), d.crs(), 1.0f, 0.0f,
-                       w, d.crs(), static_cast<const char *>(x) + n * d.c * d.h * d.w * es, 1,
-                       static_cast<char *>(y) + n * d.k * d.pq() * esy, d.pq(),
-                       dg::B_CONV_FWD, &geom};
+        dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f,
+                       w, d.crs(), static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1,
+                       static_cast<char *>(y) + n * d.k * vo * esy, vo, dg::B_CONV_FWD, &geom};
         if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
     }
     return GEMM_OK;
@@ -453,30 +593,71 @@ int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x,
 {
     dg::Dims d;
     if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::check_dims(p, &d);
+    int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
     const int es = dg::elem_size(dtype);
     if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
-    if (d.n == 0) {
-        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), 0, 1.0f, 0.0f,
-                       nullptr, 1, nullptr, 1, dw, d.crs()};
-        return dg::gemm_run(g, -1, 0, stream);
-    }
+    if (d.n == 0) return dg::zero_dw(dtype, d, dw, stream);
     if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
         return GEMM_ERR_INVALID_ARG;
     dg::ConvGeom geom;
     if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
     if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    const int64_t vo = d.vol_out();
     for (int64_t n = 0; n < d.n; ++n) {
         // dw (C_out x C_in R S) (+)= dy[n] (C_out x PQ) . cols(x[n])^T
-        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), d.pq(), 1.0f,
-                       n == 0 ? 0.0f : 1.0f,
-                       static_cast<const char *>(dy) + n * d.k * d.pq() * es, d.pq(),
-                       static_cast<const char *>(x) + n * d.c * d.h * d.w * es, 1, dw, d.crs(),
+        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
+                       n == 0 ? 0.0f : 1.0f, static_cast<const char *>(dy) + n * d.k * vo * es, vo,
+                       static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1, dw, d.crs(),
                        dg::B_CONV_WGRAD, &geom};
         if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
     }
     return GEMM_OK;
+}
+
+// ------------------------------------------------------------------- N-D --
+
+int convnd_output_size(const convnd_params *p, int64_t *out)
+{
+    dg::Dims d;
+    const int rc = dg::dims_nd(p, &d);
+    if (rc != GEMM_OK) return rc;
+    if (out)
+        for (int i = 0; i < d.nd; ++i) out[i] = d.out[i];
+    return GEMM_OK;
+}
+
+int64_t convnd_workspace_size(int dtype, const convnd_params *p)
+{
+    dg::Dims d;
+    const int rc = dg::dims_nd(p, &d);
+    return dg::workspace_bytes(dtype, rc, d);
+}
+
+int convnd_im2col(int dtype, const convnd_params *p, int64_t image, const void *x, void *cols,
+                  int64_t ld_cols, hipStream_t stream)
+{
+    dg::Dims d;
+    const int rc = dg::dims_nd(p, &d);
+    return rc != GEMM_OK ? rc : dg::im2col(dtype, d, image, x, cols, ld_cols, stream);
+}
+
+int convnd_fwd(int dtype, int dtype_y, const convnd_params *p, const void *x, const void *w,
+               void *y, void *workspace, int64_t workspace_bytes, hipStream_t stream)
+{
+    dg::Dims d;
+    const int rc = dg::dims_nd(p, &d);
+    return rc != GEMM_OK ? rc
+                         : dg::fwd(dtype, dtype_y, d, x, w, y, workspace, workspace_bytes, stream);
+}
+
+int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const void *dy, float *dw,
+                      void *workspace, int64_t workspace_bytes, hipStream_t stream)
+{
+    dg::Dims d;
+    const int rc = dg::dims_nd(p, &d);
+    return rc != GEMM_OK ? rc
+                         : dg::bwd_weight(dtype, d, x, dy, dw, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

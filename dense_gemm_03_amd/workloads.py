@@ -45,7 +45,22 @@ name                batch  C_in    H x W     C_out  R x S   pad  seed
 conv-64c-31k        1      64      128x128   64     31x31   15   108
 conv-64c-31k-bf16   1      64      128x128   64     31x31   15   109
 conv-small-batch    4      16      40x36     24     5x3     2    110
-==================  =====  ======  ========  =====  ======  ===  ====  Large operands are drawn in row chunks; the
+==================  =====  ======  ========  =====  ======  ===  ====
+
+Convolutions with more spatial dimensions (``CONVND_WORKLOADS``; the same
+page's aim of convolution beyond two dimensions: a 3-D filter over a stack of
+frames, a 4-D one over a grid of such stacks), drawn the same way; stride and
+dilation 1, padding that keeps the output the size of the input:
+
+=================  =====  ====  =====  =============  ==========  ====
+name               batch  C_in  C_out  size           kernel      seed
+=================  =====  ====  =====  =============  ==========  ====
+conv3d-32c-k7      1      32    32     16x64x64       7x7x7       111
+conv3d-32c-k7-bf16 1      32    32     16x64x64       7x7x7       112
+conv4d-16c-k5      2      16    32     6x6x24x24      3x3x5x5     113
+=================  =====  ====  =====  =============  ==========  ====
+
+Large operands are drawn in row chunks; the
 PCG64 stream yields the same values whether drawn at once or in chunks.
 
 The im2col shape is the weight-gradient GEMM of a 2-D convolution with a large
@@ -302,5 +317,89 @@ CONV_WORKLOADS = {
         ConvWorkload("conv-64c-31k", "f32", 1, 64, 128, 128, 64, 31, 31, 15, 1, 1, 108),
         ConvWorkload("conv-64c-31k-bf16", "bf16", 1, 64, 128, 128, 64, 31, 31, 15, 1, 1, 109),
         ConvWorkload("conv-small-batch", "f32", 4, 16, 40, 36, 24, 5, 3, 2, 1, 1, 110),
+    ]
+}
+
+
+@dataclass(frozen=True)
+class ConvNdWorkload:
+    """A convolution with len(size) spatial dimensions, channel-first:
+    x (batch, cin, *size), filters (cout, cin, *kernel), output (batch, cout,
+    *out); stride and dilation 1, padding pad per dimension."""
+    name: str
+    dtype: str  # "f32" or "bf16" (x, w and dy)
+    batch: int
+    cin: int
+    cout: int
+    size: tuple
+    kernel: tuple
+    pad: tuple
+    seed: int
+
+    @property
+    def nd(self) -> int:
+        return len(self.size)
+
+    @property
+    def stride(self) -> tuple:
+        return (1,) * self.nd
+
+    @property
+    def dilation(self) -> tuple:
+        return (1,) * self.nd
+
+    @property
+    def out(self) -> tuple:
+        return tuple(s + 2 * p - k + 1 for s, k, p in zip(self.size, self.kernel, self.pad))
+
+    @property
+    def vol_out(self) -> int:
+        return int(np.prod(self.out))
+
+    @property
+    def crs(self) -> int:
+        return self.cin * int(np.prod(self.kernel))
+
+    @property
+    def flops(self) -> int:
+        """Multiply-adds of the forward pass (or of the filter gradient) x 2."""
+        return 2 * self.batch * self.cout * self.vol_out * self.crs
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def im2col_bytes(self) -> int:
+        """Compulsory HBM bytes of one image's convolution matrix: read the
+        image once, write the matrix once."""
+        return (self.cin * int(np.prod(self.size)) + self.crs * self.vol_out) * self.in_bytes
+
+    def _draw(self, shape, seed):
+        if self.dtype == "f32":
+            return uniform_f32(shape, seed)
+        return normal_bf16_bits(shape, seed)
+
+    def x(self):
+        return self._draw((self.batch, self.cin) + tuple(self.size), self.seed)
+
+    def weights(self):
+        return self._draw((self.cout, self.cin) + tuple(self.kernel), self.seed + 1000)
+
+    def dy(self):
+        return self._draw((self.batch, self.cout) + self.out, self.seed + 2000)
+
+
+# A 7 x 7 x 7 filter over 16 frames of 64 x 64 (convolution matrix 10976 x
+# 65536: 2.9 GB in fp32) and a 3 x 3 x 5 x 5 filter over a 6 x 6 grid of
+# 24 x 24 images.
+CONVND_WORKLOADS = {
+    c.name: c
+    for c in [
+        ConvNdWorkload("conv3d-32c-k7", "f32", 1, 32, 32, (16, 64, 64), (7, 7, 7), (3, 3, 3), 111),
+        ConvNdWorkload("conv3d-32c-k7-bf16", "bf16", 1, 32, 32, (16, 64, 64), (7, 7, 7),
+                       (3, 3, 3), 112),
+        ConvNdWorkload("conv4d-16c-k5", "f32", 2, 16, 32, (6, 6, 24, 24), (3, 3, 5, 5),
+                       (1, 1, 2, 2), 113),
     ]
 }

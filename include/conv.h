@@ -1,5 +1,6 @@
 /*
- * 2-D convolution on MI355X (gfx950) as im2col + GEMM, on one GPU.
+ * Convolution on MI355X (gfx950) as im2col + GEMM, on one GPU: 2-D, and 1 to
+ * 4 spatial dimensions (the convnd_* calls at the end).
  *
  * The operation ("Three X's: a new level of working with large convolutions
  * in PyTorch for model training", sections "Where large convolution kernels
@@ -45,8 +46,9 @@
  * GEMM_ERR_INVALID_ARG, with nothing launched, for: a size below 1 (batch may
  * be 0: nothing to do), negative padding, stride or dilation below 1, a
  * filter that does not fit (P or Q below 1), a dimension or product of
- * dimensions beyond the library's range (each GEMM extent must stay below
- * 2^30, each tensor below 2^62 elements), a null pointer, a pointer not
+ * dimensions beyond the library's range (each GEMM extent and one image
+ * channel must stay below 2^30 elements, each tensor below 2^62), a null
+ * pointer, a pointer not
  * aligned to its element size, a workspace that is too small or not 16-byte
  * aligned, an unknown dtype.  y must not overlap x, w or the workspace; dw
  * must not overlap x, dy or the workspace.
@@ -108,6 +110,59 @@ int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const vo
                         const void *w, void *y, hipStream_t stream);
 int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x, const void *dy,
                                float *dw, hipStream_t stream);
+
+/*
+ * Convolution with D = 1 to 4 spatial dimensions ("Three X's", opening and
+ * section "CuBLAS": the page's subject is convolution beyond two dimensions;
+ * the convolution matrix gains one index per dimension in its row and column
+ * numbering and one loop per dimension over the filter taps).  With size
+ * S_d, kernel K_d, padding p_d, stride t_d and dilation l_d per dimension
+ * (d = 0 .. D-1, the last one innermost):
+ *
+ *   O_d = floor((S_d + 2 p_d - l_d (K_d - 1) - 1) / t_d) + 1
+ *   y[n][co][o] = sum_{ci, k} x[n][ci][o t - p + k l] * w[co][ci][k]
+ *
+ * with o and k D-vectors and the products element-wise, positions outside
+ * the image reading as zero, no filter flip.  The filter gradient is
+ * dw[co][ci][k] = sum_{n, o} dy[n][co][o] * x[n][ci][o t - p + k l].
+ *
+ * Layout (dense, channel-first):  x [batch][C_in][S_0]..[S_{D-1}],
+ * w and dw [C_out][C_in][K_0]..[K_{D-1}],  y and dy [batch][C_out][O_0]..[O_{D-1}].
+ * Convolution matrix of an image: row (ci, k_0, .., k_{D-1}) and column
+ * (o_0, .., o_{D-1}), both numbered row-major; C_in prod(K) rows of
+ * round_up(prod(O), 8) elements in the workspace.  D = 2 gives exactly the
+ * conv2d_* calls above (kernel_h = K_0, kernel_w = K_1, and so on).
+ *
+ * Types, workspace, ownership, streams and errors as for the 2-D calls; also
+ * GEMM_ERR_INVALID_ARG for ndim outside 1..4.  Entries of the per-dimension
+ * arrays at index ndim and beyond are ignored.
+ */
+typedef struct {
+    int64_t batch, in_channels, out_channels, ndim;
+    int64_t size[4], kernel[4], pad[4], stride[4], dilation[4];
+} convnd_params;
+
+/* Output extents O_0 .. O_{ndim-1} into out[0 .. ndim) (may be NULL).  Host
+ * logic only. */
+int convnd_output_size(const convnd_params *p, int64_t *out);
+
+/* Bytes of workspace convnd_fwd and convnd_bwd_weight need; negative (a
+ * gemm_status) on invalid arguments.  Host logic only. */
+int64_t convnd_workspace_size(int dtype, const convnd_params *p);
+
+/* The convolution matrix of image `image` of x into cols (ld_cols >= prod(O));
+ * the same bits as x, zero in the padding. */
+int convnd_im2col(int dtype, const convnd_params *p, int64_t image, const void *x, void *cols,
+                  int64_t ld_cols, hipStream_t stream);
+
+/* y := conv(x, w); dtype of x and w, dtype_y of y. */
+int convnd_fwd(int dtype, int dtype_y, const convnd_params *p, const void *x, const void *w,
+               void *y, void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* dw := sum over the batch of the filter gradient (fp32); batch == 0 gives
+ * dw = 0. */
+int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const void *dy, float *dw,
+                      void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ def header_functions():
     for path in HEADERS:
         text = open(path).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:gemm|conv2d)_\w+)\s*\(",
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:gemm|conv2d|convnd)_\w+)\s*\(",
                                 text, re.M))
     return sorted(names)
 
@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 24, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -245,3 +245,65 @@ def test_conv_host_logic_and_invalid_arguments():
     assert dg.conv2d_bwd_weight_implicit(BF16, huge, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     # an empty batch: nothing to compute for the forward
     assert dg.conv2d_fwd(F32, F32, P(0, 3, 10, 9, 4, 3, 2), None, None, None, None, 0) == dg.GEMM_OK
+
+
+def test_convnd_host_logic_and_invalid_arguments():
+    """Output and workspace sizes of the N-D entry points, the 2-D case equal
+    to the conv2d calls', and argument checks that fail before any device
+    call."""
+    N = dg.convnd_params
+    p3 = N(1, 32, 32, (16, 64, 64), (7, 7, 7), (3, 3, 3))
+    assert dg.convnd_output_size(p3) == (0, (16, 64, 64))
+    assert dg.convnd_workspace_size(dg.GEMM_DTYPE_F32, p3) == 32 * 343 * 65536 * 4
+    p4 = N(2, 16, 32, (6, 6, 24, 24), (3, 3, 5, 5), (1, 1, 2, 2))
+    assert dg.convnd_output_size(p4) == (0, (6, 6, 24, 24))
+    p1 = N(1, 2, 3, (37,), (5,), (2,), (2,), (1,))
+    assert dg.convnd_output_size(p1) == (0, (19,))
+    # rows C_in prod(K), columns round_up(prod(O), 8)
+    assert dg.convnd_workspace_size(dg.GEMM_DTYPE_BF16, p1) == 2 * 5 * 24 * 2
+    # D = 2 gives the conv2d numbers
+    for args in [(2, 3, 10, 9, 4, 3, 2, (1, 0), (2, 3), (1, 2)), (1, 64, 128, 128, 64, 31, 31, (15, 15))]:
+        b, ci, h, w, co, r, s_ = args[:7]
+        pad, stride, dil = (list(args[7:]) + [(0, 0), (1, 1), (1, 1)][len(args) - 7:])[:3]
+        p2 = dg.conv2d_params(*args)
+        pn = N(b, ci, co, (h, w), (r, s_), pad, stride, dil)
+        rc, P, Q = dg.conv2d_output_size(p2)
+        assert dg.convnd_output_size(pn) == (rc, (P, Q))
+        for dt in (dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16):
+            assert dg.convnd_workspace_size(dt, pn) == dg.conv2d_workspace_size(dt, p2)
+    bad = [N(1, 0, 1, (8,), (3,)), N(1, 1, 1, (8, 8), (9, 1)), N(1, 1, 1, (8,), (3,), (-1,)),
+           N(1, 1, 1, (8,), (3,), (0,), (0,)), N(1, 1, 1, (8,), (3,), (0,), (1,), (0,)),
+           N(-1, 1, 1, (8,), (3,)), N(1, 1, 1, (1 << 16, 1 << 15), (1, 1)),  # 2^31 per channel
+           N(1, 1 << 16, 1, (32, 32, 32), (32, 32, 32))]                     # C_in prod(K) = 2^31
+    for params in bad:
+        assert dg.convnd_output_size(params)[0] == dg.GEMM_ERR_INVALID_ARG, params.ndim
+        assert dg.convnd_workspace_size(dg.GEMM_DTYPE_F32, params) == dg.GEMM_ERR_INVALID_ARG
+    for nd in (0, 5, -1):
+        q = N(1, 1, 1, (8,), (3,))
+        q.ndim = nd
+        assert dg.convnd_output_size(q)[0] == dg.GEMM_ERR_INVALID_ARG
+        assert dg.convnd_workspace_size(dg.GEMM_DTYPE_F32, q) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.load_library().convnd_output_size(None, None) == dg.GEMM_ERR_INVALID_ARG
+    ok = N(2, 3, 4, (5, 6, 7), (3, 2, 3), (1, 0, 1))
+    need = dg.convnd_workspace_size(dg.GEMM_DTYPE_F32, ok)
+    vo = 5 * 5 * 7
+    p = 4096
+    F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
+    assert dg.convnd_workspace_size(5, ok) == dg.GEMM_ERR_INVALID_ARG
+    calls = [
+        lambda: dg.convnd_fwd(F32, F32, bad[0], p, p, p, p, need),
+        lambda: dg.convnd_fwd(7, F32, ok, p, p, p, p, need),
+        lambda: dg.convnd_fwd(F32, 7, ok, p, p, p, p, need),
+        lambda: dg.convnd_fwd(F32, F32, ok, None, p, p, p, need),
+        lambda: dg.convnd_fwd(F32, F32, ok, p, p, p, p, need - 1),
+        lambda: dg.convnd_fwd(F32, F32, ok, p, p, p, p + 8, need),
+        lambda: dg.convnd_fwd(BF16, BF16, ok, p, p, p + 1, p, need),
+        lambda: dg.convnd_bwd_weight(F32, ok, p, p, p + 2, p, need),
+        lambda: dg.convnd_bwd_weight(F32, ok, p, None, p, p, need),
+        lambda: dg.convnd_im2col(F32, ok, 2, p, p, vo),
+        lambda: dg.convnd_im2col(F32, ok, 0, p, p, vo - 1),
+        lambda: dg.convnd_im2col(BF16, ok, 0, p + 1, p, vo),
+    ]
+    for t, call in enumerate(calls):
+        assert call() == dg.GEMM_ERR_INVALID_ARG, t
+    assert dg.convnd_fwd(F32, F32, N(0, 3, 4, (5,), (3,)), None, None, None, None, 0) == dg.GEMM_OK

@@ -1,0 +1,241 @@
+"""GPU parity of convolution with 1 to 4 spatial dimensions as im2col + GEMM
+("Three X's: a new level of working with large convolutions in PyTorch for
+model training": convolution beyond two dimensions, the convolution matrix
+gaining one index and one filter loop per dimension) against the N-D
+direct-convolution oracle, through the C ABI (include/conv.h, convnd_*).
+
+* The im2col kernel is a copy with zero fill: its matrix must equal the
+  oracle's bit for bit (both element types); columns beyond the output
+  volume of a padded leading dimension stay untouched.
+* Integer-valued tensors: every sum is exact, so forward and filter gradient
+  equal the oracle bit for bit (bf16 y: the exact value rounded once).
+* Random tensors: |y - y_ref| <= tol * S (1e-5 fp32, 4e-3 bf16 inputs).
+* D = 2 through the N-D entry points gives the conv2d entry points' bits.
+* The full-size 3-D and 4-D workloads at sampled outputs and taps.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dense_gemm_03_amd as dg
+import oracle
+from dense_gemm_03_amd import workloads as wl
+from oracle import convnd as ocn
+from oracle.convnd import NdShape
+from tests.gpu_util import TOL, log, to_device
+from tests.test_conv import check_close
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
+
+SHAPES = [
+    # batch, cin, cout, size, kernel, pad, stride, dilation
+    NdShape(1, 3, 2, (37,), (5,), (2,), (2,), (1,)),                              # 1-D, stride
+    NdShape(2, 2, 3, (40,), (7,), (0,), (1,), (3,)),                              # 1-D, dilation
+    NdShape(1, 1, 1, (2100,), (9,), (4,)),                                        # > 1024 columns
+    NdShape(2, 3, 5, (7, 6, 9), (3, 2, 4), (1, 0, 2), (1, 2, 1), (2, 1, 1)),       # 3-D mixed
+    NdShape(1, 2, 70, (12, 40, 33), (5, 3, 7), (2, 1, 3)),                       # 3-D, C_out > 64
+    NdShape(1, 4, 3, (3, 3, 3), (3, 3, 3)),                                       # one output
+    NdShape(2, 2, 2, (5, 4, 6, 7), (2, 3, 2, 3), (0, 1, 1, 2), (2, 1, 1, 2), (1, 1, 2, 1)),  # 4-D
+    NdShape(1, 1, 130, (3, 3, 3, 3), (3, 3, 3, 3), (1, 1, 1, 1)),                # 4-D, C_out > 128
+    NdShape(1, 3, 4, (6, 5, 9, 11), (3, 1, 3, 4), (1, 0, 1, 2)),
+]
+
+
+def _dev(a):
+    return to_device(np.ascontiguousarray(a))
+
+
+def _ints(shape, seed, bf16):
+    return wl.small_int_bf16_bits(shape, seed) if bf16 else wl.small_int_f32(shape, seed)
+
+
+def _randn(shape, seed, bf16):
+    return wl.normal_bf16_bits(shape, seed) if bf16 else wl.uniform_f32(shape, seed)
+
+
+def _params(c: NdShape):
+    return dg.convnd_params(c.batch, c.cin, c.cout, c.size, c.kernel, c.pad, c.stride, c.dilation)
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def run_im2col(x: np.ndarray, c: NdShape, n: int, ld: int, rows=None):
+    """The library's convolution matrix of image n (all rows or the listed
+    ones) in a buffer of ld + 5 columns prefilled with a sentinel; columns
+    beyond the output volume must keep it."""
+    import torch
+    bf16 = x.dtype == np.uint16
+    sentinel = 0x7FC1 if bf16 else 0x7FC00001
+    buf = torch.full((c.crs, ld + 5), sentinel, dtype=torch.int16 if bf16 else torch.int32,
+                     device="cuda:0")
+    xd = _dev(x)
+    rc = dg.convnd_im2col(BF16 if bf16 else F32, _params(c), n, xd.data_ptr(), buf.data_ptr(),
+                          ld + 5, _stream())
+    assert rc == dg.GEMM_OK
+    torch.cuda.synchronize()
+    if rows is not None:
+        buf = buf[torch.as_tensor(np.asarray(rows), device="cuda:0")]
+    got = buf.cpu().numpy().view(np.uint16 if bf16 else np.uint32)
+    assert np.all(got[:, c.vol_out:] == sentinel), "columns beyond the output volume were written"
+    return got[:, :c.vol_out]
+
+
+def run_fwd(x, w, c: NdShape, out_bf16=False):
+    import torch
+    y = dg.conv_nd(_dev(x), _dev(w), stride=c.stride, padding=c.pad, dilation=c.dilation,
+                   out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == c.y_shape
+    if out_bf16:
+        raw = y.cpu().view(torch.int16).numpy().view(np.uint16)
+        return oracle.bf16_bits_to_f64(raw), raw
+    raw = y.cpu().numpy()
+    return raw.astype(np.float64), raw
+
+
+def run_bwd(x, dy, c: NdShape):
+    import torch
+    dw = dg.conv_nd_weight_grad(_dev(x), _dev(dy), c.w_shape, stride=c.stride, padding=c.pad,
+                                dilation=c.dilation)
+    torch.cuda.synchronize()
+    return dw.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_im2col_bit_exact(bf16):
+    for t, c in enumerate(SHAPES):
+        x = _randn(c.x_shape, 600 + t, bf16)
+        for n in sorted({0, c.batch - 1}):
+            log("im2col %s image %d" % (c, n))
+            got = run_im2col(x, c, n, c.vol_out + 3 * t)
+            want = ocn.im2col(x, c, n)
+            if not bf16:
+                want = want.view(np.uint32)
+            assert np.array_equal(got, want), "%s image %d" % (c, n)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_fwd_and_filter_gradient_exact_integers(bf16):
+    for t, c in enumerate(SHAPES):
+        x, w = _ints(c.x_shape, 700 + t, bf16), _ints(c.w_shape, 710 + t, bf16)
+        dy = _ints(c.y_shape, 720 + t, bf16)
+        ref, _ = ocn.fwd(x, w, c)
+        for out_bf16 in (False, True):
+            log("fwd %s y %s" % (c, "bf16" if out_bf16 else "f32"))
+            got, raw = run_fwd(x, w, c, out_bf16)
+            if out_bf16:
+                assert np.array_equal(raw, oracle.round_to_bf16_bits(ref)), str(c)
+            else:
+                assert np.array_equal(got, ref), str(c)
+        log("filter gradient %s" % (c,))
+        ref, _ = ocn.bwd_weight(x, dy, c)
+        assert np.array_equal(run_bwd(x, dy, c), ref), str(c)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_random_within_tolerance(bf16):
+    tol = TOL["bf16" if bf16 else "f32"]
+    for t, c in enumerate(SHAPES):
+        x, w = _randn(c.x_shape, 800 + t, bf16), _randn(c.w_shape, 810 + t, bf16)
+        dy = _randn(c.y_shape, 820 + t, bf16)
+        ref, S = ocn.fwd(x, w, c)
+        check_close(run_fwd(x, w, c)[0], ref, S, tol, "fwd %s" % (c,))
+        check_close(run_fwd(x, w, c, True)[0], ref, S, tol, "fwd bf16 y %s" % (c,), True)
+        ref, S = ocn.bwd_weight(x, dy, c)
+        check_close(run_bwd(x, dy, c), ref, S, tol, "filter gradient %s" % (c,))
+
+
+def test_two_dimensions_match_conv2d_bits():
+    """The N-D entry points at D = 2 and the conv2d ones give identical bits."""
+    import torch
+    c = NdShape(2, 5, 9, (21, 19), (5, 3), (2, 1), (2, 1), (1, 2))
+    x, w, dy = _randn(c.x_shape, 1, False), _randn(c.w_shape, 2, False), _randn(c.y_shape, 3, False)
+    xd, wd, dyd = _dev(x), _dev(w), _dev(dy)
+    y_nd = dg.conv_nd(xd, wd, stride=c.stride, padding=c.pad, dilation=c.dilation)
+    y_2d = dg.conv2d(xd, wd, stride=c.stride, padding=c.pad, dilation=c.dilation)
+    g_nd = dg.conv_nd_weight_grad(xd, dyd, c.w_shape, stride=c.stride, padding=c.pad,
+                                  dilation=c.dilation)
+    g_2d = dg.conv2d_weight_grad(xd, dyd, c.w_shape, stride=c.stride, padding=c.pad,
+                                 dilation=c.dilation)
+    torch.cuda.synchronize()
+    assert torch.equal(y_nd, y_2d) and torch.equal(g_nd, g_2d)
+
+
+def test_empty_batch():
+    """batch 0: the forward does nothing; the filter gradient is the empty
+    sum (zeros)."""
+    import torch
+    c = NdShape(0, 3, 2, (6, 7, 8), (3, 3, 3), (1, 1, 1))
+    dw = torch.full(c.w_shape, float("nan"), device="cuda:0")
+    y = torch.full((1,), 7.0, device="cuda:0")
+    assert dg.convnd_fwd(F32, F32, _params(c), None, None, y.data_ptr(), None, 0, _stream()) == dg.GEMM_OK
+    assert dg.convnd_bwd_weight(F32, _params(c), None, None, dw.data_ptr(), None, 0, _stream()) == dg.GEMM_OK
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0) and float(y[0]) == 7.0
+
+
+def _shape_of(wk):
+    return NdShape(wk.batch, wk.cin, wk.cout, wk.size, wk.kernel, wk.pad, wk.stride, wk.dilation)
+
+
+@pytest.mark.parametrize("name", sorted(wl.CONVND_WORKLOADS))
+def test_full_size_sampled(name):
+    """The N-D workloads at full size: forward outputs and filter-gradient taps
+    at sampled positions (corners included) against the oracle, one sum each,
+    and the convolution matrix of the last image bit for bit at sampled rows."""
+    wk = wl.CONVND_WORKLOADS[name]
+    c = _shape_of(wk)
+    bf16 = wk.dtype == "bf16"
+    tol = TOL[wk.dtype]
+    x, w, dy = wk.x(), wk.weights(), wk.dy()
+    rng = np.random.default_rng(wk.seed + 5)
+    log("[%s] forward" % name)
+    y, _ = run_fwd(x, w, c)
+    yflat = y.reshape(-1)
+    idx = rng.integers(0, yflat.size, 256)
+    corners = [np.ravel_multi_index((n, co) + tuple(e - 1 if hi else 0 for e, hi in zip(c.out, bits)),
+                                    c.y_shape)
+               for n, co, bits in [(0, 0, (0,) * c.nd), (c.batch - 1, c.cout - 1, (1,) * c.nd),
+                                   (0, c.cout - 1, (1,) + (0,) * (c.nd - 1)),
+                                   (c.batch - 1, 0, (0,) * (c.nd - 1) + (1,))]]
+    idx[:4] = corners
+    ref, S = ocn.fwd_at(x, w, c, idx)
+    check_close(yflat[idx], ref, S, tol, name + " fwd (256 sampled)")
+    log("[%s] filter gradient" % name)
+    dw = run_bwd(x, dy, c).reshape(-1)
+    tidx = rng.integers(0, dw.size, 256)
+    tidx[0], tidx[1] = 0, dw.size - 1
+    ref, S = ocn.bwd_weight_at(x, dy, c, tidx)
+    check_close(dw[tidx], ref, S, tol, name + " filter gradient (256 sampled)")
+    log("[%s] convolution matrix rows" % name)
+    n = c.batch - 1
+    rows = np.sort(rng.integers(0, c.crs, 16))
+    got = run_im2col(x, c, n, c.vol_out, rows=rows)
+    vol_k = int(np.prod(c.kernel))
+    one = NdShape(1, 1, 1, c.size, c.kernel, c.pad, c.stride, c.dilation)
+    for t, row in enumerate(rows):
+        ci, k = divmod(int(row), vol_k)
+        sub = ocn.im2col(np.ascontiguousarray(x[n:n + 1, ci:ci + 1]), one, 0)[k]
+        assert np.array_equal(got[t], sub.view(np.uint16) if bf16 else sub.view(np.uint32)), row
+
+
+def test_full_size_exact_integers_sampled():
+    """Integer tensors of the full 3-D shape: sampled outputs and taps exact."""
+    wk = wl.CONVND_WORKLOADS["conv3d-32c-k7"]
+    c = _shape_of(wk)
+    x, w, dy = _ints(c.x_shape, 17, False), _ints(c.w_shape, 18, False), _ints(c.y_shape, 19, False)
+    y, _ = run_fwd(x, w, c)
+    rng = np.random.default_rng(4)
+    idx = rng.integers(0, y.size, 256)
+    ref, _ = ocn.fwd_at(x, w, c, idx)
+    assert np.array_equal(y.reshape(-1)[idx], ref)
+    dw = run_bwd(x, dy, c).reshape(-1)
+    tidx = rng.integers(0, dw.size, 256)
+    ref, _ = ocn.bwd_weight_at(x, dy, c, tidx)
+    assert np.array_equal(dw[tidx], ref)

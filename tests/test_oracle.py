@@ -289,3 +289,17 @@ def test_generators_nd_shapes_and_conv_workloads():
         assert c.x().shape == (c.batch, c.cin, c.h, c.w)
         assert c.weights().shape == (c.cout, c.cin, c.r, c.s)
         assert c.dy().shape == (c.batch, c.cout, c.p, c.q)
+
+
+def test_nd_conv_workloads_match_the_oracle_shape():
+    """Every N-D convolution workload: its output extents agree with the
+    oracle's (the floor formula at stride and dilation 1), and the tensors it
+    draws have the oracle's shapes."""
+    from oracle.convnd import NdShape
+    for c in workloads.CONVND_WORKLOADS.values():
+        shape = NdShape(c.batch, c.cin, c.cout, c.size, c.kernel, c.pad, c.stride, c.dilation)
+        assert shape.out == c.out == tuple(c.size), c.name  # "same" padding
+        assert shape.crs == c.crs and shape.vol_out == c.vol_out
+        assert c.x().shape == shape.x_shape
+        assert c.weights().shape == shape.w_shape
+        assert c.dy().shape == shape.y_shape
