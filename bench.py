@@ -19,7 +19,9 @@ in HBM.  Prints ONE JSON line:
                           (transposed operands, alpha/beta, bf16 C)
   convolution             the im2col + GEMM convolution of the 64-channel
                           31x31-filter workload, fp32 and bf16 (forward,
-                          filter gradient, and the im2col kernel against HBM)
+                          filter gradient, their implicit-GEMM forms, and the
+                          im2col kernel against HBM), and of the 3-D (7x7x7
+                          filters, fp32 and bf16) and 4-D workloads
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -42,7 +44,8 @@ HBM_PEAK_GBS = 8000.0
 PRIMARY = "fp32-4096"
 SECONDARY = ["bf16-8192"]
 EXTRA = ["im2col", "tall", "bf16-8192-nt-bf16c", "bf16-8192-tn-acc", "fp32-4096-tt-ab"]
-CONV = ["conv-64c-31k", "conv-64c-31k-bf16"]
+CONV = ["conv-64c-31k", "conv-64c-31k-bf16", "conv3d-32c-k7", "conv3d-32c-k7-bf16",
+        "conv4d-16c-k5"]
 
 
 def log(msg: str) -> None:
@@ -172,17 +175,19 @@ def measure(name: str, steps: int, warmup: int):
 
 def measure_conv(name: str, steps: int, warmup: int):
     """Time the convolution `name`: forward pass and filter gradient through
-    im2col + GEMM and through the implicit GEMM, and the im2col kernel alone
-    (its HBM roofline)."""
-    import ctypes
-
+    im2col + GEMM (2-D workloads also through the implicit GEMM), and the
+    im2col kernel alone (its HBM roofline)."""
     import torch
 
     import dense_gemm_03_amd as dg
-    from dense_gemm_03_amd.workloads import CONV_WORKLOADS
+    from dense_gemm_03_amd.workloads import CONV_WORKLOADS, CONVND_WORKLOADS
 
-    c = CONV_WORKLOADS[name]
-    log("[bench] %s: drawing x %s, filters and output gradient" % (name, (c.batch, c.cin, c.h, c.w)))
+    nd = name in CONVND_WORKLOADS
+    c = CONVND_WORKLOADS[name] if nd else CONV_WORKLOADS[name]
+    x_shape = (c.batch, c.cin) + (tuple(c.size) if nd else (c.h, c.w))
+    w_shape = (c.cout, c.cin) + (tuple(c.kernel) if nd else (c.r, c.s))
+    out = c.out if nd else (c.p, c.q)
+    log("[bench] %s: drawing x %s, filters and output gradient" % (name, x_shape))
 
     def dev(a):
         if a.dtype == np.uint16:
@@ -191,26 +196,43 @@ def measure_conv(name: str, steps: int, warmup: int):
 
     x, w, dy = dev(c.x()), dev(c.weights()), dev(c.dy())
     dtype = dg.GEMM_DTYPE_F32 if c.dtype == "f32" else dg.GEMM_DTYPE_BF16
-    params = dg.conv2d_params(c.batch, c.cin, c.h, c.w, c.cout, c.r, c.s, (c.pad, c.pad),
-                              (c.stride, c.stride), (c.dilation, c.dilation))
-    need = dg.conv2d_workspace_size(dtype, params)
+    F32 = dg.GEMM_DTYPE_F32
+    if nd:
+        params = dg.convnd_params(c.batch, c.cin, c.cout, c.size, c.kernel, c.pad, c.stride,
+                                  c.dilation)
+        api = {"ws": dg.convnd_workspace_size, "fwd": dg.convnd_fwd,
+               "wgrad": dg.convnd_bwd_weight, "im2col": dg.convnd_im2col}
+    else:
+        params = dg.conv2d_params(c.batch, c.cin, c.h, c.w, c.cout, c.r, c.s, (c.pad, c.pad),
+                                  (c.stride, c.stride), (c.dilation, c.dilation))
+        api = {"ws": dg.conv2d_workspace_size, "fwd": dg.conv2d_fwd,
+               "wgrad": dg.conv2d_bwd_weight, "im2col": dg.conv2d_im2col}
+    need = api["ws"](dtype, params)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
-    y = torch.empty((c.batch, c.cout, c.p, c.q), dtype=torch.float32, device="cuda:0")
-    dw = torch.empty((c.cout, c.cin, c.r, c.s), dtype=torch.float32, device="cuda:0")
+    y = torch.empty((c.batch, c.cout) + tuple(out), dtype=torch.float32, device="cuda:0")
+    dw = torch.empty(w_shape, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     ld = need // (c.crs * c.in_bytes)
 
     def fwd():
-        assert dg.conv2d_fwd(dtype, dg.GEMM_DTYPE_F32, params, x.data_ptr(), w.data_ptr(),
-                             y.data_ptr(), ws.data_ptr(), need, sp) == dg.GEMM_OK
+        assert api["fwd"](dtype, F32, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                          ws.data_ptr(), need, sp) == dg.GEMM_OK
 
     def wgrad():
-        assert dg.conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                                    ws.data_ptr(), need, sp) == dg.GEMM_OK
+        assert api["wgrad"](dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                            ws.data_ptr(), need, sp) == dg.GEMM_OK
 
     def im2col():
-        assert dg.conv2d_im2col(dtype, params, 0, x.data_ptr(), ws.data_ptr(), ld, sp) == dg.GEMM_OK
+        assert api["im2col"](dtype, params, 0, x.data_ptr(), ws.data_ptr(), ld, sp) == dg.GEMM_OK
+
+    def fwd_implicit():
+        assert dg.conv2d_fwd_implicit(dtype, F32, params, x.data_ptr(), w.data_ptr(),
+                                      y.data_ptr(), sp) == dg.GEMM_OK
+
+    def wgrad_implicit():
+        assert dg.conv2d_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(),
+                                             dw.data_ptr(), sp) == dg.GEMM_OK
 
     def timed(fn, n):
         for _ in range(warmup):
@@ -225,18 +247,12 @@ def measure_conv(name: str, steps: int, warmup: int):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / n, e0.elapsed_time(e1) / n
 
-    def fwd_implicit():
-        assert dg.conv2d_fwd_implicit(dtype, dg.GEMM_DTYPE_F32, params, x.data_ptr(),
-                                      w.data_ptr(), y.data_ptr(), sp) == dg.GEMM_OK
-
-    def wgrad_implicit():
-        assert dg.conv2d_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(),
-                                             dw.data_ptr(), sp) == dg.GEMM_OK
-
     res = {}
     peak = PEAK_TFLOPS[c.dtype]
-    for label, fn in (("fwd", fwd), ("wgrad", wgrad), ("fwd_implicit", fwd_implicit),
-                      ("wgrad_implicit", wgrad_implicit)):
+    routes = [("fwd", fwd), ("wgrad", wgrad)]
+    if not nd:
+        routes += [("fwd_implicit", fwd_implicit), ("wgrad_implicit", wgrad_implicit)]
+    for label, fn in routes:
         wall_ms, ev_ms = timed(fn, steps)
         log("[bench] %s %s: %.3f ms per call" % (name, label, ev_ms))
         ach = c.flops / (ev_ms * 1e-3) / 1e12
@@ -250,14 +266,18 @@ def measure_conv(name: str, steps: int, warmup: int):
                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}}
     log("[bench] %s im2col: %.3f ms, %.0f GB/s" % (name, ev_ms, gbs))
-    out = {"workload": name, "dtype": c.dtype,
-           "shape": {"batch": c.batch, "cin": c.cin, "hw": [c.h, c.w], "cout": c.cout,
-                     "rs": [c.r, c.s], "pad": c.pad, "stride": c.stride, "dilation": c.dilation},
-           "gemm_fwd": [c.cout, c.p * c.q, c.crs], "gemm_wgrad": [c.cout, c.crs, c.p * c.q]}
-    out.update(res)
+    vol_out = int(np.prod(out))
+    result = {"workload": name, "dtype": c.dtype,
+              "shape": {"batch": c.batch, "cin": c.cin, "size": list(x_shape[2:]),
+                        "cout": c.cout, "kernel": list(w_shape[2:]),
+                        "pad": list(c.pad) if nd else c.pad,
+                        "stride": list(c.stride) if nd else c.stride,
+                        "dilation": list(c.dilation) if nd else c.dilation},
+              "gemm_fwd": [c.cout, vol_out, c.crs], "gemm_wgrad": [c.cout, c.crs, vol_out]}
+    result.update(res)
     del x, w, dy, ws, y, dw
     torch.cuda.empty_cache()
-    return out
+    return result
 
 
 def cpu_baseline(name: str, budget_s: float = 10.0):

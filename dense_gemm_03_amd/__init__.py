@@ -41,8 +41,10 @@ SIGNATURES = {
     "gemm_status_string": (ctypes.c_char_p, [_int]),
     "gemm_num_configs": (_int, [_int]),
     "gemm_select_config": (_int, [_int, _i64, _i64, _i64]),
+    "gemm_select_config_ex": (_int, [_int, _int, _int, _i64, _i64, _i64]),
     "gemm_config_name": (ctypes.c_char_p, [_int, _int]),
     "gemm_split_k": (_int, [_int, _int, _i64, _i64, _i64]),
+    "gemm_split_k_ex": (_int, [_int, _int, _int, _int, _i64, _i64, _i64]),
     "gemm_f32_with_config": (_int, [_int, _int] + _GEMM_ARGS),
     "gemm_bf16_with_config": (_int, [_int, _int] + _GEMM_ARGS),
     "gemm_ex": (_int, _GEMM_EX_ARGS),
@@ -169,6 +171,10 @@ def gemm_select_config(dtype: int, M: int, N: int, K: int) -> int:
     return load_library().gemm_select_config(dtype, M, N, K)
 
 
+def gemm_select_config_ex(dtype: int, transa: int, transb: int, M: int, N: int, K: int) -> int:
+    return load_library().gemm_select_config_ex(dtype, transa, transb, M, N, K)
+
+
 def gemm_config_name(dtype: int, cfg: int):
     name = load_library().gemm_config_name(dtype, cfg)
     return name.decode() if name is not None else None
@@ -176,6 +182,10 @@ def gemm_config_name(dtype: int, cfg: int):
 
 def gemm_split_k(dtype: int, cfg: int, M: int, N: int, K: int) -> int:
     return load_library().gemm_split_k(dtype, cfg, M, N, K)
+
+
+def gemm_split_k_ex(dtype: int, cfg: int, transa: int, transb: int, M: int, N: int, K: int) -> int:
+    return load_library().gemm_split_k_ex(dtype, cfg, transa, transb, M, N, K)
 
 
 # ----------------------------------------------------------- torch helper --

@@ -17,6 +17,8 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps all in-kernel int math exact
 constexpr int kComputeUnits = 256;             // MI355X: 8 XCDs x 32 CUs
 constexpr int kTargetBlocks = 2 * kComputeUnits;
+constexpr int kStreamBlocks = 6 * kComputeUnits;
+constexpr int kMaxStreamSplits = 16;
 
 const TileConfig *table(int dtype, int *count)
 {
@@ -78,12 +80,20 @@ int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N)
 // peak each tile shape reached on 4096^3 fp32 / 8192^3 bf16 (full grids), so
 // the choice trades per-block efficiency against quantisation of the grid
 // over 256 compute units.
-int select_config(int dtype, int64_t M, int64_t N, int64_t K)
+int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
 {
     (void)K;
+    // Skinny products (a few dozen rows, wide N, usually long K: the
+    // convolution GEMMs with few output channels) stream the large operand
+    // once; 32-row blocks waste no matrix-core work at M <= 32, and when that
+    // operand is read k-contiguous (B^T) rows of 256 bytes keep its reads long.
+    const bool skinny = M <= 32 && N >= 1024;
     if (dtype == GEMM_DTYPE_F32) {
         static const int tall = config_index(dtype, "f32_128x64_w2x2_s2");
         static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
+        static const int wide_t = config_index(dtype, "f32_64x128x64_w1x4_s2");
+        static const int skinny_n = config_index(dtype, "f32_32x128_w1x4_s3");
+        static const int skinny_t = config_index(dtype, "f32_32x128x64_w1x4_s2");
         static const int narrow = config_index(dtype, "f32_128x64_w2x1_s2");
         static const int small = config_index(dtype, "f32_64x64_w2x2_s2");
         static const Candidate large[] = {
@@ -92,7 +102,9 @@ int select_config(int dtype, int64_t M, int64_t N, int64_t K)
             {"f32_64x64_w2x2_s3", 3, 0.89},
         };
         if (N <= 64 && M >= 4096) return tall;   // tall-skinny: many 64-row blocks
-        if (M <= 64 && N >= 1024) return wide;   // few rows, wide N, split-K
+        if (skinny && layout == LAYOUT_NN) return skinny_n;
+        if (skinny && layout == LAYOUT_NT) return skinny_t;
+        if (M <= 64 && N >= 1024) return layout == LAYOUT_NT ? wide_t : wide;  // split-K
         if (M >= 2048 && N >= 2048) return best_of(dtype, large, 3, M, N);
         if (N <= 64) return narrow;
         return small;
@@ -104,6 +116,10 @@ int select_config(int dtype, int64_t M, int64_t N, int64_t K)
     static const int medium = config_index(dtype, "bf16_128x128x64_w2x2_s2");
     static const int small = config_index(dtype, "bf16_64x64x64_w2x2_s2");
     static const int wide = config_index(dtype, "bf16_64x256x64_w1x4_s3");
+    static const int skinny_n = config_index(dtype, "bf16_32x256x64_w1x4_s3");
+    static const int skinny_t = config_index(dtype, "bf16_32x256x128_w1x4_s2");
+    if (skinny && layout == LAYOUT_NN) return skinny_n;
+    if (skinny && layout == LAYOUT_NT) return skinny_t;
     if (M <= 64 && N >= 1024) return wide;   // few rows, wide N, split-K
     if (M >= 2048 && N >= 2048) return best_of(dtype, large, 2, M, N);
     if (M * N >= int64_t(1024) * 1024) return medium;
@@ -126,22 +142,30 @@ int select_implicit(int dtype, int64_t M)
     return M <= 64 ? wide : M <= 128 ? mid : large;
 }
 
-// Number of K slices: 1 when the output alone yields enough blocks to fill the
-// chip; otherwise enough slices for about two blocks per compute unit, each
-// slice keeping at least four k-tiles.  forced > 0 overrides the target.
-void plan_split(const TileConfig &c, int64_t M, int64_t N, int64_t K, int forced, int *splits,
-                int *k_per_split)
+// Number of K slices.  Large blocks: 1 when the output alone yields enough
+// blocks to fill the chip; otherwise enough slices for about two blocks per
+// compute unit.  Blocks of at most 64 rows (the skinny and wide classes) carry
+// little work each and stream their large operand: at most 16 slices, and when
+// B is read k-contiguous (B^T, rows of a few hundred bytes per k-tile) they
+// aim at six blocks per compute unit even when the output alone fills the
+// chip, since each block then sustains less bandwidth.  Every slice keeps at
+// least four k-tiles.  forced > 0 overrides the target.
+void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K, int forced,
+                int *splits, int *k_per_split)
 {
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int64_t ktiles = ceil_div(K, c.bk);
+    const bool streaming = c.bm <= 64;
+    const bool b_kcontig = layout == LAYOUT_NT || layout == LAYOUT_TT;
     int64_t s;
     if (forced > 0) {
         s = forced;
-    } else if (tiles >= kComputeUnits) {
+    } else if (tiles >= kComputeUnits && !(streaming && b_kcontig)) {
         s = 1;
     } else {
-        s = ceil_div(kTargetBlocks, tiles);
-        const int64_t max_s = ktiles / 4;
+        s = ceil_div(streaming && b_kcontig ? kStreamBlocks : kTargetBlocks, tiles);
+        int64_t max_s = ktiles / 4;
+        if (streaming && max_s > kMaxStreamSplits) max_s = kMaxStreamSplits;
         if (s > max_s) s = max_s;
     }
     if (s < 1) s = 1;
@@ -261,11 +285,11 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
 
     const int ci = forced_cfg >= 0             ? forced_cfg
                    : call.bsrc != B_MATRIX ? select_implicit(call.dtype, M)
-                                           : select_config(call.dtype, M, N, K);
+                                           : select_config(call.dtype, layout, M, N, K);
     const TileConfig &cfg = tab[ci];
     if (kernel_of(cfg, true) == nullptr) return GEMM_ERR_INVALID_ARG;
     int splits = 1, kps = 0;
-    plan_split(cfg, M, N, K, forced_split, &splits, &kps);
+    plan_split(cfg, layout, M, N, K, forced_split, &splits, &kps);
 
     KernelArgs a{};
     a.A = call.A;
@@ -422,7 +446,16 @@ int gemm_select_config(int dtype, int64_t M, int64_t N, int64_t K)
 {
     int count = 0;
     if (!dg::table(dtype, &count) || M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
-    return dg::select_config(dtype, M, N, K);
+    return dg::select_config(dtype, dg::LAYOUT_NN, M, N, K);
+}
+
+int gemm_select_config_ex(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K)
+{
+    int count = 0;
+    if (!dg::table(dtype, &count) || M < 0 || N < 0 || K < 0 ||
+        (transa != GEMM_OP_N && transa != GEMM_OP_T) || (transb != GEMM_OP_N && transb != GEMM_OP_T))
+        return GEMM_ERR_INVALID_ARG;
+    return dg::select_config(dtype, transa * 2 + transb, M, N, K);
 }
 
 const char *gemm_config_name(int dtype, int cfg)
@@ -440,7 +473,20 @@ int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K)
     if (!tab || cfg < 0 || cfg >= count || M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || K == 0) return 1;
     int splits = 1, kps = 0;
-    dg::plan_split(tab[cfg], M, N, K, 0, &splits, &kps);
+    dg::plan_split(tab[cfg], dg::LAYOUT_NN, M, N, K, 0, &splits, &kps);
+    return splits;
+}
+
+int gemm_split_k_ex(int dtype, int cfg, int transa, int transb, int64_t M, int64_t N, int64_t K)
+{
+    int count = 0;
+    const dg::TileConfig *tab = dg::table(dtype, &count);
+    if (!tab || cfg < 0 || cfg >= count || M < 0 || N < 0 || K < 0 ||
+        (transa != GEMM_OP_N && transa != GEMM_OP_T) || (transb != GEMM_OP_N && transb != GEMM_OP_T))
+        return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || K == 0) return 1;
+    int splits = 1, kps = 0;
+    dg::plan_split(tab[cfg], transa * 2 + transb, M, N, K, 0, &splits, &kps);
     return splits;
 }
 

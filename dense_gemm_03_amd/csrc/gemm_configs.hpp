@@ -91,7 +91,15 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("f32_128x64_w4x1_s2", false, 128, 64, 32, 4, 1, 2, 8, NN)             \
     X("f32_64x64_w1x1_s2", false, 64, 64, 32, 1, 1, 2, 8, NN)               \
     X("f32_64x64_w1x1_s4", false, 64, 64, 32, 1, 1, 4, 8, NN)               \
-    X("f32_64x256_w1x4_s2", false, 64, 256, 32, 1, 4, 2, 1, NN)
+    X("f32_64x256_w1x4_s2", false, 64, 256, 32, 1, 4, 2, 1, NN)             \
+    X("f32_32x256_w1x4_s2", false, 32, 256, 32, 1, 4, 2, 1, SKINNY)         \
+    X("f32_32x256_w1x4_s3", false, 32, 256, 32, 1, 4, 3, 1, SKINNY)         \
+    X("f32_32x128_w1x2_s3", false, 32, 128, 32, 1, 2, 3, 1, SKINNY)         \
+    X("f32_32x128_w1x4_s3", false, 32, 128, 32, 1, 4, 3, 1, SKINNY)         \
+    X("f32_32x128x64_w1x4_s2", false, 32, 128, 64, 1, 4, 2, 1, KK)          \
+    X("f32_32x128x64_w1x4_s3", false, 32, 128, 64, 1, 4, 3, 1, KK)          \
+    X("f32_32x256x64_w1x4_s2", false, 32, 256, 64, 1, 4, 2, 1, KK)          \
+    X("f32_64x128x64_w1x4_s2", false, 64, 128, 64, 1, 4, 2, 1, KK)
 
 #define DG_BF16_TABLE(X)                                                    \
     X("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8, NN)        \
@@ -101,7 +109,14 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8, CONV)      \
     X("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8, ALL)           \
     X("bf16_64x256x64_w1x4_s3", true, 64, 256, 64, 1, 4, 3, 1, CONV)        \
-    X("bf16_64x256x64_w1x4_s2", true, 64, 256, 64, 1, 4, 2, 1, NN)
+    X("bf16_64x256x64_w1x4_s2", true, 64, 256, 64, 1, 4, 2, 1, NN)         \
+    X("bf16_32x256x64_w1x4_s2", true, 32, 256, 64, 1, 4, 2, 1, SKINNY)     \
+    X("bf16_32x256x64_w1x4_s3", true, 32, 256, 64, 1, 4, 3, 1, SKINNY)     \
+    X("bf16_32x128x64_w1x2_s3", true, 32, 128, 64, 1, 2, 3, 1, SKINNY)     \
+    X("bf16_32x256x128_w1x4_s2", true, 32, 256, 128, 1, 4, 2, 1, KK)       \
+    X("bf16_32x128x128_w1x4_s2", true, 32, 128, 128, 1, 4, 2, 1, KK)       \
+    X("bf16_32x128x128_w1x4_s3", true, 32, 128, 128, 1, 4, 3, 1, KK)       \
+    X("bf16_64x128x128_w1x4_s2", true, 64, 128, 128, 1, 4, 2, 1, KK)
 
 // Launcher pointers of one entry and layout: both alignments, or nullptr.
 #define DG_FNS(BF16, BM, BN, BK, WM, WN, S, L)                                               \
@@ -119,6 +134,14 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_FNS_CONV_NT(...) DG_FNS(__VA_ARGS__, NT)
 #define DG_FNS_CONV_TN(...) DG_FNS(__VA_ARGS__, TN)
 #define DG_FNS_CONV_TT(...) DG_FNS(__VA_ARGS__, TT)
+#define DG_FNS_SKINNY_NN(...) DG_FNS(__VA_ARGS__, NN)
+#define DG_FNS_SKINNY_NT(...) DG_FNS(__VA_ARGS__, NT)
+#define DG_FNS_SKINNY_TN(...) DG_NOFNS
+#define DG_FNS_SKINNY_TT(...) DG_NOFNS
+#define DG_FNS_KK_NN(...) DG_NOFNS
+#define DG_FNS_KK_NT(...) DG_FNS(__VA_ARGS__, NT)
+#define DG_FNS_KK_TN(...) DG_NOFNS
+#define DG_FNS_KK_TT(...) DG_NOFNS
 #define DG_FNS_NN_NN(...) DG_FNS(__VA_ARGS__, NN)
 #define DG_FNS_NN_NT(...) DG_NOFNS
 #define DG_FNS_NN_TN(...) DG_NOFNS
@@ -128,6 +151,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     {DG_IFNS(BF16, BM, BN, BK, WM, WN, CF), DG_IFNS(BF16, BM, BN, BK, WM, WN, CW)}
 #define DG_IMPL_ALL(...) {DG_NOFNS, DG_NOFNS}
 #define DG_IMPL_NN(...) {DG_NOFNS, DG_NOFNS}
+#define DG_IMPL_SKINNY(...) {DG_NOFNS, DG_NOFNS}
+#define DG_IMPL_KK(...) {DG_NOFNS, DG_NOFNS}
 
 // One table entry from one list item.
 #define DG_TABLE_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                        \

@@ -108,7 +108,7 @@ struct KernelArgs {
 // 4 bytes, and a 16-byte read serves 16 lanes per pass, so the 16 addresses of
 // a pass must cover 256 bytes that fall on distinct banks.
 //
-//   KMAJOR:  OUTER rows of BK elements (64 or 128 bytes).  Chunk c of row r
+//   KMAJOR:  OUTER rows of BK elements (64, 128 or 256 bytes).  Chunk c of row r
 //            sits in slot c ^ ((r / RPL) % CPR), RPL rows sharing a 256-byte
 //            bank line: the 16 rows a 16-lane pass reads at one chunk cover
 //            all 64 banks once, and so do the writes.
@@ -140,7 +140,7 @@ struct OpTile {
     static_assert(ROW_BYTES <= 1024 && 1024 % ROW_BYTES == 0, "rows must tile a 1 KiB piece");
     static constexpr int ROWS_PER_PIECE = 1024 / ROW_BYTES;
     static constexpr int RPL = 256 / ROW_BYTES;           // KMAJOR rows per bank line
-    static_assert(LAYOUT != KMAJOR || CPR * RPL == 16, "k-contiguous rows of 64 or 128 bytes");
+    static_assert(LAYOUT != KMAJOR || CPR * RPL == 16, "k-contiguous rows of 64, 128 or 256 bytes");
     static constexpr int SEGMASK = (OUTER / 32 >= 4) ? 3 : (OUTER / 32 - 1);
     static_assert(LAYOUT != MNMAJOR || BF16 || (OUTER % 64 == 0 && BK == 32),
                   "fp32 outer-contiguous tiles: OUTER % 64 == 0, BK == 32");

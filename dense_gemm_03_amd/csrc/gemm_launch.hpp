@@ -48,6 +48,18 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_CONV_TT(...) DG_INST(__VA_ARGS__, TT)
 #define DG_INST_CONV_CF(...) DG_IINST(__VA_ARGS__, CF)
 #define DG_INST_CONV_CW(...) DG_IINST(__VA_ARGS__, CW)
+#define DG_INST_SKINNY_NN(...) DG_INST(__VA_ARGS__, NN)
+#define DG_INST_SKINNY_NT(...) DG_INST(__VA_ARGS__, NT)
+#define DG_INST_SKINNY_TN(...)
+#define DG_INST_SKINNY_TT(...)
+#define DG_INST_SKINNY_CF(...)
+#define DG_INST_SKINNY_CW(...)
+#define DG_INST_KK_NN(...)
+#define DG_INST_KK_NT(...) DG_INST(__VA_ARGS__, NT)
+#define DG_INST_KK_TN(...)
+#define DG_INST_KK_TT(...)
+#define DG_INST_KK_CF(...)
+#define DG_INST_KK_CW(...)
 #define DG_INST_NN_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_NN_NT(...)
 #define DG_INST_NN_TN(...)

@@ -141,15 +141,21 @@ const char *gemm_status_string(int status);
  *
  * gemm_num_configs: number of table entries for a dtype (negative on a bad
  *   dtype).
- * gemm_select_config: the entry the dispatcher would use for this shape
- *   (pure host logic, no GPU access); negative on bad arguments.
+ * gemm_select_config: the entry the dispatcher would use for this shape of
+ *   the plain product A . B (pure host logic, no GPU access); negative on bad
+ *   arguments.
+ * gemm_select_config_ex: the same for op(A) . op(B) with the given transa,
+ *   transb (GEMM_OP_N / GEMM_OP_T): the choice depends on which operands are
+ *   read k-contiguous.
  * gemm_config_name: a static string naming an entry ("f32_128x128x32_w2x2"...),
  *   NULL when out of range.
  * gemm_split_k: the number of K slices the dispatcher would use with entry cfg
- *   for this shape (1 = no split); negative on bad arguments.
+ *   for this shape of the plain product (1 = no split); negative on bad
+ *   arguments.  gemm_split_k_ex: the same for the operand form (transa,
+ *   transb).
  * gemm_config_layouts: bit (transa * 2 + transb) is set when entry cfg has
- *   kernels for that operand form (every entry the dispatcher chooses has all
- *   four); negative on bad arguments.
+ *   kernels for that operand form (the entry the dispatcher chooses for an
+ *   operand form always has it); negative on bad arguments.
  * gemm_f32_with_config / gemm_bf16_with_config / gemm_ex_with_config: as
  *   gemm_f32 / gemm_bf16 / gemm_ex but with the table entry forced (an entry
  *   without kernels for the requested operand form is GEMM_ERR_INVALID_ARG);
@@ -158,8 +164,10 @@ const char *gemm_status_string(int status);
  */
 int gemm_num_configs(int dtype);
 int gemm_select_config(int dtype, int64_t M, int64_t N, int64_t K);
+int gemm_select_config_ex(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K);
 const char *gemm_config_name(int dtype, int cfg);
 int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K);
+int gemm_split_k_ex(int dtype, int cfg, int transa, int transb, int64_t M, int64_t N, int64_t K);
 int gemm_config_layouts(int dtype, int cfg);
 
 int gemm_f32_with_config(int cfg, int split_k,

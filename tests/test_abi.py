@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -71,6 +71,21 @@ def test_shape_classes_of_the_workloads():
     assert _cfg_for("tall")[2] == "f32_128x64_w2x2_s2"
     dtype, c, name, splits = _cfg_for("im2col")
     assert name == "f32_64x256_w1x4_s3" and splits == 8
+    # the convolution GEMMs with 32 output channels: 32-row blocks; the
+    # filter gradient (B^T) with 256-byte k-contiguous rows and 16 slices
+    F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
+    sel = lambda dt, tb, M, N, K: dg.gemm_config_name(dt, dg.gemm_select_config_ex(dt, 0, tb, M, N, K))
+    assert sel(F32, 0, 32, 65536, 10976) == "f32_32x128_w1x4_s3"
+    assert sel(F32, 1, 32, 10976, 65536) == "f32_32x128x64_w1x4_s2"
+    assert sel(BF16, 0, 32, 65536, 10976) == "bf16_32x256x64_w1x4_s3"
+    assert sel(BF16, 1, 32, 10976, 65536) == "bf16_32x256x128_w1x4_s2"
+    assert sel(F32, 1, 64, 61504, 16384) == "f32_64x128x64_w1x4_s2"
+    c = dg.gemm_select_config_ex(F32, 0, 1, 32, 10976, 65536)
+    assert dg.gemm_split_k_ex(F32, c, 0, 1, 32, 10976, 65536) == 16
+    c = dg.gemm_select_config_ex(F32, 0, 1, 64, 61504, 16384)
+    assert dg.gemm_split_k_ex(F32, c, 0, 1, 64, 61504, 16384) == 4   # 481 blocks already
+    assert dg.gemm_split_k(F32, c, 64, 61504, 16384) == 1            # the same as A . B
+    assert dg.gemm_split_k_ex(F32, c, 0, 2, 64, 61504, 16384) == dg.GEMM_ERR_INVALID_ARG
     for big in ("fp32-4096", "bf16-8192", "tall"):
         assert _cfg_for(big)[3] == 1
 
@@ -159,16 +174,24 @@ def test_gemm_ex_invalid_arguments_rejected_before_any_device_call():
 
 
 def test_layout_masks_cover_every_dispatched_entry():
-    """Every entry the dispatcher picks has kernels for all four operand
-    forms, and every entry has the plain form."""
+    """The entry the dispatcher picks for an operand form has kernels for that
+    form; the plain-product hook agrees with the general one at (N, N); every
+    entry has kernels for some form."""
     for dtype in (dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16):
         for c in range(dg.gemm_num_configs(dtype)):
-            assert dg.gemm_config_layouts(dtype, c) & 1
+            assert dg.gemm_config_layouts(dtype, c) & 0xF
         assert dg.gemm_config_layouts(dtype, -1) == dg.GEMM_ERR_INVALID_ARG
-        for M in (1, 33, 64, 65, 100, 1000, 2048, 4096, 8192, 65536):
-            for N in (1, 33, 64, 65, 100, 1000, 2048, 4096, 16384):
-                c = dg.gemm_select_config(dtype, M, N, 1024)
-                assert dg.gemm_config_layouts(dtype, c) == 0xF, (dtype, M, N)
+        for M in (1, 20, 32, 33, 64, 65, 100, 1000, 2048, 4096, 8192, 65536):
+            for N in (1, 33, 64, 65, 100, 1000, 1024, 2048, 4096, 16384):
+                assert dg.gemm_select_config(dtype, M, N, 1024) == \
+                    dg.gemm_select_config_ex(dtype, 0, 0, M, N, 1024)
+                for ta in (0, 1):
+                    for tb in (0, 1):
+                        c = dg.gemm_select_config_ex(dtype, ta, tb, M, N, 1024)
+                        assert dg.gemm_config_layouts(dtype, c) & (1 << (ta * 2 + tb)), \
+                            (dtype, M, N, ta, tb)
+        assert dg.gemm_select_config_ex(dtype, 2, 0, 4, 4, 4) == dg.GEMM_ERR_INVALID_ARG
+        assert dg.gemm_select_config_ex(dtype, 0, 0, -1, 4, 4) == dg.GEMM_ERR_INVALID_ARG
 
 
 def test_empty_output_is_a_no_op():

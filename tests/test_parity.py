@@ -23,7 +23,9 @@ F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
 
 
 def _configs(dtype):
-    return list(range(dg.gemm_num_configs(dtype)))
+    """Entries with kernels for the plain product A . B (entries built only
+    for A . B^T are covered by tests/test_variants.py)."""
+    return [c for c in range(dg.gemm_num_configs(dtype)) if dg.gemm_config_layouts(dtype, c) & 1]
 
 
 def _ints(shape, seed, bf16):

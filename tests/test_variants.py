@@ -158,6 +158,35 @@ def test_exact_every_layout_every_config(bf16):
 
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_one_hot_and_split_every_layout_every_config(bf16):
+    """Every entry and every operand form it has: one-hot probes A = e_i e_k^T
+    (C row i = op(B) row k, nothing else) at fragment and block edges, and
+    forced K slices (2, 3, 7) on integer operands, bit for bit."""
+    dtype = BF16 if bf16 else F32
+    one = wl.f32_to_bf16_bits(np.array([1.0], np.float32))[0] if bf16 else np.float32(1)
+    M, N, K = 260, 130, 97
+    for cfg in range(dg.gemm_num_configs(dtype)):
+        name = dg.gemm_config_name(dtype, cfg)
+        mask = dg.gemm_config_layouts(dtype, cfg)
+        for ta, tb in TRANS:
+            if not mask & (1 << (2 * ta + tb)):
+                continue
+            _, B = _operands(M, N, K, ta, tb, _ints, 7, bf16)
+            for i, k in [(0, 0), (31, 1), (32, 63), (77, 64), (128, 5), (255, 96), (259, 50)]:
+                A = np.zeros((K, M) if ta else (M, K), dtype=B.dtype)
+                A[(k, i) if ta else (i, k)] = one
+                what = "%s %s one-hot (%d,%d)" % (name, TNAME[ta, tb], i, k)
+                _, raw = run_ex(A, B, ta, tb, cfg=cfg)
+                check_exact_ex(raw, A, B, ta, tb, 1.0, 0.0, None, False, what)
+            A, B = _operands(70, 520, 3001, ta, tb, _ints, 9, bf16)
+            for sk in (2, 3, 7):
+                what = "%s %s split %d" % (name, TNAME[ta, tb], sk)
+                log(what)
+                _, raw = run_ex(A, B, ta, tb, cfg=cfg, split_k=sk)
+                check_exact_ex(raw, A, B, ta, tb, 1.0, 0.0, None, False, what)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 @pytest.mark.parametrize("out_bf16", [False, True], ids=["c_f32", "c_bf16"])
 def test_exact_alpha_beta(bf16, out_bf16):
     """alpha/beta epilogue on integers, with the dispatcher's choice and with
@@ -256,3 +285,25 @@ def test_variants_deterministic():
         outs.append(C)
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_dispatched_skinny_and_wide_classes(bf16):
+    """Shapes the dispatcher sends to the 32-row and 64-row streaming entries
+    (with its own K-slice plans), every operand form: bit for bit on integer
+    operands, and within tolerance on random ones."""
+    dtype = BF16 if bf16 else F32
+    for t, (M, N, K) in enumerate([(32, 1500, 700), (20, 1100, 2000), (1, 1024, 4100),
+                                   (48, 2000, 999), (64, 1030, 5000)]):
+        for ta, tb in TRANS:
+            cfg = dg.gemm_select_config_ex(dtype, int(ta), int(tb), M, N, K)
+            what = "%s %s %dx%dx%d (%s, %d slices)" % (
+                "bf16" if bf16 else "f32", TNAME[ta, tb], M, N, K, dg.gemm_config_name(dtype, cfg),
+                dg.gemm_split_k_ex(dtype, cfg, int(ta), int(tb), M, N, K))
+            log(what)
+            A, B = _operands(M, N, K, ta, tb, _ints, 60 + t, bf16)
+            _, raw = run_ex(A, B, ta, tb)
+            check_exact_ex(raw, A, B, ta, tb, 1.0, 0.0, None, False, what)
+            A, B = _operands(M, N, K, ta, tb, _randn, 70 + t, bf16)
+            C, _ = run_ex(A, B, ta, tb)
+            check_close_ex(C, A, B, ta, tb, 1.0, 0.0, None, False, what + " random")
