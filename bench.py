@@ -19,7 +19,8 @@ in HBM.  Prints ONE JSON line:
                           (transposed operands, alpha/beta, bf16 C)
   convolution             the im2col + GEMM convolution of the 64-channel
                           31x31-filter workload, fp32 and bf16 (forward,
-                          filter gradient, their implicit-GEMM forms, and the
+                          filter gradient, their implicit-GEMM forms with
+                          analytic and table address generation, and the
                           im2col kernel against HBM), and of the 3-D (7x7x7
                           filters, fp32 and bf16) and 4-D workloads
 
@@ -226,13 +227,17 @@ def measure_conv(name: str, steps: int, warmup: int):
     def im2col():
         assert api["im2col"](dtype, params, 0, x.data_ptr(), ws.data_ptr(), ld, sp) == dg.GEMM_OK
 
-    def fwd_implicit():
-        assert dg.conv2d_fwd_implicit(dtype, F32, params, x.data_ptr(), w.data_ptr(),
-                                      y.data_ptr(), sp) == dg.GEMM_OK
+    def implicit_fwd(mode):
+        def run():
+            assert dg.conv2d_fwd_implicit_ex(dtype, F32, params, mode, x.data_ptr(), w.data_ptr(),
+                                             y.data_ptr(), sp) == dg.GEMM_OK
+        return run
 
-    def wgrad_implicit():
-        assert dg.conv2d_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(),
-                                             dw.data_ptr(), sp) == dg.GEMM_OK
+    def implicit_wgrad(mode):
+        def run():
+            assert dg.conv2d_bwd_weight_implicit_ex(dtype, params, mode, x.data_ptr(),
+                                                    dy.data_ptr(), dw.data_ptr(), sp) == dg.GEMM_OK
+        return run
 
     def timed(fn, n):
         for _ in range(warmup):
@@ -251,7 +256,9 @@ def measure_conv(name: str, steps: int, warmup: int):
     peak = PEAK_TFLOPS[c.dtype]
     routes = [("fwd", fwd), ("wgrad", wgrad)]
     if not nd:
-        routes += [("fwd_implicit", fwd_implicit), ("wgrad_implicit", wgrad_implicit)]
+        A, T = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE
+        routes += [("fwd_implicit", implicit_fwd(A)), ("wgrad_implicit", implicit_wgrad(A)),
+                   ("fwd_implicit_table", implicit_fwd(T)), ("wgrad_implicit_table", implicit_wgrad(T))]
     for label, fn in routes:
         wall_ms, ev_ms = timed(fn, steps)
         log("[bench] %s %s: %.3f ms per call" % (name, label, ev_ms))

@@ -71,7 +71,11 @@ SIGNATURES.update({
     "conv2d_bwd_weight": (_int, [_int, _pp, _p, _p, _p, _p, _i64, _p]),
     "conv2d_fwd_implicit": (_int, [_int, _int, _pp, _p, _p, _p, _p]),
     "conv2d_bwd_weight_implicit": (_int, [_int, _pp, _p, _p, _p, _p]),
+    "conv2d_fwd_implicit_ex": (_int, [_int, _int, _pp, _int, _p, _p, _p, _p]),
+    "conv2d_bwd_weight_implicit_ex": (_int, [_int, _pp, _int, _p, _p, _p, _p]),
 })
+
+CONV_ADDR_DEFAULT, CONV_ADDR_ANALYTIC, CONV_ADDR_TABLE = 0, 1, 2
 
 
 class ConvNdParams(ctypes.Structure):
@@ -301,6 +305,16 @@ def conv2d_bwd_weight_implicit(dtype, params, x, dy, dw, stream=None) -> int:
     return load_library().conv2d_bwd_weight_implicit(dtype, ctypes.byref(params), x, dy, dw, stream)
 
 
+def conv2d_fwd_implicit_ex(dtype, dtype_y, params, addressing, x, w, y, stream=None) -> int:
+    return load_library().conv2d_fwd_implicit_ex(dtype, dtype_y, ctypes.byref(params), addressing,
+                                                 x, w, y, stream)
+
+
+def conv2d_bwd_weight_implicit_ex(dtype, params, addressing, x, dy, dw, stream=None) -> int:
+    return load_library().conv2d_bwd_weight_implicit_ex(dtype, ctypes.byref(params), addressing,
+                                                        x, dy, dw, stream)
+
+
 def convnd_params(batch, in_channels, out_channels, size, kernel, pad=None, stride=None,
                   dilation=None) -> ConvNdParams:
     """ConvNdParams for len(size) spatial dimensions (unused entries 0)."""
@@ -376,11 +390,15 @@ def _workspace(workspace, need, device):
     return workspace
 
 
+_ADDRESSING = {True: CONV_ADDR_DEFAULT, "analytic": CONV_ADDR_ANALYTIC, "table": CONV_ADDR_TABLE}
+
+
 def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None,
            implicit=False):
     """y = conv2d(x, w) (cross-correlation form, as torch.nn.functional.conv2d)
     through the im2col + GEMM path, or with ``implicit`` through the
-    implicit-GEMM path (no convolution matrix).  x (N, C_in, H, W) and w
+    implicit-GEMM path (no convolution matrix): True (the library's address
+    generation), "analytic" or "table".  x (N, C_in, H, W) and w
     (C_out, C_in, R, S) are both float32 or both bfloat16; y is float32
     (default) or bfloat16.  The im2col workspace (one image's convolution
     matrix) is allocated when not given."""
@@ -394,8 +412,8 @@ def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None
         stream = torch.cuda.current_stream(x.device).cuda_stream
     dtype_y = GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32
     if implicit:
-        rc = conv2d_fwd_implicit(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
-                                 stream)
+        rc = conv2d_fwd_implicit_ex(dtype, dtype_y, params, _ADDRESSING[implicit], x.data_ptr(),
+                                    w.data_ptr(), y.data_ptr(), stream)
     else:
         ws = _workspace(workspace, need, x.device)
         rc = conv2d_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
@@ -409,7 +427,7 @@ def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wor
                        stream=None, implicit=False):
     """dw (float32, weight_shape) = the filter gradient of conv2d for input x
     and output gradient dy, through the im2col + GEMM path (or, with
-    ``implicit``, the implicit-GEMM path)."""
+    ``implicit`` -- True, "analytic" or "table" -- the implicit-GEMM path)."""
     import torch
     params, dtype, P, Q, need = _conv_setup(x, tuple(weight_shape), stride, padding, dilation)
     if dy.dtype != x.dtype or not dy.is_contiguous() or \
@@ -419,8 +437,8 @@ def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wor
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     if implicit:
-        rc = conv2d_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                                        stream)
+        rc = conv2d_bwd_weight_implicit_ex(dtype, params, _ADDRESSING[implicit], x.data_ptr(),
+                                           dy.data_ptr(), dw.data_ptr(), stream)
     else:
         ws = _workspace(workspace, need, x.device)
         rc = conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),

@@ -33,6 +33,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 62;
 constexpr int kThreads = 256;
 constexpr int kEpt = 4;                            // elements per thread and tap
 constexpr int64_t kLdAlign = 8;                    // matrix rows padded to 16 bytes (bf16)
+constexpr bool kDefaultTable = false;              // addressing of the plain implicit calls
 
 // Geometry of one image's convolution matrix with D spatial dimensions, the
 // last one innermost (contiguous in memory).  Matrix row (ci, k_0 .. k_{D-1})
@@ -432,6 +433,80 @@ int device_ok()
     return GEMM_OK;
 }
 
+// ------------------------------------------- implicit GEMM: term tables --
+
+// Table of the implicit GEMM's per-k terms, one entry per k: for the forward
+// product k is a tap (ci, r, s) with y = r dh, x = s dw and the byte offset of
+// (ci, y, x) in the image; for the filter gradient k is an output position
+// (p, q) with y = p sh - ph, x = q sw - pw and the (possibly negative) byte
+// offset of (y, x).  Entry {y | x << 16, offset} (y and x as signed 16-bit).
+__global__ void __launch_bounds__(kThreads) conv_table_kernel(ConvGeom g, int fwd, int esize,
+                                                              int count, int2 *tab)
+{
+    const int k = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (k >= count) return;
+    int y, x, off;
+    if (fwd) {
+        const int ci = k / (g.r * g.s);
+        const int rem = k - ci * g.r * g.s;
+        const int r = rem / g.s, sx = rem - r * g.s;
+        y = r * g.dh;
+        x = sx * g.dw;
+        off = ((ci * g.h + y) * g.w + x) * esize;
+    } else {
+        const int p = k / g.q, q = k - p * g.q;
+        y = p * g.sh - g.ph;
+        x = q * g.sw - g.pw;
+        off = (y * g.w + x) * esize;
+    }
+    tab[k] = make_int2((int)(((unsigned)y & 0xffffu) | ((unsigned)x << 16)), off);
+}
+
+// The table's y and x fit in signed 16 bits.
+bool table_fits(const Dims &d, bool fwd)
+{
+    const int64_t lo = -32768, hi = 32767;
+    if (fwd)
+        return (d.kern[0] - 1) * d.dil[0] <= hi && (d.kern[1] - 1) * d.dil[1] <= hi;
+    return -d.pad[0] >= lo && -d.pad[1] >= lo && (d.out[0] - 1) * d.stride[0] - d.pad[0] <= hi &&
+           (d.out[1] - 1) * d.stride[1] - d.pad[1] <= hi;
+}
+
+// Addressing of one implicit call: the bsrc to launch with, after building
+// the table when it is used.  CONV_ADDR_DEFAULT takes the table form when the
+// geometry fits it.
+int implicit_source(const Dims &d, int esize, int addressing, bool fwd, ConvGeom *geom,
+                    hipStream_t stream, int *bsrc)
+{
+    const bool fits16 = table_fits(d, fwd);
+    bool table;
+    if (addressing == CONV_ADDR_ANALYTIC)
+        table = false;
+    else if (addressing == CONV_ADDR_TABLE)
+        table = true;
+    else if (addressing == CONV_ADDR_DEFAULT)
+        table = fits16 && kDefaultTable;
+    else
+        return GEMM_ERR_INVALID_ARG;
+    if (table && !fits16) return GEMM_ERR_INVALID_ARG;
+    geom->tab = nullptr;
+    if (!table) {
+        *bsrc = fwd ? B_CONV_FWD : B_CONV_WGRAD;
+        return GEMM_OK;
+    }
+    const int count = fwd ? geom->crs : geom->pq;
+    void *buf = nullptr;
+    const int rc = conv_table_buffer(stream, (size_t)count * sizeof(int2), &buf);
+    if (rc != GEMM_OK) return rc;
+    hipLaunchKernelGGL(conv_table_kernel, dim3((unsigned)((count + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, *geom, fwd ? 1 : 0, esize, count,
+                       static_cast<int2 *>(buf));
+    if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+    geom->tab = static_cast<const int2 *>(buf);
+    *bsrc = fwd ? B_CONV_FWD_TAB : B_CONV_WGRAD_TAB;
+    return GEMM_OK;
+}
+
 // ------------------------------------ routines shared by 2-D and N-D calls --
 
 int64_t workspace_bytes(int dtype, int rc, const Dims &d)
@@ -562,13 +637,14 @@ int conv2d_bwd_weight(int dtype, const conv2d_params *p, const void *x, const vo
                          : dg::bwd_weight(dtype, d, x, dy, dw, workspace, workspace_bytes, stream);
 }
 
-int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const void *x,
-                        const void *w, void *y, hipStream_t stream)
+int conv2d_fwd_implicit_ex(int dtype, int dtype_y, const conv2d_params *p, int addressing,
+                           const void *x, const void *w, void *y, hipStream_t stream)
 {
     dg::Dims d;
     if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
     int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_TABLE) return GEMM_ERR_INVALID_ARG;
     if (d.n == 0) return GEMM_OK;
     const int es = dg::elem_size(dtype), esy = dg::elem_size(dtype_y);
     if (x == nullptr || w == nullptr || y == nullptr || !dg::aligned_to(x, es) ||
@@ -576,13 +652,55 @@ int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const vo
         return GEMM_ERR_INVALID_ARG;
     dg::ConvGeom geom;
     if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
+    if (addressing == CONV_ADDR_TABLE && !dg::table_fits(d, true)) return GEMM_ERR_INVALID_ARG;
     if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    int bsrc = 0;
+    if ((rc = dg::implicit_source(d, es, addressing, true, &geom, stream, &bsrc)) != GEMM_OK)
+        return rc;
     const int64_t vo = d.vol_out();
     for (int64_t n = 0; n < d.n; ++n) {
         // y[n] (C_out x PQ) = w (C_out x C_in R S) . cols(x[n]), cols formed in the loader
         dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f,
                        w, d.crs(), static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1,
-                       static_cast<char *>(y) + n * d.k * vo * esy, vo, dg::B_CONV_FWD, &geom};
+                       static_cast<char *>(y) + n * d.k * vo * esy, vo, bsrc, &geom};
+        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    return GEMM_OK;
+}
+
+int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const void *x,
+                        const void *w, void *y, hipStream_t stream)
+{
+    return conv2d_fwd_implicit_ex(dtype, dtype_y, p, CONV_ADDR_DEFAULT, x, w, y, stream);
+}
+
+int conv2d_bwd_weight_implicit_ex(int dtype, const conv2d_params *p, int addressing,
+                                  const void *x, const void *dy, float *dw, hipStream_t stream)
+{
+    dg::Dims d;
+    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
+    int rc = dg::dims_2d(p, &d);
+    if (rc != GEMM_OK) return rc;
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_TABLE) return GEMM_ERR_INVALID_ARG;
+    const int es = dg::elem_size(dtype);
+    if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
+    if (d.n == 0) return dg::zero_dw(dtype, d, dw, stream);
+    if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
+        return GEMM_ERR_INVALID_ARG;
+    dg::ConvGeom geom;
+    if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
+    if (addressing == CONV_ADDR_TABLE && !dg::table_fits(d, false)) return GEMM_ERR_INVALID_ARG;
+    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    int bsrc = 0;
+    if ((rc = dg::implicit_source(d, es, addressing, false, &geom, stream, &bsrc)) != GEMM_OK)
+        return rc;
+    const int64_t vo = d.vol_out();
+    for (int64_t n = 0; n < d.n; ++n) {
+        // dw (C_out x C_in R S) (+)= dy[n] (C_out x PQ) . cols(x[n])^T
+        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
+                       n == 0 ? 0.0f : 1.0f, static_cast<const char *>(dy) + n * d.k * vo * es, vo,
+                       static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1, dw, d.crs(),
+                       bsrc, &geom};
         if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
     }
     return GEMM_OK;
@@ -591,28 +709,7 @@ int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const vo
 int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x, const void *dy,
                                float *dw, hipStream_t stream)
 {
-    dg::Dims d;
-    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::dims_2d(p, &d);
-    if (rc != GEMM_OK) return rc;
-    const int es = dg::elem_size(dtype);
-    if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
-    if (d.n == 0) return dg::zero_dw(dtype, d, dw, stream);
-    if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
-        return GEMM_ERR_INVALID_ARG;
-    dg::ConvGeom geom;
-    if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    const int64_t vo = d.vol_out();
-    for (int64_t n = 0; n < d.n; ++n) {
-        // dw (C_out x C_in R S) (+)= dy[n] (C_out x PQ) . cols(x[n])^T
-        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
-                       n == 0 ? 0.0f : 1.0f, static_cast<const char *>(dy) + n * d.k * vo * es, vo,
-                       static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1, dw, d.crs(),
-                       dg::B_CONV_WGRAD, &geom};
-        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
-    }
-    return GEMM_OK;
+    return conv2d_bwd_weight_implicit_ex(dtype, p, CONV_ADDR_DEFAULT, x, dy, dw, stream);
 }
 
 // ------------------------------------------------------------------- N-D --

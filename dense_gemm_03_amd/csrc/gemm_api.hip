@@ -5,6 +5,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "gemm.h"
@@ -175,14 +176,15 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
     *splits = (int)ceil_div(K, kps);                 // every slice non-empty
 }
 
-// Split-K partial sums live in a library-owned buffer per (device, stream), so
-// that calls on different streams never share one.
+// Library-owned device buffers, one per (device, stream, slot), so that calls
+// on different streams never share one: slot 0 holds split-K partial sums,
+// slot 1 the convolution tables of the implicit GEMM.  A buffer only grows.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::map<std::tuple<int, hipStream_t, int>, Workspace> g_ws;
 
 struct WorkspaceReleaser {
     ~WorkspaceReleaser()
@@ -193,10 +195,10 @@ struct WorkspaceReleaser {
     }
 } g_ws_releaser;
 
-int get_workspace(int device, hipStream_t stream, size_t bytes, float **out)
+int get_buffer(int slot, int device, hipStream_t stream, size_t bytes, void **out)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &w = g_ws[std::make_pair(device, stream)];
+    Workspace &w = g_ws[std::make_tuple(device, stream, slot)];
     if (w.bytes < bytes) {
         if (w.ptr) {
             // hipFree waits for the device, so earlier work using it is done.
@@ -212,8 +214,16 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, float **out)
         w.ptr = p;
         w.bytes = bytes;
     }
-    *out = static_cast<float *>(w.ptr);
+    *out = w.ptr;
     return GEMM_OK;
+}
+
+int get_workspace(int device, hipStream_t stream, size_t bytes, float **out)
+{
+    void *p = nullptr;
+    const int rc = get_buffer(0, device, stream, bytes, &p);
+    *out = static_cast<float *>(p);
+    return rc;
 }
 
 int elem_size(int dtype) { return dtype == GEMM_DTYPE_F32 ? 4 : 2; }
@@ -235,8 +245,10 @@ int check_args(const Call &c)
     const int64_t a_row = c.transa == GEMM_OP_T ? c.M : c.K;
     const int64_t b_row = c.transb == GEMM_OP_T ? c.K : c.N;
     const bool implicit = c.bsrc != B_MATRIX;
-    if (implicit && (c.conv == nullptr || c.transa != GEMM_OP_N ||
-                     c.transb != (c.bsrc == B_CONV_FWD ? GEMM_OP_N : GEMM_OP_T)))
+    if (implicit && (c.bsrc < B_CONV_FWD || c.bsrc > B_CONV_WGRAD_TAB || c.conv == nullptr ||
+                     c.transa != GEMM_OP_N ||
+                     c.transb != (conv_fwd_source(c.bsrc) ? GEMM_OP_N : GEMM_OP_T) ||
+                     (conv_table_source(c.bsrc) && c.conv->tab == nullptr)))
         return GEMM_ERR_INVALID_ARG;
     if (c.lda < (a_row > 0 ? a_row : 1) || (!implicit && c.ldb < (b_row > 0 ? b_row : 1)) ||
         c.ldc < (c.N > 0 ? c.N : 1))
@@ -260,7 +272,7 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     if (tab == nullptr) return GEMM_ERR_INVALID_ARG;
     if (forced_cfg >= count) return GEMM_ERR_INVALID_ARG;
     const int layout = call.transa * 2 + call.transb;
-    const int impl = call.bsrc == B_CONV_FWD ? 0 : 1;  // implicit slot, for bsrc != B_MATRIX
+    const int impl = call.bsrc - B_CONV_FWD;  // implicit slot, for bsrc != B_MATRIX
     auto kernel_of = [&](const TileConfig &t, bool aligned) -> launch_fn {
         return call.bsrc == B_MATRIX ? t.fn[layout][aligned ? 0 : 1]
                                      : t.implicit[impl][aligned ? 0 : 1];
@@ -357,6 +369,16 @@ Call plain_call(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64
 int gemm_run(const GemmCall &call, int forced_cfg, int forced_split, hipStream_t stream)
 {
     return run_call(call, forced_cfg, forced_split, stream);
+}
+
+int conv_table_buffer(hipStream_t stream, size_t bytes, void **out)
+{
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_NO_DEVICE;
+    }
+    return get_buffer(1, device, stream, bytes, out);
 }
 
 }  // namespace dg

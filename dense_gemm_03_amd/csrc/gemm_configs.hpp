@@ -36,9 +36,10 @@ struct TileConfig {
     // the entry has no kernel for that layout.
     launch_fn fn[4][2];
     // implicit-GEMM convolution kernels (B tiles formed from an image):
-    // implicit[0] forward (B = cols), implicit[1] filter gradient (B = cols^T);
-    // [aligned], as fn.  nullptr where the entry has none.
-    launch_fn implicit[2][2];
+    // implicit[0] forward (B = cols), implicit[1] filter gradient (B = cols^T),
+    // implicit[2] / [3] the same with table-looked-up per-k terms; [aligned],
+    // as fn.  nullptr where the entry has none.
+    launch_fn implicit[4][2];
 };
 
 // Declared here; defined in gemm_launch.hpp and explicitly instantiated by the
@@ -57,6 +58,12 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_LB_CW ::dg::KMAJOR
 #define DG_BSRC_CF ::dg::B_CONV_FWD
 #define DG_BSRC_CW ::dg::B_CONV_WGRAD
+#define DG_LA_CFT ::dg::KMAJOR
+#define DG_LB_CFT ::dg::MNMAJOR
+#define DG_LA_CWT ::dg::KMAJOR
+#define DG_LB_CWT ::dg::KMAJOR
+#define DG_BSRC_CFT ::dg::B_CONV_FWD_TAB
+#define DG_BSRC_CWT ::dg::B_CONV_WGRAD_TAB
 
 // Memory orientation of op(A) / op(B) per layout combination: A as given is
 // k-contiguous, A^T (stored K x M) outer-contiguous; B as given is
@@ -148,11 +155,13 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_FNS_NN_TT(...) DG_NOFNS
 
 #define DG_IMPL_CONV(BF16, BM, BN, BK, WM, WN)                                                \
-    {DG_IFNS(BF16, BM, BN, BK, WM, WN, CF), DG_IFNS(BF16, BM, BN, BK, WM, WN, CW)}
-#define DG_IMPL_ALL(...) {DG_NOFNS, DG_NOFNS}
-#define DG_IMPL_NN(...) {DG_NOFNS, DG_NOFNS}
-#define DG_IMPL_SKINNY(...) {DG_NOFNS, DG_NOFNS}
-#define DG_IMPL_KK(...) {DG_NOFNS, DG_NOFNS}
+    {DG_IFNS(BF16, BM, BN, BK, WM, WN, CF), DG_IFNS(BF16, BM, BN, BK, WM, WN, CW),              \
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFT), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWT)}
+#define DG_IMPL_NONE {DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS}
+#define DG_IMPL_ALL(...) DG_IMPL_NONE
+#define DG_IMPL_NN(...) DG_IMPL_NONE
+#define DG_IMPL_SKINNY(...) DG_IMPL_NONE
+#define DG_IMPL_KK(...) DG_IMPL_NONE
 
 // One table entry from one list item.
 #define DG_TABLE_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                        \

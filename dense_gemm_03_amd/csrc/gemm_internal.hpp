@@ -34,4 +34,10 @@ struct GemmCall {
 // Returns a gemm_status.
 int gemm_run(const GemmCall &call, int forced_cfg, int forced_split, hipStream_t stream);
 
+// A library-owned device buffer of at least `bytes` for the convolution
+// tables of calls on `stream` (current device); it lives until the library is
+// unloaded and is reused by the next call on that stream, so the work that
+// reads it must be enqueued on `stream`.  Returns a gemm_status.
+int conv_table_buffer(hipStream_t stream, size_t bytes, void **out);
+
 }  // namespace dg

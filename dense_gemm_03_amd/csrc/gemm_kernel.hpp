@@ -69,7 +69,14 @@ enum BSource {
     B_CONV_FWD = 1,    // op(B) = cols (C_in R S x P Q): B points at the image
     B_CONV_WGRAD = 2,  // op(B) = cols^T (P Q x C_in R S), read as the k-contiguous
                        // B^T tile (rows C_in R S, columns P Q)
+    // The same two sources with the per-k terms looked up in a table made
+    // before the launch (ConvGeom::tab) instead of computed in the loader.
+    B_CONV_FWD_TAB = 3,
+    B_CONV_WGRAD_TAB = 4,
 };
+
+__host__ __device__ constexpr bool conv_fwd_source(int b) { return b == B_CONV_FWD || b == B_CONV_FWD_TAB; }
+__host__ __device__ constexpr bool conv_table_source(int b) { return b == B_CONV_FWD_TAB || b == B_CONV_WGRAD_TAB; }
 
 // Geometry of the convolution behind an implicit op(B), for one image
 // [C_in][H][W]: matrix row (ci R + r) S + s, column p Q + q holds
@@ -79,6 +86,10 @@ struct ConvGeom {
     uint64_t q_magic, rs_magic, s_magic;  // j / Q, k / (R S), k / S (exact below 2^31)
     int q_shift, rs_shift, s_shift;
     int img_bytes;                        // C_in H W element bytes (< 2^31)
+    // Table sources only: the terms that change along K, one entry per k --
+    // per tap (ci, r, s) for the forward product, per output position (p, q)
+    // for the filter gradient: {y | x << 16 (signed 16-bit each), byte offset}.
+    const int2 *tab;
 };
 
 // Arguments of one launch.  The grid is 1-D: splits * tiles_m * tiles_n blocks.
@@ -685,7 +696,10 @@ __device__ __forceinline__ int div_magic(int j, uint64_t m, int shift)
 // X's: large convolutions in PyTorch for model training", section "CUTLASS":
 // the implicit GEMM builds the matrix tiles inside the blocks, from output
 // coordinates (p, q) and filter taps (ci, r, s), instead of materialising the
-// matrix).  Addresses are computed on the fly (the page's analytic iterator).
+// matrix).  The terms that change along K are computed on the fly (the page's
+// analytic iterator) or, for the table sources, looked up in a table made once
+// per call (its optimized iterator, which precomputes offsets into lookup
+// tables).
 //
 // Every matrix element is image[ci][y][x] with y = (p sh - ph) + r dh and
 // x = (q sw - pw) + s dw: a column term (from p, q) plus a row term (from
@@ -701,9 +715,10 @@ struct ConvGather {
     using T = typename G::TB;
     using In = typename G::In;
     static constexpr int U = T::PER_THREAD, V = T::VEC, RSTEP = T::NT / T::CPR;
+    static constexpr bool FWD = conv_fwd_source(MODE);
+    static constexpr bool TAB = conv_table_source(MODE);
     static_assert(T::NT % T::CPR == 0, "a thread's chunks must share their columns");
-    static_assert((MODE == B_CONV_FWD && T::LAYOUT == MNMAJOR) ||
-                      (MODE == B_CONV_WGRAD && T::LAYOUT == KMAJOR),
+    static_assert((FWD && T::LAYOUT == MNMAJOR) || (!FWD && T::LAYOUT == KMAJOR),
                   "tile orientation of the convolution source");
 
     __amdgpu_buffer_rsrc_t rsrc;
@@ -713,9 +728,13 @@ struct ConvGather {
     // as (y, x, byte offset) plus whether that column / row lies inside the
     // matrix.  The byte offset of an element is the sum of its column and row
     // offsets; (y, x) only decide whether it lies in the image.
-    static constexpr int NF = MODE == B_CONV_FWD ? V : U;
+    static constexpr int NF = FWD ? V : U;
     int fy[NF], fx[NF], fo[NF];
     bool fok[NF];
+    // Table sources: the per-k entries of the next k-tile, loaded one tile
+    // ahead so that their latency hides behind the current tile's gathers.
+    static constexpr int NK = FWD ? U : V;   // k values per thread and tile
+    int2 nxt[TAB ? NK : 1];
 
     // Terms of tap k = (ci R + r) S + s: y = r dh, x = s dw, offset of
     // (ci, r dh, s dw) in the image.
@@ -739,14 +758,41 @@ struct ConvGather {
         tx = q * g->sw - g->pw;
         to = (ty * g->w + tx) * (int)sizeof(In);
     }
+    // Per-k terms of k (clamped into the matrix by the caller).
+    __device__ __forceinline__ void k_terms(int k, int &ty, int &tx, int &to) const
+    {
+        if constexpr (FWD)
+            tap_terms(k, ty, tx, to);
+        else
+            out_terms(k, ty, tx, to);
+    }
+    static __device__ __forceinline__ void unpack(int2 e, int &ty, int &tx, int &to)
+    {
+        ty = (e.x << 16) >> 16;
+        tx = e.x >> 16;
+        to = e.y;
+    }
+    // k of this thread's i-th per-k slot in the k-tile at k0.
+    __device__ __forceinline__ int k_of(int k0, int i) const
+    {
+        return FWD ? k0 + row0 + i * RSTEP : k0 + e0 + i;
+    }
+    __device__ __forceinline__ void prefetch(int k0, int kend)
+    {
+        if constexpr (TAB) {
+#pragma unroll
+            for (int i = 0; i < NK; ++i) nxt[i] = g->tab[min(k_of(k0, i), kend - 1)];
+        }
+    }
 
-    __device__ __forceinline__ ConvGather(const KernelArgs &a, int bn, int tid) : g(&a.conv)
+    __device__ __forceinline__ ConvGather(const KernelArgs &a, int bn, int tid, int kbeg, int kend)
+        : g(&a.conv)
     {
         rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.B), 0, a.conv.img_bytes,
                                                  0x00020000);  // gfx9 raw-buffer format word
         row0 = tid / T::CPR;
         e0 = (tid % T::CPR) * V;
-        if constexpr (MODE == B_CONV_FWD) {
+        if constexpr (FWD) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const int n = bn + e0 + e;
@@ -761,6 +807,7 @@ struct ConvGather {
                 tap_terms(min(n, a.N - 1), fy[u], fx[u], fo[u]);
             }
         }
+        prefetch(kbeg, kend);
     }
 
     // The element at image position (y, x) and byte offset off, or zero when
@@ -776,41 +823,42 @@ struct ConvGather {
             return (In)__builtin_amdgcn_raw_buffer_load_b16(rsrc, vo, 0, 0);
     }
 
-    // The B tile of the k-tile at k0 (k below kend), chunk u of this thread in r[u].
-    __device__ __forceinline__ void load(int k0, int kend, u32x4 (&r)[U]) const
+    // The B tile of the k-tile at k0 (k below kend), chunk u of this thread in
+    // r[u].  Called for consecutive k-tiles, starting at the constructor's kbeg.
+    __device__ __forceinline__ void load(int k0, int kend, u32x4 (&r)[U])
     {
         union Chunk {
             u32x4 v;
             In e[V];
         };
-        if constexpr (MODE == B_CONV_FWD) {
+        int ky[NK], kx[NK], ko[NK];
+        bool kok[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int k = k_of(k0, i);
+            kok[i] = k < kend;
+            if constexpr (TAB)
+                unpack(nxt[i], ky[i], kx[i], ko[i]);
+            else
+                k_terms(min(k, kend - 1), ky[i], kx[i], ko[i]);
+        }
+        prefetch(k0 + G::BK, kend);
+        if constexpr (FWD) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = k0 + row0 + u * RSTEP;
-                int ty, tx, to;
-                tap_terms(min(k, kend - 1), ty, tx, to);
-                const bool kok = k < kend;
                 Chunk c;
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    c.e[e] = fetch(kok & fok[e], fy[e] + ty, fx[e] + tx, fo[e] + to);
+                    c.e[e] = fetch(kok[u] & fok[e], fy[e] + ky[u], fx[e] + kx[u], fo[e] + ko[u]);
                 r[u] = c.v;
             }
         } else {
-            int cy[V], cx[V], co[V];
-            bool cok[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const int k = k0 + e0 + e;
-                cok[e] = k < kend;
-                out_terms(min(k, kend - 1), cy[e], cx[e], co[e]);
-            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 Chunk c;
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    c.e[e] = fetch(fok[u] & cok[e], fy[u] + cy[e], fx[u] + cx[e], fo[u] + co[e]);
+                    c.e[e] = fetch(fok[u] & kok[e], fy[u] + ky[e], fx[u] + kx[e], fo[u] + ko[e]);
                 r[u] = c.v;
             }
         }
@@ -895,7 +943,7 @@ gemm_kernel(KernelArgs p)
                              [&](int k0, StageRegs<G> &r) { global_load_masked<ALIGNED>(c, k0, r); });
     } else {
         // implicit GEMM: A from memory, B tiles formed from the image
-        const ConvGather<G, BSRC> gather(p, c.bn, c.tid);
+        ConvGather<G, BSRC> gather(p, c.bn, c.tid, kbeg, c.kend);
         main_loop_masked(lds0, lds1, c, kbeg, ntiles, acc, [&](int k0, StageRegs<G> &r) {
             load_tile_masked<ALIGNED, typename G::TA>(c.A, c.lda, c.bm, c.M, k0, c.kend, c.tid, r.a);
             gather.load(k0, c.kend, r.b);

@@ -1,7 +1,8 @@
 // Definition of the kernel launcher and the explicit instantiation of one
 // operand layout's kernels from the tile lists.  Included by the per-layout
 // source files, each of which defines DG_DTYPE_TABLE (the list), DG_LAYOUT
-// (NN, NT, TN, TT, or CF / CW for the implicit-GEMM convolution kernels) and
+// (NN, NT, TN, TT, or CF / CW / CFT / CWT for the implicit-GEMM convolution
+// kernels: forward / filter gradient, analytic / table-looked-up terms) and
 // then includes this header.
 #pragma once
 
@@ -42,30 +43,40 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_ALL_TT(...) DG_INST(__VA_ARGS__, TT)
 #define DG_INST_ALL_CF(...)
 #define DG_INST_ALL_CW(...)
+#define DG_INST_ALL_CFT(...)
+#define DG_INST_ALL_CWT(...)
 #define DG_INST_CONV_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_CONV_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_CONV_TN(...) DG_INST(__VA_ARGS__, TN)
 #define DG_INST_CONV_TT(...) DG_INST(__VA_ARGS__, TT)
 #define DG_INST_CONV_CF(...) DG_IINST(__VA_ARGS__, CF)
 #define DG_INST_CONV_CW(...) DG_IINST(__VA_ARGS__, CW)
+#define DG_INST_CONV_CFT(...) DG_IINST(__VA_ARGS__, CFT)
+#define DG_INST_CONV_CWT(...) DG_IINST(__VA_ARGS__, CWT)
 #define DG_INST_SKINNY_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_SKINNY_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_SKINNY_TN(...)
 #define DG_INST_SKINNY_TT(...)
 #define DG_INST_SKINNY_CF(...)
 #define DG_INST_SKINNY_CW(...)
+#define DG_INST_SKINNY_CFT(...)
+#define DG_INST_SKINNY_CWT(...)
 #define DG_INST_KK_NN(...)
 #define DG_INST_KK_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_KK_TN(...)
 #define DG_INST_KK_TT(...)
 #define DG_INST_KK_CF(...)
 #define DG_INST_KK_CW(...)
+#define DG_INST_KK_CFT(...)
+#define DG_INST_KK_CWT(...)
 #define DG_INST_NN_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_NN_NT(...)
 #define DG_INST_NN_TN(...)
 #define DG_INST_NN_TT(...)
 #define DG_INST_NN_CF(...)
 #define DG_INST_NN_CW(...)
+#define DG_INST_NN_CFT(...)
+#define DG_INST_NN_CWT(...)
 #define DG_INST_SEL2(LAYOUTS, L) DG_INST_##LAYOUTS##_##L
 #define DG_INST_SEL(LAYOUTS, L) DG_INST_SEL2(LAYOUTS, L)
 #define DG_INST_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                            \

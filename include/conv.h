@@ -112,6 +112,32 @@ int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x,
                                float *dw, hipStream_t stream);
 
 /*
+ * Address generation of the implicit-GEMM loader ("Three X's", section
+ * "CUTLASS", which names two iterator kinds: one computes every index and
+ * offset on the fly, the other computes them beforehand and reads lookup
+ * tables).  Each matrix element's image address is a fixed term per thread
+ * plus a term that changes with k (per tap for the forward product, per
+ * output position for the filter gradient):
+ *   CONV_ADDR_ANALYTIC: the k terms are computed in the loader from k
+ *     (integer division by multiply-and-shift);
+ *   CONV_ADDR_TABLE: a small kernel first writes one 8-byte entry per k into
+ *     a library-owned buffer (one per device and stream, kept for later
+ *     calls), and the loader reads its k terms from it, one k-tile ahead.
+ *     Needs the y and x terms within signed 16 bits: (R-1) dh and (S-1) dw
+ *     for the forward product, ph, pw and the last output's p sh - ph,
+ *     q sw - pw for the filter gradient (GEMM_ERR_INVALID_ARG otherwise);
+ *   CONV_ADDR_DEFAULT: the library's choice (what conv2d_fwd_implicit and
+ *     conv2d_bwd_weight_implicit use).
+ * Both give identical results (same products, same summation order).
+ */
+typedef enum { CONV_ADDR_DEFAULT = 0, CONV_ADDR_ANALYTIC = 1, CONV_ADDR_TABLE = 2 } conv_addressing;
+
+int conv2d_fwd_implicit_ex(int dtype, int dtype_y, const conv2d_params *p, int addressing,
+                           const void *x, const void *w, void *y, hipStream_t stream);
+int conv2d_bwd_weight_implicit_ex(int dtype, const conv2d_params *p, int addressing,
+                                  const void *x, const void *dy, float *dw, hipStream_t stream);
+
+/*
  * Convolution with D = 1 to 4 spatial dimensions ("Three X's", opening and
  * section "CuBLAS": the page's subject is convolution beyond two dimensions;
  * the convolution matrix gains one index per dimension in its row and column

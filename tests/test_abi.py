@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 26, names
+    assert len(names) == 28, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -266,6 +266,18 @@ def test_conv_host_logic_and_invalid_arguments():
     assert dg.conv2d_output_size(huge)[0] == dg.GEMM_OK
     assert dg.conv2d_fwd_implicit(F32, F32, huge, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.conv2d_bwd_weight_implicit(BF16, huge, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    # address generation: unknown forms are rejected; the table form needs its
+    # y and x terms within signed 16 bits
+    A, T = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, 3, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, -1, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_bwd_weight_implicit_ex(F32, ok, 7, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    wide = P(1, 1, 40001, 8, 1, 3, 1, (0, 0), (1, 1), (20000, 1))   # (R-1) dh = 40000
+    assert dg.conv2d_output_size(wide)[0] == dg.GEMM_OK
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, wide, T, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    tall = P(1, 1, 70000, 4, 1, 1, 1)                              # last p sh - ph = 69999
+    assert dg.conv2d_bwd_weight_implicit_ex(F32, tall, T, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, bad[0], A, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     # an empty batch: nothing to compute for the forward
     assert dg.conv2d_fwd(F32, F32, P(0, 3, 10, 9, 4, 3, 2), None, None, None, None, 0) == dg.GEMM_OK
 

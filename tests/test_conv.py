@@ -11,6 +11,9 @@ direct-convolution oracle, through the C ABI (include/conv.h).
 * Random tensors: |y - y_ref| <= tol * S with S the sum of |products|
   (1e-5 for fp32, 4e-3 for bf16 inputs), plus half a bf16 unit for bf16 y.
 * The full-size large-kernel convolution at sampled outputs and taps.
+* Each check runs through im2col + GEMM and through the implicit GEMM with
+  both address generations (terms computed in the loader, or looked up in a
+  table); the two implicit forms give identical bits.
 """
 from __future__ import annotations
 
@@ -27,6 +30,9 @@ from tests.gpu_util import DIAGNOSTIC, TOL, log, to_device
 pytestmark = pytest.mark.gpu
 
 F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
+# im2col + GEMM, and the implicit GEMM with either address generation
+ROUTES = [False, "analytic", "table"]
+ROUTE_IDS = ["im2col", "analytic", "table"]
 
 SHAPES = [
     # batch, cin, h, w, cout, r, s, ph, pw, sh, sw, dh, dw
@@ -135,7 +141,7 @@ def test_im2col_bit_exact(bf16):
             assert np.array_equal(got, want), "%s image %d" % (c, n)
 
 
-@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_fwd_exact_integers(bf16, implicit):
     for t, c in enumerate(SHAPES):
@@ -150,7 +156,7 @@ def test_fwd_exact_integers(bf16, implicit):
                 assert np.array_equal(got, ref), str(c)
 
 
-@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_bwd_weight_exact_integers(bf16, implicit):
     for t, c in enumerate(SHAPES):
@@ -160,7 +166,7 @@ def test_bwd_weight_exact_integers(bf16, implicit):
         assert np.array_equal(run_bwd(x, dy, c, implicit), ref), str(c)
 
 
-@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_random_within_tolerance(bf16, implicit):
     tol = TOL["bf16" if bf16 else "f32"]
@@ -174,7 +180,7 @@ def test_random_within_tolerance(bf16, implicit):
         check_close(run_bwd(x, dy, c, implicit), ref, S, tol, "filter gradient %s" % (c,))
 
 
-@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 def test_empty_batch_and_workload_small_batch(implicit):
     """batch 0: forward does nothing, the filter gradient is the empty sum
     (zeros); and the small batched workload against the oracle."""
@@ -198,7 +204,7 @@ def test_empty_batch_and_workload_small_batch(implicit):
     check_close(run_bwd(x, dy, c, implicit), ref, S, TOL["f32"], wk.name + " filter gradient")
 
 
-@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 def test_deterministic_repeats(implicit):
     import torch
     c = ConvShape(2, 8, 30, 30, 16, 5, 5, 2, 2)
@@ -217,7 +223,7 @@ def _shape_of(wk):
                      wk.stride, wk.dilation, wk.dilation)
 
 
-@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 @pytest.mark.parametrize("name", ["conv-64c-31k", "conv-64c-31k-bf16"])
 def test_full_size_sampled(name, implicit):
     """The large-kernel convolution at full size: forward outputs and filter-
@@ -252,7 +258,7 @@ def test_full_size_sampled(name, implicit):
         assert np.array_equal(got[t], sub.view(np.uint16) if bf16 else sub.view(np.uint32)), row
 
 
-@pytest.mark.parametrize("implicit", [False, True], ids=["im2col", "implicit"])
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 def test_full_size_exact_integers_sampled(implicit):
     """Integer tensors of the full-size shape: sampled outputs and taps exact."""
     wk = wl.CONV_WORKLOADS["conv-64c-31k"]
@@ -267,3 +273,21 @@ def test_full_size_exact_integers_sampled(implicit):
     tidx = [rng.integers(0, d, 256) for d in c.w_shape]
     ref, _ = oc.conv2d_bwd_weight_entries(x, dy, c, *tidx)
     assert np.array_equal(dw[tuple(tidx)], ref)
+
+
+def test_implicit_addressing_forms_agree_bitwise():
+    """Analytic and table address generation feed the same products in the
+    same order: identical bits, forward and filter gradient, both types."""
+    import torch
+    for t, c in enumerate(SHAPES[1:], 1):
+        for bf16 in (False, True):
+            x, w = _dev(_randn(c.x_shape, 900 + t, bf16)), _dev(_randn(c.w_shape, 910 + t, bf16))
+            dy = _dev(_randn(c.y_shape, 920 + t, bf16))
+            kw = dict(stride=(c.sh, c.sw), padding=(c.ph, c.pw), dilation=(c.dh, c.dw))
+            ya = dg.conv2d(x, w, implicit="analytic", **kw)
+            yt = dg.conv2d(x, w, implicit="table", **kw)
+            ga = dg.conv2d_weight_grad(x, dy, c.w_shape, implicit="analytic", **kw)
+            gt = dg.conv2d_weight_grad(x, dy, c.w_shape, implicit="table", **kw)
+            torch.cuda.synchronize()
+            log("addressing forms %s %s" % (c, "bf16" if bf16 else "f32"))
+            assert torch.equal(ya, yt) and torch.equal(ga, gt), str(c)
