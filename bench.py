@@ -117,8 +117,9 @@ def measure(name: str, steps: int, warmup: int):
                         device="cuda:0")
     stream = torch.cuda.current_stream()
     dtype_id = dg.GEMM_DTYPE_F32 if w.dtype == "f32" else dg.GEMM_DTYPE_BF16
-    cfg = dg.gemm_select_config(dtype_id, w.M, w.N, w.K)
-    splits = dg.gemm_split_k(dtype_id, cfg, w.M, w.N, w.K)
+    ta, tb = int(w.transa), int(w.transb)
+    cfg = dg.gemm_select_config_ex(dtype_id, ta, tb, w.M, w.N, w.K)
+    splits = dg.gemm_split_k_ex(dtype_id, cfg, ta, tb, w.M, w.N, w.K)
 
     def step():
         # with beta != 0 every step accumulates into C again: same work, the
