@@ -735,6 +735,10 @@ struct ConvGather {
     // ahead so that their latency hides behind the current tile's gathers.
     static constexpr int NK = FWD ? U : V;   // k values per thread and tile
     int2 nxt[TAB ? NK : 1];
+    // Forward: whether this thread's V columns are V consecutive output
+    // positions of one output row with unit horizontal stride, so that for
+    // every tap they read V consecutive image elements.
+    bool run = false;
 
     // Terms of tap k = (ci R + r) S + s: y = r dh, x = s dw, offset of
     // (ci, r dh, s dw) in the image.
@@ -808,6 +812,8 @@ struct ConvGather {
             }
         }
         prefetch(kbeg, kend);
+        if constexpr (FWD)
+            run = fok[V - 1] & (fy[0] == fy[V - 1]) & (fx[V - 1] == fx[0] + (V - 1));
     }
 
     // The element at image position (y, x) and byte offset off, or zero when
@@ -821,6 +827,14 @@ struct ConvGather {
             return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, 0, 0));
         else
             return (In)__builtin_amdgcn_raw_buffer_load_b16(rsrc, vo, 0, 0);
+    }
+
+    // 16 bytes of the image at byte offset off (inside the image; element
+    // aligned, not necessarily 16-byte aligned).
+    __device__ __forceinline__ u32x4 load_run(int off) const
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+        return u32x4{v[0], v[1], v[2], v[3]};
     }
 
     // The B tile of the k-tile at k0 (k below kend), chunk u of this thread in
@@ -843,23 +857,40 @@ struct ConvGather {
                 k_terms(min(k, kend - 1), ky[i], kx[i], ko[i]);
         }
         prefetch(k0 + G::BK, kend);
+        // A chunk whose V elements are V consecutive image elements of one
+        // image row, all inside the image, is one 16-byte load; any other
+        // chunk (crossing the padding, an output-row end, or with a stride)
+        // is gathered element by element.
         if constexpr (FWD) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                Chunk c;
+                const bool whole = run & kok[u] & ((unsigned)(fy[0] + ky[u]) < (unsigned)g->h) &
+                                   (fx[0] + kx[u] >= 0) & (fx[V - 1] + kx[u] < g->w);
+                if (whole) {
+                    r[u] = load_run(fo[0] + ko[u]);
+                } else {
+                    Chunk c;
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    c.e[e] = fetch(kok[u] & fok[e], fy[e] + ky[u], fx[e] + kx[u], fo[e] + ko[u]);
-                r[u] = c.v;
+                    for (int e = 0; e < V; ++e)
+                        c.e[e] = fetch(kok[u] & fok[e], fy[e] + ky[u], fx[e] + kx[u], fo[e] + ko[u]);
+                    r[u] = c.v;
+                }
             }
         } else {
+            const bool krun = kok[V - 1] & (ky[0] == ky[V - 1]) & (kx[V - 1] == kx[0] + (V - 1));
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                Chunk c;
+                const bool whole = krun & fok[u] & ((unsigned)(fy[u] + ky[0]) < (unsigned)g->h) &
+                                   (fx[u] + kx[0] >= 0) & (fx[u] + kx[V - 1] < g->w);
+                if (whole) {
+                    r[u] = load_run(fo[u] + ko[0]);
+                } else {
+                    Chunk c;
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    c.e[e] = fetch(fok[u] & kok[e], fy[u] + ky[e], fx[u] + kx[e], fo[u] + ko[e]);
-                r[u] = c.v;
+                    for (int e = 0; e < V; ++e)
+                        c.e[e] = fetch(fok[u] & kok[e], fy[u] + ky[e], fx[u] + kx[e], fo[u] + ko[e]);
+                    r[u] = c.v;
+                }
             }
         }
     }
