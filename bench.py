@@ -22,7 +22,8 @@ in HBM.  Prints ONE JSON line:
                           filter gradient, their implicit-GEMM forms with
                           analytic and table address generation, and the
                           im2col kernel against HBM), and of the 3-D (7x7x7
-                          filters, fp32 and bf16) and 4-D workloads
+                          filters, fp32 and bf16; also through the implicit
+                          GEMM) and 4-D workloads
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -256,6 +257,15 @@ def measure_conv(name: str, steps: int, warmup: int):
     res = {}
     peak = PEAK_TFLOPS[c.dtype]
     routes = [("fwd", fwd), ("wgrad", wgrad)]
+    if nd and c.nd <= 3:
+        def fwd_nd_implicit():
+            assert dg.convnd_fwd_implicit(dtype, F32, params, x.data_ptr(), w.data_ptr(),
+                                          y.data_ptr(), sp) == dg.GEMM_OK
+
+        def wgrad_nd_implicit():
+            assert dg.convnd_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(),
+                                                 dw.data_ptr(), sp) == dg.GEMM_OK
+        routes += [("fwd_implicit", fwd_nd_implicit), ("wgrad_implicit", wgrad_nd_implicit)]
     if not nd:
         A, T = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE
         routes += [("fwd_implicit", implicit_fwd(A)), ("wgrad_implicit", implicit_wgrad(A)),

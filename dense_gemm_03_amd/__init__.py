@@ -92,6 +92,8 @@ SIGNATURES.update({
     "convnd_im2col": (_int, [_int, _pnd, _i64, _p, _p, _i64, _p]),
     "convnd_fwd": (_int, [_int, _int, _pnd, _p, _p, _p, _p, _i64, _p]),
     "convnd_bwd_weight": (_int, [_int, _pnd, _p, _p, _p, _p, _i64, _p]),
+    "convnd_fwd_implicit": (_int, [_int, _int, _pnd, _p, _p, _p, _p]),
+    "convnd_bwd_weight_implicit": (_int, [_int, _pnd, _p, _p, _p, _p]),
 })
 
 _lib = None
@@ -354,6 +356,14 @@ def convnd_bwd_weight(dtype, params, x, dy, dw, workspace, workspace_bytes, stre
                                             workspace_bytes, stream)
 
 
+def convnd_fwd_implicit(dtype, dtype_y, params, x, w, y, stream=None) -> int:
+    return load_library().convnd_fwd_implicit(dtype, dtype_y, ctypes.byref(params), x, w, y, stream)
+
+
+def convnd_bwd_weight_implicit(dtype, params, x, dy, dw, stream=None) -> int:
+    return load_library().convnd_bwd_weight_implicit(dtype, ctypes.byref(params), x, dy, dw, stream)
+
+
 def _pair(v):
     return (v, v) if isinstance(v, int) else tuple(v)
 
@@ -469,11 +479,13 @@ def _convnd_setup(x, weight_shape, stride, padding, dilation):
     return params, dtype, out, convnd_workspace_size(dtype, params)
 
 
-def conv_nd(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None):
+def conv_nd(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None,
+            implicit=False):
     """y = convolution of x (N, C_in, S_0 .. S_{D-1}) with w (C_out, C_in,
     K_0 .. K_{D-1}), D = 1 to 4 (cross-correlation form, as torch's conv1d /
-    conv2d / conv3d), through the im2col + GEMM path.  x and w are both
-    float32 or both bfloat16; y is float32 (default) or bfloat16."""
+    conv2d / conv3d), through the im2col + GEMM path, or with ``implicit``
+    (D <= 3) the implicit GEMM.  x and w are both float32 or both bfloat16; y
+    is float32 (default) or bfloat16."""
     import torch
     if w.dtype != x.dtype or not w.is_contiguous():
         raise TypeError("w must be a contiguous tensor of x's dtype")
@@ -483,18 +495,23 @@ def conv_nd(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=Non
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     dtype_y = GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32
-    ws = _workspace(workspace, need, x.device)
-    rc = convnd_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
-                    ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if implicit:
+        rc = convnd_fwd_implicit(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                                 stream)
+    else:
+        ws = _workspace(workspace, need, x.device)
+        rc = convnd_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                        ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return y
 
 
 def conv_nd_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, workspace=None,
-                        stream=None):
+                        stream=None, implicit=False):
     """dw (float32, weight_shape) = the filter gradient of conv_nd for input x
-    and output gradient dy, through the im2col + GEMM path."""
+    and output gradient dy, through the im2col + GEMM path (or, with
+    ``implicit`` and D <= 3, the implicit GEMM)."""
     import torch
     params, dtype, out, need = _convnd_setup(x, tuple(weight_shape), stride, padding, dilation)
     if dy.dtype != x.dtype or not dy.is_contiguous() or \
@@ -503,9 +520,13 @@ def conv_nd_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wo
     dw = torch.empty(tuple(weight_shape), dtype=torch.float32, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    ws = _workspace(workspace, need, x.device)
-    rc = convnd_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                           ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if implicit:
+        rc = convnd_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                                        stream)
+    else:
+        ws = _workspace(workspace, need, x.device)
+        rc = convnd_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                               ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return dw

@@ -4,7 +4,8 @@
 // and one GEMM finishes the image; more spatial dimensions add one index to
 // the matrix's row and column numbering and one loop over the filter), and
 // 2-D convolution as an implicit GEMM (section "CUTLASS": the GEMM's loader
-// forms the matrix tiles from the image).  Declared in include/conv.h.
+// forms the matrix tiles from the image), in 2-D and, with volume tiles, in
+// 1 to 3 dimensions.  Declared in include/conv.h.
 //
 // The im2col kernel is a copy with zero fill, bound by HBM writes (the matrix
 // holds C_in times the filter volume elements per output position).
@@ -414,6 +415,54 @@ int make_geom(const Dims &d, int esize, ConvGeom *g)
     return GEMM_OK;
 }
 
+// Geometry of the volume (3-D) implicit-GEMM loaders for 1 to 3 spatial
+// dimensions; fewer than three get leading unit dimensions (size, filter,
+// stride and dilation 1, no padding), which changes nothing.  The image of
+// one batch element must span less than 2 GiB.
+int make_geom3(const Dims &d, int esize, ConvGeom *g)
+{
+    if (d.nd > 3 || d.c * d.img_elems() * esize >= (int64_t(1) << 31)) return GEMM_ERR_INVALID_ARG;
+    const int lead = 3 - (int)d.nd;
+    int64_t size[3], kern[3], pad[3], stride[3], dil[3], out[3];
+    for (int i = 0; i < 3; ++i) {
+        const bool unit = i < lead;
+        const int j = i - lead;
+        size[i] = unit ? 1 : d.size[j];
+        kern[i] = unit ? 1 : d.kern[j];
+        pad[i] = unit ? 0 : d.pad[j];
+        stride[i] = unit ? 1 : d.stride[j];
+        dil[i] = unit ? 1 : d.dil[j];
+        out[i] = unit ? 1 : d.out[j];
+    }
+    *g = ConvGeom{};
+    g->d = (int)size[0];
+    g->h = (int)size[1];
+    g->w = (int)size[2];
+    g->t = (int)kern[0];
+    g->r = (int)kern[1];
+    g->s = (int)kern[2];
+    g->pz = (int)pad[0];
+    g->ph = (int)pad[1];
+    g->pw = (int)pad[2];
+    g->sz = (int)stride[0];
+    g->sh = (int)stride[1];
+    g->sw = (int)stride[2];
+    g->lz = (int)dil[0];
+    g->dh = (int)dil[1];
+    g->dw = (int)dil[2];
+    g->p = (int)out[1];
+    g->q = (int)out[2];
+    g->pq = (int)(out[1] * out[2]);
+    g->crs = (int)d.crs();
+    div_magic((uint32_t)out[2], &g->q_magic, &g->q_shift);
+    div_magic((uint32_t)(out[1] * out[2]), &g->pq_magic, &g->pq_shift);
+    div_magic((uint32_t)(kern[1] * kern[2]), &g->rs_magic, &g->rs_shift);
+    div_magic((uint32_t)(kern[0] * kern[1] * kern[2]), &g->trs_magic, &g->trs_shift);
+    div_magic((uint32_t)kern[2], &g->s_magic, &g->s_shift);
+    g->img_bytes = (int)(d.c * d.img_elems() * esize);
+    return GEMM_OK;
+}
+
 int check_workspace(const Dims &d, int dtype, const void *ws, int64_t ws_bytes)
 {
     if (ws == nullptr || (uintptr_t)ws % 16 != 0) return GEMM_ERR_INVALID_ARG;
@@ -755,6 +804,61 @@ int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const vo
     const int rc = dg::dims_nd(p, &d);
     return rc != GEMM_OK ? rc
                          : dg::bwd_weight(dtype, d, x, dy, dw, workspace, workspace_bytes, stream);
+}
+
+int convnd_fwd_implicit(int dtype, int dtype_y, const convnd_params *p, const void *x,
+                        const void *w, void *y, hipStream_t stream)
+{
+    dg::Dims d;
+    if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
+    int rc = dg::dims_nd(p, &d);
+    if (rc != GEMM_OK) return rc;
+    if (d.nd > 3) return GEMM_ERR_INVALID_ARG;
+    if (d.n == 0) return GEMM_OK;
+    const int es = dg::elem_size(dtype), esy = dg::elem_size(dtype_y);
+    if (x == nullptr || w == nullptr || y == nullptr || !dg::aligned_to(x, es) ||
+        !dg::aligned_to(w, es) || !dg::aligned_to(y, esy))
+        return GEMM_ERR_INVALID_ARG;
+    dg::ConvGeom geom;
+    if ((rc = dg::make_geom3(d, es, &geom)) != GEMM_OK) return rc;
+    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    const int64_t vo = d.vol_out();
+    for (int64_t n = 0; n < d.n; ++n) {
+        // y[n] (C_out x output volume) = w (C_out x C_in filter volume) . cols(x[n])
+        dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f,
+                       w, d.crs(), static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1,
+                       static_cast<char *>(y) + n * d.k * vo * esy, vo, dg::B_CONV3_FWD, &geom};
+        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    return GEMM_OK;
+}
+
+int convnd_bwd_weight_implicit(int dtype, const convnd_params *p, const void *x, const void *dy,
+                               float *dw, hipStream_t stream)
+{
+    dg::Dims d;
+    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
+    int rc = dg::dims_nd(p, &d);
+    if (rc != GEMM_OK) return rc;
+    if (d.nd > 3) return GEMM_ERR_INVALID_ARG;
+    const int es = dg::elem_size(dtype);
+    if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
+    if (d.n == 0) return dg::zero_dw(dtype, d, dw, stream);
+    if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
+        return GEMM_ERR_INVALID_ARG;
+    dg::ConvGeom geom;
+    if ((rc = dg::make_geom3(d, es, &geom)) != GEMM_OK) return rc;
+    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
+    const int64_t vo = d.vol_out();
+    for (int64_t n = 0; n < d.n; ++n) {
+        // dw (C_out x C_in filter volume) (+)= dy[n] (C_out x output volume) . cols(x[n])^T
+        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
+                       n == 0 ? 0.0f : 1.0f, static_cast<const char *>(dy) + n * d.k * vo * es, vo,
+                       static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1, dw, d.crs(),
+                       dg::B_CONV3_WGRAD, &geom};
+        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    return GEMM_OK;
 }
 
 }  // extern "C"

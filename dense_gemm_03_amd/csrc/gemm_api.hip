@@ -132,15 +132,17 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
 int select_implicit(int dtype, int64_t M)
 {
     if (dtype == GEMM_DTYPE_F32) {
+        static const int skinny = config_index(dtype, "f32_32x128_w1x4_s3");
         static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
         static const int mid = config_index(dtype, "f32_128x128_w2x2_s2");
         static const int large = config_index(dtype, "f32_256x128_w4x2_s2");
-        return M <= 64 ? wide : M <= 128 ? mid : large;
+        return M <= 32 ? skinny : M <= 64 ? wide : M <= 128 ? mid : large;
     }
+    static const int skinny = config_index(dtype, "bf16_32x256x64_w1x4_s3");
     static const int wide = config_index(dtype, "bf16_64x256x64_w1x4_s3");
     static const int mid = config_index(dtype, "bf16_128x128x64_w2x2_s2");
     static const int large = config_index(dtype, "bf16_256x128x64_w2x2_s2");
-    return M <= 64 ? wide : M <= 128 ? mid : large;
+    return M <= 32 ? skinny : M <= 64 ? wide : M <= 128 ? mid : large;
 }
 
 // Number of K slices.  Large blocks: 1 when the output alone yields enough
@@ -245,7 +247,7 @@ int check_args(const Call &c)
     const int64_t a_row = c.transa == GEMM_OP_T ? c.M : c.K;
     const int64_t b_row = c.transb == GEMM_OP_T ? c.K : c.N;
     const bool implicit = c.bsrc != B_MATRIX;
-    if (implicit && (c.bsrc < B_CONV_FWD || c.bsrc > B_CONV_WGRAD_TAB || c.conv == nullptr ||
+    if (implicit && (c.bsrc < B_CONV_FWD || c.bsrc > B_CONV3_WGRAD || c.conv == nullptr ||
                      c.transa != GEMM_OP_N ||
                      c.transb != (conv_fwd_source(c.bsrc) ? GEMM_OP_N : GEMM_OP_T) ||
                      (conv_table_source(c.bsrc) && c.conv->tab == nullptr)))

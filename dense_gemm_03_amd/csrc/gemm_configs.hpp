@@ -8,7 +8,9 @@
 // with the tile shape (BM x BN block, BK k-tile), the wave grid (WM x WN
 // waves), the number of LDS stages, the raster group height, and LAYOUTS =
 // ALL (kernels for all four combinations of transposed operands), CONV (ALL,
-// plus implicit-GEMM convolution kernels) or NN (only A and B as given).  The kernels of one input type and operand layout are
+// plus implicit-GEMM convolution kernels), NN (only A and B as given),
+// SKINNY (A . B and A . B^T), SKINNYC (SKINNY plus implicit-GEMM kernels) or
+// KK (only A . B^T).  The kernels of one input type and operand layout are
 // instantiated by one compilation of gemm_instances.hip, so the slices compile
 // in parallel; the tables (gemm_tables.hip) only take their addresses.
 #pragma once
@@ -35,11 +37,12 @@ struct TileConfig {
     // element-wise loads, any alignment of the element type.  nullptr where
     // the entry has no kernel for that layout.
     launch_fn fn[4][2];
-    // implicit-GEMM convolution kernels (B tiles formed from an image):
-    // implicit[0] forward (B = cols), implicit[1] filter gradient (B = cols^T),
-    // implicit[2] / [3] the same with table-looked-up per-k terms; [aligned],
-    // as fn.  nullptr where the entry has none.
-    launch_fn implicit[4][2];
+    // implicit-GEMM convolution kernels (B tiles formed from an image),
+    // indexed by B source - 1: [0] forward (B = cols), [1] filter gradient
+    // (B = cols^T), [2] / [3] the same with table-looked-up per-k terms,
+    // [4] / [5] the volume (3-D) forms; [aligned], as fn.  nullptr where the
+    // entry has none.
+    launch_fn implicit[6][2];
 };
 
 // Declared here; defined in gemm_launch.hpp and explicitly instantiated by the
@@ -64,6 +67,12 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_LB_CWT ::dg::KMAJOR
 #define DG_BSRC_CFT ::dg::B_CONV_FWD_TAB
 #define DG_BSRC_CWT ::dg::B_CONV_WGRAD_TAB
+#define DG_LA_C3F ::dg::KMAJOR
+#define DG_LB_C3F ::dg::MNMAJOR
+#define DG_LA_C3W ::dg::KMAJOR
+#define DG_LB_C3W ::dg::KMAJOR
+#define DG_BSRC_C3F ::dg::B_CONV3_FWD
+#define DG_BSRC_C3W ::dg::B_CONV3_WGRAD
 
 // Memory orientation of op(A) / op(B) per layout combination: A as given is
 // k-contiguous, A^T (stored K x M) outer-contiguous; B as given is
@@ -100,9 +109,9 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("f32_64x64_w1x1_s4", false, 64, 64, 32, 1, 1, 4, 8, NN)               \
     X("f32_64x256_w1x4_s2", false, 64, 256, 32, 1, 4, 2, 1, NN)             \
     X("f32_32x256_w1x4_s2", false, 32, 256, 32, 1, 4, 2, 1, SKINNY)         \
-    X("f32_32x256_w1x4_s3", false, 32, 256, 32, 1, 4, 3, 1, SKINNY)         \
+    X("f32_32x256_w1x4_s3", false, 32, 256, 32, 1, 4, 3, 1, SKINNYC)        \
     X("f32_32x128_w1x2_s3", false, 32, 128, 32, 1, 2, 3, 1, SKINNY)         \
-    X("f32_32x128_w1x4_s3", false, 32, 128, 32, 1, 4, 3, 1, SKINNY)         \
+    X("f32_32x128_w1x4_s3", false, 32, 128, 32, 1, 4, 3, 1, SKINNYC)        \
     X("f32_32x128x64_w1x4_s2", false, 32, 128, 64, 1, 4, 2, 1, KK)          \
     X("f32_32x128x64_w1x4_s3", false, 32, 128, 64, 1, 4, 3, 1, KK)          \
     X("f32_32x256x64_w1x4_s2", false, 32, 256, 64, 1, 4, 2, 1, KK)          \
@@ -118,7 +127,7 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("bf16_64x256x64_w1x4_s3", true, 64, 256, 64, 1, 4, 3, 1, CONV)        \
     X("bf16_64x256x64_w1x4_s2", true, 64, 256, 64, 1, 4, 2, 1, NN)         \
     X("bf16_32x256x64_w1x4_s2", true, 32, 256, 64, 1, 4, 2, 1, SKINNY)     \
-    X("bf16_32x256x64_w1x4_s3", true, 32, 256, 64, 1, 4, 3, 1, SKINNY)     \
+    X("bf16_32x256x64_w1x4_s3", true, 32, 256, 64, 1, 4, 3, 1, SKINNYC)    \
     X("bf16_32x128x64_w1x2_s3", true, 32, 128, 64, 1, 2, 3, 1, SKINNY)     \
     X("bf16_32x256x128_w1x4_s2", true, 32, 256, 128, 1, 4, 2, 1, KK)       \
     X("bf16_32x128x128_w1x4_s2", true, 32, 128, 128, 1, 4, 2, 1, KK)       \
@@ -141,6 +150,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_FNS_CONV_NT(...) DG_FNS(__VA_ARGS__, NT)
 #define DG_FNS_CONV_TN(...) DG_FNS(__VA_ARGS__, TN)
 #define DG_FNS_CONV_TT(...) DG_FNS(__VA_ARGS__, TT)
+#define DG_FNS_SKINNYC_NN(...) DG_FNS(__VA_ARGS__, NN)
+#define DG_FNS_SKINNYC_NT(...) DG_FNS(__VA_ARGS__, NT)
+#define DG_FNS_SKINNYC_TN(...) DG_NOFNS
+#define DG_FNS_SKINNYC_TT(...) DG_NOFNS
 #define DG_FNS_SKINNY_NN(...) DG_FNS(__VA_ARGS__, NN)
 #define DG_FNS_SKINNY_NT(...) DG_FNS(__VA_ARGS__, NT)
 #define DG_FNS_SKINNY_TN(...) DG_NOFNS
@@ -156,11 +169,13 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 
 #define DG_IMPL_CONV(BF16, BM, BN, BK, WM, WN)                                                \
     {DG_IFNS(BF16, BM, BN, BK, WM, WN, CF), DG_IFNS(BF16, BM, BN, BK, WM, WN, CW),              \
-     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFT), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWT)}
-#define DG_IMPL_NONE {DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS}
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFT), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWT),            \
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, C3F), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3W)}
+#define DG_IMPL_NONE {DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS}
 #define DG_IMPL_ALL(...) DG_IMPL_NONE
 #define DG_IMPL_NN(...) DG_IMPL_NONE
 #define DG_IMPL_SKINNY(...) DG_IMPL_NONE
+#define DG_IMPL_SKINNYC(...) DG_IMPL_CONV(__VA_ARGS__)
 #define DG_IMPL_KK(...) DG_IMPL_NONE
 
 // One table entry from one list item.

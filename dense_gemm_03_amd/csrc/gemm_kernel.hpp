@@ -73,19 +73,33 @@ enum BSource {
     // before the launch (ConvGeom::tab) instead of computed in the loader.
     B_CONV_FWD_TAB = 3,
     B_CONV_WGRAD_TAB = 4,
+    // Volume (3-D) forms of the first two, analytic terms: image [C_in][D][H][W],
+    // taps (ci, t, r, s), output positions (o, p, q).
+    B_CONV3_FWD = 5,
+    B_CONV3_WGRAD = 6,
 };
 
-__host__ __device__ constexpr bool conv_fwd_source(int b) { return b == B_CONV_FWD || b == B_CONV_FWD_TAB; }
+__host__ __device__ constexpr bool conv_fwd_source(int b)
+{
+    return b == B_CONV_FWD || b == B_CONV_FWD_TAB || b == B_CONV3_FWD;
+}
 __host__ __device__ constexpr bool conv_table_source(int b) { return b == B_CONV_FWD_TAB || b == B_CONV_WGRAD_TAB; }
+__host__ __device__ constexpr bool conv_volume_source(int b) { return b == B_CONV3_FWD || b == B_CONV3_WGRAD; }
 
 // Geometry of the convolution behind an implicit op(B), for one image
 // [C_in][H][W]: matrix row (ci R + r) S + s, column p Q + q holds
 // image[ci][p sh - ph + r dh][q sw - pw + s dw], zero outside the image.
+// Volume sources add a leading dimension: image [C_in][D][H][W], row
+// ((ci T + t) R + r) S + s, column (o P + p) Q + q, depth o sz - pz + t lz.
 struct ConvGeom {
     int h, w, r, s, ph, pw, sh, sw, dh, dw, q, pq, crs;
     uint64_t q_magic, rs_magic, s_magic;  // j / Q, k / (R S), k / S (exact below 2^31)
     int q_shift, rs_shift, s_shift;
-    int img_bytes;                        // C_in H W element bytes (< 2^31)
+    int img_bytes;                        // C_in (D) H W element bytes (< 2^31)
+    // volume sources only
+    int d, t, pz, sz, lz, p;              // depth, filter depth, its padding, stride, dilation; P
+    uint64_t trs_magic, pq_magic;         // k / (T R S), j / (P Q)
+    int trs_shift, pq_shift;
     // Table sources only: the terms that change along K, one entry per k --
     // per tap (ci, r, s) for the forward product, per output position (p, q)
     // for the filter gradient: {y | x << 16 (signed 16-bit each), byte offset}.
@@ -702,8 +716,8 @@ __device__ __forceinline__ int div_magic(int j, uint64_t m, int shift)
 // tables).
 //
 // Every matrix element is image[ci][y][x] with y = (p sh - ph) + r dh and
-// x = (q sw - pw) + s dw: a column term (from p, q) plus a row term (from
-// ci, r, s).  A thread's chunks share their column positions across its chunk
+// x = (q sw - pw) + s dw (volume sources: image[ci][z][y][x], z likewise): a
+// column term (from the output position) plus a row term (from the tap).  A thread's chunks share their column positions across its chunk
 // rows (NT is a multiple of the chunks per tile row), so in the forward tile
 // (rows k = taps, columns n = outputs) the column terms are fixed for the
 // whole K loop and the row terms change per k-tile; in the filter-gradient
@@ -717,19 +731,26 @@ struct ConvGather {
     static constexpr int U = T::PER_THREAD, V = T::VEC, RSTEP = T::NT / T::CPR;
     static constexpr bool FWD = conv_fwd_source(MODE);
     static constexpr bool TAB = conv_table_source(MODE);
+    static constexpr bool VOL = conv_volume_source(MODE);
+    static constexpr int ES = (int)sizeof(In);
     static_assert(T::NT % T::CPR == 0, "a thread's chunks must share their columns");
     static_assert((FWD && T::LAYOUT == MNMAJOR) || (!FWD && T::LAYOUT == KMAJOR),
                   "tile orientation of the convolution source");
+
+    // Image coordinates (depth z for volume sources only) and byte offset of
+    // a term; an element's coordinates and offset are the sums of its
+    // column term and its row term.
+    struct Term {
+        int z, y, x, o;
+    };
 
     __amdgpu_buffer_rsrc_t rsrc;
     const ConvGeom *g;
     int row0, e0;      // first chunk row of this thread, first element in the row
     // Fixed terms -- column terms (forward) or row terms (filter gradient) --
-    // as (y, x, byte offset) plus whether that column / row lies inside the
-    // matrix.  The byte offset of an element is the sum of its column and row
-    // offsets; (y, x) only decide whether it lies in the image.
+    // plus whether that column / row lies inside the matrix.
     static constexpr int NF = FWD ? V : U;
-    int fy[NF], fx[NF], fo[NF];
+    Term f[NF];
     bool fok[NF];
     // Table sources: the per-k entries of the next k-tile, loaded one tile
     // ahead so that their latency hides behind the current tile's gathers.
@@ -740,41 +761,63 @@ struct ConvGather {
     // every tap they read V consecutive image elements.
     bool run = false;
 
-    // Terms of tap k = (ci R + r) S + s: y = r dh, x = s dw, offset of
-    // (ci, r dh, s dw) in the image.
-    __device__ __forceinline__ void tap_terms(int k, int &ty, int &tx, int &to) const
+    // Terms of tap k = (ci R + r) S + s (volume: ((ci T + t) R + r) S + s):
+    // z = t lz, y = r dh, x = s dw and the offset of (ci, z, y, x).
+    __device__ __forceinline__ Term tap_terms(int k) const
     {
-        const int ci = div_magic(k, g->rs_magic, g->rs_shift);
-        const int rem = k - ci * g->r * g->s;
+        Term e;
+        int ci, rem;
+        if constexpr (VOL) {
+            ci = div_magic(k, g->trs_magic, g->trs_shift);
+            rem = k - ci * g->t * g->r * g->s;
+            const int tt = div_magic(rem, g->rs_magic, g->rs_shift);
+            rem -= tt * g->r * g->s;
+            e.z = tt * g->lz;
+        } else {
+            ci = div_magic(k, g->rs_magic, g->rs_shift);
+            rem = k - ci * g->r * g->s;
+            e.z = 0;
+        }
         const int r = div_magic(rem, g->s_magic, g->s_shift);
         const int s = rem - r * g->s;
-        ty = r * g->dh;
-        tx = s * g->dw;
-        to = ((ci * g->h + ty) * g->w + tx) * (int)sizeof(In);
+        e.y = r * g->dh;
+        e.x = s * g->dw;
+        const int plane = VOL ? ci * g->d + e.z : ci;
+        e.o = ((plane * g->h + e.y) * g->w + e.x) * ES;
+        return e;
     }
-    // Terms of output position j = p Q + q: y = p sh - ph, x = q sw - pw and
-    // the (possibly negative) offset of (y, x).
-    __device__ __forceinline__ void out_terms(int j, int &ty, int &tx, int &to) const
+    // Terms of output position j = p Q + q (volume: (o P + p) Q + q):
+    // z = o sz - pz, y = p sh - ph, x = q sw - pw and the (possibly negative)
+    // offset of (z, y, x).
+    __device__ __forceinline__ Term out_terms(int j) const
     {
-        const int p = div_magic(j, g->q_magic, g->q_shift);
-        const int q = j - p * g->q;
-        ty = p * g->sh - g->ph;
-        tx = q * g->sw - g->pw;
-        to = (ty * g->w + tx) * (int)sizeof(In);
+        Term e;
+        int rem = j;
+        if constexpr (VOL) {
+            const int o = div_magic(j, g->pq_magic, g->pq_shift);
+            rem = j - o * g->pq;
+            e.z = o * g->sz - g->pz;
+        } else {
+            e.z = 0;
+        }
+        const int p = div_magic(rem, g->q_magic, g->q_shift);
+        const int q = rem - p * g->q;
+        e.y = p * g->sh - g->ph;
+        e.x = q * g->sw - g->pw;
+        e.o = (((VOL ? e.z * g->h : 0) + e.y) * g->w + e.x) * ES;
+        return e;
     }
     // Per-k terms of k (clamped into the matrix by the caller).
-    __device__ __forceinline__ void k_terms(int k, int &ty, int &tx, int &to) const
+    __device__ __forceinline__ Term k_terms(int k) const
     {
         if constexpr (FWD)
-            tap_terms(k, ty, tx, to);
+            return tap_terms(k);
         else
-            out_terms(k, ty, tx, to);
+            return out_terms(k);
     }
-    static __device__ __forceinline__ void unpack(int2 e, int &ty, int &tx, int &to)
+    static __device__ __forceinline__ Term unpack(int2 e)
     {
-        ty = (e.x << 16) >> 16;
-        tx = e.x >> 16;
-        to = e.y;
+        return Term{0, (e.x << 16) >> 16, e.x >> 16, e.y};
     }
     // k of this thread's i-th per-k slot in the k-tile at k0.
     __device__ __forceinline__ int k_of(int k0, int i) const
@@ -787,6 +830,11 @@ struct ConvGather {
 #pragma unroll
             for (int i = 0; i < NK; ++i) nxt[i] = g->tab[min(k_of(k0, i), kend - 1)];
         }
+    }
+    // V consecutive terms that read V consecutive image elements of one row.
+    static __device__ __forceinline__ bool is_run(const Term &a, const Term &b)
+    {
+        return (!VOL || a.z == b.z) & (a.y == b.y) & (b.x == a.x + (V - 1));
     }
 
     __device__ __forceinline__ ConvGather(const KernelArgs &a, int bn, int tid, int kbeg, int kend)
@@ -801,29 +849,36 @@ struct ConvGather {
             for (int e = 0; e < V; ++e) {
                 const int n = bn + e0 + e;
                 fok[e] = n < a.N;
-                out_terms(min(n, a.N - 1), fy[e], fx[e], fo[e]);
+                f[e] = out_terms(min(n, a.N - 1));
             }
+            run = fok[V - 1] & is_run(f[0], f[V - 1]);
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int n = bn + row0 + u * RSTEP;
                 fok[u] = n < a.N;
-                tap_terms(min(n, a.N - 1), fy[u], fx[u], fo[u]);
+                f[u] = tap_terms(min(n, a.N - 1));
             }
         }
         prefetch(kbeg, kend);
-        if constexpr (FWD)
-            run = fok[V - 1] & (fy[0] == fy[V - 1]) & (fx[V - 1] == fx[0] + (V - 1));
     }
 
-    // The element at image position (y, x) and byte offset off, or zero when
-    // ok is false or (y, x) lies in the padding.  Straight-line code: the
-    // range checks are unsigned compares joined without short-circuits.
-    __device__ __forceinline__ In fetch(bool ok, int y, int x, int off) const
+    // Whether image position (z, y, x) lies inside the image: unsigned
+    // compares joined without short-circuits.
+    __device__ __forceinline__ bool inside(int z, int y, int x) const
     {
-        const bool inside = ok & ((unsigned)y < (unsigned)g->h) & ((unsigned)x < (unsigned)g->w);
-        const int vo = inside ? off : (int)0x80000000u;
-        if constexpr (sizeof(In) == 4)
+        bool in = ((unsigned)y < (unsigned)g->h) & ((unsigned)x < (unsigned)g->w);
+        if constexpr (VOL) in = in & ((unsigned)z < (unsigned)g->d);
+        return in;
+    }
+
+    // The element of column term c and row term k, or zero when ok is false
+    // or it lies in the padding.
+    __device__ __forceinline__ In fetch(bool ok, const Term &c, const Term &k) const
+    {
+        const bool in = ok & inside(c.z + k.z, c.y + k.y, c.x + k.x);
+        const int vo = in ? c.o + k.o : (int)0x80000000u;
+        if constexpr (ES == 4)
             return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, 0, 0));
         else
             return (In)__builtin_amdgcn_raw_buffer_load_b16(rsrc, vo, 0, 0);
@@ -845,16 +900,16 @@ struct ConvGather {
             u32x4 v;
             In e[V];
         };
-        int ky[NK], kx[NK], ko[NK];
+        Term kt[NK];
         bool kok[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int k = k_of(k0, i);
             kok[i] = k < kend;
             if constexpr (TAB)
-                unpack(nxt[i], ky[i], kx[i], ko[i]);
+                kt[i] = unpack(nxt[i]);
             else
-                k_terms(min(k, kend - 1), ky[i], kx[i], ko[i]);
+                kt[i] = k_terms(min(k, kend - 1));
         }
         prefetch(k0 + G::BK, kend);
         // A chunk whose V elements are V consecutive image elements of one
@@ -864,31 +919,33 @@ struct ConvGather {
         if constexpr (FWD) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool whole = run & kok[u] & ((unsigned)(fy[0] + ky[u]) < (unsigned)g->h) &
-                                   (fx[0] + kx[u] >= 0) & (fx[V - 1] + kx[u] < g->w);
+                const Term &t = kt[u];
+                const bool whole = run & kok[u] &
+                                   inside(f[0].z + t.z, f[0].y + t.y, f[0].x + t.x) &
+                                   (f[V - 1].x + t.x < g->w);
                 if (whole) {
-                    r[u] = load_run(fo[0] + ko[u]);
+                    r[u] = load_run(f[0].o + t.o);
                 } else {
                     Chunk c;
 #pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        c.e[e] = fetch(kok[u] & fok[e], fy[e] + ky[u], fx[e] + kx[u], fo[e] + ko[u]);
+                    for (int e = 0; e < V; ++e) c.e[e] = fetch(kok[u] & fok[e], f[e], t);
                     r[u] = c.v;
                 }
             }
         } else {
-            const bool krun = kok[V - 1] & (ky[0] == ky[V - 1]) & (kx[V - 1] == kx[0] + (V - 1));
+            const bool krun = kok[V - 1] & is_run(kt[0], kt[V - 1]);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool whole = krun & fok[u] & ((unsigned)(fy[u] + ky[0]) < (unsigned)g->h) &
-                                   (fx[u] + kx[0] >= 0) & (fx[u] + kx[V - 1] < g->w);
+                const Term &t = f[u];
+                const bool whole = krun & fok[u] &
+                                   inside(t.z + kt[0].z, t.y + kt[0].y, t.x + kt[0].x) &
+                                   (t.x + kt[V - 1].x < g->w);
                 if (whole) {
-                    r[u] = load_run(fo[u] + ko[0]);
+                    r[u] = load_run(t.o + kt[0].o);
                 } else {
                     Chunk c;
 #pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        c.e[e] = fetch(fok[u] & kok[e], fy[u] + ky[e], fx[u] + kx[e], fo[u] + ko[e]);
+                    for (int e = 0; e < V; ++e) c.e[e] = fetch(fok[u] & kok[e], kt[e], t);
                     r[u] = c.v;
                 }
             }

@@ -1,8 +1,9 @@
 // Definition of the kernel launcher and the explicit instantiation of one
 // operand layout's kernels from the tile lists.  Included by the per-layout
 // source files, each of which defines DG_DTYPE_TABLE (the list), DG_LAYOUT
-// (NN, NT, TN, TT, or CF / CW / CFT / CWT for the implicit-GEMM convolution
-// kernels: forward / filter gradient, analytic / table-looked-up terms) and
+// (NN, NT, TN, TT, or CF / CW / CFT / CWT / C3F / C3W for the implicit-GEMM
+// convolution kernels: forward / filter gradient, analytic / table-looked-up
+// terms, volume) and
 // then includes this header.
 #pragma once
 
@@ -45,6 +46,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_ALL_CW(...)
 #define DG_INST_ALL_CFT(...)
 #define DG_INST_ALL_CWT(...)
+#define DG_INST_ALL_C3F(...)
+#define DG_INST_ALL_C3W(...)
 #define DG_INST_CONV_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_CONV_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_CONV_TN(...) DG_INST(__VA_ARGS__, TN)
@@ -53,6 +56,18 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_CONV_CW(...) DG_IINST(__VA_ARGS__, CW)
 #define DG_INST_CONV_CFT(...) DG_IINST(__VA_ARGS__, CFT)
 #define DG_INST_CONV_CWT(...) DG_IINST(__VA_ARGS__, CWT)
+#define DG_INST_CONV_C3F(...) DG_IINST(__VA_ARGS__, C3F)
+#define DG_INST_CONV_C3W(...) DG_IINST(__VA_ARGS__, C3W)
+#define DG_INST_SKINNYC_NN(...) DG_INST(__VA_ARGS__, NN)
+#define DG_INST_SKINNYC_NT(...) DG_INST(__VA_ARGS__, NT)
+#define DG_INST_SKINNYC_TN(...)
+#define DG_INST_SKINNYC_TT(...)
+#define DG_INST_SKINNYC_CF(...) DG_IINST(__VA_ARGS__, CF)
+#define DG_INST_SKINNYC_CW(...) DG_IINST(__VA_ARGS__, CW)
+#define DG_INST_SKINNYC_CFT(...) DG_IINST(__VA_ARGS__, CFT)
+#define DG_INST_SKINNYC_CWT(...) DG_IINST(__VA_ARGS__, CWT)
+#define DG_INST_SKINNYC_C3F(...) DG_IINST(__VA_ARGS__, C3F)
+#define DG_INST_SKINNYC_C3W(...) DG_IINST(__VA_ARGS__, C3W)
 #define DG_INST_SKINNY_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_SKINNY_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_SKINNY_TN(...)
@@ -61,6 +76,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_SKINNY_CW(...)
 #define DG_INST_SKINNY_CFT(...)
 #define DG_INST_SKINNY_CWT(...)
+#define DG_INST_SKINNY_C3F(...)
+#define DG_INST_SKINNY_C3W(...)
 #define DG_INST_KK_NN(...)
 #define DG_INST_KK_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_KK_TN(...)
@@ -69,6 +86,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_KK_CW(...)
 #define DG_INST_KK_CFT(...)
 #define DG_INST_KK_CWT(...)
+#define DG_INST_KK_C3F(...)
+#define DG_INST_KK_C3W(...)
 #define DG_INST_NN_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_NN_NT(...)
 #define DG_INST_NN_TN(...)
@@ -77,6 +96,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_NN_CW(...)
 #define DG_INST_NN_CFT(...)
 #define DG_INST_NN_CWT(...)
+#define DG_INST_NN_C3F(...)
+#define DG_INST_NN_C3W(...)
 #define DG_INST_SEL2(LAYOUTS, L) DG_INST_##LAYOUTS##_##L
 #define DG_INST_SEL(LAYOUTS, L) DG_INST_SEL2(LAYOUTS, L)
 #define DG_INST_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                            \

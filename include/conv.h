@@ -190,6 +190,18 @@ int convnd_fwd(int dtype, int dtype_y, const convnd_params *p, const void *x, co
 int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const void *dy, float *dw,
                       void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/* Implicit-GEMM forms for 1 to 3 spatial dimensions ("Three X's", section
+ * "CUTLASS", applied to the N-D matrix): no convolution matrix and no
+ * workspace; the GEMM's loader forms each tile from the image with analytic
+ * address terms (fewer than three dimensions run as three with leading unit
+ * dimensions).  Same arguments, layouts, types and results as convnd_fwd /
+ * convnd_bwd_weight; GEMM_ERR_INVALID_ARG for ndim 4 and when one batch
+ * element of x spans 2 GiB or more. */
+int convnd_fwd_implicit(int dtype, int dtype_y, const convnd_params *p, const void *x,
+                        const void *w, void *y, hipStream_t stream);
+int convnd_bwd_weight_implicit(int dtype, const convnd_params *p, const void *x, const void *dy,
+                               float *dw, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

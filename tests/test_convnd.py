@@ -12,6 +12,8 @@ direct-convolution oracle, through the C ABI (include/conv.h, convnd_*).
 * Random tensors: |y - y_ref| <= tol * S (1e-5 fp32, 4e-3 bf16 inputs).
 * D = 2 through the N-D entry points gives the conv2d entry points' bits.
 * The full-size 3-D and 4-D workloads at sampled outputs and taps.
+* Forward and filter gradient through im2col + GEMM and, up to three
+  dimensions, through the implicit GEMM (volume tiles formed in the loader).
 """
 from __future__ import annotations
 
@@ -86,10 +88,10 @@ def run_im2col(x: np.ndarray, c: NdShape, n: int, ld: int, rows=None):
     return got[:, :c.vol_out]
 
 
-def run_fwd(x, w, c: NdShape, out_bf16=False):
+def run_fwd(x, w, c: NdShape, out_bf16=False, implicit=False):
     import torch
     y = dg.conv_nd(_dev(x), _dev(w), stride=c.stride, padding=c.pad, dilation=c.dilation,
-                   out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+                   out_dtype=torch.bfloat16 if out_bf16 else torch.float32, implicit=implicit)
     torch.cuda.synchronize()
     assert tuple(y.shape) == c.y_shape
     if out_bf16:
@@ -99,10 +101,10 @@ def run_fwd(x, w, c: NdShape, out_bf16=False):
     return raw.astype(np.float64), raw
 
 
-def run_bwd(x, dy, c: NdShape):
+def run_bwd(x, dy, c: NdShape, implicit=False):
     import torch
     dw = dg.conv_nd_weight_grad(_dev(x), _dev(dy), c.w_shape, stride=c.stride, padding=c.pad,
-                                dilation=c.dilation)
+                                dilation=c.dilation, implicit=implicit)
     torch.cuda.synchronize()
     return dw.cpu().numpy().astype(np.float64)
 
@@ -120,39 +122,52 @@ def test_im2col_bit_exact(bf16):
             assert np.array_equal(got, want), "%s image %d" % (c, n)
 
 
+def _shapes(implicit):
+    """The implicit GEMM covers up to three spatial dimensions."""
+    return [(t, c) for t, c in enumerate(SHAPES) if not implicit or c.nd <= 3]
+
+
+ROUTES = [False, True]
+ROUTE_IDS = ["im2col", "implicit"]
+
+
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-def test_fwd_and_filter_gradient_exact_integers(bf16):
-    for t, c in enumerate(SHAPES):
+def test_fwd_and_filter_gradient_exact_integers(bf16, implicit):
+    for t, c in _shapes(implicit):
         x, w = _ints(c.x_shape, 700 + t, bf16), _ints(c.w_shape, 710 + t, bf16)
         dy = _ints(c.y_shape, 720 + t, bf16)
         ref, _ = ocn.fwd(x, w, c)
         for out_bf16 in (False, True):
             log("fwd %s y %s" % (c, "bf16" if out_bf16 else "f32"))
-            got, raw = run_fwd(x, w, c, out_bf16)
+            got, raw = run_fwd(x, w, c, out_bf16, implicit)
             if out_bf16:
                 assert np.array_equal(raw, oracle.round_to_bf16_bits(ref)), str(c)
             else:
                 assert np.array_equal(got, ref), str(c)
         log("filter gradient %s" % (c,))
         ref, _ = ocn.bwd_weight(x, dy, c)
-        assert np.array_equal(run_bwd(x, dy, c), ref), str(c)
+        assert np.array_equal(run_bwd(x, dy, c, implicit), ref), str(c)
 
 
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-def test_random_within_tolerance(bf16):
+def test_random_within_tolerance(bf16, implicit):
     tol = TOL["bf16" if bf16 else "f32"]
-    for t, c in enumerate(SHAPES):
+    for t, c in _shapes(implicit):
         x, w = _randn(c.x_shape, 800 + t, bf16), _randn(c.w_shape, 810 + t, bf16)
         dy = _randn(c.y_shape, 820 + t, bf16)
         ref, S = ocn.fwd(x, w, c)
-        check_close(run_fwd(x, w, c)[0], ref, S, tol, "fwd %s" % (c,))
-        check_close(run_fwd(x, w, c, True)[0], ref, S, tol, "fwd bf16 y %s" % (c,), True)
+        check_close(run_fwd(x, w, c, False, implicit)[0], ref, S, tol, "fwd %s" % (c,))
+        check_close(run_fwd(x, w, c, True, implicit)[0], ref, S, tol, "fwd bf16 y %s" % (c,), True)
         ref, S = ocn.bwd_weight(x, dy, c)
-        check_close(run_bwd(x, dy, c), ref, S, tol, "filter gradient %s" % (c,))
+        check_close(run_bwd(x, dy, c, implicit), ref, S, tol, "filter gradient %s" % (c,))
 
 
 def test_two_dimensions_match_conv2d_bits():
-    """The N-D entry points at D = 2 and the conv2d ones give identical bits."""
+    """The N-D entry points at D = 2 and the conv2d ones give identical bits,
+    for the im2col route and for the implicit GEMM (volume tiles with a unit
+    leading dimension against the 2-D tiles)."""
     import torch
     c = NdShape(2, 5, 9, (21, 19), (5, 3), (2, 1), (2, 1), (1, 2))
     x, w, dy = _randn(c.x_shape, 1, False), _randn(c.w_shape, 2, False), _randn(c.y_shape, 3, False)
@@ -163,8 +178,15 @@ def test_two_dimensions_match_conv2d_bits():
                                   dilation=c.dilation)
     g_2d = dg.conv2d_weight_grad(xd, dyd, c.w_shape, stride=c.stride, padding=c.pad,
                                  dilation=c.dilation)
+    yi_nd = dg.conv_nd(xd, wd, stride=c.stride, padding=c.pad, dilation=c.dilation, implicit=True)
+    yi_2d = dg.conv2d(xd, wd, stride=c.stride, padding=c.pad, dilation=c.dilation, implicit=True)
+    gi_nd = dg.conv_nd_weight_grad(xd, dyd, c.w_shape, stride=c.stride, padding=c.pad,
+                                   dilation=c.dilation, implicit=True)
+    gi_2d = dg.conv2d_weight_grad(xd, dyd, c.w_shape, stride=c.stride, padding=c.pad,
+                                  dilation=c.dilation, implicit=True)
     torch.cuda.synchronize()
     assert torch.equal(y_nd, y_2d) and torch.equal(g_nd, g_2d)
+    assert torch.equal(yi_nd, yi_2d) and torch.equal(gi_nd, gi_2d)
 
 
 def test_empty_batch():
@@ -184,19 +206,22 @@ def _shape_of(wk):
     return NdShape(wk.batch, wk.cin, wk.cout, wk.size, wk.kernel, wk.pad, wk.stride, wk.dilation)
 
 
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
 @pytest.mark.parametrize("name", sorted(wl.CONVND_WORKLOADS))
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, implicit):
     """The N-D workloads at full size: forward outputs and filter-gradient taps
     at sampled positions (corners included) against the oracle, one sum each,
     and the convolution matrix of the last image bit for bit at sampled rows."""
     wk = wl.CONVND_WORKLOADS[name]
     c = _shape_of(wk)
+    if implicit and c.nd > 3:
+        pytest.skip("the implicit GEMM covers up to three spatial dimensions")
     bf16 = wk.dtype == "bf16"
     tol = TOL[wk.dtype]
     x, w, dy = wk.x(), wk.weights(), wk.dy()
     rng = np.random.default_rng(wk.seed + 5)
     log("[%s] forward" % name)
-    y, _ = run_fwd(x, w, c)
+    y, _ = run_fwd(x, w, c, False, implicit)
     yflat = y.reshape(-1)
     idx = rng.integers(0, yflat.size, 256)
     corners = [np.ravel_multi_index((n, co) + tuple(e - 1 if hi else 0 for e, hi in zip(c.out, bits)),
@@ -208,7 +233,7 @@ def test_full_size_sampled(name):
     ref, S = ocn.fwd_at(x, w, c, idx)
     check_close(yflat[idx], ref, S, tol, name + " fwd (256 sampled)")
     log("[%s] filter gradient" % name)
-    dw = run_bwd(x, dy, c).reshape(-1)
+    dw = run_bwd(x, dy, c, implicit).reshape(-1)
     tidx = rng.integers(0, dw.size, 256)
     tidx[0], tidx[1] = 0, dw.size - 1
     ref, S = ocn.bwd_weight_at(x, dy, c, tidx)
@@ -225,17 +250,18 @@ def test_full_size_sampled(name):
         assert np.array_equal(got[t], sub.view(np.uint16) if bf16 else sub.view(np.uint32)), row
 
 
-def test_full_size_exact_integers_sampled():
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
+def test_full_size_exact_integers_sampled(implicit):
     """Integer tensors of the full 3-D shape: sampled outputs and taps exact."""
     wk = wl.CONVND_WORKLOADS["conv3d-32c-k7"]
     c = _shape_of(wk)
     x, w, dy = _ints(c.x_shape, 17, False), _ints(c.w_shape, 18, False), _ints(c.y_shape, 19, False)
-    y, _ = run_fwd(x, w, c)
+    y, _ = run_fwd(x, w, c, False, implicit)
     rng = np.random.default_rng(4)
     idx = rng.integers(0, y.size, 256)
     ref, _ = ocn.fwd_at(x, w, c, idx)
     assert np.array_equal(y.reshape(-1)[idx], ref)
-    dw = run_bwd(x, dy, c).reshape(-1)
+    dw = run_bwd(x, dy, c, implicit).reshape(-1)
     tidx = rng.integers(0, dw.size, 256)
     ref, _ = ocn.bwd_weight_at(x, dy, c, tidx)
     assert np.array_equal(dw[tidx], ref)
