@@ -87,7 +87,8 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
     // Skinny products (a few dozen rows, wide N, usually long K: the
     // convolution GEMMs with few output channels) stream the large operand
     // once; 32-row blocks waste no matrix-core work at M <= 32, and when that
-    // operand is read k-contiguous (B^T) rows of 256 bytes keep its reads long.
+    // operand is read k-contiguous (B^T) rows of 256 (bf16 64-row blocks: 512)
+    // bytes per k-tile keep its reads long.
     const bool skinny = M <= 32 && N >= 1024;
     if (dtype == GEMM_DTYPE_F32) {
         static const int tall = config_index(dtype, "f32_128x64_w2x2_s2");
@@ -117,11 +118,12 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
     static const int medium = config_index(dtype, "bf16_128x128x64_w2x2_s2");
     static const int small = config_index(dtype, "bf16_64x64x64_w2x2_s2");
     static const int wide = config_index(dtype, "bf16_64x256x64_w1x4_s3");
+    static const int wide_t = config_index(dtype, "bf16_64x64x256_w2x2_s2");
     static const int skinny_n = config_index(dtype, "bf16_32x256x64_w1x4_s3");
     static const int skinny_t = config_index(dtype, "bf16_32x256x128_w1x4_s2");
     if (skinny && layout == LAYOUT_NN) return skinny_n;
     if (skinny && layout == LAYOUT_NT) return skinny_t;
-    if (M <= 64 && N >= 1024) return wide;   // few rows, wide N, split-K
+    if (M <= 64 && N >= 1024) return layout == LAYOUT_NT ? wide_t : wide;  // split-K
     if (M >= 2048 && N >= 2048) return best_of(dtype, large, 2, M, N);
     if (M * N >= int64_t(1024) * 1024) return medium;
     return small;

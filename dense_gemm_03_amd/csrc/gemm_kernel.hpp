@@ -133,10 +133,10 @@ struct KernelArgs {
 // 4 bytes, and a 16-byte read serves 16 lanes per pass, so the 16 addresses of
 // a pass must cover 256 bytes that fall on distinct banks.
 //
-//   KMAJOR:  OUTER rows of BK elements (64, 128 or 256 bytes).  Chunk c of row r
+//   KMAJOR:  OUTER rows of BK elements (64 to 1024 bytes).  Chunk c of row r
 //            sits in slot c ^ ((r / RPL) % CPR), RPL rows sharing a 256-byte
-//            bank line: the 16 rows a 16-lane pass reads at one chunk cover
-//            all 64 banks once, and so do the writes.
+//            bank line (RPL = 1 for longer rows): the 16 rows a 16-lane pass
+//            reads at one chunk cover all 64 banks once, and so do the writes.
 //   MNMAJOR: BK rows of OUTER elements, row-major as in memory.
 //     fp32:  the two 32-float halves of each 64-float group swap places in
 //            rows with bit 4 set, so the two lane halves of a fragment read
@@ -164,8 +164,10 @@ struct OpTile {
     static_assert(PIECES % NW == 0, "direct loads must divide over the waves");
     static_assert(ROW_BYTES <= 1024 && 1024 % ROW_BYTES == 0, "rows must tile a 1 KiB piece");
     static constexpr int ROWS_PER_PIECE = 1024 / ROW_BYTES;
-    static constexpr int RPL = 256 / ROW_BYTES;           // KMAJOR rows per bank line
-    static_assert(LAYOUT != KMAJOR || CPR * RPL == 16, "k-contiguous rows of 64, 128 or 256 bytes");
+    // KMAJOR rows per 256-byte bank line (1 for rows of 256 bytes or more)
+    static constexpr int RPL = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
+    static_assert(LAYOUT != KMAJOR || ROW_BYTES >= 256 || CPR * RPL == 16,
+                  "k-contiguous rows of 64 bytes or more");
     static constexpr int SEGMASK = (OUTER / 32 >= 4) ? 3 : (OUTER / 32 - 1);
     static_assert(LAYOUT != MNMAJOR || BF16 || (OUTER % 64 == 0 && BK == 32),
                   "fp32 outer-contiguous tiles: OUTER % 64 == 0, BK == 32");
