@@ -118,8 +118,6 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("f32_64x128x64_w1x4_s2", false, 64, 128, 64, 1, 4, 2, 1, KK)
 
 #define DG_BF16_TABLE(X)                                                    \
-    X("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8, NN)        \
-    X("bf16_256x256x64_w2x4_s2", true, 256, 256, 64, 2, 4, 2, 8, NN)        \
     X("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 4, ALL)       \
     X("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8, CONV)      \
     X("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8, CONV)      \

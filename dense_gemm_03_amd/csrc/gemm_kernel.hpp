@@ -53,6 +53,19 @@
 
 namespace dg {
 
+// f(std::integral_constant<int, I>) for I = B .. E-1, expanded at compile
+// time: loops over accumulator fragments whose bodies are too large for the
+// unroller would otherwise index the accumulators dynamically (and move them
+// to scratch memory).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        static_for<B + 1, E>(f);
+    }
+}
+
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -1066,10 +1079,8 @@ gemm_kernel(KernelArgs p)
             }
         return;
     }
-#pragma unroll
-    for (int fm = 0; fm < G::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < G::FN; ++fn) {
+    static_for<0, G::FM>([&](auto fm) {
+        static_for<0, G::FN>([&](auto fn) {
             const int gj = c.bn + c.wcol * G::WTN + fn * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -1078,7 +1089,8 @@ gemm_kernel(KernelArgs p)
                     store_out(p.C, (int64_t)gi * p.ldc + gj, acc[fm][fn][r], p.alpha, p.beta,
                               p.out_bf16 != 0);
             }
-        }
+        });
+    });
 }
 
 }  // namespace dg
