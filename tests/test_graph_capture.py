@@ -1,0 +1,77 @@
+"""The library's calls inside a captured HIP graph: a split-K GEMM (its
+partial-sum workspace and reduce kernel), an im2col + GEMM convolution, and an
+implicit-GEMM convolution with table address terms (its table kernel and
+buffer) are captured once on a stream that has run them before (so every
+library-owned buffer already exists and nothing is allocated during capture),
+then replayed several times with new inputs written eagerly in between.
+Every replay must equal the eager calls bit for bit (the library is
+deterministic: fixed tile plans, fixed slice order).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dense_gemm_03_amd as dg
+from dense_gemm_03_amd import workloads as wl
+from tests.gpu_util import log, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_equal_eager_calls():
+    import torch
+    M, N, K = 64, 4096, 8192                       # the wide class: split into K slices
+    dt = dg.GEMM_DTYPE_F32
+    cfg = dg.gemm_select_config_ex(dt, 0, 0, M, N, K)
+    assert dg.gemm_split_k_ex(dt, cfg, 0, 0, M, N, K) > 1
+    A = to_device(wl.uniform_f32((M, K), 1))
+    B = to_device(wl.uniform_f32((K, N), 2))
+    C = torch.empty((M, N), device="cuda:0")
+    cs = (2, 6, 30, 33, 8, 5, 5, 2)                # batch, cin, h, w, cout, r, s, pad
+    x = to_device(wl.uniform_f32((cs[0], cs[1], cs[2], cs[3]), 3))
+    w = to_device(wl.uniform_f32((cs[4], cs[1], cs[5], cs[6]), 4))
+    params = dg.conv2d_params(cs[0], cs[1], cs[2], cs[3], cs[4], cs[5], cs[6], (cs[7], cs[7]))
+    rc, P, Q = dg.conv2d_output_size(params)
+    assert rc == dg.GEMM_OK
+    need = dg.conv2d_workspace_size(dt, params)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    y1 = torch.empty((cs[0], cs[4], P, Q), device="cuda:0")
+    y2 = torch.empty_like(y1)
+
+    def calls(stream):
+        sp = stream.cuda_stream
+        dg.gemm(A, B, out=C, stream=sp)
+        assert dg.conv2d_fwd(dt, dt, params, x.data_ptr(), w.data_ptr(), y1.data_ptr(),
+                             ws.data_ptr(), need, sp) == dg.GEMM_OK
+        assert dg.conv2d_fwd_implicit_ex(dt, dt, params, dg.CONV_ADDR_TABLE, x.data_ptr(),
+                                         w.data_ptr(), y2.data_ptr(), sp) == dg.GEMM_OK
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls(s)                                   # creates the per-stream buffers
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls(s)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        A.copy_(to_device(wl.uniform_f32((M, K), 10 + rep)))
+        x.copy_(to_device(wl.uniform_f32((cs[0], cs[1], cs[2], cs[3]), 20 + rep)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        C_eager = dg.gemm(A, B)
+        y1_eager = dg.conv2d(x, w, padding=cs[7])
+        y2_eager = dg.conv2d(x, w, padding=cs[7], implicit="table")
+        torch.cuda.synchronize()
+        log("replay %d: gemm %s, conv %s, implicit conv %s" % (
+            rep, torch.equal(C, C_eager), torch.equal(y1, y1_eager), torch.equal(y2, y2_eager)))
+        assert torch.equal(C, C_eager)
+        assert torch.equal(y1, y1_eager)
+        assert torch.equal(y2, y2_eager)
+        # the replay computed the new inputs, not a stale result
+        assert not np.array_equal(C.cpu().numpy(), 0)
