@@ -59,6 +59,10 @@ def log(msg: str) -> None:
 KERNEL_SOURCES = {
     "gemm": ["gemm_kernel.hpp", "gemm_launch.hpp", "gemm_instances.hip"],
     "im2col": ["conv.hip"],
+    # a convolution route: im2col and/or the GEMM kernels, the reduce, the
+    # implicit loaders and their table kernel
+    "conv": ["conv.hip", "gemm_kernel.hpp", "gemm_launch.hpp", "gemm_instances.hip",
+             "gemm_aux.hip"],
 }
 
 
@@ -176,10 +180,11 @@ def measure(name: str, steps: int, warmup: int):
     return res
 
 
-def measure_conv(name: str, steps: int, warmup: int):
+def measure_conv(name: str, steps: int, warmup: int, only: str | None = None):
     """Time the convolution `name`: forward pass and filter gradient through
-    im2col + GEMM (2-D workloads also through the implicit GEMM), and the
-    im2col kernel alone (its HBM roofline)."""
+    im2col + GEMM and through the implicit GEMM (up to three dimensions), and
+    the im2col kernel alone (its HBM roofline).  `only` names one of these
+    measurements (for per-route profiler passes)."""
     import torch
 
     import dense_gemm_03_amd as dg
@@ -270,20 +275,28 @@ def measure_conv(name: str, steps: int, warmup: int):
         A, T = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE
         routes += [("fwd_implicit", implicit_fwd(A)), ("wgrad_implicit", implicit_wgrad(A)),
                    ("fwd_implicit_table", implicit_fwd(T)), ("wgrad_implicit_table", implicit_wgrad(T))]
+    if only is not None and only not in [r[0] for r in routes] + ["im2col"]:
+        raise SystemExit("unknown route %r for %s" % (only, name))
     for label, fn in routes:
+        if only is not None and label != only:
+            continue
         wall_ms, ev_ms = timed(fn, steps)
         log("[bench] %s %s: %.3f ms per call" % (name, label, ev_ms))
         ach = c.flops / (ev_ms * 1e-3) / 1e12
+        # traffic: HBM bytes of one call of the route (all its kernels)
         res[label] = {"value": c.flops / (wall_ms * 1e-3) / 1e12, "ms_per_step": wall_ms,
                       "roofline": {"bound": "mfma", "achieved": ach, "peak": peak,
-                                   "unit": "TFLOP/s", "frac": ach / peak, "traffic": None}}
-    _, ev_ms = timed(im2col, steps)
-    gbs = c.im2col_bytes / (ev_ms * 1e-3) / 1e9
-    traffic = stored_traffic(name + "-im2col", "im2col")
-    res["im2col"] = {"ms_per_call": ev_ms,
-                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}}
-    log("[bench] %s im2col: %.3f ms, %.0f GB/s" % (name, ev_ms, gbs))
+                                   "unit": "TFLOP/s", "frac": ach / peak,
+                                   "traffic": stored_traffic(name + "-" + label, "conv")}}
+    if only is None or only == "im2col":
+        _, ev_ms = timed(im2col, steps)
+        gbs = c.im2col_bytes / (ev_ms * 1e-3) / 1e9
+        traffic = stored_traffic(name + "-im2col", "im2col")
+        res["im2col"] = {"ms_per_call": ev_ms,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                      "traffic": traffic}}
+        log("[bench] %s im2col: %.3f ms, %.0f GB/s" % (name, ev_ms, gbs))
     vol_out = int(np.prod(out))
     result = {"workload": name, "dtype": c.dtype,
               "shape": {"batch": c.batch, "cin": c.cin, "size": list(x_shape[2:]),
@@ -357,6 +370,10 @@ def main() -> int:
     ap.add_argument("--conv", default=None, metavar="NAME",
                     help="only time the convolution workload NAME (for per-kernel profiler "
                          "passes) and print its result")
+    ap.add_argument("--conv-route", default=None, metavar="ROUTE",
+                    help="with --conv: time only this route (fwd, wgrad, fwd_implicit, "
+                         "wgrad_implicit, fwd_implicit_table, wgrad_implicit_table, im2col), "
+                         "for per-route profiler passes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference kernel "
                          "for the HBM byte counters) and exit")
@@ -384,8 +401,8 @@ def main() -> int:
     import dense_gemm_03_amd as dg
     dg.load_library()
     if args.conv:
-        print(json.dumps({"convolution": {args.conv: measure_conv(args.conv, args.steps,
-                                                                   args.warmup)}}), flush=True)
+        print(json.dumps({"convolution": {args.conv: measure_conv(
+            args.conv, args.steps, args.warmup, args.conv_route)}}), flush=True)
         return 0
 
     main_res = measure(args.workload, args.steps, args.warmup)

@@ -87,11 +87,13 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_LB_TT ::dg::KMAJOR
 
 // The tile tables.  The shape classes they serve (tile sizes per task, "How to
-// do even better" on the GEMM page): square/large blocks for big M and N, a
-// wide-N block with split-K for M of a few dozen rows and long K (the im2col
-// weight-gradient shape), a tall block for N of a few dozen columns, and a
-// small block when the output holds too few large blocks to fill 256 compute
-// units.  Every entry the dispatcher can choose is built for all layouts.
+// do even better" on the GEMM page): square/large blocks for big M and N; for
+// M of a few dozen rows and wide N (the convolution GEMMs), 32- and 64-row
+// blocks with split-K, including A . B^T blocks with long k-contiguous rows;
+// a tall block for N of a few dozen columns; and a small block when the
+// output holds too few large blocks to fill 256 compute units.  Entries the
+// dispatcher picks for only some operand forms (SKINNY, SKINNYC, KK) are
+// chosen only for those forms; the others are built for all four.
 #define DG_F32_TABLE(X)                                                     \
     X("f32_256x128_w4x2_s2", false, 256, 128, 32, 4, 2, 2, 8, CONV)         \
     X("f32_128x128_w2x2_s2", false, 128, 128, 32, 2, 2, 2, 8, CONV)         \
