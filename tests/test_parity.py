@@ -171,3 +171,26 @@ def test_transpose_invariant_on_gpu():
         C = run(A, B).cpu().numpy()
         Ct = run(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T)).cpu().numpy()
         assert np.array_equal(C.T, Ct)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_leading_dimensions_beyond_32_bit_tile_offsets(bf16):
+    """Leading dimensions so large that a tile's byte offsets from its origin
+    exceed 32 bits (A rows 16 MiB + 32 bytes apart, C likewise): the kernels
+    take their 64-bit element-wise path.  The padding holds NaN and must be
+    neither read (C finite and exact) nor written."""
+    import torch
+    M, N, K = 300, 200, 100
+    ld = (1 << 22) + 8                                   # elements; 256 rows x ld x 4 B > 2^32
+    dt = torch.bfloat16 if bf16 else torch.float32
+    A, B = _ints((M, K), 91, bf16), _ints((K, N), 92, bf16)
+    Abuf = torch.full((M, ld), float("nan"), dtype=dt, device="cuda:0")
+    Abuf[:, :K] = to_device(A)
+    Cbuf = torch.full((M, ld), float("nan"), dtype=torch.float32, device="cuda:0")
+    C = Cbuf[:, :N]
+    dg.gemm(Abuf[:, :K], to_device(B), out=C)
+    torch.cuda.synchronize()
+    check_exact(C.cpu().numpy(), A, B, "lda = ldc = %d" % ld)
+    assert bool(torch.isnan(Cbuf[:, N:N + 64]).all()) and bool(torch.isnan(Cbuf[:, -8:]).all())
+    del Abuf, Cbuf
+    torch.cuda.empty_cache()
