@@ -20,10 +20,11 @@ in HBM.  Prints ONE JSON line:
   convolution             the im2col + GEMM convolution of the 64-channel
                           31x31-filter workload, fp32 and bf16 (forward,
                           filter gradient, their implicit-GEMM forms with
-                          analytic and table address generation, and the
-                          im2col kernel against HBM), and of the 3-D (7x7x7
-                          filters, fp32 and bf16; also through the implicit
-                          GEMM) and 4-D workloads
+                          analytic, table and padded-image address
+                          generation, and the im2col kernel against HBM),
+                          and of the 3-D (7x7x7 filters, fp32 and bf16; also
+                          through the implicit GEMM, analytic and padded)
+                          and 4-D workloads
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -60,7 +61,7 @@ KERNEL_SOURCES = {
     "gemm": ["gemm_kernel.hpp", "gemm_launch.hpp", "gemm_instances.hip"],
     "im2col": ["conv.hip"],
     # a convolution route: im2col and/or the GEMM kernels, the reduce, the
-    # implicit loaders and their table kernel
+    # implicit loaders and their table and pad kernels
     "conv": ["conv.hip", "gemm_kernel.hpp", "gemm_launch.hpp", "gemm_instances.hip",
              "gemm_aux.hip"],
 }
@@ -262,19 +263,28 @@ def measure_conv(name: str, steps: int, warmup: int, only: str | None = None):
     res = {}
     peak = PEAK_TFLOPS[c.dtype]
     routes = [("fwd", fwd), ("wgrad", wgrad)]
+    A, T, PD = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE, dg.CONV_ADDR_PADDED
     if nd and c.nd <= 3:
-        def fwd_nd_implicit():
-            assert dg.convnd_fwd_implicit(dtype, F32, params, x.data_ptr(), w.data_ptr(),
-                                          y.data_ptr(), sp) == dg.GEMM_OK
+        def fwd_nd_implicit(mode):
+            def run():
+                assert dg.convnd_fwd_implicit_ex(dtype, F32, params, mode, x.data_ptr(),
+                                                 w.data_ptr(), y.data_ptr(), sp) == dg.GEMM_OK
+            return run
 
-        def wgrad_nd_implicit():
-            assert dg.convnd_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(),
-                                                 dw.data_ptr(), sp) == dg.GEMM_OK
-        routes += [("fwd_implicit", fwd_nd_implicit), ("wgrad_implicit", wgrad_nd_implicit)]
+        def wgrad_nd_implicit(mode):
+            def run():
+                assert dg.convnd_bwd_weight_implicit_ex(dtype, params, mode, x.data_ptr(),
+                                                        dy.data_ptr(), dw.data_ptr(),
+                                                        sp) == dg.GEMM_OK
+            return run
+        routes += [("fwd_implicit", fwd_nd_implicit(A)), ("wgrad_implicit", wgrad_nd_implicit(A)),
+                   ("fwd_implicit_padded", fwd_nd_implicit(PD)),
+                   ("wgrad_implicit_padded", wgrad_nd_implicit(PD))]
     if not nd:
-        A, T = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE
         routes += [("fwd_implicit", implicit_fwd(A)), ("wgrad_implicit", implicit_wgrad(A)),
-                   ("fwd_implicit_table", implicit_fwd(T)), ("wgrad_implicit_table", implicit_wgrad(T))]
+                   ("fwd_implicit_table", implicit_fwd(T)), ("wgrad_implicit_table", implicit_wgrad(T)),
+                   ("fwd_implicit_padded", implicit_fwd(PD)),
+                   ("wgrad_implicit_padded", implicit_wgrad(PD))]
     if only is not None and only not in [r[0] for r in routes] + ["im2col"]:
         raise SystemExit("unknown route %r for %s" % (only, name))
     for label, fn in routes:
@@ -372,7 +382,8 @@ def main() -> int:
                          "passes) and print its result")
     ap.add_argument("--conv-route", default=None, metavar="ROUTE",
                     help="with --conv: time only this route (fwd, wgrad, fwd_implicit, "
-                         "wgrad_implicit, fwd_implicit_table, wgrad_implicit_table, im2col), "
+                         "wgrad_implicit, fwd_implicit_table, wgrad_implicit_table, "
+                         "fwd_implicit_padded, wgrad_implicit_padded, im2col), "
                          "for per-route profiler passes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference kernel "

@@ -75,7 +75,7 @@ SIGNATURES.update({
     "conv2d_bwd_weight_implicit_ex": (_int, [_int, _pp, _int, _p, _p, _p, _p]),
 })
 
-CONV_ADDR_DEFAULT, CONV_ADDR_ANALYTIC, CONV_ADDR_TABLE = 0, 1, 2
+CONV_ADDR_DEFAULT, CONV_ADDR_ANALYTIC, CONV_ADDR_TABLE, CONV_ADDR_PADDED = 0, 1, 2, 3
 
 
 class ConvNdParams(ctypes.Structure):
@@ -94,6 +94,8 @@ SIGNATURES.update({
     "convnd_bwd_weight": (_int, [_int, _pnd, _p, _p, _p, _p, _i64, _p]),
     "convnd_fwd_implicit": (_int, [_int, _int, _pnd, _p, _p, _p, _p]),
     "convnd_bwd_weight_implicit": (_int, [_int, _pnd, _p, _p, _p, _p]),
+    "convnd_fwd_implicit_ex": (_int, [_int, _int, _pnd, _int, _p, _p, _p, _p]),
+    "convnd_bwd_weight_implicit_ex": (_int, [_int, _pnd, _int, _p, _p, _p, _p]),
 })
 
 _lib = None
@@ -364,6 +366,16 @@ def convnd_bwd_weight_implicit(dtype, params, x, dy, dw, stream=None) -> int:
     return load_library().convnd_bwd_weight_implicit(dtype, ctypes.byref(params), x, dy, dw, stream)
 
 
+def convnd_fwd_implicit_ex(dtype, dtype_y, params, addressing, x, w, y, stream=None) -> int:
+    return load_library().convnd_fwd_implicit_ex(dtype, dtype_y, ctypes.byref(params), addressing,
+                                                 x, w, y, stream)
+
+
+def convnd_bwd_weight_implicit_ex(dtype, params, addressing, x, dy, dw, stream=None) -> int:
+    return load_library().convnd_bwd_weight_implicit_ex(dtype, ctypes.byref(params), addressing,
+                                                        x, dy, dw, stream)
+
+
 def _pair(v):
     return (v, v) if isinstance(v, int) else tuple(v)
 
@@ -400,7 +412,8 @@ def _workspace(workspace, need, device):
     return workspace
 
 
-_ADDRESSING = {True: CONV_ADDR_DEFAULT, "analytic": CONV_ADDR_ANALYTIC, "table": CONV_ADDR_TABLE}
+_ADDRESSING = {True: CONV_ADDR_DEFAULT, "analytic": CONV_ADDR_ANALYTIC, "table": CONV_ADDR_TABLE,
+               "padded": CONV_ADDR_PADDED}
 
 
 def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None,
@@ -408,7 +421,7 @@ def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None
     """y = conv2d(x, w) (cross-correlation form, as torch.nn.functional.conv2d)
     through the im2col + GEMM path, or with ``implicit`` through the
     implicit-GEMM path (no convolution matrix): True (the library's address
-    generation), "analytic" or "table".  x (N, C_in, H, W) and w
+    generation), "analytic", "table" or "padded".  x (N, C_in, H, W) and w
     (C_out, C_in, R, S) are both float32 or both bfloat16; y is float32
     (default) or bfloat16.  The im2col workspace (one image's convolution
     matrix) is allocated when not given."""
@@ -437,7 +450,8 @@ def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wor
                        stream=None, implicit=False):
     """dw (float32, weight_shape) = the filter gradient of conv2d for input x
     and output gradient dy, through the im2col + GEMM path (or, with
-    ``implicit`` -- True, "analytic" or "table" -- the implicit-GEMM path)."""
+    ``implicit`` -- True, "analytic", "table" or "padded" -- the implicit-GEMM
+    path)."""
     import torch
     params, dtype, P, Q, need = _conv_setup(x, tuple(weight_shape), stride, padding, dilation)
     if dy.dtype != x.dtype or not dy.is_contiguous() or \
@@ -484,7 +498,8 @@ def conv_nd(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=Non
     """y = convolution of x (N, C_in, S_0 .. S_{D-1}) with w (C_out, C_in,
     K_0 .. K_{D-1}), D = 1 to 4 (cross-correlation form, as torch's conv1d /
     conv2d / conv3d), through the im2col + GEMM path, or with ``implicit``
-    (D <= 3) the implicit GEMM.  x and w are both float32 or both bfloat16; y
+    (D <= 3) the implicit GEMM (True: the library's address generation,
+    "analytic" or "padded").  x and w are both float32 or both bfloat16; y
     is float32 (default) or bfloat16."""
     import torch
     if w.dtype != x.dtype or not w.is_contiguous():
@@ -496,8 +511,8 @@ def conv_nd(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=Non
         stream = torch.cuda.current_stream(x.device).cuda_stream
     dtype_y = GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32
     if implicit:
-        rc = convnd_fwd_implicit(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
-                                 stream)
+        rc = convnd_fwd_implicit_ex(dtype, dtype_y, params, _ADDRESSING[implicit], x.data_ptr(),
+                                    w.data_ptr(), y.data_ptr(), stream)
     else:
         ws = _workspace(workspace, need, x.device)
         rc = convnd_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
@@ -511,7 +526,8 @@ def conv_nd_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wo
                         stream=None, implicit=False):
     """dw (float32, weight_shape) = the filter gradient of conv_nd for input x
     and output gradient dy, through the im2col + GEMM path (or, with
-    ``implicit`` and D <= 3, the implicit GEMM)."""
+    ``implicit`` -- True, "analytic" or "padded" -- and D <= 3, the implicit
+    GEMM)."""
     import torch
     params, dtype, out, need = _convnd_setup(x, tuple(weight_shape), stride, padding, dilation)
     if dy.dtype != x.dtype or not dy.is_contiguous() or \
@@ -521,8 +537,8 @@ def conv_nd_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wo
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     if implicit:
-        rc = convnd_bwd_weight_implicit(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                                        stream)
+        rc = convnd_bwd_weight_implicit_ex(dtype, params, _ADDRESSING[implicit], x.data_ptr(),
+                                           dy.data_ptr(), dw.data_ptr(), stream)
     else:
         ws = _workspace(workspace, need, x.device)
         rc = convnd_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),

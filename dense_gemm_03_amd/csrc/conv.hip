@@ -34,7 +34,6 @@ constexpr int64_t kMaxElems = int64_t(1) << 62;
 constexpr int kThreads = 256;
 constexpr int kEpt = 4;                            // elements per thread and tap
 constexpr int64_t kLdAlign = 8;                    // matrix rows padded to 16 bytes (bf16)
-constexpr bool kDefaultTable = false;              // addressing of the plain implicit calls
 
 // Geometry of one image's convolution matrix with D spatial dimensions, the
 // last one innermost (contiguous in memory).  Matrix row (ci, k_0 .. k_{D-1})
@@ -521,28 +520,11 @@ bool table_fits(const Dims &d, bool fwd)
            (d.out[1] - 1) * d.stride[1] - d.pad[1] <= hi;
 }
 
-// Addressing of one implicit call: the bsrc to launch with, after building
-// the table when it is used.  CONV_ADDR_DEFAULT takes the table form when the
-// geometry fits it.
-int implicit_source(const Dims &d, int esize, int addressing, bool fwd, ConvGeom *geom,
-                    hipStream_t stream, int *bsrc)
+// Table addressing of one implicit call: writes the per-k terms into the
+// library's table buffer for this stream, points the geometry at it and
+// gives the bsrc to launch with.  The caller has checked table_fits.
+int table_source(int esize, bool fwd, ConvGeom *geom, hipStream_t stream, int *bsrc)
 {
-    const bool fits16 = table_fits(d, fwd);
-    bool table;
-    if (addressing == CONV_ADDR_ANALYTIC)
-        table = false;
-    else if (addressing == CONV_ADDR_TABLE)
-        table = true;
-    else if (addressing == CONV_ADDR_DEFAULT)
-        table = fits16 && kDefaultTable;
-    else
-        return GEMM_ERR_INVALID_ARG;
-    if (table && !fits16) return GEMM_ERR_INVALID_ARG;
-    geom->tab = nullptr;
-    if (!table) {
-        *bsrc = fwd ? B_CONV_FWD : B_CONV_WGRAD;
-        return GEMM_OK;
-    }
     const int count = fwd ? geom->crs : geom->pq;
     void *buf = nullptr;
     const int rc = conv_table_buffer(stream, (size_t)count * sizeof(int2), &buf);
@@ -553,6 +535,144 @@ int implicit_source(const Dims &d, int esize, int addressing, bool fwd, ConvGeom
     if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
     geom->tab = static_cast<const int2 *>(buf);
     *bsrc = fwd ? B_CONV_FWD_TAB : B_CONV_WGRAD_TAB;
+    return GEMM_OK;
+}
+
+int zero_dw(int dtype, const Dims &d, float *dw, hipStream_t stream);
+
+// Zero-padded copy of one image for the padded implicit sources: dst
+// [C][D + 2 pz][H + 2 ph][W + 2 pw] (D = 1, pz = 0 for 2-D) holds the image
+// with zero borders, so that every position a tile touches lies inside it.
+// One element per thread, consecutive threads along the padded rows.
+template <int ESIZE>
+__global__ void __launch_bounds__(kThreads) conv_pad_kernel(const void *src, void *dst, int total,
+                                                            int d, int h, int w, int pz, int ph,
+                                                            int pw, int dp, int hp, int wp)
+{
+    typedef typename Word<ESIZE>::T T;
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= total) return;
+    const int xp = i % wp;
+    int t = i / wp;
+    const int yp = t % hp;
+    t /= hp;
+    const int zp = t % dp;
+    const int c = t / dp;
+    const int z = zp - pz, y = yp - ph, x = xp - pw;
+    const bool in = ((unsigned)z < (unsigned)d) & ((unsigned)y < (unsigned)h) & ((unsigned)x < (unsigned)w);
+    const T *s = static_cast<const T *>(src);
+    static_cast<T *>(dst)[i] = in ? s[((int64_t)(c * d + z) * h + y) * w + x] : T(0);
+}
+
+// Spatial dimensions of the padded implicit sources: depth (1 for 2-D), rows,
+// columns, and their paddings, before and after padding.
+struct PadDims {
+    int d, h, w, pz, ph, pw, dp, hp, wp;
+};
+
+PadDims pad_dims(const Dims &d)
+{
+    const int lead = 3 - (int)d.nd;  // 2-D: one leading unit dimension
+    auto at = [&](const int64_t *v, int i, int64_t unit) {
+        return (int)(i < lead ? unit : v[i - lead]);
+    };
+    PadDims p;
+    p.d = at(d.size, 0, 1);
+    p.h = at(d.size, 1, 1);
+    p.w = at(d.size, 2, 1);
+    p.pz = at(d.pad, 0, 0);
+    p.ph = at(d.pad, 1, 0);
+    p.pw = at(d.pad, 2, 0);
+    p.dp = p.d + 2 * p.pz;
+    p.hp = p.h + 2 * p.ph;
+    p.wp = p.w + 2 * p.pw;
+    return p;
+}
+
+// Bytes of one padded image (C_in times the padded volume), or -1 when it
+// would reach 2 GiB (buffer offsets are signed 32-bit).
+int64_t padded_bytes(const Dims &d, int esize)
+{
+    const PadDims p = pad_dims(d);
+    const int64_t elems = d.c * (int64_t)p.dp * p.hp * p.wp;
+    return elems * esize < (int64_t(1) << 31) ? elems * esize : -1;
+}
+
+// One implicit-GEMM convolution call (2-D or volume), forward (a = w, out = y)
+// or filter gradient (a = dy, out = dw, fp32): checks, addressing, per-image
+// GEMMs.  CONV_ADDR_DEFAULT takes the padded form when the padded image fits,
+// else the analytic one; the table form is 2-D only.
+int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool fwd, bool vol,
+                 const void *x, const void *a, void *out, hipStream_t stream)
+{
+    const int es = elem_size(dtype), eso = elem_size(dtype_out);
+    if (fwd && d.n == 0) return GEMM_OK;
+    if (out == nullptr || !aligned_to(out, eso)) return GEMM_ERR_INVALID_ARG;
+    if (d.n == 0) return zero_dw(dtype, d, static_cast<float *>(out), stream);
+    if (x == nullptr || a == nullptr || !aligned_to(x, es) || !aligned_to(a, es))
+        return GEMM_ERR_INVALID_ARG;
+    ConvGeom geom{};
+    int rc = vol ? make_geom3(d, es, &geom) : make_geom(d, es, &geom);
+    if (rc != GEMM_OK) return rc;
+    const int64_t pbytes = padded_bytes(d, es);
+    int mode = addressing;
+    if (mode == CONV_ADDR_DEFAULT) mode = pbytes > 0 ? CONV_ADDR_PADDED : CONV_ADDR_ANALYTIC;
+    if ((mode == CONV_ADDR_PADDED && pbytes < 0) ||
+        (mode == CONV_ADDR_TABLE && (vol || !table_fits(d, fwd))))
+        return GEMM_ERR_INVALID_ARG;
+    if ((rc = device_ok()) != GEMM_OK) return rc;
+    int bsrc;
+    void *padded = nullptr;
+    const PadDims pd = pad_dims(d);
+    if (mode == CONV_ADDR_TABLE) {
+        if ((rc = table_source(es, fwd, &geom, stream, &bsrc)) != GEMM_OK) return rc;
+    } else if (mode == CONV_ADDR_PADDED) {
+        if ((rc = conv_padded_buffer(stream, (size_t)pbytes, &padded)) != GEMM_OK) return rc;
+        // the loaders read the padded image: no padding left to apply
+        if (vol) {
+            geom.d = pd.dp;
+            geom.pz = 0;
+        }
+        geom.h = pd.hp;
+        geom.w = pd.wp;
+        geom.ph = 0;
+        geom.pw = 0;
+        geom.img_bytes = (int)pbytes;
+        geom.tab = nullptr;
+        bsrc = vol ? (fwd ? B_CONV3_FWD_PAD : B_CONV3_WGRAD_PAD)
+                   : (fwd ? B_CONV_FWD_PAD : B_CONV_WGRAD_PAD);
+    } else {
+        geom.tab = nullptr;
+        bsrc = vol ? (fwd ? B_CONV3_FWD : B_CONV3_WGRAD) : (fwd ? B_CONV_FWD : B_CONV_WGRAD);
+    }
+    const int64_t vo = d.vol_out();
+    const int total = (int)(pbytes > 0 ? pbytes / es : 0);
+    for (int64_t n = 0; n < d.n; ++n) {
+        const void *img = static_cast<const char *>(x) + n * d.c * d.img_elems() * es;
+        if (padded != nullptr) {
+            const dim3 grid((unsigned)((total + kThreads - 1) / kThreads)), block(kThreads);
+            if (es == 4)
+                hipLaunchKernelGGL(conv_pad_kernel<4>, grid, block, 0, stream, img, padded, total,
+                                   pd.d, pd.h, pd.w, pd.pz, pd.ph, pd.pw, pd.dp, pd.hp, pd.wp);
+            else
+                hipLaunchKernelGGL(conv_pad_kernel<2>, grid, block, 0, stream, img, padded, total,
+                                   pd.d, pd.h, pd.w, pd.pz, pd.ph, pd.pw, pd.dp, pd.hp, pd.wp);
+            if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+            img = padded;
+        }
+        GemmCall g;
+        if (fwd)
+            // y[n] (C_out x output volume) = w (C_out x C_in filter volume) . cols(x[n])
+            g = GemmCall{dtype, dtype_out, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f,
+                         a, d.crs(), img, 1, static_cast<char *>(out) + n * d.k * vo * eso, vo,
+                         bsrc, &geom};
+        else
+            // dw (C_out x C_in filter volume) (+)= dy[n] (C_out x output volume) . cols(x[n])^T
+            g = GemmCall{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
+                         n == 0 ? 0.0f : 1.0f, static_cast<const char *>(a) + n * d.k * vo * es,
+                         vo, img, 1, out, d.crs(), bsrc, &geom};
+        if ((rc = gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
     return GEMM_OK;
 }
 
@@ -691,30 +811,10 @@ int conv2d_fwd_implicit_ex(int dtype, int dtype_y, const conv2d_params *p, int a
 {
     dg::Dims d;
     if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::dims_2d(p, &d);
+    const int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_TABLE) return GEMM_ERR_INVALID_ARG;
-    if (d.n == 0) return GEMM_OK;
-    const int es = dg::elem_size(dtype), esy = dg::elem_size(dtype_y);
-    if (x == nullptr || w == nullptr || y == nullptr || !dg::aligned_to(x, es) ||
-        !dg::aligned_to(w, es) || !dg::aligned_to(y, esy))
-        return GEMM_ERR_INVALID_ARG;
-    dg::ConvGeom geom;
-    if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
-    if (addressing == CONV_ADDR_TABLE && !dg::table_fits(d, true)) return GEMM_ERR_INVALID_ARG;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    int bsrc = 0;
-    if ((rc = dg::implicit_source(d, es, addressing, true, &geom, stream, &bsrc)) != GEMM_OK)
-        return rc;
-    const int64_t vo = d.vol_out();
-    for (int64_t n = 0; n < d.n; ++n) {
-        // y[n] (C_out x PQ) = w (C_out x C_in R S) . cols(x[n]), cols formed in the loader
-        dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f,
-                       w, d.crs(), static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1,
-                       static_cast<char *>(y) + n * d.k * vo * esy, vo, bsrc, &geom};
-        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
-    }
-    return GEMM_OK;
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED) return GEMM_ERR_INVALID_ARG;
+    return dg::run_implicit(dtype, dtype_y, d, addressing, true, false, x, w, y, stream);
 }
 
 int conv2d_fwd_implicit(int dtype, int dtype_y, const conv2d_params *p, const void *x,
@@ -728,31 +828,10 @@ int conv2d_bwd_weight_implicit_ex(int dtype, const conv2d_params *p, int address
 {
     dg::Dims d;
     if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::dims_2d(p, &d);
+    const int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_TABLE) return GEMM_ERR_INVALID_ARG;
-    const int es = dg::elem_size(dtype);
-    if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
-    if (d.n == 0) return dg::zero_dw(dtype, d, dw, stream);
-    if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
-        return GEMM_ERR_INVALID_ARG;
-    dg::ConvGeom geom;
-    if ((rc = dg::make_geom(d, es, &geom)) != GEMM_OK) return rc;
-    if (addressing == CONV_ADDR_TABLE && !dg::table_fits(d, false)) return GEMM_ERR_INVALID_ARG;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    int bsrc = 0;
-    if ((rc = dg::implicit_source(d, es, addressing, false, &geom, stream, &bsrc)) != GEMM_OK)
-        return rc;
-    const int64_t vo = d.vol_out();
-    for (int64_t n = 0; n < d.n; ++n) {
-        // dw (C_out x C_in R S) (+)= dy[n] (C_out x PQ) . cols(x[n])^T
-        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
-                       n == 0 ? 0.0f : 1.0f, static_cast<const char *>(dy) + n * d.k * vo * es, vo,
-                       static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1, dw, d.crs(),
-                       bsrc, &geom};
-        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
-    }
-    return GEMM_OK;
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED) return GEMM_ERR_INVALID_ARG;
+    return dg::run_implicit(dtype, GEMM_DTYPE_F32, d, addressing, false, false, x, dy, dw, stream);
 }
 
 int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x, const void *dy,
@@ -806,59 +885,42 @@ int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const vo
                          : dg::bwd_weight(dtype, d, x, dy, dw, workspace, workspace_bytes, stream);
 }
 
-int convnd_fwd_implicit(int dtype, int dtype_y, const convnd_params *p, const void *x,
-                        const void *w, void *y, hipStream_t stream)
+int convnd_fwd_implicit_ex(int dtype, int dtype_y, const convnd_params *p, int addressing,
+                           const void *x, const void *w, void *y, hipStream_t stream)
 {
     dg::Dims d;
     if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::dims_nd(p, &d);
+    const int rc = dg::dims_nd(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (d.nd > 3) return GEMM_ERR_INVALID_ARG;
-    if (d.n == 0) return GEMM_OK;
-    const int es = dg::elem_size(dtype), esy = dg::elem_size(dtype_y);
-    if (x == nullptr || w == nullptr || y == nullptr || !dg::aligned_to(x, es) ||
-        !dg::aligned_to(w, es) || !dg::aligned_to(y, esy))
+    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED ||
+        addressing == CONV_ADDR_TABLE)
         return GEMM_ERR_INVALID_ARG;
-    dg::ConvGeom geom;
-    if ((rc = dg::make_geom3(d, es, &geom)) != GEMM_OK) return rc;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    const int64_t vo = d.vol_out();
-    for (int64_t n = 0; n < d.n; ++n) {
-        // y[n] (C_out x output volume) = w (C_out x C_in filter volume) . cols(x[n])
-        dg::GemmCall g{dtype, dtype_y, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f,
-                       w, d.crs(), static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1,
-                       static_cast<char *>(y) + n * d.k * vo * esy, vo, dg::B_CONV3_FWD, &geom};
-        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
-    }
-    return GEMM_OK;
+    return dg::run_implicit(dtype, dtype_y, d, addressing, true, true, x, w, y, stream);
+}
+
+int convnd_fwd_implicit(int dtype, int dtype_y, const convnd_params *p, const void *x,
+                        const void *w, void *y, hipStream_t stream)
+{
+    return convnd_fwd_implicit_ex(dtype, dtype_y, p, CONV_ADDR_DEFAULT, x, w, y, stream);
+}
+
+int convnd_bwd_weight_implicit_ex(int dtype, const convnd_params *p, int addressing,
+                                  const void *x, const void *dy, float *dw, hipStream_t stream)
+{
+    dg::Dims d;
+    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
+    const int rc = dg::dims_nd(p, &d);
+    if (rc != GEMM_OK) return rc;
+    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED ||
+        addressing == CONV_ADDR_TABLE)
+        return GEMM_ERR_INVALID_ARG;
+    return dg::run_implicit(dtype, GEMM_DTYPE_F32, d, addressing, false, true, x, dy, dw, stream);
 }
 
 int convnd_bwd_weight_implicit(int dtype, const convnd_params *p, const void *x, const void *dy,
                                float *dw, hipStream_t stream)
 {
-    dg::Dims d;
-    if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
-    int rc = dg::dims_nd(p, &d);
-    if (rc != GEMM_OK) return rc;
-    if (d.nd > 3) return GEMM_ERR_INVALID_ARG;
-    const int es = dg::elem_size(dtype);
-    if (dw == nullptr || !dg::aligned_to(dw, 4)) return GEMM_ERR_INVALID_ARG;
-    if (d.n == 0) return dg::zero_dw(dtype, d, dw, stream);
-    if (x == nullptr || dy == nullptr || !dg::aligned_to(x, es) || !dg::aligned_to(dy, es))
-        return GEMM_ERR_INVALID_ARG;
-    dg::ConvGeom geom;
-    if ((rc = dg::make_geom3(d, es, &geom)) != GEMM_OK) return rc;
-    if ((rc = dg::device_ok()) != GEMM_OK) return rc;
-    const int64_t vo = d.vol_out();
-    for (int64_t n = 0; n < d.n; ++n) {
-        // dw (C_out x C_in filter volume) (+)= dy[n] (C_out x output volume) . cols(x[n])^T
-        dg::GemmCall g{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
-                       n == 0 ? 0.0f : 1.0f, static_cast<const char *>(dy) + n * d.k * vo * es, vo,
-                       static_cast<const char *>(x) + n * d.c * d.img_elems() * es, 1, dw, d.crs(),
-                       dg::B_CONV3_WGRAD, &geom};
-        if ((rc = dg::gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
-    }
-    return GEMM_OK;
+    return convnd_bwd_weight_implicit_ex(dtype, p, CONV_ADDR_DEFAULT, x, dy, dw, stream);
 }
 
 }  // extern "C"

@@ -40,9 +40,10 @@ struct TileConfig {
     // implicit-GEMM convolution kernels (B tiles formed from an image),
     // indexed by B source - 1: [0] forward (B = cols), [1] filter gradient
     // (B = cols^T), [2] / [3] the same with table-looked-up per-k terms,
-    // [4] / [5] the volume (3-D) forms; [aligned], as fn.  nullptr where the
-    // entry has none.
-    launch_fn implicit[6][2];
+    // [4] / [5] the volume (3-D) forms, [6] .. [9] the 2-D and volume forms
+    // reading a zero-padded image; [aligned], as fn.  nullptr where the entry
+    // has none.
+    launch_fn implicit[10][2];
 };
 
 // Declared here; defined in gemm_launch.hpp and explicitly instantiated by the
@@ -73,6 +74,18 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_LB_C3W ::dg::KMAJOR
 #define DG_BSRC_C3F ::dg::B_CONV3_FWD
 #define DG_BSRC_C3W ::dg::B_CONV3_WGRAD
+#define DG_LA_CFP ::dg::KMAJOR
+#define DG_LB_CFP ::dg::MNMAJOR
+#define DG_LA_CWP ::dg::KMAJOR
+#define DG_LB_CWP ::dg::KMAJOR
+#define DG_LA_C3FP ::dg::KMAJOR
+#define DG_LB_C3FP ::dg::MNMAJOR
+#define DG_LA_C3WP ::dg::KMAJOR
+#define DG_LB_C3WP ::dg::KMAJOR
+#define DG_BSRC_CFP ::dg::B_CONV_FWD_PAD
+#define DG_BSRC_CWP ::dg::B_CONV_WGRAD_PAD
+#define DG_BSRC_C3FP ::dg::B_CONV3_FWD_PAD
+#define DG_BSRC_C3WP ::dg::B_CONV3_WGRAD_PAD
 
 // Memory orientation of op(A) / op(B) per layout combination: A as given is
 // k-contiguous, A^T (stored K x M) outer-contiguous; B as given is
@@ -171,8 +184,12 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_IMPL_CONV(BF16, BM, BN, BK, WM, WN)                                                \
     {DG_IFNS(BF16, BM, BN, BK, WM, WN, CF), DG_IFNS(BF16, BM, BN, BK, WM, WN, CW),              \
      DG_IFNS(BF16, BM, BN, BK, WM, WN, CFT), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWT),            \
-     DG_IFNS(BF16, BM, BN, BK, WM, WN, C3F), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3W)}
-#define DG_IMPL_NONE {DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS}
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, C3F), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3W),            \
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFP), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWP),            \
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, C3FP), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3WP)}
+#define DG_IMPL_NONE                                                                          \
+    {DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, \
+     DG_NOFNS}
 #define DG_IMPL_ALL(...) DG_IMPL_NONE
 #define DG_IMPL_NN(...) DG_IMPL_NONE
 #define DG_IMPL_SKINNY(...) DG_IMPL_NONE

@@ -39,5 +39,7 @@ int gemm_run(const GemmCall &call, int forced_cfg, int forced_split, hipStream_t
 // unloaded and is reused by the next call on that stream, so the work that
 // reads it must be enqueued on `stream`.  Returns a gemm_status.
 int conv_table_buffer(hipStream_t stream, size_t bytes, void **out);
+// The same for the zero-padded image of the implicit GEMM.
+int conv_padded_buffer(hipStream_t stream, size_t bytes, void **out);
 
 }  // namespace dg

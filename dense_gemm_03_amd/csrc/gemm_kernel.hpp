@@ -90,14 +90,27 @@ enum BSource {
     // taps (ci, t, r, s), output positions (o, p, q).
     B_CONV3_FWD = 5,
     B_CONV3_WGRAD = 6,
+    // The analytic 2-D and volume forms reading a zero-padded copy of the
+    // image: every position a tile touches lies inside it, so the loader
+    // makes no range checks (the geometry describes the padded image, with
+    // no padding).
+    B_CONV_FWD_PAD = 7,
+    B_CONV_WGRAD_PAD = 8,
+    B_CONV3_FWD_PAD = 9,
+    B_CONV3_WGRAD_PAD = 10,
 };
 
 __host__ __device__ constexpr bool conv_fwd_source(int b)
 {
-    return b == B_CONV_FWD || b == B_CONV_FWD_TAB || b == B_CONV3_FWD;
+    return b == B_CONV_FWD || b == B_CONV_FWD_TAB || b == B_CONV3_FWD || b == B_CONV_FWD_PAD ||
+           b == B_CONV3_FWD_PAD;
 }
 __host__ __device__ constexpr bool conv_table_source(int b) { return b == B_CONV_FWD_TAB || b == B_CONV_WGRAD_TAB; }
-__host__ __device__ constexpr bool conv_volume_source(int b) { return b == B_CONV3_FWD || b == B_CONV3_WGRAD; }
+__host__ __device__ constexpr bool conv_volume_source(int b)
+{
+    return b == B_CONV3_FWD || b == B_CONV3_WGRAD || b == B_CONV3_FWD_PAD || b == B_CONV3_WGRAD_PAD;
+}
+__host__ __device__ constexpr bool conv_padded_source(int b) { return b >= B_CONV_FWD_PAD && b <= B_CONV3_WGRAD_PAD; }
 
 // Geometry of the convolution behind an implicit op(B), for one image
 // [C_in][H][W]: matrix row (ci R + r) S + s, column p Q + q holds
@@ -747,6 +760,7 @@ struct ConvGather {
     static constexpr bool FWD = conv_fwd_source(MODE);
     static constexpr bool TAB = conv_table_source(MODE);
     static constexpr bool VOL = conv_volume_source(MODE);
+    static constexpr bool PAD = conv_padded_source(MODE);
     static constexpr int ES = (int)sizeof(In);
     static_assert(T::NT % T::CPR == 0, "a thread's chunks must share their columns");
     static_assert((FWD && T::LAYOUT == MNMAJOR) || (!FWD && T::LAYOUT == KMAJOR),
@@ -882,6 +896,7 @@ struct ConvGather {
     // compares joined without short-circuits.
     __device__ __forceinline__ bool inside(int z, int y, int x) const
     {
+        if constexpr (PAD) return true;  // the padded image holds every position
         bool in = ((unsigned)y < (unsigned)g->h) & ((unsigned)x < (unsigned)g->w);
         if constexpr (VOL) in = in & ((unsigned)z < (unsigned)g->d);
         return in;
@@ -937,7 +952,7 @@ struct ConvGather {
                 const Term &t = kt[u];
                 const bool whole = run & kok[u] &
                                    inside(f[0].z + t.z, f[0].y + t.y, f[0].x + t.x) &
-                                   (f[V - 1].x + t.x < g->w);
+                                   (PAD || f[V - 1].x + t.x < g->w);
                 if (whole) {
                     r[u] = load_run(f[0].o + t.o);
                 } else {
@@ -954,7 +969,7 @@ struct ConvGather {
                 const Term &t = f[u];
                 const bool whole = krun & fok[u] &
                                    inside(t.z + kt[0].z, t.y + kt[0].y, t.x + kt[0].x) &
-                                   (t.x + kt[V - 1].x < g->w);
+                                   (PAD || t.x + kt[V - 1].x < g->w);
                 if (whole) {
                     r[u] = load_run(t.o + kt[0].o);
                 } else {

@@ -1,9 +1,9 @@
 // Definition of the kernel launcher and the explicit instantiation of one
 // operand layout's kernels from the tile lists.  Included by the per-layout
 // source files, each of which defines DG_DTYPE_TABLE (the list), DG_LAYOUT
-// (NN, NT, TN, TT, or CF / CW / CFT / CWT / C3F / C3W for the implicit-GEMM
-// convolution kernels: forward / filter gradient, analytic / table-looked-up
-// terms, volume) and
+// (NN, NT, TN, TT, or CF / CW / CFT / CWT / C3F / C3W / CFP / CWP / C3FP /
+// C3WP for the implicit-GEMM convolution kernels: forward / filter gradient,
+// analytic / table-looked-up terms, volume, padded image) and
 // then includes this header.
 #pragma once
 
@@ -48,6 +48,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_ALL_CWT(...)
 #define DG_INST_ALL_C3F(...)
 #define DG_INST_ALL_C3W(...)
+#define DG_INST_ALL_CFP(...)
+#define DG_INST_ALL_CWP(...)
+#define DG_INST_ALL_C3FP(...)
+#define DG_INST_ALL_C3WP(...)
 #define DG_INST_CONV_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_CONV_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_CONV_TN(...) DG_INST(__VA_ARGS__, TN)
@@ -58,6 +62,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_CONV_CWT(...) DG_IINST(__VA_ARGS__, CWT)
 #define DG_INST_CONV_C3F(...) DG_IINST(__VA_ARGS__, C3F)
 #define DG_INST_CONV_C3W(...) DG_IINST(__VA_ARGS__, C3W)
+#define DG_INST_CONV_CFP(...) DG_IINST(__VA_ARGS__, CFP)
+#define DG_INST_CONV_CWP(...) DG_IINST(__VA_ARGS__, CWP)
+#define DG_INST_CONV_C3FP(...) DG_IINST(__VA_ARGS__, C3FP)
+#define DG_INST_CONV_C3WP(...) DG_IINST(__VA_ARGS__, C3WP)
 #define DG_INST_SKINNYC_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_SKINNYC_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_SKINNYC_TN(...)
@@ -68,6 +76,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_SKINNYC_CWT(...) DG_IINST(__VA_ARGS__, CWT)
 #define DG_INST_SKINNYC_C3F(...) DG_IINST(__VA_ARGS__, C3F)
 #define DG_INST_SKINNYC_C3W(...) DG_IINST(__VA_ARGS__, C3W)
+#define DG_INST_SKINNYC_CFP(...) DG_IINST(__VA_ARGS__, CFP)
+#define DG_INST_SKINNYC_CWP(...) DG_IINST(__VA_ARGS__, CWP)
+#define DG_INST_SKINNYC_C3FP(...) DG_IINST(__VA_ARGS__, C3FP)
+#define DG_INST_SKINNYC_C3WP(...) DG_IINST(__VA_ARGS__, C3WP)
 #define DG_INST_SKINNY_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_SKINNY_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_SKINNY_TN(...)
@@ -78,6 +90,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_SKINNY_CWT(...)
 #define DG_INST_SKINNY_C3F(...)
 #define DG_INST_SKINNY_C3W(...)
+#define DG_INST_SKINNY_CFP(...)
+#define DG_INST_SKINNY_CWP(...)
+#define DG_INST_SKINNY_C3FP(...)
+#define DG_INST_SKINNY_C3WP(...)
 #define DG_INST_KK_NN(...)
 #define DG_INST_KK_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_KK_TN(...)
@@ -88,6 +104,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_KK_CWT(...)
 #define DG_INST_KK_C3F(...)
 #define DG_INST_KK_C3W(...)
+#define DG_INST_KK_CFP(...)
+#define DG_INST_KK_CWP(...)
+#define DG_INST_KK_C3FP(...)
+#define DG_INST_KK_C3WP(...)
 #define DG_INST_NN_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_NN_NT(...)
 #define DG_INST_NN_TN(...)
@@ -98,6 +118,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_NN_CWT(...)
 #define DG_INST_NN_C3F(...)
 #define DG_INST_NN_C3W(...)
+#define DG_INST_NN_CFP(...)
+#define DG_INST_NN_CWP(...)
+#define DG_INST_NN_C3FP(...)
+#define DG_INST_NN_C3WP(...)
 #define DG_INST_SEL2(LAYOUTS, L) DG_INST_##LAYOUTS##_##L
 #define DG_INST_SEL(LAYOUTS, L) DG_INST_SEL2(LAYOUTS, L)
 #define DG_INST_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                            \

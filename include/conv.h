@@ -126,11 +126,24 @@ int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x,
  *     Needs the y and x terms within signed 16 bits: (R-1) dh and (S-1) dw
  *     for the forward product, ph, pw and the last output's p sh - ph,
  *     q sw - pw for the filter gradient (GEMM_ERR_INVALID_ARG otherwise);
+ *   CONV_ADDR_PADDED: before each batch element's product a small kernel
+ *     copies its image into a library-owned buffer (one per device and
+ *     stream, kept for later calls) with zero borders of the padding's
+ *     width, [C_in][H + 2 ph][W + 2 pw]; the loader then reads that copy with
+ *     the analytic terms and no padding, so no element needs a range check.
+ *     Needs the padded image under 2 GiB (GEMM_ERR_INVALID_ARG otherwise);
+ *     costs one extra read and write of the image per call;
  *   CONV_ADDR_DEFAULT: the library's choice (what conv2d_fwd_implicit and
- *     conv2d_bwd_weight_implicit use).
- * Both give identical results (same products, same summation order).
+ *     conv2d_bwd_weight_implicit use): the padded form when the padded image
+ *     fits, else the analytic one.
+ * All give identical results (same products, same summation order).
  */
-typedef enum { CONV_ADDR_DEFAULT = 0, CONV_ADDR_ANALYTIC = 1, CONV_ADDR_TABLE = 2 } conv_addressing;
+typedef enum {
+    CONV_ADDR_DEFAULT = 0,
+    CONV_ADDR_ANALYTIC = 1,
+    CONV_ADDR_TABLE = 2,
+    CONV_ADDR_PADDED = 3
+} conv_addressing;
 
 int conv2d_fwd_implicit_ex(int dtype, int dtype_y, const conv2d_params *p, int addressing,
                            const void *x, const void *w, void *y, hipStream_t stream);
@@ -196,11 +209,19 @@ int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const vo
  * address terms (fewer than three dimensions run as three with leading unit
  * dimensions).  Same arguments, layouts, types and results as convnd_fwd /
  * convnd_bwd_weight; GEMM_ERR_INVALID_ARG for ndim 4 and when one batch
- * element of x spans 2 GiB or more. */
+ * element of x spans 2 GiB or more.  The _ex forms take the addressing:
+ * CONV_ADDR_ANALYTIC, CONV_ADDR_PADDED (the image copied with zero borders
+ * in every padded dimension, as for the 2-D calls) or CONV_ADDR_DEFAULT
+ * (padded when the padded image is under 2 GiB, else analytic; what the
+ * plain forms use); CONV_ADDR_TABLE is 2-D only (GEMM_ERR_INVALID_ARG). */
 int convnd_fwd_implicit(int dtype, int dtype_y, const convnd_params *p, const void *x,
                         const void *w, void *y, hipStream_t stream);
 int convnd_bwd_weight_implicit(int dtype, const convnd_params *p, const void *x, const void *dy,
                                float *dw, hipStream_t stream);
+int convnd_fwd_implicit_ex(int dtype, int dtype_y, const convnd_params *p, int addressing,
+                           const void *x, const void *w, void *y, hipStream_t stream);
+int convnd_bwd_weight_implicit_ex(int dtype, const convnd_params *p, int addressing,
+                                  const void *x, const void *dy, float *dw, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 30, names
+    assert len(names) == 32, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -269,8 +269,8 @@ def test_conv_host_logic_and_invalid_arguments():
     assert dg.conv2d_bwd_weight_implicit(BF16, huge, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     # address generation: unknown forms are rejected; the table form needs its
     # y and x terms within signed 16 bits
-    A, T = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE
-    assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, 3, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    A, T, PD = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE, dg.CONV_ADDR_PADDED
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, 4, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, -1, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.conv2d_bwd_weight_implicit_ex(F32, ok, 7, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     wide = P(1, 1, 40001, 8, 1, 3, 1, (0, 0), (1, 1), (20000, 1))   # (R-1) dh = 40000
@@ -279,6 +279,12 @@ def test_conv_host_logic_and_invalid_arguments():
     tall = P(1, 1, 70000, 4, 1, 1, 1)                              # last p sh - ph = 69999
     assert dg.conv2d_bwd_weight_implicit_ex(F32, tall, T, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.conv2d_fwd_implicit_ex(F32, F32, bad[0], A, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    # the padded form needs the padded image below 2 GiB: this image is just
+    # under it (2^31 - 2^19 bytes), its copy with 2-wide zero borders is not
+    edge = P(1, 1, 1 << 14, (1 << 15) - 8, 1, 5, 5, (2, 2))
+    assert dg.conv2d_output_size(edge)[0] == dg.GEMM_OK
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, edge, PD, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_bwd_weight_implicit_ex(F32, edge, PD, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     # an empty batch: nothing to compute for the forward
     assert dg.conv2d_fwd(F32, F32, P(0, 3, 10, 9, 4, 3, 2), None, None, None, None, 0) == dg.GEMM_OK
 
@@ -352,3 +358,12 @@ def test_convnd_host_logic_and_invalid_arguments():
     big = N(1, 4, 1, (512, 512, 512), (1, 1, 1))      # 4 x 2^27 fp32 elements: 2 GiB
     assert dg.convnd_fwd_implicit(F32, F32, big, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.convnd_fwd_implicit(F32, F32, N(0, 3, 4, (5,), (3,)), None, None, None) == dg.GEMM_OK
+    # addressing: analytic, padded or the default; the table form is 2-D only
+    for mode in (dg.CONV_ADDR_TABLE, 4, -1):
+        assert dg.convnd_fwd_implicit_ex(F32, F32, ok, mode, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+        assert dg.convnd_bwd_weight_implicit_ex(F32, ok, mode, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    # an image just under 2 GiB whose zero-bordered copy is not
+    edge = N(1, 1, 1, (8, 1 << 12, (1 << 14) - 8), (3, 3, 3), (1, 1, 1))
+    assert dg.convnd_output_size(edge)[0] == dg.GEMM_OK
+    assert dg.convnd_fwd_implicit_ex(F32, F32, edge, dg.CONV_ADDR_PADDED, p, p, p) == \
+        dg.GEMM_ERR_INVALID_ARG

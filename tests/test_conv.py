@@ -12,8 +12,9 @@ direct-convolution oracle, through the C ABI (include/conv.h).
   (1e-5 for fp32, 4e-3 for bf16 inputs), plus half a bf16 unit for bf16 y.
 * The full-size large-kernel convolution at sampled outputs and taps.
 * Each check runs through im2col + GEMM and through the implicit GEMM with
-  both address generations (terms computed in the loader, or looked up in a
-  table); the two implicit forms give identical bits.
+  each address generation (terms computed in the loader, looked up in a
+  table, or computed over a zero-bordered copy of the image with no range
+  checks); the implicit forms give identical bits.
 """
 from __future__ import annotations
 
@@ -30,9 +31,9 @@ from tests.gpu_util import DIAGNOSTIC, TOL, log, to_device
 pytestmark = pytest.mark.gpu
 
 F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
-# im2col + GEMM, and the implicit GEMM with either address generation
-ROUTES = [False, "analytic", "table"]
-ROUTE_IDS = ["im2col", "analytic", "table"]
+# im2col + GEMM, and the implicit GEMM with each address generation
+ROUTES = [False, "analytic", "table", "padded"]
+ROUTE_IDS = ["im2col", "analytic", "table", "padded"]
 
 SHAPES = [
     # batch, cin, h, w, cout, r, s, ph, pw, sh, sw, dh, dw
@@ -276,8 +277,9 @@ def test_full_size_exact_integers_sampled(implicit):
 
 
 def test_implicit_addressing_forms_agree_bitwise():
-    """Analytic and table address generation feed the same products in the
-    same order: identical bits, forward and filter gradient, both types."""
+    """Analytic, table and padded-image address generation feed the same
+    products in the same order: identical bits, forward and filter gradient,
+    both types."""
     import torch
     for t, c in enumerate(SHAPES[1:], 1):
         for bf16 in (False, True):
@@ -286,8 +288,11 @@ def test_implicit_addressing_forms_agree_bitwise():
             kw = dict(stride=(c.sh, c.sw), padding=(c.ph, c.pw), dilation=(c.dh, c.dw))
             ya = dg.conv2d(x, w, implicit="analytic", **kw)
             yt = dg.conv2d(x, w, implicit="table", **kw)
+            yp = dg.conv2d(x, w, implicit="padded", **kw)
             ga = dg.conv2d_weight_grad(x, dy, c.w_shape, implicit="analytic", **kw)
             gt = dg.conv2d_weight_grad(x, dy, c.w_shape, implicit="table", **kw)
+            gp = dg.conv2d_weight_grad(x, dy, c.w_shape, implicit="padded", **kw)
             torch.cuda.synchronize()
             log("addressing forms %s %s" % (c, "bf16" if bf16 else "f32"))
             assert torch.equal(ya, yt) and torch.equal(ga, gt), str(c)
+            assert torch.equal(ya, yp) and torch.equal(ga, gp), str(c)

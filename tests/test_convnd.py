@@ -13,7 +13,9 @@ direct-convolution oracle, through the C ABI (include/conv.h, convnd_*).
 * D = 2 through the N-D entry points gives the conv2d entry points' bits.
 * The full-size 3-D and 4-D workloads at sampled outputs and taps.
 * Forward and filter gradient through im2col + GEMM and, up to three
-  dimensions, through the implicit GEMM (volume tiles formed in the loader).
+  dimensions, through the implicit GEMM (volume tiles formed in the loader,
+  from the image with analytic terms or from a zero-bordered copy of it);
+  the two implicit forms give identical bits.
 """
 from __future__ import annotations
 
@@ -127,8 +129,10 @@ def _shapes(implicit):
     return [(t, c) for t, c in enumerate(SHAPES) if not implicit or c.nd <= 3]
 
 
-ROUTES = [False, True]
-ROUTE_IDS = ["im2col", "implicit"]
+# im2col + GEMM, and the implicit GEMM with analytic terms or over a
+# zero-bordered copy of the image
+ROUTES = [False, "analytic", "padded"]
+ROUTE_IDS = ["im2col", "analytic", "padded"]
 
 
 @pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
@@ -187,6 +191,25 @@ def test_two_dimensions_match_conv2d_bits():
     torch.cuda.synchronize()
     assert torch.equal(y_nd, y_2d) and torch.equal(g_nd, g_2d)
     assert torch.equal(yi_nd, yi_2d) and torch.equal(gi_nd, gi_2d)
+
+
+def test_implicit_addressing_forms_agree_bitwise():
+    """Analytic terms and the padded image feed the same products in the same
+    order: identical bits, forward and filter gradient, both types, for
+    every shape of up to three dimensions."""
+    import torch
+    for t, c in _shapes(True):
+        for bf16 in (False, True):
+            x, w = _dev(_randn(c.x_shape, 700 + t, bf16)), _dev(_randn(c.w_shape, 710 + t, bf16))
+            dy = _dev(_randn(c.y_shape, 720 + t, bf16))
+            kw = dict(stride=c.stride, padding=c.pad, dilation=c.dilation)
+            ya = dg.conv_nd(x, w, implicit="analytic", **kw)
+            yp = dg.conv_nd(x, w, implicit="padded", **kw)
+            ga = dg.conv_nd_weight_grad(x, dy, c.w_shape, implicit="analytic", **kw)
+            gp = dg.conv_nd_weight_grad(x, dy, c.w_shape, implicit="padded", **kw)
+            torch.cuda.synchronize()
+            log("addressing forms %s %s" % (c, "bf16" if bf16 else "f32"))
+            assert torch.equal(ya, yp) and torch.equal(ga, gp), str(c)
 
 
 def test_empty_batch():

@@ -1,6 +1,7 @@
 """The library's calls inside a captured HIP graph: a split-K GEMM (its
 partial-sum workspace and reduce kernel), an im2col + GEMM convolution, and an
 implicit-GEMM convolution with table address terms (its table kernel and
+buffer) and one over the zero-bordered image copy (its pad kernel and
 buffer) are captured once on a stream that has run them before (so every
 library-owned buffer already exists and nothing is allocated during capture),
 then replayed several times with new inputs written eagerly in between.
@@ -38,6 +39,7 @@ def test_graph_replays_equal_eager_calls():
     ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
     y1 = torch.empty((cs[0], cs[4], P, Q), device="cuda:0")
     y2 = torch.empty_like(y1)
+    y3 = torch.empty_like(y1)
 
     def calls(stream):
         sp = stream.cuda_stream
@@ -46,6 +48,8 @@ def test_graph_replays_equal_eager_calls():
                              ws.data_ptr(), need, sp) == dg.GEMM_OK
         assert dg.conv2d_fwd_implicit_ex(dt, dt, params, dg.CONV_ADDR_TABLE, x.data_ptr(),
                                          w.data_ptr(), y2.data_ptr(), sp) == dg.GEMM_OK
+        assert dg.conv2d_fwd_implicit_ex(dt, dt, params, dg.CONV_ADDR_PADDED, x.data_ptr(),
+                                         w.data_ptr(), y3.data_ptr(), sp) == dg.GEMM_OK
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -67,11 +71,14 @@ def test_graph_replays_equal_eager_calls():
         C_eager = dg.gemm(A, B)
         y1_eager = dg.conv2d(x, w, padding=cs[7])
         y2_eager = dg.conv2d(x, w, padding=cs[7], implicit="table")
+        y3_eager = dg.conv2d(x, w, padding=cs[7], implicit="padded")
         torch.cuda.synchronize()
-        log("replay %d: gemm %s, conv %s, implicit conv %s" % (
-            rep, torch.equal(C, C_eager), torch.equal(y1, y1_eager), torch.equal(y2, y2_eager)))
+        log("replay %d: gemm %s, conv %s, implicit conv %s, padded %s" % (
+            rep, torch.equal(C, C_eager), torch.equal(y1, y1_eager), torch.equal(y2, y2_eager),
+            torch.equal(y3, y3_eager)))
         assert torch.equal(C, C_eager)
         assert torch.equal(y1, y1_eager)
         assert torch.equal(y2, y2_eager)
+        assert torch.equal(y3, y3_eager)
         # the replay computed the new inputs, not a stale result
         assert not np.array_equal(C.cpu().numpy(), 0)
