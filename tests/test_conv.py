@@ -296,3 +296,43 @@ def test_implicit_addressing_forms_agree_bitwise():
             log("addressing forms %s %s" % (c, "bf16" if bf16 else "f32"))
             assert torch.equal(ya, yt) and torch.equal(ga, gt), str(c)
             assert torch.equal(ya, yp) and torch.equal(ga, gp), str(c)
+
+
+def test_default_addressing_near_2gib():
+    """An fp32 image just under 2 GiB (16384 x 32760, 2^31 - 2^19 bytes)
+    whose zero-bordered copy would reach 2 GiB: the padded form is refused
+    before any device work, and the default form falls back to analytic
+    terms.  Forward outputs and filter-gradient taps, at the corners and at
+    random positions, match the oracle: buffer offsets up to the end of the
+    image are addressed correctly."""
+    import torch
+    c = ConvShape(1, 1, 1 << 14, (1 << 15) - 8, 1, 5, 5, 2, 2)
+    assert c.cin * c.h * c.w * 4 < 1 << 31 <= c.cin * (c.h + 4) * (c.w + 4) * 4
+    p = _params(c)
+    x, w, dy = wl.uniform_f32(c.x_shape, 41), wl.uniform_f32(c.w_shape, 42), \
+        wl.uniform_f32(c.y_shape, 43)
+    xd, wd, dyd = _dev(x), _dev(w), _dev(dy)
+    y = torch.empty(c.y_shape, device="cuda:0")
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, p, dg.CONV_ADDR_PADDED, xd.data_ptr(), wd.data_ptr(),
+                                     y.data_ptr(), _stream()) == dg.GEMM_ERR_INVALID_ARG
+    log("near-2GiB forward (default addressing)")
+    assert dg.conv2d_fwd_implicit(F32, F32, p, xd.data_ptr(), wd.data_ptr(), y.data_ptr(),
+                                  _stream()) == dg.GEMM_OK
+    rng = np.random.default_rng(44)
+    n = 64
+    pp, qq = rng.integers(0, c.p, n), rng.integers(0, c.q, n)
+    pp[:4], qq[:4] = [0, 0, c.p - 1, c.p - 1], [0, c.q - 1, 0, c.q - 1]
+    got = y[0, 0][torch.as_tensor(pp, device="cuda:0"), torch.as_tensor(qq, device="cuda:0")]
+    got = got.cpu().numpy().astype(np.float64)
+    z = np.zeros(n, np.int64)
+    ref, S = oc.conv2d_fwd_entries(x, w, c, z, z, pp, qq)
+    check_close(got, ref, S, TOL["f32"], "near-2GiB fwd (64 sampled)")
+    del y
+    log("near-2GiB filter gradient (default addressing)")
+    dw = dg.conv2d_weight_grad(xd, dyd, c.w_shape, padding=2, implicit=True)
+    torch.cuda.synchronize()
+    rr, ss = np.array([0, 0, 4, 4, 2]), np.array([0, 4, 0, 4, 2])
+    z = np.zeros(5, np.int64)
+    ref, S = oc.conv2d_bwd_weight_entries(x, dy, c, z, z, rr, ss)
+    check_close(dw.cpu().numpy().astype(np.float64)[0, 0][rr, ss], ref, S, TOL["f32"],
+                "near-2GiB filter gradient (5 taps)")
