@@ -336,3 +336,38 @@ def test_default_addressing_near_2gib():
     ref, S = oc.conv2d_bwd_weight_entries(x, dy, c, z, z, rr, ss)
     check_close(dw.cpu().numpy().astype(np.float64)[0, 0][rr, ss], ref, S, TOL["f32"],
                 "near-2GiB filter gradient (5 taps)")
+
+
+@pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
+def test_non_finite_image_values(implicit):
+    """NaN and +-Inf pixels (at image corners and inside) reach exactly the
+    outputs and filter taps whose sums include them: each entry's class
+    (finite, NaN, +Inf, -Inf) equals the float64 oracle's and the finite ones
+    are exact (integer tensors), fp32 and bf16.  The zero padding -- written
+    by im2col, zero-filled loads or the zero-bordered copy -- never meets
+    them."""
+    def classes(a):
+        return np.select([np.isnan(a), np.isposinf(a), np.isneginf(a)], [1, 2, 3], 0)
+
+    c = ConvShape(2, 3, 17, 19, 4, 3, 5, 1, 2)
+    for bf16 in (False, True):
+        if bf16:
+            nan, pinf, ninf = np.uint16(0x7FC0), np.uint16(0x7F80), np.uint16(0xFF80)
+        else:
+            nan, pinf, ninf = np.float32(np.nan), np.float32(np.inf), np.float32(-np.inf)
+        x, w, dy = _ints(c.x_shape, 61, bf16), _ints(c.w_shape, 62, bf16), _ints(c.y_shape, 63, bf16)
+        x[0, 1, 0, 0] = nan
+        x[1, 2, c.h - 1, c.w - 1] = pinf
+        x[0, 0, 8, 9] = ninf
+        x[1, 0, 3, c.w - 1] = pinf
+        for what, got, ref in [
+                ("fwd", run_fwd(x, w, c, False, implicit)[0], oc.conv2d_fwd(x, w, c)[0]),
+                ("filter gradient", run_bwd(x, dy, c, implicit), oc.conv2d_bwd_weight(x, dy, c)[0])]:
+            what = "%s %s %s" % ("bf16" if bf16 else "f32", what, implicit)
+            log(what)
+            assert np.any(~np.isfinite(ref)) and np.any(np.isfinite(ref)), what
+            bad = np.argwhere(classes(got) != classes(ref))
+            assert bad.size == 0, "%s: %d classes differ, first %s: gpu %r oracle %r" % (
+                what, len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])])
+            fin = np.isfinite(ref)
+            assert np.array_equal(got[fin], ref[fin]), what

@@ -307,3 +307,53 @@ def test_dispatched_skinny_and_wide_classes(bf16):
             A, B = _operands(M, N, K, ta, tb, _randn, 70 + t, bf16)
             C, _ = run_ex(A, B, ta, tb)
             check_close_ex(C, A, B, ta, tb, 1.0, 0.0, None, False, what + " random")
+
+
+def _classes(C):
+    """Per entry: 0 finite, 1 NaN, 2 +Inf, 3 -Inf."""
+    return np.select([np.isnan(C), np.isposinf(C), np.isneginf(C)], [1, 2, 3], 0)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_non_finite_inputs_every_layout_every_config(bf16):
+    """NaN and +-Inf in both operands reach exactly the outputs whose sums
+    include them, as IEEE arithmetic says: each entry's class (finite, NaN,
+    +Inf, -Inf) equals the float64 oracle's, and the finite entries are exact
+    (integer operands).  Every entry and operand form, 16-byte and
+    element-wise loads, and K split in 3: the zero-filled tile edges and the
+    padding are never multiplied with a non-finite value."""
+    dtype = BF16 if bf16 else F32
+    if bf16:
+        nan, pinf, ninf = np.uint16(0x7FC0), np.uint16(0x7F80), np.uint16(0xFF80)
+    else:
+        nan, pinf, ninf = np.float32(np.nan), np.float32(np.inf), np.float32(-np.inf)
+    M, N, K = 130, 90, 800
+
+    def put(X, trans, r, c, v):       # logical (op) coordinates
+        X[(c, r) if trans else (r, c)] = v
+
+    for cfg in range(dg.gemm_num_configs(dtype)):
+        name = dg.gemm_config_name(dtype, cfg)
+        mask = dg.gemm_config_layouts(dtype, cfg)
+        for ta, tb in TRANS:
+            if not mask & (1 << (2 * ta + tb)):
+                continue
+            A, B = _operands(M, N, K, ta, tb, _ints, 11, bf16)
+            put(A, ta, 5, 17, nan)
+            put(A, ta, 64, 3, pinf)
+            put(A, ta, 64, 200, ninf)
+            put(A, ta, 129, 799, pinf)            # last row, last (partial) k-tile
+            put(B, tb, 40, 7, ninf)
+            put(B, tb, 799, 89, pinf)             # last k, last column
+            ref, _ = expected(A, B, ta, tb, 1.0, 0.0, None)
+            assert np.any(np.isnan(ref)) and np.any(np.isposinf(ref)) and np.any(np.isneginf(ref))
+            fin = np.isfinite(ref)
+            for pad, sk in ((0, 0), (1, 0), (0, 3)):
+                what = "%s %s non-finite pad %d split %d" % (name, TNAME[ta, tb], pad, sk)
+                log(what)
+                _, raw = run_ex(A, B, ta, tb, cfg=cfg, pad=pad, split_k=sk)
+                C = raw.astype(np.float64)
+                bad = np.argwhere(_classes(C) != _classes(ref))
+                assert bad.size == 0, "%s: %d classes differ, first %s: gpu %r oracle %r" % (
+                    what, len(bad), tuple(bad[0]), C[tuple(bad[0])], ref[tuple(bad[0])])
+                assert np.array_equal(C[fin], ref[fin]), what
