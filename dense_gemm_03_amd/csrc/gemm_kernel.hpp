@@ -386,7 +386,7 @@ struct BlockCtx {
     int bm, bn;   // block origin in C
     int kend;     // end of this block's K range
     int tid, lane, wrow, wcol;
-    int rot;      // interior k-tile the block starts at (see main_loop_direct)
+    int rot;      // interior k-tile the block may start at (see main_loop_direct)
 };
 
 // Fragments of one step: per 32-row A fragment 16 bytes (4 fp32 or 8 bf16 k
@@ -615,7 +615,10 @@ __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
     tile_offsets(c.tid >> 6, c.lane, c.ldb, o.b);
     // k of the next tile to load; past the last tile the loads wrap round to
     // tiles already done (never read, and in bounds), so the code has no branch
-    int kt = c.rot;
+    // rotated start for bf16 (measured: +3-6% on large square products;
+    // fp32, which needs an eighth of the bytes per flop, gains nothing), only
+    // on long K loops, where the wrapped tiles are few
+    int kt = G::BF16 && ntiles >= 32 ? c.rot : 0;
     auto next_k = [&]() {
         const int k = k_first + kt * BK;
         kt = kt + 1 == ntiles ? 0 : kt + 1;
@@ -1065,10 +1068,7 @@ gemm_kernel(KernelArgs p)
     if constexpr (BSRC == B_MATRIX) {
         const bool edge = !ALIGNED || !p.direct_ok || c.bm + BM > p.M || c.bn + BN > p.N;
         const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
-        // rotated start for bf16 (measured: +3-6% on large square products;
-        // fp32, which needs an eighth of the bytes per flop, gains nothing),
-        // only on long K loops, where the wrapped tiles are few
-        c.rot = BF16 && nfast >= 32 ? (tm + tn) & 7 : 0;
+        c.rot = (tm + tn) % 8;
         if (nfast > 0) main_loop_direct(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
         if (ntiles > nfast)
             main_loop_masked(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc,
