@@ -75,7 +75,8 @@ SIGNATURES.update({
     "conv2d_bwd_weight_implicit_ex": (_int, [_int, _pp, _int, _p, _p, _p, _p]),
 })
 
-CONV_ADDR_DEFAULT, CONV_ADDR_ANALYTIC, CONV_ADDR_TABLE, CONV_ADDR_PADDED = 0, 1, 2, 3
+CONV_ADDR_DEFAULT, CONV_ADDR_ANALYTIC, CONV_ADDR_TABLE, CONV_ADDR_PADDED, CONV_ADDR_WINDOW = \
+    0, 1, 2, 3, 4
 
 
 class ConvNdParams(ctypes.Structure):
@@ -413,7 +414,7 @@ def _workspace(workspace, need, device):
 
 
 _ADDRESSING = {True: CONV_ADDR_DEFAULT, "analytic": CONV_ADDR_ANALYTIC, "table": CONV_ADDR_TABLE,
-               "padded": CONV_ADDR_PADDED}
+               "padded": CONV_ADDR_PADDED, "window": CONV_ADDR_WINDOW}
 
 
 def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None, stream=None,
@@ -421,7 +422,7 @@ def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None
     """y = conv2d(x, w) (cross-correlation form, as torch.nn.functional.conv2d)
     through the im2col + GEMM path, or with ``implicit`` through the
     implicit-GEMM path (no convolution matrix): True (the library's address
-    generation), "analytic", "table" or "padded".  x (N, C_in, H, W) and w
+    generation), "analytic", "table", "padded" or "window".  x (N, C_in, H, W) and w
     (C_out, C_in, R, S) are both float32 or both bfloat16; y is float32
     (default) or bfloat16.  The im2col workspace (one image's convolution
     matrix) is allocated when not given."""
@@ -450,8 +451,8 @@ def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wor
                        stream=None, implicit=False):
     """dw (float32, weight_shape) = the filter gradient of conv2d for input x
     and output gradient dy, through the im2col + GEMM path (or, with
-    ``implicit`` -- True, "analytic", "table" or "padded" -- the implicit-GEMM
-    path)."""
+    ``implicit`` -- True, "analytic", "table", "padded" or "window" -- the
+    implicit-GEMM path)."""
     import torch
     params, dtype, P, Q, need = _conv_setup(x, tuple(weight_shape), stride, padding, dilation)
     if dy.dtype != x.dtype or not dy.is_contiguous() or \

@@ -19,6 +19,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "conv.h"
@@ -564,6 +565,20 @@ __global__ void __launch_bounds__(kThreads) conv_pad_kernel(const void *src, voi
     static_cast<T *>(dst)[i] = in ? s[((int64_t)(c * d + z) * h + y) * w + x] : T(0);
 }
 
+// Filters with every filter row padded from S to S' taps, for the image-window
+// source: dst[co][row][s] = src[co][row][s] for s < S, 0 for S <= s < S'
+// (rows = C_in R).  One element per thread.
+template <int ESIZE>
+__global__ void __launch_bounds__(kThreads) conv_filter_pad_kernel(const void *src, void *dst,
+                                                                   int total, int s, int sp)
+{
+    typedef typename Word<ESIZE>::T T;
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= total) return;
+    const int row = i / sp, tap = i - row * sp;
+    static_cast<T *>(dst)[i] = tap < s ? static_cast<const T *>(src)[(int64_t)row * s + tap] : T(0);
+}
+
 // Spatial dimensions of the padded implicit sources: depth (1 for 2-D), rows,
 // columns, and their paddings, before and after padding.
 struct PadDims {
@@ -598,10 +613,70 @@ int64_t padded_bytes(const Dims &d, int esize)
     return elems * esize < (int64_t(1) << 31) ? elems * esize : -1;
 }
 
+// Geometry of the image-window source for a 2-D forward product (see
+// ConvWindow in gemm_kernel.hpp), for the tile entry the dispatcher picks for
+// C_out output channels.  False when the product does not qualify: it needs
+// unit horizontal stride and dilation, S' (S rounded up to a 16-byte slot) must
+// divide the k-tile, and one k-tile's window -- NP = BK / S' filter rows of NR
+// output rows x W' slots each, rounded up to the thread count -- must fit the
+// entry's B stage (BN x BK elements).  *pref: the window pays -- the zero taps
+// add at most a quarter to the product (S' <= 5/4 S) and the window is at most
+// half the stage (the gather it replaces reads the whole stage per k-tile).
+bool window_geom(int dtype, const Dims &d, const PadDims &pd, int64_t pbytes, ConvGeom *g,
+                 bool *pref)
+{
+    *pref = false;
+    if (d.nd != 2 || d.stride[1] != 1 || d.dil[1] != 1 || pbytes <= 0) return false;
+    const int es = elem_size(dtype), ks = 16 / es;
+    int bn = 0, bk = 0, threads = 0;
+    implicit_tile(dtype, d.k, &bn, &bk, &threads);
+    const int64_t S = d.kern[1], sp = (S + ks - 1) / ks * ks;
+    if (bk % sp != 0) return false;
+    const int64_t P = d.out[0], Q = d.out[1];
+    // output rows spanned by one block's BN positions (blocks start at
+    // multiples of BN)
+    int64_t nr = bn % Q == 0 ? bn / Q : Q % bn == 0 ? 1 : (bn - 1) / Q + 2;
+    nr = std::min(nr, P);
+    const int64_t np = bk / sp;
+    const int64_t nrwp = (nr * pd.wp + threads - 1) / threads * threads;
+    const int64_t stage_slots = (int64_t)bn * bk * es / 16;
+    if (np * nrwp > stage_slots) return false;
+    // K' = C_in R S' a valid k extent; offsets of the rows past the last output
+    // row (loaded, never read) still in 32 bits
+    const int64_t cr = d.c * d.kern[0];
+    if (cr * sp >= (int64_t(1) << 31) ||
+        (d.c * pd.hp + (P + nr) * d.stride[0] + d.kern[0] * d.dil[0]) * pd.wp * es >=
+            (int64_t(1) << 31))
+        return false;
+    *g = ConvGeom{};
+    g->h = pd.hp;
+    g->w = pd.wp;
+    g->r = (int)d.kern[0];
+    g->s = (int)S;
+    g->sh = (int)d.stride[0];
+    g->dh = (int)d.dil[0];
+    g->q = (int)Q;
+    g->pq = (int)(P * Q);
+    g->sp = (int)sp;
+    g->cr = (int)cr;
+    g->nr = (int)nr;
+    g->img_bytes = (int)pbytes;
+    div_magic((uint32_t)Q, &g->q_magic, &g->q_shift);
+    div_magic((uint32_t)sp, &g->sp_magic, &g->sp_shift);
+    div_magic((uint32_t)d.kern[0], &g->r_magic, &g->r_shift);
+    div_magic((uint32_t)pd.wp, &g->w_magic, &g->w_shift);
+    *pref = 4 * sp <= 5 * S && 2 * np * nrwp <= stage_slots;
+    return true;
+}
+
 // One implicit-GEMM convolution call (2-D or volume), forward (a = w, out = y)
 // or filter gradient (a = dy, out = dw, fp32): checks, addressing, per-image
-// GEMMs.  CONV_ADDR_DEFAULT takes the padded form when the padded image fits,
-// else the analytic one; the table form is 2-D only.
+// GEMMs.  CONV_ADDR_DEFAULT takes the image-window form where it applies (2-D
+// forward, unit horizontal stride and dilation, window within the B stage)
+// and pays (window_geom), else the padded form when the padded image fits,
+// else the analytic one;
+// CONV_ADDR_WINDOW runs the padded form where the window does not apply; the
+// table form is 2-D only.
 int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool fwd, bool vol,
                  const void *x, const void *a, void *out, hipStream_t stream)
 {
@@ -615,16 +690,42 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
     int rc = vol ? make_geom3(d, es, &geom) : make_geom(d, es, &geom);
     if (rc != GEMM_OK) return rc;
     const int64_t pbytes = padded_bytes(d, es);
+    const PadDims pd = pad_dims(d);
+    ConvGeom wgeom;
+    bool window_pref = false;
+    const bool window = fwd && !vol && window_geom(dtype, d, pd, pbytes, &wgeom, &window_pref);
     int mode = addressing;
-    if (mode == CONV_ADDR_DEFAULT) mode = pbytes > 0 ? CONV_ADDR_PADDED : CONV_ADDR_ANALYTIC;
+    if (mode == CONV_ADDR_DEFAULT)
+        mode = window_pref ? CONV_ADDR_WINDOW : pbytes > 0 ? CONV_ADDR_PADDED : CONV_ADDR_ANALYTIC;
+    if (mode == CONV_ADDR_WINDOW && !window) mode = CONV_ADDR_PADDED;  // where it does not apply
     if ((mode == CONV_ADDR_PADDED && pbytes < 0) ||
         (mode == CONV_ADDR_TABLE && (vol || !table_fits(d, fwd))))
         return GEMM_ERR_INVALID_ARG;
     if ((rc = device_ok()) != GEMM_OK) return rc;
     int bsrc;
     void *padded = nullptr;
-    const PadDims pd = pad_dims(d);
-    if (mode == CONV_ADDR_TABLE) {
+    const void *filters = a;
+    int64_t kdim = fwd ? d.crs() : d.vol_out();
+    if (mode == CONV_ADDR_WINDOW) {
+        if ((rc = conv_padded_buffer(stream, (size_t)pbytes, &padded)) != GEMM_OK) return rc;
+        // filters with rows padded to S' taps: K' = C_in R S'
+        kdim = (int64_t)wgeom.cr * wgeom.sp;
+        const int64_t total = d.k * kdim;
+        if (total * es >= (int64_t(1) << 31)) return GEMM_ERR_INVALID_ARG;
+        void *fbuf = nullptr;
+        if ((rc = conv_filter_buffer(stream, (size_t)(total * es), &fbuf)) != GEMM_OK) return rc;
+        const dim3 grid((unsigned)((total + kThreads - 1) / kThreads)), block(kThreads);
+        if (es == 4)
+            hipLaunchKernelGGL(conv_filter_pad_kernel<4>, grid, block, 0, stream, a, fbuf,
+                               (int)total, wgeom.s, wgeom.sp);
+        else
+            hipLaunchKernelGGL(conv_filter_pad_kernel<2>, grid, block, 0, stream, a, fbuf,
+                               (int)total, wgeom.s, wgeom.sp);
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+        filters = fbuf;
+        geom = wgeom;
+        bsrc = B_CONV_FWD_WIN;
+    } else if (mode == CONV_ADDR_TABLE) {
         if ((rc = table_source(es, fwd, &geom, stream, &bsrc)) != GEMM_OK) return rc;
     } else if (mode == CONV_ADDR_PADDED) {
         if ((rc = conv_padded_buffer(stream, (size_t)pbytes, &padded)) != GEMM_OK) return rc;
@@ -663,8 +764,9 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
         GemmCall g;
         if (fwd)
             // y[n] (C_out x output volume) = w (C_out x C_in filter volume) . cols(x[n])
-            g = GemmCall{dtype, dtype_out, GEMM_OP_N, GEMM_OP_N, d.k, vo, d.crs(), 1.0f, 0.0f,
-                         a, d.crs(), img, 1, static_cast<char *>(out) + n * d.k * vo * eso, vo,
+            // (the window source: filter rows padded to S' taps, K = C_in R S')
+            g = GemmCall{dtype, dtype_out, GEMM_OP_N, GEMM_OP_N, d.k, vo, kdim, 1.0f, 0.0f,
+                         filters, kdim, img, 1, static_cast<char *>(out) + n * d.k * vo * eso, vo,
                          bsrc, &geom};
         else
             // dw (C_out x C_in filter volume) (+)= dy[n] (C_out x output volume) . cols(x[n])^T
@@ -813,7 +915,7 @@ int conv2d_fwd_implicit_ex(int dtype, int dtype_y, const conv2d_params *p, int a
     if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
     const int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED) return GEMM_ERR_INVALID_ARG;
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW) return GEMM_ERR_INVALID_ARG;
     return dg::run_implicit(dtype, dtype_y, d, addressing, true, false, x, w, y, stream);
 }
 
@@ -830,7 +932,7 @@ int conv2d_bwd_weight_implicit_ex(int dtype, const conv2d_params *p, int address
     if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
     const int rc = dg::dims_2d(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED) return GEMM_ERR_INVALID_ARG;
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW) return GEMM_ERR_INVALID_ARG;
     return dg::run_implicit(dtype, GEMM_DTYPE_F32, d, addressing, false, false, x, dy, dw, stream);
 }
 
@@ -892,7 +994,7 @@ int convnd_fwd_implicit_ex(int dtype, int dtype_y, const convnd_params *p, int a
     if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
     const int rc = dg::dims_nd(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED ||
+    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW ||
         addressing == CONV_ADDR_TABLE)
         return GEMM_ERR_INVALID_ARG;
     return dg::run_implicit(dtype, dtype_y, d, addressing, true, true, x, w, y, stream);
@@ -911,7 +1013,7 @@ int convnd_bwd_weight_implicit_ex(int dtype, const convnd_params *p, int address
     if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
     const int rc = dg::dims_nd(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_PADDED ||
+    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW ||
         addressing == CONV_ADDR_TABLE)
         return GEMM_ERR_INVALID_ARG;
     return dg::run_implicit(dtype, GEMM_DTYPE_F32, d, addressing, false, true, x, dy, dw, stream);

@@ -41,5 +41,11 @@ int gemm_run(const GemmCall &call, int forced_cfg, int forced_split, hipStream_t
 int conv_table_buffer(hipStream_t stream, size_t bytes, void **out);
 // The same for the zero-padded image of the implicit GEMM.
 int conv_padded_buffer(hipStream_t stream, size_t bytes, void **out);
+// The same for the filters with rows padded to S' taps (image-window source).
+int conv_filter_buffer(hipStream_t stream, size_t bytes, void **out);
+
+// Block width BN, k-tile BK and threads of the entry gemm_run picks for an
+// implicit convolution product with M output channels.
+void implicit_tile(int dtype, int64_t M, int *bn, int *bk, int *threads);
 
 }  // namespace dg

@@ -98,12 +98,16 @@ enum BSource {
     B_CONV_WGRAD_PAD = 8,
     B_CONV3_FWD_PAD = 9,
     B_CONV3_WGRAD_PAD = 10,
+    // forward product, 2-D, unit horizontal stride and dilation: B fragments
+    // read from a window of the zero-bordered image held in LDS (see
+    // ConvWindow); A is the filters with each filter row padded to S' taps
+    B_CONV_FWD_WIN = 11,
 };
 
 __host__ __device__ constexpr bool conv_fwd_source(int b)
 {
     return b == B_CONV_FWD || b == B_CONV_FWD_TAB || b == B_CONV3_FWD || b == B_CONV_FWD_PAD ||
-           b == B_CONV3_FWD_PAD;
+           b == B_CONV3_FWD_PAD || b == B_CONV_FWD_WIN;
 }
 __host__ __device__ constexpr bool conv_table_source(int b) { return b == B_CONV_FWD_TAB || b == B_CONV_WGRAD_TAB; }
 __host__ __device__ constexpr bool conv_volume_source(int b)
@@ -126,6 +130,13 @@ struct ConvGeom {
     int d, t, pz, sz, lz, p;              // depth, filter depth, its padding, stride, dilation; P
     uint64_t trs_magic, pq_magic;         // k / (T R S), j / (P Q)
     int trs_shift, pq_shift;
+    // Window source only (all on the zero-bordered image: h, w are its padded
+    // sizes): sp = S' taps per filter row (S rounded up to a 16-byte slot and
+    // dividing BK; s >= S are zero filter taps), cr = C_in R filter rows, nr
+    // output rows per window, and the divisions they need.
+    int sp, cr, nr;
+    uint64_t sp_magic, r_magic, w_magic;  // k / S', filter row / R, slot / W'
+    int sp_shift, r_shift, w_shift;
     // Table sources only: the terms that change along K, one entry per k --
     // per tap (ci, r, s) for the forward product, per output position (p, q)
     // for the filter gradient: {y | x << 16 (signed 16-bit each), byte offset}.
@@ -996,6 +1007,180 @@ struct ConvGather {
     }
 };
 
+// B fragments of the forward convolution product from a window of the image
+// in LDS ("Three X's: large convolutions in PyTorch for model training",
+// section "CUTLASS": the implicit GEMM forms the matrix tiles in the block;
+// here for unit horizontal stride and dilation, where the matrix element of
+// tap (ci, r, s) and output (p, q) is image[ci][p sh + r dh][q + s] of the
+// zero-bordered image).  A lane's fragment holds KS consecutive taps
+// s0 .. s0 + KS - 1 of one filter row for one output position, which are KS
+// consecutive image elements from x = q + s0.  Filter rows are padded to S'
+// taps (a multiple of KS dividing BK), so every k-tile covers NP = BK / S'
+// whole filter rows, and its B values all come from NP x NR image rows (filter
+// row kp, output row p): one window per k-tile instead of BK x BN gathered
+// elements.  Window slot (j, i, x), at j NRWP + i W' + x (NRWP = NR W'
+// rounded up to the thread count), holds the KS elements from x of the row of
+// filter row kp0 + j and output row p_first + i; every fragment is one
+// aligned 16-byte LDS read and consecutive lanes (consecutive q) read
+// consecutive slots.  Because S' divides BK, a fragment step's filter row j
+// and first tap s0 are the same in every k-tile, and so is the slot of a
+// thread's u-th staged load within its filter row: all of it is computed once
+// per block.  Taps s >= S (zero filter taps, only in a row's last slot) are
+// zeroed in the fragment, so a non-finite pixel is never multiplied by them;
+// filter rows past C_in R load zeros.
+template <class G>
+struct ConvWindow {
+    using In = typename G::In;
+    static constexpr int KS = G::KS;             // taps per slot and fragment
+    static constexpr int U = G::TB::PER_THREAD;  // staged slots per thread
+    static_assert(G::TB::CHUNKS == U * G::NT, "window slots fill the B stage");
+
+    __amdgpu_buffer_rsrc_t rsrc;
+    const ConvGeom *g;
+    int nrwp, vrows;  // slots per filter row of the window (a multiple of NT), NT-rows of them
+    int jrow[U];      // per staged load u: its filter row in the window, u / vrows (uniform)
+    int pos[G::FN];   // per B fragment: i W' + q of this lane's output position
+    int col[U];       // per staged load u: element offset of its slot within a filter
+                      // row's image rows, (p_first + i) sh W' + x, or -1 past them
+    int base[G::STEPS];      // per fragment step: j NRWP + s0 of this lane's half
+    bool last[G::STEPS];     // per fragment step: the slot holds zero taps
+    uint32_t keep[4];        // the real taps of such a slot, as a mask of its dwords
+
+    __device__ __forceinline__ ConvWindow(const KernelArgs &a, int bn, int tid, int wcol, int lane)
+        : g(&a.conv)
+    {
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.B), 0, a.conv.img_bytes,
+                                                 0x00020000);  // gfx9 raw-buffer format word
+        const int p_first = div_magic(bn, g->q_magic, g->q_shift);
+        const int nrw = g->nr * g->w;
+        vrows = (nrw + G::NT - 1) / G::NT;
+        nrwp = vrows * G::NT;
+#pragma unroll
+        for (int fn = 0; fn < G::FN; ++fn) {
+            // columns past N repeat the last position (their outputs are not stored)
+            const int n = min(bn + wcol * G::WTN + fn * 32 + (lane & 31), a.N - 1);
+            const int p = div_magic(n, g->q_magic, g->q_shift);
+            pos[fn] = (p - p_first) * g->w + (n - p * g->q);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            jrow[u] = u / vrows;
+            const int in = tid + (u - jrow[u] * vrows) * G::NT;  // slot within its filter row
+            const int i = div_magic(in, g->w_magic, g->w_shift);
+            col[u] = in < nrw ? (p_first + i) * g->sh * g->w + (in - i * g->w) : -1;
+        }
+        const int h = lane >> 5;
+#pragma unroll
+        for (int st = 0; st < G::STEPS; ++st) {
+            const int kk = h * G::KH + st * KS;  // k within the k-tile
+            const int j = div_magic(kk, g->sp_magic, g->sp_shift);
+            const int s0 = kk - j * g->sp;
+            base[st] = j * nrwp + s0;
+            last[st] = s0 + KS > g->s;
+        }
+        const int real = g->s - (g->sp - KS);  // real taps of a row's last slot
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            if constexpr (KS == 8)  // bf16: two taps per dword
+                keep[d] = (2 * d < real ? 0x0000FFFFu : 0u) | (2 * d + 1 < real ? 0xFFFF0000u : 0u);
+            else
+                keep[d] = d < real ? 0xFFFFFFFFu : 0u;
+        }
+    }
+
+    // The window of the k-tile at k0 (a multiple of BK), slot tid + u NT in
+    // r[u]: staged load u serves filter row j = u / vrows (uniform), whose
+    // image-row offset is computed once per filter row on the scalar unit.
+    __device__ __forceinline__ void load(int k0, u32x4 (&r)[U]) const
+    {
+        const int kp0 = div_magic(k0, g->sp_magic, g->sp_shift);
+        const int np = G::BK / g->sp;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = jrow[u];
+            if (j >= np) break;  // past the window: no load (block-uniform)
+            const int kp = kp0 + j;
+            const int ci = div_magic(kp, g->r_magic, g->r_shift);
+            const int rr = kp - ci * g->r;
+            const int row = (ci * g->h + rr * g->dh) * g->w;  // element offset of the filter row
+            const bool ok = (kp < g->cr) & (col[u] >= 0);
+            const int off = ok ? (row + col[u]) * (int)sizeof(In) : (int)0x80000000u;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+            r[u] = u32x4{v[0], v[1], v[2], v[3]};
+        }
+    }
+
+    __device__ __forceinline__ void store(unsigned char *win, int tid, const u32x4 (&r)[U]) const
+    {
+        const int np = G::BK / g->sp;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (jrow[u] >= np) break;
+            lds_store16(win, (tid + u * G::NT) * 16, r[u]);
+        }
+    }
+
+    __device__ __forceinline__ u32x4 frag(const unsigned char *win, int st, int fn) const
+    {
+        const u32x4 v = lds_load16(win, (base[st] + pos[fn]) * 16);
+        if (!last[st]) return v;
+        return u32x4{v[0] & keep[0], v[1] & keep[1], v[2] & keep[2], v[3] & keep[3]};
+    }
+};
+
+template <class G>
+__device__ __forceinline__ void load_frags_window(const unsigned char *stage, const BlockCtx<G> &c,
+                                                  const ConvWindow<G> &win, int step, Frags<G> &f)
+{
+    const int kk = (c.lane >> 5) * G::KH + step * G::KS;
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm)
+        f.a[fm] = read_frag<typename G::TA>(stage, c.lane, c.wrow * G::WTM + fm * 32, kk);
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn) f.b[fn] = win.frag(stage + G::A_BYTES, step, fn);
+}
+
+// main_loop_masked with the window source: A tiles as there, B from windows.
+template <bool ALIGNED, class G>
+__device__ __forceinline__ void main_loop_window(unsigned char *smem0, unsigned char *smem1,
+                                                 const BlockCtx<G> &c, const ConvWindow<G> &win,
+                                                 int k_first, int ntiles,
+                                                 floatx16 (&acc)[G::FM][G::FN])
+{
+    StageRegs<G> regs;
+    Frags<G> cur, nxt;
+    auto load = [&](int k0) {
+        load_tile_masked<ALIGNED, typename G::TA>(c.A, c.lda, c.bm, c.M, k0, c.kend, c.tid, regs.a);
+        win.load(k0, regs.b);
+    };
+    auto store = [&](unsigned char *stage) {
+        store_tile<typename G::TA>(stage, c.tid, regs.a);
+        win.store(stage + G::A_BYTES, c.tid, regs.b);
+    };
+    load(k_first);
+    store(smem0);
+    __syncthreads();
+    load_frags_window(smem0, c, win, 0, cur);
+    for (int t = 0; t < ntiles; ++t) {
+        unsigned char *stage = (t & 1) ? smem1 : smem0;
+        unsigned char *other = (t & 1) ? smem0 : smem1;
+        const int k0 = k_first + t * G::BK;
+        const bool more = t + 1 < ntiles;
+        if (more) load(k0 + G::BK);
+#pragma unroll
+        for (int step = 0; step < G::STEPS - 1; ++step) {
+            load_frags_window(stage, c, win, step + 1, nxt);
+            mma(cur, acc);
+            cur = nxt;
+        }
+        if (more) store(other);
+        __syncthreads();
+        if (more) load_frags_window(other, c, win, 0, nxt);
+        mma(cur, acc);
+        cur = nxt;
+    }
+}
+
 // --------------------------------------------------------------- epilogue --
 
 // Final value of one element of C: alpha * sum, plus beta * (old C) when
@@ -1073,6 +1258,10 @@ gemm_kernel(KernelArgs p)
         if (ntiles > nfast)
             main_loop_masked(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc,
                              [&](int k0, StageRegs<G> &r) { global_load_masked<ALIGNED>(c, k0, r); });
+    } else if constexpr (BSRC == B_CONV_FWD_WIN) {
+        // implicit GEMM: A from memory, B fragments from image windows in LDS
+        ConvWindow<G> win(p, c.bn, c.tid, c.wcol, c.lane);
+        main_loop_window<ALIGNED>(lds0, lds1, c, win, kbeg, ntiles, acc);
     } else {
         // implicit GEMM: A from memory, B tiles formed from the image
         ConvGather<G, BSRC> gather(p, c.bn, c.tid, kbeg, c.kend);

@@ -133,16 +133,33 @@ int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x,
  *     the analytic terms and no padding, so no element needs a range check.
  *     Needs the padded image under 2 GiB (GEMM_ERR_INVALID_ARG otherwise);
  *     costs one extra read and write of the image per call;
+ *   CONV_ADDR_WINDOW: for the forward product with unit horizontal stride
+ *     and dilation, the padded copy as above, and the filters copied into a
+ *     library-owned buffer with each filter row padded from S to S' taps (S
+ *     rounded up to 8 bf16 or 4 fp32 taps, the extra taps zero); each block
+ *     then loads, per k-tile, only the image rows its filter rows and output
+ *     rows need into a window in LDS and reads every B fragment from it with
+ *     one aligned 16-byte load (instead of gathering each matrix element).
+ *     Applies when one k-tile's window fits the block's B stage; other calls
+ *     (filter gradient, strides or dilations along the rows, larger windows)
+ *     run the padded form.  Same error as CONV_ADDR_PADDED for the padded
+ *     image;
  *   CONV_ADDR_DEFAULT: the library's choice (what conv2d_fwd_implicit and
- *     conv2d_bwd_weight_implicit use): the padded form when the padded image
- *     fits, else the analytic one.
- * All give identical results (same products, same summation order).
+ *     conv2d_bwd_weight_implicit use): the window form where it applies and
+ *     pays (the zero taps add at most a quarter, S' <= 5/4 S, and the window
+ *     is at most half the B stage: wide filters), else the padded form when
+ *     the padded image fits, else the analytic one.
+ * The analytic, table and padded forms give identical results (same
+ * products, same summation order); the window form sums the same products
+ * (plus zero taps) in a different k order, so its results differ from theirs
+ * by rounding only.
  */
 typedef enum {
     CONV_ADDR_DEFAULT = 0,
     CONV_ADDR_ANALYTIC = 1,
     CONV_ADDR_TABLE = 2,
-    CONV_ADDR_PADDED = 3
+    CONV_ADDR_PADDED = 3,
+    CONV_ADDR_WINDOW = 4
 } conv_addressing;
 
 int conv2d_fwd_implicit_ex(int dtype, int dtype_y, const conv2d_params *p, int addressing,
@@ -211,9 +228,10 @@ int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const vo
  * convnd_bwd_weight; GEMM_ERR_INVALID_ARG for ndim 4 and when one batch
  * element of x spans 2 GiB or more.  The _ex forms take the addressing:
  * CONV_ADDR_ANALYTIC, CONV_ADDR_PADDED (the image copied with zero borders
- * in every padded dimension, as for the 2-D calls) or CONV_ADDR_DEFAULT
- * (padded when the padded image is under 2 GiB, else analytic; what the
- * plain forms use); CONV_ADDR_TABLE is 2-D only (GEMM_ERR_INVALID_ARG). */
+ * in every padded dimension, as for the 2-D calls; CONV_ADDR_WINDOW runs
+ * this form here) or CONV_ADDR_DEFAULT (padded when the padded image is
+ * under 2 GiB, else analytic; what the plain forms use); CONV_ADDR_TABLE is
+ * 2-D only (GEMM_ERR_INVALID_ARG). */
 int convnd_fwd_implicit(int dtype, int dtype_y, const convnd_params *p, const void *x,
                         const void *w, void *y, hipStream_t stream);
 int convnd_bwd_weight_implicit(int dtype, const convnd_params *p, const void *x, const void *dy,

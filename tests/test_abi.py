@@ -270,7 +270,7 @@ def test_conv_host_logic_and_invalid_arguments():
     # address generation: unknown forms are rejected; the table form needs its
     # y and x terms within signed 16 bits
     A, T, PD = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE, dg.CONV_ADDR_PADDED
-    assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, 4, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, 5, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.conv2d_fwd_implicit_ex(F32, F32, ok, -1, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.conv2d_bwd_weight_implicit_ex(F32, ok, 7, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     wide = P(1, 1, 40001, 8, 1, 3, 1, (0, 0), (1, 1), (20000, 1))   # (R-1) dh = 40000
@@ -284,6 +284,9 @@ def test_conv_host_logic_and_invalid_arguments():
     edge = P(1, 1, 1 << 14, (1 << 15) - 8, 1, 5, 5, (2, 2))
     assert dg.conv2d_output_size(edge)[0] == dg.GEMM_OK
     assert dg.conv2d_fwd_implicit_ex(F32, F32, edge, PD, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    # the window form reads the same copy
+    assert dg.conv2d_fwd_implicit_ex(F32, F32, edge, dg.CONV_ADDR_WINDOW, p, p, p) == \
+        dg.GEMM_ERR_INVALID_ARG
     assert dg.conv2d_bwd_weight_implicit_ex(F32, edge, PD, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     # an empty batch: nothing to compute for the forward
     assert dg.conv2d_fwd(F32, F32, P(0, 3, 10, 9, 4, 3, 2), None, None, None, None, 0) == dg.GEMM_OK
@@ -359,7 +362,7 @@ def test_convnd_host_logic_and_invalid_arguments():
     assert dg.convnd_fwd_implicit(F32, F32, big, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.convnd_fwd_implicit(F32, F32, N(0, 3, 4, (5,), (3,)), None, None, None) == dg.GEMM_OK
     # addressing: analytic, padded or the default; the table form is 2-D only
-    for mode in (dg.CONV_ADDR_TABLE, 4, -1):
+    for mode in (dg.CONV_ADDR_TABLE, 5, -1):
         assert dg.convnd_fwd_implicit_ex(F32, F32, ok, mode, p, p, p) == dg.GEMM_ERR_INVALID_ARG
         assert dg.convnd_bwd_weight_implicit_ex(F32, ok, mode, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     # an image just under 2 GiB whose zero-bordered copy is not

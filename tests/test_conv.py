@@ -14,7 +14,8 @@ direct-convolution oracle, through the C ABI (include/conv.h).
 * Each check runs through im2col + GEMM and through the implicit GEMM with
   each address generation (terms computed in the loader, looked up in a
   table, or computed over a zero-bordered copy of the image with no range
-  checks); the implicit forms give identical bits.
+  checks, and the forward product from image windows in LDS); the first
+  three implicit forms give identical bits.
 """
 from __future__ import annotations
 
@@ -31,9 +32,10 @@ from tests.gpu_util import DIAGNOSTIC, TOL, log, to_device
 pytestmark = pytest.mark.gpu
 
 F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
-# im2col + GEMM, and the implicit GEMM with each address generation
-ROUTES = [False, "analytic", "table", "padded"]
-ROUTE_IDS = ["im2col", "analytic", "table", "padded"]
+# im2col + GEMM, and the implicit GEMM with each address generation ("window":
+# the forward product from image windows in LDS where it applies, else padded)
+ROUTES = [False, "analytic", "table", "padded", "window"]
+ROUTE_IDS = ["im2col", "analytic", "table", "padded", "window"]
 
 SHAPES = [
     # batch, cin, h, w, cout, r, s, ph, pw, sh, sw, dh, dw
@@ -371,3 +373,39 @@ def test_non_finite_image_values(implicit):
                 what, len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])])
             fin = np.isfinite(ref)
             assert np.array_equal(got[fin], ref[fin]), what
+
+
+# wide filters, where the forward product reads image windows from LDS:
+# 32-, 64-, 100- and 300-channel outputs (every tile entry with implicit
+# kernels, 256- and 512-thread blocks), vertical stride and dilation, filter
+# rows padded from S to S' (15 -> 16, 31 -> 32) or not (16, 32), blocks of 1
+# to 6 output rows, rows of 300 outputs
+WINDOW_SHAPES = [
+    ConvShape(1, 4, 30, 70, 32, 5, 15, 2, 7),
+    ConvShape(2, 3, 24, 50, 64, 7, 16, 3, 8, 2, 1, 1, 1),
+    ConvShape(1, 2, 20, 45, 100, 3, 32, 1, 16, 1, 1, 2, 1),
+    ConvShape(1, 2, 16, 40, 300, 3, 31, 1, 15),
+    ConvShape(1, 1, 8, 300, 8, 1, 31, 0, 15),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_window_form_wide_filters(bf16):
+    """The image-window forward product on wide filters: exact on integers
+    (bf16 y: rounded once), within tolerance on random tensors, and the
+    default addressing within tolerance too."""
+    for t, c in enumerate(WINDOW_SHAPES):
+        x, w = _ints(c.x_shape, 300 + t, bf16), _ints(c.w_shape, 310 + t, bf16)
+        ref, _ = oc.conv2d_fwd(x, w, c)
+        for out_bf16 in (False, True):
+            log("window %s %s out %s" % (c, "bf16" if bf16 else "f32", "bf16" if out_bf16 else "f32"))
+            got, raw = run_fwd(x, w, c, out_bf16, "window")
+            if out_bf16:
+                assert np.array_equal(raw, oracle.round_to_bf16_bits(ref)), str(c)
+            else:
+                assert np.array_equal(got, ref), str(c)
+        x, w = _randn(c.x_shape, 320 + t, bf16), _randn(c.w_shape, 330 + t, bf16)
+        ref, S = oc.conv2d_fwd(x, w, c)
+        tol = TOL["bf16" if bf16 else "f32"]
+        check_close(run_fwd(x, w, c, False, "window")[0], ref, S, tol, "window random %s" % (c,))
+        check_close(run_fwd(x, w, c, False, True)[0], ref, S, tol, "default random %s" % (c,))
