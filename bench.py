@@ -21,7 +21,7 @@ in HBM.  Prints ONE JSON line:
                           31x31-filter workload, fp32 and bf16 (forward,
                           filter gradient, their implicit-GEMM forms with
                           analytic, table and padded-image address
-                          generation and the forward product from image
+                          generation and both products from image
                           windows, and the im2col kernel against HBM),
                           and of the 3-D (7x7x7 filters, fp32 and bf16; also
                           through the implicit GEMM, analytic and padded)
@@ -286,7 +286,8 @@ def measure_conv(name: str, steps: int, warmup: int, only: str | None = None):
                    ("fwd_implicit_table", implicit_fwd(T)), ("wgrad_implicit_table", implicit_wgrad(T)),
                    ("fwd_implicit_padded", implicit_fwd(PD)),
                    ("wgrad_implicit_padded", implicit_wgrad(PD)),
-                   ("fwd_implicit_window", implicit_fwd(dg.CONV_ADDR_WINDOW))]
+                   ("fwd_implicit_window", implicit_fwd(dg.CONV_ADDR_WINDOW)),
+                   ("wgrad_implicit_window", implicit_wgrad(dg.CONV_ADDR_WINDOW))]
     if only is not None and only not in [r[0] for r in routes] + ["im2col"]:
         raise SystemExit("unknown route %r for %s" % (only, name))
     for label, fn in routes:
@@ -386,7 +387,7 @@ def main() -> int:
                     help="with --conv: time only this route (fwd, wgrad, fwd_implicit, "
                          "wgrad_implicit, fwd_implicit_table, wgrad_implicit_table, "
                          "fwd_implicit_padded, wgrad_implicit_padded, fwd_implicit_window, "
-                         "im2col), "
+                         "wgrad_implicit_window, im2col), "
                          "for per-route profiler passes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference kernel "

@@ -579,6 +579,17 @@ __global__ void __launch_bounds__(kThreads) conv_filter_pad_kernel(const void *s
     static_cast<T *>(dst)[i] = tap < s ? static_cast<const T *>(src)[(int64_t)row * s + tap] : T(0);
 }
 
+// The inverse for the fp32 filter gradient: dst[row][s] = src[row][s], s < S,
+// rows of S' in src, of S in dst.
+__global__ void __launch_bounds__(kThreads) conv_filter_unpad_kernel(const float *src, float *dst,
+                                                                     int total, int s, int sp)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= total) return;
+    const int row = i / s, tap = i - row * s;
+    dst[i] = src[(int64_t)row * sp + tap];
+}
+
 // Spatial dimensions of the padded implicit sources: depth (1 for 2-D), rows,
 // columns, and their paddings, before and after padding.
 struct PadDims {
@@ -669,12 +680,59 @@ bool window_geom(int dtype, const Dims &d, const PadDims &pd, int64_t pbytes, Co
     return true;
 }
 
+// Geometry of the image-window source for a 2-D filter gradient (see
+// ConvWindowW in gemm_kernel.hpp), for the entry the dispatcher picks for C_out
+// output channels: unit horizontal stride and dilation, S' dividing BN (a
+// block's columns are whole filter rows), and per k-tile BN / S' window rows
+// of BK + S' - 1 slots, each rounded up to the thread count, within the
+// entry's staging registers.  Output rows are padded to Q' = Q rounded up to
+// BK.  *pref: bf16 (measured on 31-wide filters: bf16 25% faster than the
+// padded gather, fp32 3% slower), the padding adds at most a quarter
+// (S' <= 5/4 S, Q' <= 5/4 Q) and the window holds at most half the B stage.
+bool window_geom_w(int dtype, const Dims &d, const PadDims &pd, int64_t pbytes, ConvGeom *g,
+                   bool *pref)
+{
+    *pref = false;
+    if (d.nd != 2 || d.stride[1] != 1 || d.dil[1] != 1 || pbytes <= 0) return false;
+    const int es = elem_size(dtype), ks = 16 / es;
+    int bn = 0, bk = 0, threads = 0;
+    implicit_tile(dtype, d.k, &bn, &bk, &threads);
+    const int64_t S = d.kern[1], sp = (S + ks - 1) / ks * ks;
+    if (bn % sp != 0) return false;
+    const int64_t P = d.out[0], Q = d.out[1], qp = (Q + bk - 1) / bk * bk;
+    const int64_t len = bk + sp - 1, vrows = (len + threads - 1) / threads;
+    const int64_t stage_slots = (int64_t)bn * bk * es / 16;
+    if ((bn / sp) * vrows * threads > stage_slots) return false;
+    const int64_t cr = d.c * d.kern[0];
+    if (cr * sp >= (int64_t(1) << 31) || P * qp >= (int64_t(1) << 31) ||
+        d.k * P * qp * es >= (int64_t(1) << 31) ||
+        (d.c * pd.hp * pd.wp + len + bk) * es >= (int64_t(1) << 31))
+        return false;
+    *g = ConvGeom{};
+    g->h = pd.hp;
+    g->w = pd.wp;
+    g->r = (int)d.kern[0];
+    g->s = (int)S;
+    g->sh = (int)d.stride[0];
+    g->dh = (int)d.dil[0];
+    g->q = (int)Q;
+    g->sp = (int)sp;
+    g->cr = (int)cr;
+    g->qp = (int)qp;
+    g->img_bytes = (int)pbytes;
+    div_magic((uint32_t)sp, &g->sp_magic, &g->sp_shift);
+    div_magic((uint32_t)d.kern[0], &g->r_magic, &g->r_shift);
+    div_magic((uint32_t)qp, &g->qp_magic, &g->qp_shift);
+    *pref = es == 2 && 4 * sp <= 5 * S && 4 * qp <= 5 * Q && 2 * (bn / sp) * len <= stage_slots;
+    return true;
+}
+
 // One implicit-GEMM convolution call (2-D or volume), forward (a = w, out = y)
 // or filter gradient (a = dy, out = dw, fp32): checks, addressing, per-image
-// GEMMs.  CONV_ADDR_DEFAULT takes the image-window form where it applies (2-D
-// forward, unit horizontal stride and dilation, window within the B stage)
-// and pays (window_geom), else the padded form when the padded image fits,
-// else the analytic one;
+// GEMMs.  CONV_ADDR_DEFAULT takes the image-window form where it applies (2-D,
+// unit horizontal stride and dilation, window within the B stage) and pays
+// (window_geom, window_geom_w), else the padded form when the padded image
+// fits, else the analytic one;
 // CONV_ADDR_WINDOW runs the padded form where the window does not apply; the
 // table form is 2-D only.
 int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool fwd, bool vol,
@@ -693,7 +751,9 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
     const PadDims pd = pad_dims(d);
     ConvGeom wgeom;
     bool window_pref = false;
-    const bool window = fwd && !vol && window_geom(dtype, d, pd, pbytes, &wgeom, &window_pref);
+    const bool window =
+        !vol && (fwd ? window_geom(dtype, d, pd, pbytes, &wgeom, &window_pref)
+                     : window_geom_w(dtype, d, pd, pbytes, &wgeom, &window_pref));
     int mode = addressing;
     if (mode == CONV_ADDR_DEFAULT)
         mode = window_pref ? CONV_ADDR_WINDOW : pbytes > 0 ? CONV_ADDR_PADDED : CONV_ADDR_ANALYTIC;
@@ -706,7 +766,17 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
     void *padded = nullptr;
     const void *filters = a;
     int64_t kdim = fwd ? d.crs() : d.vol_out();
-    if (mode == CONV_ADDR_WINDOW) {
+    void *dyp = nullptr, *dwp = nullptr;  // filter-gradient window: padded dy rows, dw rows
+    if (mode == CONV_ADDR_WINDOW && !fwd) {
+        if ((rc = conv_padded_buffer(stream, (size_t)pbytes, &padded)) != GEMM_OK) return rc;
+        const int64_t P = d.out[0];
+        if ((rc = conv_filter_buffer(stream, (size_t)(d.k * P * wgeom.qp * es), &dyp)) != GEMM_OK ||
+            (rc = conv_result_buffer(stream, (size_t)(d.k * wgeom.cr * wgeom.sp) * sizeof(float),
+                                     &dwp)) != GEMM_OK)
+            return rc;
+        geom = wgeom;
+        bsrc = B_CONV_WGRAD_WIN;
+    } else if (mode == CONV_ADDR_WINDOW) {
         if ((rc = conv_padded_buffer(stream, (size_t)pbytes, &padded)) != GEMM_OK) return rc;
         // filters with rows padded to S' taps: K' = C_in R S'
         kdim = (int64_t)wgeom.cr * wgeom.sp;
@@ -768,12 +838,36 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
             g = GemmCall{dtype, dtype_out, GEMM_OP_N, GEMM_OP_N, d.k, vo, kdim, 1.0f, 0.0f,
                          filters, kdim, img, 1, static_cast<char *>(out) + n * d.k * vo * eso, vo,
                          bsrc, &geom};
-        else
+        else if (dyp != nullptr) {
+            // dw' (C_out x C_in R S') (+)= dy'[n] (C_out x P Q') . cols(x[n])^T, with the
+            // rows of dy[n] padded from Q to Q' positions (zeros)
+            const int64_t P = d.out[0], rows = d.k * P, total_dy = rows * wgeom.qp;
+            const dim3 grid((unsigned)((total_dy + kThreads - 1) / kThreads)), block(kThreads);
+            const void *dyn = static_cast<const char *>(a) + n * d.k * vo * es;
+            if (es == 4)
+                hipLaunchKernelGGL(conv_filter_pad_kernel<4>, grid, block, 0, stream, dyn, dyp,
+                                   (int)total_dy, (int)d.out[1], wgeom.qp);
+            else
+                hipLaunchKernelGGL(conv_filter_pad_kernel<2>, grid, block, 0, stream, dyn, dyp,
+                                   (int)total_dy, (int)d.out[1], wgeom.qp);
+            if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+            const int64_t ncols = (int64_t)wgeom.cr * wgeom.sp, kp = P * wgeom.qp;
+            g = GemmCall{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, ncols, kp, 1.0f,
+                         n == 0 ? 0.0f : 1.0f, dyp, kp, img, 1, dwp, ncols, bsrc, &geom};
+        } else
             // dw (C_out x C_in filter volume) (+)= dy[n] (C_out x output volume) . cols(x[n])^T
             g = GemmCall{dtype, GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_T, d.k, d.crs(), vo, 1.0f,
                          n == 0 ? 0.0f : 1.0f, static_cast<const char *>(a) + n * d.k * vo * es,
                          vo, img, 1, out, d.crs(), bsrc, &geom};
         if ((rc = gemm_run(g, -1, 0, stream)) != GEMM_OK) return rc;
+    }
+    if (dwp != nullptr) {
+        // dw = dw' without the zero-tap columns
+        const int64_t total = d.k * d.crs();
+        hipLaunchKernelGGL(conv_filter_unpad_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, static_cast<const float *>(dwp),
+                           static_cast<float *>(out), (int)total, wgeom.s, wgeom.sp);
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
     }
     return GEMM_OK;
 }

@@ -183,7 +183,9 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
 // Library-owned device buffers, one per (device, stream, slot), so that calls
 // on different streams never share one: slot 0 holds split-K partial sums,
 // slot 1 the convolution tables of the implicit GEMM, slot 2 its zero-padded
-// image, slot 3 its filters with padded rows.  A buffer only grows.
+// image, slot 3 its filters with padded rows (or, for the filter gradient,
+// the output gradient with padded rows), slot 4 that filter gradient with
+// padded rows.  A buffer only grows.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
@@ -250,7 +252,7 @@ int check_args(const Call &c)
     const int64_t a_row = c.transa == GEMM_OP_T ? c.M : c.K;
     const int64_t b_row = c.transb == GEMM_OP_T ? c.K : c.N;
     const bool implicit = c.bsrc != B_MATRIX;
-    if (implicit && (c.bsrc < B_CONV_FWD || c.bsrc > B_CONV_FWD_WIN || c.conv == nullptr ||
+    if (implicit && (c.bsrc < B_CONV_FWD || c.bsrc > B_CONV_WGRAD_WIN || c.conv == nullptr ||
                      c.transa != GEMM_OP_N ||
                      c.transb != (conv_fwd_source(c.bsrc) ? GEMM_OP_N : GEMM_OP_T) ||
                      (conv_table_source(c.bsrc) && c.conv->tab == nullptr)))
@@ -404,6 +406,16 @@ int conv_filter_buffer(hipStream_t stream, size_t bytes, void **out)
         return GEMM_ERR_NO_DEVICE;
     }
     return get_buffer(3, device, stream, bytes, out);
+}
+
+int conv_result_buffer(hipStream_t stream, size_t bytes, void **out)
+{
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_NO_DEVICE;
+    }
+    return get_buffer(4, device, stream, bytes, out);
 }
 
 void implicit_tile(int dtype, int64_t M, int *bn, int *bk, int *threads)

@@ -41,9 +41,10 @@ struct TileConfig {
     // indexed by B source - 1: [0] forward (B = cols), [1] filter gradient
     // (B = cols^T), [2] / [3] the same with table-looked-up per-k terms,
     // [4] / [5] the volume (3-D) forms, [6] .. [9] the 2-D and volume forms
-    // reading a zero-padded image, [10] the 2-D forward product from image
-    // windows in LDS; [aligned], as fn.  nullptr where the entry has none.
-    launch_fn implicit[11][2];
+    // reading a zero-padded image, [10] / [11] the 2-D forward product and
+    // filter gradient from image windows in LDS; [aligned], as fn.  nullptr
+    // where the entry has none.
+    launch_fn implicit[12][2];
 };
 
 // Declared here; defined in gemm_launch.hpp and explicitly instantiated by the
@@ -89,6 +90,9 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_LA_CFW ::dg::KMAJOR
 #define DG_LB_CFW ::dg::MNMAJOR
 #define DG_BSRC_CFW ::dg::B_CONV_FWD_WIN
+#define DG_LA_CWW ::dg::KMAJOR
+#define DG_LB_CWW ::dg::KMAJOR
+#define DG_BSRC_CWW ::dg::B_CONV_WGRAD_WIN
 
 // Memory orientation of op(A) / op(B) per layout combination: A as given is
 // k-contiguous, A^T (stored K x M) outer-contiguous; B as given is
@@ -190,10 +194,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
      DG_IFNS(BF16, BM, BN, BK, WM, WN, C3F), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3W),            \
      DG_IFNS(BF16, BM, BN, BK, WM, WN, CFP), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWP),            \
      DG_IFNS(BF16, BM, BN, BK, WM, WN, C3FP), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3WP),          \
-     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFW)}
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFW), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWW)}
 #define DG_IMPL_NONE                                                                          \
     {DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, \
-     DG_NOFNS, DG_NOFNS}
+     DG_NOFNS, DG_NOFNS, DG_NOFNS}
 #define DG_IMPL_ALL(...) DG_IMPL_NONE
 #define DG_IMPL_NN(...) DG_IMPL_NONE
 #define DG_IMPL_SKINNY(...) DG_IMPL_NONE

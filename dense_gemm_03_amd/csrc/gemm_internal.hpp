@@ -41,8 +41,11 @@ int gemm_run(const GemmCall &call, int forced_cfg, int forced_split, hipStream_t
 int conv_table_buffer(hipStream_t stream, size_t bytes, void **out);
 // The same for the zero-padded image of the implicit GEMM.
 int conv_padded_buffer(hipStream_t stream, size_t bytes, void **out);
-// The same for the filters with rows padded to S' taps (image-window source).
+// The same for the filters with rows padded to S' taps (image-window source),
+// or the output gradient with rows padded to Q' positions.
 int conv_filter_buffer(hipStream_t stream, size_t bytes, void **out);
+// The same for the filter gradient with rows padded to S' taps.
+int conv_result_buffer(hipStream_t stream, size_t bytes, void **out);
 
 // Block width BN, k-tile BK and threads of the entry gemm_run picks for an
 // implicit convolution product with M output channels.

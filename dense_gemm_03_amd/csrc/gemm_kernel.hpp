@@ -102,6 +102,10 @@ enum BSource {
     // read from a window of the zero-bordered image held in LDS (see
     // ConvWindow); A is the filters with each filter row padded to S' taps
     B_CONV_FWD_WIN = 11,
+    // filter gradient, 2-D, unit horizontal stride and dilation: the same
+    // windows, with A the output gradient with rows padded to Q' positions
+    // and C the gradient of the filters with rows padded to S' taps
+    B_CONV_WGRAD_WIN = 12,
 };
 
 __host__ __device__ constexpr bool conv_fwd_source(int b)
@@ -137,6 +141,11 @@ struct ConvGeom {
     int sp, cr, nr;
     uint64_t sp_magic, r_magic, w_magic;  // k / S', filter row / R, slot / W'
     int sp_shift, r_shift, w_shift;
+    // filter-gradient window: output rows padded to qp = Q' positions (a
+    // multiple of BK), k / Q'
+    int qp;
+    uint64_t qp_magic;
+    int qp_shift;
     // Table sources only: the terms that change along K, one entry per k --
     // per tap (ci, r, s) for the forward product, per output position (p, q)
     // for the filter gradient: {y | x << 16 (signed 16-bit each), byte offset}.
@@ -1128,22 +1137,141 @@ struct ConvWindow {
     }
 };
 
+// The filter-gradient product from the same windows ("Three X's", section
+// "CUTLASS", the implicit GEMM of the weight gradient): dW'[co][kp S' + s] =
+// sum over positions k of dY'[co][k] X[k][kp S' + s], k = p Q' + q with every
+// output row padded to Q' positions (a multiple of BK; dY' is zero at q >= Q)
+// and the taps of every filter row padded to S' (their columns are dropped by
+// the caller).  A lane's B fragment holds KS consecutive positions
+// q .. q + KS - 1 of one output row for one tap (kp, s): KS consecutive
+// image elements from x = q + s of image row (ci, p sh + r dh).  A block's
+// BN columns are BN / S' whole filter rows, fixed for the block; a k-tile's
+// BK positions lie in one output row p, from qa = k0 - p Q'.  So the window
+// of a k-tile is, per filter row j of the block, the BK + S' - 1 elements of
+// its image row from qa: slot (j, x') holds the KS elements from qa + x', at
+// j LP + x' (LP = BK + S' - 1 rounded up to the thread count).  A fragment is
+// slot (j, q_local + s): its offset is fixed per lane and step; per k-tile
+// only the uniform term (p sh W' + qa) changes.  Positions q >= Q are zeroed
+// in the fragment (dY' is zero there and a non-finite pixel must not meet
+// it).
 template <class G>
+struct ConvWindowW {
+    using In = typename G::In;
+    static constexpr int KS = G::KS;
+    static constexpr int U = G::TB::PER_THREAD;
+    static_assert(G::TB::CHUNKS == U * G::NT, "window slots fill the B stage");
+
+    __amdgpu_buffer_rsrc_t rsrc;
+    const ConvGeom *g;
+    int vrows, lp;       // NT-rows of slots per filter row, LP slots per filter row
+    int jrow[U];         // per staged load u: its filter row (uniform)
+    int col[U];          // element offset of its slot within the image for qa = 0,
+                         // p = 0: (ci Hp + r dh) W' + x', or -1 (no load)
+    int pos[G::FN];      // per B fragment: j LP + s of this lane's tap column
+
+    __device__ __forceinline__ ConvWindowW(const KernelArgs &a, int bn, int tid, int wcol, int lane)
+        : g(&a.conv)
+    {
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.B), 0, a.conv.img_bytes,
+                                                 0x00020000);  // gfx9 raw-buffer format word
+        const int len = G::BK + g->sp - 1;  // window slots per filter row
+        vrows = (len + G::NT - 1) / G::NT;
+        lp = vrows * G::NT;
+        const int kp_first = div_magic(bn, g->sp_magic, g->sp_shift);
+#pragma unroll
+        for (int fn = 0; fn < G::FN; ++fn) {
+            // columns past N repeat the last tap (their sums are not stored)
+            const int t = min(bn + wcol * G::WTN + fn * 32 + (lane & 31), a.N - 1) - bn;
+            const int j = div_magic(t, g->sp_magic, g->sp_shift);
+            pos[fn] = j * lp + (t - j * g->sp);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            jrow[u] = u / vrows;
+            const int xo = tid + (u - jrow[u] * vrows) * G::NT;  // slot within its filter row
+            const int kp = kp_first + jrow[u];
+            const int ci = div_magic(min(kp, g->cr - 1), g->r_magic, g->r_shift);
+            const int rr = min(kp, g->cr - 1) - ci * g->r;
+            col[u] = (xo < len) & (kp < g->cr) ? (ci * g->h + rr * g->dh) * g->w + xo : -1;
+        }
+    }
+
+    // The window of the k-tile at k0 (a multiple of BK, inside one output row).
+    __device__ __forceinline__ void load(int k0, u32x4 (&r)[U]) const
+    {
+        const int p = div_magic(k0, g->qp_magic, g->qp_shift);
+        const int shift = p * g->sh * g->w + (k0 - p * g->qp);  // uniform
+        const int npb = G::BN / g->sp;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (jrow[u] >= npb) break;  // past the window: no load (block-uniform)
+            const int off = col[u] >= 0 ? (col[u] + shift) * (int)sizeof(In) : (int)0x80000000u;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+            r[u] = u32x4{v[0], v[1], v[2], v[3]};
+        }
+    }
+
+    __device__ __forceinline__ void store(unsigned char *win, int tid, const u32x4 (&r)[U]) const
+    {
+        const int npb = G::BN / g->sp;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (jrow[u] >= npb) break;
+            lds_store16(win, (tid + u * G::NT) * 16, r[u]);
+        }
+    }
+
+    // Fragment step st of the k-tile at k0: positions q = qa + kk .. + KS - 1.
+    __device__ __forceinline__ u32x4 frag(const unsigned char *win, int k0, int st, int fn,
+                                          int lane) const
+    {
+        const int kk = (lane >> 5) * G::KH + st * KS;
+        const u32x4 v = lds_load16(win, (pos[fn] + kk) * 16);
+        const int p = div_magic(k0, g->qp_magic, g->qp_shift);
+        const int real = g->q - (k0 - p * g->qp) - kk;  // positions of the fragment below Q
+        if (real >= KS) return v;
+        uint32_t keep[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            if constexpr (KS == 8)
+                keep[d] = (2 * d < real ? 0x0000FFFFu : 0u) | (2 * d + 1 < real ? 0xFFFF0000u : 0u);
+            else
+                keep[d] = d < real ? 0xFFFFFFFFu : 0u;
+        }
+        return u32x4{v[0] & keep[0], v[1] & keep[1], v[2] & keep[2], v[3] & keep[3]};
+    }
+};
+
+template <class G>
+__device__ __forceinline__ u32x4 window_frag(const ConvWindow<G> &win, const unsigned char *w,
+                                             int, int st, int fn, int)
+{
+    return win.frag(w, st, fn);
+}
+template <class G>
+__device__ __forceinline__ u32x4 window_frag(const ConvWindowW<G> &win, const unsigned char *w,
+                                             int k0, int st, int fn, int lane)
+{
+    return win.frag(w, k0, st, fn, lane);
+}
+
+template <class G, class W>
 __device__ __forceinline__ void load_frags_window(const unsigned char *stage, const BlockCtx<G> &c,
-                                                  const ConvWindow<G> &win, int step, Frags<G> &f)
+                                                  const W &win, int k0, int step, Frags<G> &f)
 {
     const int kk = (c.lane >> 5) * G::KH + step * G::KS;
 #pragma unroll
     for (int fm = 0; fm < G::FM; ++fm)
         f.a[fm] = read_frag<typename G::TA>(stage, c.lane, c.wrow * G::WTM + fm * 32, kk);
 #pragma unroll
-    for (int fn = 0; fn < G::FN; ++fn) f.b[fn] = win.frag(stage + G::A_BYTES, step, fn);
+    for (int fn = 0; fn < G::FN; ++fn)
+        f.b[fn] = window_frag<G>(win, stage + G::A_BYTES, k0, step, fn, c.lane);
 }
 
-// main_loop_masked with the window source: A tiles as there, B from windows.
-template <bool ALIGNED, class G>
+// main_loop_masked with a window source: A tiles as there, B from windows.
+template <bool ALIGNED, class G, class W>
 __device__ __forceinline__ void main_loop_window(unsigned char *smem0, unsigned char *smem1,
-                                                 const BlockCtx<G> &c, const ConvWindow<G> &win,
+                                                 const BlockCtx<G> &c, const W &win,
                                                  int k_first, int ntiles,
                                                  floatx16 (&acc)[G::FM][G::FN])
 {
@@ -1160,7 +1288,7 @@ __device__ __forceinline__ void main_loop_window(unsigned char *smem0, unsigned 
     load(k_first);
     store(smem0);
     __syncthreads();
-    load_frags_window(smem0, c, win, 0, cur);
+    load_frags_window(smem0, c, win, k_first, 0, cur);
     for (int t = 0; t < ntiles; ++t) {
         unsigned char *stage = (t & 1) ? smem1 : smem0;
         unsigned char *other = (t & 1) ? smem0 : smem1;
@@ -1169,13 +1297,13 @@ __device__ __forceinline__ void main_loop_window(unsigned char *smem0, unsigned 
         if (more) load(k0 + G::BK);
 #pragma unroll
         for (int step = 0; step < G::STEPS - 1; ++step) {
-            load_frags_window(stage, c, win, step + 1, nxt);
+            load_frags_window(stage, c, win, k0, step + 1, nxt);
             mma(cur, acc);
             cur = nxt;
         }
         if (more) store(other);
         __syncthreads();
-        if (more) load_frags_window(other, c, win, 0, nxt);
+        if (more) load_frags_window(other, c, win, k0 + G::BK, 0, nxt);
         mma(cur, acc);
         cur = nxt;
     }
@@ -1261,6 +1389,9 @@ gemm_kernel(KernelArgs p)
     } else if constexpr (BSRC == B_CONV_FWD_WIN) {
         // implicit GEMM: A from memory, B fragments from image windows in LDS
         ConvWindow<G> win(p, c.bn, c.tid, c.wcol, c.lane);
+        main_loop_window<ALIGNED>(lds0, lds1, c, win, kbeg, ntiles, acc);
+    } else if constexpr (BSRC == B_CONV_WGRAD_WIN) {
+        ConvWindowW<G> win(p, c.bn, c.tid, c.wcol, c.lane);
         main_loop_window<ALIGNED>(lds0, lds1, c, win, kbeg, ntiles, acc);
     } else {
         // implicit GEMM: A from memory, B tiles formed from the image

@@ -133,26 +133,30 @@ int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x,
  *     the analytic terms and no padding, so no element needs a range check.
  *     Needs the padded image under 2 GiB (GEMM_ERR_INVALID_ARG otherwise);
  *     costs one extra read and write of the image per call;
- *   CONV_ADDR_WINDOW: for the forward product with unit horizontal stride
- *     and dilation, the padded copy as above, and the filters copied into a
- *     library-owned buffer with each filter row padded from S to S' taps (S
- *     rounded up to 8 bf16 or 4 fp32 taps, the extra taps zero); each block
- *     then loads, per k-tile, only the image rows its filter rows and output
- *     rows need into a window in LDS and reads every B fragment from it with
- *     one aligned 16-byte load (instead of gathering each matrix element).
- *     Applies when one k-tile's window fits the block's B stage; other calls
- *     (filter gradient, strides or dilations along the rows, larger windows)
- *     run the padded form.  Same error as CONV_ADDR_PADDED for the padded
- *     image;
+ *   CONV_ADDR_WINDOW: with unit horizontal stride and dilation, the padded
+ *     copy as above, and each block loads, per k-tile, only the image rows
+ *     its filter rows and output rows need into a window in LDS and reads
+ *     every B fragment from it with one aligned 16-byte load (instead of
+ *     gathering each matrix element).  Filter rows are padded from S to S'
+ *     taps (S rounded up to 8 bf16 or 4 fp32 taps): the forward product reads
+ *     a library-owned copy of the filters with zero extra taps; the filter
+ *     gradient accumulates into a library-owned buffer with S' taps per row
+ *     (copied to dw without the extra ones at the end) and reads a copy of
+ *     each dy[n] with its output rows padded with zeros to a multiple of the
+ *     k-tile.  Applies when one k-tile's window fits the block's staging
+ *     (for the filter gradient also S' dividing the block width); other
+ *     calls run the padded form.  Same error as CONV_ADDR_PADDED for the
+ *     padded image;
  *   CONV_ADDR_DEFAULT: the library's choice (what conv2d_fwd_implicit and
  *     conv2d_bwd_weight_implicit use): the window form where it applies and
- *     pays (the zero taps add at most a quarter, S' <= 5/4 S, and the window
- *     is at most half the B stage: wide filters), else the padded form when
- *     the padded image fits, else the analytic one.
+ *     pays (the padding adds at most a quarter, S' <= 5/4 S, and the window
+ *     is at most half the B stage: wide filters; for the filter gradient,
+ *     bf16 only), else the padded form when the padded image fits, else the
+ *     analytic one.
  * The analytic, table and padded forms give identical results (same
- * products, same summation order); the window form sums the same products
- * (plus zero taps) in a different k order, so its results differ from theirs
- * by rounding only.
+ * products, same summation order); the window forward product sums the same
+ * products (plus zero taps) in a different k order, so its results differ
+ * from theirs by rounding only.
  */
 typedef enum {
     CONV_ADDR_DEFAULT = 0,

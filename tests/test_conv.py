@@ -391,11 +391,14 @@ WINDOW_SHAPES = [
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_window_form_wide_filters(bf16):
-    """The image-window forward product on wide filters: exact on integers
-    (bf16 y: rounded once), within tolerance on random tensors, and the
-    default addressing within tolerance too."""
+    """The image-window forward product and filter gradient on wide filters:
+    exact on integers (bf16 y: rounded once), within tolerance on random
+    tensors, and the default addressing within tolerance too; a non-finite
+    pixel reaches exactly the outputs and taps whose sums include it."""
+    tol = TOL["bf16" if bf16 else "f32"]
     for t, c in enumerate(WINDOW_SHAPES):
         x, w = _ints(c.x_shape, 300 + t, bf16), _ints(c.w_shape, 310 + t, bf16)
+        dy = _ints(c.y_shape, 340 + t, bf16)
         ref, _ = oc.conv2d_fwd(x, w, c)
         for out_bf16 in (False, True):
             log("window %s %s out %s" % (c, "bf16" if bf16 else "f32", "bf16" if out_bf16 else "f32"))
@@ -404,8 +407,26 @@ def test_window_form_wide_filters(bf16):
                 assert np.array_equal(raw, oracle.round_to_bf16_bits(ref)), str(c)
             else:
                 assert np.array_equal(got, ref), str(c)
+        log("window filter gradient %s" % (c,))
+        assert np.array_equal(run_bwd(x, dy, c, "window"), oc.conv2d_bwd_weight(x, dy, c)[0]), str(c)
         x, w = _randn(c.x_shape, 320 + t, bf16), _randn(c.w_shape, 330 + t, bf16)
+        dy = _randn(c.y_shape, 350 + t, bf16)
         ref, S = oc.conv2d_fwd(x, w, c)
-        tol = TOL["bf16" if bf16 else "f32"]
         check_close(run_fwd(x, w, c, False, "window")[0], ref, S, tol, "window random %s" % (c,))
         check_close(run_fwd(x, w, c, False, True)[0], ref, S, tol, "default random %s" % (c,))
+        ref, S = oc.conv2d_bwd_weight(x, dy, c)
+        check_close(run_bwd(x, dy, c, "window"), ref, S, tol, "window filter gradient %s" % (c,))
+        check_close(run_bwd(x, dy, c, True), ref, S, tol, "default filter gradient %s" % (c,))
+    # non-finite pixels, inside and at the edges of the last shape's image
+    c = WINDOW_SHAPES[-1]
+    x, w, dy = _ints(c.x_shape, 360, bf16), _ints(c.w_shape, 361, bf16), _ints(c.y_shape, 362, bf16)
+    nan, inf = (np.uint16(0x7FC0), np.uint16(0x7F80)) if bf16 else (np.float32(np.nan), np.float32(np.inf))
+    x[0, 0, 3, 0], x[0, 0, 5, c.w - 1], x[0, 0, 2, 150] = inf, nan, inf
+    for what, got, ref in [("fwd", run_fwd(x, w, c, False, "window")[0], oc.conv2d_fwd(x, w, c)[0]),
+                           ("filter gradient", run_bwd(x, dy, c, "window"),
+                            oc.conv2d_bwd_weight(x, dy, c)[0])]:
+        cls = lambda a: np.select([np.isnan(a), np.isposinf(a), np.isneginf(a)], [1, 2, 3], 0)
+        assert np.any(~np.isfinite(ref)), what
+        assert np.array_equal(cls(got), cls(ref)), "window non-finite " + what
+        fin = np.isfinite(ref)
+        assert np.array_equal(got[fin], ref[fin]), "window non-finite " + what
