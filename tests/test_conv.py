@@ -430,3 +430,40 @@ def test_window_form_wide_filters(bf16):
         assert np.array_equal(cls(got), cls(ref)), "window non-finite " + what
         fin = np.isfinite(ref)
         assert np.array_equal(got[fin], ref[fin]), "window non-finite " + what
+
+
+def _random_window_shapes(n, seed):
+    """Seeded shapes with unit horizontal stride and dilation and 13- to
+    32-wide filters: every C_out class (tile entry), padding, vertical
+    stride and dilation, rows of any length."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        s = int(rng.integers(13, 33))
+        r = int(rng.integers(1, 6))
+        dh = int(rng.integers(1, 3))
+        sh = int(rng.integers(1, 3))
+        ph = int(rng.integers(0, r))
+        pw = int(rng.integers(0, s // 2 + 1))
+        h = int(rng.integers(max(1, (r - 1) * dh + 1 - 2 * ph), 14))
+        w = int(rng.integers(max(1, s - 2 * pw), 160))
+        c = ConvShape(int(rng.integers(1, 3)), int(rng.integers(1, 4)), h, w,
+                      int(rng.choice([3, 17, 40, 70, 130, 300])), r, s, ph, pw, sh, 1, dh, 1)
+        if c.p >= 1 and c.q >= 1:
+            out.append(c)
+    return out
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_window_form_random_shapes(bf16):
+    """Both image-window products on seeded random wide-filter shapes, exact on
+    integers (the form runs where its window fits, the padded gather
+    elsewhere; both must be exact)."""
+    for t, c in enumerate(_random_window_shapes(16, 7 + bf16)):
+        x, w = _ints(c.x_shape, 400 + t, bf16), _ints(c.w_shape, 430 + t, bf16)
+        dy = _ints(c.y_shape, 460 + t, bf16)
+        log("random window shape %d %s" % (t, c))
+        got, _ = run_fwd(x, w, c, False, "window")
+        assert np.array_equal(got, oc.conv2d_fwd(x, w, c)[0]), "fwd %s" % (c,)
+        assert np.array_equal(run_bwd(x, dy, c, "window"), oc.conv2d_bwd_weight(x, dy, c)[0]), \
+            "filter gradient %s" % (c,)
