@@ -127,11 +127,22 @@ def measure(name: str, steps: int, warmup: int):
     ta, tb = int(w.transa), int(w.transb)
     cfg = dg.gemm_select_config_ex(dtype_id, ta, tb, w.M, w.N, w.K)
     splits = dg.gemm_split_k_ex(dtype_id, cfg, ta, tb, w.M, w.N, w.K)
+    # Workloads judged on HBM bandwidth whose operands would fit the 256 MB
+    # MALL (Infinity Cache) across back-to-back steps rotate over three copies
+    # of A and B, so every step streams its operands from HBM.  (The im2col
+    # shape's 4 GB B cannot stay cached; the compute-bound shapes are not
+    # judged on bandwidth.)
+    operands = [(A, B)]
+    if name == "tall":
+        operands += [(A.clone(), B.clone()) for _ in range(2)]
+    turn = [0]
 
     def step():
         # with beta != 0 every step accumulates into C again: same work, the
         # values only grow (they stay finite over these step counts)
-        dg.gemm(A, B, out=C, alpha=w.alpha, beta=w.beta, transa=w.transa, transb=w.transb)
+        a_op, b_op = operands[turn[0] % len(operands)]
+        turn[0] += 1
+        dg.gemm(a_op, b_op, out=C, alpha=w.alpha, beta=w.beta, transa=w.transa, transb=w.transb)
 
     for _ in range(warmup):
         step()
@@ -176,8 +187,9 @@ def measure(name: str, steps: int, warmup: int):
             "traffic": traffic,
         },
         "hbm_gbs": w.algorithmic_bytes / (event_ms * 1e-3) / 1e9,
+        "operand_sets": len(operands),
     }
-    del A, B, C
+    del A, B, C, operands
     torch.cuda.empty_cache()
     return res
 
@@ -462,10 +474,16 @@ def main() -> int:
         "cpu_baseline": cpu,
         "also": {n: {k: r[k] for k in ("value", "ms_per_step", "dtype", "op", "alpha", "beta",
                                         "c_dtype", "kernel_config", "split_k", "roofline",
-                                        "hbm_gbs")} for n, r in also.items()},
+                                        "hbm_gbs", "operand_sets")} for n, r in also.items()},
     }
     if conv:
         line["convolution"] = conv
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    line["device"] = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
+                      "compute_units": prop.multi_processor_count,
+                      "memory_gib": round(prop.total_memory / 2**30, 1),
+                      "hip": torch.version.hip}
     print(json.dumps(line), flush=True)
     return 0
 
