@@ -56,15 +56,16 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-# Sources that define each kernel family's device code: stored counter
-# readings are used only while these are unchanged.
+# Sources that define each kernel family's device code (and, for the
+# convolution routes, the dispatcher that picks their GEMM kernels): stored
+# counter readings are used only while these are unchanged.
 KERNEL_SOURCES = {
     "gemm": ["gemm_kernel.hpp", "gemm_launch.hpp", "gemm_instances.hip"],
     "im2col": ["conv.hip"],
     # a convolution route: im2col and/or the GEMM kernels, the reduce, the
     # implicit loaders and their table and pad kernels
     "conv": ["conv.hip", "gemm_kernel.hpp", "gemm_launch.hpp", "gemm_instances.hip",
-             "gemm_aux.hip"],
+             "gemm_aux.hip", "gemm_api.hip"],
 }
 
 

@@ -92,6 +92,11 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
     const bool skinny = M <= 32 && N >= 1024;
     if (dtype == GEMM_DTYPE_F32) {
         static const int tall = config_index(dtype, "f32_128x64_w2x2_s2");
+        // wide: A . B takes two LDS stages (80 KB: two resident blocks per
+        // CU, so one block's loads run under the other's products; measured
+        // 3-11% faster than three stages at M = 64, N 8192-16384, and equal
+        // at N = 2048); the other operand forms have the three-stage entry
+        static const int wide_nn = config_index(dtype, "f32_64x256_w1x4_s2");
         static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
         static const int wide_t = config_index(dtype, "f32_64x128x64_w1x4_s2");
         static const int skinny_n = config_index(dtype, "f32_32x128_w1x4_s3");
@@ -106,7 +111,8 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
         if (N <= 64 && M >= 4096) return tall;   // tall-skinny: many 64-row blocks
         if (skinny && layout == LAYOUT_NN) return skinny_n;
         if (skinny && layout == LAYOUT_NT) return skinny_t;
-        if (M <= 64 && N >= 1024) return layout == LAYOUT_NT ? wide_t : wide;  // split-K
+        if (M <= 64 && N >= 1024)  // split-K
+            return layout == LAYOUT_NT ? wide_t : layout == LAYOUT_NN ? wide_nn : wide;
         if (M >= 2048 && N >= 2048) return best_of(dtype, large, 3, M, N);
         if (N <= 64) return narrow;
         return small;
@@ -135,6 +141,11 @@ int select_implicit(int dtype, int64_t M)
 {
     if (dtype == GEMM_DTYPE_F32) {
         static const int skinny = config_index(dtype, "f32_32x128_w1x4_s3");
+        // wide: A . B takes two LDS stages (80 KB: two resident blocks per
+        // CU, so one block's loads run under the other's products; measured
+        // 3-11% faster than three stages at M = 64, N 8192-16384, and equal
+        // at N = 2048); the other operand forms have the three-stage entry
+        static const int wide_nn = config_index(dtype, "f32_64x256_w1x4_s2");
         static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
         static const int mid = config_index(dtype, "f32_128x128_w2x2_s2");
         static const int large = config_index(dtype, "f32_256x128_w4x2_s2");

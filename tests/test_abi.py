@@ -70,7 +70,11 @@ def test_shape_classes_of_the_workloads():
     assert _cfg_for("bf16-8192")[2] == "bf16_256x256x32_w4x2_s4"
     assert _cfg_for("tall")[2] == "f32_128x64_w2x2_s2"
     dtype, c, name, splits = _cfg_for("im2col")
-    assert name == "f32_64x256_w1x4_s3" and splits == 8
+    assert name == "f32_64x256_w1x4_s2" and splits == 8
+    # the same class for A^T . B (no two-stage kernel for that form)
+    F32 = dg.GEMM_DTYPE_F32
+    assert dg.gemm_config_name(F32, dg.gemm_select_config_ex(F32, 1, 0, 64, 16384, 61504)) == \
+        "f32_64x256_w1x4_s3"
     # the convolution GEMMs with 32 output channels: 32-row blocks; the
     # filter gradient (B^T) with 256-byte k-contiguous rows and 16 slices
     F32, BF16 = dg.GEMM_DTYPE_F32, dg.GEMM_DTYPE_BF16
