@@ -54,7 +54,12 @@
  * touch the GPU.
  *
  * Threads: the entry points may be called from several host threads; the
- * tile table is read-only and the workspace is guarded by a mutex.
+ * tile table is read-only and the workspace is guarded by a mutex.  Library
+ * buffers are kept per (device, stream): calls on different streams never
+ * share one.  Two threads must not call on the same stream at the same time
+ * (the order of their work on that stream would be undefined anyway): a call
+ * that grows a stream's buffer frees the old one, which a concurrent call on
+ * that stream may still be about to use.
  */
 #ifndef DENSE_GEMM_03_AMD_GEMM_H
 #define DENSE_GEMM_03_AMD_GEMM_H
