@@ -137,7 +137,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("f32_32x128x64_w1x4_s2", false, 32, 128, 64, 1, 4, 2, 1, KK)          \
     X("f32_32x128x64_w1x4_s3", false, 32, 128, 64, 1, 4, 3, 1, KK)          \
     X("f32_32x256x64_w1x4_s2", false, 32, 256, 64, 1, 4, 2, 1, KK)          \
-    X("f32_64x128x64_w1x4_s2", false, 64, 128, 64, 1, 4, 2, 1, KK)
+    X("f32_64x128x64_w1x4_s2", false, 64, 128, 64, 1, 4, 2, 1, KK)         \
+    X("f32_64x64x64_w2x2_s2", false, 64, 64, 64, 2, 2, 2, 1, KK)
 
 #define DG_BF16_TABLE(X)                                                    \
     X("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 4, ALL)       \
