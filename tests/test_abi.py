@@ -84,7 +84,7 @@ def test_shape_classes_of_the_workloads():
     assert sel(BF16, 0, 32, 65536, 10976) == "bf16_32x256x64_w1x4_s3"
     assert sel(BF16, 1, 32, 10976, 65536) == "bf16_32x256x128_w1x4_s2"
     assert sel(F32, 1, 64, 61504, 16384) == "f32_64x64x64_w2x2_s2"
-    assert sel(BF16, 1, 64, 61504, 16384) == "bf16_64x64x256_w2x2_s2"
+    assert sel(BF16, 1, 64, 61504, 16384) == "bf16_64x64x64_w2x2_s4"
     c = dg.gemm_select_config_ex(F32, 0, 1, 32, 10976, 65536)
     assert dg.gemm_split_k_ex(F32, c, 0, 1, 32, 10976, 65536) == 16
     c = dg.gemm_select_config_ex(F32, 0, 1, 64, 61504, 16384)
