@@ -147,11 +147,6 @@ int select_implicit(int dtype, int64_t M)
 {
     if (dtype == GEMM_DTYPE_F32) {
         static const int skinny = config_index(dtype, "f32_32x128_w1x4_s3");
-        // wide: A . B takes two LDS stages (80 KB: two resident blocks per
-        // CU, so one block's loads run under the other's products; measured
-        // 3-11% faster than three stages at M = 64, N 8192-16384, and equal
-        // at N = 2048); the other operand forms have the three-stage entry
-        static const int wide_nn = config_index(dtype, "f32_64x256_w1x4_s2");
         static const int wide = config_index(dtype, "f32_64x256_w1x4_s3");
         static const int mid = config_index(dtype, "f32_128x128_w2x2_s2");
         static const int large = config_index(dtype, "f32_256x128_w4x2_s2");

@@ -1192,7 +1192,7 @@ struct ConvWindowW {
             const int kp = kp_first + jrow[u];
             const int ci = div_magic(min(kp, g->cr - 1), g->r_magic, g->r_shift);
             const int rr = min(kp, g->cr - 1) - ci * g->r;
-            col[u] = (xo < len) & (kp < g->cr) ? (ci * g->h + rr * g->dh) * g->w + xo : -1;
+            col[u] = ((xo < len) & (kp < g->cr)) ? (ci * g->h + rr * g->dh) * g->w + xo : -1;
         }
     }
 
