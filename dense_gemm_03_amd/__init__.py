@@ -229,6 +229,8 @@ def gemm(A, B, out=None, cfg: int | None = None, split_k: int = 0, stream=None, 
         raise TypeError("A and B must both be float32 or both bfloat16")
     if A.device.type != "cuda" or B.device.type != "cuda":
         raise ValueError("A and B must be GPU tensors")
+    if B.device != A.device:
+        raise ValueError("A and B must be on the same GPU")
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A and B must be 2-D")
     M, K = (A.shape[1], A.shape[0]) if transa else (A.shape[0], A.shape[1])
@@ -251,19 +253,22 @@ def gemm(A, B, out=None, cfg: int | None = None, split_k: int = 0, stream=None, 
     bf16 = A.dtype == torch.bfloat16
     plain = (alpha == 1.0 and beta == 0.0 and not transa and not transb
              and out_dtype == torch.float32)
-    if plain:
-        args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, stream)
-        if cfg is None:
-            rc = (gemm_bf16 if bf16 else gemm_f32)(*args)
+    # the library launches on the calling thread's current device
+    with torch.cuda.device(A.device):
+        if plain:
+            args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, stream)
+            if cfg is None:
+                rc = (gemm_bf16 if bf16 else gemm_f32)(*args)
+            else:
+                rc = (gemm_bf16_with_config if bf16 else gemm_f32_with_config)(cfg, split_k,
+                                                                                *args)
         else:
-            rc = (gemm_bf16_with_config if bf16 else gemm_f32_with_config)(cfg, split_k, *args)
-    else:
-        args = (GEMM_DTYPE_BF16 if bf16 else GEMM_DTYPE_F32,
-                GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32,
-                GEMM_OP_T if transa else GEMM_OP_N, GEMM_OP_T if transb else GEMM_OP_N,
-                M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta),
-                out.data_ptr(), ldc, stream)
-        rc = gemm_ex(*args) if cfg is None else gemm_ex_with_config(cfg, split_k, *args)
+            args = (GEMM_DTYPE_BF16 if bf16 else GEMM_DTYPE_F32,
+                    GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32,
+                    GEMM_OP_T if transa else GEMM_OP_N, GEMM_OP_T if transb else GEMM_OP_N,
+                    M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta),
+                    out.data_ptr(), ldc, stream)
+            rc = gemm_ex(*args) if cfg is None else gemm_ex_with_config(cfg, split_k, *args)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return out
@@ -429,19 +434,23 @@ def conv2d(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=None
     import torch
     if w.dtype != x.dtype or not w.is_contiguous() or w.dim() != 4:
         raise TypeError("w must be a contiguous 4-D tensor of x's dtype")
+    if w.device != x.device:
+        raise ValueError("x and w must be on the same GPU")
     params, dtype, P, Q, need = _conv_setup(x, tuple(w.shape), stride, padding, dilation)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     y = torch.empty((x.shape[0], w.shape[0], P, Q), dtype=out_dtype, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     dtype_y = GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32
-    if implicit:
-        rc = conv2d_fwd_implicit_ex(dtype, dtype_y, params, _ADDRESSING[implicit], x.data_ptr(),
-                                    w.data_ptr(), y.data_ptr(), stream)
-    else:
-        ws = _workspace(workspace, need, x.device)
-        rc = conv2d_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
-                        ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    # the library launches on the calling thread's current device
+    with torch.cuda.device(x.device):
+        if implicit:
+            rc = conv2d_fwd_implicit_ex(dtype, dtype_y, params, _ADDRESSING[implicit], x.data_ptr(),
+                                        w.data_ptr(), y.data_ptr(), stream)
+        else:
+            ws = _workspace(workspace, need, x.device)
+            rc = conv2d_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                            ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return y
@@ -458,16 +467,20 @@ def conv2d_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wor
     if dy.dtype != x.dtype or not dy.is_contiguous() or \
             tuple(dy.shape) != (x.shape[0], weight_shape[0], P, Q):
         raise ValueError("dy must be a contiguous (N, C_out, P, Q) tensor of x's dtype")
+    if dy.device != x.device:
+        raise ValueError("x and dy must be on the same GPU")
     dw = torch.empty(tuple(weight_shape), dtype=torch.float32, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    if implicit:
-        rc = conv2d_bwd_weight_implicit_ex(dtype, params, _ADDRESSING[implicit], x.data_ptr(),
-                                           dy.data_ptr(), dw.data_ptr(), stream)
-    else:
-        ws = _workspace(workspace, need, x.device)
-        rc = conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                               ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    # the library launches on the calling thread's current device
+    with torch.cuda.device(x.device):
+        if implicit:
+            rc = conv2d_bwd_weight_implicit_ex(dtype, params, _ADDRESSING[implicit], x.data_ptr(),
+                                               dy.data_ptr(), dw.data_ptr(), stream)
+        else:
+            ws = _workspace(workspace, need, x.device)
+            rc = conv2d_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                                   ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return dw
@@ -505,19 +518,23 @@ def conv_nd(x, w, stride=1, padding=0, dilation=1, out_dtype=None, workspace=Non
     import torch
     if w.dtype != x.dtype or not w.is_contiguous():
         raise TypeError("w must be a contiguous tensor of x's dtype")
+    if w.device != x.device:
+        raise ValueError("x and w must be on the same GPU")
     params, dtype, out, need = _convnd_setup(x, tuple(w.shape), stride, padding, dilation)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     y = torch.empty((x.shape[0], w.shape[0]) + out, dtype=out_dtype, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     dtype_y = GEMM_DTYPE_BF16 if out_dtype == torch.bfloat16 else GEMM_DTYPE_F32
-    if implicit:
-        rc = convnd_fwd_implicit_ex(dtype, dtype_y, params, _ADDRESSING[implicit], x.data_ptr(),
-                                    w.data_ptr(), y.data_ptr(), stream)
-    else:
-        ws = _workspace(workspace, need, x.device)
-        rc = convnd_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
-                        ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    # the library launches on the calling thread's current device
+    with torch.cuda.device(x.device):
+        if implicit:
+            rc = convnd_fwd_implicit_ex(dtype, dtype_y, params, _ADDRESSING[implicit], x.data_ptr(),
+                                        w.data_ptr(), y.data_ptr(), stream)
+        else:
+            ws = _workspace(workspace, need, x.device)
+            rc = convnd_fwd(dtype, dtype_y, params, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                            ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return y
@@ -534,16 +551,20 @@ def conv_nd_weight_grad(x, dy, weight_shape, stride=1, padding=0, dilation=1, wo
     if dy.dtype != x.dtype or not dy.is_contiguous() or \
             tuple(dy.shape) != (x.shape[0], weight_shape[0]) + out:
         raise ValueError("dy must be a contiguous (N, C_out, O_0 ..) tensor of x's dtype")
+    if dy.device != x.device:
+        raise ValueError("x and dy must be on the same GPU")
     dw = torch.empty(tuple(weight_shape), dtype=torch.float32, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    if implicit:
-        rc = convnd_bwd_weight_implicit_ex(dtype, params, _ADDRESSING[implicit], x.data_ptr(),
-                                           dy.data_ptr(), dw.data_ptr(), stream)
-    else:
-        ws = _workspace(workspace, need, x.device)
-        rc = convnd_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
-                               ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    # the library launches on the calling thread's current device
+    with torch.cuda.device(x.device):
+        if implicit:
+            rc = convnd_bwd_weight_implicit_ex(dtype, params, _ADDRESSING[implicit], x.data_ptr(),
+                                               dy.data_ptr(), dw.data_ptr(), stream)
+        else:
+            ws = _workspace(workspace, need, x.device)
+            rc = convnd_bwd_weight(dtype, params, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                                   ws.data_ptr(), ws.numel() * ws.element_size(), stream)
     if rc != GEMM_OK:
         raise GemmError(rc)
     return dw
