@@ -285,7 +285,7 @@ def test_generators_nd_shapes_and_conv_workloads():
     assert workloads.uniform_f32((9,), 1).shape == (9,)
     for c in workloads.CONV_WORKLOADS.values():
         if c.crs * c.p * c.q > 1 << 24:
-            continue  # the full-size ones are drawn on the GPU machine only
+            continue  # the full-size ones are drawn only where a GPU runs them
         assert c.x().shape == (c.batch, c.cin, c.h, c.w)
         assert c.weights().shape == (c.cout, c.cin, c.r, c.s)
         assert c.dy().shape == (c.batch, c.cout, c.p, c.q)
