@@ -4,28 +4,33 @@
 One step is one call of the library's GEMM (grid decomposition, global->LDS
 staging, MFMA main loop, edge handling and epilogue, and for the split-K class
 the reduce) on a seeded synthetic workload whose operands are already resident
-in HBM.  Prints ONE JSON line:
+in HBM.  Prints ONE JSON line (last line of stdout):
 
-  metric / value / unit   GEMM TFLOP/s (2*M*N*K per step over the timed steps)
-  roofline                the GEMM kernel against the MI355X dense matrix peak of
-                          its input type, from HIP events on the stream the
-                          kernel runs on; traffic from the committed rocprofv3
-                          counter summary when it matches the current sources
+  metric / value / unit   GEMM TFLOP/s of --workload (default fp32 4096^3):
+                          2*M*N*K per step over the timed steps
+  roofline                the GEMM kernel against the MI355X dense matrix peak
+                          of its input type (the tall-skinny shape: achieved
+                          HBM GB/s against 8 TB/s), from HIP events on the
+                          stream the kernel runs on; `traffic` is the HBM bytes
+                          per launch read from the committed rocprofv3 counter
+                          summary (profiles/traffic.json) when it was taken on
+                          the current sources, else null -- it is a stored
+                          reading, not measured in this run
+  sclk                    the graphics clock sampled (amdsmi GPU metrics)
+                          while the timed steps ran, when readable
   cpu_baseline            the oracle (CPU, fp64) timed on a bounded sample of the
                           same workload on this host
-  also                    the same measurement for the other headline workload
-                          (bf16 8192^3), and with --all for the im2col and
-                          tall-skinny shapes and the generalised-GEMM variants
-                          (transposed operands, alpha/beta, bf16 C)
-  convolution             the im2col + GEMM convolution of the 64-channel
-                          31x31-filter workload, fp32 and bf16 (forward,
-                          filter gradient, their implicit-GEMM forms with
-                          analytic, table and padded-image address
-                          generation and both products from image
-                          windows, and the im2col kernel against HBM),
-                          and of the 3-D (7x7x7 filters, fp32 and bf16; also
-                          through the implicit GEMM, analytic and padded)
-                          and 4-D workloads
+  also                    the same measurement, in short form, for the other
+                          configurations: bf16 8192^3, the im2col and
+                          tall-skinny shapes, fp32 1000^3 and the ragged
+                          4097 x 4095 x 4099 (all measured before the headline
+                          workload, each with its own warm-up); with --all
+                          also the generalised-GEMM variants (transposed
+                          operands, alpha/beta, bf16 C)
+
+With --all the convolution routes (im2col + GEMM, implicit GEMM with each
+address form, the im2col kernel against HBM; 2-D, 3-D and 4-D workloads) are
+timed too and printed as a separate JSON line before the last one.
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -46,8 +51,11 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense matrix peaks
 HBM_PEAK_GBS = 8000.0
 PRIMARY = "fp32-4096"
-SECONDARY = ["bf16-8192"]
-EXTRA = ["im2col", "tall", "bf16-8192-nt-bf16c", "bf16-8192-tn-acc", "fp32-4096-tt-ab"]
+SECONDARY = ["bf16-8192", "im2col", "tall", "fp32-1000", "fp32-rag"]
+EXTRA = ["bf16-8192-nt-bf16c", "bf16-8192-tn-acc", "fp32-4096-tt-ab"]
+# Judged on HBM bandwidth rather than matrix throughput (its MFMA-limited time
+# at the fp32 peak caps the achievable rate below 8 TB/s).
+HBM_BOUND = {"tall"}
 CONV = ["conv-64c-31k", "conv-64c-31k-bf16", "conv3d-32c-k7", "conv3d-32c-k7-bf16",
         "conv4d-16c-k5"]
 
@@ -94,6 +102,77 @@ def stored_traffic(workload: str, family: str = "gemm", config: str | None = Non
     if config is not None and entry.get("config") != config:
         return None
     return entry.get("bytes_per_launch")
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi GPU metrics) on a background
+    thread while a timed region runs.  Readings come from the SMU's metrics
+    table; when amdsmi is missing or the call is not permitted the result
+    says why instead."""
+
+    def __init__(self):
+        self.err = None
+        self.handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) != 1:
+                raise RuntimeError("%d GPUs visible to amdsmi, expected 1" % len(handles))
+            self.handle = handles[0]
+            self.amdsmi = amdsmi
+            self._read()
+        except Exception as e:  # noqa: BLE001 - reported, not fatal
+            self.err = "%s: %s" % (type(e).__name__, e)
+            self.handle = None
+
+    def _read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        cur = m.get("current_gfxclk")
+        if clks:
+            return float(sum(clks)) / len(clks)
+        if isinstance(cur, (int, float)) and cur > 0:
+            return float(cur)
+        raise RuntimeError("no graphics clock in the GPU metrics")
+
+    def start(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        if self.handle is None:
+            return
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:  # noqa: BLE001
+                    self.err = "%s: %s" % (type(e).__name__, e)
+                    return
+                time.sleep(0.0005)
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self.handle is None:
+            return {"mhz": None, "error": self.err}
+        self._stop.set()
+        self._thread.join()
+        s = sorted(self.samples)
+        if not s:
+            return {"mhz": None, "error": self.err or "no sample"}
+        return {"mhz": s[len(s) // 2], "min_mhz": s[0], "max_mhz": s[-1], "samples": len(s),
+                "source": "amdsmi gpu_metrics current_gfxclk(s), median over the timed steps"}
+
+
+_CLOCK = None
+
+
+def clock_sampler():
+    global _CLOCK
+    if _CLOCK is None:
+        _CLOCK = ClockSampler()
+    return _CLOCK
 
 
 def _workload(name: str):
@@ -155,7 +234,9 @@ def measure(name: str, steps: int, warmup: int):
     # stream, passed to the C ABI), bracketing the timed region.
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    clock = clock_sampler()
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
@@ -163,12 +244,27 @@ def measure(name: str, steps: int, warmup: int):
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = clock.stop()
     event_ms = ev0.elapsed_time(ev1) / steps
     ms_per_step = wall * 1e3 / steps
     tflops = w.flops * steps / wall / 1e12
     achieved = w.flops / (event_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = stored_traffic(name, "gemm", dg.gemm_config_name(dtype_id, cfg))
+    hbm_gbs = w.algorithmic_bytes / (event_ms * 1e-3) / 1e9
+    if name in HBM_BOUND:
+        # the shape is judged on HBM bandwidth; at the fp32 matrix peak its
+        # flops alone take w.flops / peak, which caps the reachable rate
+        roofline = {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": hbm_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                    "mfma_cap_gbs": w.algorithmic_bytes / (w.flops / (peak * 1e12)) / 1e9,
+                    "tflops": achieved}
+    else:
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak, "traffic": traffic}
+    roofline["traffic_source"] = ("stored rocprofv3 FETCH_SIZE/WRITE_SIZE reading "
+                                  "(profiles/traffic.json), not measured in this run"
+                                  if traffic is not None else None)
     res = {
         "workload": name,
         "M": w.M, "N": w.N, "K": w.K,
@@ -179,16 +275,10 @@ def measure(name: str, steps: int, warmup: int):
         "ms_per_step": ms_per_step,
         "kernel_config": dg.gemm_config_name(dtype_id, cfg),
         "split_k": splits,
-        "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": achieved / peak,
-            "traffic": traffic,
-        },
-        "hbm_gbs": w.algorithmic_bytes / (event_ms * 1e-3) / 1e9,
+        "roofline": roofline,
+        "hbm_gbs": hbm_gbs,
         "operand_sets": len(operands),
+        "sclk": sclk,
     }
     del A, B, C, operands
     torch.cuda.empty_cache()
@@ -389,7 +479,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--all", action="store_true",
-                    help="also time the im2col and tall shapes and the generalised-GEMM variants")
+                    help="also time the generalised-GEMM variants and the convolution routes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true",
                     help="time only --workload (for per-kernel profiler passes)")
@@ -433,24 +523,49 @@ def main() -> int:
             args.conv, args.steps, args.warmup, args.conv_route)}}), flush=True)
         return 0
 
-    main_res = measure(args.workload, args.steps, args.warmup)
+    # The other configurations first, each with its own warm-up, then the
+    # headline workload: W warm-up steps and K timed steps of it, on a GPU
+    # that has been running (its clock settled) rather than straight after
+    # process start.
     also = {}
     others = [] if args.no_also else [
         n for n in SECONDARY + (EXTRA if args.all else []) if n != args.workload]
     for n in others:
         also[n] = measure(n, max(10, args.steps // 2), max(20, args.warmup))
 
-    conv = {}
-    if not args.no_also:
+    if args.all and not args.no_also:
+        conv = {}
         for n in CONV:
             conv[n] = measure_conv(n, max(10, args.steps // 5), max(5, args.warmup // 5))
+        # its own line, before the result line
+        print(json.dumps({"convolution": conv}), flush=True)
+
+    main_res = measure(args.workload, args.steps, args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] oracle baseline on the host")
         cpu = cpu_baseline(args.workload)
 
+    def short(r):
+        rf = dict(r["roofline"])
+        rf.pop("traffic_source", None)
+        for k in ("achieved", "frac", "mfma_cap_gbs", "tflops"):
+            if rf.get(k) is not None:
+                rf[k] = round(rf[k], 4 if k == "frac" else 1)
+        if rf.get("traffic") is not None:
+            rf["traffic"] = int(rf["traffic"])
+        out = {"shape": "%s %dx%dx%d %s" % (r["dtype"], r["M"], r["N"], r["K"], r["op"]),
+               "value": round(r["value"], 2), "ms_per_step": round(r["ms_per_step"], 4),
+               "kernel_config": r["kernel_config"], "split_k": r["split_k"], "roofline": rf,
+               "sclk_mhz": r["sclk"].get("mhz")}
+        if r["alpha"] != 1.0 or r["beta"] != 0.0 or r["c_dtype"] != "f32":
+            out["alpha"], out["beta"], out["c_dtype"] = r["alpha"], r["beta"], r["c_dtype"]
+        return out
+
     w = main_res
+    import torch
+    prop = torch.cuda.get_device_properties(0)
     line = {
         "metric": "GEMM TFLOP/s and % of MI355X matrix peak (fp32 4096^3, bf16 8192^3)",
         "value": w["value"],
@@ -472,19 +587,13 @@ def main() -> int:
             "parallelism": "single GPU",
         },
         "roofline": w["roofline"],
+        "sclk": w["sclk"],
         "cpu_baseline": cpu,
-        "also": {n: {k: r[k] for k in ("value", "ms_per_step", "dtype", "op", "alpha", "beta",
-                                        "c_dtype", "kernel_config", "split_k", "roofline",
-                                        "hbm_gbs", "operand_sets")} for n, r in also.items()},
+        "also": {n: short(r) for n, r in also.items()},
+        "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
+                   "compute_units": prop.multi_processor_count,
+                   "memory_gib": round(prop.total_memory / 2**30, 1), "hip": torch.version.hip},
     }
-    if conv:
-        line["convolution"] = conv
-    import torch
-    prop = torch.cuda.get_device_properties(0)
-    line["device"] = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
-                      "compute_units": prop.multi_processor_count,
-                      "memory_gib": round(prop.total_memory / 2**30, 1),
-                      "hip": torch.version.hip}
     print(json.dumps(line), flush=True)
     return 0
 

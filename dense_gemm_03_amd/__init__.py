@@ -26,6 +26,8 @@ GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_HIP = -2
 GEMM_ERR_NO_DEVICE = -3
 GEMM_ERR_OUT_OF_MEMORY = -4
+GEMM_ERR_INTERNAL = -5
+GEMM_ERR_CAPTURING = -6
 GEMM_DTYPE_F32 = 0
 GEMM_DTYPE_BF16 = 1
 GEMM_OP_N = 0
@@ -50,6 +52,7 @@ SIGNATURES = {
     "gemm_ex": (_int, _GEMM_EX_ARGS),
     "gemm_ex_with_config": (_int, [_int, _int] + _GEMM_EX_ARGS),
     "gemm_config_layouts": (_int, [_int, _int]),
+    "gemm_release_buffers": (_int, [_p]),
 }
 
 
@@ -162,6 +165,10 @@ def gemm_ex_with_config(cfg, split_k, dtype_ab, dtype_c, transa, transb, M, N, K
                         ldb, beta, C, ldc, stream=None) -> int:
     return load_library().gemm_ex_with_config(cfg, split_k, dtype_ab, dtype_c, transa, transb, M, N,
                                               K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_release_buffers(stream=None) -> int:
+    return load_library().gemm_release_buffers(stream)
 
 
 def gemm_config_layouts(dtype: int, cfg: int) -> int:

@@ -41,6 +41,7 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    "-Werror",
     # No packed-fp32 instructions anywhere in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

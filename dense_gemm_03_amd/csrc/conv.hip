@@ -640,7 +640,7 @@ bool window_geom(int dtype, const Dims &d, const PadDims &pd, int64_t pbytes, Co
     if (d.nd != 2 || d.stride[1] != 1 || d.dil[1] != 1 || pbytes <= 0) return false;
     const int es = elem_size(dtype), ks = 16 / es;
     int bn = 0, bk = 0, threads = 0;
-    implicit_tile(dtype, d.k, &bn, &bk, &threads);
+    if (implicit_tile(dtype, d.k, &bn, &bk, &threads) != GEMM_OK) return false;
     const int64_t S = d.kern[1], sp = (S + ks - 1) / ks * ks;
     if (bk % sp != 0) return false;
     const int64_t P = d.out[0], Q = d.out[1];
@@ -696,7 +696,7 @@ bool window_geom_w(int dtype, const Dims &d, const PadDims &pd, int64_t pbytes, 
     if (d.nd != 2 || d.stride[1] != 1 || d.dil[1] != 1 || pbytes <= 0) return false;
     const int es = elem_size(dtype), ks = 16 / es;
     int bn = 0, bk = 0, threads = 0;
-    implicit_tile(dtype, d.k, &bn, &bk, &threads);
+    if (implicit_tile(dtype, d.k, &bn, &bk, &threads) != GEMM_OK) return false;
     const int64_t S = d.kern[1], sp = (S + ks - 1) / ks * ks;
     if (bn % sp != 0) return false;
     const int64_t P = d.out[0], Q = d.out[1], qp = (Q + bk - 1) / bk * bk;

@@ -2,11 +2,14 @@
 // the tile table, split-K workspace, launches.  Declared in include/gemm.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstdio>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <tuple>
 #include <utility>
+#include <vector>
 
 #include "gemm.h"
 #include "gemm_configs.hpp"
@@ -16,10 +19,32 @@ namespace dg {
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps all in-kernel int math exact
-constexpr int kComputeUnits = 256;             // MI355X: 8 XCDs x 32 CUs
-constexpr int kTargetBlocks = 2 * kComputeUnits;
-constexpr int kStreamBlocks = 6 * kComputeUnits;
+// Compute units assumed when no device can be queried (the tile-table hooks on
+// a host without a GPU): MI355X, 8 XCDs x 32 CUs.
+constexpr int kDefaultComputeUnits = 256;
 constexpr int kMaxStreamSplits = 16;
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (hipDeviceGetAttribute, cached per
+// device), or kDefaultComputeUnits when no device is visible.
+int compute_units()
+{
+    static std::atomic<int> cached[kMaxDevices];
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kDefaultComputeUnits;
+    }
+    int cus = cached[device].load(std::memory_order_relaxed);
+    if (cus > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        return kDefaultComputeUnits;
+    }
+    cached[device].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 const TileConfig *table(int dtype, int *count)
 {
@@ -31,15 +56,18 @@ const TileConfig *table(int dtype, int *count)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Index of the table entry called `name` (the tables are fixed, so each
-// lookup result is cached by the caller).
+// Index of the table entry called `name`, or -1 when the table has no such
+// entry (the dispatcher's names and the tables disagree: an internal error
+// that the callers report as GEMM_ERR_INTERNAL).  The tables are fixed, so each
+// lookup result is cached by the caller.
 int config_index(int dtype, const char *name)
 {
     int count = 0;
     const TileConfig *tab = table(dtype, &count);
     for (int i = 0; i < count; ++i)
         if (std::strcmp(tab[i].name, name) == 0) return i;
-    return 0;
+    std::fprintf(stderr, "dense_gemm: tile table has no entry \"%s\"\n", name);
+    return -1;
 }
 
 // Fraction of the GPU's block slots a grid of `tiles` blocks keeps busy over
@@ -58,8 +86,8 @@ struct Candidate {
 };
 
 // Among `cands`, the entry with the best measured efficiency times the fill
-// of its grid for this M x N.
-int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N)
+// of its grid for this M x N on `cus` compute units (-1 if a name is missing).
+int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N, int cus)
 {
     int count = 0;
     const TileConfig *tab = table(dtype, &count);
@@ -67,8 +95,9 @@ int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N)
     double best_score = -1.0;
     for (int i = 0; i < n; ++i) {
         const int idx = config_index(dtype, cands[i].name);
+        if (idx < 0) return -1;
         const int64_t tiles = ceil_div(M, tab[idx].bm) * ceil_div(N, tab[idx].bn);
-        const double score = cands[i].measured * fill(tiles, (int64_t)kComputeUnits * cands[i].per_cu);
+        const double score = cands[i].measured * fill(tiles, (int64_t)cus * cands[i].per_cu);
         if (score > best_score) {
             best_score = score;
             best = idx;
@@ -77,11 +106,11 @@ int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N)
     return best;
 }
 
-// Shape classes -> table entry.  The "measured" factors are the fractions of
-// peak each tile shape reached on 4096^3 fp32 / 8192^3 bf16 (full grids), so
-// the choice trades per-block efficiency against quantisation of the grid
-// over 256 compute units.
-int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
+// Shape classes -> table entry (-1 if an entry it names is missing).  The
+// "measured" factors are the fractions of peak each tile shape reached on
+// 4096^3 fp32 / 8192^3 bf16 (full grids), so the choice trades per-block
+// efficiency against quantisation of the grid over the `cus` compute units.
+int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cus)
 {
     (void)K;
     // Skinny products (a few dozen rows, wide N, usually long K: the
@@ -116,7 +145,7 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
         if (skinny && layout == LAYOUT_NT) return skinny_t;
         if (M <= 64 && N >= 1024)  // split-K
             return layout == LAYOUT_NT ? wide_t : layout == LAYOUT_NN ? wide_nn : wide;
-        if (M >= 2048 && N >= 2048) return best_of(dtype, large, 3, M, N);
+        if (M >= 2048 && N >= 2048) return best_of(dtype, large, 3, M, N, cus);
         if (N <= 64) return narrow;
         return small;
     }
@@ -136,7 +165,7 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K)
     if (skinny && layout == LAYOUT_NN) return skinny_n;
     if (skinny && layout == LAYOUT_NT) return skinny_t;
     if (M <= 64 && N >= 1024) return layout == LAYOUT_NT ? wide_t : wide;  // split-K
-    if (M >= 2048 && N >= 2048) return best_of(dtype, large, 2, M, N);
+    if (M >= 2048 && N >= 2048) return best_of(dtype, large, 2, M, N, cus);
     if (M * N >= int64_t(1024) * 1024) return medium;
     return small;
 }
@@ -168,8 +197,9 @@ int select_implicit(int dtype, int64_t M)
 // chip, since each block then sustains less bandwidth.  Every slice keeps at
 // least four k-tiles.  forced > 0 overrides the target.
 void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K, int forced,
-                int *splits, int *k_per_split)
+                int cus, int *splits, int *k_per_split)
 {
+    const int64_t target_blocks = 2 * (int64_t)cus, stream_blocks = 6 * (int64_t)cus;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int64_t ktiles = ceil_div(K, c.bk);
     const bool streaming = c.bm <= 64;
@@ -177,10 +207,10 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
     int64_t s;
     if (forced > 0) {
         s = forced;
-    } else if (tiles >= kComputeUnits && !(streaming && b_kcontig)) {
+    } else if (tiles >= cus && !(streaming && b_kcontig)) {
         s = 1;
     } else {
-        s = ceil_div(streaming && b_kcontig ? kStreamBlocks : kTargetBlocks, tiles);
+        s = ceil_div(streaming && b_kcontig ? stream_blocks : target_blocks, tiles);
         int64_t max_s = ktiles / 4;
         if (streaming && max_s > kMaxStreamSplits) max_s = kMaxStreamSplits;
         if (s > max_s) s = max_s;
@@ -197,10 +227,16 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
 // slot 1 the convolution tables of the implicit GEMM, slot 2 its zero-padded
 // image, slot 3 its filters with padded rows (or, for the filter gradient,
 // the output gradient with padded rows), slot 4 that filter gradient with
-// padded rows.  A buffer only grows.
+// padded rows.  A buffer only grows, by at least half its size each time.
+// The buffer it replaces is retired, not freed: a HIP graph captured earlier
+// on that stream still holds its address, so it stays valid until the
+// stream's buffers are released (gemm_release_buffers) or the library is
+// unloaded.  Growth during stream capture would call hipMalloc inside the
+// capture, so it is refused (GEMM_ERR_CAPTURING).
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
+    std::vector<void *> retired;
 };
 std::mutex g_ws_mutex;
 std::map<std::tuple<int, hipStream_t, int>, Workspace> g_ws;
@@ -209,32 +245,68 @@ struct WorkspaceReleaser {
     ~WorkspaceReleaser()
     {
         // At unload the runtime may already be gone; freeing is best effort.
-        for (auto &kv : g_ws)
+        for (auto &kv : g_ws) {
             if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+            for (void *p : kv.second.retired) (void)hipFree(p);
+        }
     }
 } g_ws_releaser;
+
+// Whether work enqueued on `stream` is being captured into a graph.
+bool capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
 
 int get_buffer(int slot, int device, hipStream_t stream, size_t bytes, void **out)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_tuple(device, stream, slot)];
     if (w.bytes < bytes) {
-        if (w.ptr) {
-            // hipFree waits for the device, so earlier work using it is done.
-            if (hipFree(w.ptr) != hipSuccess) return GEMM_ERR_HIP;
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
+        if (capturing(stream)) return GEMM_ERR_CAPTURING;
+        const size_t want = bytes > w.bytes + w.bytes / 2 ? bytes : w.bytes + w.bytes / 2;
         void *p = nullptr;
-        if (hipMalloc(&p, bytes) != hipSuccess) {
+        if (hipMalloc(&p, want) != hipSuccess) {
             (void)hipGetLastError();
             return GEMM_ERR_OUT_OF_MEMORY;
         }
+        if (w.ptr) w.retired.push_back(w.ptr);
         w.ptr = p;
-        w.bytes = bytes;
+        w.bytes = want;
     }
     *out = w.ptr;
     return GEMM_OK;
+}
+
+// Frees every buffer (current and retired) of `stream` on the current device.
+int release_buffers(hipStream_t stream)
+{
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_ERR_NO_DEVICE;
+    }
+    if (capturing(stream)) return GEMM_ERR_CAPTURING;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int rc = GEMM_OK;
+    for (auto it = g_ws.begin(); it != g_ws.end();) {
+        if (std::get<0>(it->first) == device && std::get<1>(it->first) == stream) {
+            // hipFree waits for the device, so work still using a buffer is done
+            if (it->second.ptr && hipFree(it->second.ptr) != hipSuccess) rc = GEMM_ERR_HIP;
+            for (void *p : it->second.retired)
+                if (hipFree(p) != hipSuccess) rc = GEMM_ERR_HIP;
+            it = g_ws.erase(it);
+        } else {
+            ++it;
+        }
+    }
+    if (rc != GEMM_OK) (void)hipGetLastError();
+    return rc;
 }
 
 int get_workspace(int device, hipStream_t stream, size_t bytes, float **out)
@@ -314,13 +386,15 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
                    ? GEMM_OK
                    : GEMM_ERR_HIP;
 
+    const int cus = compute_units();
     const int ci = forced_cfg >= 0             ? forced_cfg
                    : call.bsrc != B_MATRIX ? select_implicit(call.dtype, M)
-                                           : select_config(call.dtype, layout, M, N, K);
+                                           : select_config(call.dtype, layout, M, N, K, cus);
+    if (ci < 0) return GEMM_ERR_INTERNAL;
     const TileConfig &cfg = tab[ci];
     if (kernel_of(cfg, true) == nullptr) return GEMM_ERR_INVALID_ARG;
     int splits = 1, kps = 0;
-    plan_split(cfg, layout, M, N, K, forced_split, &splits, &kps);
+    plan_split(cfg, layout, M, N, K, forced_split, cus, &splits, &kps);
 
     KernelArgs a{};
     a.A = call.A;
@@ -430,13 +504,16 @@ int conv_result_buffer(hipStream_t stream, size_t bytes, void **out)
     return get_buffer(4, device, stream, bytes, out);
 }
 
-void implicit_tile(int dtype, int64_t M, int *bn, int *bk, int *threads)
+int implicit_tile(int dtype, int64_t M, int *bn, int *bk, int *threads)
 {
     int count = 0;
-    const TileConfig &c = table(dtype, &count)[select_implicit(dtype, M)];
-    *bn = c.bn;
-    *bk = c.bk;
-    *threads = c.threads;
+    const TileConfig *tab = table(dtype, &count);
+    const int ci = tab ? select_implicit(dtype, M) : -1;
+    if (ci < 0) return GEMM_ERR_INTERNAL;
+    *bn = tab[ci].bn;
+    *bk = tab[ci].bk;
+    *threads = tab[ci].threads;
+    return GEMM_OK;
 }
 
 }  // namespace dg
@@ -493,6 +570,8 @@ int gemm_ex_with_config(int cfg, int split_k, int dtype_ab, int dtype_c, int tra
                    cfg, split_k, stream);
 }
 
+int gemm_release_buffers(hipStream_t stream) { return dg::release_buffers(stream); }
+
 int gemm_config_layouts(int dtype, int cfg)
 {
     int count = 0;
@@ -512,6 +591,10 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_NO_DEVICE: return "no HIP device";
     case GEMM_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case GEMM_ERR_INTERNAL: return "internal error: a tile-table entry the dispatcher names is missing";
+    case GEMM_ERR_CAPTURING:
+        return "a library buffer must grow while the stream is being captured into a graph "
+               "(run the call once on this stream before capturing)";
     default: return "unknown status";
     }
 }
@@ -526,7 +609,8 @@ int gemm_select_config(int dtype, int64_t M, int64_t N, int64_t K)
 {
     int count = 0;
     if (!dg::table(dtype, &count) || M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
-    return dg::select_config(dtype, dg::LAYOUT_NN, M, N, K);
+    const int ci = dg::select_config(dtype, dg::LAYOUT_NN, M, N, K, dg::compute_units());
+    return ci < 0 ? GEMM_ERR_INTERNAL : ci;
 }
 
 int gemm_select_config_ex(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K)
@@ -535,7 +619,8 @@ int gemm_select_config_ex(int dtype, int transa, int transb, int64_t M, int64_t 
     if (!dg::table(dtype, &count) || M < 0 || N < 0 || K < 0 ||
         (transa != GEMM_OP_N && transa != GEMM_OP_T) || (transb != GEMM_OP_N && transb != GEMM_OP_T))
         return GEMM_ERR_INVALID_ARG;
-    return dg::select_config(dtype, transa * 2 + transb, M, N, K);
+    const int ci = dg::select_config(dtype, transa * 2 + transb, M, N, K, dg::compute_units());
+    return ci < 0 ? GEMM_ERR_INTERNAL : ci;
 }
 
 const char *gemm_config_name(int dtype, int cfg)
@@ -553,7 +638,7 @@ int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K)
     if (!tab || cfg < 0 || cfg >= count || M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || K == 0) return 1;
     int splits = 1, kps = 0;
-    dg::plan_split(tab[cfg], dg::LAYOUT_NN, M, N, K, 0, &splits, &kps);
+    dg::plan_split(tab[cfg], dg::LAYOUT_NN, M, N, K, 0, dg::compute_units(), &splits, &kps);
     return splits;
 }
 
@@ -566,7 +651,8 @@ int gemm_split_k_ex(int dtype, int cfg, int transa, int transb, int64_t M, int64
         return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || K == 0) return 1;
     int splits = 1, kps = 0;
-    dg::plan_split(tab[cfg], transa * 2 + transb, M, N, K, 0, &splits, &kps);
+    dg::plan_split(tab[cfg], transa * 2 + transb, M, N, K, 0, dg::compute_units(), &splits,
+                   &kps);
     return splits;
 }
 

@@ -48,7 +48,8 @@ int conv_filter_buffer(hipStream_t stream, size_t bytes, void **out);
 int conv_result_buffer(hipStream_t stream, size_t bytes, void **out);
 
 // Block width BN, k-tile BK and threads of the entry gemm_run picks for an
-// implicit convolution product with M output channels.
-void implicit_tile(int dtype, int64_t M, int *bn, int *bk, int *threads);
+// implicit convolution product with M output channels.  Returns a
+// gemm_status (GEMM_ERR_INTERNAL if the entry is missing from the table).
+int implicit_tile(int dtype, int64_t M, int *bn, int *bk, int *threads);
 
 }  // namespace dg

@@ -157,6 +157,12 @@ int conv2d_bwd_weight_implicit(int dtype, const conv2d_params *p, const void *x,
  * products, same summation order); the window forward product sums the same
  * products (plus zero taps) in a different k order, so its results differ
  * from theirs by rounding only.
+ *
+ * The library-owned buffers follow the rules of gemm.h ("Memory and
+ * ownership", "Graph capture"): kept per (device, stream), grown on demand,
+ * replaced buffers kept until gemm_release_buffers(stream); a call that
+ * would grow one while its stream is being captured returns
+ * GEMM_ERR_CAPTURING.
  */
 typedef enum {
     CONV_ADDR_DEFAULT = 0,

@@ -33,9 +33,21 @@
  *
  * Memory and ownership: A, B and C are device pointers owned by the caller
  * (for example tensors allocated by PyTorch).  C must not overlap A or B.  The
- * library never frees caller memory.  It owns one split-K workspace per
- * device, allocated on first need, grown when a larger one is needed and
- * released when the library is unloaded; growing it synchronises the device.
+ * library never frees caller memory.  It owns a few device buffers per
+ * (device, stream): the split-K partial sums of the GEMM, and for the
+ * convolution calls of conv.h their term tables, zero-bordered image copies
+ * and row-padded filter copies.  A buffer is allocated with hipMalloc on the
+ * first call on a stream that needs it and grown (by at least half its size)
+ * when a later call on that stream needs more; the buffer it replaces is kept,
+ * not freed, until gemm_release_buffers(stream) or library unload, so that a
+ * graph captured earlier on that stream stays valid.
+ *
+ * Graph capture: a call made while `stream` is being captured must not grow a
+ * buffer (that would call hipMalloc inside the capture): it returns
+ * GEMM_ERR_CAPTURING and enqueues nothing.  Run the same call (or a larger
+ * one) once on that stream before capturing, so the buffers already exist.
+ * Calls that need no library buffer (no split-K, which the dispatcher picks
+ * for most shapes; gemm_split_k tells) capture on any stream.
  *
  * Streams: all work is enqueued on `stream` (NULL is the default stream) and
  * the calls return without waiting for it.  A fault inside a kernel surfaces
@@ -50,16 +62,22 @@
  *   - K == 0: C is filled with zeros (the empty sum), GEMM_OK.
  *   - a HIP error while launching or allocating: GEMM_ERR_HIP or
  *     GEMM_ERR_OUT_OF_MEMORY.
+ *   - a library buffer would have to grow during stream capture:
+ *     GEMM_ERR_CAPTURING (see "Graph capture").
+ *   - GEMM_ERR_INTERNAL: the dispatcher names a tile-table entry the build
+ *     does not hold (a build error; never returned by a consistent build).
  * Argument checks happen before any HIP call, so an invalid call does not
  * touch the GPU.
  *
  * Threads: the entry points may be called from several host threads; the
- * tile table is read-only and the workspace is guarded by a mutex.  Library
- * buffers are kept per (device, stream): calls on different streams never
- * share one.  Two threads must not call on the same stream at the same time
- * (the order of their work on that stream would be undefined anyway): a call
- * that grows a stream's buffer frees the old one, which a concurrent call on
- * that stream may still be about to use.
+ * tile table is read-only and the buffer registry is guarded by a mutex.
+ * Library buffers are kept per (device, stream): calls on different streams
+ * never share one.  Two threads must not call on the same stream at the same
+ * time: their kernels would share that stream's buffers.
+ *
+ * Dispatch: the tile choice and split-K plan depend on the shape, the operand
+ * form and the compute-unit count of the current device (queried once per
+ * device; 256, MI355X's count, when no device is visible).
  */
 #ifndef DENSE_GEMM_03_AMD_GEMM_H
 #define DENSE_GEMM_03_AMD_GEMM_H
@@ -77,7 +95,9 @@ typedef enum {
     GEMM_ERR_INVALID_ARG = -1,
     GEMM_ERR_HIP = -2,
     GEMM_ERR_NO_DEVICE = -3,
-    GEMM_ERR_OUT_OF_MEMORY = -4
+    GEMM_ERR_OUT_OF_MEMORY = -4,
+    GEMM_ERR_INTERNAL = -5,
+    GEMM_ERR_CAPTURING = -6
 } gemm_status;
 
 typedef enum { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1 } gemm_dtype;
@@ -139,6 +159,17 @@ int gemm_ex(int dtype_ab, int dtype_c, int transa, int transb,
 const char *gemm_status_string(int status);
 
 /*
+ * Frees every library buffer (current and retired) that calls on `stream`
+ * made on the current device, e.g. before the caller destroys the stream.
+ * The next call on that stream allocates afresh.  The caller must ensure no
+ * enqueued work and no graph that will still be launched uses them (hipFree
+ * waits for the device, so work already enqueued completes first).
+ * GEMM_ERR_CAPTURING while `stream` is being captured; GEMM_ERR_NO_DEVICE
+ * without a device; GEMM_ERR_HIP if a free failed.
+ */
+int gemm_release_buffers(hipStream_t stream);
+
+/*
  * Tile-table hooks, for tests and tuning.  The dispatcher of gemm_f32 and
  * gemm_bf16 picks one entry of a per-dtype table of tile configurations by the
  * shape class of (M, N, K) -- how tile sizes must be chosen per task and
@@ -147,7 +178,8 @@ const char *gemm_status_string(int status);
  * gemm_num_configs: number of table entries for a dtype (negative on a bad
  *   dtype).
  * gemm_select_config: the entry the dispatcher would use for this shape of
- *   the plain product A . B (pure host logic, no GPU access); negative on bad
+ *   the plain product A . B on the current device (host logic; it reads the
+ *   device's compute-unit count, 256 without a device); negative on bad
  *   arguments.
  * gemm_select_config_ex: the same for op(A) . op(B) with the given transa,
  *   transb (GEMM_OP_N / GEMM_OP_T): the choice depends on which operands are

@@ -29,3 +29,14 @@ def cuda():
     if not torch.cuda.is_available():
         pytest.fail("gpu-marked test run without a visible GPU")
     return torch.device("cuda:0")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Repeat the parity lines the GPU tests reported (whole-output error
+    ratios and exact comparisons), so they stay visible under -q."""
+    mod = sys.modules.get("tests.gpu_util")
+    lines = getattr(mod, "SUMMARY", None) if mod is not None else None
+    if lines:
+        terminalreporter.write_sep("-", "parity summary")
+        for line in lines:
+            terminalreporter.write_line(line)

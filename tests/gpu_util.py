@@ -20,6 +20,17 @@ def log(*args):
     sys.stdout.flush()
 
 
+# Lines printed in the terminal summary at the end of the run (after the
+# captured output of passing tests is gone): the headline parity results.
+SUMMARY: list[str] = []
+
+
+def report(line: str):
+    """log() now, and repeat the line in the run's terminal summary."""
+    log(line)
+    SUMMARY.append(line)
+
+
 def to_device(x: np.ndarray):
     """float32 -> torch.float32 and uint16 bf16 patterns -> torch.bfloat16 on cuda:0."""
     import torch

@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 32, names
+    assert len(names) == 33, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -43,7 +43,18 @@ def test_status_strings():
     assert dg.gemm_status_string(dg.GEMM_ERR_HIP) == "HIP runtime error"
     assert dg.gemm_status_string(dg.GEMM_ERR_NO_DEVICE) == "no HIP device"
     assert dg.gemm_status_string(dg.GEMM_ERR_OUT_OF_MEMORY) == "out of device memory"
+    assert dg.gemm_status_string(dg.GEMM_ERR_INTERNAL).startswith("internal error")
+    assert "captured" in dg.gemm_status_string(dg.GEMM_ERR_CAPTURING)
     assert dg.gemm_status_string(12345) == "unknown status"
+
+
+def test_release_buffers_without_a_device():
+    """No GPU here: releasing a stream's buffers reports the missing device
+    instead of touching one."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check")
+    assert dg.gemm_release_buffers(None) == dg.GEMM_ERR_NO_DEVICE
 
 
 def test_config_table():

@@ -1,9 +1,9 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
-times (the default dispatch).  The oracle cannot redo a full product in
-seconds, so outputs are checked at 256 sampled positions (corners, last row
-and column, random) against the stored oracle values of tests/golden/, and
-integer-valued operands of the same shapes are checked exactly at sampled
-positions computed by the oracle one entry at a time.
+times (the default dispatch), at sampled positions: the plain product against
+the oracle values stored in tests/golden/ (256 positions: corners, last row
+and column, random), and the generalised-product variants against the oracle
+computed one entry at a time.  The whole-output comparisons of the plain
+product live in tests/test_whole_c.py.
 """
 from __future__ import annotations
 
@@ -31,34 +31,6 @@ def test_full_size_sampled_against_golden(name):
     ratio = float(np.max(np.abs(C[I, J].astype(np.float64) - C_ref) / S))
     log("[%s] sampled max |C-C_ref|/S = %.3e (tol %.0e)" % (name, ratio, TOL[w.dtype]))
     assert ratio <= TOL[w.dtype]
-
-
-@pytest.mark.parametrize("name", list(wl.WORKLOADS))
-def test_full_size_exact_integers_sampled(name):
-    w = wl.WORKLOADS[name]
-    log("[%s] integer operands %dx%dx%d" % (name, w.M, w.N, w.K))
-    if w.dtype == "f32":
-        A, B = wl.small_int_f32((w.M, w.K), w.seed + 7), wl.small_int_f32((w.K, w.N), w.seed + 8)
-        ent, full = oracle.entries_f32, oracle.gemm_f32
-    else:
-        A = wl.small_int_bf16_bits((w.M, w.K), w.seed + 7)
-        B = wl.small_int_bf16_bits((w.K, w.N), w.seed + 8)
-        ent, full = oracle.entries_bf16, oracle.gemm_bf16
-    C = run(A, B).cpu().numpy()
-    I, J = wl.sample_positions(w.M, w.N, 512, w.seed + 9)
-    C_ref, _ = ent(A, B, I, J)
-    bad = np.flatnonzero(C[I, J].astype(np.float64) != C_ref)
-    assert bad.size == 0, "%d sampled entries differ, first (%d,%d): %r vs %r" % (
-        bad.size, I[bad[0]], J[bad[0]], C[I[bad[0]], J[bad[0]]], C_ref[bad[0]])
-    # every row and column sum is also an exact integer: compare one full row
-    # and one full column with the oracle
-    row = w.M // 2
-    Cr = full(np.ascontiguousarray(A[row:row + 1]), B, with_s=False)
-    assert np.array_equal(C[row].astype(np.float64), Cr[0])
-    col = w.N - 1
-    Cc, _ = ent(A, B, np.arange(w.M), np.full(w.M, col))
-    assert np.array_equal(C[:, col].astype(np.float64), Cc)
-
 
 
 # ------------------------------------------------- generalised-GEMM variants --
