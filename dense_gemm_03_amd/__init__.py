@@ -28,6 +28,8 @@ GEMM_ERR_NO_DEVICE = -3
 GEMM_ERR_OUT_OF_MEMORY = -4
 GEMM_ERR_INTERNAL = -5
 GEMM_ERR_CAPTURING = -6
+GEMM_ERR_SCRATCH_LIMIT = -7
+GEMM_SCRATCH_BYTES = 64 << 20
 GEMM_DTYPE_F32 = 0
 GEMM_DTYPE_BF16 = 1
 GEMM_OP_N = 0
@@ -51,6 +53,7 @@ SIGNATURES = {
     "gemm_bf16_with_config": (_int, [_int, _int] + _GEMM_ARGS),
     "gemm_ex": (_int, _GEMM_EX_ARGS),
     "gemm_ex_with_config": (_int, [_int, _int] + _GEMM_EX_ARGS),
+    "gemm_ex_noalloc": (_int, _GEMM_EX_ARGS),
     "gemm_config_layouts": (_int, [_int, _int]),
     "gemm_release_buffers": (_int, [_p]),
 }
@@ -159,6 +162,12 @@ def gemm_ex(dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda, B, ldb, b
             stream=None) -> int:
     return load_library().gemm_ex(dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda, B, ldb,
                                   beta, C, ldc, stream)
+
+
+def gemm_ex_noalloc(dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                    ldc, stream=None) -> int:
+    return load_library().gemm_ex_noalloc(dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda,
+                                          B, ldb, beta, C, ldc, stream)
 
 
 def gemm_ex_with_config(cfg, split_k, dtype_ab, dtype_c, transa, transb, M, N, K, alpha, A, lda, B,

@@ -354,7 +354,41 @@ int check_args(const Call &c)
     return GEMM_OK;
 }
 
-int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t stream)
+// Fixed split-K scratch of gemm_ex_noalloc: one array per GPU (every GPU the
+// library runs on holds its own copy until the process ends), for callers
+// that cannot allocate.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in for the symbol): the device address of
+// each GPU's copy is looked up once, with that GPU current, and kept.  The
+// partial sums need no clearing: every slice writes all of its M x N values
+// before the reduce reads them.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `device`'s scratch array (the current device).
+int scratch_address(int device, void **out)
+{
+    if (device < 0 || device >= kMaxDevices) return GEMM_ERR_NO_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[device] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return GEMM_ERR_HIP;
+        }
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
+    return GEMM_OK;
+}
+
+// Where a call's split-K partial sums go: the library's per-(device, stream)
+// buffer, grown with hipMalloc on demand, or (no_alloc) the fixed per-device
+// scratch array below, never allocating.
+int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t stream,
+             bool no_alloc = false)
 {
     int rc = check_args(call);
     if (rc != GEMM_OK) return rc;
@@ -416,8 +450,13 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     a.beta = call.beta;
     a.out_bf16 = out_bf16;
     if (splits > 1) {
-        rc = get_workspace(device, stream, (size_t)splits * (size_t)M * (size_t)N * sizeof(float),
-                           &a.ws);
+        const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+        if (no_alloc) {
+            if (need > kScratchBytes) return GEMM_ERR_SCRATCH_LIMIT;
+            rc = scratch_address(device, reinterpret_cast<void **>(&a.ws));
+        } else {
+            rc = get_workspace(device, stream, need, &a.ws);
+        }
         if (rc != GEMM_OK) return rc;
     }
 
@@ -559,6 +598,15 @@ int gemm_ex(int dtype_ab, int dtype_c, int transa, int transb, int64_t M, int64_
                    -1, 0, stream);
 }
 
+int gemm_ex_noalloc(int dtype_ab, int dtype_c, int transa, int transb, int64_t M, int64_t N,
+                    int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                    int64_t ldb, float beta, void *C, int64_t ldc, hipStream_t stream)
+{
+    return dg::run_call(dg::Call{dtype_ab, dtype_c, transa, transb, M, N, K, alpha, beta, A, lda, B,
+                                 ldb, C, ldc},
+                        -1, 0, stream, true);
+}
+
 int gemm_ex_with_config(int cfg, int split_k, int dtype_ab, int dtype_c, int transa, int transb,
                         int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
                         const void *B, int64_t ldb, float beta, void *C, int64_t ldc,
@@ -592,6 +640,8 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_NO_DEVICE: return "no HIP device";
     case GEMM_ERR_OUT_OF_MEMORY: return "out of device memory";
     case GEMM_ERR_INTERNAL: return "internal error: a tile-table entry the dispatcher names is missing";
+    case GEMM_ERR_SCRATCH_LIMIT:
+        return "the call needs more split-K scratch than the fixed array of gemm_ex_noalloc holds";
     case GEMM_ERR_CAPTURING:
         return "a library buffer must grow while the stream is being captured into a graph "
                "(run the call once on this stream before capturing)";

@@ -97,7 +97,8 @@ typedef enum {
     GEMM_ERR_NO_DEVICE = -3,
     GEMM_ERR_OUT_OF_MEMORY = -4,
     GEMM_ERR_INTERNAL = -5,
-    GEMM_ERR_CAPTURING = -6
+    GEMM_ERR_CAPTURING = -6,
+    GEMM_ERR_SCRATCH_LIMIT = -7
 } gemm_status;
 
 typedef enum { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1 } gemm_dtype;
@@ -154,6 +155,37 @@ int gemm_ex(int dtype_ab, int dtype_c, int transa, int transb,
             float beta,
             void *C, int64_t ldc,
             hipStream_t stream);
+
+/*
+ * gemm_ex without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, result and errors as gemm_ex, and the
+ * same kernels and split-K plan, so its output equals gemm_ex's bit for bit.
+ * The split-K partial sums go to a fixed array of 64 MiB in the library's
+ * device code (GEMM_SCRATCH_BYTES), one per GPU, held by each GPU the library
+ * runs on until the process ends; the library allocates nothing, and the
+ * call never calls hipMalloc or hipFree.  The first call on a device looks up
+ * that GPU's copy of the array (hipGetSymbolAddress, which may load the
+ * library's device code onto it); make that first call outside any capture.
+ *   - a call whose split-K plan needs more than GEMM_SCRATCH_BYTES of
+ *     partial sums (splits * M * N * 4 bytes; gemm_select_config_ex and
+ *     gemm_split_k_ex give the plan) returns GEMM_ERR_SCRATCH_LIMIT and
+ *     enqueues nothing;
+ *   - every call on one GPU shares that GPU's array: two calls that may run
+ *     at the same time on one GPU (different streams, or different host
+ *     threads) race on it and give wrong results.  Calls on one stream are
+ *     ordered and safe.  The array keeps the last call's partial sums; nothing
+ *     in it needs to start at zero.
+ */
+#define GEMM_SCRATCH_BYTES ((size_t)64 << 20)
+int gemm_ex_noalloc(int dtype_ab, int dtype_c, int transa, int transb,
+                    int64_t M, int64_t N, int64_t K,
+                    float alpha,
+                    const void *A, int64_t lda,
+                    const void *B, int64_t ldb,
+                    float beta,
+                    void *C, int64_t ldc,
+                    hipStream_t stream);
 
 /* A static, human-readable description of a gemm_status value. */
 const char *gemm_status_string(int status);

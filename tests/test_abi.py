@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 33, names
+    assert len(names) == 34, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
