@@ -79,6 +79,16 @@ double fill(int64_t tiles, int64_t slots)
     return (double)tiles / (double)(rounds * slots);
 }
 
+// Rows (or columns) of the product given to full blocks of `b` when the last
+// block row (column) would hold only a thin remainder -- at most an eighth of
+// a block: those few rows then run as a separate, small product, so that the
+// main grid has no block row doing a full K loop for a handful of outputs.
+int64_t main_extent(int64_t M, int b)
+{
+    const int64_t r = M % b;
+    return r > 0 && 8 * r <= b && M > r ? M - r : M;
+}
+
 struct Candidate {
     const char *name;
     int per_cu;        // resident blocks per compute unit (LDS-limited)
@@ -96,7 +106,9 @@ int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N, int 
     for (int i = 0; i < n; ++i) {
         const int idx = config_index(dtype, cands[i].name);
         if (idx < 0) return -1;
-        const int64_t tiles = ceil_div(M, tab[idx].bm) * ceil_div(N, tab[idx].bn);
+        // the grid of the main part (thin remainders run apart, see run_call)
+        const int64_t tiles = ceil_div(main_extent(M, tab[idx].bm), tab[idx].bm) *
+                              ceil_div(main_extent(N, tab[idx].bn), tab[idx].bn);
         const double score = cands[i].measured * fill(tiles, (int64_t)cus * cands[i].per_cu);
         if (score > best_score) {
             best_score = score;
@@ -429,6 +441,48 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     if (kernel_of(cfg, true) == nullptr) return GEMM_ERR_INVALID_ARG;
     int splits = 1, kps = 0;
     plan_split(cfg, layout, M, N, K, forced_split, cus, &splits, &kps);
+
+    // Thin remainders (dispatcher's choice only; a forced entry runs as asked):
+    // when the last block row or column would hold at most an eighth of a
+    // block and leaving it out saves a round of blocks over the chip, the
+    // full blocks run as one product and the remainder strips as products of
+    // their own (rows M' .. M-1 with all columns, then columns N' .. N-1 of
+    // rows 0 .. M'-1), each dispatched for its shape.  The strips write
+    // disjoint parts of C, so alpha and beta apply to each as to the whole.
+    if (forced_cfg < 0 && call.bsrc == B_MATRIX && splits == 1) {
+        const int64_t Mm = main_extent(M, cfg.bm), Nm = main_extent(N, cfg.bn);
+        const int64_t slots = (int64_t)cus;  // blocks of the large entries: one per CU
+        const int64_t full = ceil_div(M, cfg.bm) * ceil_div(N, cfg.bn);
+        const int64_t main = ceil_div(Mm, cfg.bm) * ceil_div(Nm, cfg.bn);
+        if ((Mm < M || Nm < N) && ceil_div(main, slots) < ceil_div(full, slots)) {
+            const int64_t esz_ab = elem_size(call.dtype), esz_c = elem_size(call.dtype_c);
+            auto at = [](const void *p, int64_t elems, int64_t esz) {
+                return static_cast<const void *>(static_cast<const char *>(p) + elems * esz);
+            };
+            Call part = call;
+            part.M = Mm;
+            part.N = Nm;
+            rc = run_call(part, ci, 0, stream, no_alloc);
+            if (rc != GEMM_OK) return rc;
+            if (Mm < M) {
+                Call rows = call;
+                rows.M = M - Mm;
+                rows.A = at(call.A, call.transa == GEMM_OP_T ? Mm : Mm * call.lda, esz_ab);
+                rows.C = const_cast<void *>(at(call.C, Mm * call.ldc, esz_c));
+                rc = run_call(rows, -1, 0, stream, no_alloc);
+                if (rc != GEMM_OK) return rc;
+            }
+            if (Nm < N) {
+                Call cols = call;
+                cols.M = Mm;
+                cols.N = N - Nm;
+                cols.B = at(call.B, call.transb == GEMM_OP_T ? Nm * call.ldb : Nm, esz_ab);
+                cols.C = const_cast<void *>(at(call.C, Nm, esz_c));
+                rc = run_call(cols, -1, 0, stream, no_alloc);
+            }
+            return rc;
+        }
+    }
 
     KernelArgs a{};
     a.A = call.A;

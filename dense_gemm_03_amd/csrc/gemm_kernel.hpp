@@ -244,6 +244,17 @@ struct OpTile {
             return phys ^ (((row >> 4) & 1) << 5);
     }
 
+    // The same for any physical element position (the swizzles move whole
+    // 16-byte chunks, or for fp32 outer-contiguous tiles flip bit 5 of the
+    // element, so an element keeps its place inside its chunk).
+    static __device__ __forceinline__ int logical_elem(int row, int phys)
+    {
+        if constexpr (LAYOUT == KMAJOR)
+            return logical(row, phys - phys % VEC) + phys % VEC;
+        else
+            return logical(row, phys);
+    }
+
     // LDS reads per fragment and step.
     static constexpr int READS = LAYOUT == KMAJOR ? 1 : (BF16 ? 2 : VEC);
 };
@@ -277,6 +288,18 @@ struct Geo {
     static constexpr int N_MMA = BF16 ? FM * FN : KS * FM * FN;
     static constexpr int N_DS = FM * TA::READS + FN * TB::READS;
     static constexpr int LOADS_PER_TILE = (TA::PIECES + TB::PIECES) / NW;
+
+    // Direct loads of 4 bytes per lane (256 B per instruction), range-checked
+    // buffer loads: fp32 only (a lane's dword is one whole element), for rows
+    // at any 4-byte alignment and for blocks crossing the M or N edge.  The
+    // entry must split its tiles into whole 256-byte pieces per wave, keep
+    // k-contiguous rows within one 256-byte bank line (so a piece's rows share
+    // one swizzle key), and count its loads in flight within vmcnt's range.
+    static constexpr int LOADS4_PER_TILE = (TA::BYTES / 256 + TB::BYTES / 256) / NW;
+    static constexpr bool DMA4 =
+        !BF16 && (TA::BYTES / 256) % NW == 0 && (TB::BYTES / 256) % NW == 0 &&
+        (LA == MNMAJOR || TA::ROW_BYTES <= 256) && (LB == MNMAJOR || TB::ROW_BYTES <= 256) &&
+        LOADS4_PER_TILE * (STAGES - 2) <= 63;
 
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
@@ -329,6 +352,18 @@ __device__ __forceinline__ void direct_load16(const void *base, uint32_t voff, u
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(lds_addr), "v"(voff), "s"(base)
+                 : "m0");
+}
+
+// One range-checked direct load of 4 bytes per lane: lane l's dword at
+// rsrc.base + voff lands at LDS byte address lds_addr + 4 * l; a lane whose
+// offset is at or past the resource's size reads zero and touches no memory.
+__device__ __forceinline__ void direct_load4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                             uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
                  : "m0");
 }
 #pragma clang diagnostic pop
@@ -407,6 +442,7 @@ struct BlockCtx {
     int kend;     // end of this block's K range
     int tid, lane, wrow, wcol;
     int rot;      // interior k-tile the block may start at (see main_loop_direct)
+    int64_t a_end, b_end;  // bytes from A / B to just past their last element
 };
 
 // Fragments of one step: per 32-row A fragment 16 bytes (4 fp32 or 8 bf16 k
@@ -504,67 +540,118 @@ __device__ __forceinline__ void interleave_step()
 // -------------------------------------------------- interior (direct) path --
 
 // Per-thread byte offsets of one operand's direct loads, relative to the tile
-// origin.  They do not change from one k-tile to the next, so they are
-// computed once per block and the per-tile address is a uniform base plus a
-// 32-bit offset.
-template <class T>
+// origin, for loads of DW bytes per lane (16: one 1 KiB piece of the tile
+// per instruction; 4: one 256-byte piece).  They do not change from one
+// k-tile to the next, so they are computed once per block and the per-tile
+// address is a uniform base plus a 32-bit offset.
+template <class T, int DW>
 struct TileOffsets {
-    uint32_t v[T::PIECES / T::NW];
+    static constexpr int PIECE = 64 * DW;
+    static constexpr int PER_WAVE = T::BYTES / PIECE / T::NW;
+    uint32_t v[PER_WAVE];
 };
 
-// The LDS side of a direct load is fixed -- 1 KiB per instruction, lane l at
-// byte 16*l -- so each lane fetches the global chunk that the tile's swizzle
-// places at its LDS position.  LDS row r is memory row r of the tile (an
-// outer index for KMAJOR, a k for MNMAJOR).
-template <class T>
-__device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t ld, TileOffsets<T> &o)
+// The LDS side of a direct load is fixed -- lane l at byte DW*l of the piece
+// -- so each lane fetches the global element(s) that the tile's swizzle places
+// at its LDS position.  LDS row r is memory row r of the tile (an outer index
+// for KMAJOR, a k for MNMAJOR).
+template <class T, int DW>
+__device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t ld, TileOffsets<T, DW> &o)
 {
+    using O = TileOffsets<T, DW>;
 #pragma unroll
-    for (int i = 0; i < T::PIECES / T::NW; ++i) {
+    for (int i = 0; i < O::PER_WAVE; ++i) {
         const int piece = wave + T::NW * i;
-        const int row = piece * T::ROWS_PER_PIECE + lane / T::CPR;
-        const int e = T::logical(row, (lane % T::CPR) * T::VEC);
+        const int byte = piece * O::PIECE + DW * lane;
+        const int row = byte / T::ROW_BYTES;
+        const int e = T::logical_elem(row, (byte % T::ROW_BYTES) / T::ES);
         o.v[i] = (uint32_t)(((int64_t)row * ld + e) * T::ES);
     }
 }
 
-template <class G>
+template <class G, int DW>
 struct DirectOffsets {
-    TileOffsets<typename G::TA> a;
-    TileOffsets<typename G::TB> b;
+    TileOffsets<typename G::TA, DW> a;
+    TileOffsets<typename G::TB, DW> b;
+    static constexpr int LOADS_PER_TILE =
+        TileOffsets<typename G::TA, DW>::PER_WAVE + TileOffsets<typename G::TB, DW>::PER_WAVE;
 };
 
-// Global address of the origin of one operand's k-tile: KMAJOR rows are
-// outer indices (origin row outer0, column k0), MNMAJOR rows are k (origin
-// row k0, column outer0).
+// Byte offset of the origin of one operand's k-tile from the matrix start:
+// KMAJOR rows are outer indices (origin row outer0, column k0), MNMAJOR rows
+// are k (origin row k0, column outer0).
 template <class T>
-__device__ __forceinline__ const void *tile_origin(const typename T::In *X, int64_t ld, int outer0,
-                                                   int k0)
+__device__ __forceinline__ int64_t tile_origin_bytes(int64_t ld, int outer0, int k0)
 {
     if constexpr (T::LAYOUT == KMAJOR)
-        return X + ((int64_t)outer0 * ld + k0);
+        return ((int64_t)outer0 * ld + k0) * T::ES;
     else
-        return X + ((int64_t)k0 * ld + outer0);
+        return ((int64_t)k0 * ld + outer0) * T::ES;
 }
 
-// Direct copy of the k-tile at k0 into `stage` (interior tiles only: every
-// address is inside the matrix and 16-byte aligned).
-template <class G>
+// Bytes from the start of a stored operand to just past its last element:
+// the range a buffer load may touch.
+template <class T>
+__device__ __forceinline__ int64_t operand_end_bytes(int64_t ld, int n_outer, int K)
+{
+    if constexpr (T::LAYOUT == KMAJOR)
+        return ((int64_t)(n_outer - 1) * ld + K) * T::ES;
+    else
+        return ((int64_t)(K - 1) * ld + n_outer) * T::ES;
+}
+
+// Range-checked buffer resource over one operand's k-tile: from the tile
+// origin to the end of the matrix, capped at 4 GiB - 1 bytes (the tile's own
+// offsets are below 2^32, so a cap never cuts into the tile).
+template <class T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const typename T::In *X, int64_t ld,
+                                                            int64_t end, int outer0, int k0)
+{
+    const int64_t org = tile_origin_bytes<T>(ld, outer0, k0);
+    const int64_t left = end - org;
+    const uint32_t size = (uint32_t)(left < 0xFFFFFFFFll ? left : 0xFFFFFFFFll);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char *>(reinterpret_cast<const unsigned char *>(X) + org), 0, (int)size,
+        0x00020000);  // gfx9 raw-buffer format word
+}
+
+// Direct copy of the k-tile at k0 into `stage`.  DW = 16: every address is
+// inside the matrix and 16-byte aligned (interior blocks of aligned
+// operands).  DW = 4 (fp32): range-checked loads; elements of rows or columns
+// past the M or N edge read other in-bounds elements or zero, and only feed
+// outputs that are never stored.
+template <class G, int DW>
 __device__ __forceinline__ void direct_tile_load(unsigned char *stage, const BlockCtx<G> &c,
-                                                 const DirectOffsets<G> &o, int k0)
+                                                 const DirectOffsets<G, DW> &o, int k0)
 {
     using TA = typename G::TA;
     using TB = typename G::TB;
     constexpr int NW = G::NW;
+    constexpr int PIECE = 64 * DW;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + 1024 * wave;
-    const void *a_base = tile_origin<TA>(c.A, c.lda, c.bm, k0);
-    const void *b_base = tile_origin<TB>(c.B, c.ldb, c.bn, k0);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + PIECE * wave;
+    if constexpr (DW == 16) {
+        const unsigned char *a_base =
+            reinterpret_cast<const unsigned char *>(c.A) + tile_origin_bytes<TA>(c.lda, c.bm, k0);
+        const unsigned char *b_base =
+            reinterpret_cast<const unsigned char *>(c.B) + tile_origin_bytes<TB>(c.ldb, c.bn, k0);
 #pragma unroll
-    for (int i = 0; i < TA::PIECES / NW; ++i) direct_load16(a_base, o.a.v[i], lds + 1024 * NW * i);
+        for (int i = 0; i < decltype(o.a)::PER_WAVE; ++i)
+            direct_load16(a_base, o.a.v[i], lds + PIECE * NW * i);
 #pragma unroll
-    for (int i = 0; i < TB::PIECES / NW; ++i)
-        direct_load16(b_base, o.b.v[i], lds + G::A_BYTES + 1024 * NW * i);
+        for (int i = 0; i < decltype(o.b)::PER_WAVE; ++i)
+            direct_load16(b_base, o.b.v[i], lds + G::A_BYTES + PIECE * NW * i);
+    } else {
+        static_assert(DW == 4 && G::DMA4, "4-byte direct loads: fp32 entries only");
+        const auto ra = tile_rsrc<TA>(c.A, c.lda, c.a_end, c.bm, k0);
+        const auto rb = tile_rsrc<TB>(c.B, c.ldb, c.b_end, c.bn, k0);
+#pragma unroll
+        for (int i = 0; i < decltype(o.a)::PER_WAVE; ++i)
+            direct_load4(ra, o.a.v[i], lds + PIECE * NW * i);
+#pragma unroll
+        for (int i = 0; i < decltype(o.b)::PER_WAVE; ++i)
+            direct_load4(rb, o.b.v[i], lds + G::A_BYTES + PIECE * NW * i);
+    }
 }
 
 // One interior k-tile: multiply the tile in `stage` while the tile at k_load
@@ -573,13 +660,14 @@ __device__ __forceinline__ void direct_tile_load(unsigned char *stage, const Blo
 // a barrier, after which the next tile's first fragments are read under the
 // last products of this one.  (Past the last tile the caller passes an
 // in-bounds k_load again, so the code has no branch.)
-template <class G>
+template <class G, int DW>
 __device__ __forceinline__ void direct_tile(const unsigned char *stage, const unsigned char *next,
                                             unsigned char *load,
-                                            const BlockCtx<G> &c, const DirectOffsets<G> &o,
+                                            const BlockCtx<G> &c, const DirectOffsets<G, DW> &o,
                                             int k_load, Frags<G> &cur,
                                             floatx16 (&acc)[G::FM][G::FN])
 {
+    constexpr int LOADS = DirectOffsets<G, DW>::LOADS_PER_TILE;
     Frags<G> nxt;
     direct_tile_load(load, c, o, k_load);
     load_frags(stage, c, 1, nxt);
@@ -587,7 +675,7 @@ __device__ __forceinline__ void direct_tile(const unsigned char *stage, const un
     // share a SIMD, the one ready to feed the matrix core goes first.
     __builtin_amdgcn_s_setprio(1);
     mma(cur, acc);
-    interleave_step<G::N_MMA, G::N_DS, G::LOADS_PER_TILE>();
+    interleave_step<G::N_MMA, G::N_DS, LOADS>();
     cur = nxt;
 #pragma unroll
     for (int step = 1; step < G::STEPS - 1; ++step) {
@@ -601,7 +689,7 @@ __device__ __forceinline__ void direct_tile(const unsigned char *stage, const un
     // issued; every wave waits for its own share before the barrier, so after
     // it the whole tile is in LDS.  lgkmcnt(0): this tile's reads are done
     // before anyone may overwrite the stage.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(G::LOADS_PER_TILE * (G::STAGES - 2)));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LOADS * (G::STAGES - 2)));
     __builtin_amdgcn_s_barrier();
     load_frags(next, c, 0, nxt);
     mma(cur, acc);
@@ -619,7 +707,7 @@ __device__ __forceinline__ void direct_tile(const unsigned char *stage, const un
 // alias scopes this gives every LDS read and direct load let the compiler see
 // that reading one stage need not wait for loads into the others.  On entry
 // no wave may read or load any stage; on exit no load is in flight.
-template <class G>
+template <class G, int DW>
 __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
                                                  unsigned char *__restrict__ s1,
                                                  unsigned char *__restrict__ s2,
@@ -628,9 +716,11 @@ __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
                                                  floatx16 (&acc)[G::FM][G::FN])
 {
     constexpr int S = G::STAGES, BK = G::BK;
+    constexpr int LOADS = DirectOffsets<G, DW>::LOADS_PER_TILE;
+    static_assert(LOADS * (S - 2) <= 63, "vmcnt counts at most 63 loads");
     unsigned char *const st[4] = {s0, s1, s2, s3};
     Frags<G> cur;
-    DirectOffsets<G> o;
+    DirectOffsets<G, DW> o;
     tile_offsets(c.tid >> 6, c.lane, c.lda, o.a);
     tile_offsets(c.tid >> 6, c.lane, c.ldb, o.b);
     // k of the next tile to load; past the last tile the loads wrap round to
@@ -647,7 +737,7 @@ __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
     // prologue: tiles 0 .. S-2 in flight, tile 0 complete
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) direct_tile_load(st[s], c, o, next_k());
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(G::LOADS_PER_TILE * (S - 2)));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LOADS * (S - 2)));
     __builtin_amdgcn_s_barrier();
     load_frags(st[0], c, 0, cur);
 
@@ -1379,10 +1469,26 @@ gemm_kernel(KernelArgs p)
     // and leading dimensions too large for 32-bit tile offsets take the
     // masked loads.  The choice is uniform per workgroup.
     if constexpr (BSRC == B_MATRIX) {
-        const bool edge = !ALIGNED || !p.direct_ok || c.bm + BM > p.M || c.bn + BN > p.N;
-        const int nfast = edge ? 0 : (c.kend - kbeg) / BK;
+        // Whole k-tiles go through direct global->LDS loads: 16 bytes per lane
+        // for interior blocks of aligned operands; for fp32 entries also 4
+        // range-checked bytes per lane for blocks crossing the M or N edge and
+        // for rows at any alignment.  Other cases, and the partial last
+        // k-tile, take the masked loads.
+        const bool edge_mn = c.bm + BM > p.M || c.bn + BN > p.N;
+        const bool x4 = ALIGNED && p.direct_ok && !edge_mn;
+        const bool dw = G::DMA4 && p.direct_ok && !x4;
+        const int nfast = x4 || dw ? (c.kend - kbeg) / BK : 0;
         c.rot = (tm + tn) % 8;
-        if (nfast > 0) main_loop_direct(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
+        if constexpr (G::DMA4) {
+            c.a_end = operand_end_bytes<typename G::TA>(p.lda, p.M, p.K);
+            c.b_end = operand_end_bytes<typename G::TB>(p.ldb, p.N, p.K);
+            if (dw && nfast > 0)
+                main_loop_direct<G, 4>(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
+        }
+        if constexpr (ALIGNED) {
+            if (x4 && nfast > 0)
+                main_loop_direct<G, 16>(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
+        }
         if (ntiles > nfast)
             main_loop_masked(lds0, lds1, c, kbeg + nfast * BK, ntiles - nfast, acc,
                              [&](int k0, StageRegs<G> &r) { global_load_masked<ALIGNED>(c, k0, r); });

@@ -25,7 +25,7 @@ import pytest
 import dense_gemm_03_amd as dg
 import oracle
 from dense_gemm_03_amd import workloads as wl
-from tests.gpu_util import DIAGNOSTIC, TOL, log, report, run
+from tests.gpu_util import DIAGNOSTIC, TOL, log, report, run, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +130,41 @@ def test_many_blocks_xcd_renumbering_exact(bf16):
         A, B = _ints((M, K), 60 + M % 7, bf16), _ints((K, N), 70 + N % 7, bf16)
         C = run(A, B, cfg=cfg).cpu().numpy()
         _exact_whole(C, A, B, "%s %dx%dx%d" % (name, M, N, K))
+
+
+@pytest.mark.parametrize("case", [
+    ("f32", False, False, 4097, 4095, 256, 1.0, 0.0),
+    ("f32", True, True, 4099, 4098, 200, 2.0, -1.0),
+    ("f32", False, True, 4095, 4100, 160, 1.0, 1.0),
+    ("bf16", False, False, 4097, 4095, 192, 1.0, 0.0),
+    ("bf16", True, False, 4100, 4099, 128, -1.0, 2.0),
+], ids=lambda c: "%s-%s%s-%dx%dx%d" % (c[0], "T" if c[1] else "N", "T" if c[2] else "N",
+                                        c[3], c[4], c[5]))
+def test_thin_remainders_run_apart_exact(case):
+    """Large products whose last block row or column would hold only a few
+    rows (columns): the dispatcher runs the full 256 x 256 blocks as one
+    product and the thin strips as products of their own.  Every entry of C,
+    for transposed operands and alpha/beta too, equals the oracle's exact
+    value (integer operands and C)."""
+    import torch
+    dt, ta, tb, M, N, K, alpha, beta = case
+    bf16 = dt == "bf16"
+    dtype = BF16 if bf16 else F32
+    cfg = dg.gemm_select_config_ex(dtype, int(ta), int(tb), M, N, K)
+    assert dg.gemm_config_name(dtype, cfg).endswith(("256x256_w4x2_s2", "256x256x32_w4x2_s4"))
+    A = _ints((K, M) if ta else (M, K), 80 + M % 5, bf16)
+    B = _ints((N, K) if tb else (K, N), 90 + N % 5, bf16)
+    C0 = np.random.default_rng(K).integers(-9, 10, size=(M, N)).astype(np.float32)
+    Ad, Bd = to_device(A), to_device(B)
+    C = torch.from_numpy(C0).to("cuda:0")
+    dg.gemm(Ad, Bd, out=C, alpha=alpha, beta=beta, transa=ta, transb=tb)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    want, _ = oracle.gemm_general(A, B, alpha, beta, C0.astype(np.float64) if beta else None, ta,
+                                  tb, kind=dt)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, "%d of %d entries differ, first at %s" % (
+        bad.size, got.size, divmod(int(bad[0]), N))
+    report("whole C, integer operands, thin remainders %s %s%s %dx%dx%d alpha %g beta %g: all %d "
+           "entries equal the oracle bit for bit" % (dt, "T" if ta else "N", "T" if tb else "N",
+                                                      M, N, K, alpha, beta, got.size))
