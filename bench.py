@@ -16,8 +16,10 @@ in HBM.  Prints ONE JSON line (last line of stdout):
                           summary (profiles/traffic.json) when it was taken on
                           the current sources, else null -- it is a stored
                           reading, not measured in this run
-  sclk                    the graphics clock sampled (amdsmi GPU metrics)
-                          while the timed steps ran, when readable
+  sclk_sustained          the graphics clock the GPU holds over 2.5 s of the
+                          headline workload run back to back after the timed
+                          steps (amdsmi GPU metrics, when readable; also for
+                          bf16 8192^3 in 'also')
   cpu_baseline            the oracle (CPU, fp64) timed on a bounded sample of the
                           same workload on this host
   also                    the same measurement, in short form, for the other
@@ -104,75 +106,57 @@ def stored_traffic(workload: str, family: str = "gemm", config: str | None = Non
     return entry.get("bytes_per_launch")
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi GPU metrics) on a background
-    thread while a timed region runs.  Readings come from the SMU's metrics
-    table; when amdsmi is missing or the call is not permitted the result
-    says why instead."""
+def sustained_clock(step, seconds: float = 2.5):
+    """The graphics clock the GPU holds while running `step` back to back:
+    the workload runs for `seconds` while a thread samples amdsmi's GPU
+    metrics; the SMU refreshes that table too slowly for the timed steps
+    themselves, and readings lag by up to about a second), and the median of
+    the samples of the last second is reported.  Outside the timed steps."""
+    import threading
 
-    def __init__(self):
-        self.err = None
-        self.handle = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            if len(handles) != 1:
-                raise RuntimeError("%d GPUs visible to amdsmi, expected 1" % len(handles))
-            self.handle = handles[0]
-            self.amdsmi = amdsmi
-            self._read()
-        except Exception as e:  # noqa: BLE001 - reported, not fatal
-            self.err = "%s: %s" % (type(e).__name__, e)
-            self.handle = None
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            raise RuntimeError("%d GPUs visible to amdsmi" % len(handles))
+        handle = handles[0]
+    except Exception as e:  # noqa: BLE001 - reported, not fatal
+        return {"mhz": None, "error": "%s: %s" % (type(e).__name__, e)}
 
-    def _read(self):
-        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
-        cur = m.get("current_gfxclk")
-        if clks:
-            return float(sum(clks)) / len(clks)
-        if isinstance(cur, (int, float)) and cur > 0:
-            return float(cur)
-        raise RuntimeError("no graphics clock in the GPU metrics")
+        return float(sum(clks)) / len(clks) if clks else float(m.get("current_gfxclk") or 0)
 
-    def start(self):
-        import threading
-        self.samples = []
-        self._stop = threading.Event()
-        if self.handle is None:
-            return
-        def loop():
-            while not self._stop.is_set():
-                try:
-                    self.samples.append(self._read())
-                except Exception as e:  # noqa: BLE001
-                    self.err = "%s: %s" % (type(e).__name__, e)
-                    return
-                time.sleep(0.0005)
-        self._thread = threading.Thread(target=loop, daemon=True)
-        self._thread.start()
+    samples, stop, err = [], threading.Event(), []
 
-    def stop(self):
-        if self.handle is None:
-            return {"mhz": None, "error": self.err}
-        self._stop.set()
-        self._thread.join()
-        s = sorted(self.samples)
-        if not s:
-            return {"mhz": None, "error": self.err or "no sample"}
-        return {"mhz": s[len(s) // 2], "min_mhz": s[0], "max_mhz": s[-1], "samples": len(s),
-                "source": "amdsmi gpu_metrics current_gfxclk(s), median over the timed steps"}
+    def loop():
+        while not stop.is_set():
+            try:
+                samples.append((time.perf_counter(), read()))
+            except Exception as e:  # noqa: BLE001
+                err.append("%s: %s" % (type(e).__name__, e))
+                return
+            time.sleep(0.002)
 
-
-_CLOCK = None
-
-
-def clock_sampler():
-    global _CLOCK
-    if _CLOCK is None:
-        _CLOCK = ClockSampler()
-    return _CLOCK
+    th = threading.Thread(target=loop, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    late = sorted(v for t, v in samples if t - t0 >= seconds - 1.0)
+    if not late:
+        return {"mhz": None, "error": err[0] if err else "no sample"}
+    return {"mhz": late[len(late) // 2], "min_mhz": late[0], "max_mhz": late[-1],
+            "samples": len(late), "window_s": seconds,
+            "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), median over the "
+                      "last second of a %.1f s back-to-back run of this workload" % seconds}
 
 
 def _workload(name: str):
@@ -180,8 +164,9 @@ def _workload(name: str):
     return WORKLOADS[name] if name in WORKLOADS else VARIANTS[name]
 
 
-def measure(name: str, steps: int, warmup: int):
-    """Time `steps` GEMM calls on workload `name`; returns a result dict."""
+def prepare(name: str):
+    """Draw workload `name`'s operands on the host and copy them to the GPU;
+    returns what measure() needs."""
     import torch
 
     import dense_gemm_03_amd as dg
@@ -202,11 +187,6 @@ def measure(name: str, steps: int, warmup: int):
     else:
         C = torch.empty((w.M, w.N), dtype=torch.float32 if w.out == "f32" else torch.bfloat16,
                         device="cuda:0")
-    stream = torch.cuda.current_stream()
-    dtype_id = dg.GEMM_DTYPE_F32 if w.dtype == "f32" else dg.GEMM_DTYPE_BF16
-    ta, tb = int(w.transa), int(w.transb)
-    cfg = dg.gemm_select_config_ex(dtype_id, ta, tb, w.M, w.N, w.K)
-    splits = dg.gemm_split_k_ex(dtype_id, cfg, ta, tb, w.M, w.N, w.K)
     # Workloads judged on HBM bandwidth whose operands would fit the 256 MB
     # MALL (Infinity Cache) across back-to-back steps rotate over three copies
     # of A and B, so every step streams its operands from HBM.  (The im2col
@@ -215,6 +195,22 @@ def measure(name: str, steps: int, warmup: int):
     operands = [(A, B)]
     if name == "tall":
         operands += [(A.clone(), B.clone()) for _ in range(2)]
+    torch.cuda.synchronize()
+    return {"name": name, "w": w, "operands": operands, "C": C}
+
+
+def measure(ctx, steps: int, warmup: int):
+    """Time `steps` GEMM calls on a prepared workload; returns a result dict."""
+    import torch
+
+    import dense_gemm_03_amd as dg
+
+    name, w, operands, C = ctx["name"], ctx["w"], ctx["operands"], ctx["C"]
+    stream = torch.cuda.current_stream()
+    dtype_id = dg.GEMM_DTYPE_F32 if w.dtype == "f32" else dg.GEMM_DTYPE_BF16
+    ta, tb = int(w.transa), int(w.transb)
+    cfg = dg.gemm_select_config_ex(dtype_id, ta, tb, w.M, w.N, w.K)
+    splits = dg.gemm_split_k_ex(dtype_id, cfg, ta, tb, w.M, w.N, w.K)
     turn = [0]
 
     def step():
@@ -234,9 +230,7 @@ def measure(name: str, steps: int, warmup: int):
     # stream, passed to the C ABI), bracketing the timed region.
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    clock = clock_sampler()
     torch.cuda.synchronize()
-    clock.start()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
@@ -244,7 +238,6 @@ def measure(name: str, steps: int, warmup: int):
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sclk = clock.stop()
     event_ms = ev0.elapsed_time(ev1) / steps
     ms_per_step = wall * 1e3 / steps
     tflops = w.flops * steps / wall / 1e12
@@ -278,10 +271,8 @@ def measure(name: str, steps: int, warmup: int):
         "roofline": roofline,
         "hbm_gbs": hbm_gbs,
         "operand_sets": len(operands),
-        "sclk": sclk,
+        "step": step,
     }
-    del A, B, C, operands
-    torch.cuda.empty_cache()
     return res
 
 
@@ -523,24 +514,32 @@ def main() -> int:
             args.conv, args.steps, args.warmup, args.conv_route)}}), flush=True)
         return 0
 
-    # The other configurations first, each with its own warm-up, then the
-    # headline workload: W warm-up steps and K timed steps of it, on a GPU
-    # that has been running (its clock settled) rather than straight after
-    # process start.
-    also = {}
+    # Every workload's operands are drawn and copied to the GPU first; then the
+    # other configurations are timed, each with its own warm-up, and the
+    # headline workload last (W warm-up steps, K timed steps), so that the
+    # timed steps run back to back on a GPU that is already busy rather than
+    # after seconds of host-side drawing with the GPU idle.
     others = [] if args.no_also else [
         n for n in SECONDARY + (EXTRA if args.all else []) if n != args.workload]
-    for n in others:
-        also[n] = measure(n, max(10, args.steps // 2), max(20, args.warmup))
-
+    ctxs = {n: prepare(n) for n in others + [args.workload]}
     if args.all and not args.no_also:
         conv = {}
         for n in CONV:
             conv[n] = measure_conv(n, max(10, args.steps // 5), max(5, args.warmup // 5))
         # its own line, before the result line
         print(json.dumps({"convolution": conv}), flush=True)
+    also = {}
+    for n in others:
+        also[n] = measure(ctxs[n], max(10, args.steps // 2), max(20, args.warmup))
+    main_res = measure(ctxs[args.workload], args.steps, args.warmup)
 
-    main_res = measure(args.workload, args.steps, args.warmup)
+    # the clock each headline workload sustains (outside the timed steps)
+    clocks = {}
+    if not args.no_also:
+        for n, r in [(args.workload, main_res)] + [(n, also[n]) for n in also if n in ("bf16-8192",)]:
+            clocks[n] = sustained_clock(r["step"])
+            log("[bench] %s sustained clock: %s MHz" % (n, clocks[n].get("mhz")))
+    del ctxs
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -557,8 +556,9 @@ def main() -> int:
             rf["traffic"] = int(rf["traffic"])
         out = {"shape": "%s %dx%dx%d %s" % (r["dtype"], r["M"], r["N"], r["K"], r["op"]),
                "value": round(r["value"], 2), "ms_per_step": round(r["ms_per_step"], 4),
-               "kernel_config": r["kernel_config"], "split_k": r["split_k"], "roofline": rf,
-               "sclk_mhz": r["sclk"].get("mhz")}
+               "kernel_config": r["kernel_config"], "split_k": r["split_k"], "roofline": rf}
+        if r["workload"] in clocks:
+            out["sclk_sustained_mhz"] = clocks[r["workload"]].get("mhz")
         if r["alpha"] != 1.0 or r["beta"] != 0.0 or r["c_dtype"] != "f32":
             out["alpha"], out["beta"], out["c_dtype"] = r["alpha"], r["beta"], r["c_dtype"]
         return out
@@ -587,7 +587,7 @@ def main() -> int:
             "parallelism": "single GPU",
         },
         "roofline": w["roofline"],
-        "sclk": w["sclk"],
+        "sclk_sustained": clocks.get(args.workload),
         "cpu_baseline": cpu,
         "also": {n: short(r) for n, r in also.items()},
         "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),

@@ -141,7 +141,7 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("f32_64x64x64_w2x2_s2", false, 64, 64, 64, 2, 2, 2, 1, KK)
 
 #define DG_BF16_TABLE(X)                                                    \
-    X("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 4, ALL)       \
+    X("bf16_256x256x32_w4x2_s4", true, 256, 256, 32, 4, 2, 4, 8, ALL)       \
     X("bf16_128x128x64_w2x2_s2", true, 128, 128, 64, 2, 2, 2, 8, CONV)      \
     X("bf16_256x128x64_w2x2_s2", true, 256, 128, 64, 2, 2, 2, 8, CONV)      \
     X("bf16_64x64x64_w2x2_s2", true, 64, 64, 64, 2, 2, 2, 8, ALL)           \

@@ -1515,10 +1515,9 @@ gemm_kernel(KernelArgs p)
     const int half = c.lane >> 5, l32 = c.lane & 31;
     const bool store_edge = c.bm + BM > p.M || c.bn + BN > p.N;
     const bool partial = p.splits > 1;
-    if (partial || (p.alpha == 1.0f && p.beta == 0.0f && !p.out_bf16)) {
-        // raw sums: the split-K partials, or the plain product into fp32 C
-        float *out = partial ? p.ws + (int64_t)slice * p.M * p.N : static_cast<float *>(p.C);
-        const int64_t ldo = partial ? (int64_t)p.N : p.ldc;
+    if (partial) {
+        // raw sums of this slice, read back by the reduce kernel
+        float *out = p.ws + (int64_t)slice * p.M * p.N;
 #pragma unroll
         for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
@@ -1529,7 +1528,28 @@ gemm_kernel(KernelArgs p)
                     const int gi =
                         c.bm + c.wrow * G::WTM + fm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                     if (!store_edge || (gi < p.M && gj < p.N))
-                        out[(int64_t)gi * ldo + gj] = acc[fm][fn][r];
+                        out[(int64_t)gi * p.N + gj] = acc[fm][fn][r];
+                }
+            }
+        return;
+    }
+    if (p.alpha == 1.0f && p.beta == 0.0f && !p.out_bf16) {
+        // the plain product into fp32 C.  C is written once and not read
+        // again here: non-temporal stores keep it from evicting the operand
+        // tiles other blocks still stream through the caches (measured
+        // 1-2.5% on bf16 8192^3).
+        float *out = static_cast<float *>(p.C);
+#pragma unroll
+        for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < G::FN; ++fn) {
+                const int gj = c.bn + c.wcol * G::WTN + fn * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gi =
+                        c.bm + c.wrow * G::WTM + fm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (!store_edge || (gi < p.M && gj < p.N))
+                        __builtin_nontemporal_store(acc[fm][fn][r], &out[(int64_t)gi * p.ldc + gj]);
                 }
             }
         return;
