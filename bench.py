@@ -446,10 +446,16 @@ def cpu_baseline(name: str, budget_s: float = 10.0):
 
     rows = min(w.M, max(threads, 16))
     dt = run(rows)
-    # grow the sample to about budget_s seconds of wall time
-    target = int(rows * budget_s / max(dt, 1e-3))
-    rows2 = max(rows, min(w.M, target - target % threads if target > threads else target))
-    if rows2 > rows:
+    # grow the sample towards budget_s seconds of wall time (the whole
+    # product when it takes less); small first samples overestimate the
+    # per-row time, so re-estimate up to three times
+    for _ in range(3):
+        if rows >= w.M or dt >= budget_s / 2:
+            break
+        target = int(rows * budget_s / max(dt, 1e-3))
+        rows2 = max(rows, min(w.M, target - target % threads if target > threads else target))
+        if rows2 == rows:
+            break
         dt = run(rows2)
         rows = rows2
     flops = 2.0 * rows * w.N * w.K
