@@ -16,10 +16,10 @@ in HBM.  Prints ONE JSON line (last line of stdout):
                           summary (profiles/traffic.json) when it was taken on
                           the current sources, else null -- it is a stored
                           reading, not measured in this run
-  sclk_sustained          the graphics clock the GPU holds over 2.5 s of the
-                          headline workload run back to back after the timed
-                          steps (amdsmi GPU metrics, when readable; also for
-                          bf16 8192^3 in 'also')
+  sclk_sustained          the graphics clock and board power the GPU holds over
+                          2.5 s of the headline workload run back to back after
+                          the timed steps (amdsmi GPU metrics, when readable;
+                          also for bf16 8192^3 in 'also')
   cpu_baseline            the oracle (CPU, fp64) timed on a bounded sample of the
                           same workload on this host
   also                    the same measurement, in short form, for the other
@@ -128,14 +128,16 @@ def sustained_clock(step, seconds: float = 2.5):
     def read():
         m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
-        return float(sum(clks)) / len(clks) if clks else float(m.get("current_gfxclk") or 0)
+        mhz = float(sum(clks)) / len(clks) if clks else float(m.get("current_gfxclk") or 0)
+        w = m.get("current_socket_power")
+        return mhz, float(w) if isinstance(w, (int, float)) else None
 
     samples, stop, err = [], threading.Event(), []
 
     def loop():
         while not stop.is_set():
             try:
-                samples.append((time.perf_counter(), read()))
+                samples.append((time.perf_counter(),) + read())
             except Exception as e:  # noqa: BLE001
                 err.append("%s: %s" % (type(e).__name__, e))
                 return
@@ -150,13 +152,16 @@ def sustained_clock(step, seconds: float = 2.5):
         torch.cuda.synchronize()
     stop.set()
     th.join()
-    late = sorted(v for t, v in samples if t - t0 >= seconds - 1.0)
+    late = sorted(v for t, v, _ in samples if t - t0 >= seconds - 1.0)
+    watts = sorted(w for t, _, w in samples if t - t0 >= seconds - 1.0 and w is not None)
     if not late:
         return {"mhz": None, "error": err[0] if err else "no sample"}
     return {"mhz": late[len(late) // 2], "min_mhz": late[0], "max_mhz": late[-1],
+            "socket_power_w": watts[len(watts) // 2] if watts else None,
             "samples": len(late), "window_s": seconds,
-            "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), median over the "
-                      "last second of a %.1f s back-to-back run of this workload" % seconds}
+            "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs) and "
+                      "current_socket_power, medians over the last second of a %.1f s "
+                      "back-to-back run of this workload" % seconds}
 
 
 def _workload(name: str):
@@ -565,6 +570,7 @@ def main() -> int:
                "kernel_config": r["kernel_config"], "split_k": r["split_k"], "roofline": rf}
         if r["workload"] in clocks:
             out["sclk_sustained_mhz"] = clocks[r["workload"]].get("mhz")
+            out["socket_power_w"] = clocks[r["workload"]].get("socket_power_w")
         if r["alpha"] != 1.0 or r["beta"] != 0.0 or r["c_dtype"] != "f32":
             out["alpha"], out["beta"], out["c_dtype"] = r["alpha"], r["beta"], r["c_dtype"]
         return out
