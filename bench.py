@@ -283,7 +283,7 @@ def measure(ctx, steps: int, warmup: int):
 
 def measure_conv(name: str, steps: int, warmup: int, only: str | None = None):
     """Time the convolution `name`: forward pass and filter gradient through
-    im2col + GEMM and through the implicit GEMM (up to three dimensions), and
+    im2col + GEMM and through the implicit GEMM (one to four dimensions), and
     the im2col kernel alone (its HBM roofline).  `only` names one of these
     measurements (for per-route profiler passes)."""
     import torch
@@ -364,7 +364,7 @@ def measure_conv(name: str, steps: int, warmup: int, only: str | None = None):
     peak = PEAK_TFLOPS[c.dtype]
     routes = [("fwd", fwd), ("wgrad", wgrad)]
     A, T, PD = dg.CONV_ADDR_ANALYTIC, dg.CONV_ADDR_TABLE, dg.CONV_ADDR_PADDED
-    if nd and c.nd <= 3:
+    if nd:
         def fwd_nd_implicit(mode):
             def run():
                 assert dg.convnd_fwd_implicit_ex(dtype, F32, params, mode, x.data_ptr(),

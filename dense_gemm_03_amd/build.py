@@ -30,7 +30,7 @@ SOURCES = [("gemm_api.hip", "gemm_api", []),
            ("conv.hip", "conv", [])]
 for _dtype in ("F32", "BF16"):
     for _layout in ("NN", "NT", "TN", "TT", "CF", "CW", "CFT", "CWT", "C3F", "C3W", "CFP", "CWP",
-                    "C3FP", "C3WP", "CFW", "CWW"):
+                    "C3FP", "C3WP", "CFW", "CWW", "C4F", "C4W", "C4FP", "C4WP"):
         SOURCES.append(("gemm_instances.hip", "gemm_%s_%s" % (_dtype.lower(), _layout.lower()),
                         ["DG_DTYPE_TABLE=DG_%s_TABLE" % _dtype, "DG_LAYOUT=" + _layout]))
 

@@ -415,16 +415,18 @@ int make_geom(const Dims &d, int esize, ConvGeom *g)
     return GEMM_OK;
 }
 
-// Geometry of the volume (3-D) implicit-GEMM loaders for 1 to 3 spatial
-// dimensions; fewer than three get leading unit dimensions (size, filter,
-// stride and dilation 1, no padding), which changes nothing.  The image of
-// one batch element must span less than 2 GiB.
+// Geometry of the volume implicit-GEMM loaders for 1 to 4 spatial dimensions.
+// The loaders see four (u, z, y, x); fewer get leading unit dimensions (size,
+// filter, stride and dilation 1, no padding), which changes nothing.  The
+// three-dimensional sources read only (z, y, x); the four-dimensional ones
+// (nd = 4) also the outermost u.  The image of one batch element must span
+// less than 2 GiB.
 int make_geom3(const Dims &d, int esize, ConvGeom *g)
 {
-    if (d.nd > 3 || d.c * d.img_elems() * esize >= (int64_t(1) << 31)) return GEMM_ERR_INVALID_ARG;
-    const int lead = 3 - (int)d.nd;
-    int64_t size[3], kern[3], pad[3], stride[3], dil[3], out[3];
-    for (int i = 0; i < 3; ++i) {
+    if (d.nd > 4 || d.c * d.img_elems() * esize >= (int64_t(1) << 31)) return GEMM_ERR_INVALID_ARG;
+    const int lead = 4 - (int)d.nd;
+    int64_t size[4], kern[4], pad[4], stride[4], dil[4], out[4];
+    for (int i = 0; i < 4; ++i) {
         const bool unit = i < lead;
         const int j = i - lead;
         size[i] = unit ? 1 : d.size[j];
@@ -435,30 +437,38 @@ int make_geom3(const Dims &d, int esize, ConvGeom *g)
         out[i] = unit ? 1 : d.out[j];
     }
     *g = ConvGeom{};
-    g->d = (int)size[0];
-    g->h = (int)size[1];
-    g->w = (int)size[2];
-    g->t = (int)kern[0];
-    g->r = (int)kern[1];
-    g->s = (int)kern[2];
-    g->pz = (int)pad[0];
-    g->ph = (int)pad[1];
-    g->pw = (int)pad[2];
-    g->sz = (int)stride[0];
-    g->sh = (int)stride[1];
-    g->sw = (int)stride[2];
-    g->lz = (int)dil[0];
-    g->dh = (int)dil[1];
-    g->dw = (int)dil[2];
-    g->p = (int)out[1];
-    g->q = (int)out[2];
-    g->pq = (int)(out[1] * out[2]);
+    g->du = (int)size[0];
+    g->d = (int)size[1];
+    g->h = (int)size[2];
+    g->w = (int)size[3];
+    g->ku = (int)kern[0];
+    g->t = (int)kern[1];
+    g->r = (int)kern[2];
+    g->s = (int)kern[3];
+    g->pu = (int)pad[0];
+    g->pz = (int)pad[1];
+    g->ph = (int)pad[2];
+    g->pw = (int)pad[3];
+    g->su = (int)stride[0];
+    g->sz = (int)stride[1];
+    g->sh = (int)stride[2];
+    g->sw = (int)stride[3];
+    g->lu = (int)dil[0];
+    g->lz = (int)dil[1];
+    g->dh = (int)dil[2];
+    g->dw = (int)dil[3];
+    g->p = (int)out[2];
+    g->q = (int)out[3];
+    g->pq = (int)(out[2] * out[3]);
+    g->opq = (int)(out[1] * out[2] * out[3]);
     g->crs = (int)d.crs();
-    div_magic((uint32_t)out[2], &g->q_magic, &g->q_shift);
-    div_magic((uint32_t)(out[1] * out[2]), &g->pq_magic, &g->pq_shift);
-    div_magic((uint32_t)(kern[1] * kern[2]), &g->rs_magic, &g->rs_shift);
-    div_magic((uint32_t)(kern[0] * kern[1] * kern[2]), &g->trs_magic, &g->trs_shift);
-    div_magic((uint32_t)kern[2], &g->s_magic, &g->s_shift);
+    div_magic((uint32_t)out[3], &g->q_magic, &g->q_shift);
+    div_magic((uint32_t)(out[2] * out[3]), &g->pq_magic, &g->pq_shift);
+    div_magic((uint32_t)(out[1] * out[2] * out[3]), &g->opq_magic, &g->opq_shift);
+    div_magic((uint32_t)(kern[2] * kern[3]), &g->rs_magic, &g->rs_shift);
+    div_magic((uint32_t)(kern[1] * kern[2] * kern[3]), &g->trs_magic, &g->trs_shift);
+    div_magic((uint32_t)(kern[0] * kern[1] * kern[2] * kern[3]), &g->ktrs_magic, &g->ktrs_shift);
+    div_magic((uint32_t)kern[3], &g->s_magic, &g->s_shift);
     g->img_bytes = (int)(d.c * d.img_elems() * esize);
     return GEMM_OK;
 }
@@ -541,28 +551,38 @@ int table_source(int esize, bool fwd, ConvGeom *geom, hipStream_t stream, int *b
 
 int zero_dw(int dtype, const Dims &d, float *dw, hipStream_t stream);
 
+// Spatial dimensions of the padded implicit sources -- outermost (1 below four
+// dimensions), depth (1 for 2-D), rows, columns -- their paddings, and the
+// padded extents.
+struct PadDims {
+    int u, d, h, w, pu, pz, ph, pw, up, dp, hp, wp;
+};
+
 // Zero-padded copy of one image for the padded implicit sources: dst
-// [C][D + 2 pz][H + 2 ph][W + 2 pw] (D = 1, pz = 0 for 2-D) holds the image
-// with zero borders, so that every position a tile touches lies inside it.
-// One element per thread, consecutive threads along the padded rows.
+// [C][U + 2 pu][D + 2 pz][H + 2 ph][W + 2 pw] (U = 1, pu = 0 below four
+// dimensions; D = 1, pz = 0 for 2-D) holds the image with zero borders, so that
+// every position a tile touches lies inside it.  One element per thread,
+// consecutive threads along the padded rows.
 template <int ESIZE>
 __global__ void __launch_bounds__(kThreads) conv_pad_kernel(const void *src, void *dst, int total,
-                                                            int d, int h, int w, int pz, int ph,
-                                                            int pw, int dp, int hp, int wp)
+                                                            PadDims p)
 {
     typedef typename Word<ESIZE>::T T;
     const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
     if (i >= total) return;
-    const int xp = i % wp;
-    int t = i / wp;
-    const int yp = t % hp;
-    t /= hp;
-    const int zp = t % dp;
-    const int c = t / dp;
-    const int z = zp - pz, y = yp - ph, x = xp - pw;
-    const bool in = ((unsigned)z < (unsigned)d) & ((unsigned)y < (unsigned)h) & ((unsigned)x < (unsigned)w);
+    const int xp = i % p.wp;
+    int t = i / p.wp;
+    const int yp = t % p.hp;
+    t /= p.hp;
+    const int zp = t % p.dp;
+    t /= p.dp;
+    const int up = t % p.up;
+    const int c = t / p.up;
+    const int u = up - p.pu, z = zp - p.pz, y = yp - p.ph, x = xp - p.pw;
+    const bool in = ((unsigned)u < (unsigned)p.u) & ((unsigned)z < (unsigned)p.d) &
+                    ((unsigned)y < (unsigned)p.h) & ((unsigned)x < (unsigned)p.w);
     const T *s = static_cast<const T *>(src);
-    static_cast<T *>(dst)[i] = in ? s[((int64_t)(c * d + z) * h + y) * w + x] : T(0);
+    static_cast<T *>(dst)[i] = in ? s[(((int64_t)(c * p.u + u) * p.d + z) * p.h + y) * p.w + x] : T(0);
 }
 
 // Filters with every filter row padded from S to S' taps, for the image-window
@@ -590,25 +610,22 @@ __global__ void __launch_bounds__(kThreads) conv_filter_unpad_kernel(const float
     dst[i] = src[(int64_t)row * sp + tap];
 }
 
-// Spatial dimensions of the padded implicit sources: depth (1 for 2-D), rows,
-// columns, and their paddings, before and after padding.
-struct PadDims {
-    int d, h, w, pz, ph, pw, dp, hp, wp;
-};
-
 PadDims pad_dims(const Dims &d)
 {
-    const int lead = 3 - (int)d.nd;  // 2-D: one leading unit dimension
+    const int lead = 4 - (int)d.nd;  // 2-D: two leading unit dimensions
     auto at = [&](const int64_t *v, int i, int64_t unit) {
         return (int)(i < lead ? unit : v[i - lead]);
     };
     PadDims p;
-    p.d = at(d.size, 0, 1);
-    p.h = at(d.size, 1, 1);
-    p.w = at(d.size, 2, 1);
-    p.pz = at(d.pad, 0, 0);
-    p.ph = at(d.pad, 1, 0);
-    p.pw = at(d.pad, 2, 0);
+    p.u = at(d.size, 0, 1);
+    p.d = at(d.size, 1, 1);
+    p.h = at(d.size, 2, 1);
+    p.w = at(d.size, 3, 1);
+    p.pu = at(d.pad, 0, 0);
+    p.pz = at(d.pad, 1, 0);
+    p.ph = at(d.pad, 2, 0);
+    p.pw = at(d.pad, 3, 0);
+    p.up = p.u + 2 * p.pu;
     p.dp = p.d + 2 * p.pz;
     p.hp = p.h + 2 * p.ph;
     p.wp = p.w + 2 * p.pw;
@@ -620,7 +637,7 @@ PadDims pad_dims(const Dims &d)
 int64_t padded_bytes(const Dims &d, int esize)
 {
     const PadDims p = pad_dims(d);
-    const int64_t elems = d.c * (int64_t)p.dp * p.hp * p.wp;
+    const int64_t elems = d.c * (int64_t)p.up * p.dp * p.hp * p.wp;
     return elems * esize < (int64_t(1) << 31) ? elems * esize : -1;
 }
 
@@ -745,6 +762,7 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
     if (x == nullptr || a == nullptr || !aligned_to(x, es) || !aligned_to(a, es))
         return GEMM_ERR_INVALID_ARG;
     ConvGeom geom{};
+    const bool four = vol && d.nd == 4;  // the four-dimensional sources
     int rc = vol ? make_geom3(d, es, &geom) : make_geom(d, es, &geom);
     if (rc != GEMM_OK) return rc;
     const int64_t pbytes = padded_bytes(d, es);
@@ -801,6 +819,8 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
         if ((rc = conv_padded_buffer(stream, (size_t)pbytes, &padded)) != GEMM_OK) return rc;
         // the loaders read the padded image: no padding left to apply
         if (vol) {
+            geom.du = pd.up;
+            geom.pu = 0;
             geom.d = pd.dp;
             geom.pz = 0;
         }
@@ -810,11 +830,14 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
         geom.pw = 0;
         geom.img_bytes = (int)pbytes;
         geom.tab = nullptr;
-        bsrc = vol ? (fwd ? B_CONV3_FWD_PAD : B_CONV3_WGRAD_PAD)
-                   : (fwd ? B_CONV_FWD_PAD : B_CONV_WGRAD_PAD);
+        bsrc = four ? (fwd ? B_CONV4_FWD_PAD : B_CONV4_WGRAD_PAD)
+               : vol ? (fwd ? B_CONV3_FWD_PAD : B_CONV3_WGRAD_PAD)
+                     : (fwd ? B_CONV_FWD_PAD : B_CONV_WGRAD_PAD);
     } else {
         geom.tab = nullptr;
-        bsrc = vol ? (fwd ? B_CONV3_FWD : B_CONV3_WGRAD) : (fwd ? B_CONV_FWD : B_CONV_WGRAD);
+        bsrc = four ? (fwd ? B_CONV4_FWD : B_CONV4_WGRAD)
+               : vol ? (fwd ? B_CONV3_FWD : B_CONV3_WGRAD)
+                     : (fwd ? B_CONV_FWD : B_CONV_WGRAD);
     }
     const int64_t vo = d.vol_out();
     const int total = (int)(pbytes > 0 ? pbytes / es : 0);
@@ -824,10 +847,10 @@ int run_implicit(int dtype, int dtype_out, const Dims &d, int addressing, bool f
             const dim3 grid((unsigned)((total + kThreads - 1) / kThreads)), block(kThreads);
             if (es == 4)
                 hipLaunchKernelGGL(conv_pad_kernel<4>, grid, block, 0, stream, img, padded, total,
-                                   pd.d, pd.h, pd.w, pd.pz, pd.ph, pd.pw, pd.dp, pd.hp, pd.wp);
+                                   pd);
             else
                 hipLaunchKernelGGL(conv_pad_kernel<2>, grid, block, 0, stream, img, padded, total,
-                                   pd.d, pd.h, pd.w, pd.pz, pd.ph, pd.pw, pd.dp, pd.hp, pd.wp);
+                                   pd);
             if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
             img = padded;
         }
@@ -1088,7 +1111,7 @@ int convnd_fwd_implicit_ex(int dtype, int dtype_y, const convnd_params *p, int a
     if (!dg::valid_dtype(dtype) || !dg::valid_dtype(dtype_y)) return GEMM_ERR_INVALID_ARG;
     const int rc = dg::dims_nd(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW ||
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW ||
         addressing == CONV_ADDR_TABLE)
         return GEMM_ERR_INVALID_ARG;
     return dg::run_implicit(dtype, dtype_y, d, addressing, true, true, x, w, y, stream);
@@ -1107,7 +1130,7 @@ int convnd_bwd_weight_implicit_ex(int dtype, const convnd_params *p, int address
     if (!dg::valid_dtype(dtype)) return GEMM_ERR_INVALID_ARG;
     const int rc = dg::dims_nd(p, &d);
     if (rc != GEMM_OK) return rc;
-    if (d.nd > 3 || addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW ||
+    if (addressing < CONV_ADDR_DEFAULT || addressing > CONV_ADDR_WINDOW ||
         addressing == CONV_ADDR_TABLE)
         return GEMM_ERR_INVALID_ARG;
     return dg::run_implicit(dtype, GEMM_DTYPE_F32, d, addressing, false, true, x, dy, dw, stream);

@@ -348,7 +348,7 @@ int check_args(const Call &c)
     const int64_t a_row = c.transa == GEMM_OP_T ? c.M : c.K;
     const int64_t b_row = c.transb == GEMM_OP_T ? c.K : c.N;
     const bool implicit = c.bsrc != B_MATRIX;
-    if (implicit && (c.bsrc < B_CONV_FWD || c.bsrc > B_CONV_WGRAD_WIN || c.conv == nullptr ||
+    if (implicit && (c.bsrc < B_CONV_FWD || c.bsrc > B_CONV4_WGRAD_PAD || c.conv == nullptr ||
                      c.transa != GEMM_OP_N ||
                      c.transb != (conv_fwd_source(c.bsrc) ? GEMM_OP_N : GEMM_OP_T) ||
                      (conv_table_source(c.bsrc) && c.conv->tab == nullptr)))

@@ -42,9 +42,10 @@ struct TileConfig {
     // (B = cols^T), [2] / [3] the same with table-looked-up per-k terms,
     // [4] / [5] the volume (3-D) forms, [6] .. [9] the 2-D and volume forms
     // reading a zero-padded image, [10] / [11] the 2-D forward product and
-    // filter gradient from image windows in LDS; [aligned], as fn.  nullptr
-    // where the entry has none.
-    launch_fn implicit[12][2];
+    // filter gradient from image windows in LDS, [12] .. [15] the
+    // four-dimensional forms (forward, filter gradient; on the image, on its
+    // zero-padded copy); [aligned], as fn.  nullptr where the entry has none.
+    launch_fn implicit[16][2];
 };
 
 // Declared here; defined in gemm_launch.hpp and explicitly instantiated by the
@@ -93,6 +94,18 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_LA_CWW ::dg::KMAJOR
 #define DG_LB_CWW ::dg::KMAJOR
 #define DG_BSRC_CWW ::dg::B_CONV_WGRAD_WIN
+#define DG_LA_C4F ::dg::KMAJOR
+#define DG_LB_C4F ::dg::MNMAJOR
+#define DG_BSRC_C4F ::dg::B_CONV4_FWD
+#define DG_LA_C4W ::dg::KMAJOR
+#define DG_LB_C4W ::dg::KMAJOR
+#define DG_BSRC_C4W ::dg::B_CONV4_WGRAD
+#define DG_LA_C4FP ::dg::KMAJOR
+#define DG_LB_C4FP ::dg::MNMAJOR
+#define DG_BSRC_C4FP ::dg::B_CONV4_FWD_PAD
+#define DG_LA_C4WP ::dg::KMAJOR
+#define DG_LB_C4WP ::dg::KMAJOR
+#define DG_BSRC_C4WP ::dg::B_CONV4_WGRAD_PAD
 
 // Memory orientation of op(A) / op(B) per layout combination: A as given is
 // k-contiguous, A^T (stored K x M) outer-contiguous; B as given is
@@ -196,10 +209,12 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
      DG_IFNS(BF16, BM, BN, BK, WM, WN, C3F), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3W),            \
      DG_IFNS(BF16, BM, BN, BK, WM, WN, CFP), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWP),            \
      DG_IFNS(BF16, BM, BN, BK, WM, WN, C3FP), DG_IFNS(BF16, BM, BN, BK, WM, WN, C3WP),          \
-     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFW), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWW)}
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, CFW), DG_IFNS(BF16, BM, BN, BK, WM, WN, CWW),            \
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, C4F), DG_IFNS(BF16, BM, BN, BK, WM, WN, C4W),            \
+     DG_IFNS(BF16, BM, BN, BK, WM, WN, C4FP), DG_IFNS(BF16, BM, BN, BK, WM, WN, C4WP)}
 #define DG_IMPL_NONE                                                                          \
     {DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, \
-     DG_NOFNS, DG_NOFNS, DG_NOFNS}
+     DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS, DG_NOFNS}
 #define DG_IMPL_ALL(...) DG_IMPL_NONE
 #define DG_IMPL_NN(...) DG_IMPL_NONE
 #define DG_IMPL_SKINNY(...) DG_IMPL_NONE

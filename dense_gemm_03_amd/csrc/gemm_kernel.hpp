@@ -106,19 +106,33 @@ enum BSource {
     // windows, with A the output gradient with rows padded to Q' positions
     // and C the gradient of the filters with rows padded to S' taps
     B_CONV_WGRAD_WIN = 12,
+    // Four spatial dimensions: the volume sources with one more, outermost
+    // dimension u -- image [C_in][U][D][H][W], taps (ci, ku, t, r, s), output
+    // positions (ou, o, p, q) -- analytic terms, on the image or on its
+    // zero-padded copy.
+    B_CONV4_FWD = 13,
+    B_CONV4_WGRAD = 14,
+    B_CONV4_FWD_PAD = 15,
+    B_CONV4_WGRAD_PAD = 16,
 };
 
 __host__ __device__ constexpr bool conv_fwd_source(int b)
 {
     return b == B_CONV_FWD || b == B_CONV_FWD_TAB || b == B_CONV3_FWD || b == B_CONV_FWD_PAD ||
-           b == B_CONV3_FWD_PAD || b == B_CONV_FWD_WIN;
+           b == B_CONV3_FWD_PAD || b == B_CONV_FWD_WIN || b == B_CONV4_FWD || b == B_CONV4_FWD_PAD;
 }
 __host__ __device__ constexpr bool conv_table_source(int b) { return b == B_CONV_FWD_TAB || b == B_CONV_WGRAD_TAB; }
+__host__ __device__ constexpr bool conv_4d_source(int b) { return b >= B_CONV4_FWD && b <= B_CONV4_WGRAD_PAD; }
 __host__ __device__ constexpr bool conv_volume_source(int b)
 {
-    return b == B_CONV3_FWD || b == B_CONV3_WGRAD || b == B_CONV3_FWD_PAD || b == B_CONV3_WGRAD_PAD;
+    return b == B_CONV3_FWD || b == B_CONV3_WGRAD || b == B_CONV3_FWD_PAD || b == B_CONV3_WGRAD_PAD ||
+           conv_4d_source(b);
 }
-__host__ __device__ constexpr bool conv_padded_source(int b) { return b >= B_CONV_FWD_PAD && b <= B_CONV3_WGRAD_PAD; }
+__host__ __device__ constexpr bool conv_padded_source(int b)
+{
+    return (b >= B_CONV_FWD_PAD && b <= B_CONV3_WGRAD_PAD) || b == B_CONV4_FWD_PAD ||
+           b == B_CONV4_WGRAD_PAD;
+}
 
 // Geometry of the convolution behind an implicit op(B), for one image
 // [C_in][H][W]: matrix row (ci R + r) S + s, column p Q + q holds
@@ -134,6 +148,12 @@ struct ConvGeom {
     int d, t, pz, sz, lz, p;              // depth, filter depth, its padding, stride, dilation; P
     uint64_t trs_magic, pq_magic;         // k / (T R S), j / (P Q)
     int trs_shift, pq_shift;
+    // four-dimensional sources only: the outermost dimension's size, filter
+    // size, padding, stride and dilation, O P Q (positions per outermost
+    // output index), and k / (KU T R S), j / (O P Q)
+    int du, ku, pu, su, lu, opq;
+    uint64_t ktrs_magic, opq_magic;
+    int ktrs_shift, opq_shift;
     // Window source only (all on the zero-bordered image: h, w are its padded
     // sizes): sp = S' taps per filter row (S rounded up to a 16-byte slot and
     // dividing BK; s >= S are zero filter taps), cr = C_in R filter rows, nr
@@ -883,17 +903,18 @@ struct ConvGather {
     static constexpr bool FWD = conv_fwd_source(MODE);
     static constexpr bool TAB = conv_table_source(MODE);
     static constexpr bool VOL = conv_volume_source(MODE);
+    static constexpr bool V4 = conv_4d_source(MODE);
     static constexpr bool PAD = conv_padded_source(MODE);
     static constexpr int ES = (int)sizeof(In);
     static_assert(T::NT % T::CPR == 0, "a thread's chunks must share their columns");
     static_assert((FWD && T::LAYOUT == MNMAJOR) || (!FWD && T::LAYOUT == KMAJOR),
                   "tile orientation of the convolution source");
 
-    // Image coordinates (depth z for volume sources only) and byte offset of
-    // a term; an element's coordinates and offset are the sums of its
-    // column term and its row term.
+    // Image coordinates (depth z for volume sources only, the outermost u for
+    // four-dimensional ones) and byte offset of a term; an element's
+    // coordinates and offset are the sums of its column term and its row term.
     struct Term {
-        int z, y, x, o;
+        int u, z, y, x, o;
     };
 
     __amdgpu_buffer_rsrc_t rsrc;
@@ -913,13 +934,24 @@ struct ConvGather {
     // every tap they read V consecutive image elements.
     bool run = false;
 
-    // Terms of tap k = (ci R + r) S + s (volume: ((ci T + t) R + r) S + s):
-    // z = t lz, y = r dh, x = s dw and the offset of (ci, z, y, x).
+    // Terms of tap k = (ci R + r) S + s (volume: ((ci T + t) R + r) S + s;
+    // four dimensions: (((ci KU + ku) T + t) R + r) S + s): u = ku lu,
+    // z = t lz, y = r dh, x = s dw and the offset of (ci, u, z, y, x).
     __device__ __forceinline__ Term tap_terms(int k) const
     {
         Term e;
         int ci, rem;
-        if constexpr (VOL) {
+        e.u = 0;
+        if constexpr (V4) {
+            ci = div_magic(k, g->ktrs_magic, g->ktrs_shift);
+            rem = k - ci * g->ku * g->t * g->r * g->s;
+            const int uu = div_magic(rem, g->trs_magic, g->trs_shift);
+            rem -= uu * g->t * g->r * g->s;
+            e.u = uu * g->lu;
+            const int tt = div_magic(rem, g->rs_magic, g->rs_shift);
+            rem -= tt * g->r * g->s;
+            e.z = tt * g->lz;
+        } else if constexpr (VOL) {
             ci = div_magic(k, g->trs_magic, g->trs_shift);
             rem = k - ci * g->t * g->r * g->s;
             const int tt = div_magic(rem, g->rs_magic, g->rs_shift);
@@ -934,20 +966,27 @@ struct ConvGather {
         const int s = rem - r * g->s;
         e.y = r * g->dh;
         e.x = s * g->dw;
-        const int plane = VOL ? ci * g->d + e.z : ci;
+        const int plane = V4 ? (ci * g->du + e.u) * g->d + e.z : VOL ? ci * g->d + e.z : ci;
         e.o = ((plane * g->h + e.y) * g->w + e.x) * ES;
         return e;
     }
-    // Terms of output position j = p Q + q (volume: (o P + p) Q + q):
-    // z = o sz - pz, y = p sh - ph, x = q sw - pw and the (possibly negative)
-    // offset of (z, y, x).
+    // Terms of output position j = p Q + q (volume: (o P + p) Q + q; four
+    // dimensions: ((ou O + o) P + p) Q + q): u = ou su - pu, z = o sz - pz,
+    // y = p sh - ph, x = q sw - pw and the (possibly negative) offset of
+    // (u, z, y, x).
     __device__ __forceinline__ Term out_terms(int j) const
     {
         Term e;
         int rem = j;
+        e.u = 0;
+        if constexpr (V4) {
+            const int ou = div_magic(j, g->opq_magic, g->opq_shift);
+            rem = j - ou * g->opq;
+            e.u = ou * g->su - g->pu;
+        }
         if constexpr (VOL) {
-            const int o = div_magic(j, g->pq_magic, g->pq_shift);
-            rem = j - o * g->pq;
+            const int o = div_magic(rem, g->pq_magic, g->pq_shift);
+            rem -= o * g->pq;
             e.z = o * g->sz - g->pz;
         } else {
             e.z = 0;
@@ -956,7 +995,7 @@ struct ConvGather {
         const int q = rem - p * g->q;
         e.y = p * g->sh - g->ph;
         e.x = q * g->sw - g->pw;
-        e.o = (((VOL ? e.z * g->h : 0) + e.y) * g->w + e.x) * ES;
+        e.o = (((VOL ? ((V4 ? e.u * g->d : 0) + e.z) * g->h : 0) + e.y) * g->w + e.x) * ES;
         return e;
     }
     // Per-k terms of k (clamped into the matrix by the caller).
@@ -969,7 +1008,7 @@ struct ConvGather {
     }
     static __device__ __forceinline__ Term unpack(int2 e)
     {
-        return Term{0, (e.x << 16) >> 16, e.x >> 16, e.y};
+        return Term{0, 0, (e.x << 16) >> 16, e.x >> 16, e.y};
     }
     // k of this thread's i-th per-k slot in the k-tile at k0.
     __device__ __forceinline__ int k_of(int k0, int i) const
@@ -986,7 +1025,7 @@ struct ConvGather {
     // V consecutive terms that read V consecutive image elements of one row.
     static __device__ __forceinline__ bool is_run(const Term &a, const Term &b)
     {
-        return (!VOL || a.z == b.z) & (a.y == b.y) & (b.x == a.x + (V - 1));
+        return (!V4 || a.u == b.u) & (!VOL || a.z == b.z) & (a.y == b.y) & (b.x == a.x + (V - 1));
     }
 
     __device__ __forceinline__ ConvGather(const KernelArgs &a, int bn, int tid, int kbeg, int kend)
@@ -1015,13 +1054,14 @@ struct ConvGather {
         prefetch(kbeg, kend);
     }
 
-    // Whether image position (z, y, x) lies inside the image: unsigned
+    // Whether image position (u, z, y, x) lies inside the image: unsigned
     // compares joined without short-circuits.
-    __device__ __forceinline__ bool inside(int z, int y, int x) const
+    __device__ __forceinline__ bool inside(int u, int z, int y, int x) const
     {
         if constexpr (PAD) return true;  // the padded image holds every position
         bool in = ((unsigned)y < (unsigned)g->h) & ((unsigned)x < (unsigned)g->w);
         if constexpr (VOL) in = in & ((unsigned)z < (unsigned)g->d);
+        if constexpr (V4) in = in & ((unsigned)u < (unsigned)g->du);
         return in;
     }
 
@@ -1029,7 +1069,7 @@ struct ConvGather {
     // or it lies in the padding.
     __device__ __forceinline__ In fetch(bool ok, const Term &c, const Term &k) const
     {
-        const bool in = ok & inside(c.z + k.z, c.y + k.y, c.x + k.x);
+        const bool in = ok & inside(c.u + k.u, c.z + k.z, c.y + k.y, c.x + k.x);
         const int vo = in ? c.o + k.o : (int)0x80000000u;
         if constexpr (ES == 4)
             return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, 0, 0));
@@ -1074,7 +1114,8 @@ struct ConvGather {
             for (int u = 0; u < U; ++u) {
                 const Term &t = kt[u];
                 const bool whole = run & kok[u] &
-                                   inside(f[0].z + t.z, f[0].y + t.y, f[0].x + t.x) &
+                                   inside(f[0].u + t.u, f[0].z + t.z, f[0].y + t.y,
+                                          f[0].x + t.x) &
                                    (PAD || f[V - 1].x + t.x < g->w);
                 if (whole) {
                     r[u] = load_run(f[0].o + t.o);
@@ -1091,7 +1132,8 @@ struct ConvGather {
             for (int u = 0; u < U; ++u) {
                 const Term &t = f[u];
                 const bool whole = krun & fok[u] &
-                                   inside(t.z + kt[0].z, t.y + kt[0].y, t.x + kt[0].x) &
+                                   inside(t.u + kt[0].u, t.z + kt[0].z, t.y + kt[0].y,
+                                          t.x + kt[0].x) &
                                    (PAD || t.x + kt[V - 1].x < g->w);
                 if (whole) {
                     r[u] = load_run(t.o + kt[0].o);

@@ -2,9 +2,10 @@
 // operand layout's kernels from the tile lists.  Included by the per-layout
 // source files, each of which defines DG_DTYPE_TABLE (the list), DG_LAYOUT
 // (NN, NT, TN, TT, or CF / CW / CFT / CWT / C3F / C3W / CFP / CWP / C3FP /
-// C3WP / CFW / CWW for the implicit-GEMM convolution kernels: forward /
-// filter gradient, analytic / table-looked-up terms, volume, padded image,
-// image windows) and then includes this header.
+// C3WP / CFW / CWW / C4F / C4W / C4FP / C4WP for the implicit-GEMM convolution
+// kernels: forward / filter gradient, analytic / table-looked-up terms,
+// volume, padded image, image windows, four dimensions) and then includes
+// this header.
 #pragma once
 
 #include "gemm_configs.hpp"
@@ -54,6 +55,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_ALL_C3WP(...)
 #define DG_INST_ALL_CFW(...)
 #define DG_INST_ALL_CWW(...)
+#define DG_INST_ALL_C4F(...)
+#define DG_INST_ALL_C4W(...)
+#define DG_INST_ALL_C4FP(...)
+#define DG_INST_ALL_C4WP(...)
 #define DG_INST_CONV_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_CONV_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_CONV_TN(...) DG_INST(__VA_ARGS__, TN)
@@ -70,6 +75,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_CONV_C3WP(...) DG_IINST(__VA_ARGS__, C3WP)
 #define DG_INST_CONV_CFW(...) DG_IINST(__VA_ARGS__, CFW)
 #define DG_INST_CONV_CWW(...) DG_IINST(__VA_ARGS__, CWW)
+#define DG_INST_CONV_C4F(...) DG_IINST(__VA_ARGS__, C4F)
+#define DG_INST_CONV_C4W(...) DG_IINST(__VA_ARGS__, C4W)
+#define DG_INST_CONV_C4FP(...) DG_IINST(__VA_ARGS__, C4FP)
+#define DG_INST_CONV_C4WP(...) DG_IINST(__VA_ARGS__, C4WP)
 #define DG_INST_SKINNYC_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_SKINNYC_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_SKINNYC_TN(...)
@@ -86,6 +95,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_SKINNYC_C3WP(...) DG_IINST(__VA_ARGS__, C3WP)
 #define DG_INST_SKINNYC_CFW(...) DG_IINST(__VA_ARGS__, CFW)
 #define DG_INST_SKINNYC_CWW(...) DG_IINST(__VA_ARGS__, CWW)
+#define DG_INST_SKINNYC_C4F(...) DG_IINST(__VA_ARGS__, C4F)
+#define DG_INST_SKINNYC_C4W(...) DG_IINST(__VA_ARGS__, C4W)
+#define DG_INST_SKINNYC_C4FP(...) DG_IINST(__VA_ARGS__, C4FP)
+#define DG_INST_SKINNYC_C4WP(...) DG_IINST(__VA_ARGS__, C4WP)
 #define DG_INST_SKINNY_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_SKINNY_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_SKINNY_TN(...)
@@ -102,6 +115,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_SKINNY_C3WP(...)
 #define DG_INST_SKINNY_CFW(...)
 #define DG_INST_SKINNY_CWW(...)
+#define DG_INST_SKINNY_C4F(...)
+#define DG_INST_SKINNY_C4W(...)
+#define DG_INST_SKINNY_C4FP(...)
+#define DG_INST_SKINNY_C4WP(...)
 #define DG_INST_KK_NN(...)
 #define DG_INST_KK_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_KK_TN(...)
@@ -118,6 +135,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_KK_C3WP(...)
 #define DG_INST_KK_CFW(...)
 #define DG_INST_KK_CWW(...)
+#define DG_INST_KK_C4F(...)
+#define DG_INST_KK_C4W(...)
+#define DG_INST_KK_C4FP(...)
+#define DG_INST_KK_C4WP(...)
 #define DG_INST_NN_NN(...) DG_INST(__VA_ARGS__, NN)
 #define DG_INST_NN_NT(...)
 #define DG_INST_NN_TN(...)
@@ -134,6 +155,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_NN_C3WP(...)
 #define DG_INST_NN_CFW(...)
 #define DG_INST_NN_CWW(...)
+#define DG_INST_NN_C4F(...)
+#define DG_INST_NN_C4W(...)
+#define DG_INST_NN_C4FP(...)
+#define DG_INST_NN_C4WP(...)
 #define DG_INST_SEL2(LAYOUTS, L) DG_INST_##LAYOUTS##_##L
 #define DG_INST_SEL(LAYOUTS, L) DG_INST_SEL2(LAYOUTS, L)
 #define DG_INST_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                            \

@@ -230,13 +230,13 @@ int convnd_fwd(int dtype, int dtype_y, const convnd_params *p, const void *x, co
 int convnd_bwd_weight(int dtype, const convnd_params *p, const void *x, const void *dy, float *dw,
                       void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
-/* Implicit-GEMM forms for 1 to 3 spatial dimensions ("Three X's", section
+/* Implicit-GEMM forms for 1 to 4 spatial dimensions ("Three X's", section
  * "CUTLASS", applied to the N-D matrix): no convolution matrix and no
  * workspace; the GEMM's loader forms each tile from the image with analytic
- * address terms (fewer than three dimensions run as three with leading unit
- * dimensions).  Same arguments, layouts, types and results as convnd_fwd /
- * convnd_bwd_weight; GEMM_ERR_INVALID_ARG for ndim 4 and when one batch
- * element of x spans 2 GiB or more.  The _ex forms take the addressing:
+ * address terms (one to three dimensions run as three with leading unit
+ * dimensions; four add the outermost index to those terms).  Same
+ * arguments, layouts, types and results as convnd_fwd / convnd_bwd_weight;
+ * GEMM_ERR_INVALID_ARG when one batch element of x spans 2 GiB or more.  The _ex forms take the addressing:
  * CONV_ADDR_ANALYTIC, CONV_ADDR_PADDED (the image copied with zero borders
  * in every padded dimension, as for the 2-D calls; CONV_ADDR_WINDOW runs
  * this form here) or CONV_ADDR_DEFAULT (padded when the padded image is

@@ -368,9 +368,12 @@ def test_convnd_host_logic_and_invalid_arguments():
     for t, call in enumerate(calls):
         assert call() == dg.GEMM_ERR_INVALID_ARG, t
     assert dg.convnd_fwd(F32, F32, N(0, 3, 4, (5,), (3,)), None, None, None, None, 0) == dg.GEMM_OK
-    # implicit forms: up to three dimensions, one image below 2 GiB
-    assert dg.convnd_fwd_implicit(F32, F32, p4, p, p, p) == dg.GEMM_ERR_INVALID_ARG
-    assert dg.convnd_bwd_weight_implicit(F32, p4, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    # implicit forms: one to four dimensions, one image below 2 GiB
+    assert dg.convnd_fwd_implicit(F32, F32, p4, p, p, p + 2) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.convnd_bwd_weight_implicit(F32, p4, p, p + 1, p) == dg.GEMM_ERR_INVALID_ARG
+    big4 = N(1, 4, 1, (2, 256, 512, 512), (1, 1, 1, 1))   # 4 x 2^27 fp32 elements: 2 GiB
+    assert dg.convnd_fwd_implicit(F32, F32, big4, p, p, p) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.convnd_bwd_weight_implicit(F32, big4, p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.convnd_fwd_implicit(F32, F32, bad[0], p, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.convnd_fwd_implicit(F32, F32, ok, None, p, p) == dg.GEMM_ERR_INVALID_ARG
     assert dg.convnd_bwd_weight_implicit(F32, ok, p, p, p + 2) == dg.GEMM_ERR_INVALID_ARG

@@ -12,10 +12,11 @@ direct-convolution oracle, through the C ABI (include/conv.h, convnd_*).
 * Random tensors: |y - y_ref| <= tol * S (1e-5 fp32, 4e-3 bf16 inputs).
 * D = 2 through the N-D entry points gives the conv2d entry points' bits.
 * The full-size 3-D and 4-D workloads at sampled outputs and taps.
-* Forward and filter gradient through im2col + GEMM and, up to three
-  dimensions, through the implicit GEMM (volume tiles formed in the loader,
-  from the image with analytic terms or from a zero-bordered copy of it);
-  the two implicit forms give identical bits.
+* Forward and filter gradient through im2col + GEMM and through the
+  implicit GEMM (volume tiles formed in the loader, from the image with
+  analytic terms or from a zero-bordered copy of it; four dimensions add the
+  outermost index to the loader's terms); the two implicit forms give
+  identical bits.
 """
 from __future__ import annotations
 
@@ -125,8 +126,9 @@ def test_im2col_bit_exact(bf16):
 
 
 def _shapes(implicit):
-    """The implicit GEMM covers up to three spatial dimensions."""
-    return [(t, c) for t, c in enumerate(SHAPES) if not implicit or c.nd <= 3]
+    """Every shape, for each route (the implicit GEMM covers one to four
+    spatial dimensions, as the im2col route does)."""
+    return list(enumerate(SHAPES))
 
 
 # im2col + GEMM, and the implicit GEMM with analytic terms or over a
@@ -196,7 +198,7 @@ def test_two_dimensions_match_conv2d_bits():
 def test_implicit_addressing_forms_agree_bitwise():
     """Analytic terms and the padded image feed the same products in the same
     order: identical bits, forward and filter gradient, both types, for
-    every shape of up to three dimensions."""
+    every shape of one to four dimensions."""
     import torch
     for t, c in _shapes(True):
         for bf16 in (False, True):
@@ -237,8 +239,6 @@ def test_full_size_sampled(name, implicit):
     and the convolution matrix of the last image bit for bit at sampled rows."""
     wk = wl.CONVND_WORKLOADS[name]
     c = _shape_of(wk)
-    if implicit and c.nd > 3:
-        pytest.skip("the implicit GEMM covers up to three spatial dimensions")
     bf16 = wk.dtype == "bf16"
     tol = TOL[wk.dtype]
     x, w, dy = wk.x(), wk.weights(), wk.dy()
@@ -274,9 +274,11 @@ def test_full_size_sampled(name, implicit):
 
 
 @pytest.mark.parametrize("implicit", ROUTES, ids=ROUTE_IDS)
-def test_full_size_exact_integers_sampled(implicit):
-    """Integer tensors of the full 3-D shape: sampled outputs and taps exact."""
-    wk = wl.CONVND_WORKLOADS["conv3d-32c-k7"]
+@pytest.mark.parametrize("name", ["conv3d-32c-k7", "conv4d-16c-k5"])
+def test_full_size_exact_integers_sampled(name, implicit):
+    """Integer tensors of the full 3-D and 4-D shapes: sampled outputs and
+    taps exact."""
+    wk = wl.CONVND_WORKLOADS[name]
     c = _shape_of(wk)
     x, w, dy = _ints(c.x_shape, 17, False), _ints(c.w_shape, 18, False), _ints(c.y_shape, 19, False)
     y, _ = run_fwd(x, w, c, False, implicit)
