@@ -1461,6 +1461,102 @@ __device__ __forceinline__ void store_out(void *C, int64_t idx, float sum, float
     }
 }
 
+// Finished C through LDS, for interior blocks whose output is not the plain
+// fp32 product (alpha != 1, beta != 0 or bf16 C) and whose C rows are aligned:
+// the fragment layout gives each lane single elements of 32 columns, so
+// element-wise stores (and, with beta != 0, loads of the old C) would move 4
+// or 2 bytes per lane.  After the main loop the stages are free: each wave
+// writes one 32-row fragment row of its sub-block (32 x WTN fp32) to its own
+// LDS scratch, reads it back as 16-byte row pieces (4 consecutive columns),
+// and loads, scales and stores C in those pieces -- whole 128-byte lines
+// per half-wave.  The scratch is row-major with the 32-column halves of
+// each 64-column group swapped in rows with bit 2 set, so the two lane halves
+// of a fragment write (rows i and i+4) fall on different banks and the
+// 16-byte reads of 16 lanes cover 256 contiguous bytes.
+template <class G>
+struct StagedOut {
+    static constexpr int BYTES = 32 * G::WTN * 4;                // one wave's scratch
+    static constexpr int PER_STAGE = G::STAGE_BYTES / BYTES;     // scratches per stage array
+    static constexpr int CPR = G::WTN / 4;                       // 16-byte pieces per row
+    static constexpr int PER_LANE = 32 * CPR / 64;               // pieces per lane and row block
+    static constexpr bool OK = G::WTN % 64 == 0 && PER_STAGE * G::STAGES >= G::NW;
+};
+
+template <class G>
+__device__ __forceinline__ int staged_col(int row, int col)
+{
+    return col ^ (((row >> 2) & 1) << 5);
+}
+
+template <class G>
+__device__ __forceinline__ void staged_epilogue(unsigned char *l0, unsigned char *l1,
+                                                unsigned char *l2, unsigned char *l3,
+                                                const BlockCtx<G> &c, const KernelArgs &p,
+                                                const floatx16 (&acc)[G::FM][G::FN])
+{
+    using S = StagedOut<G>;
+    const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+    const int arr = wave / S::PER_STAGE;
+    unsigned char *scr = (arr == 0 ? l0 : arr == 1 ? l1 : arr == 2 ? l2 : l3) +
+                         (wave % S::PER_STAGE) * S::BYTES;
+    const int half = c.lane >> 5, l32 = c.lane & 31;
+    const bool out_bf16 = p.out_bf16 != 0, read_c = p.beta != 0.0f;
+    const float alpha = p.alpha, beta = p.beta;
+    // the stages' last readers are done before any wave writes its scratch
+    __syncthreads();
+    static_for<0, G::FM>([&](auto fm) {
+#pragma unroll
+        for (int fn = 0; fn < G::FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+                *reinterpret_cast<float *>(scr + 4 * (row * G::WTN +
+                                                      staged_col<G>(row, fn * 32 + l32))) =
+                    acc[fm][fn][r];
+            }
+        // A wave's LDS accesses complete in order: the reads below see the
+        // writes above, and the next row block's writes follow these reads.
+        const int64_t row0 = c.bm + c.wrow * G::WTM + fm * 32;
+        const int col0 = c.bn + c.wcol * G::WTN;
+        u32x4 old[S::PER_LANE];
+        if (read_c) {
+#pragma unroll
+            for (int u = 0; u < S::PER_LANE; ++u) {
+                const int ch = c.lane + 64 * u, rr = ch / S::CPR, cc = ch % S::CPR;
+                const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
+                if (out_bf16) {
+                    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.C) + idx);
+                    old[u] = u32x4{w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u};
+                } else {
+                    old[u] = load16(static_cast<const float *>(p.C) + idx);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < S::PER_LANE; ++u) {
+            const int ch = c.lane + 64 * u, rr = ch / S::CPR, cc = ch % S::CPR;
+            const u32x4 raw = lds_load16(scr, 4 * (rr * G::WTN + staged_col<G>(rr, 4 * cc)));
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = alpha * __uint_as_float(raw[e]);
+                if (read_c) v[e] += beta * __uint_as_float(old[u][e]);
+            }
+            const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
+            if (out_bf16) {
+                uint2 w;
+                w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+                w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.C) + idx) = w;
+            } else {
+                *reinterpret_cast<u32x4 *>(static_cast<float *>(p.C) + idx) =
+                    u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3])};
+            }
+        }
+    });
+}
+
 // ------------------------------------------------------------------ kernel --
 
 template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
@@ -1595,6 +1691,15 @@ gemm_kernel(KernelArgs p)
                 }
             }
         return;
+    }
+    if constexpr (StagedOut<G>::OK) {
+        // whole C pieces: C rows 16-byte (fp32) or 8-byte (bf16) aligned
+        const int64_t align = p.out_bf16 ? 8 : 16;
+        const int64_t esz = p.out_bf16 ? 2 : 4;
+        if (!store_edge && (p.ldc * esz) % align == 0 && (uintptr_t)p.C % align == 0) {
+            staged_epilogue<G>(lds0, lds1, lds2, lds3, c, p, acc);
+            return;
+        }
     }
     static_for<0, G::FM>([&](auto fm) {
         static_for<0, G::FN>([&](auto fn) {
