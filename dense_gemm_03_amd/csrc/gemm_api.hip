@@ -2,6 +2,7 @@
 // the tile table, split-K workspace, launches.  Declared in include/gemm.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstring>
@@ -23,6 +24,8 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;  // keeps all in-kernel int math e
 // a host without a GPU): MI355X, 8 XCDs x 32 CUs.
 constexpr int kDefaultComputeUnits = 256;
 constexpr int kMaxStreamSplits = 16;
+// LDS bytes of one compute unit (gfx950).
+constexpr int64_t kLdsBytes = 160 * 1024;
 constexpr int kMaxDevices = 64;
 
 // Compute units of the current device (hipDeviceGetAttribute, cached per
@@ -210,6 +213,18 @@ int select_implicit(int dtype, int64_t M)
     return M <= 32 ? skinny : M <= 64 ? wide : M <= 128 ? mid : large;
 }
 
+// Whether the blocks of a plain product at the M and N edges take the 16-byte
+// direct loads (the kernel's condition, assuming aligned rows): each operand
+// read outer-contiguous (A^T, or B as given) must have an outer extent that is
+// a whole number of 16-byte chunks.
+bool direct_edges(int layout, int64_t M, int64_t N, int esize)
+{
+    const int vec = 16 / esize;
+    const bool a_outer = layout == LAYOUT_TN || layout == LAYOUT_TT;
+    const bool b_outer = layout == LAYOUT_NN || layout == LAYOUT_TN;
+    return (!a_outer || M % vec == 0) && (!b_outer || N % vec == 0);
+}
+
 // Number of K slices.  Large blocks: 1 when the output alone yields enough
 // blocks to fill the chip; otherwise enough slices for about two blocks per
 // compute unit.  Blocks of at most 64 rows (the skinny and wide classes) carry
@@ -217,9 +232,15 @@ int select_implicit(int dtype, int64_t M)
 // B is read k-contiguous (B^T, rows of a few hundred bytes per k-tile) they
 // aim at six blocks per compute unit even when the output alone fills the
 // chip, since each block then sustains less bandwidth.  Every slice keeps at
-// least four k-tiles.  forced > 0 overrides the target.
+// least four k-tiles.  bf16 blocks of more than 64 rows whose blocks at the M
+// and N edges also take the direct loads (direct_edges) split only as far as
+// one round of resident blocks and twelve k-tiles per slice allow: on 128 x
+// 128 blocks at M, N of 1024-2048 (K 512-8192) a split that adds a round of
+// blocks, or leaves shorter slices, costs more in partial sums and pipeline
+// fill than it gains (1536^3: 30.3 us with the four slices of the two-blocks-
+// per-CU target, 21.3 us unsplit).  forced > 0 overrides the target.
 void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K, int forced,
-                int cus, int *splits, int *k_per_split)
+                int cus, int esize, bool direct_edges, int *splits, int *k_per_split)
 {
     const int64_t target_blocks = 2 * (int64_t)cus, stream_blocks = 6 * (int64_t)cus;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
@@ -231,6 +252,10 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
         s = forced;
     } else if (tiles >= cus && !(streaming && b_kcontig)) {
         s = 1;
+    } else if (esize == 2 && !streaming && direct_edges) {
+        const int64_t lds = (int64_t)c.stages * (c.bm + c.bn) * c.bk * esize;
+        const int64_t per_cu = std::max<int64_t>(1, kLdsBytes / lds);
+        s = std::min((int64_t)cus * per_cu / tiles, ktiles / 12);
     } else {
         s = ceil_div(streaming && b_kcontig ? stream_blocks : target_blocks, tiles);
         int64_t max_s = ktiles / 4;
@@ -450,7 +475,15 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     const TileConfig &cfg = tab[ci];
     if (kernel_of(cfg, true) == nullptr) return GEMM_ERR_INVALID_ARG;
     int splits = 1, kps = 0;
-    plan_split(cfg, layout, M, N, K, forced_split, cus, &splits, &kps);
+    {
+        const int esize = (int)elem_size(call.dtype);
+        const int v = 16 / esize;
+        const bool rows_aligned = call.lda % v == 0 && (uintptr_t)call.A % 16 == 0 &&
+                                  call.ldb % v == 0 && (uintptr_t)call.B % 16 == 0;
+        plan_split(cfg, layout, M, N, K, forced_split, cus, esize,
+                   call.bsrc == B_MATRIX && rows_aligned && direct_edges(layout, M, N, esize),
+                   &splits, &kps);
+    }
 
     // Thin remainders (dispatcher's choice only; a forced entry runs as asked):
     // when the last block row or column would hold at most an eighth of a
@@ -752,7 +785,9 @@ int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K)
     if (!tab || cfg < 0 || cfg >= count || M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || K == 0) return 1;
     int splits = 1, kps = 0;
-    dg::plan_split(tab[cfg], dg::LAYOUT_NN, M, N, K, 0, dg::compute_units(), &splits, &kps);
+    const int es = dtype == GEMM_DTYPE_BF16 ? 2 : 4;
+    dg::plan_split(tab[cfg], dg::LAYOUT_NN, M, N, K, 0, dg::compute_units(), es,
+                   dg::direct_edges(dg::LAYOUT_NN, M, N, es), &splits, &kps);
     return splits;
 }
 
@@ -765,8 +800,9 @@ int gemm_split_k_ex(int dtype, int cfg, int transa, int transb, int64_t M, int64
         return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || K == 0) return 1;
     int splits = 1, kps = 0;
-    dg::plan_split(tab[cfg], transa * 2 + transb, M, N, K, 0, dg::compute_units(), &splits,
-                   &kps);
+    const int es = dtype == GEMM_DTYPE_BF16 ? 2 : 4;
+    dg::plan_split(tab[cfg], transa * 2 + transb, M, N, K, 0, dg::compute_units(), es,
+                   dg::direct_edges(transa * 2 + transb, M, N, es), &splits, &kps);
     return splits;
 }
 

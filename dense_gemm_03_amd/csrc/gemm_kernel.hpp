@@ -575,16 +575,32 @@ struct TileOffsets {
 // -- so each lane fetches the global element(s) that the tile's swizzle places
 // at its LDS position.  LDS row r is memory row r of the tile (an outer index
 // for KMAJOR, a k for MNMAJOR).
+//
+// 16-byte loads of a block at the M or N edge fetch in-bounds data for the
+// positions past the edge: a KMAJOR row past the last outer index reads the
+// last row, and an MNMAJOR chunk past the edge reads the last chunk (the
+// caller takes this form only when that outer extent is a whole number of
+// chunks, so no chunk straddles the edge).  Those LDS positions only feed
+// outputs past the edge, which are never stored.  outer0 is the block's
+// first outer index, n_outer the matrix's outer extent; for interior blocks
+// the clamps change nothing.
 template <class T, int DW>
-__device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t ld, TileOffsets<T, DW> &o)
+__device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t ld, int outer0,
+                                             int n_outer, TileOffsets<T, DW> &o)
 {
     using O = TileOffsets<T, DW>;
 #pragma unroll
     for (int i = 0; i < O::PER_WAVE; ++i) {
         const int piece = wave + T::NW * i;
         const int byte = piece * O::PIECE + DW * lane;
-        const int row = byte / T::ROW_BYTES;
-        const int e = T::logical_elem(row, (byte % T::ROW_BYTES) / T::ES);
+        int row = byte / T::ROW_BYTES;
+        int e = T::logical_elem(row, (byte % T::ROW_BYTES) / T::ES);
+        if constexpr (DW == 16) {
+            if constexpr (T::LAYOUT == KMAJOR)
+                row = min(outer0 + row, n_outer - 1) - outer0;
+            else
+                e = min(outer0 + e, n_outer - T::VEC) - outer0;
+        }
         o.v[i] = (uint32_t)(((int64_t)row * ld + e) * T::ES);
     }
 }
@@ -741,8 +757,8 @@ __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
     unsigned char *const st[4] = {s0, s1, s2, s3};
     Frags<G> cur;
     DirectOffsets<G, DW> o;
-    tile_offsets(c.tid >> 6, c.lane, c.lda, o.a);
-    tile_offsets(c.tid >> 6, c.lane, c.ldb, o.b);
+    tile_offsets(c.tid >> 6, c.lane, c.lda, c.bm, c.M, o.a);
+    tile_offsets(c.tid >> 6, c.lane, c.ldb, c.bn, c.N, o.b);
     // k of the next tile to load; past the last tile the loads wrap round to
     // tiles already done (never read, and in bounds), so the code has no branch
     // rotated start for bf16 (measured: +3-6% on large square products;
@@ -1608,12 +1624,16 @@ gemm_kernel(KernelArgs p)
     // masked loads.  The choice is uniform per workgroup.
     if constexpr (BSRC == B_MATRIX) {
         // Whole k-tiles go through direct global->LDS loads: 16 bytes per lane
-        // for interior blocks of aligned operands; for fp32 entries also 4
-        // range-checked bytes per lane for blocks crossing the M or N edge and
+        // for aligned operands, in interior blocks and in blocks crossing the
+        // M or N edge when each outer-contiguous operand's outer extent is a
+        // whole number of 16-byte chunks (see tile_offsets); for fp32 entries
+        // also 4 range-checked bytes per lane for the other edge blocks and
         // for rows at any alignment.  Other cases, and the partial last
         // k-tile, take the masked loads.
         const bool edge_mn = c.bm + BM > p.M || c.bn + BN > p.N;
-        const bool x4 = ALIGNED && p.direct_ok && !edge_mn;
+        const bool edge16 = (G::LA == KMAJOR || p.M % G::VEC == 0) &&
+                            (G::LB == KMAJOR || p.N % G::VEC == 0);
+        const bool x4 = ALIGNED && p.direct_ok && (!edge_mn || edge16);
         const bool dw = G::DMA4 && p.direct_ok && !x4;
         const int nfast = x4 || dw ? (c.kend - kbeg) / BK : 0;
         c.rot = (tm + tn) % 8;
