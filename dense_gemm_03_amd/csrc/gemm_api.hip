@@ -178,6 +178,7 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     };
     static const int medium = config_index(dtype, "bf16_128x128x64_w2x2_s2");
     static const int small = config_index(dtype, "bf16_64x64x64_w2x2_s2");
+    static const int small_deep = config_index(dtype, "bf16_64x64x64_w2x2_s4");
     static const int wide = config_index(dtype, "bf16_64x256x64_w1x4_s3");
     // wide A . B^T: 64x64 blocks, four stages of 64 k (64 KB of LDS: two
     // resident blocks per CU); measured 3% faster than 256-deep k-tiles
@@ -191,8 +192,18 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     if (M >= 2048 && N >= 2048)
         return layout == LAYOUT_NT || layout == LAYOUT_TT ? best_of(dtype, large_bt, 2, M, N, cus)
                                                           : best_of(dtype, large, 2, M, N, cus);
-    if (M * N >= int64_t(1024) * 1024) return medium;
-    return small;
+    // Mid-size and small products, from a sweep of A . B and A . B^T at M, N
+    // of 512-2048 and K of 512-8192: 128x128 blocks (K-sliced when they do
+    // not fill the chip) where they fill it or K is long; 64x64 blocks where
+    // the 128x128 grid would leave compute units idle and K is at most 2048
+    // (1536^3: 16.8 us against 24.4 with 128x128 blocks in two slices); four
+    // stages when even the 64x64 grid or the 128x128 one is small and K is
+    // longer (1024 x 1024 x 4096: 18.0 us against 23.2).
+    const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), t64 = ceil_div(M, 64) * ceil_div(N, 64);
+    const int64_t kt = ceil_div(K, 64);
+    if (t128 >= cus || kt >= 96) return medium;
+    if (kt <= 32) return t64 >= cus ? small : small_deep;
+    return 4 * t128 <= cus ? small_deep : medium;
 }
 
 // Entry for an implicit-GEMM convolution product (the entries built with
@@ -245,7 +256,7 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
     const int64_t target_blocks = 2 * (int64_t)cus, stream_blocks = 6 * (int64_t)cus;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int64_t ktiles = ceil_div(K, c.bk);
-    const bool streaming = c.bm <= 64;
+    const bool streaming = c.bm <= 64 && M <= 64;   // the skinny and wide classes
     const bool b_kcontig = layout == LAYOUT_NT || layout == LAYOUT_TT;
     int64_t s;
     if (forced > 0) {
@@ -255,7 +266,8 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
     } else if (esize == 2 && !streaming && direct_edges) {
         const int64_t lds = (int64_t)c.stages * (c.bm + c.bn) * c.bk * esize;
         const int64_t per_cu = std::max<int64_t>(1, kLdsBytes / lds);
-        s = std::min((int64_t)cus * per_cu / tiles, ktiles / 12);
+        // 64-row blocks serve small outputs with K below 6144: unsplit
+        s = c.bm <= 64 && ktiles < 96 ? 1 : std::min((int64_t)cus * per_cu / tiles, ktiles / 12);
     } else {
         s = ceil_div(streaming && b_kcontig ? stream_blocks : target_blocks, tiles);
         int64_t max_s = ktiles / 4;

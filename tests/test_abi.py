@@ -114,6 +114,22 @@ def test_shape_classes_of_the_workloads():
     for ta in (0, 1):
         assert dg.gemm_config_name(BF16, dg.gemm_select_config_ex(BF16, ta, 0, 8192, 8192, 8192)) \
             == "bf16_256x256x32_w4x2_s4"
+    # bf16 mid-size and small products (256 compute units assumed off the GPU):
+    # 128x128 blocks where they fill the chip or K is long (K-sliced when they
+    # do not fill it), 64x64 blocks otherwise, four stages for small grids
+    # with longer K; the 64-row blocks of M > 64 run unsplit
+    for tb in (0, 1):
+        for (M, N, K), name, splits in [
+                ((1536, 1536, 1536), "bf16_64x64x64_w2x2_s2", 1),
+                ((1024, 1024, 4096), "bf16_64x64x64_w2x2_s4", 1),
+                ((768, 768, 2048), "bf16_64x64x64_w2x2_s4", 1),
+                ((1000, 1000, 1000), "bf16_64x64x64_w2x2_s2", 1),
+                ((1024, 1024, 8192), "bf16_128x128x64_w2x2_s2", 8),
+                ((2000, 1000, 3000), "bf16_128x128x64_w2x2_s2", 3),
+                ((1024, 4096, 1024), "bf16_128x128x64_w2x2_s2", 1)]:
+            c = dg.gemm_select_config_ex(BF16, 0, tb, M, N, K)
+            assert dg.gemm_config_name(BF16, c) == name, (M, N, K, tb)
+            assert dg.gemm_split_k_ex(BF16, c, 0, tb, M, N, K) == splits, (M, N, K, tb)
 
 
 def test_grid_fill_steers_the_large_class():
