@@ -310,14 +310,16 @@ struct Geo {
     static constexpr int LOADS_PER_TILE = (TA::PIECES + TB::PIECES) / NW;
 
     // Direct loads of 4 bytes per lane (256 B per instruction), range-checked
-    // buffer loads: fp32 only (a lane's dword is one whole element), for rows
-    // at any 4-byte alignment and for blocks crossing the M or N edge.  The
-    // entry must split its tiles into whole 256-byte pieces per wave, keep
-    // k-contiguous rows within one 256-byte bank line (so a piece's rows share
-    // one swizzle key), and count its loads in flight within vmcnt's range.
+    // buffer loads, for rows at any 4-byte alignment and for blocks crossing
+    // the M or N edge: a lane's dword is one fp32 element or two consecutive
+    // bf16 elements (the kernel takes this form for bf16 only when every row
+    // starts 4-byte aligned and no pair straddles an edge).  The entry must
+    // split its tiles into whole 256-byte pieces per wave, keep k-contiguous
+    // rows within one 256-byte bank line (so a piece's rows share one swizzle
+    // key), and count its loads in flight within vmcnt's range.
     static constexpr int LOADS4_PER_TILE = (TA::BYTES / 256 + TB::BYTES / 256) / NW;
     static constexpr bool DMA4 =
-        !BF16 && (TA::BYTES / 256) % NW == 0 && (TB::BYTES / 256) % NW == 0 &&
+        (TA::BYTES / 256) % NW == 0 && (TB::BYTES / 256) % NW == 0 &&
         (LA == MNMAJOR || TA::ROW_BYTES <= 256) && (LB == MNMAJOR || TB::ROW_BYTES <= 256) &&
         LOADS4_PER_TILE * (STAGES - 2) <= 63;
 
@@ -653,7 +655,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const typename T::In
 
 // Direct copy of the k-tile at k0 into `stage`.  DW = 16: every address is
 // inside the matrix and 16-byte aligned (interior blocks of aligned
-// operands).  DW = 4 (fp32): range-checked loads; elements of rows or columns
+// operands).  DW = 4: range-checked loads (one fp32 element or two bf16
+// elements per lane); elements of rows or columns
 // past the M or N edge read other in-bounds elements or zero, and only feed
 // outputs that are never stored.
 template <class G, int DW>
@@ -678,7 +681,7 @@ __device__ __forceinline__ void direct_tile_load(unsigned char *stage, const Blo
         for (int i = 0; i < decltype(o.b)::PER_WAVE; ++i)
             direct_load16(b_base, o.b.v[i], lds + G::A_BYTES + PIECE * NW * i);
     } else {
-        static_assert(DW == 4 && G::DMA4, "4-byte direct loads: fp32 entries only");
+        static_assert(DW == 4 && G::DMA4, "4-byte direct loads: entries with whole 256-byte pieces");
         const auto ra = tile_rsrc<TA>(c.A, c.lda, c.a_end, c.bm, k0);
         const auto rb = tile_rsrc<TB>(c.B, c.ldb, c.b_end, c.bn, k0);
 #pragma unroll
@@ -1626,15 +1629,24 @@ gemm_kernel(KernelArgs p)
         // Whole k-tiles go through direct global->LDS loads: 16 bytes per lane
         // for aligned operands, in interior blocks and in blocks crossing the
         // M or N edge when each outer-contiguous operand's outer extent is a
-        // whole number of 16-byte chunks (see tile_offsets); for fp32 entries
-        // also 4 range-checked bytes per lane for the other edge blocks and
-        // for rows at any alignment.  Other cases, and the partial last
-        // k-tile, take the masked loads.
+        // whole number of 16-byte chunks (see tile_offsets); 4 range-checked
+        // bytes per lane for the other edge blocks and for rows at any 4-byte
+        // alignment.  Other cases, and the partial last k-tile, take the
+        // masked loads.
         const bool edge_mn = c.bm + BM > p.M || c.bn + BN > p.N;
         const bool edge16 = (G::LA == KMAJOR || p.M % G::VEC == 0) &&
                             (G::LB == KMAJOR || p.N % G::VEC == 0);
         const bool x4 = ALIGNED && p.direct_ok && (!edge_mn || edge16);
-        const bool dw = G::DMA4 && p.direct_ok && !x4;
+        // bf16 dwords are element pairs (k, k+1) of a k-contiguous row or
+        // (n, n+1) of an outer-contiguous one: rows must start 4-byte aligned,
+        // and an outer-contiguous extent must be even, so that the last pair
+        // of the last row does not reach past the operand (a range check
+        // that cut it would zero a valid element).  Pairs along k stay inside
+        // K: only whole k-tiles, which start at even k, take these loads.
+        const bool pairs_ok =
+            !G::BF16 || (((p.lda | p.ldb) & 1) == 0 && (((uintptr_t)p.A | (uintptr_t)p.B) & 3) == 0 &&
+                         (G::LA == KMAJOR || (p.M & 1) == 0) && (G::LB == KMAJOR || (p.N & 1) == 0));
+        const bool dw = G::DMA4 && p.direct_ok && pairs_ok && !x4;
         const int nfast = x4 || dw ? (c.kend - kbeg) / BK : 0;
         c.rot = (tm + tn) % 8;
         if constexpr (G::DMA4) {

@@ -119,26 +119,6 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_SKINNY_C4W(...)
 #define DG_INST_SKINNY_C4FP(...)
 #define DG_INST_SKINNY_C4WP(...)
-#define DG_INST_BT_NN(...)
-#define DG_INST_BT_NT(...) DG_INST(__VA_ARGS__, NT)
-#define DG_INST_BT_TN(...)
-#define DG_INST_BT_TT(...) DG_INST(__VA_ARGS__, TT)
-#define DG_INST_BT_CF(...)
-#define DG_INST_BT_CW(...)
-#define DG_INST_BT_CFT(...)
-#define DG_INST_BT_CWT(...)
-#define DG_INST_BT_C3F(...)
-#define DG_INST_BT_C3W(...)
-#define DG_INST_BT_CFP(...)
-#define DG_INST_BT_CWP(...)
-#define DG_INST_BT_C3FP(...)
-#define DG_INST_BT_C3WP(...)
-#define DG_INST_BT_CFW(...)
-#define DG_INST_BT_CWW(...)
-#define DG_INST_BT_C4F(...)
-#define DG_INST_BT_C4W(...)
-#define DG_INST_BT_C4FP(...)
-#define DG_INST_BT_C4WP(...)
 #define DG_INST_KK_NN(...)
 #define DG_INST_KK_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_KK_TN(...)

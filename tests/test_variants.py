@@ -235,6 +235,35 @@ def test_staged_epilogue_every_config(bf16):
                 check_exact_ex(raw, A, B, ta, tb, alpha, beta, c0, out_bf16, what)
 
 
+def test_bf16_rows_4byte_aligned_every_config():
+    """bf16 rows that start 4-byte but not 16-byte aligned, and edge blocks
+    whose outer extents are even but not whole 16-byte chunks, stream their
+    whole k-tiles through 4-byte range-checked direct loads of element pairs.
+    Every entry and operand form on integer operands, bit for bit: all
+    extents even (166, 202, 262, 514, 1030 elements), and an odd outer extent
+    (301 x 203), where a pair of the outer-contiguous operand would straddle
+    the edge and the element-wise loads take over.  Then the dispatcher's
+    choice at 1502 x 1498 x 1500 (rows of 3000 bytes) with the whole C
+    compared."""
+    for cfg in range(dg.gemm_num_configs(BF16)):
+        name = dg.gemm_config_name(BF16, cfg)
+        mask = dg.gemm_config_layouts(BF16, cfg)
+        for ta, tb in TRANS:
+            if not mask & (1 << (2 * ta + tb)):
+                continue
+            for t, (M, N, K) in enumerate([(300, 202, 166), (262, 514, 1030), (301, 203, 166)]):
+                A, B = _operands(M, N, K, ta, tb, _ints, 50 + t, True)
+                what = "%s %s %dx%dx%d" % (name, TNAME[ta, tb], M, N, K)
+                log(what)
+                _, raw = run_ex(A, B, ta, tb, cfg=cfg)
+                check_exact_ex(raw, A, B, ta, tb, 1.0, 0.0, None, False, what)
+    for ta, tb in TRANS:
+        A, B = _operands(1502, 1498, 1500, ta, tb, _ints, 60, True)
+        _, raw = run_ex(A, B, ta, tb)
+        check_exact_ex(raw, A, B, ta, tb, 1.0, 0.0, None, False,
+                       "dispatched %s 1502x1498x1500" % TNAME[ta, tb])
+
+
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_random_within_tolerance(bf16):
     rng_c = np.random.default_rng(8)
