@@ -1498,7 +1498,13 @@ struct StagedOut {
     static constexpr int PER_STAGE = G::STAGE_BYTES / BYTES;     // scratches per stage array
     static constexpr int CPR = G::WTN / 4;                       // 16-byte pieces per row
     static constexpr int PER_LANE = 32 * CPR / 64;               // pieces per lane and row block
-    static constexpr bool OK = G::WTN % 64 == 0 && PER_STAGE * G::STAGES >= G::NW;
+    // Blocks of at most 64 rows (the skinny, wide and small classes, and most
+    // convolution products) keep the element-wise epilogue: their outputs are
+    // split-K partials or plain products almost always, and the staged code
+    // alone, never executed, measured 3% slower on the 64 x 256 entry's
+    // streaming product (64 x 16384 x 61504 in 8 K slices).
+    static constexpr bool OK =
+        G::BM > 64 && G::WTN % 64 == 0 && PER_STAGE * G::STAGES >= G::NW;
 };
 
 template <class G>
@@ -1535,42 +1541,50 @@ __device__ __forceinline__ void staged_epilogue(unsigned char *l0, unsigned char
             }
         // A wave's LDS accesses complete in order: the reads below see the
         // writes above, and the next row block's writes follow these reads.
+        // Pieces go in groups of four (16 registers of old C per group), so
+        // the epilogue does not raise the kernel's register count past what
+        // its main loop needs.
         const int64_t row0 = c.bm + c.wrow * G::WTM + fm * 32;
         const int col0 = c.bn + c.wcol * G::WTN;
-        u32x4 old[S::PER_LANE];
-        if (read_c) {
+        constexpr int GRP = S::PER_LANE < 4 ? S::PER_LANE : 4;
 #pragma unroll
-            for (int u = 0; u < S::PER_LANE; ++u) {
-                const int ch = c.lane + 64 * u, rr = ch / S::CPR, cc = ch % S::CPR;
-                const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
-                if (out_bf16) {
-                    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.C) + idx);
-                    old[u] = u32x4{w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u};
-                } else {
-                    old[u] = load16(static_cast<const float *>(p.C) + idx);
+        for (int u0 = 0; u0 < S::PER_LANE; u0 += GRP) {
+            u32x4 old[GRP];
+            if (read_c) {
+#pragma unroll
+                for (int g = 0; g < GRP; ++g) {
+                    const int ch = c.lane + 64 * (u0 + g), rr = ch / S::CPR, cc = ch % S::CPR;
+                    const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
+                    if (out_bf16) {
+                        const uint2 w =
+                            *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.C) + idx);
+                        old[g] = u32x4{w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u};
+                    } else {
+                        old[g] = load16(static_cast<const float *>(p.C) + idx);
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int u = 0; u < S::PER_LANE; ++u) {
-            const int ch = c.lane + 64 * u, rr = ch / S::CPR, cc = ch % S::CPR;
-            const u32x4 raw = lds_load16(scr, 4 * (rr * G::WTN + staged_col<G>(rr, 4 * cc)));
-            float v[4];
+            for (int g = 0; g < GRP; ++g) {
+                const int ch = c.lane + 64 * (u0 + g), rr = ch / S::CPR, cc = ch % S::CPR;
+                const u32x4 raw = lds_load16(scr, 4 * (rr * G::WTN + staged_col<G>(rr, 4 * cc)));
+                float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = alpha * __uint_as_float(raw[e]);
-                if (read_c) v[e] += beta * __uint_as_float(old[u][e]);
-            }
-            const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
-            if (out_bf16) {
-                uint2 w;
-                w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-                w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.C) + idx) = w;
-            } else {
-                *reinterpret_cast<u32x4 *>(static_cast<float *>(p.C) + idx) =
-                    u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                          __float_as_uint(v[3])};
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = alpha * __uint_as_float(raw[e]);
+                    if (read_c) v[e] += beta * __uint_as_float(old[g][e]);
+                }
+                const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
+                if (out_bf16) {
+                    uint2 w;
+                    w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+                    w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.C) + idx) = w;
+                } else {
+                    *reinterpret_cast<u32x4 *>(static_cast<float *>(p.C) + idx) =
+                        u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])};
+                }
             }
         }
     });

@@ -210,7 +210,8 @@ def test_exact_alpha_beta(bf16, out_bf16):
 def test_staged_epilogue_every_config(bf16):
     """Interior blocks whose output is not the plain fp32 product (alpha != 1,
     beta != 0 or bf16 C) and whose C rows are aligned finish C through LDS in
-    16-byte row pieces (entries whose waves own at least 64 columns).  Every
+    16-byte row pieces (entries of more than 64 rows whose waves own at
+    least 64 columns; the others take the element-wise epilogue here).  Every
     entry and operand form with C at an aligned leading dimension (N + 4),
     integer operands, bit for bit against the oracle: alpha/beta with C read,
     bf16 C, and beta == 0 over a NaN-filled C (never read).  The blocks at the
