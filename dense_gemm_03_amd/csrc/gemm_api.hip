@@ -251,14 +251,14 @@ bool direct_edges(int layout, int64_t M, int64_t N, int esize)
 // aim at six blocks per compute unit even when the output alone fills the
 // chip, since each block then sustains less bandwidth.  Every slice keeps at
 // least four k-tiles.  bf16 blocks of more than 64 rows whose blocks at the M
-// and N edges also take the direct loads (direct_edges) split only as far as
+// and N edges also take the direct loads (edges_direct) split only as far as
 // one round of resident blocks and twelve k-tiles per slice allow: on 128 x
 // 128 blocks at M, N of 1024-2048 (K 512-8192) a split that adds a round of
 // blocks, or leaves shorter slices, costs more in partial sums and pipeline
 // fill than it gains (1536^3: 30.3 us with the four slices of the two-blocks-
 // per-CU target, 21.3 us unsplit).  forced > 0 overrides the target.
 void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K, int forced,
-                int cus, int esize, bool direct_edges, int *splits, int *k_per_split)
+                int cus, int esize, bool edges_direct, int *splits, int *k_per_split)
 {
     const int64_t target_blocks = 2 * (int64_t)cus, stream_blocks = 6 * (int64_t)cus;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
@@ -270,7 +270,7 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
         s = forced;
     } else if (tiles >= cus && !(streaming && b_kcontig)) {
         s = 1;
-    } else if (esize == 2 && !streaming && direct_edges) {
+    } else if (esize == 2 && !streaming && edges_direct) {
         const int64_t lds = (int64_t)c.stages * (c.bm + c.bn) * c.bk * esize;
         const int64_t per_cu = std::max<int64_t>(1, kLdsBytes / lds);
         // 64-row blocks serve small outputs with K below 6144: unsplit

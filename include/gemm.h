@@ -77,7 +77,8 @@
  *
  * Dispatch: the tile choice and split-K plan depend on the shape, the operand
  * form and the compute-unit count of the current device (queried once per
- * device; 256, MI355X's count, when no device is visible).
+ * device; 256, MI355X's count, when no device is visible); the bf16 split-K
+ * plan also on whether the operand rows are 16-byte aligned.
  */
 #ifndef DENSE_GEMM_03_AMD_GEMM_H
 #define DENSE_GEMM_03_AMD_GEMM_H
@@ -219,8 +220,8 @@ int gemm_release_buffers(hipStream_t stream);
  * gemm_config_name: a static string naming an entry ("f32_128x128x32_w2x2"...),
  *   NULL when out of range.
  * gemm_split_k: the number of K slices the dispatcher would use with entry cfg
- *   for this shape of the plain product (1 = no split); negative on bad
- *   arguments.  gemm_split_k_ex: the same for the operand form (transa,
+ *   for this shape of the plain product with 16-byte aligned rows (1 = no
+ *   split); negative on bad arguments.  gemm_split_k_ex: the same for the operand form (transa,
  *   transb).
  * gemm_config_layouts: bit (transa * 2 + transb) is set when entry cfg has
  *   kernels for that operand form (the entry the dispatcher chooses for an
