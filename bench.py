@@ -19,7 +19,10 @@ in HBM.  Prints ONE JSON line (last line of stdout):
   sclk_sustained          the graphics clock and board power the GPU holds over
                           2.5 s of the headline workload run back to back after
                           the timed steps (amdsmi GPU metrics, when readable;
-                          also for bf16 8192^3 in 'also')
+                          likewise for every configuration in 'also', as
+                          sclk_sustained_mhz and socket_power_w -- for the
+                          shortest calls the host's launch rate, not the GPU,
+                          can bound that back-to-back run)
   cpu_baseline            the oracle (CPU, fp64) timed on a bounded sample of the
                           same workload on this host
   also                    the same measurement, in short form, for the other
@@ -547,7 +550,7 @@ def main() -> int:
     # the clock each headline workload sustains (outside the timed steps)
     clocks = {}
     if not args.no_also:
-        for n, r in [(args.workload, main_res)] + [(n, also[n]) for n in also if n in ("bf16-8192",)]:
+        for n, r in [(args.workload, main_res)] + [(n, also[n]) for n in also]:
             clocks[n] = sustained_clock(r["step"])
             log("[bench] %s sustained clock: %s MHz" % (n, clocks[n].get("mhz")))
     del ctxs
