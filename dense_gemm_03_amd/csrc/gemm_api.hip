@@ -174,12 +174,13 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
         {"bf16_256x256x32_w4x2_s4", 1, 0.52},
         {"bf16_128x128x64_w2x2_s2", 2, 0.42},
     };
-    // A . B^T (both operands k-contiguous): with 32-deep k-tiles their
-    // 64-byte row pieces keep the data-return path busy (97% at 8192^3);
-    // 64-deep k-tiles in two stages read whole 128-byte lines (measured +5%
-    // at 4096^3 and 8192^3, +1% at K = 2048).  A^T . B^T gained 2%, not
-    // enough for a kernel of its own (its element-wise variant spills).
-    static const Candidate large_bt[] = {
+    // A read k-contiguous (A . B, A . B^T): 64-deep k-tiles in two stages
+    // read whole 128-byte lines of A (and of B^T, whose 64-byte pieces kept
+    // the data-return path 97% busy at 8192^3 A . B^T); measured against the
+    // 32-deep four-stage block: A . B^T +5% at 4096^3 and 8192^3, A . B
+    // +1.9% at 8192^3 and +1.2% at 4096^3 (alternating, two boxes).  A^T . B
+    // lost 2% with it, and A^T . B^T's element-wise variant spilled.
+    static const Candidate large_ak[] = {
         {"bf16_256x256x64_w4x2_s2", 1, 0.55},
         {"bf16_128x128x64_w2x2_s2", 2, 0.42},
     };
@@ -197,8 +198,8 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     if (skinny && layout == LAYOUT_NT) return skinny_t;
     if (M <= 64 && N >= 1024) return layout == LAYOUT_NT ? wide_t : wide;  // split-K
     if (M >= 2048 && N >= 2048)
-        return layout == LAYOUT_NT ? best_of(dtype, large_bt, 2, M, N, cus)
-                                   : best_of(dtype, large, 2, M, N, cus);
+        return layout == LAYOUT_NN || layout == LAYOUT_NT ? best_of(dtype, large_ak, 2, M, N, cus)
+                                                          : best_of(dtype, large, 2, M, N, cus);
     // Mid-size and small products, from a sweep of A . B and A . B^T at M, N
     // of 512-2048 and K of 512-8192: 128x128 blocks (K-sliced when they do
     // not fill the chip) where they fill it or K is long; 64x64 blocks where

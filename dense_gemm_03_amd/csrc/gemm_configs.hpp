@@ -9,8 +9,9 @@
 // waves), the number of LDS stages, the raster group height, and LAYOUTS =
 // ALL (kernels for all four combinations of transposed operands), CONV (ALL,
 // plus implicit-GEMM convolution kernels), NN (only A and B as given),
-// SKINNY (A . B and A . B^T), SKINNYC (SKINNY plus implicit-GEMM kernels) or
-// KK (only A . B^T).  The kernels of one input type and operand layout are
+// SKINNY (A . B and A . B^T), SKINNYC (SKINNY plus implicit-GEMM kernels),
+// KK (only A . B^T) or AK (A . B and A . B^T: the forms that read A
+// k-contiguous, for large blocks).  The kernels of one input type and operand layout are
 // instantiated by one compilation of gemm_instances.hip, so the slices compile
 // in parallel; the tables (gemm_tables.hip) only take their addresses.
 #pragma once
@@ -125,9 +126,9 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 // blocks with split-K, including A . B^T blocks with long k-contiguous rows;
 // a tall block for N of a few dozen columns; and a small block when the
 // output holds too few large blocks to fill 256 compute units; large bf16
-// blocks with 64-deep k-tiles for A . B^T (both operands k-contiguous).
+// blocks with 64-deep k-tiles for the forms that read A k-contiguous.
 // Entries the dispatcher picks for only some operand forms (SKINNY, SKINNYC,
-// KK) are built only for those forms; the others for all four.
+// KK, AK) are built only for those forms; the others for all four.
 #define DG_F32_TABLE(X)                                                     \
     X("f32_256x128_w4x2_s2", false, 256, 128, 32, 4, 2, 2, 8, CONV)         \
     X("f32_128x128_w2x2_s2", false, 128, 128, 32, 2, 2, 2, 8, CONV)         \
@@ -170,7 +171,7 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("bf16_64x128x128_w1x4_s2", true, 64, 128, 128, 1, 4, 2, 1, KK)       \
     X("bf16_64x64x256_w2x2_s2", true, 64, 64, 256, 2, 2, 2, 1, KK)         \
     X("bf16_64x64x64_w2x2_s4", true, 64, 64, 64, 2, 2, 4, 1, ALL)          \
-    X("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8, KK)
+    X("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8, AK)
 
 // Launcher pointers of one entry and layout: both alignments, or nullptr.
 #define DG_FNS(BF16, BM, BN, BK, WM, WN, S, L)                                               \
@@ -200,6 +201,10 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_FNS_KK_NT(...) DG_FNS(__VA_ARGS__, NT)
 #define DG_FNS_KK_TN(...) DG_NOFNS
 #define DG_FNS_KK_TT(...) DG_NOFNS
+#define DG_FNS_AK_NN(...) DG_FNS(__VA_ARGS__, NN)
+#define DG_FNS_AK_NT(...) DG_FNS(__VA_ARGS__, NT)
+#define DG_FNS_AK_TN(...) DG_NOFNS
+#define DG_FNS_AK_TT(...) DG_NOFNS
 #define DG_FNS_NN_NN(...) DG_FNS(__VA_ARGS__, NN)
 #define DG_FNS_NN_NT(...) DG_NOFNS
 #define DG_FNS_NN_TN(...) DG_NOFNS
@@ -222,6 +227,7 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
 #define DG_IMPL_SKINNY(...) DG_IMPL_NONE
 #define DG_IMPL_SKINNYC(...) DG_IMPL_CONV(__VA_ARGS__)
 #define DG_IMPL_KK(...) DG_IMPL_NONE
+#define DG_IMPL_AK(...) DG_IMPL_NONE
 
 // One table entry from one list item.
 #define DG_TABLE_ENTRY(NAME, BF16, BM, BN, BK, WM, WN, S, G, LAYOUTS)                        \

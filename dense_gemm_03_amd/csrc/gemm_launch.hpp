@@ -119,6 +119,26 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream)
 #define DG_INST_SKINNY_C4W(...)
 #define DG_INST_SKINNY_C4FP(...)
 #define DG_INST_SKINNY_C4WP(...)
+#define DG_INST_AK_NN(...) DG_INST(__VA_ARGS__, NN)
+#define DG_INST_AK_NT(...) DG_INST(__VA_ARGS__, NT)
+#define DG_INST_AK_TN(...)
+#define DG_INST_AK_TT(...)
+#define DG_INST_AK_CF(...)
+#define DG_INST_AK_CW(...)
+#define DG_INST_AK_CFT(...)
+#define DG_INST_AK_CWT(...)
+#define DG_INST_AK_C3F(...)
+#define DG_INST_AK_C3W(...)
+#define DG_INST_AK_CFP(...)
+#define DG_INST_AK_CWP(...)
+#define DG_INST_AK_C3FP(...)
+#define DG_INST_AK_C3WP(...)
+#define DG_INST_AK_CFW(...)
+#define DG_INST_AK_CWW(...)
+#define DG_INST_AK_C4F(...)
+#define DG_INST_AK_C4W(...)
+#define DG_INST_AK_C4FP(...)
+#define DG_INST_AK_C4WP(...)
 #define DG_INST_KK_NN(...)
 #define DG_INST_KK_NT(...) DG_INST(__VA_ARGS__, NT)
 #define DG_INST_KK_TN(...)

@@ -79,7 +79,7 @@ def test_shape_classes_of_the_workloads():
     assert _cfg_for("fp32-4096")[2] == "f32_256x256_w4x2_s2"
     # 4097 x 4095: 256 blocks of 256 x 256 once the one-row remainder runs apart
     assert _cfg_for("fp32-rag")[2] == "f32_256x256_w4x2_s2"
-    assert _cfg_for("bf16-8192")[2] == "bf16_256x256x32_w4x2_s4"
+    assert _cfg_for("bf16-8192")[2] == "bf16_256x256x64_w4x2_s2"
     assert _cfg_for("tall")[2] == "f32_128x64_w2x2_s2"
     dtype, c, name, splits = _cfg_for("im2col")
     assert name == "f32_64x256_w1x4_s2" and splits == 8
@@ -105,12 +105,13 @@ def test_shape_classes_of_the_workloads():
     assert dg.gemm_split_k_ex(F32, c, 0, 2, 64, 61504, 16384) == dg.GEMM_ERR_INVALID_ARG
     for big in ("fp32-4096", "bf16-8192", "tall"):
         assert _cfg_for(big)[3] == 1
-    # large bf16 A . B^T (both operands k-contiguous): 64-deep k-tiles
-    for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096)]:
-        c = dg.gemm_select_config_ex(BF16, 0, 1, M, N, K)
-        assert dg.gemm_config_name(BF16, c) == "bf16_256x256x64_w4x2_s2"
-        assert dg.gemm_config_layouts(BF16, c) == 1 << 1   # A . B^T only
-    for ta, tb in [(0, 0), (1, 0), (1, 1)]:
+    # large bf16 with A k-contiguous (A . B, A . B^T): 64-deep k-tiles
+    for tb in (0, 1):
+        for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096)]:
+            c = dg.gemm_select_config_ex(BF16, 0, tb, M, N, K)
+            assert dg.gemm_config_name(BF16, c) == "bf16_256x256x64_w4x2_s2"
+            assert dg.gemm_config_layouts(BF16, c) == (1 << 0) | (1 << 1)   # A . B and A . B^T
+    for ta, tb in [(1, 0), (1, 1)]:
         assert dg.gemm_config_name(BF16, dg.gemm_select_config_ex(BF16, ta, tb, 8192, 8192, 8192)) \
             == "bf16_256x256x32_w4x2_s4"
     # bf16 mid-size and small products (256 compute units assumed off the GPU):

@@ -93,25 +93,27 @@ def _config(dtype, name):
     raise KeyError(name)
 
 
-def test_rotated_k_order_interior_blocks_exact():
+@pytest.mark.parametrize("name,bk", [("bf16_256x256x32_w4x2_s4", 32), ("bf16_256x256x64_w4x2_s2", 64)])
+def test_rotated_k_order_interior_blocks_exact(name, bk):
     """The bf16 256x256 blocks walk their k-tiles from a start tile that depends
     on the block's position once a block holds at least 32 interior k-tiles.
-    512 x 512 x 2048 (64 k-tiles of 32) puts four interior blocks, with
-    different start tiles, on that path; integer operands make the whole C
-    exact."""
-    cfg = _config(BF16, "bf16_256x256x32_w4x2_s4")
-    for (M, N, K, seed) in [(512, 512, 2048, 1), (768, 1024, 1056, 2)]:
+    512 x 512 x 64 BK (64 k-tiles) puts four interior blocks, with different
+    start tiles, on that path, and 768 x 1024 x 33 BK exactly 33; integer
+    operands make the whole C exact."""
+    cfg = _config(BF16, name)
+    for (M, N, K, seed) in [(512, 512, 64 * bk, 1), (768, 1024, 33 * bk, 2)]:
         A, B = _ints((M, K), 40 + seed, True), _ints((K, N), 50 + seed, True)
-        log("bf16_256x256x32_w4x2_s4 %dx%dx%d (%d k-tiles per block)" % (M, N, K, K // 32))
+        log("%s %dx%dx%d (%d k-tiles per block)" % (name, M, N, K, K // bk))
         C = run(A, B, cfg=cfg).cpu().numpy()
-        _exact_whole(C, A, B, "rotated %dx%dx%d" % (M, N, K))
+        _exact_whole(C, A, B, "%s rotated %dx%dx%d" % (name, M, N, K))
     # random values within the tolerance on the same path
-    A, B = wl.normal_bf16_bits((1024, 2048), 3), wl.normal_bf16_bits((2048, 1024), 4)
+    K = 64 * bk
+    A, B = wl.normal_bf16_bits((1024, K), 3), wl.normal_bf16_bits((K, 1024), 4)
     C = run(A, B, cfg=cfg).cpu().numpy()
     C_ref, S = _oracle(A, B)
     ratio, zeros_ok = oracle.max_error_ratio(C, C_ref, S)
-    report("whole C, random operands, rotated k-order 1024x1024x2048: max over all entries of "
-           "|C-C_ref|/S = %.3e" % ratio)
+    report("whole C, random operands, %s rotated k-order 1024x1024x%d: max over all entries of "
+           "|C-C_ref|/S = %.3e" % (name, K, ratio))
     assert zeros_ok and ratio <= TOL["bf16"]
 
 
@@ -151,7 +153,7 @@ def test_thin_remainders_run_apart_exact(case):
     bf16 = dt == "bf16"
     dtype = BF16 if bf16 else F32
     cfg = dg.gemm_select_config_ex(dtype, int(ta), int(tb), M, N, K)
-    assert dg.gemm_config_name(dtype, cfg).endswith(("256x256_w4x2_s2", "256x256x32_w4x2_s4"))
+    assert dg.gemm_config_name(dtype, cfg).endswith(("256x256_w4x2_s2", "256x256x32_w4x2_s4", "256x256x64_w4x2_s2"))
     A = _ints((K, M) if ta else (M, K), 80 + M % 5, bf16)
     B = _ints((N, K) if tb else (K, N), 90 + N % 5, bf16)
     C0 = np.random.default_rng(K).integers(-9, 10, size=(M, N)).astype(np.float32)
