@@ -403,12 +403,33 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p)
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
 
 // Masked 16-byte chunk: elements [e0, e0+VEC) of one row, zero where the row
-// is outside the matrix (row_ok false) or e0+e >= eend.  Never dereferences
-// an address outside the matrix.
+// is outside the matrix (row_ok false) or e0+e >= eend.  Element loads never
+// touch an address outside the matrix.  A whole bf16 chunk of an unaligned
+// row (2-byte aligned, as rows at an odd leading dimension are every other
+// row) comes from the five 4-byte-aligned dwords that cover it, shifted
+// into place: each of them holds at least one element of the chunk, so it
+// lies on a page the matrix occupies, and its bytes outside the chunk are
+// discarded.
 template <typename In, int VEC, bool ALIGNED>
 __device__ __forceinline__ u32x4 load_chunk_masked(const In *row, bool row_ok, int e0, int eend)
 {
     if (ALIGNED && row_ok && e0 + VEC <= eend) return load16(row + e0);
+    if constexpr (!ALIGNED && sizeof(In) == 2) {
+        if (row_ok && e0 + VEC <= eend) {
+            const unsigned char *s = reinterpret_cast<const unsigned char *>(row + e0);
+            const uint32_t mis = (uint32_t)reinterpret_cast<uintptr_t>(s) & 2;
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(s - mis);
+            const uint32_t sh = mis * 8;                 // 0 or 16 bits
+            const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+            const uint32_t w4 = q[sh ? 4 : 3];           // past the chunk only when shifted
+            u32x4 v;
+            v[0] = __builtin_amdgcn_alignbit(w1, w0, sh);
+            v[1] = __builtin_amdgcn_alignbit(w2, w1, sh);
+            v[2] = __builtin_amdgcn_alignbit(w3, w2, sh);
+            v[3] = __builtin_amdgcn_alignbit(w4, w3, sh);
+            return v;
+        }
+    }
     union {
         u32x4 v;
         In e[VEC];
