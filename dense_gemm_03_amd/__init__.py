@@ -56,6 +56,7 @@ SIGNATURES = {
     "gemm_ex_noalloc": (_int, _GEMM_EX_ARGS),
     "gemm_config_layouts": (_int, [_int, _int]),
     "gemm_release_buffers": (_int, [_p]),
+    "gemm_operand_copy_bytes": (_i64, [_int, _int, _int, _i64, _i64, _i64, _p, _i64, _p, _i64]),
 }
 
 
@@ -211,6 +212,11 @@ def gemm_split_k(dtype: int, cfg: int, M: int, N: int, K: int) -> int:
 
 def gemm_split_k_ex(dtype: int, cfg: int, transa: int, transb: int, M: int, N: int, K: int) -> int:
     return load_library().gemm_split_k_ex(dtype, cfg, transa, transb, M, N, K)
+
+
+def gemm_operand_copy_bytes(dtype_ab, transa, transb, M, N, K, A, lda, B, ldb) -> int:
+    return load_library().gemm_operand_copy_bytes(dtype_ab, transa, transb, M, N, K, A, lda, B,
+                                                  ldb)
 
 
 # ----------------------------------------------------------- torch helper --

@@ -232,18 +232,6 @@ int select_implicit(int dtype, int64_t M)
     return M <= 32 ? skinny : M <= 64 ? wide : M <= 128 ? mid : large;
 }
 
-// Whether the blocks of a plain product at the M and N edges take the 16-byte
-// direct loads (the kernel's condition, assuming aligned rows): each operand
-// read outer-contiguous (A^T, or B as given) must have an outer extent that is
-// a whole number of 16-byte chunks.
-bool direct_edges(int layout, int64_t M, int64_t N, int esize)
-{
-    const int vec = 16 / esize;
-    const bool a_outer = layout == LAYOUT_TN || layout == LAYOUT_TT;
-    const bool b_outer = layout == LAYOUT_NN || layout == LAYOUT_TN;
-    return (!a_outer || M % vec == 0) && (!b_outer || N % vec == 0);
-}
-
 // Number of K slices.  Large blocks: 1 when the output alone yields enough
 // blocks to fill the chip; otherwise enough slices for about two blocks per
 // compute unit.  Blocks of at most 64 rows (the skinny and wide classes) carry
@@ -252,7 +240,9 @@ bool direct_edges(int layout, int64_t M, int64_t N, int esize)
 // aim at six blocks per compute unit even when the output alone fills the
 // chip, since each block then sustains less bandwidth.  Every slice keeps at
 // least four k-tiles.  bf16 blocks of more than 64 rows whose blocks at the M
-// and N edges also take the direct loads (edges_direct) split only as far as
+// and N edges also take the direct loads (edges_direct: both operands have
+// 16-byte-aligned rows, whose loads may run to the next 16 bytes past M or N
+// when those lie along the rows) split only as far as
 // one round of resident blocks and twelve k-tiles per slice allow: on 128 x
 // 128 blocks at M, N of 1024-2048 (K 512-8192) a split that adds a round of
 // blocks, or leaves shorter slices, costs more in partial sums and pipeline
@@ -294,7 +284,7 @@ void plan_split(const TileConfig &c, int layout, int64_t M, int64_t N, int64_t K
 // slot 1 the convolution tables of the implicit GEMM, slot 2 its zero-padded
 // image, slot 3 its filters with padded rows (or, for the filter gradient,
 // the output gradient with padded rows), slot 4 that filter gradient with
-// padded rows.  A buffer only grows, by at least half its size each time.
+// padded rows, slot 5 row-aligned copies of bf16 GEMM operands.  A buffer only grows, by at least half its size each time.
 // The buffer it replaces is retired, not freed: a HIP graph captured earlier
 // on that stream still holds its address, so it stays valid until the
 // stream's buffers are released (gemm_release_buffers) or the library is
@@ -390,9 +380,9 @@ bool valid_dtype(int dtype) { return dtype == GEMM_DTYPE_F32 || dtype == GEMM_DT
 
 using Call = GemmCall;
 
-int check_args(const Call &c)
+int check_args(const Call &c, bool with_c = true)
 {
-    if (!valid_dtype(c.dtype) || !valid_dtype(c.dtype_c)) return GEMM_ERR_INVALID_ARG;
+    if (!valid_dtype(c.dtype) || (with_c && !valid_dtype(c.dtype_c))) return GEMM_ERR_INVALID_ARG;
     if ((c.transa != GEMM_OP_N && c.transa != GEMM_OP_T) ||
         (c.transb != GEMM_OP_N && c.transb != GEMM_OP_T))
         return GEMM_ERR_INVALID_ARG;
@@ -409,14 +399,14 @@ int check_args(const Call &c)
                      (conv_table_source(c.bsrc) && c.conv->tab == nullptr)))
         return GEMM_ERR_INVALID_ARG;
     if (c.lda < (a_row > 0 ? a_row : 1) || (!implicit && c.ldb < (b_row > 0 ? b_row : 1)) ||
-        c.ldc < (c.N > 0 ? c.N : 1))
+        (with_c && c.ldc < (c.N > 0 ? c.N : 1)))
         return GEMM_ERR_INVALID_ARG;
-    if (c.M > 0 && c.N > 0 && c.C == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (with_c && c.M > 0 && c.N > 0 && c.C == nullptr) return GEMM_ERR_INVALID_ARG;
     if (c.M > 0 && c.N > 0 && c.K > 0 && (c.A == nullptr || c.B == nullptr))
         return GEMM_ERR_INVALID_ARG;
     const uintptr_t esz = (uintptr_t)elem_size(c.dtype);
     if ((uintptr_t)c.A % esz || (uintptr_t)c.B % esz ||
-        (uintptr_t)c.C % (uintptr_t)elem_size(c.dtype_c))
+        (with_c && (uintptr_t)c.C % (uintptr_t)elem_size(c.dtype_c)))
         return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
 }
@@ -449,6 +439,99 @@ int scratch_address(int device, void **out)
     }
     *out = g_scratch_ptr[device];
     return GEMM_OK;
+}
+
+// bf16 operands whose rows are not all 4-byte aligned (an odd leading
+// dimension, a 2-byte-aligned address, or pairs along an odd outer extent)
+// take neither direct load in the kernels: every k-tile goes through
+// registers, at a third to a half of the aligned rate.  When the product has
+// enough work per byte of the operands whose rows are not 16-byte aligned,
+// those are first copied into a library buffer with 16-byte-aligned rows
+// (one pass over each at HBM speed) and the product runs on the copies.
+// Copying costs an operand's bytes twice in HBM traffic plus a launch, and
+// saves time in proportion to the K loop's share of the call; operands read
+// outer-contiguous (B, A^T) lose more in place than k-contiguous ones.
+// Measured on MI355X against the in-place call: copying a k-contiguous
+// operand won from about 190 flops per copied byte (8191 x 192 x 8191, A
+// copied: 140 -> 107 us) and lost 9-16% at 128; copying an outer-contiguous
+// one won already at 64 (64 x 8191 x 8191, B copied: 115 -> 89 us); with K
+// of 255 or less, where writing C dominates, copying lost up to 7%.  So the
+// product must do 160 flops per copied byte of a k-contiguous operand plus
+// 56 per copied byte of an outer-contiguous one.  Returns whether it
+// enqueued copies (then *out is the call on them); a buffer that cannot grow
+// (stream capture, out of memory) leaves the call in place.
+constexpr double kStageFlopsPerByteK = 160.0;
+constexpr double kStageFlopsPerByteOuter = 56.0;
+constexpr double kStageMinFlops = double(1 << 26);
+constexpr int64_t kStageMinK = 256;
+constexpr int64_t kStageAlign = 256;
+
+// Which operands to copy and where: A at the buffer's start, B after it.
+struct StagePlan {
+    bool a = false, b = false;                 // copy A / B
+    bool a_outer = false, b_outer = false;     // stored with M (A^T) / N (B) along rows
+    int64_t a_rows = 0, a_cols = 0, a_ld = 0, a_bytes = 0;
+    int64_t b_rows = 0, b_cols = 0, b_ld = 0, b_bytes = 0;
+};
+
+bool plan_stage(const Call &call, int layout, StagePlan *sp)
+{
+    if (call.dtype != GEMM_DTYPE_BF16 || call.bsrc != B_MATRIX) return false;
+    sp->a_outer = layout == LAYOUT_TN || layout == LAYOUT_TT;
+    sp->b_outer = layout == LAYOUT_NN || layout == LAYOUT_TN;
+    const bool pairs = ((call.lda | call.ldb) & 1) == 0 &&
+                       (((uintptr_t)call.A | (uintptr_t)call.B) & 3) == 0 &&
+                       (!sp->a_outer || (call.M & 1) == 0) && (!sp->b_outer || (call.N & 1) == 0);
+    const bool a16 = call.lda % 8 == 0 && (uintptr_t)call.A % 16 == 0;
+    const bool b16 = call.ldb % 8 == 0 && (uintptr_t)call.B % 16 == 0;
+    if (pairs || (a16 && b16)) return false;
+    sp->a = !a16;
+    sp->b = !b16;
+    // stored shapes: A is M x K (K x M transposed), B is K x N (N x K)
+    sp->a_rows = call.transa == GEMM_OP_T ? call.K : call.M;
+    sp->a_cols = call.transa == GEMM_OP_T ? call.M : call.K;
+    sp->b_rows = call.transb == GEMM_OP_T ? call.N : call.K;
+    sp->b_cols = call.transb == GEMM_OP_T ? call.K : call.N;
+    sp->a_ld = (sp->a_cols + 7) / 8 * 8;
+    sp->b_ld = (sp->b_cols + 7) / 8 * 8;
+    sp->a_bytes = sp->a ? (sp->a_rows * sp->a_ld * 2 + kStageAlign - 1) / kStageAlign * kStageAlign : 0;
+    sp->b_bytes = sp->b ? sp->b_rows * sp->b_ld * 2 : 0;
+    const double flops = 2.0 * (double)call.M * (double)call.N * (double)call.K;
+    const double need = (sp->a_outer ? kStageFlopsPerByteOuter : kStageFlopsPerByteK) * sp->a_bytes +
+                        (sp->b_outer ? kStageFlopsPerByteOuter : kStageFlopsPerByteK) * sp->b_bytes;
+    return call.K >= kStageMinK && flops >= kStageMinFlops && flops >= need;
+}
+
+bool stage_operands(const Call &call, int layout, int device, hipStream_t stream, Call *out,
+                    int *rc)
+{
+    *rc = GEMM_OK;
+    StagePlan sp;
+    if (!plan_stage(call, layout, &sp)) return false;
+    void *buf = nullptr;
+    if (get_buffer(5, device, stream, (size_t)(sp.a_bytes + sp.b_bytes), &buf) != GEMM_OK)
+        return false;
+    *out = call;
+    if (sp.a) {
+        if (launch_stage_rows(call.A, call.lda, sp.a_rows, sp.a_cols, 2, buf, sp.a_ld, stream) !=
+            hipSuccess) {
+            *rc = GEMM_ERR_HIP;
+            return true;
+        }
+        out->A = buf;
+        out->lda = sp.a_ld;
+    }
+    if (sp.b) {
+        void *bb = static_cast<char *>(buf) + sp.a_bytes;
+        if (launch_stage_rows(call.B, call.ldb, sp.b_rows, sp.b_cols, 2, bb, sp.b_ld, stream) !=
+            hipSuccess) {
+            *rc = GEMM_ERR_HIP;
+            return true;
+        }
+        out->B = bb;
+        out->ldb = sp.b_ld;
+    }
+    return true;
 }
 
 // Where a call's split-K partial sums go: the library's per-(device, stream)
@@ -494,16 +577,28 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     if (ci < 0) return GEMM_ERR_INTERNAL;
     const TileConfig &cfg = tab[ci];
     if (kernel_of(cfg, true) == nullptr) return GEMM_ERR_INVALID_ARG;
-    int splits = 1, kps = 0;
-    {
-        const int esize = (int)elem_size(call.dtype);
-        const int v = 16 / esize;
-        const bool rows_aligned = call.lda % v == 0 && (uintptr_t)call.A % 16 == 0 &&
-                                  call.ldb % v == 0 && (uintptr_t)call.B % 16 == 0;
-        plan_split(cfg, layout, M, N, K, forced_split, cus, esize,
-                   call.bsrc == B_MATRIX && rows_aligned && direct_edges(layout, M, N, esize),
-                   &splits, &kps);
+
+    // bf16 operands with rows below 4-byte alignment: row-aligned copies
+    // (dispatcher's choice only; a forced entry runs on the operands as given)
+    if (forced_cfg < 0 && call.bsrc == B_MATRIX && !no_alloc) {
+        Call staged;
+        if (stage_operands(call, layout, device, stream, &staged, &rc))
+            return rc != GEMM_OK ? rc : run_call(staged, -1, 0, stream, false);
     }
+    // Outer extents the loads may read.  An operand stored with M (A^T) or N
+    // (B) along 16-byte-aligned rows is loaded in whole 16-byte chunks up to
+    // the next multiple of 16 bytes: each such chunk holds an element of its
+    // row, so it lies within the row's pitch or, in the last row, on the page
+    // of that element; the values past M or N feed only outputs that are
+    // never stored.  So the blocks at that edge keep the direct loads.
+    const int esize = (int)elem_size(call.dtype);
+    const int vec = 16 / esize;
+    const bool a_rows16 = call.lda % vec == 0 && (uintptr_t)call.A % 16 == 0;
+    const bool b_rows16 = call.bsrc == B_MATRIX && call.ldb % vec == 0 && (uintptr_t)call.B % 16 == 0;
+    const int64_t m_load = call.transa == GEMM_OP_T && a_rows16 ? ceil_div(M, vec) * vec : M;
+    const int64_t n_load = call.transb == GEMM_OP_N && b_rows16 ? ceil_div(N, vec) * vec : N;
+    int splits = 1, kps = 0;
+    plan_split(cfg, layout, M, N, K, forced_split, cus, esize, a_rows16 && b_rows16, &splits, &kps);
 
     // Thin remainders (dispatcher's choice only; a forced entry runs as asked):
     // when the last block row or column would hold at most an eighth of a
@@ -558,6 +653,8 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
+    a.m_load = (int)m_load;
+    a.n_load = (int)n_load;
     a.tiles_m = (int)ceil_div(M, cfg.bm);
     a.tiles_n = (int)ceil_div(N, cfg.bn);
     a.splits = splits;
@@ -577,12 +674,9 @@ int run_call(const Call &call, int forced_cfg, int forced_split, hipStream_t str
         if (rc != GEMM_OK) return rc;
     }
 
-    const int64_t esz = elem_size(call.dtype);
-    const int vec = (int)(16 / esz);
+    const int64_t esz = esize;
     // (an implicit B is gathered element by element: only A's alignment counts)
-    const bool aligned = call.lda % vec == 0 && (uintptr_t)call.A % 16 == 0 &&
-                         (call.bsrc != B_MATRIX ||
-                          (call.ldb % vec == 0 && (uintptr_t)call.B % 16 == 0));
+    const bool aligned = a_rows16 && (call.bsrc != B_MATRIX || b_rows16);
     // The direct-load path addresses a tile with per-thread 32-bit byte
     // offsets from the tile origin, over the tile's memory rows: BM (A as
     // given) or BK (A transposed) rows of A, BK (B as given) or BN (B
@@ -807,7 +901,7 @@ int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K)
     int splits = 1, kps = 0;
     const int es = dtype == GEMM_DTYPE_BF16 ? 2 : 4;
     dg::plan_split(tab[cfg], dg::LAYOUT_NN, M, N, K, 0, dg::compute_units(), es,
-                   dg::direct_edges(dg::LAYOUT_NN, M, N, es), &splits, &kps);
+                   true, &splits, &kps);
     return splits;
 }
 
@@ -822,8 +916,19 @@ int gemm_split_k_ex(int dtype, int cfg, int transa, int transb, int64_t M, int64
     int splits = 1, kps = 0;
     const int es = dtype == GEMM_DTYPE_BF16 ? 2 : 4;
     dg::plan_split(tab[cfg], transa * 2 + transb, M, N, K, 0, dg::compute_units(), es,
-                   dg::direct_edges(transa * 2 + transb, M, N, es), &splits, &kps);
+                   true, &splits, &kps);
     return splits;
+}
+
+int64_t gemm_operand_copy_bytes(int dtype_ab, int transa, int transb, int64_t M, int64_t N,
+                                int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb)
+{
+    const dg::GemmCall call{dtype_ab, dtype_ab, transa, transb, M, N, K, 1.0f, 0.0f,
+                            A, lda, B, ldb, nullptr, 0};
+    if (dg::check_args(call, false) != GEMM_OK) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    dg::StagePlan sp;
+    return dg::plan_stage(call, transa * 2 + transb, &sp) ? sp.a_bytes + sp.b_bytes : 0;
 }
 
 }  // extern "C"

@@ -1,6 +1,8 @@
 // The split-K reduce and the scale kernel (K == 0 or alpha == 0), with their
 // launchers.  Both finish elements of C the way the GEMM epilogue does:
 // alpha * sum + beta * C (C read only when beta != 0), stored as fp32 or bf16.
+#include <type_traits>
+
 #include "gemm_configs.hpp"
 
 namespace dg {
@@ -75,6 +77,54 @@ __global__ void scale_kernel(int M, int N, void *__restrict__ C, int64_t ldc, fl
     }
 }
 
+// Copy of a stored operand, `rows` rows of `cols` elements of ES bytes at a
+// pitch of ld_bytes, into dst at a pitch of ldd_bytes (16-byte aligned rows,
+// ldd_bytes >= cols * ES rounded up to 16).  Thread (lane l of a row group)
+// copies 16-byte chunk c of row r; a block holds 256 >> tpr_shift rows of
+// 1 << tpr_shift chunk lanes each, so narrow rows do not leave lanes idle.
+// A whole chunk at a source address that is 2 but not 4 bytes aligned comes
+// from the five aligned dwords that cover it, shifted into place (each holds
+// an element of the chunk, so it lies on a page the source occupies); the
+// last chunk of a row is read element by element and padded with zeros.
+template <int ES>
+__global__ void stage_rows_kernel(const unsigned char *__restrict__ src, int64_t ld_bytes,
+                                  int64_t rows, int cols, int cpr, int tpr_shift,
+                                  unsigned char *__restrict__ dst, int64_t ldd_bytes)
+{
+    constexpr int VEC = 16 / ES;
+    using E = typename std::conditional<ES == 2, uint16_t, uint32_t>::type;
+    const int rpb = (int)blockDim.x >> tpr_shift;
+    const int c = (int)blockIdx.x * (1 << tpr_shift) + ((int)threadIdx.x & ((1 << tpr_shift) - 1));
+    if (c >= cpr) return;
+    const int e0 = c * VEC;
+    for (int64_t r = (int64_t)blockIdx.y * rpb + ((int)threadIdx.x >> tpr_shift); r < rows;
+         r += (int64_t)gridDim.y * rpb) {
+        const unsigned char *s = src + r * ld_bytes + (int64_t)e0 * ES;
+        u32x4 v;
+        if (e0 + VEC <= cols) {
+            const uint32_t mis = (uint32_t)reinterpret_cast<uintptr_t>(s) & 3;   // 0 or 2
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(s - mis);
+            const uint32_t sh = mis * 8;
+            const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+            const uint32_t w4 = q[sh ? 4 : 3];
+            v[0] = __builtin_amdgcn_alignbit(w1, w0, sh);
+            v[1] = __builtin_amdgcn_alignbit(w2, w1, sh);
+            v[2] = __builtin_amdgcn_alignbit(w3, w2, sh);
+            v[3] = __builtin_amdgcn_alignbit(w4, w3, sh);
+        } else {
+            union {
+                u32x4 v;
+                E e[VEC];
+            } u;
+            const E *se = reinterpret_cast<const E *>(s);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) u.e[e] = e0 + e < cols ? se[e] : E(0);
+            v = u.v;
+        }
+        *reinterpret_cast<u32x4 *>(dst + r * ldd_bytes + (int64_t)e0 * ES) = v;
+    }
+}
+
 int grid_for(int64_t work, int threads)
 {
     int64_t blocks = (work + threads - 1) / threads;
@@ -98,6 +148,28 @@ hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, void 
                            dim3(threads), 0, stream, ws, splits, M, N, C, ldc, alpha, beta,
                            out_bf16);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_stage_rows(const void *src, int64_t ld, int64_t rows, int64_t cols, int esize,
+                             void *dst, int64_t ldd, hipStream_t stream)
+{
+    const int vec = 16 / esize;
+    const int64_t cpr = (cols + vec - 1) / vec;
+    int shift = 0;
+    while ((int64_t(1) << shift) < cpr && shift < 8) ++shift;
+    const int64_t rpb = 256 >> shift;
+    const int64_t gx = (cpr + (int64_t(1) << shift) - 1) >> shift;
+    int64_t gy = (rows + rpb - 1) / rpb;
+    if (gy > 32768) gy = 32768;  // the row loop covers the rest
+    if (esize == 2)
+        hipLaunchKernelGGL(stage_rows_kernel<2>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
+                           stream, static_cast<const unsigned char *>(src), ld * 2, rows,
+                           (int)cols, (int)cpr, shift, static_cast<unsigned char *>(dst), ldd * 2);
+    else
+        hipLaunchKernelGGL(stage_rows_kernel<4>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
+                           stream, static_cast<const unsigned char *>(src), ld * 4, rows,
+                           (int)cols, (int)cpr, shift, static_cast<unsigned char *>(dst), ldd * 4);
     return hipGetLastError();
 }
 

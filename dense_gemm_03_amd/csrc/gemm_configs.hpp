@@ -246,6 +246,12 @@ const TileConfig *bf16_configs(int *count);
 // (C read only when beta != 0), stored as fp32 or bf16.
 hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, void *C, int64_t ldc,
                                 float alpha, float beta, int out_bf16, hipStream_t stream);
+// Copies a stored operand (rows x cols elements of esize bytes at pitch ld,
+// any esize-aligned address) into dst (16-byte aligned) at pitch ldd, a
+// multiple of 16 bytes no smaller than the row; the columns from cols up to
+// the next multiple of 16 bytes are written as zeros.
+hipError_t launch_stage_rows(const void *src, int64_t ld, int64_t rows, int64_t cols, int esize,
+                             void *dst, int64_t ldd, hipStream_t stream);
 // C := beta * C over the M x N window, or C := 0 when beta == 0 (C not read):
 // the whole result when K == 0 or alpha == 0.
 hipError_t launch_scale(int M, int N, void *C, int64_t ldc, float beta, int out_bf16,

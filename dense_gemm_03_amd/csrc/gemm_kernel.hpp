@@ -180,6 +180,11 @@ struct KernelArgs {
     float *ws;        // split-K partial sums, slice-major, ld = N (splits > 1)
     int64_t lda, ldb, ldc;
     int M, N, K;
+    // outer extents the loads may read (>= M, N): for an operand stored with
+    // M or N along its rows, up to its row width when its rows are padded
+    // (the values there feed only outputs that are not stored); M and N for
+    // the others
+    int m_load, n_load;
     int tiles_m, tiles_n;
     int splits;       // number of K slices
     int k_per_split;  // K extent of a slice, a multiple of the k-tile
@@ -480,7 +485,7 @@ struct BlockCtx {
     const In *A;
     const In *B;
     int64_t lda, ldb;
-    int M, N;
+    int M, N;     // outer extents the loads may read (KernelArgs::m_load, n_load)
     int bm, bn;   // block origin in C
     int kend;     // end of this block's K range
     int tid, lane, wrow, wcol;
@@ -1642,8 +1647,8 @@ gemm_kernel(KernelArgs p)
     c.B = static_cast<const In *>(p.B);
     c.lda = p.lda;
     c.ldb = p.ldb;
-    c.M = p.M;
-    c.N = p.N;
+    c.M = p.m_load;
+    c.N = p.n_load;
     const int kbeg = slice * p.k_per_split;
     c.kend = min(p.K, kbeg + p.k_per_split);
     const int ntiles = (c.kend - kbeg + BK - 1) / BK;
@@ -1668,9 +1673,9 @@ gemm_kernel(KernelArgs p)
         // bytes per lane for the other edge blocks and for rows at any 4-byte
         // alignment.  Other cases, and the partial last k-tile, take the
         // masked loads.
-        const bool edge_mn = c.bm + BM > p.M || c.bn + BN > p.N;
-        const bool edge16 = (G::LA == KMAJOR || p.M % G::VEC == 0) &&
-                            (G::LB == KMAJOR || p.N % G::VEC == 0);
+        const bool edge_mn = c.bm + BM > c.M || c.bn + BN > c.N;
+        const bool edge16 = (G::LA == KMAJOR || c.M % G::VEC == 0) &&
+                            (G::LB == KMAJOR || c.N % G::VEC == 0);
         const bool x4 = ALIGNED && p.direct_ok && (!edge_mn || edge16);
         // bf16 dwords are element pairs (k, k+1) of a k-contiguous row or
         // (n, n+1) of an outer-contiguous one: rows must start 4-byte aligned,
@@ -1680,13 +1685,13 @@ gemm_kernel(KernelArgs p)
         // K: only whole k-tiles, which start at even k, take these loads.
         const bool pairs_ok =
             !G::BF16 || (((p.lda | p.ldb) & 1) == 0 && (((uintptr_t)p.A | (uintptr_t)p.B) & 3) == 0 &&
-                         (G::LA == KMAJOR || (p.M & 1) == 0) && (G::LB == KMAJOR || (p.N & 1) == 0));
+                         (G::LA == KMAJOR || (c.M & 1) == 0) && (G::LB == KMAJOR || (c.N & 1) == 0));
         const bool dw = G::DMA4 && p.direct_ok && pairs_ok && !x4;
         const int nfast = x4 || dw ? (c.kend - kbeg) / BK : 0;
         c.rot = (tm + tn) % 8;
         if constexpr (G::DMA4) {
-            c.a_end = operand_end_bytes<typename G::TA>(p.lda, p.M, p.K);
-            c.b_end = operand_end_bytes<typename G::TB>(p.ldb, p.N, p.K);
+            c.a_end = operand_end_bytes<typename G::TA>(p.lda, c.M, p.K);
+            c.b_end = operand_end_bytes<typename G::TB>(p.ldb, c.N, p.K);
             if (dw && nfast > 0)
                 main_loop_direct<G, 4>(lds0, lds1, lds2, lds3, c, kbeg, nfast, acc);
         }

@@ -34,9 +34,9 @@
  * Memory and ownership: A, B and C are device pointers owned by the caller
  * (for example tensors allocated by PyTorch).  C must not overlap A or B.  The
  * library never frees caller memory.  It owns a few device buffers per
- * (device, stream): the split-K partial sums of the GEMM, and for the
- * convolution calls of conv.h their term tables, zero-bordered image copies
- * and row-padded filter copies.  A buffer is allocated with hipMalloc on the
+ * (device, stream): the split-K partial sums of the GEMM, row-aligned copies
+ * of bf16 operands (see "Dispatch"), and for the convolution calls of conv.h
+ * their term tables, zero-bordered image copies and row-padded filter copies.  A buffer is allocated with hipMalloc on the
  * first call on a stream that needs it and grown (by at least half its size)
  * when a later call on that stream needs more; the buffer it replaces is kept,
  * not freed, until gemm_release_buffers(stream) or library unload, so that a
@@ -47,7 +47,10 @@
  * GEMM_ERR_CAPTURING and enqueues nothing.  Run the same call (or a larger
  * one) once on that stream before capturing, so the buffers already exist.
  * Calls that need no library buffer (no split-K, which the dispatcher picks
- * for most shapes; gemm_split_k tells) capture on any stream.
+ * for most shapes; gemm_split_k tells) capture on any stream.  The operand
+ * copies are an optimisation: a call that would copy but whose buffer cannot
+ * grow during capture runs on the operands in place instead (same result,
+ * slower); gemm_operand_copy_bytes gives the size to warm up.
  *
  * Streams: all work is enqueued on `stream` (NULL is the default stream) and
  * the calls return without waiting for it.  A fault inside a kernel surfaces
@@ -78,7 +81,18 @@
  * Dispatch: the tile choice and split-K plan depend on the shape, the operand
  * form and the compute-unit count of the current device (queried once per
  * device; 256, MI355X's count, when no device is visible); the bf16 split-K
- * plan also on whether the operand rows are 16-byte aligned.
+ * plan also on whether the operand rows are 16-byte aligned.  bf16 operands
+ * whose rows are not all 4-byte aligned (an odd leading dimension, an address
+ * that is 2 but not 4 bytes aligned, or an odd M for A^T or N for B) cannot
+ * be streamed with the kernels' direct loads.  When K >= 256, the product
+ * does at least 2^26 flops, and at least 160 flops per byte of those of its
+ * operands that lack 16-byte-aligned rows and are read k-contiguous (A, B^T)
+ * plus 56 per byte of those read outer-contiguous (A^T, B), the dispatcher
+ * first copies those operands into a library buffer with 16-byte-aligned,
+ * zero-padded rows, then runs the product on the copies; other products run
+ * on the operands in place.
+ * Calls with a forced table entry (the *_with_config entry points) and
+ * gemm_ex_noalloc never copy.
  */
 #ifndef DENSE_GEMM_03_AMD_GEMM_H
 #define DENSE_GEMM_03_AMD_GEMM_H
@@ -161,7 +175,11 @@ int gemm_ex(int dtype_ab, int dtype_c, int transa, int transb,
  * gemm_ex without any allocation, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, result and errors as gemm_ex, and the
- * same kernels and split-K plan, so its output equals gemm_ex's bit for bit.
+ * same kernels and split-K plan, so its output equals gemm_ex's bit for bit,
+ * except for the bf16 calls that gemm_ex runs on row-aligned copies
+ * (gemm_operand_copy_bytes > 0): this entry point runs them on the operands
+ * in place, where the k sum may be ordered differently (integer-valued
+ * operands still give the same result).
  * The split-K partial sums go to a fixed array of 64 MiB in the library's
  * device code (GEMM_SCRATCH_BYTES), one per GPU, held by each GPU the library
  * runs on until the process ends; the library allocates nothing, and the
@@ -239,6 +257,20 @@ const char *gemm_config_name(int dtype, int cfg);
 int gemm_split_k(int dtype, int cfg, int64_t M, int64_t N, int64_t K);
 int gemm_split_k_ex(int dtype, int cfg, int transa, int transb, int64_t M, int64_t N, int64_t K);
 int gemm_config_layouts(int dtype, int cfg);
+
+/*
+ * Bytes of the per-(device, stream) buffer that gemm_ex (and gemm_bf16) would
+ * use for row-aligned copies of the operands of this call (see "Dispatch"):
+ * 0 when it runs on them in place, GEMM_ERR_INVALID_ARG (negative) for the
+ * arguments gemm_ex rejects, apart from C.  A and B are examined for their
+ * alignment only, never read; no HIP call is made.  Callers that capture
+ * graphs run one such call (or a larger one) on the stream first, so that
+ * the buffer exists.
+ */
+int64_t gemm_operand_copy_bytes(int dtype_ab, int transa, int transb,
+                                int64_t M, int64_t N, int64_t K,
+                                const void *A, int64_t lda,
+                                const void *B, int64_t ldb);
 
 int gemm_f32_with_config(int cfg, int split_k,
                          int64_t M, int64_t N, int64_t K,

@@ -31,7 +31,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = ctypes.CDLL(dg.LIB_PATH)
     names = header_functions()
-    assert len(names) == 34, names
+    assert len(names) == 35, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(dg.SIGNATURES)
@@ -55,6 +55,80 @@ def test_release_buffers_without_a_device():
     if torch.cuda.is_available():
         pytest.skip("host-only check")
     assert dg.gemm_release_buffers(None) == dg.GEMM_ERR_NO_DEVICE
+
+
+def test_operand_copy_rule():
+    """bf16 operands whose rows are not all 4-byte aligned are copied into
+    zero-padded 16-byte-aligned rows when the product does 160 flops per
+    copied byte of a k-contiguous operand (A, B^T) plus 56 per copied byte of
+    an outer-contiguous one (A^T, B), K >= 256 and 2^26 flops.  The query
+    looks at the pointers' alignment only and never reads them, so integers
+    stand in for device addresses here."""
+    BF16, F32 = dg.GEMM_DTYPE_BF16, dg.GEMM_DTYPE_F32
+    q = dg.gemm_operand_copy_bytes
+    base = 1 << 20
+    rup = lambda x, m: -(-x // m) * m
+    # odd pitches: both operands, rows padded to 16 bytes, B after A at 256 bytes
+    assert q(BF16, 0, 0, 8191, 8191, 8191, base, 8191, base, 8191) == \
+        rup(8191 * 8192 * 2, 256) + 8191 * 8192 * 2
+    M, N, K = 4095, 2047, 3001          # stored shapes: A^T is K x M, B^T is N x K
+    for ta in (0, 1):
+        for tb in (0, 1):
+            ar, ac = (K, M) if ta else (M, K)
+            br, bc = (N, K) if tb else (K, N)
+            want = rup(ar * rup(ac, 8) * 2, 256) + br * rup(bc, 8) * 2
+            assert q(BF16, ta, tb, M, N, K, base, ac, base, bc) == want, (ta, tb)
+    # in place: 4-byte-aligned rows with even outer extents (pair loads), and
+    # 16-byte-aligned rows whatever the extents
+    assert q(BF16, 0, 0, 8190, 8190, 8190, base, 8190, base, 8190) == 0
+    assert q(BF16, 0, 0, 8191, 8191, 8191, base, 8192, base, 8192) == 0
+    assert q(BF16, 1, 0, 8191, 8191, 8191, base, 8192, base, 8192) == 0
+    # only the operand without 16-byte rows is copied: A at a 2-byte-aligned
+    # address; B with an even pitch but an odd N along its rows
+    assert q(BF16, 0, 0, 4096, 4096, 4096, base + 2, 4096, base, 4096) == 4096 * 4096 * 2
+    assert q(BF16, 0, 0, 4096, 4095, 4096, base, 4096, base, 4098) == 4096 * 4096 * 2
+    # the thresholds, one operand copied: M N / 8192 flops per copied byte of
+    # an operand with 8192-element padded rows along N (B, outer-contiguous;
+    # B^T, k-contiguous) or of A (k-contiguous)
+    assert q(BF16, 0, 0, 57, 8191, 4096, base, 4096, base, 8191) == 4096 * 8192 * 2
+    assert q(BF16, 0, 0, 56, 8191, 4096, base, 4096, base, 8191) == 0
+    assert q(BF16, 0, 1, 161, 8191, 4096, base, 4096, base, 4097) == 8191 * 4096 * 2
+    assert q(BF16, 0, 1, 159, 8191, 4096, base, 4096, base, 4097) == 0
+    assert q(BF16, 0, 0, 8191, 161, 4096, base, 4097, base, 168) == rup(8191 * 4096 * 2, 256)
+    assert q(BF16, 0, 0, 8191, 159, 4096, base, 4097, base, 168) == 0
+    assert q(BF16, 1, 0, 8191, 57, 4096, base, 8191, base, 64) == rup(4096 * 8192 * 2, 256)
+    assert q(BF16, 1, 0, 8191, 56, 4096, base, 8191, base, 64) == 0
+    # both copied: 160 per byte of A plus 56 per byte of B
+    assert q(BF16, 0, 0, 383, 383, 383, base, 383, base, 383) > 0
+    assert q(BF16, 0, 0, 207, 207, 4096, base, 4097, base, 207) == 0
+    assert q(BF16, 0, 0, 8191, 8191, 256, base, 257, base, 8191) > 0        # K = 256
+    assert q(BF16, 0, 0, 8191, 8191, 255, base, 255, base, 8191) == 0       # K < 256: C-bound
+    assert q(BF16, 0, 0, 320, 321, 256, base, 256, base, 321) == 0          # 313 per byte, < 2^26
+    assert q(F32, 0, 0, 8191, 8191, 8191, base, 8191, base, 8191) == 0      # fp32: never
+    assert q(BF16, 0, 0, 8191, 8191, 0, base, 1, base, 8191) == 0           # nothing to multiply
+    # the arguments gemm_ex rejects
+    bad = dg.GEMM_ERR_INVALID_ARG
+    assert q(BF16, 0, 0, 10, 10, 10, base, 9, base, 10) == bad              # lda < K
+    assert q(BF16, 0, 1, 10, 10, 10, base, 10, base, 9) == bad              # ldb < K for B^T
+    assert q(BF16, 0, 0, 10, 10, 10, base + 1, 10, base, 10) == bad         # not element aligned
+    assert q(BF16, 0, 0, 10, 10, 10, 0, 10, base, 10) == bad                # null A
+    assert q(5, 0, 0, 10, 10, 10, base, 10, base, 10) == bad
+    assert q(BF16, 2, 0, 10, 10, 10, base, 10, base, 10) == bad
+    assert q(BF16, 0, 0, -1, 10, 10, base, 10, base, 10) == bad
+
+
+def test_split_plan_with_aligned_rows_ignores_outer_parity():
+    """With 16-byte-aligned rows the loads at the M and N edges run to the
+    next 16 bytes, so every block takes the direct loads and the bf16 split
+    plan of a shape with odd M or N is that of the padded shape."""
+    BF16 = dg.GEMM_DTYPE_BF16
+    for ta, tb in [(0, 0), (1, 0), (1, 1), (0, 1)]:
+        for (M, N, K) in [(1535, 1535, 1536), (1023, 1021, 4096), (2001, 999, 3000)]:
+            c = dg.gemm_select_config_ex(BF16, ta, tb, M, N, K)
+            Mp, Np = -(-M // 8) * 8, -(-N // 8) * 8
+            assert dg.gemm_select_config_ex(BF16, ta, tb, Mp, Np, K) == c
+            assert dg.gemm_split_k_ex(BF16, c, ta, tb, M, N, K) == \
+                dg.gemm_split_k_ex(BF16, c, ta, tb, Mp, Np, K), (ta, tb, M, N, K)
 
 
 def test_config_table():
