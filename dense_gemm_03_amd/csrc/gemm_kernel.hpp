@@ -790,10 +790,12 @@ __device__ __forceinline__ void main_loop_direct(unsigned char *__restrict__ s0,
     tile_offsets(c.tid >> 6, c.lane, c.ldb, c.bn, c.N, o.b);
     // k of the next tile to load; past the last tile the loads wrap round to
     // tiles already done (never read, and in bounds), so the code has no branch
-    // rotated start for bf16 (measured: +3-6% on large square products;
-    // fp32, which needs an eighth of the bytes per flop, gains nothing), only
-    // on long K loops, where the wrapped tiles are few
-    int kt = G::BF16 && ntiles >= 32 ? c.rot : 0;
+    // rotated start for bf16 blocks with 64-byte tile rows (measured: +3-6% on
+    // large square products; fp32, which needs an eighth of the bytes per flop,
+    // gains nothing, and the 64-deep bf16 blocks, which request whole 128-byte
+    // lines, ran 0.8% faster without it at 8192^3), only on long K loops,
+    // where the wrapped tiles are few
+    int kt = G::BF16 && BK == 32 && ntiles >= 32 ? c.rot : 0;
     auto next_k = [&]() {
         const int k = k_first + kt * BK;
         kt = kt + 1 == ntiles ? 0 : kt + 1;

@@ -95,8 +95,9 @@ def _config(dtype, name):
 
 @pytest.mark.parametrize("name,bk", [("bf16_256x256x32_w4x2_s4", 32), ("bf16_256x256x64_w4x2_s2", 64)])
 def test_rotated_k_order_interior_blocks_exact(name, bk):
-    """The bf16 256x256 blocks walk their k-tiles from a start tile that depends
-    on the block's position once a block holds at least 32 interior k-tiles.
+    """The 32-deep bf16 256x256 blocks walk their k-tiles from a start tile
+    that depends on the block's position once a block holds at least 32
+    interior k-tiles (the 64-deep blocks walk the same long loops in order).
     512 x 512 x 64 BK (64 k-tiles) puts four interior blocks, with different
     start tiles, on that path, and 768 x 1024 x 33 BK exactly 33; integer
     operands make the whole C exact."""
