@@ -220,24 +220,21 @@ def gemm_general(A: np.ndarray, B: np.ndarray, alpha: float = 1.0, beta: float =
 def round_to_bf16_bits(x) -> np.ndarray:
     """Round float64 values to the nearest bf16 (8 significant bits), ties to
     the even significand, and return the bit patterns; overflow gives +-inf and
-    NaN a quiet NaN.  Subnormals keep the binary32 spacing 2^-133."""
+    NaN a quiet NaN.  Subnormals keep the binary32 spacing 2^-133.  The steps,
+    applied to every element at once: |v| = m 2^e with 0.5 <= m < 1, so 8-bit
+    significands are spaced 2^(e-8) apart (never closer than 2^-133); v is
+    rounded to a multiple of that spacing, halves to even; the result is
+    exactly representable in binary32, whose upper 16 bits are the bf16."""
     x = np.asarray(x, dtype=np.float64)
-    out = np.empty(x.shape, dtype=np.uint16)
-    flat, res = x.reshape(-1), out.reshape(-1)
-    for t, v in enumerate(flat):
-        if np.isnan(v):
-            res[t] = 0x7FC0
-            continue
-        if np.isinf(v) or v == 0.0:
-            res[t] = np.array([v], dtype=np.float32).view(np.uint32)[0] >> 16
-            continue
-        _, e = np.frexp(v)                     # |v| = m * 2^e, 0.5 <= m < 1
-        step = np.ldexp(1.0, max(int(e) - 8, -133))   # spacing of 8-bit significands
-        q = np.rint(v / step) * step           # np.rint rounds halves to even
-        if abs(q) >= 2.0 ** 128:
-            q = np.copysign(np.inf, v)
-        res[t] = np.array([q], dtype=np.float32).view(np.uint32)[0] >> 16
-    return out
+    with np.errstate(invalid="ignore", over="ignore"):
+        _, e = np.frexp(x)
+        step = np.ldexp(1.0, np.maximum(e.astype(np.int64) - 8, -133))
+        q = np.rint(x / step) * step                  # np.rint rounds halves to even
+        q = np.where(np.abs(q) >= 2.0 ** 128, np.copysign(np.inf, x), q)
+        q = np.where(np.isinf(x) | (x == 0.0), x, q)  # infinities and signed zeros as they are
+        bits = (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bits = np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
+    return bits.reshape(x.shape)
 
 
 def entries_general(A: np.ndarray, B: np.ndarray, I, J, alpha: float = 1.0, beta: float = 0.0,

@@ -252,6 +252,33 @@ def test_round_to_bf16_matches_torch_on_float32():
     assert np.array_equal(got, want)
 
 
+def test_round_to_bf16_matches_exact_rational_rounding():
+    """float64 values that binary32 cannot hold (so torch's conversion, which
+    starts from binary32, does not apply): the bf16 pattern equals rounding
+    the exact value with Python fractions -- the multiple of 2^(e-8) (at
+    least 2^-133) nearest to it, ties to even -- packed through binary32."""
+    import math
+    import struct
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal(3000) * np.exp(rng.uniform(-95, 95, 3000))
+    x = np.concatenate([x, (rng.integers(-(1 << 20), 1 << 20, 500) + 0.5) * 2.0 ** -12,
+                        [2.0 ** -140, -3 * 2.0 ** -135, 3.4e38, -3.5e38]])
+    got = oracle.round_to_bf16_bits(x)
+    for v, g in zip(x, got):
+        m, e = math.frexp(abs(v))
+        sp = max(e - 8, -133)
+        q = round(Fraction(abs(v)) / Fraction(2) ** sp)       # round half to even
+        val = Fraction(q) * Fraction(2) ** sp
+        if val >= Fraction(2) ** 128:
+            want = 0x7F80
+        else:
+            want = struct.unpack(">I", struct.pack(">f", float(val)))[0] >> 16
+        if v < 0:
+            want |= 0x8000
+        assert int(g) == want, "round(%r) = %#06x, want %#06x" % (v, int(g), want)
+
+
 def test_entries_general_match_full_product_bitwise():
     """The one-entry-at-a-time form equals the full generalised product at
     the same positions, bit for bit (same k order), for every transpose
