@@ -69,6 +69,7 @@ __device__ __forceinline__ void static_for(F &&f)
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -1508,15 +1509,16 @@ __device__ __forceinline__ void store_out(void *C, int64_t idx, float sum, float
     }
 }
 
-// Finished C through LDS, for interior blocks whose output is not the plain
-// fp32 product (alpha != 1, beta != 0 or bf16 C) and whose C rows are aligned:
-// the fragment layout gives each lane single elements of 32 columns, so
-// element-wise stores (and, with beta != 0, loads of the old C) would move 4
-// or 2 bytes per lane.  After the main loop the stages are free: each wave
-// writes one 32-row fragment row of its sub-block (32 x WTN fp32) to its own
-// LDS scratch, reads it back as 16-byte row pieces (4 consecutive columns),
-// and loads, scales and stores C in those pieces -- whole 128-byte lines
-// per half-wave.  The scratch is row-major with the 32-column halves of
+// Finished C through LDS, for interior blocks (the cases are listed where
+// the epilogue picks it): the fragment layout gives each lane single elements
+// of 32 columns, so element-wise stores (and, with beta != 0, loads of the
+// old C) would move 4 or 2 bytes per lane.  After the main loop the stages
+// are free: each wave writes one 32-row fragment row of its sub-block
+// (32 x WTN fp32) to its own LDS scratch, reads it back as 16-byte row pieces
+// (4 consecutive columns), and loads, scales and stores C in those pieces of
+// 4 elements -- a wave's row run of WTN elements in one piece per lane, or,
+// with `halves`, each piece as two stores of 2 elements (C rows 8-byte
+// aligned for fp32, 4-byte for bf16).  The scratch is row-major with the 32-column halves of
 // each 64-column group swapped in rows with bit 2 set, so the two lane halves
 // of a fragment write (rows i and i+4) fall on different banks and the
 // 16-byte reads of 16 lanes cover 256 contiguous bytes.
@@ -1545,7 +1547,7 @@ template <class G>
 __device__ __forceinline__ void staged_epilogue(unsigned char *l0, unsigned char *l1,
                                                 unsigned char *l2, unsigned char *l3,
                                                 const BlockCtx<G> &c, const KernelArgs &p,
-                                                const floatx16 (&acc)[G::FM][G::FN])
+                                                const floatx16 (&acc)[G::FM][G::FN], bool halves)
 {
     using S = StagedOut<G>;
     const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
@@ -1584,9 +1586,15 @@ __device__ __forceinline__ void staged_epilogue(unsigned char *l0, unsigned char
                     const int ch = c.lane + 64 * (u0 + g), rr = ch / S::CPR, cc = ch % S::CPR;
                     const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
                     if (out_bf16) {
-                        const uint2 w =
-                            *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.C) + idx);
-                        old[g] = u32x4{w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u};
+                        const uint32_t *q = reinterpret_cast<const uint32_t *>(
+                            static_cast<const uint16_t *>(p.C) + idx);
+                        const uint32_t w0 = q[0], w1 = q[1];
+                        old[g] = u32x4{w0 << 16, w0 & 0xFFFF0000u, w1 << 16, w1 & 0xFFFF0000u};
+                    } else if (halves) {
+                        const u32x2 *q = reinterpret_cast<const u32x2 *>(
+                            static_cast<const float *>(p.C) + idx);
+                        const u32x2 lo = q[0], hi = q[1];
+                        old[g] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                     } else {
                         old[g] = load16(static_cast<const float *>(p.C) + idx);
                     }
@@ -1603,15 +1611,32 @@ __device__ __forceinline__ void staged_epilogue(unsigned char *l0, unsigned char
                     if (read_c) v[e] += beta * __uint_as_float(old[g][e]);
                 }
                 const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
+                // non-temporal, as on the plain path: C is not read again here
                 if (out_bf16) {
-                    uint2 w;
-                    w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-                    w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.C) + idx) = w;
+                    const uint32_t w0 =
+                        (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+                    const uint32_t w1 =
+                        (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+                    uint16_t *out = static_cast<uint16_t *>(p.C) + idx;
+                    if (halves) {
+                        __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t *>(out));
+                        __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t *>(out + 2));
+                    } else {
+                        __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2 *>(out));
+                    }
                 } else {
-                    *reinterpret_cast<u32x4 *>(static_cast<float *>(p.C) + idx) =
-                        u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                              __float_as_uint(v[3])};
+                    float *out = static_cast<float *>(p.C) + idx;
+                    if (halves) {
+                        __builtin_nontemporal_store(u32x2{__float_as_uint(v[0]), __float_as_uint(v[1])},
+                                                    reinterpret_cast<u32x2 *>(out));
+                        __builtin_nontemporal_store(u32x2{__float_as_uint(v[2]), __float_as_uint(v[3])},
+                                                    reinterpret_cast<u32x2 *>(out + 2));
+                    } else {
+                        __builtin_nontemporal_store(
+                            u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                  __float_as_uint(v[3])},
+                            reinterpret_cast<u32x4 *>(out));
+                    }
                 }
             }
         }
@@ -1745,11 +1770,37 @@ gemm_kernel(KernelArgs p)
             }
         return;
     }
+    // Interior blocks of entries with a staged epilogue finish C through LDS
+    // in 4-element row pieces when the rows hold whole pieces (16 bytes fp32,
+    // 8 bytes bf16) or half pieces ("halves": rows 8- or 4-byte aligned,
+    // each piece stored in two halves): the outputs other than the plain
+    // fp32 product always, and the plain product when C's rows are not whole
+    // 128-byte lines.  Then a wave's 32-element row runs straddle two lines
+    // each, and the element-wise stores below issue twice as many partial-line
+    // writes as the staged pieces (measured: bf16 8192 x 30520 x 768,
+    // 587 -> 793 TF/s; 8192 x 8184 x 8192, 1288 -> 1311).
+    int staged = 0;   // 0: no, 1: whole pieces, 2: halves
+    if constexpr (StagedOut<G>::OK) {
+        const int64_t piece = p.out_bf16 ? 8 : 16;
+        const bool plain = p.alpha == 1.0f && p.beta == 0.0f && !p.out_bf16;
+        const bool lines = (p.ldc * 4) % 128 == 0 && (uintptr_t)p.C % 128 == 0;
+        if (!store_edge && !(plain && lines)) {
+            const int64_t esz = p.out_bf16 ? 2 : 4;
+            if ((p.ldc * esz) % piece == 0 && (uintptr_t)p.C % piece == 0)
+                staged = 1;
+            else if ((p.ldc * esz) % (piece / 2) == 0 && (uintptr_t)p.C % (piece / 2) == 0)
+                staged = 2;
+        }
+    }
+    if (staged) {
+        staged_epilogue<G>(lds0, lds1, lds2, lds3, c, p, acc, staged == 2);
+        return;
+    }
     if (p.alpha == 1.0f && p.beta == 0.0f && !p.out_bf16) {
         // the plain product into fp32 C.  C is written once and not read
         // again here: non-temporal stores keep it from evicting the operand
         // tiles other blocks still stream through the caches (measured
-        // 1-2.5% on bf16 8192^3).
+        // 1-2.5% on bf16 8192^3, 8% in a later build).
         float *out = static_cast<float *>(p.C);
 #pragma unroll
         for (int fm = 0; fm < G::FM; ++fm)
@@ -1765,15 +1816,6 @@ gemm_kernel(KernelArgs p)
                 }
             }
         return;
-    }
-    if constexpr (StagedOut<G>::OK) {
-        // whole C pieces: C rows 16-byte (fp32) or 8-byte (bf16) aligned
-        const int64_t align = p.out_bf16 ? 8 : 16;
-        const int64_t esz = p.out_bf16 ? 2 : 4;
-        if (!store_edge && (p.ldc * esz) % align == 0 && (uintptr_t)p.C % align == 0) {
-            staged_epilogue<G>(lds0, lds1, lds2, lds3, c, p, acc);
-            return;
-        }
     }
     static_for<0, G::FM>([&](auto fm) {
         static_for<0, G::FN>([&](auto fn) {

@@ -208,17 +208,21 @@ def test_exact_alpha_beta(bf16, out_bf16):
 
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 def test_staged_epilogue_every_config(bf16):
-    """Interior blocks whose output is not the plain fp32 product (alpha != 1,
-    beta != 0 or bf16 C) and whose C rows are aligned finish C through LDS in
-    16-byte row pieces (entries of more than 64 rows whose waves own at
-    least 64 columns; the others take the element-wise epilogue here).  Every
-    entry and operand form with C at an aligned leading dimension (N + 4),
-    integer operands, bit for bit against the oracle: alpha/beta with C read,
-    bf16 C, and beta == 0 over a NaN-filled C (never read).  The blocks at the
-    M and N edges take the element-wise path in the same call."""
+    """Interior blocks of entries of more than 64 rows whose waves own at
+    least 64 columns finish C through LDS in row pieces of 4 elements: every
+    output but the plain fp32 product, and the plain product too when C's rows
+    are not whole 128-byte lines.  Every entry and operand form, integer
+    operands, bit for bit against the oracle: C at a leading dimension of N + 4
+    (whole pieces: alpha/beta with C read, bf16 C, beta == 0 over a NaN-filled
+    C, and the plain product, whose 2080-byte rows are not whole lines), and
+    at N + 2 (rows only 8-byte aligned for fp32 C, 4-byte for bf16 C: each
+    piece stored in two halves).  The blocks at the M and N edges take the
+    element-wise path in the same call."""
     dtype = BF16 if bf16 else F32
     M, N, K = 520, 516, 100
     C0 = np.random.default_rng(12).integers(-9, 10, size=(M, N)).astype(np.float64)
+    cases = [(4, 2.0, -3.0, False), (4, 1.0, 0.0, True), (4, 0.5, 1.0, True), (4, -1.0, 0.0, False),
+             (4, 1.0, 0.0, False), (2, 1.0, 0.0, False), (2, 0.5, 1.0, True), (2, 2.0, -3.0, False)]
     for cfg in range(dg.gemm_num_configs(dtype)):
         name = dg.gemm_config_name(dtype, cfg)
         mask = dg.gemm_config_layouts(dtype, cfg)
@@ -226,13 +230,12 @@ def test_staged_epilogue_every_config(bf16):
             if not mask & (1 << (2 * ta + tb)):
                 continue
             A, B = _operands(M, N, K, ta, tb, _ints, 40, bf16)
-            for alpha, beta, out_bf16 in [(2.0, -3.0, False), (1.0, 0.0, True), (0.5, 1.0, True),
-                                          (-1.0, 0.0, False)]:
+            for pad_c, alpha, beta, out_bf16 in cases:
                 c0 = C0 if beta != 0.0 else None
                 what = "%s %s a=%g b=%g %s, ldc %d" % (name, TNAME[ta, tb], alpha, beta,
-                                                       "c_bf16" if out_bf16 else "c_f32", N + 4)
+                                                       "c_bf16" if out_bf16 else "c_f32", N + pad_c)
                 log(what)
-                _, raw = run_ex(A, B, ta, tb, alpha, beta, c0, out_bf16, cfg=cfg, pad_c=4)
+                _, raw = run_ex(A, B, ta, tb, alpha, beta, c0, out_bf16, cfg=cfg, pad_c=pad_c)
                 check_exact_ex(raw, A, B, ta, tb, alpha, beta, c0, out_bf16, what)
 
 
