@@ -38,6 +38,7 @@ address form, the im2col kernel against HBM; 2-D, 3-D and 4-D workloads) are
 timed too and printed as a separate JSON line before the last one.
 
 Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+                       [--operand-values workload|small-int|zero]
 """
 from __future__ import annotations
 
@@ -172,6 +173,25 @@ def _workload(name: str):
     return WORKLOADS[name] if name in WORKLOADS else VARIANTS[name]
 
 
+def _operands(w, values: str):
+    """The workload's operands (values "workload"), or arrays of the same
+    shapes and types holding small integers in [-3, 3] or zeros: the same
+    calls and instructions on other data, to show how the operand values move
+    the board's power and so its clock."""
+    from dense_gemm_03_amd import workloads as wl
+    if values == "workload":
+        return w.operands()
+    shapes = [(w.K, w.M) if w.transa else (w.M, w.K), (w.N, w.K) if w.transb else (w.K, w.N)]
+    bf16 = w.dtype == "bf16"
+    if values == "small-int":
+        gen = wl.small_int_bf16_bits if bf16 else wl.small_int_f32
+        return tuple(gen(sh, w.seed + 1 + i) for i, sh in enumerate(shapes))
+    return tuple(np.zeros(sh, dtype=np.uint16 if bf16 else np.float32) for sh in shapes)
+
+
+OPERAND_VALUES = "workload"
+
+
 def prepare(name: str):
     """Draw workload `name`'s operands on the host and copy them to the GPU;
     returns what measure() needs."""
@@ -180,14 +200,15 @@ def prepare(name: str):
     import dense_gemm_03_amd as dg
 
     w = _workload(name)
-    log("[bench] %s: drawing operands %dx%dx%d (%s)" % (name, w.M, w.N, w.K, w.dtype))
+    log("[bench] %s: drawing operands %dx%dx%d (%s, values: %s)" % (
+        name, w.M, w.N, w.K, w.dtype, OPERAND_VALUES))
 
     def dev(x):
         if x.dtype == np.uint16:
             return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
         return torch.from_numpy(x).to("cuda:0")
 
-    A_np, B_np = w.operands()
+    A_np, B_np = _operands(w, OPERAND_VALUES)
     A, B = dev(A_np), dev(B_np)
     del A_np, B_np
     if w.beta != 0.0:
@@ -497,10 +518,18 @@ def main() -> int:
                          "fwd_implicit_padded, wgrad_implicit_padded, fwd_implicit_window, "
                          "wgrad_implicit_window, im2col), "
                          "for per-route profiler passes")
+    ap.add_argument("--operand-values", choices=("workload", "small-int", "zero"),
+                    default="workload",
+                    help="operand values of the GEMM workloads: the workloads' own seeded "
+                         "distributions (default), integers in [-3, 3], or zeros -- the same "
+                         "calls on other data, to show how the values move power and clock "
+                         "(the CPU baseline keeps the workloads' values)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference kernel "
                          "for the HBM byte counters) and exit")
     args = ap.parse_args()
+    global OPERAND_VALUES
+    OPERAND_VALUES = args.operand_values
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this GEMM is built and timed on a single MI355X, "
@@ -593,7 +622,11 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w["dtype"],
-        "data": "synthetic (seeded uniform[-1,1] fp32 / normal(0,1) rounded to bf16)",
+        "data": "synthetic (seeded uniform[-1,1] fp32 / normal(0,1) rounded to bf16)"
+                if OPERAND_VALUES == "workload" else
+                "synthetic (%s operands: the workloads' shapes with %s)" % (
+                    OPERAND_VALUES, "integers in [-3, 3]" if OPERAND_VALUES == "small-int"
+                    else "zeros"),
         "config": {
             "workload": "%s GEMM %dx%dx%d" % (w["dtype"], w["M"], w["N"], w["K"]),
             "name": w["workload"],
