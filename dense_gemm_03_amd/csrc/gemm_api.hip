@@ -170,9 +170,17 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
         if (ceil_div(M, 64) * ceil_div(N, 64) <= cus && ceil_div(K, 32) >= 24) return small3;
         return small;
     }
+    // 128x128 blocks: two stages (64 KB, two resident per CU) where the grid
+    // needs more than one block per CU, three (96 KB, one per CU) where it
+    // fits in one round, so the third stage costs no residency: 2048^3 A . B
+    // 552 -> 740 TF/s, 2048 x 2048 x 4096 642 -> 849; at 2560^3 (400 blocks)
+    // three stages lost, 651 against 860 (harness, one box).  The efficiency
+    // figures rank the entries by the fill model; three stages rank just
+    // below two at equal fill.
     static const Candidate large[] = {
         {"bf16_256x256x32_w4x2_s4", 1, 0.52},
         {"bf16_128x128x64_w2x2_s2", 2, 0.42},
+        {"bf16_128x128x64_w2x2_s3", 1, 0.40},
     };
     // A read k-contiguous (A . B, A . B^T): 64-deep k-tiles in two stages
     // read whole 128-byte lines of A (and of B^T, whose 64-byte pieces kept
@@ -183,8 +191,10 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     static const Candidate large_ak[] = {
         {"bf16_256x256x64_w4x2_s2", 1, 0.55},
         {"bf16_128x128x64_w2x2_s2", 2, 0.42},
+        {"bf16_128x128x64_w2x2_s3", 1, 0.40},
     };
     static const int medium = config_index(dtype, "bf16_128x128x64_w2x2_s2");
+    static const int medium3 = config_index(dtype, "bf16_128x128x64_w2x2_s3");
     static const int small = config_index(dtype, "bf16_64x64x64_w2x2_s2");
     static const int small_deep = config_index(dtype, "bf16_64x64x64_w2x2_s4");
     static const int wide = config_index(dtype, "bf16_64x256x64_w1x4_s3");
@@ -198,8 +208,8 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     if (skinny && layout == LAYOUT_NT) return skinny_t;
     if (M <= 64 && N >= 1024) return layout == LAYOUT_NT ? wide_t : wide;  // split-K
     if (M >= 2048 && N >= 2048)
-        return layout == LAYOUT_NN || layout == LAYOUT_NT ? best_of(dtype, large_ak, 2, M, N, cus)
-                                                          : best_of(dtype, large, 2, M, N, cus);
+        return layout == LAYOUT_NN || layout == LAYOUT_NT ? best_of(dtype, large_ak, 3, M, N, cus)
+                                                          : best_of(dtype, large, 3, M, N, cus);
     // Mid-size and small products, from a sweep of A . B and A . B^T at M, N
     // of 512-2048 and K of 512-8192: 128x128 blocks (K-sliced when they do
     // not fill the chip) where they fill it or K is long; 64x64 blocks where
@@ -209,7 +219,9 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     // longer (1024 x 1024 x 4096: 18.0 us against 23.2).
     const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), t64 = ceil_div(M, 64) * ceil_div(N, 64);
     const int64_t kt = ceil_div(K, 64);
-    if (t128 >= cus || kt >= 96) return medium;
+    // a 128x128 grid of exactly one block per CU: one round, so the third
+    // stage costs no residency (as in the large class)
+    if (t128 >= cus || kt >= 96) return t128 == cus ? medium3 : medium;
     if (kt <= 32) return t64 >= cus ? small : small_deep;
     return 4 * t128 <= cus ? small_deep : medium;
 }

@@ -179,6 +179,13 @@ def test_shape_classes_of_the_workloads():
     assert dg.gemm_split_k_ex(F32, c, 0, 2, 64, 61504, 16384) == dg.GEMM_ERR_INVALID_ARG
     for big in ("fp32-4096", "bf16-8192", "tall"):
         assert _cfg_for(big)[3] == 1
+    # bf16 grids of exactly one 128x128 block per compute unit: three stages
+    # (one resident block, nothing lost); more than one per unit: two stages
+    for ta, tb in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+        assert dg.gemm_config_name(BF16, dg.gemm_select_config_ex(BF16, ta, tb, 2048, 2048, 2048)) \
+            == "bf16_128x128x64_w2x2_s3"
+        assert dg.gemm_config_name(BF16, dg.gemm_select_config_ex(BF16, ta, tb, 2560, 2560, 2560)) \
+            == "bf16_128x128x64_w2x2_s2"
     # large bf16 with A k-contiguous (A . B, A . B^T): 64-deep k-tiles
     for tb in (0, 1):
         for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096)]:
@@ -200,7 +207,7 @@ def test_shape_classes_of_the_workloads():
                 ((1000, 1000, 1000), "bf16_64x64x64_w2x2_s2", 1),
                 ((1024, 1024, 8192), "bf16_128x128x64_w2x2_s2", 8),
                 ((2000, 1000, 3000), "bf16_128x128x64_w2x2_s2", 3),
-                ((1024, 4096, 1024), "bf16_128x128x64_w2x2_s2", 1)]:
+                ((1024, 4096, 1024), "bf16_128x128x64_w2x2_s3", 1)]:
             c = dg.gemm_select_config_ex(BF16, 0, tb, M, N, K)
             assert dg.gemm_config_name(BF16, c) == name, (M, N, K, tb)
             assert dg.gemm_split_k_ex(BF16, c, 0, tb, M, N, K) == splits, (M, N, K, tb)
