@@ -100,7 +100,8 @@ struct Candidate {
 
 // Among `cands`, the entry with the best measured efficiency times the fill
 // of its grid for this M x N on `cus` compute units (-1 if a name is missing).
-int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N, int cus)
+int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N, int cus,
+            bool whole_grids = false)
 {
     int count = 0;
     const TileConfig *tab = table(dtype, &count);
@@ -112,6 +113,9 @@ int best_of(int dtype, const Candidate *cands, int n, int64_t M, int64_t N, int 
         // the grid of the main part (thin remainders run apart, see run_call)
         const int64_t tiles = ceil_div(main_extent(M, tab[idx].bm), tab[idx].bm) *
                               ceil_div(main_extent(N, tab[idx].bn), tab[idx].bn);
+        // whole_grids: entries of one resident block per CU whose grid leaves
+        // CUs idle would run K-sliced; left out where that is slow
+        if (whole_grids && cands[i].per_cu == 1 && tiles < cus) continue;
         const double score = cands[i].measured * fill(tiles, (int64_t)cus * cands[i].per_cu);
         if (score > best_score) {
             best_score = score;
@@ -151,17 +155,28 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
         static const int narrow = config_index(dtype, "f32_128x64_w2x1_s2");
         static const int small = config_index(dtype, "f32_64x64_w2x2_s2");
         static const int small3 = config_index(dtype, "f32_64x64_w2x2_s3");
+        // The efficiency figures rank the entries under the fill model; they
+        // were set against a sweep of A . B at M, N of 2048-4096 (every
+        // entry and split): 64x64 blocks in two stages (two resident per CU)
+        // where their grid fills whole rounds better than the three-stage
+        // ones (2048^3: 127 against 159 us; 2560^3: 274 against 326 for
+        // 256x128 blocks in three K slices; 3584^3: 699 against 712), three
+        // stages where they fill whole rounds (3072^3: 425 against 460), and
+        // the 256-column blocks where their grid covers the chip.  One-block
+        // entries whose grid would not cover the chip are left out: K-sliced,
+        // they lost (2560^3 above).
         static const Candidate large[] = {
             {"f32_256x256_w4x2_s2", 1, 0.93},
-            {"f32_256x128_w4x2_s2", 1, 0.85},
+            {"f32_256x128_w4x2_s2", 1, 0.885},
             {"f32_64x64_w2x2_s3", 3, 0.89},
+            {"f32_64x64_w2x2_s2", 2, 0.88},
         };
         if (N <= 64 && M >= 4096) return tall;   // tall-skinny: many 64-row blocks
         if (skinny && layout == LAYOUT_NN) return skinny_n;
         if (skinny && layout == LAYOUT_NT) return skinny_t;
         if (M <= 64 && N >= 1024)  // split-K
             return layout == LAYOUT_NT ? wide_t : layout == LAYOUT_NN ? wide_nn : wide;
-        if (M >= 2048 && N >= 2048) return best_of(dtype, large, 3, M, N, cus);
+        if (M >= 2048 && N >= 2048) return best_of(dtype, large, 4, M, N, cus, true);
         if (N <= 64) return narrow;
         // at most one 64x64 block per compute unit and a K loop of 24 or more
         // k-tiles: three stages hide more of the load latency (1000^3: 24.7

@@ -179,6 +179,17 @@ def test_shape_classes_of_the_workloads():
     assert dg.gemm_split_k_ex(F32, c, 0, 2, 64, 61504, 16384) == dg.GEMM_ERR_INVALID_ARG
     for big in ("fp32-4096", "bf16-8192", "tall"):
         assert _cfg_for(big)[3] == 1
+    # fp32 large class: 64x64 blocks in two stages where their grid fills
+    # whole rounds better than three stages, three stages where those fill
+    # whole rounds, and one-block entries only where their grid covers the chip
+    for (M, N, K), name in [((2048, 2048, 2048), "f32_64x64_w2x2_s2"),
+                            ((2560, 2560, 2560), "f32_64x64_w2x2_s2"),
+                            ((3072, 3072, 3072), "f32_64x64_w2x2_s3"),
+                            ((4096, 4096, 4096), "f32_256x256_w4x2_s2"),
+                            ((2048, 4096, 2048), "f32_256x128_w4x2_s2")]:
+        c = dg.gemm_select_config(F32, M, N, K)
+        assert dg.gemm_config_name(F32, c) == name, (M, N, K)
+        assert dg.gemm_split_k(F32, c, M, N, K) == 1
     # bf16 grids of exactly one 128x128 block per compute unit: three stages
     # (one resident block, nothing lost); more than one per unit: two stages
     for ta, tb in [(0, 0), (0, 1), (1, 0), (1, 1)]:
