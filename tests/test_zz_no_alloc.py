@@ -89,22 +89,23 @@ def test_noalloc_alpha_beta_and_unsplit_shape():
 
 
 def test_noalloc_refuses_plans_beyond_the_array():
-    """2048 x 7936 x 1024 fp32 takes 248 blocks of 256 x 256 and 3 K slices:
-    195 MB of partial sums, more than the array holds: refused, nothing
-    enqueued, C left as it was."""
+    """fp32 A^T . B^T at 64 x 32768 x 4096 takes 128 blocks of 64 x 256 and 12
+    K slices: 96 MB of partial sums, more than the array holds: refused,
+    nothing enqueued, C left as it was; gemm_ex runs the same call."""
     import torch
-    M, N, K = 2048, 7936, 1024
-    cfg = dg.gemm_select_config(F32, M, N, K)
-    splits = dg.gemm_split_k(F32, cfg, M, N, K)
+    M, N, K = 64, 32768, 4096
+    cfg = dg.gemm_select_config_ex(F32, 1, 1, M, N, K)
+    splits = dg.gemm_split_k_ex(F32, cfg, 1, 1, M, N, K)
     assert splits * M * N * 4 > dg.GEMM_SCRATCH_BYTES
-    A = torch.ones((M, K), device="cuda:0")
-    B = torch.ones((K, N), device="cuda:0")
+    A = torch.ones((K, M), device="cuda:0")        # stored K x M: op(A) = A^T
+    B = torch.ones((N, K), device="cuda:0")        # stored N x K: op(B) = B^T
     C = torch.full((M, N), 7.0, device="cuda:0")
-    rc = _call(dg.gemm_ex_noalloc, F32, A, B, C, M, N, K)
-    assert rc == dg.GEMM_ERR_SCRATCH_LIMIT
+    args = (F32, F32, dg.GEMM_OP_T, dg.GEMM_OP_T, M, N, K, 1.0, A.data_ptr(), M, B.data_ptr(), K,
+            0.0, C.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+    assert dg.gemm_ex_noalloc(*args) == dg.GEMM_ERR_SCRATCH_LIMIT
     torch.cuda.synchronize()
     assert bool((C == 7.0).all())
     # the allocating entry point runs the same call
-    assert _call(dg.gemm_ex, F32, A, B, C, M, N, K) == dg.GEMM_OK
+    assert dg.gemm_ex(*args) == dg.GEMM_OK
     torch.cuda.synchronize()
     assert bool((C == float(K)).all())
