@@ -14,8 +14,9 @@
  *   DIR/c0_bf16.bin                initial C (M x N), bf16
  *   DIR/x.bin, w.bin               fp32 image batch and filters
  * writes DIR/c_f32.out (gemm_f32), c_bf16.out (gemm_bf16), c_ex.out (gemm_ex:
- * bf16 C := 0.5 A^T.B^T - 2 C0), y.out (conv2d_fwd, fp32), and prints the
- * status string of one invalid call.  Exit status 0 when every call
+ * bf16 C := 0.5 A^T.B^T - 2 C0), y.out (conv2d_fwd, fp32), and prints two
+ * answers of the operand-copy query and the status string of one invalid
+ * call.  Exit status 0 when every call
  * returned GEMM_OK (and the invalid one GEMM_ERR_INVALID_ARG).
  */
 #include <stdint.h>
@@ -159,6 +160,16 @@ int main(int argc, char **argv)
     float *y = malloc(ys * 4);
     to_host(y, dy, ys * 4);
     write_file(dir, "y.out", y, ys * 4);
+
+    /* the operand-copy query (host only; the addresses are examined, not
+       read): none for this call's aligned rows, both operands of an 8191^3
+       bf16 product at odd pitches */
+    printf("copy bytes: %lld %lld\n",
+           (long long)gemm_operand_copy_bytes(GEMM_DTYPE_BF16, GEMM_OP_N, GEMM_OP_N, M, N, K, dAh, K,
+                                              dBh, N),
+           (long long)gemm_operand_copy_bytes(GEMM_DTYPE_BF16, GEMM_OP_N, GEMM_OP_N, 8191, 8191,
+                                              8191, (const void *)(uintptr_t)0x100000, 8191,
+                                              (const void *)(uintptr_t)0x100000, 8191));
 
     /* an invalid call: lda below the row length; nothing is launched */
     const int rc = gemm_f32(M, N, K, dA, K - 1, dB, N, dC, N, NULL);

@@ -1,7 +1,7 @@
 """The C ABI from plain C: tests/c_abi_consumer.c (built here with gcc against
 include/*.h and libdense_gemm.so, no Python or torch in that process) runs
-gemm_f32, gemm_bf16, gemm_ex and conv2d_fwd on seeded integer operands and
-one invalid call; its outputs must equal the oracle's bit for bit (integer
+gemm_f32, gemm_bf16, gemm_ex and conv2d_fwd on seeded integer operands, the
+operand-copy query, and one invalid call; its outputs must equal the oracle's bit for bit (integer
 operands make every sum exact; bf16 C is the exact value rounded once).
 """
 from __future__ import annotations
@@ -66,6 +66,10 @@ def test_plain_c_consumer_matches_the_oracle(tmp_path):
     log(res.stdout.strip())
     assert res.returncode == 0, res.stdout + res.stderr
     assert "invalid call: " + dg.gemm_status_string(dg.GEMM_ERR_INVALID_ARG) in res.stdout
+    big = dg.gemm_operand_copy_bytes(dg.GEMM_DTYPE_BF16, 0, 0, 8191, 8191, 8191, 1 << 20, 8191,
+                                     1 << 20, 8191)
+    assert big > 0
+    assert "copy bytes: 0 %d" % big in res.stdout
 
     got = np.fromfile(str(d / "c_f32.out"), dtype=np.float32).reshape(M, N)
     assert np.array_equal(got.astype(np.float64), oracle.gemm_f32(a, b)[0])

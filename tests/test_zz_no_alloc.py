@@ -4,6 +4,7 @@ runs the same kernels and split plan as gemm_ex, so through the C ABI its
 output must equal gemm_ex's bit for bit, on consecutive calls of shrinking
 size (the array keeps the previous call's contents), and a call whose plan
 needs more partial sums than the array holds is refused without touching C.
+bf16 products that gemm_ex runs on row-aligned copies run in place here.
 """
 from __future__ import annotations
 
@@ -86,6 +87,29 @@ def test_noalloc_alpha_beta_and_unsplit_shape():
     ref, got = _pair(F32, A, B)
     assert np.array_equal(ref, got)
     check_exact(got, A, B, "noalloc unsplit")
+
+
+def test_noalloc_runs_copy_eligible_bf16_in_place():
+    """A bf16 product at odd pitches that gemm_ex runs on row-aligned copies
+    (gemm_operand_copy_bytes > 0): the no-alloc entry point, which never
+    copies, runs it on the operands in place; on integer operands both equal
+    the oracle bit for bit, on two calls in a row, the second smaller."""
+    import torch
+    for (M, N, K, seed) in [(1537, 1539, 1541, 5), (1153, 1151, 1155, 6)]:
+        A_np = wl.small_int_bf16_bits((M, K), seed)
+        B_np = wl.small_int_bf16_bits((K, N), seed + 1)
+        A, B = to_device(A_np), to_device(B_np)
+        assert dg.gemm_operand_copy_bytes(BF16, 0, 0, M, N, K, A.data_ptr(), K, B.data_ptr(), N) > 0
+        out = []
+        for fn in (dg.gemm_ex_noalloc, dg.gemm_ex):
+            C = torch.full((M, N), float("nan"), device="cuda:0")
+            assert _call(fn, BF16, A, B, C, M, N, K) == dg.GEMM_OK
+            torch.cuda.synchronize()
+            out.append(C.cpu().numpy())
+        check_exact(out[0], A_np, B_np, "noalloc bf16 in place %dx%dx%d" % (M, N, K))
+        assert np.array_equal(out[0], out[1])
+        log("noalloc bf16 %dx%dx%d at odd pitches: in place, equal to gemm_ex's copies and the "
+            "oracle" % (M, N, K))
 
 
 def test_noalloc_refuses_plans_beyond_the_array():
