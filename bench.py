@@ -16,13 +16,17 @@ in HBM.  Prints ONE JSON line (last line of stdout):
                           summary (profiles/traffic.json) when it was taken on
                           the current sources, else null -- it is a stored
                           reading, not measured in this run
-  sclk_sustained          the graphics clock and board power the GPU holds over
-                          2.5 s of the headline workload run back to back after
-                          the timed steps (amdsmi GPU metrics, when readable;
-                          likewise for every configuration in 'also', as
-                          sclk_sustained_mhz and socket_power_w -- for the
-                          shortest calls the host's launch rate, not the GPU,
-                          can bound that back-to-back run)
+  per_call_ms             median, minimum and maximum of single calls (HIP events
+                          between consecutive calls, up to 50 calls after the
+                          timed steps; likewise in each 'also' entry)
+  sclk_sustained          the graphics clock, memory clock, board power and
+                          temperatures the GPU holds over 2.5 s of the headline
+                          workload run back to back after the timed steps
+                          (amdsmi GPU metrics, when readable; likewise for every
+                          configuration in 'also', as sclk_sustained_mhz,
+                          socket_power_w, mclk_mhz, hotspot_c and hbm_c -- for
+                          the shortest calls the host's launch rate, not the
+                          GPU, can bound that back-to-back run)
   cpu_baseline            the oracle (CPU, fp64) timed on a bounded sample of the
                           same workload on this host
   also                    the same measurement, in short form, for the other
@@ -129,12 +133,15 @@ def sustained_clock(step, seconds: float = 2.5):
     except Exception as e:  # noqa: BLE001 - reported, not fatal
         return {"mhz": None, "error": "%s: %s" % (type(e).__name__, e)}
 
+    def num(v):
+        return float(v) if isinstance(v, (int, float)) and not isinstance(v, bool) else None
+
     def read():
         m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
         mhz = float(sum(clks)) / len(clks) if clks else float(m.get("current_gfxclk") or 0)
-        w = m.get("current_socket_power")
-        return mhz, float(w) if isinstance(w, (int, float)) else None
+        return (mhz, num(m.get("current_socket_power")), num(m.get("current_uclk")),
+                num(m.get("temperature_hotspot")), num(m.get("temperature_mem")))
 
     samples, stop, err = [], threading.Event(), []
 
@@ -156,16 +163,23 @@ def sustained_clock(step, seconds: float = 2.5):
         torch.cuda.synchronize()
     stop.set()
     th.join()
-    late = sorted(v for t, v, _ in samples if t - t0 >= seconds - 1.0)
-    watts = sorted(w for t, _, w in samples if t - t0 >= seconds - 1.0 and w is not None)
+    tail = [x for x in samples if x[0] - t0 >= seconds - 1.0]
+
+    def median(i):
+        v = sorted(x[i] for x in tail if x[i] is not None)
+        return v[len(v) // 2] if v else None
+
+    late = sorted(x[1] for x in tail)
     if not late:
         return {"mhz": None, "error": err[0] if err else "no sample"}
     return {"mhz": late[len(late) // 2], "min_mhz": late[0], "max_mhz": late[-1],
-            "socket_power_w": watts[len(watts) // 2] if watts else None,
+            "socket_power_w": median(2), "mclk_mhz": median(3),
+            "hotspot_c": median(4), "hbm_c": median(5),
             "samples": len(late), "window_s": seconds,
-            "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs) and "
-                      "current_socket_power, medians over the last second of a %.1f s "
-                      "back-to-back run of this workload" % seconds}
+            "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), current_uclk, "
+                      "current_socket_power, temperature_hotspot and temperature_mem, medians "
+                      "over the last second of a %.1f s back-to-back run of this workload"
+                      % seconds}
 
 
 def _workload(name: str):
@@ -268,6 +282,19 @@ def measure(ctx, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     event_ms = ev0.elapsed_time(ev1) / steps
+
+    # Spread of single calls, outside the timed region: HIP events recorded
+    # between consecutive calls on the same stream, median and minimum.
+    n_calls = min(steps, 50)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
+    evs[0].record(stream)
+    for i in range(n_calls):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n_calls))
+    per_call_ms = {"median": per_call[n_calls // 2], "min": per_call[0], "max": per_call[-1],
+                   "calls": n_calls}
     ms_per_step = wall * 1e3 / steps
     tflops = w.flops * steps / wall / 1e12
     achieved = w.flops / (event_ms * 1e-3) / 1e12
@@ -299,6 +326,7 @@ def measure(ctx, steps: int, warmup: int):
         "split_k": splits,
         "roofline": roofline,
         "hbm_gbs": hbm_gbs,
+        "per_call_ms": per_call_ms,
         "operand_sets": len(operands),
         "step": step,
     }
@@ -599,10 +627,16 @@ def main() -> int:
             rf["traffic"] = int(rf["traffic"])
         out = {"shape": "%s %dx%dx%d %s" % (r["dtype"], r["M"], r["N"], r["K"], r["op"]),
                "value": round(r["value"], 2), "ms_per_step": round(r["ms_per_step"], 4),
-               "kernel_config": r["kernel_config"], "split_k": r["split_k"], "roofline": rf}
+               "kernel_config": r["kernel_config"], "split_k": r["split_k"], "roofline": rf,
+               "per_call_ms": {k: round(v, 4) if k != "calls" else v
+                               for k, v in r["per_call_ms"].items()}}
         if r["workload"] in clocks:
-            out["sclk_sustained_mhz"] = clocks[r["workload"]].get("mhz")
-            out["socket_power_w"] = clocks[r["workload"]].get("socket_power_w")
+            ck = clocks[r["workload"]]
+            out["sclk_sustained_mhz"] = ck.get("mhz")
+            out["socket_power_w"] = ck.get("socket_power_w")
+            for k in ("mclk_mhz", "hotspot_c", "hbm_c"):
+                if ck.get(k) is not None:
+                    out[k] = ck[k]
         if r["alpha"] != 1.0 or r["beta"] != 0.0 or r["c_dtype"] != "f32":
             out["alpha"], out["beta"], out["c_dtype"] = r["alpha"], r["beta"], r["c_dtype"]
         return out
@@ -635,6 +669,7 @@ def main() -> int:
             "parallelism": "single GPU",
         },
         "roofline": w["roofline"],
+        "per_call_ms": w["per_call_ms"],
         "sclk_sustained": clocks.get(args.workload),
         "cpu_baseline": cpu,
         "also": {n: short(r) for n, r in also.items()},
