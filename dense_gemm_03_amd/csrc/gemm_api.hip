@@ -203,10 +203,19 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     // 32-deep four-stage block: A . B^T +5% at 4096^3 and 8192^3, A . B
     // +1.9% at 8192^3 and +1.2% at 4096^3 (alternating, two boxes).  A^T . B
     // lost 2% with it, and A^T . B^T's element-wise variant spilled.
+    // 192 x 256 blocks (8 waves of 96 x 64) cover outputs that 256 x 256
+    // blocks leave a quarter or more of the chip idle on: 3072^2 is 192 of
+    // them against 144, 6144^2 three whole rounds against 2.25.  Measured
+    // against the previous choice (median of single calls, one box): A . B
+    // 3072^3 70.5 -> 60.2 us, 4608^3 203.6 -> 180.5, 6144^3 426.7 -> 381.4,
+    // 3072 x 3072 x 8192 152.6 -> 136.7; A . B^T 8-11% faster at the same
+    // shapes.  On a full grid they reach 0.48 of the peak (6144^3), against
+    // 0.55 for 256 x 256, which therefore stays at 4096^3 and 8192^3.
     static const Candidate large_ak[] = {
         {"bf16_256x256x64_w4x2_s2", 1, 0.55},
         {"bf16_128x128x64_w2x2_s2", 2, 0.42},
         {"bf16_128x128x64_w2x2_s3", 1, 0.40},
+        {"bf16_192x256x64_w2x4_s2", 1, 0.48},
     };
     static const int medium = config_index(dtype, "bf16_128x128x64_w2x2_s2");
     static const int medium3 = config_index(dtype, "bf16_128x128x64_w2x2_s3");
@@ -223,7 +232,7 @@ int select_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, int cu
     if (skinny && layout == LAYOUT_NT) return skinny_t;
     if (M <= 64 && N >= 1024) return layout == LAYOUT_NT ? wide_t : wide;  // split-K
     if (M >= 2048 && N >= 2048)
-        return layout == LAYOUT_NN || layout == LAYOUT_NT ? best_of(dtype, large_ak, 3, M, N, cus)
+        return layout == LAYOUT_NN || layout == LAYOUT_NT ? best_of(dtype, large_ak, 4, M, N, cus)
                                                           : best_of(dtype, large, 3, M, N, cus);
     // Mid-size and small products, from a sweep of A . B and A . B^T at M, N
     // of 512-2048 and K of 512-8192: 128x128 blocks (K-sliced when they do

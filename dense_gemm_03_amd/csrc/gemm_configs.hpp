@@ -172,7 +172,8 @@ hipError_t launch_gemm(const KernelArgs &args, int blocks, hipStream_t stream);
     X("bf16_64x64x256_w2x2_s2", true, 64, 64, 256, 2, 2, 2, 1, KK)         \
     X("bf16_64x64x64_w2x2_s4", true, 64, 64, 64, 2, 2, 4, 1, ALL)          \
     X("bf16_256x256x64_w4x2_s2", true, 256, 256, 64, 4, 2, 2, 8, AK)        \
-    X("bf16_128x128x64_w2x2_s3", true, 128, 128, 64, 2, 2, 3, 8, ALL)
+    X("bf16_128x128x64_w2x2_s3", true, 128, 128, 64, 2, 2, 3, 8, ALL)       \
+    X("bf16_192x256x64_w2x4_s2", true, 192, 256, 64, 2, 4, 2, 8, AK)
 
 // Launcher pointers of one entry and layout: both alignments, or nullptr.
 #define DG_FNS(BF16, BM, BN, BK, WM, WN, S, L)                                               \

@@ -206,6 +206,24 @@ def test_shape_classes_of_the_workloads():
     for ta, tb in [(1, 0), (1, 1)]:
         assert dg.gemm_config_name(BF16, dg.gemm_select_config_ex(BF16, ta, tb, 8192, 8192, 8192)) \
             == "bf16_256x256x32_w4x2_s4"
+    # 192 x 256 blocks (A . B and A . B^T) where 256 x 256 blocks would leave a
+    # quarter or more of the chip idle, unsplit; not where 256 x 256 or
+    # 128 x 128 blocks fill it better
+    for tb in (0, 1):
+        for (M, N, K), name in [((3072, 3072, 3072), "bf16_192x256x64_w2x4_s2"),
+                                ((4608, 4608, 4608), "bf16_192x256x64_w2x4_s2"),
+                                ((6144, 6144, 6144), "bf16_192x256x64_w2x4_s2"),
+                                ((3072, 4096, 2048), "bf16_192x256x64_w2x4_s2"),
+                                ((2560, 2560, 2560), "bf16_128x128x64_w2x2_s2"),
+                                ((2304, 3072, 4096), "bf16_128x128x64_w2x2_s2"),
+                                ((5120, 5120, 5120), "bf16_256x256x64_w4x2_s2")]:
+            c = dg.gemm_select_config_ex(BF16, 0, tb, M, N, K)
+            assert dg.gemm_config_name(BF16, c) == name, (M, N, K, tb)
+            assert dg.gemm_split_k_ex(BF16, c, 0, tb, M, N, K) == 1, (M, N, K, tb)
+    c = dg.gemm_select_config_ex(BF16, 0, 0, 3072, 3072, 3072)
+    assert dg.gemm_config_layouts(BF16, c) == (1 << 0) | (1 << 1)
+    assert dg.gemm_config_name(BF16, dg.gemm_select_config_ex(BF16, 1, 0, 3072, 3072, 3072)) \
+        != "bf16_192x256x64_w2x4_s2"
     # bf16 mid-size and small products (256 compute units assumed off the GPU):
     # 128x128 blocks where they fill the chip or K is long (K-sliced when they
     # do not fill it), 64x64 blocks otherwise, four stages for small grids
