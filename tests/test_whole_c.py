@@ -141,12 +141,14 @@ def test_many_blocks_xcd_renumbering_exact(bf16):
     ("f32", False, True, 4095, 4100, 160, 1.0, 1.0),
     ("bf16", False, False, 4097, 4095, 192, 1.0, 0.0),
     ("bf16", True, False, 4100, 4099, 128, -1.0, 2.0),
+    ("bf16", False, False, 3080, 3075, 192, 1.0, 0.0),
+    ("bf16", False, True, 3075, 3090, 160, 2.0, -1.0),
 ], ids=lambda c: "%s-%s%s-%dx%dx%d" % (c[0], "T" if c[1] else "N", "T" if c[2] else "N",
                                         c[3], c[4], c[5]))
 def test_thin_remainders_run_apart_exact(case):
     """Large products whose last block row or column would hold only a few
-    rows (columns): the dispatcher runs the full 256 x 256 blocks as one
-    product and the thin strips as products of their own.  Every entry of C,
+    rows (columns): the dispatcher runs the full 256 x 256 (or 192 x 256)
+    blocks as one product and the thin strips as products of their own.  Every entry of C,
     for transposed operands and alpha/beta too, equals the oracle's exact
     value (integer operands and C)."""
     import torch
@@ -154,7 +156,8 @@ def test_thin_remainders_run_apart_exact(case):
     bf16 = dt == "bf16"
     dtype = BF16 if bf16 else F32
     cfg = dg.gemm_select_config_ex(dtype, int(ta), int(tb), M, N, K)
-    assert dg.gemm_config_name(dtype, cfg).endswith(("256x256_w4x2_s2", "256x256x32_w4x2_s4", "256x256x64_w4x2_s2"))
+    assert dg.gemm_config_name(dtype, cfg).endswith(("256x256_w4x2_s2", "256x256x32_w4x2_s4",
+                                                     "256x256x64_w4x2_s2", "192x256x64_w2x4_s2"))
     A = _ints((K, M) if ta else (M, K), 80 + M % 5, bf16)
     B = _ints((N, K) if tb else (K, N), 90 + N % 5, bf16)
     C0 = np.random.default_rng(K).integers(-9, 10, size=(M, N)).astype(np.float32)
