@@ -1643,6 +1643,54 @@ __device__ __forceinline__ void staged_epilogue(unsigned char *l0, unsigned char
     });
 }
 
+// The staged epilogue for bf16 C with beta == 0 and C rows 16-byte aligned:
+// the scaled values are rounded to bf16 before they go through the wave's
+// scratch (the same single rounding of alpha * acc as above), so the scratch
+// holds half the bytes and each lane stores whole 16-byte pieces of 8
+// columns.  Same swizzle as the fp32 scratch: the two lane halves of a write
+// (rows 4 apart) fall on different banks, and a 16-lane read covers 256
+// contiguous bytes.
+template <class G>
+__device__ __forceinline__ void staged_epilogue_bf16(unsigned char *l0, unsigned char *l1,
+                                                     unsigned char *l2, unsigned char *l3,
+                                                     const BlockCtx<G> &c, const KernelArgs &p,
+                                                     const floatx16 (&acc)[G::FM][G::FN])
+{
+    using S = StagedOut<G>;
+    constexpr int CPR = G::WTN / 8;               // 16-byte pieces per row
+    constexpr int PER_LANE = 32 * CPR / 64;       // pieces per lane and row block
+    const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+    const int arr = wave / S::PER_STAGE;
+    unsigned char *scr = (arr == 0 ? l0 : arr == 1 ? l1 : arr == 2 ? l2 : l3) +
+                         (wave % S::PER_STAGE) * S::BYTES;
+    const int half = c.lane >> 5, l32 = c.lane & 31;
+    const float alpha = p.alpha;
+    // the stages' last readers are done before any wave writes its scratch
+    __syncthreads();
+    static_for<0, G::FM>([&](auto fm) {
+#pragma unroll
+        for (int fn = 0; fn < G::FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+                *reinterpret_cast<uint16_t *>(scr + 2 * (row * G::WTN +
+                                                         staged_col<G>(row, fn * 32 + l32))) =
+                    f32_to_bf16_rne(alpha * acc[fm][fn][r]);
+            }
+        // in-order LDS accesses of one wave: the reads see the writes above,
+        // and the next row block's writes follow these reads
+        const int64_t row0 = c.bm + c.wrow * G::WTM + fm * 32;
+        const int col0 = c.bn + c.wcol * G::WTN;
+#pragma unroll
+        for (int u = 0; u < PER_LANE; ++u) {
+            const int ch = c.lane + 64 * u, rr = ch / CPR, cc = ch % CPR;
+            const u32x4 v = lds_load16(scr, 2 * (rr * G::WTN + staged_col<G>(rr, 8 * cc)));
+            uint16_t *out = static_cast<uint16_t *>(p.C) + (row0 + rr) * p.ldc + col0 + 8 * cc;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out));
+        }
+    });
+}
+
 // ------------------------------------------------------------------ kernel --
 
 template <bool BF16, int BM, int BN, int BK, int WM, int WN, int STAGES, int LA, int LB,
@@ -1779,18 +1827,24 @@ gemm_kernel(KernelArgs p)
     // each, and the element-wise stores below issue twice as many partial-line
     // writes as the staged pieces (measured: bf16 8192 x 30520 x 768,
     // 587 -> 793 TF/s; 8192 x 8184 x 8192, 1288 -> 1311).
-    int staged = 0;   // 0: no, 1: whole pieces, 2: halves
+    int staged = 0;   // 0: no, 1: whole pieces, 2: halves, 3: bf16 pieces of 8 (beta == 0)
     if constexpr (StagedOut<G>::OK) {
         const int64_t piece = p.out_bf16 ? 8 : 16;
         const bool plain = p.alpha == 1.0f && p.beta == 0.0f && !p.out_bf16;
         const bool lines = (p.ldc * 4) % 128 == 0 && (uintptr_t)p.C % 128 == 0;
         if (!store_edge && !(plain && lines)) {
             const int64_t esz = p.out_bf16 ? 2 : 4;
-            if ((p.ldc * esz) % piece == 0 && (uintptr_t)p.C % piece == 0)
+            if (p.out_bf16 && p.beta == 0.0f && (p.ldc * 2) % 16 == 0 && (uintptr_t)p.C % 16 == 0)
+                staged = 3;
+            else if ((p.ldc * esz) % piece == 0 && (uintptr_t)p.C % piece == 0)
                 staged = 1;
             else if ((p.ldc * esz) % (piece / 2) == 0 && (uintptr_t)p.C % (piece / 2) == 0)
                 staged = 2;
         }
+    }
+    if (staged == 3) {
+        staged_epilogue_bf16<G>(lds0, lds1, lds2, lds3, c, p, acc);
+        return;
     }
     if (staged) {
         staged_epilogue<G>(lds0, lds1, lds2, lds3, c, p, acc, staged == 2);

@@ -211,18 +211,22 @@ def test_staged_epilogue_every_config(bf16):
     """Interior blocks of entries of more than 64 rows whose waves own at
     least 64 columns finish C through LDS in row pieces of 4 elements: every
     output but the plain fp32 product, and the plain product too when C's rows
-    are not whole 128-byte lines.  Every entry and operand form, integer
-    operands, bit for bit against the oracle: C at a leading dimension of N + 4
-    (whole pieces: alpha/beta with C read, bf16 C, beta == 0 over a NaN-filled
-    C, and the plain product, whose 2080-byte rows are not whole lines), and
-    at N + 2 (rows only 8-byte aligned for fp32 C, 4-byte for bf16 C: each
-    piece stored in two halves).  The blocks at the M and N edges take the
-    element-wise path in the same call."""
+    are not whole 128-byte lines; bf16 C with beta == 0 on 16-byte-aligned
+    rows goes through the scratch already rounded, in pieces of 8.  Every
+    entry and operand form, integer operands, bit for bit against the oracle:
+    C at a leading dimension of N + 4 (whole pieces: alpha/beta with C read,
+    bf16 C with and without beta, beta == 0 over a NaN-filled C, and the plain
+    product, whose 2080-byte rows are not whole lines), at N + 8 (bf16 rows
+    8-byte but not 16-byte aligned: pieces of 4), and at N + 2 (rows only
+    8-byte aligned for fp32 C, 4-byte for bf16 C: each piece stored in two
+    halves).  The blocks at the M and N edges take the element-wise path in
+    the same call."""
     dtype = BF16 if bf16 else F32
     M, N, K = 520, 516, 100
     C0 = np.random.default_rng(12).integers(-9, 10, size=(M, N)).astype(np.float64)
     cases = [(4, 2.0, -3.0, False), (4, 1.0, 0.0, True), (4, 0.5, 1.0, True), (4, -1.0, 0.0, False),
-             (4, 1.0, 0.0, False), (2, 1.0, 0.0, False), (2, 0.5, 1.0, True), (2, 2.0, -3.0, False)]
+             (4, 1.0, 0.0, False), (2, 1.0, 0.0, False), (2, 0.5, 1.0, True), (2, 2.0, -3.0, False),
+             (4, 2.0, 0.0, True), (8, 1.0, 0.0, True), (2, -1.0, 0.0, True)]
     for cfg in range(dg.gemm_num_configs(dtype)):
         name = dg.gemm_config_name(dtype, cfg)
         mask = dg.gemm_config_layouts(dtype, cfg)
