@@ -71,6 +71,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // Memory orientation of an operand tile.
@@ -445,13 +447,22 @@ __device__ __forceinline__ u32x4 load_chunk_masked(const In *row, bool row_ok, i
     return u.v;
 }
 
-// fp32 -> bf16 bit pattern, rounded to nearest with ties to even; a NaN stays
-// a (quiet) NaN.
+// Two fp32 values -> bf16 bit patterns (lo in the low half), rounded to
+// nearest with ties to even; a NaN stays a NaN with its sign and leading
+// payload bits and the quiet bit set.  In integer terms: u -> (u + 0x7FFF +
+// ((u >> 16) & 1)) >> 16 for numbers, u -> (u >> 16) | 0x40 for NaNs.  gfx950
+// converts a pair in one instruction (v_cvt_pk_bf16_f32); on the GPU it gave
+// exactly those integer results for 2^20 bit patterns (every upper half with
+// 16 lower halves: ties, half-ulp neighbours, NaN payloads, denormals), and
+// costs a sixth of the VALU work of the integer form.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{lo, hi}, bf16x2));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    return (uint16_t)f32x2_to_bf16x2_rne(f, 0.0f);
 }
 
 // Map a linear block id to (slice, tile row, tile column).
@@ -1613,10 +1624,8 @@ __device__ __forceinline__ void staged_epilogue(unsigned char *l0, unsigned char
                 const int64_t idx = (row0 + rr) * p.ldc + col0 + 4 * cc;
                 // non-temporal, as on the plain path: C is not read again here
                 if (out_bf16) {
-                    const uint32_t w0 =
-                        (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-                    const uint32_t w1 =
-                        (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+                    const uint32_t w0 = f32x2_to_bf16x2_rne(v[0], v[1]);
+                    const uint32_t w1 = f32x2_to_bf16x2_rne(v[2], v[3]);
                     uint16_t *out = static_cast<uint16_t *>(p.C) + idx;
                     if (halves) {
                         __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t *>(out));
@@ -1671,11 +1680,17 @@ __device__ __forceinline__ void staged_epilogue_bf16(unsigned char *l0, unsigned
 #pragma unroll
         for (int fn = 0; fn < G::FN; ++fn)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; r += 2) {
+                // rows `row` and `row + 1` of one column, rounded as a pair
                 const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+                const uint32_t w =
+                    f32x2_to_bf16x2_rne(alpha * acc[fm][fn][r], alpha * acc[fm][fn][r + 1]);
                 *reinterpret_cast<uint16_t *>(scr + 2 * (row * G::WTN +
                                                          staged_col<G>(row, fn * 32 + l32))) =
-                    f32_to_bf16_rne(alpha * acc[fm][fn][r]);
+                    (uint16_t)w;
+                *reinterpret_cast<uint16_t *>(
+                    scr + 2 * ((row + 1) * G::WTN + staged_col<G>(row + 1, fn * 32 + l32))) =
+                    (uint16_t)(w >> 16);
             }
         // in-order LDS accesses of one wave: the reads see the writes above,
         // and the next row block's writes follow these reads
