@@ -750,8 +750,7 @@ __device__ __forceinline__ void direct_tile(const unsigned char *stage, const un
     load_frags(stage, c, 1, nxt);
     // The two waves of a SIMD keep the default priority: raising it around
     // the MFMA bursts measured 0.7-0.9% slower on the large products (fp32
-    // 4096^3, bf16 8192^3), so the wave that reaches the barrier first does
-    // not hold the issue slot from the one behind it.
+    // 4096^3, bf16 8192^3, alternating runs).
     mma(cur, acc);
     interleave_step<G::N_MMA, G::N_DS, LOADS>();
     cur = nxt;
