@@ -315,11 +315,12 @@ struct Geo {
     // and wave.
     static constexpr int N_MMA = BF16 ? FM * FN : KS * FM * FN;
     static constexpr int N_DS = FM * TA::READS + FN * TB::READS;
-    // Interleave hints for the main loop (interleave_step): kept for bf16 and
-    // the smaller fp32 blocks; the fp32 256 x 256 block ran 0.7% faster at
-    // 4096^3 with the compiler's own order, bf16 8192^3 1.5-2% slower and the
-    // 64 x 256 fp32 block 0.6% slower (alternating runs).
-    static constexpr bool HINTS = BF16 || BM < 256 || BN < 256;
+    // Interleave hints for the main loop (interleave_step), bf16 only: with
+    // the compiler's own order bf16 8192^3 ran 1.5-2% slower, while the fp32
+    // blocks ran as fast or faster (alternating runs: 4096^3 -0.9%,
+    // 4097 x 4095 x 4099 -1.7%, 2048^3 -1.7%, 1000^3 -3%, the tall and
+    // im2col shapes within noise).
+    static constexpr bool HINTS = BF16;
     static constexpr int LOADS_PER_TILE = (TA::PIECES + TB::PIECES) / NW;
 
     // Direct loads of 4 bytes per lane (256 B per instruction), range-checked
