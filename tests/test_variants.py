@@ -338,6 +338,60 @@ def test_bf16_output_rounds_to_nearest_even():
         assert np.array_equal(raw, want), (value, alpha, raw[0, 0], want[0, 0])
 
 
+def _bf16_edge_values(rows, cols, seed):
+    """fp32 values whose bf16 rounding is decided at the last bit: upper
+    halves with normal exponents and random signs, lower halves at the exact
+    midpoint (0x8000, ties to even both ways), one unit either side of it,
+    zero and random; plus the largest finite values, whose rounding goes to
+    infinity (0x7F7F8000 is a midpoint with an odd significand, 0x7F7FFFFF
+    above it) or stays finite (0x7F7F7FFF)."""
+    rng = np.random.default_rng(seed)
+    hi = rng.integers(0x0080, 0x7F7F, size=(rows, cols), dtype=np.uint32)
+    hi |= rng.integers(0, 2, size=(rows, cols), dtype=np.uint32) << 15
+    lows = np.array([0x8000, 0x8000, 0x7FFF, 0x8001, 0x0000], dtype=np.uint32)
+    lo = lows[rng.integers(0, lows.size, size=(rows, cols))]
+    pick = rng.random((rows, cols)) < 0.2
+    lo = np.where(pick, rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint32), lo)
+    bits = (hi << 16) | lo
+    specials = np.array([0x7F7F8000, 0x7F7FFFFF, 0x7F7F7FFF, 0xFF7F8000, 0x3F808000, 0x3F818000],
+                        dtype=np.uint32)
+    bits[0, :7 * specials.size:7] = specials                 # an interior block
+    bits[rows // 2, :specials.size] = specials
+    bits[rows // 3, cols - specials.size:] = specials        # the edge block column
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("split", [1, 4], ids=["epilogue", "reduce"])
+@pytest.mark.parametrize("pad_c", [8, 4, 2], ids=["rows16", "rows8", "rows4"])
+@pytest.mark.parametrize("alpha", [1.0, 0.5])
+def test_bf16_rounding_edge_values_every_epilogue(pad_c, alpha, split):
+    """bf16 C from fp32 products whose exact results are chosen bit patterns:
+    A = I, so C = alpha B exactly before the one rounding, and B holds bf16
+    midpoints, their neighbours and values that round to infinity.  The
+    256 x 256 fp32 block finishes its interior blocks through LDS (C rows
+    16-byte aligned: pieces of 8 rounded before the scratch; 8-byte aligned:
+    pieces of 4; 4-byte aligned: halves) and its edge blocks element by
+    element; forced into four K slices, the reduce rounds instead (every
+    slice holds the one nonzero term or only zeros, so C is still exact).
+    Every output equals the oracle's rounding bit for bit."""
+    M, N = 512, 520
+    cfg = [c for c in range(dg.gemm_num_configs(F32))
+           if dg.gemm_config_name(F32, c) == "f32_256x256_w4x2_s2"][0]
+    A = np.eye(M, dtype=np.float32)
+    B = _bf16_edge_values(M, N, 31 + pad_c)
+    assert dg.gemm_split_k(F32, cfg, M, N, M) > 1            # unforced, it would slice K
+    _, raw = run_ex(A, B, False, False, alpha, 0.0, None, True, cfg=cfg, split_k=split, pad_c=pad_c)
+    want = oracle.round_to_bf16_bits(alpha * B.astype(np.float64))
+    bad = np.argwhere(raw != want)
+    assert bad.size == 0, "%d outputs differ, first %s: input %#010x gpu %#06x want %#06x" % (
+        len(bad), tuple(bad[0]), int(B.view(np.uint32)[tuple(bad[0])]), int(raw[tuple(bad[0])]),
+        int(want[tuple(bad[0])]))
+    if alpha == 1.0:
+        assert np.count_nonzero(want == 0x7F80) >= 6 and np.count_nonzero(want == 0xFF80) >= 3
+    log("bf16 rounding of %d chosen values (ldc %d, alpha %g, %d slices): bit for bit" % (
+        M * N, N + pad_c, alpha, split))
+
+
 def test_variants_deterministic():
     import torch
     M, N, K = 512, 384, 2048
